@@ -1,0 +1,31 @@
+"""CPU oracle for the exact attention forward and its MXFP4 Direct-P variant.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, links or
+calls this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+kernels, the C-ABI library or its Python binding; the only common input is
+the seeded generator in ``synth/``.
+
+Everything here is plain float64 numpy (or pure Python for the brute-force
+check), written from the definitions so that a reader can check it by eye:
+
+* ``exact``  -- O = softmax(scale * Q K^T + mask) V and the row log-sum-exp.
+  The FlashAttention series reaches this result exactly (tiling plus
+  recomputation avoids the N x N matrix in memory but does not change the
+  value; "FlashAttention-4发布：原生支持Blackwell…", section
+  "从V1到V4：一部浓缩的注意力优化史", the FlashAttention (2022) entry), so the
+  oracle is the plain definition, row chunk by row chunk.
+* ``mx``     -- OCP MXFP4 quantisation (E2M1 payload, E8M0 block scale) and a
+  step-by-step emulation of Direct-P ("Hardware-Aware FP4 FlashAttention-4",
+  section "1. Direct-P para Inferencia Directa").
+
+Parity status: every function is pinned by tests under ``tests/`` against
+brute force, a library routine (torch's CPU attention in float64), closed
+forms and invariants; see the test modules ``test_oracle_exact.py`` and
+``test_oracle_mx.py``.
+"""
+
+from .exact import attention, attention_brute, attention_head, attention_rows, kv_head
+from . import mx
+
+__all__ = ["attention", "attention_brute", "attention_head", "attention_rows", "kv_head", "mx"]

@@ -1,0 +1,137 @@
+"""Exact attention forward in float64: the plain definition, no tiling.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Definition followed (the series' forward, "FlashAttention-4发布：原生支持
+Blackwell…", section "从V1到V4", FlashAttention (2022) entry: tiling and
+recomputation reach the same output without storing the N x N matrix):
+
+    s_ij   = scale * sum_c q[i, c] * k[j, c]
+    s_ij   = -inf            if causal and j > i
+    m_i    = max_j s_ij
+    l_i    = sum_j exp(s_ij - m_i)
+    O[i,:] = sum_j exp(s_ij - m_i) * v[j, :] / l_i
+    LSE_i  = m_i + ln(l_i)                      (natural log)
+
+Grouped-query attention (named in the same section's FlashAttention-2 entry)
+maps query head hq to key/value head hq // (Hq / Hkv).  A row whose keys are
+all masked (never reached with the causal mask when Q and K have the same
+length) gets O = 0 and LSE = -inf.
+
+Inputs are float64 arrays q [B, Hq, N, d], k and v [B, Hkv, N, d]; bf16
+inputs are widened exactly by the caller.
+"""
+
+import math
+
+import numpy as np
+
+
+def kv_head(hq, Hq, Hkv):
+    """Key/value head serving query head hq: contiguous groups of Hq/Hkv heads."""
+    return hq // (Hq // Hkv)
+
+
+def scores(q_rows, k_head, scale):
+    """scale * q_rows @ k^T  ->  [rows, N_k]."""
+    return scale * (q_rows @ k_head.T)
+
+
+def apply_mask(s, row_ids, causal):
+    """Additive -inf mask: key j is hidden from query i when causal and j > i."""
+    if not causal:
+        return s
+    cols = np.arange(s.shape[1])
+    return np.where(cols[None, :] > row_ids[:, None], -np.inf, s)
+
+
+def softmax_parts(s):
+    """Row max m, unnormalised weights e = exp(s - m) and their sum l."""
+    m = s.max(axis=1)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    e = np.exp(s - m_safe[:, None])
+    l = e.sum(axis=1)
+    return m, e, l
+
+
+def finish(m, e, l, v_head):
+    """O = (e @ v) / l and LSE = m + ln l; all-masked rows give O = 0, LSE = -inf."""
+    live = l > 0
+    l_safe = np.where(live, l, 1.0)
+    o = (e @ v_head) / l_safe[:, None]
+    o[~live] = 0.0
+    with np.errstate(divide="ignore"):
+        lse = np.where(live, m + np.log(l_safe), -np.inf)
+    return o, lse
+
+
+def attention_rows(q, k, v, causal, scale, b, hq, rows):
+    """O and LSE for the listed query rows of one (batch, query head) slice."""
+    B, Hq, N, d = q.shape
+    hk = kv_head(hq, Hq, k.shape[1])
+    rows = np.asarray(rows, dtype=np.int64)
+    s = scores(q[b, hq, rows, :], k[b, hk], scale)
+    s = apply_mask(s, rows, causal)
+    m, e, l = softmax_parts(s)
+    return finish(m, e, l, v[b, hk])
+
+
+def attention_head(q, k, v, causal, scale, b, hq, chunk=512):
+    """All rows of one (batch, query head) slice, in chunks of whole rows."""
+    N = q.shape[2]
+    o = np.empty((N, v.shape[3]), dtype=np.float64)
+    lse = np.empty((N,), dtype=np.float64)
+    for r0 in range(0, N, chunk):
+        rows = np.arange(r0, min(N, r0 + chunk))
+        o[rows], lse[rows] = attention_rows(q, k, v, causal, scale, b, hq, rows)
+    return o, lse
+
+
+def attention(q, k, v, causal, scale, chunk=512):
+    """Exact forward over the whole [B, Hq, N, d] problem: returns (O, LSE)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, N, d = q.shape
+    if k.shape[1] == 0 or Hq % k.shape[1] != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    o = np.empty(q.shape[:3] + (v.shape[3],), dtype=np.float64)
+    lse = np.empty(q.shape[:3], dtype=np.float64)
+    for b in range(B):
+        for hq in range(Hq):
+            o[b, hq], lse[b, hq] = attention_head(q, k, v, causal, scale, b, hq, chunk)
+    return o, lse
+
+
+def attention_brute(q, k, v, causal, scale):
+    """The same definition as scalar Python loops with math.exp (tiny inputs only)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, N, d = q.shape
+    Hkv, Nk, dv = k.shape[1], k.shape[2], v.shape[3]
+    group = Hq // Hkv
+    o = np.zeros((B, Hq, N, dv))
+    lse = np.zeros((B, Hq, N))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // group
+            for i in range(N):
+                s = []
+                for j in range(Nk):
+                    if causal and j > i:
+                        continue
+                    acc = 0.0
+                    for c in range(d):
+                        acc += float(q[b, h, i, c]) * float(k[b, g, j, c])
+                    s.append((j, scale * acc))
+                if not s:
+                    lse[b, h, i] = -math.inf
+                    continue
+                mx = max(val for _, val in s)
+                w = [(j, math.exp(val - mx)) for j, val in s]
+                tot = sum(x for _, x in w)
+                for c in range(dv):
+                    o[b, h, i, c] = sum(x * float(v[b, g, j, c]) for j, x in w) / tot
+                lse[b, h, i] = mx + math.log(tot)
+    return o, lse

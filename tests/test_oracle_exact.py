@@ -1,0 +1,107 @@
+"""The exact float64 oracle against its pins, and planted mistakes against the pins."""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import exact
+import pins_exact
+
+
+@pytest.mark.parametrize("pin", pins_exact.ALL_PINS, ids=lambda p: p.__name__)
+def test_oracle_pin(pin):
+    pin(oracle.attention)
+
+
+def test_rows_match_full():
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((1, 4, 40, 8))
+    k = rng.standard_normal((1, 2, 40, 8))
+    v = rng.standard_normal((1, 2, 40, 8))
+    o, lse = oracle.attention(q, k, v, True, 0.4, chunk=7)
+    rows = np.array([0, 5, 39, 17])
+    orow, lrow = oracle.attention_rows(q, k, v, True, 0.4, 0, 3, rows)
+    assert np.array_equal(orow, o[0, 3, rows]) or np.allclose(orow, o[0, 3, rows], atol=1e-14)
+    assert np.allclose(lrow, lse[0, 3, rows], atol=1e-14)
+
+
+def test_fully_masked_row_reading():
+    """A row with no visible key (not reachable with equal Q/K lengths) gives O = 0, LSE = -inf."""
+    m, e, l = exact.softmax_parts(np.full((1, 4), -np.inf))
+    o, lse = exact.finish(m, e, l, np.ones((4, 3)))
+    assert np.all(o == 0) and np.isneginf(lse[0])
+
+
+# ---- planted mistakes: each must fail at least one pin -------------------------------
+
+def _mut_drop_scale(monkeypatch):
+    monkeypatch.setattr(exact, "scores", lambda qr, kh, scale: qr @ kh.T)
+
+
+def _mut_mask_diagonal(monkeypatch):
+    def bad(s, rows, causal):
+        if not causal:
+            return s
+        cols = np.arange(s.shape[1])
+        return np.where(cols[None, :] >= rows[:, None], -np.inf, s)
+    monkeypatch.setattr(exact, "apply_mask", bad)
+
+
+def _mut_gqa_modulo(monkeypatch):
+    monkeypatch.setattr(exact, "kv_head", lambda hq, Hq, Hkv: hq % Hkv)
+
+
+def _mut_lse_log2(monkeypatch):
+    orig = exact.finish
+
+    def bad(m, e, l, vh):
+        o, lse = orig(m, e, l, vh)
+        return o, m + np.log2(np.where(l > 0, l, 1.0))
+    monkeypatch.setattr(exact, "finish", bad)
+
+
+def _mut_sign(monkeypatch):
+    def bad(s):
+        m = s.max(axis=1)
+        m_safe = np.where(np.isfinite(m), m, 0.0)
+        with np.errstate(over="ignore", invalid="ignore"):
+            e = np.exp(m_safe[:, None] - s)
+        e = np.where(np.isfinite(s), e, 0.0)
+        return m, e, e.sum(axis=1)
+    monkeypatch.setattr(exact, "softmax_parts", bad)
+
+
+def _mut_transposed_operand(monkeypatch):
+    orig = exact.attention_rows
+
+    def bad(q, k, v, causal, scale, b, hq, rows):
+        return orig(q, k, k if k.shape == v.shape else v, causal, scale, b, hq, rows)
+    monkeypatch.setattr(exact, "attention_rows", bad)
+
+
+def _mut_lse_without_max(monkeypatch):
+    orig = exact.finish
+
+    def bad(m, e, l, vh):
+        o, lse = orig(m, e, l, vh)
+        return o, np.log(np.where(l > 0, l, 1.0))
+    monkeypatch.setattr(exact, "finish", bad)
+
+
+def _mut_unnormalised(monkeypatch):
+    def bad(m, e, l, vh):
+        live = l > 0
+        return e @ vh, np.where(live, m + np.log(np.where(live, l, 1.0)), -np.inf)
+    monkeypatch.setattr(exact, "finish", bad)
+
+
+MUTANTS = [_mut_drop_scale, _mut_mask_diagonal, _mut_gqa_modulo, _mut_lse_log2, _mut_sign,
+           _mut_transposed_operand, _mut_lse_without_max, _mut_unnormalised]
+
+
+@pytest.mark.parametrize("mutant", MUTANTS, ids=lambda m: m.__name__)
+def test_planted_mistake_is_caught(mutant, monkeypatch):
+    mutant(monkeypatch)
+    with np.errstate(all="ignore"):
+        failures = pins_exact.run_all(oracle.attention)
+    assert failures, "a planted mistake passed every pin"
