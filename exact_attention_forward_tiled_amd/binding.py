@@ -1,0 +1,199 @@
+"""ctypes binding of libattn.so (declared in include/attn.h).
+
+Argument marshalling only: every step of the attention forward runs in the
+HIP kernels behind the C ABI.  torch is used for device memory and streams.
+There is no fallback: if libattn.so is missing or fails to load, importing
+this module raises.
+"""
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libattn.so")
+
+ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, -1, -2, -3
+EXP_MODES = {"hw": 0, "poly": 1}
+
+# entry points declared in include/attn.h
+EXPORTS = ("attn_default_opts", "attn_fwd", "attn_fwd_ex", "attn_fwd_mxfp4", "attn_fwd_mxfp4_ex",
+           "attn_quantize_mxfp4_rows", "attn_quantize_mxfp4_cols_t", "attn_strerror",
+           "attn_last_hip_error")
+
+
+class AttnOpts(ctypes.Structure):
+    _fields_ = [("tau", ctypes.c_float), ("exp_mode", ctypes.c_int),
+                ("stats", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run "
+                          "`python -m exact_attention_forward_tiled_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F, LL = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_longlong
+    OP = ctypes.POINTER(AttnOpts)
+    sig = {
+        "attn_default_opts": (None, [OP]),
+        "attn_fwd": (I, [P, P, P, P, P, I, I, I, I, I, I, F]),
+        "attn_fwd_ex": (I, [P, P, P, P, P, I, I, I, I, I, I, F, OP, P]),
+        "attn_fwd_mxfp4": (I, [P] * 8 + [I] * 6 + [F]),
+        "attn_fwd_mxfp4_ex": (I, [P] * 8 + [I] * 6 + [F, OP, P]),
+        "attn_quantize_mxfp4_rows": (I, [P, P, P, LL, I, P]),
+        "attn_quantize_mxfp4_cols_t": (I, [P, P, P, I, I, I, P]),
+        "attn_strerror": (ctypes.c_char_p, [I]),
+        "attn_last_hip_error": (I, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+class AttnError(RuntimeError):
+    pass
+
+
+def check(status):
+    """Map a libattn status code to an exception."""
+    if status == ATTN_OK:
+        return
+    msg = lib.attn_strerror(status).decode()
+    if status == ATTN_EINVAL:
+        raise ValueError(f"libattn: {msg}")
+    if status == ATTN_EUNSUPPORTED:
+        raise NotImplementedError(f"libattn: {msg}")
+    if status == ATTN_EHIP:
+        raise AttnError(f"libattn: {msg} (hipError_t {lib.attn_last_hip_error()})")
+    raise AttnError(f"libattn: status {status}")
+
+
+def make_opts(tau=8.0, exp_mode="hw", stats_ptr=None):
+    o = AttnOpts()
+    lib.attn_default_opts(ctypes.byref(o))
+    o.tau = float(tau)
+    o.exp_mode = EXP_MODES[exp_mode] if isinstance(exp_mode, str) else int(exp_mode)
+    o.stats = stats_ptr
+    return o
+
+
+# ---- raw C-ABI calls (pointers are ints, streams are hipStream_t handles or None) ----
+
+def attn_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale):
+    return lib.attn_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale)
+
+
+def attn_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, opts=None, stream=None):
+    return lib.attn_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale,
+                           ctypes.byref(opts) if opts is not None else None, stream)
+
+
+def attn_fwd_mxfp4_ex(q4, qs, k4, ks, vt4, vts, o, lse, B, Hq, Hkv, N, d, causal, scale,
+                      opts=None, stream=None):
+    return lib.attn_fwd_mxfp4_ex(q4, qs, k4, ks, vt4, vts, o, lse, B, Hq, Hkv, N, d, causal,
+                                 scale, ctypes.byref(opts) if opts is not None else None, stream)
+
+
+def attn_fwd_mxfp4(q4, qs, k4, ks, vt4, vts, o, lse, B, Hq, Hkv, N, d, causal, scale):
+    return lib.attn_fwd_mxfp4(q4, qs, k4, ks, vt4, vts, o, lse, B, Hq, Hkv, N, d, causal, scale)
+
+
+def attn_quantize_mxfp4_rows(x, codes, scales, rows, cols, stream=None):
+    return lib.attn_quantize_mxfp4_rows(x, codes, scales, rows, cols, stream)
+
+
+def attn_quantize_mxfp4_cols_t(x, codes, scales, batch, rows, cols, stream=None):
+    return lib.attn_quantize_mxfp4_cols_t(x, codes, scales, batch, rows, cols, stream)
+
+
+# ---- torch-level wrappers: shape checks, output allocation, current stream ----
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(torch, device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def fwd(q, k, v, causal=False, scale=None, tau=8.0, exp_mode="hw", stats=None, out=None):
+    """bf16 attention forward on the GPU: returns (O fp32 [B,Hq,N,d], LSE fp32 [B,Hq,N])."""
+    torch = _torch()
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous bf16 CUDA tensors")
+    B, Hq, N, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError("k and v must be [B, Hkv, N, d] matching q")
+    Hkv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        o = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device)
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+    opts = make_opts(tau, exp_mode, stats.data_ptr() if stats is not None else None)
+    check(attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                      B, Hq, Hkv, N, d, int(bool(causal)), float(scale), opts,
+                      _stream(torch, q.device)))
+    return o, lse
+
+
+def quantize_mxfp4_rows(x):
+    """fp32 [..., cols] -> (codes uint8 [..., cols/2], scales uint8 [..., cols/32])."""
+    torch = _torch()
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous fp32 CUDA tensor")
+    cols = x.shape[-1]
+    rows = x.numel() // cols
+    codes = torch.empty(x.shape[:-1] + (cols // 2,), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(x.shape[:-1] + (cols // 32,), dtype=torch.uint8, device=x.device)
+    check(attn_quantize_mxfp4_rows(x.data_ptr(), codes.data_ptr(), scales.data_ptr(), rows, cols,
+                                   _stream(torch, x.device)))
+    return codes, scales
+
+
+def quantize_mxfp4_cols_t(x):
+    """fp32 [..., rows, cols] -> transposed (codes [..., cols, rows/2], scales [..., cols, rows/32])."""
+    torch = _torch()
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous fp32 CUDA tensor")
+    rows, cols = x.shape[-2], x.shape[-1]
+    batch = x.numel() // (rows * cols)
+    lead = x.shape[:-2]
+    codes = torch.empty(lead + (cols, rows // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(lead + (cols, rows // 32), dtype=torch.uint8, device=x.device)
+    check(attn_quantize_mxfp4_cols_t(x.data_ptr(), codes.data_ptr(), scales.data_ptr(), batch,
+                                     rows, cols, _stream(torch, x.device)))
+    return codes, scales
+
+
+def fwd_mxfp4(q4, qs, k4, ks, vt4, vts, causal=False, scale=None, tau=8.0, stats=None, out=None):
+    """MXFP4 Direct-P forward: returns (O fp32 [B,Hq,N,d], LSE fp32 [B,Hq,N])."""
+    torch = _torch()
+    B, Hq, N, half_d = q4.shape
+    d = 2 * half_d
+    Hkv = k4.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        o = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q4.device)
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q4.device)
+    else:
+        o, lse = out
+    for t in (q4, qs, k4, ks, vt4, vts):
+        if t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("codes and scales must be contiguous uint8 CUDA tensors")
+    opts = make_opts(tau, "hw", stats.data_ptr() if stats is not None else None)
+    check(attn_fwd_mxfp4_ex(q4.data_ptr(), qs.data_ptr(), k4.data_ptr(), ks.data_ptr(),
+                            vt4.data_ptr(), vts.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                            B, Hq, Hkv, N, d, int(bool(causal)), float(scale), opts,
+                            _stream(torch, q4.device)))
+    return o, lse

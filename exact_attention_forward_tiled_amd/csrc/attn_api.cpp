@@ -1,0 +1,149 @@
+// C-ABI entry points of libattn: argument validation, then one kernel launch
+// on the caller's stream.  Nothing here allocates or synchronises.
+
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "../../include/attn.h"
+#include "launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return ATTN_OK;
+  g_last_hip_error = (int)e;
+  return ATTN_EHIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_opts(const attn_opts* o) {
+  if (!(o->tau >= 0.f) || !isfinite(o->tau)) return ATTN_EINVAL;
+  if (o->exp_mode != ATTN_EXP_HW && o->exp_mode != ATTN_EXP_POLY) return ATTN_EINVAL;
+  return ATTN_OK;
+}
+
+int check_common(int B, int Hq, int Hkv, int N, int d, int causal, float scale) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || d < 1) return ATTN_EINVAL;
+  if (Hq % Hkv != 0) return ATTN_EINVAL;
+  if (causal != 0 && causal != 1) return ATTN_EINVAL;
+  if (!isfinite(scale)) return ATTN_EINVAL;
+  // every flat row index b*Hq*N + h*N + i must fit in 32 bits
+  if ((long long)B * Hq * N >= (1LL << 31)) return ATTN_EUNSUPPORTED;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void attn_default_opts(attn_opts* opts) {
+  if (opts == nullptr) return;
+  opts->tau = 8.0f;
+  opts->exp_mode = ATTN_EXP_HW;
+  opts->stats = nullptr;
+}
+
+const char* attn_strerror(int status) {
+  switch (status) {
+    case ATTN_OK: return "success";
+    case ATTN_EINVAL: return "invalid argument";
+    case ATTN_EUNSUPPORTED: return "unsupported shape or format";
+    case ATTN_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int attn_last_hip_error(void) { return g_last_hip_error; }
+
+int attn_fwd_ex(const void* q, const void* k, const void* v, float* o, float* lse, int B, int Hq,
+                int Hkv, int N, int d, int causal, float scale, const attn_opts* opts,
+                void* stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4))
+    return ATTN_EINVAL;
+  int st = check_common(B, Hq, Hkv, N, d, causal, scale);
+  if (st != ATTN_OK) return st;
+  attn_opts def;
+  attn_default_opts(&def);
+  const attn_opts* op = opts ? opts : &def;
+  st = check_opts(op);
+  if (st != ATTN_OK) return st;
+  if (d != 64 && d != 128) return ATTN_EUNSUPPORTED;
+
+  attn::FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N = N; a.d = d; a.causal = causal;
+  a.c = fabsf(scale) * 1.4426950408889634f;
+  a.tau = op->tau;
+  a.qsign = scale < 0.f ? 0x80008000u : 0u;
+  a.exp_mode = op->exp_mode;
+  a.stats = op->stats;
+  a.stream = stream;
+  return hip_status(attn::launch_fwd_bf16(a));
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse, int B, int Hq,
+             int Hkv, int N, int d, int causal, float scale) {
+  return attn_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, nullptr, nullptr);
+}
+
+int attn_fwd_mxfp4_ex(const uint8_t* q4, const uint8_t* qs, const uint8_t* k4, const uint8_t* ks,
+                      const uint8_t* vt4, const uint8_t* vts, float* o, float* lse, int B, int Hq,
+                      int Hkv, int N, int d, int causal, float scale, const attn_opts* opts,
+                      void* stream) {
+  if (!q4 || !qs || !k4 || !ks || !vt4 || !vts || !o || !lse) return ATTN_EINVAL;
+  if (!aligned(q4, 16) || !aligned(k4, 16) || !aligned(vt4, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4))
+    return ATTN_EINVAL;
+  int st = check_common(B, Hq, Hkv, N, d, causal, scale);
+  if (st != ATTN_OK) return st;
+  attn_opts def;
+  attn_default_opts(&def);
+  const attn_opts* op = opts ? opts : &def;
+  st = check_opts(op);
+  if (st != ATTN_OK) return st;
+  if (d != 128 || N % 32 != 0) return ATTN_EUNSUPPORTED;
+
+  attn::Mxfp4Args a;
+  a.q4 = q4; a.qs = qs; a.k4 = k4; a.ks = ks; a.vt4 = vt4; a.vts = vts;
+  a.o = o; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N = N; a.d = d; a.causal = causal;
+  a.c = scale * 1.4426950408889634f;
+  a.tau = op->tau;
+  a.stats = op->stats;
+  a.stream = stream;
+  hipError_t e = attn::launch_fwd_mxfp4(a);
+  if (e == hipErrorNotSupported) return ATTN_EUNSUPPORTED;
+  return hip_status(e);
+}
+
+int attn_fwd_mxfp4(const uint8_t* q4, const uint8_t* qs, const uint8_t* k4, const uint8_t* ks,
+                   const uint8_t* vt4, const uint8_t* vts, float* o, float* lse, int B, int Hq,
+                   int Hkv, int N, int d, int causal, float scale) {
+  return attn_fwd_mxfp4_ex(q4, qs, k4, ks, vt4, vts, o, lse, B, Hq, Hkv, N, d, causal, scale,
+                           nullptr, nullptr);
+}
+
+int attn_quantize_mxfp4_rows(const float* x, uint8_t* codes, uint8_t* scales, long long rows,
+                             int cols, void* stream) {
+  if (!x || !codes || !scales) return ATTN_EINVAL;
+  if (rows < 1 || cols < 32 || cols % 32 != 0) return ATTN_EINVAL;
+  if (!aligned(x, 16)) return ATTN_EINVAL;
+  return hip_status(attn::launch_quantize_rows(x, codes, scales, rows, cols, stream));
+}
+
+int attn_quantize_mxfp4_cols_t(const float* x, uint8_t* codes, uint8_t* scales, int batch,
+                               int rows, int cols, void* stream) {
+  if (!x || !codes || !scales) return ATTN_EINVAL;
+  if (batch < 1 || rows < 32 || rows % 32 != 0 || cols < 1) return ATTN_EINVAL;
+  if ((long long)batch * rows * cols >= (1LL << 40)) return ATTN_EUNSUPPORTED;
+  return hip_status(attn::launch_quantize_cols_t(x, codes, scales, batch, rows, cols, stream));
+}
+
+}  // extern "C"

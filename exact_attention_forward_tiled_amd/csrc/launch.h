@@ -1,0 +1,43 @@
+// Internal interface between the C-ABI entry points (attn_api.cpp) and the
+// kernel launchers.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* o;
+  float* lse;
+  int B, Hq, Hkv, N, d, causal;
+  float c;          // |scale| * log2(e): scores to log2 units
+  float tau;        // rescale threshold, log2 units
+  uint32_t qsign;   // 0x80008000 flips the sign of every bf16 Q element (scale < 0)
+  int exp_mode;     // 0 hardware, 1 cubic
+  unsigned long long* stats;
+  void* stream;
+};
+
+struct Mxfp4Args {
+  const uint8_t *q4, *qs, *k4, *ks, *vt4, *vts;
+  float* o;
+  float* lse;
+  int B, Hq, Hkv, N, d, causal;
+  float c;          // scale * log2(e), any sign
+  float tau;
+  unsigned long long* stats;
+  void* stream;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a);
+hipError_t launch_fwd_mxfp4(const Mxfp4Args& a);
+hipError_t launch_quantize_rows(const float* x, uint8_t* codes, uint8_t* scales, long long rows,
+                                int cols, void* stream);
+hipError_t launch_quantize_cols_t(const float* x, uint8_t* codes, uint8_t* scales, int batch,
+                                  int rows, int cols, void* stream);
+
+}  // namespace attn

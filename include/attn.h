@@ -1,0 +1,133 @@
+/*
+ * attn.h -- C ABI of libattn: fused, tiled, exact attention forward on gfx950.
+ *
+ * Operation.  For every batch b, query head hq and query row i:
+ *     s_ij   = scale * sum_c q[b,hq,i,c] * k[b,hk,j,c]        hk = hq / (Hq/Hkv)
+ *     s_ij   = -inf  when causal and j > i
+ *     O[i,:] = sum_j exp(s_ij - m_i) v[b,hk,j,:] / sum_j exp(s_ij - m_i),  m_i = max_j s_ij
+ *     LSE_i  = m_i + ln(sum_j exp(s_ij - m_i))                  (natural log)
+ * This is the FlashAttention forward: the N x N score matrix is never stored;
+ * K/V are streamed in tiles and the softmax is carried online
+ * ("FlashAttention-4发布：原生支持Blackwell…", section "从V1到V4", FlashAttention
+ * (2022) entry: tiling and recomputation keep memory O(N); FlashAttention-2
+ * entry: grouped-query attention).  The running row maximum is only moved,
+ * and the output only rescaled, when a tile's maximum exceeds it by more than
+ * a threshold tau ("FlashAttention-4 de NVIDIA: Un instrument…", section
+ * "La ventaja técnica", and the aigc.bar page, section "FlashAttention-4：为
+ * Blackwell而生的性能猛兽": rescaling only when the maximum changes enough);
+ * this is exact in exact arithmetic.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers, row-major and contiguous, owned
+ *    by the caller.  The library allocates no device memory, keeps no state
+ *    between calls (except a thread-local last HIP error) and never
+ *    synchronises: work is queued on the given stream (the null stream for the
+ *    short forms) and outputs are valid once that stream has completed it.
+ *  - Outputs must not alias inputs.
+ *  - Arguments are validated before anything is launched; on error nothing is
+ *    written.  Return codes are attn_status values; no C++ exception crosses
+ *    the ABI.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_status {
+    ATTN_OK = 0,
+    ATTN_EINVAL = -1,        /* null pointer, non-positive size, Hq % Hkv != 0, causal not 0/1,
+                                non-finite scale, bad option value */
+    ATTN_EUNSUPPORTED = -2,  /* valid request this build does not implement (e.g. d not 64/128) */
+    ATTN_EHIP = -3           /* a HIP runtime call or kernel launch failed; see attn_last_hip_error */
+} attn_status;
+
+/* Exponential used for the softmax weights. */
+enum attn_exp_mode {
+    ATTN_EXP_HW = 0,         /* hardware v_exp_f32 */
+    ATTN_EXP_POLY = 1        /* VALU cubic polynomial for 2^f on [0,1) plus exponent add
+                                ("FlashAttention-4 de NVIDIA…", section "La ventaja técnica":
+                                exponentials approximated by cubic polynomials on the FMA units) */
+};
+
+typedef struct attn_opts {
+    float tau;               /* rescale threshold in log2 units, >= 0 and finite; 0 rescales on
+                                every increase of the maximum (the textbook online softmax) */
+    int exp_mode;            /* attn_exp_mode */
+    unsigned long long* stats; /* nullable DEVICE pointer to 2 counters, accumulated atomically:
+                                [0] wave-tile steps after each wave's first tile,
+                                [1] rescale events among those steps.  Skip ratio = 1 - [1]/[0]. */
+} attn_opts;
+
+/* Default options: tau = 8, hardware exp, no stats. */
+void attn_default_opts(attn_opts* opts);
+
+/*
+ * bf16 forward.
+ *   q    bf16 [B, Hq,  N, d]      k, v  bf16 [B, Hkv, N, d]
+ *   o    fp32 [B, Hq,  N, d]      lse   fp32 [B, Hq, N]   (natural log)
+ *   d in {64, 128}; N >= 1 (any value; the tail tile is masked); causal in {0, 1}
+ *   (key j visible to query i iff j <= i); scale finite (any sign).
+ */
+int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
+             int B, int Hq, int Hkv, int N, int d, int causal, float scale);
+
+/* As attn_fwd, with options (nullable: defaults) and a hipStream_t (nullable: null stream). */
+int attn_fwd_ex(const void* q, const void* k, const void* v, float* o, float* lse,
+                int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                const attn_opts* opts, void* stream);
+
+/*
+ * MXFP4 forward with Direct-P ("Hardware-Aware FP4 FlashAttention-4", section
+ * "1. Direct-P para Inferencia Directa"): QK^T and PV run on the scaled FP4
+ * MFMA; the softmax weights are mapped straight to E2M1 codes with one
+ * power-of-two scale per 32 keys (relative to an integer running maximum), and
+ * the denominator is accumulated from those same codes and scales.
+ *   q4, k4   E2M1 codes [B, H*, N, d/2]  (two codes per byte: element 2i in the low nibble)
+ *   qs, ks   E8M0 scales [B, H*, N, d/32] (block of 32 along d)
+ *   vt4      E2M1 codes of V transposed [B, Hkv, d, N/2] (block of 32 along keys)
+ *   vts      E8M0 scales [B, Hkv, d, N/32]
+ *   o fp32 [B, Hq, N, d], lse fp32 [B, Hq, N]
+ *   d = 128; N a multiple of 32 (else ATTN_EUNSUPPORTED).
+ */
+int attn_fwd_mxfp4(const uint8_t* q4, const uint8_t* qs, const uint8_t* k4, const uint8_t* ks,
+                   const uint8_t* vt4, const uint8_t* vts, float* o, float* lse,
+                   int B, int Hq, int Hkv, int N, int d, int causal, float scale);
+
+int attn_fwd_mxfp4_ex(const uint8_t* q4, const uint8_t* qs, const uint8_t* k4, const uint8_t* ks,
+                      const uint8_t* vt4, const uint8_t* vts, float* o, float* lse,
+                      int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                      const attn_opts* opts, void* stream);
+
+/*
+ * MXFP4 quantisation of fp32 inputs (OCP MX v1.0 rule: shared exponent
+ * floor(log2(amax)) - 2 per block of 32, elements rounded to nearest E2M1
+ * magnitude with ties to even, saturating at 6; an all-zero block gets
+ * exponent 0; a value that rounds to 0 is stored as +0).
+ *
+ * attn_quantize_mxfp4_rows: x fp32 [rows, cols] -> codes [rows, cols/2], scales [rows, cols/32]
+ *   (blocks along the contiguous axis; used for Q and K with cols = d).
+ * attn_quantize_mxfp4_cols_t: x fp32 [batch, rows, cols] -> codes [batch, cols, rows/2],
+ *   scales [batch, cols, rows/32] (blocks along rows, output transposed; used for V with
+ *   rows = N keys, cols = d).
+ * cols (resp. rows) must be a positive multiple of 32.
+ */
+int attn_quantize_mxfp4_rows(const float* x, uint8_t* codes, uint8_t* scales,
+                             long long rows, int cols, void* stream);
+int attn_quantize_mxfp4_cols_t(const float* x, uint8_t* codes, uint8_t* scales,
+                               int batch, int rows, int cols, void* stream);
+
+/* Static description of a status code; never NULL. */
+const char* attn_strerror(int status);
+
+/* The hipError_t value behind the last ATTN_EHIP returned on this thread (0 if none). */
+int attn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

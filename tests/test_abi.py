@@ -1,0 +1,114 @@
+"""Host-side checks of the C ABI (no GPU needed: nothing here launches a kernel).
+
+* libattn.so loads and exports every function declared in include/attn.h;
+* argument validation returns the documented codes before any launch;
+* the cubic used by the VALU exp2 meets its error bound.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PKG = os.path.join(ROOT, "exact_attention_forward_tiled_amd")
+
+
+@pytest.fixture(scope="module")
+def fa():
+    if not os.path.exists(os.path.join(PKG, "libattn.so")):
+        from exact_attention_forward_tiled_amd.build import build
+        build()
+    import exact_attention_forward_tiled_amd as fa
+    return fa
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "attn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(fa):
+    names = _declared()
+    assert "attn_fwd" in names and "attn_fwd_mxfp4" in names
+    lib = ctypes.CDLL(os.path.join(PKG, "libattn.so"))
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(fa.EXPORTS)
+
+
+FAKE = 4096  # a 16-byte aligned non-null address; never dereferenced on these paths
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(q=0), -1),
+    (dict(o=0), -1),
+    (dict(q=FAKE + 8), -1),            # misaligned
+    (dict(B=0), -1),
+    (dict(N=0), -1),
+    (dict(Hq=6, Hkv=4), -1),
+    (dict(causal=2), -1),
+    (dict(scale=float("nan")), -1),
+    (dict(scale=float("inf")), -1),
+    (dict(d=96), -2),
+    (dict(d=256), -2),
+])
+def test_fwd_validation(fa, args, code):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, Hq=2, Hkv=1, N=16, d=64, causal=0,
+             scale=0.125)
+    a.update(args)
+    st = fa.attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["N"],
+                     a["d"], a["causal"], a["scale"])
+    assert st == code
+
+
+def test_opts_validation(fa):
+    for tau, mode in [(-1.0, "hw"), (float("nan"), "hw"), (8.0, 7)]:
+        opts = fa.make_opts(tau, mode)
+        st = fa.attn_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 16, 64, 0, 0.1, opts, None)
+        assert st == -1
+
+
+def test_mxfp4_validation(fa):
+    base = [FAKE] * 8
+    assert fa.attn_fwd_mxfp4(*base, 1, 2, 2, 64, 64, 0, 0.1) == -2      # d must be 128
+    assert fa.attn_fwd_mxfp4(*base, 1, 2, 2, 48, 128, 0, 0.1) == -2     # N % 32
+    assert fa.attn_fwd_mxfp4(0, *base[1:], 1, 2, 2, 64, 128, 0, 0.1) == -1
+    assert fa.attn_quantize_mxfp4_rows(FAKE, FAKE, FAKE, 4, 48) == -1
+    assert fa.attn_quantize_mxfp4_cols_t(FAKE, FAKE, FAKE, 1, 40, 8) == -1
+
+
+def test_strerror(fa):
+    from exact_attention_forward_tiled_amd.binding import lib
+    assert lib.attn_strerror(0) == b"success"
+    assert lib.attn_strerror(-2) == b"unsupported shape or format"
+    assert lib.attn_strerror(12345) == b"unknown status"
+    with pytest.raises(ValueError):
+        fa.check(-1)
+    with pytest.raises(NotImplementedError):
+        fa.check(-2)
+
+
+def _poly_coeffs():
+    text = open(os.path.join(PKG, "csrc", "exp2_poly.h")).read()
+    return [np.float32(float(re.search(rf"ATTN_EXP2_{n} ([-0-9.e+]+)f", text).group(1)))
+            for n in ("C1", "C2", "C3")]
+
+
+def test_exp2_cubic_error_bound():
+    """The committed cubic, evaluated in fp32 as the kernel does, stays within 1.2e-4 relative
+    error of 2^x over the whole range the kernel feeds it (x in [-126, 8])."""
+    c1, c2, c3 = _poly_coeffs()
+    x = np.concatenate([np.linspace(-126.0, 8.0, 2_000_003, dtype=np.float32),
+                        np.float32(np.arange(-126, 9)),
+                        np.nextafter(np.float32(np.arange(-125, 9)), np.float32(-200))])
+    n = np.floor(x)
+    f = (x - n).astype(np.float32)
+    p = (f * (f * (f * c3 + c2) + c1) + np.float32(1.0)).astype(np.float32)
+    bits = p.view(np.int32) + (n.astype(np.int32) << 23)
+    got = bits.view(np.float32).astype(np.float64)
+    rel = np.abs(got / np.exp2(x.astype(np.float64)) - 1.0)
+    assert rel.max() < 1.2e-4

@@ -1,0 +1,181 @@
+"""bf16 forward on the GPU (through the C ABI) against the float64 oracle.
+
+Tolerances: relative RMS of O <= 5e-3 and max |LSE error| <= 1e-3.  Small and
+ragged shapes are compared element by element on every output; the full-size
+workloads are compared on sampled query rows that the oracle computes one by
+one, in the same launch configuration the bench times.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth.configs import random_case
+from gpu_util import BF16_LSE_ABS, BF16_O_RELRMS, cuda_ok, log, rel_rms, to_dev_bf16
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not cuda_ok(), reason="needs a GPU")]
+
+
+def _run(qb, kb, vb, causal, scale, **kw):
+    import torch
+    import exact_attention_forward_tiled_amd as fa
+    q, k, v = to_dev_bf16(qb), to_dev_bf16(kb), to_dev_bf16(vb)
+    B, Hq, N, d = q.shape
+    # pre-fill outputs with NaN so a tile the kernel forgot to write shows up
+    o = torch.full((B, Hq, N, d), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((B, Hq, N), float("nan"), dtype=torch.float32, device="cuda")
+    fa.fwd(q, k, v, causal=causal, scale=scale, out=(o, lse), **kw)
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), lse.cpu().numpy()
+
+
+def _check(o, lse, ro, rl, what):
+    assert not np.isnan(o).any() and not np.isnan(lse).any(), f"{what}: unwritten outputs"
+    r = rel_rms(o, ro)
+    e = float(np.max(np.abs(lse - rl)))
+    log(f"  {what}: relRMS(O)={r:.3e} max|dLSE|={e:.3e}")
+    assert r <= BF16_O_RELRMS, (what, r)
+    assert e <= BF16_LSE_ABS, (what, e)
+
+
+SMALL = [
+    # B, Hq, Hkv, N, d, causal
+    (1, 2, 2, 256, 64, False),
+    (1, 2, 2, 256, 64, True),
+    (1, 1, 1, 1, 64, False),
+    (1, 1, 1, 1, 128, True),
+    (1, 3, 3, 65, 128, False),
+    (2, 4, 2, 129, 64, True),
+    (1, 2, 1, 200, 128, True),
+    (1, 2, 2, 333, 128, False),
+    (1, 8, 2, 512, 128, True),
+    (2, 2, 2, 127, 128, True),
+    (1, 4, 4, 1000, 128, True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "B%dHq%dHkv%dN%dd%d%s" % (
+    c[0], c[1], c[2], c[3], c[4], "c" if c[5] else "n"))
+@pytest.mark.parametrize("mode", [("hw", 8.0), ("hw", 0.0), ("poly", 8.0)],
+                         ids=lambda m: f"{m[0]}-tau{m[1]:g}")
+def test_small_shapes(case, mode):
+    B, Hq, Hkv, N, d, causal = case
+    qb, kb, vb = random_case(sum(case[:5]) + 7, B, Hq, Hkv, N, d, sigma=1.5)
+    scale = 1.0 / np.sqrt(d)
+    log(f"case {case} mode {mode}")
+    o, lse = _run(qb, kb, vb, causal, scale, exp_mode=mode[0], tau=mode[1])
+    ro, rl = oracle.attention(synth.bf16_bits_to_f64(qb), synth.bf16_bits_to_f64(kb),
+                              synth.bf16_bits_to_f64(vb), causal, scale)
+    _check(o, lse, ro, rl, f"{case} {mode}")
+
+
+def test_workload_1_full():
+    w = synth.workload(1)
+    qb, kb, vb = w.make()
+    log(f"workload {w.name}")
+    o, lse = _run(qb, kb, vb, w.causal, w.scale)
+    ro, rl = oracle.attention(synth.bf16_bits_to_f64(qb), synth.bf16_bits_to_f64(kb),
+                              synth.bf16_bits_to_f64(vb), w.causal, w.scale)
+    _check(o, lse, ro, rl, w.name)
+
+
+@pytest.mark.parametrize("idx", [2, 3, 4])
+def test_full_size_sampled_rows(idx):
+    """Full-size workloads: sampled rows of several heads against the oracle's row-wise definition."""
+    w = synth.workload(idx)
+    qb, kb, vb = w.make()
+    log(f"workload {w.name}")
+    o, lse = _run(qb, kb, vb, w.causal, w.scale)
+    q64, k64, v64 = (synth.bf16_bits_to_f64(x) for x in (qb, kb, vb))
+    rng = np.random.default_rng(idx)
+    heads = [(0, 0), (w.B - 1, w.Hq - 1), (rng.integers(w.B), rng.integers(w.Hq))]
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, w.N - 1],
+                                     rng.integers(0, w.N, 40)]))
+    got_o, got_l, ref_o, ref_l = [], [], [], []
+    for b, h in heads:
+        ro, rl = oracle.attention_rows(q64, k64, v64, w.causal, w.scale, int(b), int(h), rows)
+        got_o.append(o[b, h, rows]); got_l.append(lse[b, h, rows])
+        ref_o.append(ro); ref_l.append(rl)
+    _check(np.concatenate(got_o), np.concatenate(got_l), np.concatenate(ref_o),
+           np.concatenate(ref_l), w.name)
+    assert not np.isnan(o).any() and not np.isnan(lse).any()
+
+
+def test_constant_v_gives_one():
+    qb, kb, _ = random_case(31, 1, 4, 2, 300, 128, sigma=2.0)
+    vb = np.full((1, 2, 300, 128), 0x3F80, dtype=np.uint16)      # bf16 1.0
+    for causal in (False, True):
+        o, _ = _run(qb, kb, vb, causal, 0.09)
+        assert np.max(np.abs(o - 1.0)) < 4e-3
+
+
+def test_zero_query_prefix_mean():
+    _, kb, vb = random_case(32, 1, 2, 2, 257, 64)
+    qb = np.zeros((1, 2, 257, 64), dtype=np.uint16)
+    v64 = synth.bf16_bits_to_f64(vb)
+    for causal in (False, True):
+        o, lse = _run(qb, kb, vb, causal, 0.125)
+        if causal:
+            ref = np.cumsum(v64, axis=2) / np.arange(1, 258)[None, None, :, None]
+            ref_l = np.log(np.arange(1, 258))[None, None, :]
+        else:
+            ref = np.broadcast_to(v64.mean(axis=2, keepdims=True), v64.shape)
+            ref_l = np.full((1, 2, 257), np.log(257.0))
+        assert rel_rms(o, ref) < 5e-3
+        assert np.max(np.abs(lse - ref_l)) < 1e-4
+
+
+def test_causal_first_row_is_first_value():
+    qb, kb, vb = random_case(33, 1, 2, 2, 130, 128)
+    o, lse = _run(qb, kb, vb, True, 0.088)
+    v64 = synth.bf16_bits_to_f64(vb)
+    q64, k64 = synth.bf16_bits_to_f64(qb), synth.bf16_bits_to_f64(kb)
+    assert np.max(np.abs(o[:, :, 0] - v64[:, :, 0])) < 1e-6
+    s0 = 0.088 * np.einsum("bhd,bhd->bh", q64[:, :, 0], k64[:, :, 0])
+    assert np.max(np.abs(lse[:, :, 0] - s0)) < 1e-5
+
+
+def test_gqa_equals_repeated_heads_bitwise():
+    qb, kb, vb = random_case(34, 1, 8, 2, 200, 128)
+    for causal in (False, True):
+        o1, l1 = _run(qb, kb, vb, causal, 0.088)
+        o2, l2 = _run(qb, np.repeat(kb, 4, axis=1), np.repeat(vb, 4, axis=1), causal, 0.088)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_deterministic():
+    qb, kb, vb = random_case(35, 2, 4, 4, 700, 128, sigma=3.0)
+    runs = [_run(qb, kb, vb, True, 0.088) for _ in range(3)]
+    for o, l in runs[1:]:
+        assert np.array_equal(o, runs[0][0]) and np.array_equal(l, runs[0][1])
+
+
+def test_scale_sign_and_zero():
+    qb, kb, vb = random_case(36, 1, 2, 2, 150, 64)
+    q64, k64, v64 = (synth.bf16_bits_to_f64(x) for x in (qb, kb, vb))
+    for scale in (-0.125, 0.0, 0.5):
+        for causal in (False, True):
+            o, lse = _run(qb, kb, vb, causal, scale)
+            ro, rl = oracle.attention(q64, k64, v64, causal, scale)
+            _check(o, lse, ro, rl, f"scale={scale} causal={causal}")
+
+
+def test_skip_ratio_stats():
+    """The rescale counter: tau = 0 rescales on most steps, tau = 8 skips most of them."""
+    import torch
+    w = synth.workload(4)
+    qb, kb, vb = random_case(37, 1, 2, 2, 4096, 128, sigma=w.sigma_qk)
+    ratios = {}
+    for tau in (0.0, 8.0):
+        stats = torch.zeros(2, dtype=torch.int64, device="cuda")
+        import exact_attention_forward_tiled_amd as fa
+        fa.fwd(to_dev_bf16(qb), to_dev_bf16(kb), to_dev_bf16(vb), causal=False,
+               scale=w.scale, tau=tau, stats=stats)
+        torch.cuda.synchronize()
+        steps, resc = (int(x) for x in stats.cpu())
+        assert steps == 2 * (4096 // 32) * (4096 // 64 - 1)
+        ratios[tau] = 1.0 - resc / steps
+        log(f"  tau={tau}: steps={steps} rescales={resc} skip={ratios[tau]:.3f}")
+    assert ratios[8.0] > ratios[0.0]
