@@ -88,6 +88,81 @@ __global__ void rate_probe(float* out, int iters, float seed) {
   out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+
+// MFMA issue-rate probe: 4 independent 32x32x16 bf16 accumulation chains per wave.
+__global__ void mfma_rate_probe(float* out, int iters) {
+  const int l = threadIdx.x & 63;
+  u32x4 av = {(uint32_t)l, 1u, 2u, 3u}, bv = {3u, 2u, 1u, (uint32_t)l};
+  const bf16x8 a = as_bf16x8(av), b = as_bf16x8(bv);
+  f32x16 c0 = zero16(), c1 = zero16(), c2 = zero16(), c3 = zero16();
+  for (int it = 0; it < iters; ++it) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// LDS read-rate probe: 256 threads, each wave reads 16 B (mode 0, ds_read_b128) or
+// 8 B with the transposing read (mode 1) per lane per step from a 32 KiB buffer.
+template <int MODE>
+__global__ void lds_rate_probe(float* out, int iters) {
+  __shared__ __attribute__((aligned(16))) u32x4 buf[2048];
+  const int t = threadIdx.x, l = t & 63;
+  for (int i = t; i < 2048; i += blockDim.x) buf[i] = u32x4{(uint32_t)i, 1u, 2u, 3u};
+  __syncthreads();
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int idx = ((it * 8 + u) * 64 + l) & 2047;
+      if constexpr (MODE == 0) {
+        acc += buf[idx];
+      } else {
+        typedef short i16x4 __attribute__((ext_vector_type(4)));
+        i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)((uint16_t*)buf + idx * 4));
+        acc[0] += (uint32_t)r[0]; acc[1] += (uint32_t)r[1];
+        acc[2] += (uint32_t)r[2]; acc[3] += (uint32_t)r[3];
+      }
+    }
+  }
+  out[blockIdx.x * blockDim.x + t] = (float)(acc[0] + acc[1] + acc[2] + acc[3]);
+}
+
+// Direct-to-LDS load probe: one wave; lane l fetches the 16 bytes at global
+// element 4*(63 - l) (u32 values = element index) with global_load_lds_dwordx4
+// into a 1 KiB LDS block; the block is then copied out linearly.
+// src: 256 u32; out: 256 u32.
+__global__ void lds_dma_probe(const uint32_t* src, uint32_t* out) {
+  __shared__ __attribute__((aligned(16))) uint32_t lds[256];
+  const int l = threadIdx.x;
+  for (int i = l; i < 256; i += 64) lds[i] = 0xFFFFFFFFu;
+  __syncthreads();
+  __builtin_amdgcn_global_load_lds((const void*)(src + 4 * (63 - l)),
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int i = l; i < 256; i += 64) out[i] = lds[i];
+}
+
+// Rounding probe: lane i converts x[2i], x[2i+1] with the packed bf16 convert
+// and accumulates their dot product with (1, 1) onto acc[i].
+// x: 128 floats; acc: 64 floats; out: 64 x (u32 packed pair, f32 dot result).
+__global__ void cvt_dot_probe(const float* x, const float* acc, uint32_t* out) {
+  const int l = threadIdx.x;
+  const uint32_t pk = pack_bf16x2(x[2 * l], x[2 * l + 1]);
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  const float d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), one, acc[l], false);
+  out[2 * l] = pk;
+  out[2 * l + 1] = __float_as_uint(d);
+}
+
 }  // namespace
 
 extern "C" {
@@ -126,6 +201,35 @@ int probe_rate(float* out, int blocks, int iters, int mode, void* stream) {
     hipLaunchKernelGGL(rate_probe<1>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters, 1.0f);
   else
     hipLaunchKernelGGL(rate_probe<2>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters, 1.0f);
+  return (int)hipGetLastError();
+}
+
+// out must hold blocks * 256 floats.
+int probe_mfma_rate(float* out, int blocks, int iters, void* stream) {
+  if (blocks < 1 || iters < 1) return -1;
+  hipLaunchKernelGGL(mfma_rate_probe, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters);
+  return (int)hipGetLastError();
+}
+
+// out must hold blocks * 256 floats.
+int probe_lds_rate(float* out, int blocks, int iters, int mode, void* stream) {
+  if (blocks < 1 || iters < 1) return -1;
+  if (mode == 0)
+    hipLaunchKernelGGL(lds_rate_probe<0>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters);
+  else
+    hipLaunchKernelGGL(lds_rate_probe<1>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters);
+  return (int)hipGetLastError();
+}
+
+int probe_lds_dma(const void* src, void* out, void* stream) {
+  hipLaunchKernelGGL(lds_dma_probe, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                     (const uint32_t*)src, (uint32_t*)out);
+  return (int)hipGetLastError();
+}
+
+int probe_cvt_dot(const void* x, const void* acc, void* out, void* stream) {
+  hipLaunchKernelGGL(cvt_dot_probe, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                     (const float*)x, (const float*)acc, (uint32_t*)out);
   return (int)hipGetLastError();
 }
 
