@@ -1,12 +1,22 @@
 // bf16 fused attention forward for gfx950 (CDNA4).
 //
 // Work split.  One workgroup = 8 waves = 256 query rows of one (batch, query
-// head); each wave owns 32 query rows, so every SIMD runs two waves and the
-// hardware interleaves one wave's softmax (VALU) with the other's matrix
-// products (MFMA).  K/V are streamed through LDS in tiles of 128 keys, double
-// buffered: while tile j is computed, tile j+1 is already in flight, so the
-// N x N score matrix never leaves registers ("FlashAttention-4发布：原生支持
-// Blackwell…", section "从V1到V4", FlashAttention (2022) entry).
+// head); each wave owns 32 query rows.  K/V are streamed through LDS in tiles
+// of 64 keys, so the N x N score matrix never leaves registers
+// ("FlashAttention-4发布：原生支持Blackwell…", section "从V1到V4",
+// FlashAttention (2022) entry).
+//
+// Ping-pong.  Waves 0-3 (group A) and 4-7 (group B) put one wave of each group
+// on every SIMD.  Each wave alternates two phases per key tile:
+//   VALU phase:  online softmax of the scores it holds (max, exp2, bf16 pack)
+//   MFMA phase:  O^T += V^T P^T for this tile, then S^T = K Q^T for the next
+// Group B runs one phase behind group A, and the workgroup barrier between
+// phases keeps it there, so on every SIMD one wave's exponentials overlap the
+// other wave's matrix products.  This is the CDNA form of overlapping the
+// softmax stage with the tensor-core stage ("FlashAttention-4 de NVIDIA…",
+// section "La ventaja técnica"; "Hardware-Aware FP4 FlashAttention-4",
+// section "1. Direct-P…", two query tiles sharing K/V so that one tile's
+// softmax overlaps the other's MMA).
 //
 // Products.  Both run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation:
 //   S^T  = K Q^T     A = K tile from LDS (rows permuted, see perm_row), B = Q in VGPRs
@@ -19,11 +29,13 @@
 // B-operand layout of the PV product, so P goes from S to the next MFMA with
 // no data movement.
 //
-// Staging.  K goes global -> LDS with direct 16-byte loads (no VGPRs), in an
-// XOR-swizzled layout that makes the MFMA operand reads bank-conflict free.
-// V is read with coalesced 4-byte loads, transposed in registers and written
-// as V^T (the PV A operand needs 8 consecutive keys of one column per lane),
-// again swizzled so both the writes and the reads are conflict free.
+// Staging.  K/V tiles are fetched from HBM/L2 into registers with coalesced
+// buffer loads two phases before they are needed, then written to LDS.  K is
+// stored row-major with the 16-byte chunks of each row XOR-permuted so that
+// both the writes and the MFMA operand reads are bank-conflict free; V is
+// transposed in registers and stored as V^T (the PV A operand needs 8
+// consecutive keys of one column per lane).  Rows past N read as zeros
+// through the buffer descriptor's range check and are masked.
 //
 // Softmax.  Online, in log2 units, with a rescale threshold
 // ("FlashAttention-4 de NVIDIA…", section "La ventaja técnica"; aigc.bar page,
@@ -48,23 +60,22 @@ namespace {
 constexpr int kWaves = 8;
 constexpr int kRowsPerWave = 32;
 constexpr int kBr = kWaves * kRowsPerWave;  // 256 query rows per workgroup
-constexpr int kBc = 128;                    // keys per K/V tile in LDS
-constexpr int kSub = 64;                    // keys per compute step (online-softmax update)
+constexpr int kBc = 64;                     // keys per K/V tile (one online-softmax step)
 constexpr int kThreads = kWaves * 64;
 
 template <int D>
 struct Geo {
-  static constexpr int NCH = D / 8;                        // 16-byte chunks per K row
-  static constexpr int KCH = kBc * NCH;                    // 16-byte chunks per K tile
-  static constexpr int KDMA_PER_WAVE = KCH / 64 / kWaves;  // 1 KiB direct loads per wave
-  static constexpr int VKC = kBc / 8;                      // 8-key chunks per tile
-  static constexpr int VCH = D * VKC;                      // 16-byte chunks per V^T tile
+  static constexpr int NCH = D / 8;                        // 16-byte chunks per row
+  static constexpr int KUNITS = kBc * NCH;                 // 16-byte units per K tile
+  static constexpr int K_PER_THREAD = KUNITS / kThreads;   // K units staged per thread
+  static constexpr int VUNITS = D * (kBc / 8);             // 16-byte units per V^T tile
   static constexpr int CP = D / 2;                         // column pairs of a V row
-  static constexpr int KG_STRIDE = kThreads / CP;          // key groups covered per pass
-  static constexpr int KG_PER_THREAD = (kBc / 8) / KG_STRIDE;
-  static_assert(KCH % (64 * kWaves) == 0, "K tile must split into whole direct loads");
-  static_assert(kBc % 64 == 0, "a direct load covers 64 rows of one chunk column");
-  static_assert(KG_PER_THREAD >= 1 && (kBc / 8) % KG_STRIDE == 0, "V staging split");
+  static constexpr int V_THREADS = CP * (kBc / 8);         // threads that stage V
+  static constexpr int SW_SHIFT = (NCH == 16) ? 0 : 1;     // chunk swizzle granularity
+  static constexpr int ROW_BYTES = D * 2;
+  static_assert(KUNITS % kThreads == 0, "K tile must split evenly over the workgroup");
+  static_assert(V_THREADS <= kThreads, "V tile staging needs at most one thread per pair");
+  static_assert(NCH == 8 || NCH == 16, "d = 64 or 128");
 };
 
 // Raw buffer descriptor over `bytes` bytes at `base`: loads past the end return 0.
@@ -104,114 +115,158 @@ __device__ __forceinline__ float half_swap_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// LDS layouts (16-byte units):
-//   K tile   sk[c * kBc + r]   c = 16-byte chunk of the d axis, r = key row
-//   V^T tile svt[kc * D + col] kc = group of 8 keys, col = d column
-// In both, the 16 lanes that the LDS serves together read 16 consecutive units
-// (bank-conflict free), and an operand's address is one per-lane base plus a
-// compile-time offset.
-
-// K tile -> LDS with direct 16-byte loads: each load fills one chunk column for
-// 64 consecutive rows.  Rows past N come back as zeros (their scores are masked).
-template <int D>
-__device__ __forceinline__ void issue_k_tile(u32x4* sk, __amdgpu_buffer_rsrc_t rk, const int* koff,
-                                             int wave) {
-  using G = Geo<D>;
-#pragma unroll
-  for (int i = 0; i < G::KDMA_PER_WAVE; ++i) {
-    const int g0 = (wave * G::KDMA_PER_WAVE + i) * 64;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rk, (__attribute__((address_space(3))) void*)(sk + g0), 16, koff[i], 0, 0, 0);
-  }
+// Workgroup barrier for LDS hand-over only: this wave's LDS writes are
+// complete before it arrives; outstanding global loads stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Per-lane byte offsets (within a K tile) of this wave's direct loads.
-template <int D>
-__device__ __forceinline__ void k_offsets(int* koff, int wave, int lane) {
-  using G = Geo<D>;
-#pragma unroll
-  for (int i = 0; i < G::KDMA_PER_WAVE; ++i) {
-    const int g0 = (wave * G::KDMA_PER_WAVE + i) * 64;
-    const int c = g0 / kBc, r = g0 % kBc + lane;
-    koff[i] = r * D * 2 + c * 16;
-  }
-}
+// ---- LDS layouts (16-byte units) ----
+//   K tile   unit(row, c) = row * NCH + (c ^ sw(row)),  sw(row) = perm_row(row & 15) >> SW_SHIFT
+//   V^T tile unit(kc, col) = kc * D + col              kc = group of 8 keys, col = d column
+// In both, the 16 lanes that the LDS serves together touch 16 distinct bank
+// groups for every MFMA operand read and every staging write.
 
 template <int D>
-struct VRegs {
-  uint32_t w[Geo<D>::KG_PER_THREAD][8];
+struct Stage {
+  u32x4 k[Geo<D>::K_PER_THREAD];   // K rows, 16-byte chunks, in global order
+  uint32_t v[8];                   // V: one column pair for 8 consecutive keys
 };
 
-// V tile: thread (cp, kg) reads columns 2cp, 2cp+1 of keys 8kg .. 8kg+7 (each load
-// instruction covers whole rows: coalesced).  Rows past N come back as zeros.
 template <int D>
-__device__ __forceinline__ void load_v_tile(VRegs<D>& r, __amdgpu_buffer_rsrc_t rv, int voff) {
+__device__ __forceinline__ void load_k(Stage<D>& s, __amdgpu_buffer_rsrc_t rk, int tid) {
   using G = Geo<D>;
 #pragma unroll
-  for (int kk = 0; kk < G::KG_PER_THREAD; ++kk)
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      r.w[kk][e] = __builtin_amdgcn_raw_buffer_load_b32(
-          rv, voff + (8 * kk * G::KG_STRIDE + e) * D * 2, 0, 0);
+  for (int i = 0; i < G::K_PER_THREAD; ++i) {
+    const int g = tid + i * kThreads;
+    s.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, (g / G::NCH) * G::ROW_BYTES + (g % G::NCH) * 16,
+                                                   0, 0);
+  }
 }
 
 template <int D>
-__device__ __forceinline__ void store_v_tile(const VRegs<D>& r, u32x4* svt, int tid) {
+__device__ __forceinline__ void load_v(Stage<D>& s, __amdgpu_buffer_rsrc_t rv, int tid) {
   using G = Geo<D>;
-  const int cp = tid % G::CP, kgb = tid / G::CP;
+  if (G::V_THREADS == kThreads || tid < G::V_THREADS) {
+    const int cp = tid % G::CP, kg = tid / G::CP;
+    const int base = (8 * kg * D + 2 * cp) * 2;
 #pragma unroll
-  for (int kk = 0; kk < G::KG_PER_THREAD; ++kk) {
-    const int kg = kgb + kk * G::KG_STRIDE;
+    for (int e = 0; e < 8; ++e)
+      s.v[e] = __builtin_amdgcn_raw_buffer_load_b32(rv, base + e * G::ROW_BYTES, 0, 0);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_k(const Stage<D>& s, u32x4* sk, int tid) {
+  using G = Geo<D>;
+#pragma unroll
+  for (int i = 0; i < G::K_PER_THREAD; ++i) {
+    const int g = tid + i * kThreads;
+    const int row = g / G::NCH, c = g % G::NCH;
+    sk[row * G::NCH + (c ^ (perm_row(row & 15) >> G::SW_SHIFT))] = s.k[i];
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_v(const Stage<D>& s, u32x4* sv, int tid) {
+  using G = Geo<D>;
+  if (G::V_THREADS == kThreads || tid < G::V_THREADS) {
+    const int cp = tid % G::CP, kg = tid / G::CP;
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
       u32x4 out;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const uint32_t a = r.w[kk][2 * p], b = r.w[kk][2 * p + 1];
-        out[p] = cc ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+        const uint32_t a = s.v[2 * p], b = s.v[2 * p + 1];
+        out[p] = cc ? __builtin_amdgcn_perm(b, a, 0x07060302u)
+                    : __builtin_amdgcn_perm(b, a, 0x05040100u);
       }
-      svt[kg * D + 2 * cp + cc] = out;
+      sv[kg * D + 2 * cp + cc] = out;
     }
   }
 }
 
-struct RowState {
-  float m;       // running max, log2 units (-inf before the first visible key)
-  float l;       // this lane's partial row sum (keys of its half of each block)
-  unsigned steps, rescales;
-  bool first;
-};
+// ---- MFMA phase ----
+//
+// One phase issues up to 32 MFMAs: first O^T += V^T P^T for the current tile
+// (D/32 accumulator blocks x 4 key steps of 16), then S^T = K Q^T for the next
+// tile (2 key blocks of 32 x D/16 steps).  Every MFMA takes its A operand from
+// LDS; the operands are read into a ring of registers kDepth MFMAs ahead of
+// their use, and the issue order is pinned to "one MFMA, one LDS read", so the
+// LDS latency hides behind the MFMAs already in the pipe.
 
-// One 64-key step (keys kv0 .. kv0+63, at key offset `sub` of the LDS tile) for
-// this wave's 32 query rows.
-template <int D, bool CAUSAL, bool POLY, bool MASK>
-__device__ __forceinline__ void tile_step(const u32x4* __restrict__ kb,
-                                          const u32x4* __restrict__ vb,
-                                          const bf16x8 (&qf)[D / 16], f32x16 (&acc)[D / 32],
-                                          RowState& st, int sub, int kv0, int qi, int N, float c,
-                                          float tau, int n32, int h) {
+constexpr int kDepth = 6;
+
+template <int D, bool PV, bool QK>
+__device__ __forceinline__ void mfma_phase(const u32x4* sv, const u32x4* sk, const bf16x8 (&p)[4],
+                                           f32x16 (&acc)[D / 32], const bf16x8 (&qf)[D / 16],
+                                           f32x16 (&s)[2], uint32_t vaddr, uint32_t kaddr) {
   using G = Geo<D>;
-  constexpr int MB = kSub / 32;  // 32-key blocks per step
-  const float NEG_INF = -__builtin_inff();
+  constexpr int NPV = PV ? 4 * (D / 32) : 0;
+  constexpr int NQK = QK ? 2 * (D / 16) : 0;
+  constexpr int NOPS = NPV + NQK;
+  const char* vb = (const char*)sv;
+  const char* kb = (const char*)sk;
 
-  // ---- S^T = K Q^T ----
-  f32x16 s[MB];
+  // operand i: PV (ks = i / (D/32), cb = i % (D/32)), then QK (t = k / 2, mb = k % 2)
+  auto load = [&](int i) -> u32x4 {
+    if (i < NPV) {
+      const int ks = i / (D / 32), cb = i % (D / 32);
+      return *(const u32x4*)(vb + vaddr + 16 * (2 * ks * D + 32 * cb));
+    }
+    const int k = i - NPV, t = k / 2, mb = k % 2;
+    return *(const u32x4*)(kb + (kaddr ^ (32u * t)) + mb * 32 * G::NCH * 16);
+  };
+
+  u32x4 ring[kDepth];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) s[mb] = zero16();
+  for (int i = 0; i < kDepth; ++i)
+    if (i < NOPS) ring[i] = load(i);
+  if constexpr (QK) {
+    s[0] = zero16();
+    s[1] = zero16();
+  }
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) {
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int row = sub + mb * 32 + perm_row(n32);
-      const bf16x8 a = as_bf16x8(kb[(2 * t + h) * kBc + row]);
+  for (int i = 0; i < NOPS; ++i) {
+    const bf16x8 a = as_bf16x8(ring[i % kDepth]);
+    if (i + kDepth < NOPS) ring[i % kDepth] = load(i + kDepth);
+    if (i < NPV) {
+      const int ks = i / (D / 32), cb = i % (D / 32);
+      acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[ks], acc[cb], 0, 0, 0);
+    } else {
+      const int k = i - NPV, t = k / 2, mb = k % 2;
       s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[mb], 0, 0, 0);
     }
   }
-  // register r of block mb holds key kv0 + 32*mb + 16*(r/8) + 8*h + r%8
+  // S^T register r of block mb now holds key 32*mb + 16*(r/8) + 8*h + r%8
 
+  // issue order: the first reads, then alternate one MFMA with one read
+  __builtin_amdgcn_sched_group_barrier(0x100, NOPS < kDepth ? NOPS : kDepth, 0);
+#pragma unroll
+  for (int i = 0; i < NOPS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i + kDepth < NOPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+}
+
+// ---- VALU phase: online softmax of one tile ----
+
+struct RowState {
+  float m;       // running max, log2 units (-inf before the first visible key)
+  float l;       // this lane's partial row sum (its half of each 32-key block)
+  unsigned steps, rescales;
+  bool first;
+  bool rescale;  // wave-uniform: O must be multiplied by alpha before the next PV product
+  float alpha;
+};
+
+template <int D, bool CAUSAL, bool POLY, bool MASK>
+__device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], bf16x8 (&p)[4], RowState& st, int kv0,
+                                             int qi, int N, float c, float tau, int h) {
+  const float NEG_INF = -__builtin_inff();
   if constexpr (MASK) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kv0 + 32 * mb + 16 * (r >> 3) + 8 * h + (r & 7);
@@ -222,30 +277,28 @@ __device__ __forceinline__ void tile_step(const u32x4* __restrict__ kb,
 
   float mx = NEG_INF;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+  for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
   mx = half_swap_max(mx);
   const float mt = (mx == NEG_INF) ? NEG_INF : mx * c;
 
   if (!st.first) ++st.steps;
+  st.rescale = false;
   if (__ballot(mt > st.m + tau)) {
     const float m_new = fmaxf(st.m, mt);
-    const float alpha = (m_new == NEG_INF) ? 1.f : exp2_sel<POLY>(st.m - m_new);
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
-    st.l *= alpha;
+    st.alpha = (m_new == NEG_INF) ? 1.f : exp2_sel<POLY>(st.m - m_new);
+    st.l *= st.alpha;
     st.m = m_new;
+    st.rescale = true;
     if (!st.first) ++st.rescales;
   }
   st.first = false;
   const float mu = (st.m == NEG_INF) ? 0.f : st.m;
 
-  // ---- P = 2^(t - m), packed as the bf16 B operand (one 16-key step per 8 registers) ----
-  bf16x8 p[kSub / 16];
   float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+  for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       u32x4 pk;
@@ -264,18 +317,16 @@ __device__ __forceinline__ void tile_step(const u32x4* __restrict__ kb,
       p[mb * 2 + hf] = as_bf16x8(pk);
     }
   st.l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+}
 
-  // ---- O^T += V^T P^T ----
-#pragma unroll
-  for (int ks = 0; ks < kSub / 16; ++ks) {
-#pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb) {
-      const int col = cb * 32 + n32;
-      const int kc = sub / 8 + 2 * ks + h;
-      const bf16x8 a = as_bf16x8(vb[kc * D + col]);
-      acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[ks], acc[cb], 0, 0, 0);
-    }
-  }
+template <int D, bool CAUSAL, bool POLY>
+__device__ __forceinline__ void softmax_any(bool masked, f32x16 (&s)[2], bf16x8 (&p)[4],
+                                            RowState& st, int kv0, int qi, int N, float c,
+                                            float tau, int h) {
+  if (masked)
+    softmax_tile<D, CAUSAL, POLY, true>(s, p, st, kv0, qi, N, c, tau, h);
+  else
+    softmax_tile<D, CAUSAL, POLY, false>(s, p, st, kv0, qi, N, c, tau, h);
 }
 
 template <int D, bool CAUSAL, bool POLY>
@@ -285,11 +336,12 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                      int Hq, int Hkv, int N, int nqb, float c, float tau, uint32_t qsign,
                      unsigned long long* __restrict__ stats) {
   using G = Geo<D>;
-  __shared__ u32x4 sk[2][G::KCH];
-  __shared__ u32x4 svt[2][G::VCH];
+  __shared__ u32x4 sk[2][G::KUNITS];
+  __shared__ u32x4 sv[2][G::VUNITS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n32 = lane & 31, h = lane >> 5;
+  const bool lead = wave < kWaves / 2;   // group A leads, group B trails by one phase
 
   // Workgroup -> (batch, kv head, query block, query head in the group).  Workgroups
   // are dealt round-robin to the 8 XCDs; renumber so each XCD gets a contiguous
@@ -328,54 +380,85 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   f32x16 acc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = zero16();
-  RowState st{-__builtin_inff(), 0.f, 0u, 0u, true};
+  RowState st{-__builtin_inff(), 0.f, 0u, 0u, true, false, 1.f};
 
+  // Tiles of 64 keys this workgroup visits, and which of them touch this wave's rows.
   const int kv_end = CAUSAL ? min(N, Q0 + kBr) : N;
-  const int ntiles = (kv_end + kBc - 1) / kBc;
-
-  // Per-tile buffer descriptors: rows at or past N read as zeros.
-  auto tile_rsrc = [&](const uint16_t* head, int kv0) {
-    return make_rsrc(head + (size_t)kv0 * D, (N - kv0) * D * 2);
-  };
-  int koff[G::KDMA_PER_WAVE];
-  k_offsets<D>(koff, wave, lane);
-  const int voff = ((8 * (tid / G::CP)) * D + 2 * (tid % G::CP)) * 2;
-
-  VRegs<D> vr;
-  issue_k_tile<D>(sk[0], tile_rsrc(Kh, 0), koff, wave);
-  load_v_tile<D>(vr, tile_rsrc(Vh, 0), voff);
-  store_v_tile<D>(vr, svt[0], tid);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  for (int j = 0; j < ntiles; ++j) {
+  const int n = (kv_end + kBc - 1) / kBc;
+  const int wave_end = CAUSAL ? min(N, q0 + kRowsPerWave) : N;   // keys this wave can see
+  const bool wave_live = q0 < N;
+  auto active = [&](int j) { return wave_live && j * kBc < wave_end; };
+  auto masked = [&](int j) {
     const int kv0 = j * kBc;
-    const int nb = (j + 1) & 1;
-    const bool more = j + 1 < ntiles;
-    if (more) {
-      issue_k_tile<D>(sk[nb], tile_rsrc(Kh, kv0 + kBc), koff, wave);
-      load_v_tile<D>(vr, tile_rsrc(Vh, kv0 + kBc), voff);
-    }
+    return (CAUSAL && kv0 + kBc - 1 > q0) || (kv0 + kBc > N);
+  };
 
-#pragma unroll
-    for (int sub = 0; sub < kBc; sub += kSub) {
-      const int ks0 = kv0 + sub;
-      const bool active = (!CAUSAL || ks0 <= q0 + kRowsPerWave - 1) && q0 < N && ks0 < N;
-      if (active) {
-        const bool masked = (CAUSAL && ks0 + kSub - 1 > q0) || (ks0 + kSub > N);
-        if (masked)
-          tile_step<D, CAUSAL, POLY, true>(sk[j & 1], svt[j & 1], qf, acc, st, sub, ks0, qi, N,
-                                           c, tau, n32, h);
-        else
-          tile_step<D, CAUSAL, POLY, false>(sk[j & 1], svt[j & 1], qf, acc, st, sub, ks0, qi, N,
-                                            c, tau, n32, h);
-      }
-    }
+  auto tile_rsrc = [&](const uint16_t* head, int kv0) {
+    return make_rsrc(head + (size_t)kv0 * D, (N - kv0) * G::ROW_BYTES);
+  };
+  // Stage t of the pipeline holds K tile t+1 and V tile t.
+  auto load_stage = [&](Stage<D>& s, int t) {
+    if (t + 1 < n) load_k<D>(s, tile_rsrc(Kh, (t + 1) * kBc), tid);
+    load_v<D>(s, tile_rsrc(Vh, t * kBc), tid);
+  };
+  auto store_stage = [&](const Stage<D>& s, int t) {
+    if (t + 1 < n) store_k<D>(s, sk[t & 1], tid);
+    store_v<D>(s, sv[t & 1], tid);
+  };
 
-    if (more) store_v_tile<D>(vr, svt[nb], tid);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+  // Per-lane operand addresses (bytes within a tile).
+  const uint32_t kaddr = (uint32_t)(perm_row(n32) * G::NCH * 16) ^
+                         (uint32_t)(16 * (h ^ ((n32 & 15) >> G::SW_SHIFT)));
+  const uint32_t vaddr = (uint32_t)(16 * (h * D + n32));
+
+  // ---- prologue: K tile 0 -> sk[1], stage 0 -> buffer 0, stage 1 in registers ----
+  Stage<D> stg;
+  {
+    Stage<D> s0;
+    load_k<D>(s0, tile_rsrc(Kh, 0), tid);
+    load_stage(stg, 0);
+    store_k<D>(s0, sk[1], tid);
+    store_stage(stg, 0);
   }
+  if (n > 1) load_stage(stg, 1);
+  lds_barrier();
+  if (!lead) lds_barrier();
+
+  f32x16 s[2];
+  bf16x8 p[4];
+  if (active(0)) mfma_phase<D, false, true>(sv[0], sk[1], p, acc, qf, s, vaddr, kaddr);
+  lds_barrier();
+
+  for (int j = 0; j < n; ++j) {
+    // VALU phase: softmax of tile j.  A wave whose rows see no key of the tile
+    // (causal, past its diagonal) contributes P = 0 to the shared MFMA code.
+    if (active(j)) {
+      softmax_any<D, CAUSAL, POLY>(masked(j), s, p, st, j * kBc, qi, N, c, tau, h);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+      st.rescale = false;
+    }
+    lds_barrier();
+
+    // MFMA phase: stage j+1 to LDS, prefetch stage j+2, PV of tile j, QK of tile j+1
+    // (in the last iteration the QK half reads a stale buffer and its result is unused).
+    if (j + 1 < n) {
+      store_stage(stg, j + 1);
+      if (j + 2 < n) load_stage(stg, j + 2);
+    }
+    const u32x4* svj = sv[j & 1];
+    const u32x4* skj = sk[j & 1];
+    if (st.rescale) {
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) acc[i] *= st.alpha;
+      mfma_phase<D, true, true>(svj, skj, p, acc, qf, s, vaddr, kaddr);
+    } else {
+      mfma_phase<D, true, true>(svj, skj, p, acc, qf, s, vaddr, kaddr);
+    }
+    lds_barrier();
+  }
+  if (lead) lds_barrier();
 
   // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l) ----
   const float ltot = half_swap_sum(st.l);
@@ -394,7 +477,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       LSE[(size_t)(b * Hq + hq) * N + qi] =
           ltot > 0.f ? (st.m + __builtin_log2f(ltot)) * kLn2 : -__builtin_inff();
   }
-  if (stats != nullptr && lane == 0 && q0 < N) {
+  if (stats != nullptr && lane == 0 && wave_live) {
     atomicAdd(stats, (unsigned long long)st.steps);
     atomicAdd(stats + 1, (unsigned long long)st.rescales);
   }
