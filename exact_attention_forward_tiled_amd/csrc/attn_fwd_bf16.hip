@@ -6,17 +6,17 @@
 // ("FlashAttention-4发布：原生支持Blackwell…", section "从V1到V4",
 // FlashAttention (2022) entry).
 //
-// Ping-pong.  Waves 0-3 (group A) and 4-7 (group B) put one wave of each group
-// on every SIMD.  Each wave alternates two phases per key tile:
-//   VALU phase:  online softmax of the scores it holds (max, exp2, bf16 pack)
-//   MFMA phase:  O^T += V^T P^T for this tile, then S^T = K Q^T for the next
-// Group B runs one phase behind group A, and the workgroup barrier between
-// phases keeps it there, so on every SIMD one wave's exponentials overlap the
-// other wave's matrix products.  This is the CDNA form of overlapping the
+// Software pipeline.  Each wave works through the key tiles with three
+// tiles in flight: while its VALU computes the online softmax of tile j, the
+// matrix unit runs O^T += V^T P^T for tile j-1 and S^T = K Q^T for tile j+1.
+// The three streams are independent, so they are issued as one interleaved
+// instruction sequence ("one MFMA, one LDS operand read, a few VALU
+// instructions").  Both waves of a SIMD do this, so two waves feed the VALU
+// while the matrix unit stays busy.  This is the CDNA form of overlapping the
 // softmax stage with the tensor-core stage ("FlashAttention-4 de NVIDIA…",
-// section "La ventaja técnica"; "Hardware-Aware FP4 FlashAttention-4",
-// section "1. Direct-P…", two query tiles sharing K/V so that one tile's
-// softmax overlaps the other's MMA).
+// section "La ventaja técnica", the pipeline of load / MMA / softmax / correction
+// roles; "Hardware-Aware FP4 FlashAttention-4", section "1. Direct-P…", keeping
+// the exponential work off the critical path between the two matrix products).
 //
 // Products.  Both run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation:
 //   S^T  = K Q^T     A = K tile from LDS (rows permuted, see perm_row), B = Q in VGPRs
@@ -186,84 +186,104 @@ __device__ __forceinline__ void store_v(const Stage<D>& s, u32x4* sv, int tid) {
   }
 }
 
-// ---- MFMA phase ----
+// ---- one pipeline step ----
 //
-// One phase issues up to 32 MFMAs: first O^T += V^T P^T for the current tile
-// (D/32 accumulator blocks x 4 key steps of 16), then S^T = K Q^T for the next
-// tile (2 key blocks of 32 x D/16 steps).  Every MFMA takes its A operand from
-// LDS; the operands are read into a ring of registers kDepth MFMAs ahead of
-// their use, and the issue order is pinned to "one MFMA, one LDS read", so the
-// LDS latency hides behind the MFMAs already in the pipe.
+// MFMA stream: O^T += V^T P^T for the previous tile (D/32 accumulator blocks x 4
+// key steps of 16), then S^T = K Q^T for the next tile (2 key blocks of 32 x
+// D/16 steps); every A operand comes from LDS through a ring of registers
+// filled kDepth MFMAs ahead.  VALU stream: the online softmax of the current
+// tile, cut into per-MFMA slots (row max, threshold test, new reference max,
+// then the exponentials two scores at a time).  Each slot issues one MFMA, one
+// operand read and its share of the softmax; scheduling barriers between the
+// slots keep that interleave in the final instruction order.
 
-constexpr int kDepth = 6;
-
-template <int D, bool PV, bool QK>
-__device__ __forceinline__ void mfma_phase(const u32x4* sv, const u32x4* sk, const bf16x8 (&p)[4],
-                                           f32x16 (&acc)[D / 32], const bf16x8 (&qf)[D / 16],
-                                           f32x16 (&s)[2], uint32_t vaddr, uint32_t kaddr) {
-  using G = Geo<D>;
-  constexpr int NPV = PV ? 4 * (D / 32) : 0;
-  constexpr int NQK = QK ? 2 * (D / 16) : 0;
-  constexpr int NOPS = NPV + NQK;
-  const char* vb = (const char*)sv;
-  const char* kb = (const char*)sk;
-
-  // operand i: PV (ks = i / (D/32), cb = i % (D/32)), then QK (t = k / 2, mb = k % 2)
-  auto load = [&](int i) -> u32x4 {
-    if (i < NPV) {
-      const int ks = i / (D / 32), cb = i % (D / 32);
-      return *(const u32x4*)(vb + vaddr + 16 * (2 * ks * D + 32 * cb));
-    }
-    const int k = i - NPV, t = k / 2, mb = k % 2;
-    return *(const u32x4*)(kb + (kaddr ^ (32u * t)) + mb * 32 * G::NCH * 16);
-  };
-
-  u32x4 ring[kDepth];
-#pragma unroll
-  for (int i = 0; i < kDepth; ++i)
-    if (i < NOPS) ring[i] = load(i);
-  if constexpr (QK) {
-    s[0] = zero16();
-    s[1] = zero16();
-  }
-#pragma unroll
-  for (int i = 0; i < NOPS; ++i) {
-    const bf16x8 a = as_bf16x8(ring[i % kDepth]);
-    if (i + kDepth < NOPS) ring[i % kDepth] = load(i + kDepth);
-    if (i < NPV) {
-      const int ks = i / (D / 32), cb = i % (D / 32);
-      acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[ks], acc[cb], 0, 0, 0);
-    } else {
-      const int k = i - NPV, t = k / 2, mb = k % 2;
-      s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[mb], 0, 0, 0);
-    }
-  }
-  // S^T register r of block mb now holds key 32*mb + 16*(r/8) + 8*h + r%8
-
-  // issue order: the first reads, then alternate one MFMA with one read
-  __builtin_amdgcn_sched_group_barrier(0x100, NOPS < kDepth ? NOPS : kDepth, 0);
-#pragma unroll
-  for (int i = 0; i < NOPS; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (i + kDepth < NOPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-}
-
-// ---- VALU phase: online softmax of one tile ----
+constexpr int kDepth = 4;
 
 struct RowState {
   float m;       // running max, log2 units (-inf before the first visible key)
   float l;       // this lane's partial row sum (its half of each 32-key block)
-  unsigned steps, rescales;
-  bool first;
-  bool rescale;  // wave-uniform: O must be multiplied by alpha before the next PV product
-  float alpha;
 };
 
+template <int D, bool PV, bool QK>
+struct StepShape {
+  static constexpr int NPV = PV ? 4 * (D / 32) : 0;
+  static constexpr int NQK = QK ? 2 * (D / 16) : 0;
+  static constexpr int NOPS = NPV + NQK;
+  // softmax slot plan: 0-3 row max, 4 threshold test, 5 new max, then score pairs
+  static constexpr int PAIR0 = 6;
+  static constexpr int PAIRS_PER_SLOT = (16 + (NOPS - PAIR0 - 2)) / (NOPS - PAIR0 - 1);
+  static constexpr int LSUM = PAIR0 + (16 + PAIRS_PER_SLOT - 1) / PAIRS_PER_SLOT;
+  static_assert(!(PV && QK) || LSUM < NOPS, "softmax must fit in the MFMA slots");
+};
+
+// Operand i of a step: PV (ks = i / (D/32), cb = i % (D/32)), then QK (t = k/2, mb = k%2).
+template <int D, int NPV>
+__device__ __forceinline__ u32x4 load_operand(const char* vb, const char* kb, uint32_t vaddr,
+                                              uint32_t kaddr, int i) {
+  using G = Geo<D>;
+  if (i < NPV) {
+    const int ks = i / (D / 32), cb = i % (D / 32);
+    return *(const u32x4*)(vb + vaddr + 16 * (2 * ks * D + 32 * cb));
+  }
+  const int k = i - NPV, t = k / 2, mb = k % 2;
+  return *(const u32x4*)(kb + (kaddr ^ (32u * t)) + mb * 32 * G::NCH * 16);
+}
+
+template <int D, int NPV>
+__device__ __forceinline__ void issue_mfma(int i, const u32x4& op, const bf16x8 (&pp)[4],
+                                           f32x16 (&acc)[D / 32], const bf16x8 (&qf)[D / 16],
+                                           f32x16 (&sn)[2]) {
+  const bf16x8 a = as_bf16x8(op);
+  if (i < NPV) {
+    const int ks = i / (D / 32), cb = i % (D / 32);
+    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pp[ks], acc[cb], 0, 0, 0);
+  } else {
+    const int k = i - NPV, t = k / 2, mb = k % 2;
+    sn[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], sn[mb], 0, 0, 0);
+  }
+}
+
+// MFMAs only (pipeline prologue and the final PV product).
+template <int D, bool PV, bool QK>
+__device__ __forceinline__ void mfma_only(const u32x4* svp, const u32x4* skn,
+                                          const bf16x8 (&pp)[4], f32x16 (&acc)[D / 32],
+                                          const bf16x8 (&qf)[D / 16], f32x16 (&sn)[2],
+                                          uint32_t vaddr, uint32_t kaddr) {
+  using SS = StepShape<D, PV, QK>;
+  const char* vb = (const char*)svp;
+  const char* kb = (const char*)skn;
+  u32x4 ring[kDepth];
+#pragma unroll
+  for (int i = 0; i < kDepth; ++i)
+    if (i < SS::NOPS) ring[i] = load_operand<D, SS::NPV>(vb, kb, vaddr, kaddr, i);
+  if constexpr (QK) {
+    sn[0] = zero16();
+    sn[1] = zero16();
+  }
+#pragma unroll
+  for (int i = 0; i < SS::NOPS; ++i) {
+    const u32x4 op = ring[i % kDepth];
+    if (i + kDepth < SS::NOPS)
+      ring[i % kDepth] = load_operand<D, SS::NPV>(vb, kb, vaddr, kaddr, i + kDepth);
+    issue_mfma<D, SS::NPV>(i, op, pp, acc, qf, sn);
+  }
+}
+
+// One pipeline step: PV of tile j-1 (pp, V^T tile in svp), QK of tile j+1 into
+// sn (K tile in skn), and the online softmax of tile j (sc -> pc), interleaved.
+// Returns whether any row of the wave raised its reference max by more than tau;
+// then O must be multiplied by alpha before the next PV product.
 template <int D, bool CAUSAL, bool POLY, bool MASK>
-__device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], bf16x8 (&p)[4], RowState& st, int kv0,
-                                             int qi, int N, float c, float tau, int h) {
+__device__ __forceinline__ bool step(const u32x4* svp, const u32x4* skn, const bf16x8 (&pp)[4],
+                                     f32x16 (&acc)[D / 32], const bf16x8 (&qf)[D / 16],
+                                     f32x16 (&sc)[2], f32x16 (&sn)[2], bf16x8 (&pc)[4],
+                                     RowState& st, float& alpha, int kv0, int qi, int N, float c,
+                                     float tau, int h, uint32_t vaddr, uint32_t kaddr) {
+  using SS = StepShape<D, true, true>;
   const float NEG_INF = -__builtin_inff();
+  const char* vb = (const char*)svp;
+  const char* kb = (const char*)skn;
+
   if constexpr (MASK) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -271,62 +291,70 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], bf16x8 (&p)[4], Row
       for (int r = 0; r < 16; ++r) {
         const int key = kv0 + 32 * mb + 16 * (r >> 3) + 8 * h + (r & 7);
         const bool ok = key < N && (!CAUSAL || key <= qi);
-        s[mb][r] = ok ? s[mb][r] : NEG_INF;
+        sc[mb][r] = ok ? sc[mb][r] : NEG_INF;
       }
   }
 
-  float mx = NEG_INF;
+  u32x4 ring[kDepth];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
-  mx = half_swap_max(mx);
-  const float mt = (mx == NEG_INF) ? NEG_INF : mx * c;
+  for (int i = 0; i < kDepth; ++i) ring[i] = load_operand<D, SS::NPV>(vb, kb, vaddr, kaddr, i);
+  sn[0] = zero16();
+  sn[1] = zero16();
 
-  if (!st.first) ++st.steps;
-  st.rescale = false;
-  if (__ballot(mt > st.m + tau)) {
-    const float m_new = fmaxf(st.m, mt);
-    st.alpha = (m_new == NEG_INF) ? 1.f : exp2_sel<POLY>(st.m - m_new);
-    st.l *= st.alpha;
-    st.m = m_new;
-    st.rescale = true;
-    if (!st.first) ++st.rescales;
-  }
-  st.first = false;
-  const float mu = (st.m == NEG_INF) ? 0.f : st.m;
-
+  float mx = NEG_INF, mt = NEG_INF, mu = 0.f;
+  bool any = false;
+  u32x4 pk[4];
   float ls[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      u32x4 pk;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float s0 = s[mb][hf * 8 + 2 * e], s1 = s[mb][hf * 8 + 2 * e + 1];
-        float e0 = exp2_sel<POLY>(__builtin_fmaf(s0, c, -mu));
-        float e1 = exp2_sel<POLY>(__builtin_fmaf(s1, c, -mu));
-        if constexpr (MASK) {
-          e0 = (s0 == NEG_INF) ? 0.f : e0;
-          e1 = (s1 == NEG_INF) ? 0.f : e1;
-        }
-        pk[e] = pack_bf16x2(e0, e1);
-        ls[e] += e0 + e1;
-      }
-      p[mb * 2 + hf] = as_bf16x8(pk);
-    }
-  st.l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-}
 
-template <int D, bool CAUSAL, bool POLY>
-__device__ __forceinline__ void softmax_any(bool masked, f32x16 (&s)[2], bf16x8 (&p)[4],
-                                            RowState& st, int kv0, int qi, int N, float c,
-                                            float tau, int h) {
-  if (masked)
-    softmax_tile<D, CAUSAL, POLY, true>(s, p, st, kv0, qi, N, c, tau, h);
-  else
-    softmax_tile<D, CAUSAL, POLY, false>(s, p, st, kv0, qi, N, c, tau, h);
+#pragma unroll
+  for (int k = 0; k < SS::NOPS; ++k) {
+    const u32x4 op = ring[k % kDepth];
+    if (k + kDepth < SS::NOPS)
+      ring[k % kDepth] = load_operand<D, SS::NPV>(vb, kb, vaddr, kaddr, k + kDepth);
+    issue_mfma<D, SS::NPV>(k, op, pp, acc, qf, sn);
+
+    if (k < 4) {                       // row max over 8 scores
+      const int mb = k >> 1, r0 = (k & 1) * 8;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) mx = fmaxf(mx, sc[mb][r0 + r]);
+    } else if (k == 4) {               // whole row (other half-wave), threshold test
+      mx = half_swap_max(mx);
+      mt = (mx == NEG_INF) ? NEG_INF : mx * c;
+      any = __ballot(mt > st.m + tau) != 0;
+    } else if (k == 5) {               // thresholded update of the reference max
+      const float m_new = any ? fmaxf(st.m, mt) : st.m;
+      alpha = (m_new == NEG_INF) ? 1.f : exp2_sel<POLY>(st.m - m_new);
+      st.m = m_new;
+      mu = (m_new == NEG_INF) ? 0.f : m_new;
+    } else if (k >= SS::PAIR0 && k < SS::LSUM) {
+#pragma unroll
+      for (int q = 0; q < SS::PAIRS_PER_SLOT; ++q) {
+        const int e = (k - SS::PAIR0) * SS::PAIRS_PER_SLOT + q;   // score pair 0..15
+        if (e < 16) {
+          const int mb = e >> 3, hf = (e >> 2) & 1, ee = e & 3;
+          const float s0 = sc[mb][hf * 8 + 2 * ee], s1 = sc[mb][hf * 8 + 2 * ee + 1];
+          float e0 = exp2_sel<POLY>(__builtin_fmaf(s0, c, -mu));
+          float e1 = exp2_sel<POLY>(__builtin_fmaf(s1, c, -mu));
+          if constexpr (MASK) {
+            e0 = (s0 == NEG_INF) ? 0.f : e0;
+            e1 = (s1 == NEG_INF) ? 0.f : e1;
+          }
+          pk[mb * 2 + hf][ee] = pack_bf16x2(e0, e1);
+          ls[ee] += e0 + e1;
+          // a use in this slot keeps the compiler from sinking the work out of it
+          asm volatile("" ::"v"(pk[mb * 2 + hf][ee]), "v"(ls[ee]));
+        }
+      }
+    } else if (k == SS::LSUM) {
+      st.l = __builtin_fmaf(st.l, alpha, (ls[0] + ls[1]) + (ls[2] + ls[3]));
+      asm volatile("" ::"v"(st.l));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // S^T register r of block mb (next tile) holds key 32*mb + 16*(r/8) + 8*h + r%8
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pc[i] = as_bf16x8(pk[i]);
+  return any;
 }
 
 template <int D, bool CAUSAL, bool POLY>
@@ -341,20 +369,46 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n32 = lane & 31, h = lane >> 5;
-  const bool lead = wave < kWaves / 2;   // group A leads, group B trails by one phase
 
-  // Workgroup -> (batch, kv head, query block, query head in the group).  Workgroups
-  // are dealt round-robin to the 8 XCDs; renumber so each XCD gets a contiguous
-  // range, in which the query heads of one kv head and neighbouring query blocks
-  // sit together and share K/V tiles in that XCD's L2.  Causal: heaviest blocks first.
+  // Workgroup -> (batch, kv head, query head in the group, query block).
+  // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).  When
+  // the kv heads split evenly over the XCDs, each XCD gets a contiguous range of
+  // kv heads, so the query heads sharing a kv head and all their query blocks
+  // read K/V through the same L2.  Within an XCD the dispatch order is: causal,
+  // query block outermost with the heaviest (longest key range) first, so the
+  // XCD's CUs take the longest work first and end together; non-causal, query
+  // heads of a group, then query blocks, then kv heads.
   const int G_ = gridDim.x, w = blockIdx.x;
-  const int L = (G_ % 8 == 0) ? (w % 8) * (G_ / 8) + (w / 8) : w;
   const int group = Hq / Hkv;
-  const int g = L % group;
-  const int t1 = L / group;
-  const int qb_rank = t1 % nqb;
-  const int t2 = t1 / nqb;
-  const int hkv = t2 % Hkv, b = t2 / Hkv;
+  const int nkv = (int)(G_ / (group * nqb));          // B * Hkv
+  int b, hkv, g, qb_rank;
+  if (nkv % 8 == 0) {
+    const int x = w % 8, r = w / 8;                   // XCD and dispatch rank within it
+    const int kv_per = nkv / 8;
+    int kvl;
+    if (CAUSAL) {
+      qb_rank = r / (kv_per * group);
+      const int t = r % (kv_per * group);
+      kvl = t / group;
+      g = t % group;
+    } else {
+      g = r % group;
+      qb_rank = (r / group) % nqb;
+      kvl = r / (group * nqb);
+    }
+    const int kv = x * kv_per + kvl;
+    hkv = kv % Hkv;
+    b = kv / Hkv;
+  } else {
+    // uneven split: plain order; causal, heaviest query blocks first across the grid
+    const int hw = nkv * group;
+    const int r = CAUSAL ? w % hw : w / nqb;
+    qb_rank = CAUSAL ? w / hw : w % nqb;
+    g = r % group;
+    const int kv = r / group;
+    hkv = kv % Hkv;
+    b = kv / Hkv;
+  }
   const int hq = hkv * group + g;
   const int qb = CAUSAL ? (nqb - 1 - qb_rank) : qb_rank;
 
@@ -380,30 +434,28 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   f32x16 acc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = zero16();
-  RowState st{-__builtin_inff(), 0.f, 0u, 0u, true, false, 1.f};
+  RowState st{-__builtin_inff(), 0.f};
+  unsigned n_steps = 0, n_rescales = 0;
+  bool first = true;
 
-  // Tiles of 64 keys this workgroup visits, and which of them touch this wave's rows.
+  // Tiles of 64 keys this workgroup visits; per wave, which need element masks.
   const int kv_end = CAUSAL ? min(N, Q0 + kBr) : N;
   const int n = (kv_end + kBc - 1) / kBc;
   const int wave_end = CAUSAL ? min(N, q0 + kRowsPerWave) : N;   // keys this wave can see
   const bool wave_live = q0 < N;
   auto active = [&](int j) { return wave_live && j * kBc < wave_end; };
-  auto masked = [&](int j) {
-    const int kv0 = j * kBc;
-    return (CAUSAL && kv0 + kBc - 1 > q0) || (kv0 + kBc > N);
-  };
 
   auto tile_rsrc = [&](const uint16_t* head, int kv0) {
     return make_rsrc(head + (size_t)kv0 * D, (N - kv0) * G::ROW_BYTES);
   };
-  // Stage t of the pipeline holds K tile t+1 and V tile t.
+  // Stage t (read by pipeline step t from buffer t & 1) holds K tile t+1 and V tile t-1.
   auto load_stage = [&](Stage<D>& s, int t) {
     if (t + 1 < n) load_k<D>(s, tile_rsrc(Kh, (t + 1) * kBc), tid);
-    load_v<D>(s, tile_rsrc(Vh, t * kBc), tid);
+    if (t >= 1 && t - 1 < n) load_v<D>(s, tile_rsrc(Vh, (t - 1) * kBc), tid);
   };
   auto store_stage = [&](const Stage<D>& s, int t) {
     if (t + 1 < n) store_k<D>(s, sk[t & 1], tid);
-    store_v<D>(s, sv[t & 1], tid);
+    if (t >= 1 && t - 1 < n) store_v<D>(s, sv[t & 1], tid);
   };
 
   // Per-lane operand addresses (bytes within a tile).
@@ -411,7 +463,8 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                          (uint32_t)(16 * (h ^ ((n32 & 15) >> G::SW_SHIFT)));
   const uint32_t vaddr = (uint32_t)(16 * (h * D + n32));
 
-  // ---- prologue: K tile 0 -> sk[1], stage 0 -> buffer 0, stage 1 in registers ----
+  // ---- prologue: K tile 0 -> sk[1]; stage 0 (K tile 1, V^T = 0) -> buffer 0;
+  //      stage 1 (K tile 2, V tile 0) in registers; S of tile 0 ----
   Stage<D> stg;
   {
     Stage<D> s0;
@@ -419,46 +472,76 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     load_stage(stg, 0);
     store_k<D>(s0, sk[1], tid);
     store_stage(stg, 0);
+    for (int u = tid; u < G::VUNITS; u += kThreads) sv[0][u] = u32x4{0u, 0u, 0u, 0u};
   }
-  if (n > 1) load_stage(stg, 1);
-  lds_barrier();
-  if (!lead) lds_barrier();
-
-  f32x16 s[2];
-  bf16x8 p[4];
-  if (active(0)) mfma_phase<D, false, true>(sv[0], sk[1], p, acc, qf, s, vaddr, kaddr);
+  load_stage(stg, 1);   // V tile 0 always exists; K tile 2 only if n > 2
   lds_barrier();
 
-  for (int j = 0; j < n; ++j) {
-    // VALU phase: softmax of tile j.  A wave whose rows see no key of the tile
-    // (causal, past its diagonal) contributes P = 0 to the shared MFMA code.
+  // S of the current tile and of the next one, P of the current tile and the previous one.
+  f32x16 s_cur[2], s_nxt[2];
+  bf16x8 p_prev[4], p_cur[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p_prev[i] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  mfma_only<D, false, true>(sv[0], sk[1], p_prev, acc, qf, s_cur, vaddr, kaddr);
+  lds_barrier();
+
+  // One pipeline step j: the rescale of O decided by step j-1 (a rare branch,
+  // kept outside the interleaved region), then PV of tile j-1, QK of tile j+1 and
+  // the softmax of tile j as one straight-line region; then the staging of the
+  // next stage and one barrier.
+  bool any_prev = false;
+  float alpha_prev = 1.f;
+  auto rescale = [&]() {
+    if (any_prev) {
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) acc[i] *= alpha_prev;
+    }
+  };
+  auto finish_step = [&](int j, bool any, float alpha) {
+    any_prev = any;
+    alpha_prev = alpha;
     if (active(j)) {
-      softmax_any<D, CAUSAL, POLY>(masked(j), s, p, st, j * kBc, qi, N, c, tau, h);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-      st.rescale = false;
+      if (!first) {
+        ++n_steps;
+        n_rescales += any ? 1u : 0u;
+      }
+      first = false;
     }
-    lds_barrier();
-
-    // MFMA phase: stage j+1 to LDS, prefetch stage j+2, PV of tile j, QK of tile j+1
-    // (in the last iteration the QK half reads a stale buffer and its result is unused).
-    if (j + 1 < n) {
+    if (j + 1 <= n) {
       store_stage(stg, j + 1);
-      if (j + 2 < n) load_stage(stg, j + 2);
+      if (j + 2 <= n) load_stage(stg, j + 2);
     }
-    const u32x4* svj = sv[j & 1];
-    const u32x4* skj = sk[j & 1];
-    if (st.rescale) {
 #pragma unroll
-      for (int i = 0; i < D / 32; ++i) acc[i] *= st.alpha;
-      mfma_phase<D, true, true>(svj, skj, p, acc, qf, s, vaddr, kaddr);
-    } else {
-      mfma_phase<D, true, true>(svj, skj, p, acc, qf, s, vaddr, kaddr);
-    }
+    for (int i = 0; i < 2; ++i) s_cur[i] = s_nxt[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p_prev[i] = p_cur[i];
     lds_barrier();
+  };
+
+  // Tiles [0, n_full) need no element mask for any row of the workgroup: causal,
+  // the keys below the workgroup's first query; otherwise the whole 64-key tiles.
+  const int n_full = CAUSAL ? min(Q0, N) / kBc : N / kBc;
+  int j = 0;
+  for (; j < n_full; ++j) {
+    rescale();
+    float alpha;
+    const bool any = step<D, CAUSAL, POLY, false>(
+        sv[j & 1], sk[j & 1], p_prev, acc, qf, s_cur, s_nxt, p_cur, st, alpha, j * kBc, qi, N, c,
+        tau, h, vaddr, kaddr);
+    finish_step(j, any, alpha);
   }
-  if (lead) lds_barrier();
+  for (; j < n; ++j) {
+    rescale();
+    float alpha;
+    const bool any = step<D, CAUSAL, POLY, true>(
+        sv[j & 1], sk[j & 1], p_prev, acc, qf, s_cur, s_nxt, p_cur, st, alpha, j * kBc, qi, N, c,
+        tau, h, vaddr, kaddr);
+    finish_step(j, any, alpha);
+  }
+  rescale();
+
+  // ---- last PV product (tile n-1, V tile in stage n) ----
+  mfma_only<D, true, false>(sv[n & 1], sk[n & 1], p_prev, acc, qf, s_nxt, vaddr, kaddr);
 
   // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l) ----
   const float ltot = half_swap_sum(st.l);
@@ -478,8 +561,8 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
           ltot > 0.f ? (st.m + __builtin_log2f(ltot)) * kLn2 : -__builtin_inff();
   }
   if (stats != nullptr && lane == 0 && wave_live) {
-    atomicAdd(stats, (unsigned long long)st.steps);
-    atomicAdd(stats + 1, (unsigned long long)st.rescales);
+    atomicAdd(stats, (unsigned long long)n_steps);
+    atomicAdd(stats + 1, (unsigned long long)n_rescales);
   }
 }
 
