@@ -4,19 +4,28 @@
 A step is one fused attention forward (QK^T, mask, online softmax with
 thresholded rescale, PV, LSE) over one batch of synthetic inputs already
 resident in HBM.  The headline workload is causal B=4, H=16, N=2048, d=128
-bf16 (workload 2); `--config` picks another.  The spec workloads with
-N >= 8192 (3 and 4) and the exp-mode comparison are reported under "extra".
+bf16; `--config` picks another workload and `--extra` times more of them
+(reported under "extra", never in the headline fields).
 
-Timing: W untimed warm-up launches, then K launches bracketed by a device
-synchronise on both sides; each launch is also bracketed by HIP events on the
-stream it runs on, which gives the average kernel duration used for the
-roofline.  FLOPs follow the metric: 4*B*H*N^2*d, halved for causal.
+Timing: the GPU is first driven with untimed launches for `--warmup-seconds`
+(clocks ramp up under load), then W untimed warm-up steps, then K timed steps
+bracketed by a device synchronise on both sides and by two HIP events on the
+stream the kernel runs on; the events' span / K is the step time and the mean
+kernel duration used for the roofline (the launches run back to back).  A
+separate pass with events around every launch gives min / median / max.
+FLOPs follow the metric: 4*B*H*N^2*d, halved for causal.
+
+Other modes (for rocprofv3 counter runs; they print nothing on stdout):
+  --mode launch   run the workload's kernel --steps times, no timing, no oracle
+  --mode copy     a plain device-to-device copy of --copy-mib MiB, --steps times
+                  (calibrates the HBM byte counters against a known transfer)
 """
 
 import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -25,10 +34,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attn fwd TFLOP/s (4·B·H·N²·d, causal halved) and % of MI355X MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6      # dense bf16 MFMA, 256 CUs x 2.4 GHz x 4096 flop/clk
-PEAK_FP4_TFLOPS = 10066.3      # dense MXFP4 MFMA
 KERNEL_SOURCES = ["exact_attention_forward_tiled_amd/csrc/attn_fwd_bf16.hip",
-                  "exact_attention_forward_tiled_amd/csrc/attn_mxfp4.hip",
-                  "exact_attention_forward_tiled_amd/csrc/common.h"]
+                  "exact_attention_forward_tiled_amd/csrc/common.h",
+                  "exact_attention_forward_tiled_amd/csrc/exp2_poly.h"]
 
 
 def log(*a):
@@ -47,7 +55,8 @@ def load_traffic(workload_name):
     """HBM bytes per launch from committed rocprofv3 counter runs, if taken on this kernel."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
-        rec = json.load(open(path))[workload_name]
+        with open(path) as fh:
+            rec = json.load(fh)[workload_name]
     except (OSError, KeyError, ValueError):
         return None
     if rec.get("kernel_hash") != kernel_hash():
@@ -55,64 +64,87 @@ def load_traffic(workload_name):
     return rec.get("hbm_bytes_per_launch")
 
 
-def make_inputs(w):
-    import torch
-    from synth import workload  # noqa: F401  (inputs come from the seeded generator only)
+def device_inputs(w):
     import numpy as np
-    qb, kb, vb = w.make()
-    dev = [torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
-           for x in (qb, kb, vb)]
-    return dev, (qb, kb, vb)
-
-
-def time_launches(fn, steps, warmup):
     import torch
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
+    qb, kb, vb = w.make()
+    return [torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+            for x in (qb, kb, vb)]
+
+
+class Workload:
+    """Device buffers and one launch closure for a bf16 workload."""
+
+    def __init__(self, w, exp_mode, tau):
+        import torch
+        import exact_attention_forward_tiled_amd as fa
+        self.w = w
+        self.q, self.k, self.v = device_inputs(w)
+        self.o = torch.empty((w.B, w.Hq, w.N, w.d), dtype=torch.float32, device="cuda")
+        self.lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device="cuda")
+        self.fa = fa
+        self.exp_mode, self.tau = exp_mode, tau
+
+    def launch(self, stats=None):
+        self.fa.fwd(self.q, self.k, self.v, causal=self.w.causal, scale=self.w.scale, tau=self.tau,
+                    exp_mode=self.exp_mode, stats=stats, out=(self.o, self.lse))
+
+
+def time_workload(wl, steps, warmup, warmup_seconds):
+    """Ramp, warm up, then K back-to-back launches between two HIP events on the launch
+    stream (their span / K is both ms_per_step and the mean kernel duration); a second,
+    separate pass brackets each launch with its own events for min / median / max."""
+    import torch
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    t_end = time.perf_counter() + warmup_seconds
+    n_ramp = 0
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            wl.launch()
+        n_ramp += 8
+        torch.cuda.synchronize()
+    for _ in range(warmup):
+        wl.launch()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for a, b in ev:
-        a.record(stream)
-        fn()
-        b.record(stream)
+    e0.record(stream)
+    for _ in range(steps):
+        wl.launch()
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    total_ms = e0.elapsed_time(e1)
+    # per-launch spread (events between launches add a small gap; diagnostic only)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        wl.launch()
+        b.record(stream)
+    torch.cuda.synchronize()
     per = [a.elapsed_time(b) for a, b in ev]
-    total_ms = ev[0][0].elapsed_time(ev[-1][1])
-    return {"ms_per_step": total_ms / steps, "kernel_ms_avg": sum(per) / len(per),
-            "kernel_ms_min": min(per), "kernel_ms_max": max(per), "wall_s": wall}
+    w = wl.w
+    r = {"ms_per_step": total_ms / steps, "kernel_ms_avg": total_ms / steps,
+         "kernel_ms_median": statistics.median(per), "kernel_ms_min": min(per),
+         "kernel_ms_max": max(per), "wall_s": wall, "ramp_launches": n_ramp}
+    r["tflops"] = w.flops / (r["ms_per_step"] * 1e-3) / 1e12
+    r["kernel_tflops"] = w.flops / (r["kernel_ms_avg"] * 1e-3) / 1e12
+    return r
 
 
-def bench_bf16(w, steps, warmup, exp_mode="hw", tau=8.0):
+def skip_ratio(wl):
+    """Fraction of (wave, tile) steps after each wave's first that skipped the O rescale."""
     import torch
-    import exact_attention_forward_tiled_amd as fa
-    (q, k, v), _ = make_inputs(w)
-    o = torch.empty((w.B, w.Hq, w.N, w.d), dtype=torch.float32, device="cuda")
-    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device="cuda")
-
-    def step():
-        fa.fwd(q, k, v, causal=w.causal, scale=w.scale, tau=tau, exp_mode=exp_mode, out=(o, lse))
-    t = time_launches(step, steps, warmup)
-    t["tflops"] = w.flops / (t["ms_per_step"] * 1e-3) / 1e12
-    t["kernel_tflops"] = w.flops / (t["kernel_ms_avg"] * 1e-3) / 1e12
-    # skip ratio of the thresholded rescale (separate, untimed launch)
     stats = torch.zeros(2, dtype=torch.int64, device="cuda")
-    fa.fwd(q, k, v, causal=w.causal, scale=w.scale, tau=tau, exp_mode=exp_mode, stats=stats,
-           out=(o, lse))
+    wl.launch(stats=stats)
     torch.cuda.synchronize()
     s, r = (int(x) for x in stats.cpu())
-    t["skip_ratio"] = (1.0 - r / s) if s else None
-    del q, k, v, o, lse
-    torch.cuda.empty_cache()
-    return t
+    return (1.0 - r / s) if s else None
 
 
-def cpu_baseline(w, budget_s=12.0):
+def cpu_baseline(w, budget_s=10.0):
     """The float64 oracle, as it stands, on whole (batch, head) slices of the same workload."""
-    import numpy as np
     import oracle
     import synth
     from threadpoolctl import threadpool_info
@@ -120,19 +152,18 @@ def cpu_baseline(w, budget_s=12.0):
     q, k, v = (synth.bf16_bits_to_f64(x) for x in (qb, kb, vb))
     heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
     done, t0 = 0, time.perf_counter()
-    for b, h in heads:
+    while time.perf_counter() - t0 < budget_s:
+        b, h = heads[done % len(heads)]
         oracle.attention_head(q, k, v, w.causal, w.scale, b, h)
         done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
     el = time.perf_counter() - t0
     flops = w.flops * done / len(heads)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()
                    if i.get("user_api") == "blas"] or [1])
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{done} of {len(heads)} (batch, head) slices of {w.name}, float64 numpy, "
-                      f"{el:.1f} s"}
+            "sample": f"{done} (batch, head) slices of {w.name} ({len(heads)} per step), "
+                      f"float64 numpy, {el:.1f} s"}
 
 
 def main():
@@ -140,11 +171,16 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup-seconds", type=float, default=0.5)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--exp", default="hw", choices=["hw", "poly"])
     ap.add_argument("--tau", type=float, default=8.0)
-    ap.add_argument("--extra", default="3,4", help="other workloads to time (comma list, or '')")
+    ap.add_argument("--extra", default="", help="other workloads to time (comma list), e.g. 3,4")
+    ap.add_argument("--compare-exp", action="store_true",
+                    help="also time the headline workload with the other exp mode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", default="bench", choices=["bench", "launch", "copy"])
+    ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -158,35 +194,68 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+
+    if args.mode == "copy":
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {args.copy_mib} MiB x {args.steps}")
+        return
+
     w = synth.workload(args.config)
     if w.fmt != "bf16":
         print("bench.py: the headline line times a bf16 workload", file=sys.stderr)
         sys.exit(2)
 
-    log(f"timing {w.name}: warmup {args.warmup}, steps {args.steps}")
-    t = bench_bf16(w, args.steps, args.warmup, args.exp, args.tau)
-    kernel_tf = t["kernel_tflops"]
-    traffic = load_traffic(w.name)
+    if args.mode == "launch":
+        wl = Workload(w, args.exp, args.tau)
+        for _ in range(args.steps):
+            wl.launch()
+        torch.cuda.synchronize()
+        log(f"launched {w.name} x {args.steps}")
+        return
 
-    extra = {"kernel_ms_avg": t["kernel_ms_avg"], "kernel_ms_min": t["kernel_ms_min"],
+    log(f"timing {w.name}: ramp {args.warmup_seconds} s, warmup {args.warmup}, steps {args.steps}")
+    wl = Workload(w, args.exp, args.tau)
+    t = time_workload(wl, args.steps, args.warmup, args.warmup_seconds)
+    skip = skip_ratio(wl)
+    del wl
+    torch.cuda.empty_cache()
+    kernel_tf = t["kernel_tflops"]
+    props = torch.cuda.get_device_properties(0)
+
+    extra = {"kernel_ms_avg": t["kernel_ms_avg"], "kernel_ms_median": t["kernel_ms_median"],
+             "kernel_ms_min": t["kernel_ms_min"], "kernel_ms_max": t["kernel_ms_max"],
              "pct_of_bf16_peak": 100.0 * t["tflops"] / PEAK_BF16_TFLOPS,
-             "skip_ratio": t["skip_ratio"], "exp_mode": args.exp, "tau": args.tau,
-             "kernel_hash": kernel_hash(), "workloads": {}}
-    other = "poly" if args.exp == "hw" else "hw"
-    log(f"timing {w.name} with exp mode {other}")
-    t2 = bench_bf16(w, args.steps, args.warmup, other, args.tau)
-    extra["workloads"][f"{w.name}/exp={other}"] = {
-        "tflops": round(t2["tflops"], 2), "ms": round(t2["ms_per_step"], 4)}
+             "skip_ratio": skip, "exp_mode": args.exp, "tau": args.tau,
+             "kernel_hash": kernel_hash(), "device": props.name,
+             "compute_units": props.multi_processor_count, "workloads": {}}
+    if args.compare_exp:
+        other = "poly" if args.exp == "hw" else "hw"
+        log(f"timing {w.name} with exp mode {other}")
+        wl = Workload(w, other, args.tau)
+        t2 = time_workload(wl, args.steps, args.warmup, args.warmup_seconds)
+        del wl
+        extra["workloads"][f"{w.name}/exp={other}"] = {
+            "tflops": round(t2["tflops"], 2), "ms": round(t2["ms_per_step"], 4)}
     for idx in [int(x) for x in args.extra.split(",") if x.strip()]:
         wx = synth.workload(idx)
         if wx.fmt != "bf16" or idx == args.config:
             continue
         log(f"timing {wx.name}")
-        tx = bench_bf16(wx, max(5, args.steps // 2), args.warmup, args.exp, args.tau)
+        wl = Workload(wx, args.exp, args.tau)
+        tx = time_workload(wl, max(5, args.steps // 2), args.warmup, args.warmup_seconds)
+        sx = skip_ratio(wl)
+        del wl
+        torch.cuda.empty_cache()
         extra["workloads"][wx.name] = {
             "tflops": round(tx["tflops"], 2), "ms": round(tx["ms_per_step"], 4),
+            "kernel_ms_avg": round(tx["kernel_ms_avg"], 4),
             "pct_of_bf16_peak": round(100.0 * tx["tflops"] / PEAK_BF16_TFLOPS, 2),
-            "skip_ratio": tx["skip_ratio"]}
+            "skip_ratio": sx}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -209,7 +278,7 @@ def main():
         "config": dict(w.describe()),
         "roofline": {"bound": "mfma", "achieved": round(kernel_tf, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(kernel_tf / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic},
+                     "traffic": load_traffic(w.name)},
         "cpu_baseline": cpu,
         "extra": extra,
     }
