@@ -163,6 +163,49 @@ __global__ void cvt_dot_probe(const float* x, const float* acc, uint32_t* out) {
   out[2 * l + 1] = __float_as_uint(d);
 }
 
+
+// fp4 convert probe.  x: 64 lanes x 2 floats; scale: 64 floats; out: 64 lanes x 4 u32,
+// out[4l + sel] = v_cvt_scalef32_pk_fp4_f32 of (x[2l], x[2l+1]) into byte `sel` of 0xFFFFFFFF.
+__global__ void cvt_fp4_probe(const float* x, const float* scale, uint32_t* out) {
+  const int l = threadIdx.x;
+  const float a = x[2 * l], b = x[2 * l + 1], s = scale[l];
+  out[4 * l + 0] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0xFFFFFFFFu, a, b, s, 0);
+  out[4 * l + 1] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0xFFFFFFFFu, a, b, s, 1);
+  out[4 * l + 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0xFFFFFFFFu, a, b, s, 2);
+  out[4 * l + 3] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0xFFFFFFFFu, a, b, s, 3);
+}
+
+// fp4 decode probe.  src: 64 u32; scale: 64 floats; out: 64 lanes x 4 sels x 2 floats.
+__global__ void dec_fp4_probe(const uint32_t* src, const float* scale, float* out) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const int l = threadIdx.x;
+  const uint32_t v = src[l];
+  const float s = scale[l];
+  f2 d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, s, 0);
+  f2 d1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, s, 1);
+  f2 d2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, s, 2);
+  f2 d3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, s, 3);
+  out[8 * l + 0] = d0[0]; out[8 * l + 1] = d0[1];
+  out[8 * l + 2] = d1[0]; out[8 * l + 3] = d1[1];
+  out[8 * l + 4] = d2[0]; out[8 * l + 5] = d2[1];
+  out[8 * l + 6] = d3[0]; out[8 * l + 7] = d3[1];
+}
+
+// fp4 MFMA with 32-bit scale words and byte selection 2 for both operands.
+// a, b: 64 lanes x 16 bytes; sa, sb: 64 u32; c: 64 lanes x 16 fp32.
+__global__ void mfma_fp4_sel2_probe(const uint8_t* a, const uint8_t* b, const uint32_t* sa,
+                                    const uint32_t* sb, float* c) {
+  const int l = threadIdx.x;
+  const u32x4 a4 = *(const u32x4*)(a + 16 * l);
+  const u32x4 b4 = *(const u32x4*)(b + 16 * l);
+  i32x8 av = {(int)a4[0], (int)a4[1], (int)a4[2], (int)a4[3], 0, 0, 0, 0};
+  i32x8 bv = {(int)b4[0], (int)b4[1], (int)b4[2], (int)b4[3], 0, 0, 0, 0};
+  f32x16 acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, zero16(), 4, 4, 2,
+                                                                (int)sa[l], 2, (int)sb[l]);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) c[16 * l + i] = acc[i];
+}
+
 }  // namespace
 
 extern "C" {
@@ -230,6 +273,26 @@ int probe_lds_dma(const void* src, void* out, void* stream) {
 int probe_cvt_dot(const void* x, const void* acc, void* out, void* stream) {
   hipLaunchKernelGGL(cvt_dot_probe, dim3(1), dim3(64), 0, (hipStream_t)stream,
                      (const float*)x, (const float*)acc, (uint32_t*)out);
+  return (int)hipGetLastError();
+}
+
+int probe_cvt_fp4(const void* x, const void* scale, void* out, void* stream) {
+  hipLaunchKernelGGL(cvt_fp4_probe, dim3(1), dim3(64), 0, (hipStream_t)stream, (const float*)x,
+                     (const float*)scale, (uint32_t*)out);
+  return (int)hipGetLastError();
+}
+
+int probe_dec_fp4(const void* src, const void* scale, void* out, void* stream) {
+  hipLaunchKernelGGL(dec_fp4_probe, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                     (const uint32_t*)src, (const float*)scale, (float*)out);
+  return (int)hipGetLastError();
+}
+
+int probe_mfma_fp4_sel2(const void* a, const void* b, const void* sa, const void* sb, float* c,
+                        void* stream) {
+  hipLaunchKernelGGL(mfma_fp4_sel2_probe, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                     (const uint8_t*)a, (const uint8_t*)b, (const uint32_t*)sa,
+                     (const uint32_t*)sb, c);
   return (int)hipGetLastError();
 }
 

@@ -11,6 +11,14 @@ CDNA3/CDNA4 operand layouts:
   half of the second.
 * 16-byte direct-to-LDS loads: lane l's 16 bytes land at LDS base + 16*l.
 * the packed fp32 -> bf16 convert rounds to nearest even.
+* v_mfma_scale_f32_32x32x64_f8f6f4 with fp4 (E2M1) operands: lane l holds row
+  (A) or column (B) l % 32 and the 32 k-elements 32*(l // 32) .. +31, element i
+  in nibble i of its 16 bytes (low nibble first); lane l's E8M0 scale byte,
+  picked from its 32-bit scale register by op_sel, scales exactly those 32
+  elements; the accumulator layout is that of the bf16 product.
+* v_cvt_scalef32_pk_fp4_f32 writes RNE(x / scale) onto the E2M1 grid (ties to
+  the even code, saturating at +-6) into the selected byte, keeping the others;
+  v_cvt_scalef32_pk_f32_fp4 decodes a selected byte times the scale.
 """
 
 import ctypes
@@ -33,7 +41,9 @@ def lib():
     P, I = ctypes.c_void_p, ctypes.c_int
     for name, args in {"probe_mfma_bf16": [P, P, P, P], "probe_permlane32": [P, P],
                        "probe_lds_dma": [P, P, P], "probe_cvt_dot": [P, P, P, P],
-                       "probe_mfma_fp4": [P, P, P, P, P, P]}.items():
+                       "probe_mfma_fp4": [P, P, P, P, P, P],
+                       "probe_mfma_fp4_sel2": [P, P, P, P, P, P],
+                       "probe_cvt_fp4": [P, P, P, P], "probe_dec_fp4": [P, P, P, P]}.items():
         fn = getattr(lib, name)
         fn.restype = I
         fn.argtypes = args
@@ -115,9 +125,111 @@ def test_bf16_convert_rounds_to_nearest_even(lib):
     acc = np.zeros(64, np.float32)
     out = torch.zeros(128, dtype=torch.int32, device="cuda")
     log("probe cvt_dot")
-    assert lib.probe_cvt_dot(_dev(x).data_ptr(), _dev(acc).data_ptr(), out.data_ptr(), None) == 0
+    xd, accd = _dev(x), _dev(acc)       # keep the device buffers alive across the launch
+    assert lib.probe_cvt_dot(xd.data_ptr(), accd.data_ptr(), out.data_ptr(), None) == 0
     _sync()
     got = out.cpu().numpy().view(np.uint32).reshape(64, 2)
     ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     want = ref[0::2].astype(np.uint32) | (ref[1::2].astype(np.uint32) << 16)
     assert np.array_equal(got[:, 0], want)
+
+
+E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _fp4_value(code):
+    return (-1.0 if code & 8 else 1.0) * E2M1[code & 7]
+
+
+def _fp4_case(seed):
+    rng = np.random.default_rng(seed)
+    ca = rng.integers(0, 16, size=(64, 32)).astype(np.uint8)
+    cb = rng.integers(0, 16, size=(64, 32)).astype(np.uint8)
+    sa = rng.integers(124, 131, size=64).astype(np.uint32)
+    sb = rng.integers(124, 131, size=64).astype(np.uint32)
+    A = np.zeros((32, 64))
+    B = np.zeros((64, 32))
+    for l in range(64):
+        for i in range(32):
+            A[l % 32, 32 * (l // 32) + i] = _fp4_value(ca[l, i]) * 2.0 ** (int(sa[l]) - 127)
+            B[32 * (l // 32) + i, l % 32] = _fp4_value(cb[l, i]) * 2.0 ** (int(sb[l]) - 127)
+    C = A @ B
+    want = np.array([[C[8 * (r // 4) + 4 * (l // 32) + r % 4, l % 32] for r in range(16)]
+                     for l in range(64)])
+    pack = lambda c: np.ascontiguousarray(c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+    return pack(ca), pack(cb), sa, sb, want, rng
+
+
+def test_mfma_fp4_layout_and_scales(lib):
+    import torch
+    a, b, sa, sb, want, rng = _fp4_case(7)
+    bufs = [_dev(a), _dev(b), _dev(sa.astype(np.uint8)), _dev(sb.astype(np.uint8))]
+    c = torch.zeros((64, 16), dtype=torch.float32, device="cuda")
+    log("probe mfma_fp4")
+    assert lib.probe_mfma_fp4(*[t.data_ptr() for t in bufs], c.data_ptr(), None) == 0
+    _sync()
+    assert np.array_equal(c.cpu().numpy().astype(np.float64), want)
+    # scale byte 2 of a 32-bit register (other bytes hold noise)
+    wa = (rng.integers(0, 256, 64) | (sa << 16) | (rng.integers(0, 256, 64) << 24)).astype(np.uint32)
+    wb = (rng.integers(0, 256, 64) | (sb << 16) | (rng.integers(0, 256, 64) << 8)).astype(np.uint32)
+    bufs2 = [_dev(a), _dev(b), _dev(wa.view(np.int32)), _dev(wb.view(np.int32))]
+    c2 = torch.zeros((64, 16), dtype=torch.float32, device="cuda")
+    log("probe mfma_fp4_sel2")
+    assert lib.probe_mfma_fp4_sel2(*[t.data_ptr() for t in bufs2], c2.data_ptr(), None) == 0
+    _sync()
+    assert np.array_equal(c2.cpu().numpy().astype(np.float64), want)
+
+
+def _rne_e2m1(y):
+    """Nearest E2M1 magnitude code of y >= 0 (ties to the even code, saturating at 6)."""
+    best = None
+    for code in range(8):
+        dist = abs(E2M1[code] - y)
+        if best is None or dist < best[0] - 1e-12 or (abs(dist - best[0]) <= 1e-12 and code % 2 == 0):
+            best = (dist, code)
+    return best[1] if y <= 6.0 else 7
+
+
+def test_fp4_convert_rounding_saturation_and_byte_select(lib):
+    import torch
+    grid = np.array([0.0, 0.25, 0.26, 0.5, 0.74, 0.75, 0.76, 1.0, 1.25, 1.3, 1.5, 1.75, 1.8, 2.0,
+                     2.5, 2.6, 3.0, 3.5, 3.6, 4.0, 5.0, 5.1, 6.0, 7.0, 100.0, 1e-30, 0.124, 0.126],
+                    np.float32)
+    x = np.resize(grid, 128).astype(np.float32)
+    x[100:] = -x[100:]
+    scale = np.where(np.arange(64) % 3 == 0, 1.0, np.where(np.arange(64) % 3 == 1, 2.0, 0.5))
+    scale = scale.astype(np.float32)
+    bufs = [_dev(x), _dev(scale)]
+    out = torch.zeros(256, dtype=torch.int32, device="cuda")
+    log("probe cvt_fp4")
+    assert lib.probe_cvt_fp4(bufs[0].data_ptr(), bufs[1].data_ptr(), out.data_ptr(), None) == 0
+    _sync()
+    got = out.cpu().numpy().view(np.uint32).reshape(64, 4)
+    for l in range(64):
+        codes = []
+        for v in (x[2 * l], x[2 * l + 1]):
+            y = float(v) / float(scale[l])
+            mag = _rne_e2m1(abs(y))
+            codes.append(mag | (8 if np.signbit(v) else 0))
+        byte = codes[0] | (codes[1] << 4)
+        for sel in range(4):
+            want = (0xFFFFFFFF & ~(0xFF << (8 * sel))) | (byte << (8 * sel))
+            assert got[l, sel] == want, (l, sel, x[2 * l], x[2 * l + 1], scale[l], hex(got[l, sel]))
+
+
+def test_fp4_decode(lib):
+    import torch
+    src = np.arange(256, dtype=np.uint32).reshape(64, 4)
+    word = (src[:, 0] | (src[:, 1] << 8) | (src[:, 2] << 16) | (src[:, 3] << 24)).astype(np.uint32)
+    scale = np.where(np.arange(64) % 2 == 0, 1.0, 0.25).astype(np.float32)
+    bufs = [_dev(word.view(np.int32)), _dev(scale)]
+    out = torch.zeros(64 * 8, dtype=torch.float32, device="cuda")
+    log("probe dec_fp4")
+    assert lib.probe_dec_fp4(bufs[0].data_ptr(), bufs[1].data_ptr(), out.data_ptr(), None) == 0
+    _sync()
+    got = out.cpu().numpy().reshape(64, 4, 2)
+    for l in range(64):
+        for sel in range(4):
+            byte = int(src[l, sel])
+            assert got[l, sel, 0] == _fp4_value(byte & 15) * scale[l]
+            assert got[l, sel, 1] == _fp4_value(byte >> 4) * scale[l]
