@@ -99,7 +99,7 @@ int attn_fwd_mxfp4_ex(const uint8_t* q4, const uint8_t* qs, const uint8_t* k4, c
                       void* stream) {
   if (!q4 || !qs || !k4 || !ks || !vt4 || !vts || !o || !lse) return ATTN_EINVAL;
   if (!aligned(q4, 16) || !aligned(k4, 16) || !aligned(vt4, 16) || !aligned(o, 16) ||
-      !aligned(lse, 4))
+      !aligned(lse, 4) || !aligned(ks, 4))
     return ATTN_EINVAL;
   int st = check_common(B, Hq, Hkv, N, d, causal, scale);
   if (st != ATTN_OK) return st;
@@ -114,7 +114,8 @@ int attn_fwd_mxfp4_ex(const uint8_t* q4, const uint8_t* qs, const uint8_t* k4, c
   a.q4 = q4; a.qs = qs; a.k4 = k4; a.ks = ks; a.vt4 = vt4; a.vts = vts;
   a.o = o; a.lse = lse;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N = N; a.d = d; a.causal = causal;
-  a.c = scale * 1.4426950408889634f;
+  a.c = fabsf(scale) * 1.4426950408889634f;
+  a.qsign = scale < 0.f ? 0x88888888u : 0u;
   a.tau = op->tau;
   a.stats = op->stats;
   a.stream = stream;

@@ -370,47 +370,11 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n32 = lane & 31, h = lane >> 5;
 
-  // Workgroup -> (batch, kv head, query head in the group, query block).
-  // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).  When
-  // the kv heads split evenly over the XCDs, each XCD gets a contiguous range of
-  // kv heads, so the query heads sharing a kv head and all their query blocks
-  // read K/V through the same L2.  Within an XCD the dispatch order is: causal,
-  // query block outermost with the heaviest (longest key range) first, so the
-  // XCD's CUs take the longest work first and end together; non-causal, query
-  // heads of a group, then query blocks, then kv heads.
-  const int G_ = gridDim.x, w = blockIdx.x;
   const int group = Hq / Hkv;
-  const int nkv = (int)(G_ / (group * nqb));          // B * Hkv
-  int b, hkv, g, qb_rank;
-  if (nkv % 8 == 0) {
-    const int x = w % 8, r = w / 8;                   // XCD and dispatch rank within it
-    const int kv_per = nkv / 8;
-    int kvl;
-    if (CAUSAL) {
-      qb_rank = r / (kv_per * group);
-      const int t = r % (kv_per * group);
-      kvl = t / group;
-      g = t % group;
-    } else {
-      g = r % group;
-      qb_rank = (r / group) % nqb;
-      kvl = r / (group * nqb);
-    }
-    const int kv = x * kv_per + kvl;
-    hkv = kv % Hkv;
-    b = kv / Hkv;
-  } else {
-    // uneven split: plain order; causal, heaviest query blocks first across the grid
-    const int hw = nkv * group;
-    const int r = CAUSAL ? w % hw : w / nqb;
-    qb_rank = CAUSAL ? w / hw : w % nqb;
-    g = r % group;
-    const int kv = r / group;
-    hkv = kv % Hkv;
-    b = kv / Hkv;
-  }
+  const WorkItem wi = decode_workgroup(blockIdx.x, gridDim.x, Hkv, group, nqb, CAUSAL);
+  const int b = wi.b, hkv = wi.hkv, g = wi.g;
+  const int qb = CAUSAL ? (nqb - 1 - wi.qb_rank) : wi.qb_rank;
   const int hq = hkv * group + g;
-  const int qb = CAUSAL ? (nqb - 1 - qb_rank) : qb_rank;
 
   const int Q0 = qb * kBr;
   const int q0 = Q0 + wave * kRowsPerWave;

@@ -96,6 +96,392 @@ __global__ void quantize_cols_t_kernel(const float* __restrict__ x, uint8_t* __r
   scales[crow * nrb + rb] = (uint8_t)(e + 127);
 }
 
+
+// ---------------------------------------------------------------------------
+// Direct-P forward ("Hardware-Aware FP4 FlashAttention-4", section "1. Direct-P
+// para Inferencia Directa").
+//
+// Work split, staging and the software pipeline follow the bf16 kernel: one
+// workgroup = 8 waves x 32 query rows; 64-key tiles of K codes/scales and V^T
+// codes/scales are staged through registers into double-buffered LDS; pipeline
+// step j issues the PV product of tile j-1, the QK product of tile j+1 and the
+// Direct-P mapping of tile j.  All three products run on
+// v_mfma_scale_f32_32x32x64_f8f6f4 with E2M1 operands and E8M0 block scales:
+//   S^T  = K Q^T       A = K codes (32 keys x 64 d), B = Q codes (registers)
+//   O^T += V^T P^T     A = V^T codes (32 d x 64 keys), B = P codes (registers)
+//   L   += 1 P^T       A = all-ones codes: every accumulator row is the row sum
+// The last one is the consistent normaliser of the page's "Normalización
+// Consistente": the denominator is summed from exactly the rounded codes and
+// block scales that the PV product consumes, by the same hardware.
+//
+// Direct-P (same section, "Mapeo Directo"): the log-scores t = s * scale * log2(e)
+// go straight to E2M1 codes, one power-of-two scale per 32 keys, relative to an
+// integer reference max m (moved only when a tile's max exceeds m + tau):
+//   E    = floor(block max - m) - 2                 (block max in [4, 8) * 2^E)
+//   code = RNE_E2M1(2^(t - m - E))                  (saturating at 6)
+// The code is the E2M1 value nearest 2^x, i.e. x compared against the log2
+// midpoints of the E2M1 grid; on gfx950 the cheapest exact form of that
+// comparison is one v_exp_f32 and the hardware fp4 convert (two codes per
+// instruction), which is what is issued.  Because m is an integer, the codes do
+// not depend on which m the kernel held, and the rescale factors are exact
+// powers of two.
+
+constexpr int kMWaves = 8;
+constexpr int kMRows = 32;
+constexpr int kMBr = kMWaves * kMRows;   // 256 query rows per workgroup
+constexpr int kMBc = 64;                 // keys per tile
+constexpr int kMThreads = kMWaves * 64;
+constexpr int kMD = 128;                 // head dimension of this path
+constexpr int kCodeRow = kMD / 2;        // code bytes per Q/K row
+constexpr int kScaleRow = kMD / 32;      // scale bytes per Q/K row
+
+// Raw buffer descriptor over `bytes` bytes at `base`: loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mrsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// K row of the tile read by A-row m of 32-key MFMA block mb.  With this order the
+// S^T accumulator of lane half h holds exactly keys 32h .. 32h+31 of the tile
+// (register r of block mb: key 32h + 16mb + r), i.e. one whole P scale block.
+__device__ __forceinline__ int krow(int mb, int m) {
+  return 32 * ((m >> 2) & 1) + 16 * mb + 4 * (m >> 3) + (m & 3);
+}
+// 16-byte chunk swizzle of a K code row (64 B = 4 chunks): the 16 lanes the LDS
+// serves together read 16 distinct bank groups.
+__device__ __forceinline__ int kswz(int row) { return ((row >> 2) & 1) | (((row >> 5) & 1) << 1); }
+
+__device__ __forceinline__ i32x8 fp4_operand(u32x4 v) {
+  return i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+}
+
+struct MBuf {
+  u32x4 kcode[kMBc * kCodeRow / 16];     // 256 units: unit(row, c) = row*4 + (c ^ kswz(row))
+  u32x4 vcode[kMD * 2];                  // 256 units: unit(col, h) = col*2 + (h ^ ((col>>3)&1))
+  uint32_t kscale[kMBc];                 // 4 scale bytes per key row
+  uint8_t vscale[kMD * 2];               // byte (col*2 + h): scale of key block h of column col
+};
+
+struct MStage {
+  u32x4 codes;     // tid < 256: K codes (row tid/4, chunk tid%4); else V^T codes (col, half)
+  uint32_t sc;     // tid < 64: K scales of row tid; 64 <= tid < 192: V scales of col tid-64
+};
+
+// Direct-P mapping of one 64-key tile for this lane (32 keys: its P scale block).
+// Returns whether any row of the wave moved its reference max (then O and the
+// row sum must be multiplied by alpha before the next PV product).
+template <bool CAUSAL, bool MASK>
+__device__ __forceinline__ bool directp_tile(const f32x16 (&s)[2], u32x4& codes, uint32_t& sbyte,
+                                             float& m, float& alpha, int kv0, int qi, int N,
+                                             float c, float tau, int h) {
+  const float NEG_INF = -__builtin_inff();
+  auto visible = [&](int mb, int r) {
+    const int key = kv0 + 32 * h + 16 * mb + r;
+    return key < N && (!CAUSAL || key <= qi);
+  };
+  float bm = NEG_INF;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float v = (!MASK || visible(mb, r)) ? s[mb][r] : NEG_INF;
+      bm = fmaxf(bm, v);
+    }
+  const float Mb = (bm == NEG_INF) ? NEG_INF : bm * c;      // this lane's block max (log2)
+  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(Mb), __float_as_uint(Mb), false,
+                                             false);
+  const float mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));   // tile row max
+
+  const bool any = __ballot(mx > m + tau) != 0;
+  const float m_new = any ? fmaxf(m, __builtin_ceilf(mx)) : m;
+  alpha = (m_new == NEG_INF) ? 1.f
+          : (m == NEG_INF ? 0.f : __builtin_ldexpf(1.f, (int)(m - m_new)));
+  m = m_new;
+
+  bool flush = (Mb == NEG_INF) || (m_new == NEG_INF);
+  float e = flush ? 0.f : __builtin_floorf(Mb - m_new) - 2.f;
+  flush = flush || e < -127.f;
+  e = flush ? 0.f : e;
+  const float bias = flush ? __builtin_inff() : m_new + e;
+  sbyte = (uint32_t)((int)e + 127);
+
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    float y[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int el = 8 * w + q;                // element index = key - 32h = 16mb + r
+      const int mb = el >> 4, r = el & 15;
+      float x = __builtin_fmaf(s[mb][r], c, -bias);
+      if constexpr (MASK) x = visible(mb, r) ? x : NEG_INF;
+      y[q] = __builtin_amdgcn_exp2f(x);
+    }
+    uint32_t word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[0], y[1], 1.0f, 0);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, y[2], y[3], 1.0f, 1);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, y[4], y[5], 1.0f, 2);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, y[6], y[7], 1.0f, 3);
+    codes[w] = word;
+  }
+  return any;
+}
+
+template <bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(kMThreads, kMThreads), amdgpu_waves_per_eu(2, 2)))
+void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict__ QS,
+                      const uint8_t* __restrict__ K4, const uint8_t* __restrict__ KS,
+                      const uint8_t* __restrict__ VT4, const uint8_t* __restrict__ VTS,
+                      float* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int N,
+                      int nqb, float c, float tau, uint32_t qsign,
+                      unsigned long long* __restrict__ stats) {
+  __shared__ MBuf buf[2];
+  const float NEG_INF = -__builtin_inff();
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n32 = lane & 31, h = lane >> 5;
+
+  const int group = Hq / Hkv;
+  const WorkItem wi = decode_workgroup(blockIdx.x, gridDim.x, Hkv, group, nqb, CAUSAL);
+  const int b = wi.b, hkv = wi.hkv, g = wi.g;
+  const int qb = CAUSAL ? (nqb - 1 - wi.qb_rank) : wi.qb_rank;
+  const int hq = hkv * group + g;
+  const int Q0 = qb * kMBr;
+  const int q0 = Q0 + wave * kMRows;
+  const int qi = q0 + n32;
+
+  const size_t qhead = (size_t)(b * Hq + hq) * N;
+  const size_t khead = (size_t)(b * Hkv + hkv) * N;
+  const uint8_t* K4h = K4 + khead * kCodeRow;
+  const uint8_t* KSh = KS + khead * kScaleRow;
+  const uint8_t* VT4h = VT4 + khead * kCodeRow;       // [kMD][N/2] per head
+  const uint8_t* VTSh = VTS + khead * kScaleRow;      // [kMD][N/32] per head
+  const int nvb = N / 32;                             // V scale bytes per column
+  const __amdgpu_buffer_rsrc_t rvt = mrsrc(VT4h, kMD * (N / 2));
+  const __amdgpu_buffer_rsrc_t rvs = mrsrc(VTSh, kMD * nvb);
+
+  // Q codes: lane holds d elements 64kc + 32h .. +31 of query qi (B operand of QK);
+  // byte 2kc of qsc is the scale of that block.
+  u32x4 qc[2];
+  uint32_t qsc;
+  {
+    const int qr = min(qi, N - 1);
+    const uint8_t* qrow = Q4 + (qhead + qr) * kCodeRow;
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) qc[kc] = *(const u32x4*)(qrow + 32 * kc + 16 * h) ^ qsign;
+    const uint8_t* srow = QS + (qhead + qr) * kScaleRow;
+    qsc = ((uint32_t)srow[0] | ((uint32_t)srow[1] << 8) | ((uint32_t)srow[2] << 16) |
+           ((uint32_t)srow[3] << 24)) >> (8 * h);
+  }
+
+  f32x16 acc[kMD / 32], lacc;
+#pragma unroll
+  for (int i = 0; i < kMD / 32; ++i) acc[i] = zero16();
+  lacc = zero16();
+  float m = NEG_INF;
+  unsigned n_steps = 0, n_rescales = 0;
+  bool first = true;
+
+  const int kv_end = CAUSAL ? min(N, Q0 + kMBr) : N;
+  const int n = (kv_end + kMBc - 1) / kMBc;
+  const int wave_end = CAUSAL ? min(N, q0 + kMRows) : N;
+  const bool wave_live = q0 < N;
+  auto active = [&](int j) { return wave_live && j * kMBc < wave_end; };
+
+  // Stage t (read by pipeline step t from buffer t & 1) holds K tile t+1 and V tile t-1.
+  auto load_stage = [&](MStage& sg, int t) {
+    if (tid < 256) {
+      if (t + 1 < n) {
+        const int kv0 = (t + 1) * kMBc;
+        const __amdgpu_buffer_rsrc_t rk =
+            mrsrc(K4h + (size_t)kv0 * kCodeRow, (N - kv0) * kCodeRow);
+        sg.codes = __builtin_amdgcn_raw_buffer_load_b128(rk, (tid >> 2) * kCodeRow + (tid & 3) * 16,
+                                                         0, 0);
+      }
+    } else if (t >= 1 && t - 1 < n) {
+      const int kv0 = (t - 1) * kMBc, u = tid - 256;
+      sg.codes = __builtin_amdgcn_raw_buffer_load_b128(
+          rvt, (u >> 1) * (N / 2) + kv0 / 2 + 16 * (u & 1), 0, 0);
+    }
+    if (tid < 64) {
+      if (t + 1 < n) {
+        const int kv0 = (t + 1) * kMBc;
+        const __amdgpu_buffer_rsrc_t rs =
+            mrsrc(KSh + (size_t)kv0 * kScaleRow, (N - kv0) * kScaleRow);
+        sg.sc = __builtin_amdgcn_raw_buffer_load_b32(rs, tid * kScaleRow, 0, 0);
+      }
+    } else if (tid < 64 + kMD) {
+      if (t >= 1 && t - 1 < n) {
+        const int kv0 = (t - 1) * kMBc, col = tid - 64;
+        const uint32_t b0 = __builtin_amdgcn_raw_buffer_load_b8(rvs, col * nvb + kv0 / 32, 0, 0);
+        // a key block past N gets a neutral scale (its codes meet zero P codes)
+        const uint32_t b1 =
+            (kv0 + 32 < N) ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(
+                                 rvs, col * nvb + kv0 / 32 + 1, 0, 0)
+                           : 127u;
+        sg.sc = b0 | (b1 << 8);
+      }
+    }
+  };
+  auto store_stage = [&](const MStage& sg, int t) {
+    MBuf& bb = buf[t & 1];
+    if (tid < 256) {
+      if (t + 1 < n) {
+        const int row = tid >> 2, cc = tid & 3;
+        bb.kcode[row * 4 + (cc ^ kswz(row))] = sg.codes;
+      }
+    } else if (t >= 1 && t - 1 < n) {
+      const int u = tid - 256, col = u >> 1, hh = u & 1;
+      bb.vcode[col * 2 + (hh ^ ((col >> 3) & 1))] = sg.codes;
+    }
+    if (tid < 64) {
+      if (t + 1 < n) bb.kscale[tid] = sg.sc;
+    } else if (tid < 64 + kMD) {
+      if (t >= 1 && t - 1 < n) {
+        const int col = tid - 64;
+        bb.vscale[col * 2] = (uint8_t)(sg.sc & 0xFF);
+        bb.vscale[col * 2 + 1] = (uint8_t)(sg.sc >> 8);
+      }
+    }
+  };
+
+  const int kr0 = krow(0, n32), kr1 = krow(1, n32);
+  const uint32_t ONES = 0x22222222u;   // E2M1 code 2 (= 1.0) in every nibble
+
+  // MFMAs of one pipeline step: PV + row sum of the previous tile (P codes pp,
+  // P scale byte ep, V^T from bb), then QK of the next tile into sn (K from bb).
+  auto mfmas = [&](const MBuf& bb, const u32x4& pp, uint32_t ep, bool pv, bool qk,
+                   f32x16 (&sn)[2]) {
+    if (pv) {
+      const i32x8 bp = fp4_operand(pp);
+#pragma unroll
+      for (int cb = 0; cb < kMD / 32; ++cb) {
+        const int col = 32 * cb + n32;
+        const u32x4 va = bb.vcode[col * 2 + (h ^ ((col >> 3) & 1))];
+        const int vs = bb.vscale[col * 2 + h];
+        acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp4_operand(va), bp, acc[cb], 4,
+                                                                  4, 0, vs, 0, (int)ep);
+      }
+      lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          fp4_operand(u32x4{ONES, ONES, ONES, ONES}), bp, lacc, 4, 4, 0, 127, 0, (int)ep);
+    }
+    if (qk) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int row = mb ? kr1 : kr0;
+        const int ksc = (int)(bb.kscale[row] >> (8 * h));
+        // d elements 0..63 (scale byte 0 of the shifted scale words), then 64..127 (byte 2)
+        const u32x4 ka0 = bb.kcode[row * 4 + ((0 + h) ^ kswz(row))];
+        const u32x4 ka1 = bb.kcode[row * 4 + ((2 + h) ^ kswz(row))];
+        f32x16 a = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            fp4_operand(ka0), fp4_operand(qc[0]), zero16(), 4, 4, 0, ksc, 0, (int)qsc);
+        a = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp4_operand(ka1), fp4_operand(qc[1]), a,
+                                                            4, 4, 2, ksc, 2, (int)qsc);
+        sn[mb] = a;
+      }
+    }
+  };
+
+  // ---- prologue: K tile 0 -> buffer 1; stage 0 -> buffer 0; stage 1 in registers ----
+  MStage stg;
+  {
+    MStage s0;
+    if (tid < 256) {
+      const __amdgpu_buffer_rsrc_t rk = mrsrc(K4h, N * kCodeRow);
+      s0.codes = __builtin_amdgcn_raw_buffer_load_b128(rk, (tid >> 2) * kCodeRow + (tid & 3) * 16,
+                                                       0, 0);
+    }
+    if (tid < 64)
+      s0.sc = __builtin_amdgcn_raw_buffer_load_b32(mrsrc(KSh, N * kScaleRow), tid * kScaleRow, 0, 0);
+    load_stage(stg, 0);
+    if (tid < 256) {
+      const int row = tid >> 2, cc = tid & 3;
+      buf[1].kcode[row * 4 + (cc ^ kswz(row))] = s0.codes;
+    }
+    if (tid < 64) buf[1].kscale[tid] = s0.sc;
+    store_stage(stg, 0);
+    // no V tile precedes tile 0: zero codes, neutral scales
+    if (tid >= 256) buf[0].vcode[tid - 256] = u32x4{0u, 0u, 0u, 0u};
+    else buf[0].vscale[tid] = 127;
+  }
+  load_stage(stg, 1);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  f32x16 s_cur[2], s_nxt[2];
+  u32x4 p_prev = u32x4{0u, 0u, 0u, 0u}, p_cur;
+  uint32_t e_prev = 127u, e_cur = 127u;
+  mfmas(buf[1], p_prev, e_prev, false, true, s_cur);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  bool any_prev = false;
+  float alpha_prev = 1.f;
+  const int n_full = CAUSAL ? min(Q0, N) / kMBc : N / kMBc;
+  for (int j = 0; j < n; ++j) {
+    if (any_prev) {
+#pragma unroll
+      for (int i = 0; i < kMD / 32; ++i) acc[i] *= alpha_prev;
+      lacc *= alpha_prev;
+    }
+    mfmas(buf[j & 1], p_prev, e_prev, j >= 1, j + 1 < n, s_nxt);
+    float alpha;
+    bool any;
+    if (j >= n_full)
+      any = directp_tile<CAUSAL, true>(s_cur, p_cur, e_cur, m, alpha, j * kMBc, qi, N, c, tau, h);
+    else
+      any = directp_tile<CAUSAL, false>(s_cur, p_cur, e_cur, m, alpha, j * kMBc, qi, N, c, tau, h);
+    any_prev = any;
+    alpha_prev = alpha;
+    if (active(j)) {
+      if (!first) {
+        ++n_steps;
+        n_rescales += any ? 1u : 0u;
+      }
+      first = false;
+    }
+    store_stage(stg, j + 1);
+    if (j + 2 <= n) load_stage(stg, j + 2);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) s_cur[i] = s_nxt[i];
+    p_prev = p_cur;
+    e_prev = e_cur;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+  if (any_prev) {
+#pragma unroll
+    for (int i = 0; i < kMD / 32; ++i) acc[i] *= alpha_prev;
+    lacc *= alpha_prev;
+  }
+  mfmas(buf[n & 1], p_prev, e_prev, true, false, s_nxt);
+
+  // ---- epilogue: O = acc / l, LSE = ln2 * m + ln l ----
+  const float l = lacc[0];
+  if (qi < N) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float* Orow = O + (qhead + qi) * kMD;
+#pragma unroll
+    for (int cb = 0; cb < kMD / 32; ++cb)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        f32x4 out = {acc[cb][4 * a4] * inv, acc[cb][4 * a4 + 1] * inv, acc[cb][4 * a4 + 2] * inv,
+                     acc[cb][4 * a4 + 3] * inv};
+        *(f32x4*)(Orow + cb * 32 + 8 * a4 + 4 * h) = out;
+      }
+    if (h == 0)
+      LSE[qhead + qi] = l > 0.f ? (m + __builtin_log2f(l)) * kLn2 : -__builtin_inff();
+  }
+  if (stats != nullptr && lane == 0 && wave_live) {
+    atomicAdd(stats, (unsigned long long)n_steps);
+    atomicAdd(stats + 1, (unsigned long long)n_rescales);
+  }
+}
+
+template <bool CAUSAL>
+hipError_t launch_mxfp4(const Mxfp4Args& a) {
+  const int nqb = (a.N + kMBr - 1) / kMBr;
+  const long long grid = (long long)a.B * a.Hq * nqb;
+  if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fwd_mxfp4_kernel<CAUSAL>), dim3((unsigned)grid), dim3(kMThreads), 0,
+                     (hipStream_t)a.stream, a.q4, a.qs, a.k4, a.ks, a.vt4, a.vts, a.o, a.lse,
+                     a.Hq, a.Hkv, a.N, nqb, a.c, a.tau, a.qsign, a.stats);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_quantize_rows(const float* x, uint8_t* codes, uint8_t* scales, long long rows,
@@ -121,8 +507,8 @@ hipError_t launch_quantize_cols_t(const float* x, uint8_t* codes, uint8_t* scale
 }
 
 hipError_t launch_fwd_mxfp4(const Mxfp4Args& a) {
-  (void)a;
-  return hipErrorNotSupported;
+  if (a.d != kMD) return hipErrorNotSupported;
+  return a.causal ? launch_mxfp4<true>(a) : launch_mxfp4<false>(a);
 }
 
 }  // namespace attn

@@ -27,8 +27,9 @@ struct Mxfp4Args {
   float* o;
   float* lse;
   int B, Hq, Hkv, N, d, causal;
-  float c;          // scale * log2(e), any sign
+  float c;          // |scale| * log2(e): scores to log2 units
   float tau;
+  uint32_t qsign;   // 0x88888888 flips the sign of every E2M1 Q element (scale < 0)
   unsigned long long* stats;
   void* stream;
 };

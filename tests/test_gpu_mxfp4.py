@@ -1,0 +1,185 @@
+"""MXFP4 path on the GPU (through the C ABI) against the float64 oracle.
+
+* The quantisation kernels must reproduce the oracle's OCP MX codes and scales
+  bit for bit (byte work: exact equality).
+* The Direct-P forward is compared with the oracle's step-by-step emulation of
+  the same quantisation (oracle.mx.directp_attention) on the dequantised
+  operands: relative RMS of O <= 0.1 (the stated tolerance for this path).
+  Because the emulation follows the same integer-reference rule, the two agree
+  far closer than that unless an exponential lands on an E2M1 midpoint; the
+  measured error is printed.
+* Exact invariants: V = 1 gives O = 1 (the normaliser is summed from the same
+  codes and scales as PV); Q = 0 gives the mean of the dequantised V rows.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import mx
+from gpu_util import MXFP4_O_RELRMS, cuda_ok, log, rel_rms, to_dev_f32
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not cuda_ok(), reason="needs a GPU")]
+
+
+def _pack(codes):
+    """One 4-bit code per element along the last axis -> bytes (element 2i in the low nibble)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    return (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+
+
+def _gpu_quantize(q, k, v):
+    import exact_attention_forward_tiled_amd as fa
+    qd, kd, vd = to_dev_f32(q), to_dev_f32(k), to_dev_f32(v)
+    q4, qs = fa.quantize_mxfp4_rows(qd)
+    k4, ks = fa.quantize_mxfp4_rows(kd)
+    vt4, vts = fa.quantize_mxfp4_cols_t(vd)
+    return q4, qs, k4, ks, vt4, vts
+
+
+def _run(q, k, v, causal, scale, **kw):
+    import torch
+    import exact_attention_forward_tiled_amd as fa
+    q4, qs, k4, ks, vt4, vts = _gpu_quantize(q, k, v)
+    B, Hq, N, d = q.shape
+    o = torch.full((B, Hq, N, d), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((B, Hq, N), float("nan"), dtype=torch.float32, device="cuda")
+    fa.fwd_mxfp4(q4, qs, k4, ks, vt4, vts, causal=causal, scale=scale, out=(o, lse), **kw)
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), lse.cpu().numpy()
+
+
+def _case(seed, B, Hq, Hkv, N, d=128, sigma=1.0):
+    rng = np.random.default_rng(seed)
+    q = (rng.standard_normal((B, Hq, N, d)) * sigma).astype(np.float32)
+    k = (rng.standard_normal((B, Hkv, N, d)) * sigma).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, N, d)).astype(np.float32)
+    return q, k, v
+
+
+def test_quantizers_bit_exact():
+    import torch
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((3, 96, 128)).astype(np.float32)
+    x[0, 5, 32:64] = 0.0                                  # an all-zero block
+    x[1, 7, :32] = np.float32(2.0 ** -3) * np.array(     # exact ties in block units
+        [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 4.0] * 4, np.float32)
+    x[2, 9, :32] *= 1e6                                   # large exponents
+    x[2, 10, :32] *= 1e-30                                # tiny exponents
+    import exact_attention_forward_tiled_amd as fa
+    xd = to_dev_f32(x)
+    c, s = fa.quantize_mxfp4_rows(xd)
+    torch.cuda.synchronize()
+    rc, rs = mx.quantize(x.astype(np.float64), axis=-1)
+    assert np.array_equal(c.cpu().numpy(), _pack(rc))
+    assert np.array_equal(s.cpu().numpy(), rs)
+    ct, st = fa.quantize_mxfp4_cols_t(xd)
+    torch.cuda.synchronize()
+    rct, rst = mx.quantize(x.astype(np.float64), axis=-2)        # blocks along rows
+    assert np.array_equal(ct.cpu().numpy(), _pack(np.swapaxes(rct, -1, -2)))
+    assert np.array_equal(st.cpu().numpy(), np.swapaxes(rst, -1, -2))
+
+
+def _reference(q, k, v, causal, scale):
+    t = mx.quantize_inputs(q, k, v)
+    return mx.directp_attention(t["q"], t["k"], t["v"], causal, scale)
+
+
+SMALL = [
+    # B, Hq, Hkv, N, causal
+    (1, 2, 2, 256, False),
+    (1, 2, 2, 256, True),
+    (1, 1, 1, 32, False),
+    (1, 2, 2, 96, True),
+    (2, 4, 2, 160, False),
+    (1, 8, 2, 512, True),
+    (1, 3, 3, 320, False),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "B%dHq%dHkv%dN%d%s" % (
+    c[0], c[1], c[2], c[3], "c" if c[4] else "n"))
+@pytest.mark.parametrize("tau", [8.0, 0.0])
+def test_directp_small(case, tau):
+    B, Hq, Hkv, N, causal = case
+    q, k, v = _case(sum(case[:4]) + 3, B, Hq, Hkv, N)
+    scale = 1.0 / math.sqrt(128)
+    log(f"case {case} tau {tau}")
+    o, lse = _run(q, k, v, causal, scale, tau=tau)
+    ro, rl = _reference(q, k, v, causal, scale)
+    assert not np.isnan(o).any() and not np.isnan(lse).any()
+    r = rel_rms(o, ro)
+    e = float(np.max(np.abs(lse - rl)))
+    log(f"  relRMS(O)={r:.3e} max|dLSE|={e:.3e}")
+    assert r <= MXFP4_O_RELRMS, r
+    assert e <= 0.05, e
+
+
+def test_directp_scale_sign_and_large_logits():
+    q, k, v = _case(21, 1, 2, 2, 192, sigma=3.0)
+    for scale in (-0.2, 0.3):
+        log(f"scale {scale}")
+        o, lse = _run(q, k, v, False, scale)
+        ro, rl = _reference(q, k, v, False, scale)
+        r = rel_rms(o, ro)
+        log(f"  relRMS(O)={r:.3e} max|dLSE|={float(np.max(np.abs(lse - rl))):.3e}")
+        assert r <= MXFP4_O_RELRMS
+
+
+def test_directp_constant_v_gives_one():
+    q, k, _ = _case(22, 1, 4, 2, 256, sigma=2.0)
+    v = np.ones((1, 2, 256, 128), np.float32)
+    for causal in (False, True):
+        o, _ = _run(q, k, v, causal, 0.09)
+        assert np.max(np.abs(o - 1.0)) < 1e-6
+
+
+def test_directp_zero_query_is_mean_of_v():
+    _, k, v = _case(23, 1, 2, 2, 128)
+    q = np.zeros((1, 2, 128, 128), np.float32)
+    t = mx.quantize_inputs(q, k, v)
+    o, lse = _run(q, k, v, False, 0.1)
+    ref = np.broadcast_to(t["v"].mean(axis=2, keepdims=True), o.shape)
+    assert rel_rms(o, ref) < 1e-5
+    assert np.max(np.abs(lse - math.log(128))) < 1e-5
+
+
+def test_directp_gqa_equals_repeated_heads():
+    q, k, v = _case(24, 1, 8, 2, 192)
+    for causal in (False, True):
+        o1, l1 = _run(q, k, v, causal, 0.09)
+        o2, l2 = _run(q, np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1), causal, 0.09)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_directp_workload_sampled_rows():
+    """The full-size MXFP4 workload: sampled rows of several heads against the emulation, and
+    the cosine against exact attention on the unquantised inputs (context only)."""
+    w = synth.workload(5)
+    q, k, v = w.make()
+    log(f"workload {w.name}")
+    o, lse = _run(q, k, v, w.causal, w.scale)
+    assert not np.isnan(o).any() and not np.isnan(lse).any()
+    rng = np.random.default_rng(5)
+    heads = [0, w.Hq - 1, int(rng.integers(w.Hq))]
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 63, 64, w.N - 1], rng.integers(0, w.N, 29)]))
+    got, ref, exact = [], [], []
+    for h in heads:
+        t = mx.quantize_inputs(q[:, h:h + 1, rows], k[:, h:h + 1], v[:, h:h + 1])
+        ro, rl, _ = mx.directp_rows(t["q"][0, 0], t["k"][0, 0], t["v"][0, 0], rows, False, w.scale)
+        got.append(o[0, h, rows])
+        ref.append(ro)
+        eo, _ = oracle.attention(q[:, h:h + 1, rows].astype(np.float64),
+                                 k[:, h:h + 1].astype(np.float64),
+                                 v[:, h:h + 1].astype(np.float64), False, w.scale)
+        exact.append(eo[0, 0])
+        assert np.max(np.abs(lse[0, h, rows] - rl)) < 0.05
+    got, ref, exact = (np.concatenate(x) for x in (got, ref, exact))
+    r = rel_rms(got, ref)
+    cos = np.mean(np.sum(got * exact, -1) / np.linalg.norm(got, axis=-1) /
+                  np.linalg.norm(exact, axis=-1))
+    log(f"  relRMS(O) vs emulation {r:.3e}; mean row cosine vs unquantised exact {cos:.4f}")
+    assert r <= MXFP4_O_RELRMS
