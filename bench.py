@@ -34,24 +34,29 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attn fwd TFLOP/s (4·B·H·N²·d, causal halved) and % of MI355X MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6      # dense bf16 MFMA, 256 CUs x 2.4 GHz x 4096 flop/clk
-KERNEL_SOURCES = ["exact_attention_forward_tiled_amd/csrc/attn_fwd_bf16.hip",
-                  "exact_attention_forward_tiled_amd/csrc/common.h",
-                  "exact_attention_forward_tiled_amd/csrc/exp2_poly.h"]
+PEAK_FP4_TFLOPS = 10066.3      # dense MXFP4 MFMA, 256 CUs x 2.4 GHz x 16384 flop/clk
+KERNEL_SOURCES = {
+    "bf16": ["exact_attention_forward_tiled_amd/csrc/attn_fwd_bf16.hip",
+             "exact_attention_forward_tiled_amd/csrc/common.h",
+             "exact_attention_forward_tiled_amd/csrc/exp2_poly.h"],
+    "mxfp4": ["exact_attention_forward_tiled_amd/csrc/attn_mxfp4.hip",
+              "exact_attention_forward_tiled_amd/csrc/common.h"],
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_hash():
+def kernel_hash(fmt="bf16"):
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[fmt]:
         with open(os.path.join(ROOT, p), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload_name):
+def load_traffic(workload_name, fmt="bf16"):
     """HBM bytes per launch from committed rocprofv3 counter runs, if taken on this kernel."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
@@ -59,7 +64,7 @@ def load_traffic(workload_name):
             rec = json.load(fh)[workload_name]
     except (OSError, KeyError, ValueError):
         return None
-    if rec.get("kernel_hash") != kernel_hash():
+    if rec.get("kernel_hash") != kernel_hash(fmt):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -88,6 +93,36 @@ class Workload:
     def launch(self, stats=None):
         self.fa.fwd(self.q, self.k, self.v, causal=self.w.causal, scale=self.w.scale, tau=self.tau,
                     exp_mode=self.exp_mode, stats=stats, out=(self.o, self.lse))
+
+
+class Mxfp4Workload:
+    """MXFP4 Direct-P workload: fp32 draws quantised on the GPU once (untimed), then the
+    forward on the resident codes and scales."""
+
+    def __init__(self, w, tau):
+        import numpy as np
+        import torch
+        import exact_attention_forward_tiled_amd as fa
+        self.w = w
+        q, k, v = (torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in w.make())
+        self.q4, self.qs = fa.quantize_mxfp4_rows(q)
+        self.k4, self.ks = fa.quantize_mxfp4_rows(k)
+        self.vt4, self.vts = fa.quantize_mxfp4_cols_t(v)
+        torch.cuda.synchronize()
+        del q, k, v
+        self.o = torch.empty((w.B, w.Hq, w.N, w.d), dtype=torch.float32, device="cuda")
+        self.lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device="cuda")
+        self.fa = fa
+        self.tau = tau
+
+    def launch(self, stats=None):
+        self.fa.fwd_mxfp4(self.q4, self.qs, self.k4, self.ks, self.vt4, self.vts,
+                          causal=self.w.causal, scale=self.w.scale, tau=self.tau, stats=stats,
+                          out=(self.o, self.lse))
+
+
+def make_workload(w, exp_mode, tau):
+    return Workload(w, exp_mode, tau) if w.fmt == "bf16" else Mxfp4Workload(w, tau)
 
 
 def time_workload(wl, steps, warmup, warmup_seconds):
@@ -144,17 +179,34 @@ def skip_ratio(wl):
 
 
 def cpu_baseline(w, budget_s=10.0):
-    """The float64 oracle, as it stands, on whole (batch, head) slices of the same workload."""
+    """The float64 oracle, as it stands, on whole (batch, head) slices of the same workload
+    (the MXFP4 workload runs the Direct-P emulation on the quantised operands)."""
     import oracle
     import synth
     from threadpoolctl import threadpool_info
-    qb, kb, vb = w.make()
-    q, k, v = (synth.bf16_bits_to_f64(x) for x in (qb, kb, vb))
     heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    if w.fmt == "bf16":
+        qb, kb, vb = w.make()
+        q, k, v = (synth.bf16_bits_to_f64(x) for x in (qb, kb, vb))
+
+        def one(b, h):
+            oracle.attention_head(q, k, v, w.causal, w.scale, b, h)
+    else:
+        import numpy as np
+        q, k, v = w.make()
+        group = w.Hq // w.Hkv
+
+        def one(b, h):
+            t = oracle.mx.quantize_inputs(q[b:b + 1, h:h + 1], k[b:b + 1, h // group:h // group + 1],
+                                          v[b:b + 1, h // group:h // group + 1])
+            for r0 in range(0, w.N, 256):
+                rows = np.arange(r0, min(w.N, r0 + 256))
+                oracle.mx.directp_rows(t["q"][0, 0, rows], t["k"][0, 0], t["v"][0, 0], rows,
+                                       w.causal, w.scale)
     done, t0 = 0, time.perf_counter()
     while time.perf_counter() - t0 < budget_s:
         b, h = heads[done % len(heads)]
-        oracle.attention_head(q, k, v, w.causal, w.scale, b, h)
+        one(b, h)
         done += 1
     el = time.perf_counter() - t0
     flops = w.flops * done / len(heads)
@@ -206,12 +258,9 @@ def main():
         return
 
     w = synth.workload(args.config)
-    if w.fmt != "bf16":
-        print("bench.py: the headline line times a bf16 workload", file=sys.stderr)
-        sys.exit(2)
 
     if args.mode == "launch":
-        wl = Workload(w, args.exp, args.tau)
+        wl = make_workload(w, args.exp, args.tau)
         for _ in range(args.steps):
             wl.launch()
         torch.cuda.synchronize()
@@ -219,7 +268,7 @@ def main():
         return
 
     log(f"timing {w.name}: ramp {args.warmup_seconds} s, warmup {args.warmup}, steps {args.steps}")
-    wl = Workload(w, args.exp, args.tau)
+    wl = make_workload(w, args.exp, args.tau)
     t = time_workload(wl, args.steps, args.warmup, args.warmup_seconds)
     skip = skip_ratio(wl)
     del wl
@@ -230,10 +279,12 @@ def main():
     extra = {"kernel_ms_avg": t["kernel_ms_avg"], "kernel_ms_median": t["kernel_ms_median"],
              "kernel_ms_min": t["kernel_ms_min"], "kernel_ms_max": t["kernel_ms_max"],
              "pct_of_bf16_peak": 100.0 * t["tflops"] / PEAK_BF16_TFLOPS,
-             "skip_ratio": skip, "exp_mode": args.exp, "tau": args.tau,
-             "kernel_hash": kernel_hash(), "device": props.name,
+             "skip_ratio": skip, "exp_mode": args.exp if w.fmt == "bf16" else "directp",
+             "tau": args.tau, "kernel_hash": kernel_hash(w.fmt), "device": props.name,
              "compute_units": props.multi_processor_count, "workloads": {}}
-    if args.compare_exp:
+    if w.fmt != "bf16":
+        extra["pct_of_fp4_peak"] = 100.0 * t["tflops"] / PEAK_FP4_TFLOPS
+    if args.compare_exp and w.fmt == "bf16":
         other = "poly" if args.exp == "hw" else "hw"
         log(f"timing {w.name} with exp mode {other}")
         wl = Workload(w, other, args.tau)
@@ -243,10 +294,10 @@ def main():
             "tflops": round(t2["tflops"], 2), "ms": round(t2["ms_per_step"], 4)}
     for idx in [int(x) for x in args.extra.split(",") if x.strip()]:
         wx = synth.workload(idx)
-        if wx.fmt != "bf16" or idx == args.config:
+        if idx == args.config:
             continue
         log(f"timing {wx.name}")
-        wl = Workload(wx, args.exp, args.tau)
+        wl = make_workload(wx, args.exp, args.tau)
         tx = time_workload(wl, max(5, args.steps // 2), args.warmup, args.warmup_seconds)
         sx = skip_ratio(wl)
         del wl
@@ -256,12 +307,16 @@ def main():
             "kernel_ms_avg": round(tx["kernel_ms_avg"], 4),
             "pct_of_bf16_peak": round(100.0 * tx["tflops"] / PEAK_BF16_TFLOPS, 2),
             "skip_ratio": sx}
+        if wx.fmt != "bf16":
+            extra["workloads"][wx.name]["pct_of_fp4_peak"] = round(
+                100.0 * tx["tflops"] / PEAK_FP4_TFLOPS, 2)
 
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on the host")
         cpu = cpu_baseline(w)
 
+    peak = PEAK_BF16_TFLOPS if w.fmt == "bf16" else PEAK_FP4_TFLOPS
     line = {
         "metric": METRIC,
         "value": round(t["tflops"], 3),
@@ -273,12 +328,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if w.fmt == "bf16" else "mxfp4",
         "data": "synthetic",
         "config": dict(w.describe()),
-        "roofline": {"bound": "mfma", "achieved": round(kernel_tf, 3), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(kernel_tf / PEAK_BF16_TFLOPS, 4),
-                     "traffic": load_traffic(w.name)},
+        "roofline": {"bound": "mfma", "achieved": round(kernel_tf, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(kernel_tf / peak, 4),
+                     "traffic": load_traffic(w.name, w.fmt)},
         "cpu_baseline": cpu,
         "extra": extra,
     }
