@@ -209,11 +209,22 @@ struct StepShape {
   static constexpr int NPV = PV ? 4 * (D / 32) : 0;
   static constexpr int NQK = QK ? 2 * (D / 16) : 0;
   static constexpr int NOPS = NPV + NQK;
-  // softmax slot plan: 0-3 row max, 4 threshold test, 5 new max, then score pairs
-  static constexpr int PAIR0 = 6;
-  static constexpr int PAIRS_PER_SLOT = (16 + (NOPS - PAIR0 - 2)) / (NOPS - PAIR0 - 1);
-  static constexpr int LSUM = PAIR0 + (16 + PAIRS_PER_SLOT - 1) / PAIRS_PER_SLOT;
-  static_assert(!(PV && QK) || LSUM < NOPS, "softmax must fit in the MFMA slots");
+  // softmax slot plan, spread evenly over the MFMA slots: row max over 32 scores in
+  // MAXS slots, threshold test, new reference max, the 16 score pairs over the
+  // following slots, the row-sum update in the last slot; the staging of the next
+  // K/V stage sits in the middle slot.
+  static constexpr int MAXS = NOPS >= 32 ? 8 : 4;
+  static constexpr int TEST = MAXS;
+  static constexpr int MNEW = MAXS + 1;
+  static constexpr int PAIR0 = MAXS + 2;
+  static constexpr int PAIR_SLOTS = NOPS - 1 - PAIR0;
+  static constexpr int LSUM = NOPS - 1;
+  static constexpr int MID = NOPS / 2;
+  // score pairs [pair_lo(k), pair_lo(k + 1)) go to slot k (at most two per slot)
+  static constexpr int pair_lo(int k) {
+    return k <= PAIR0 ? 0 : (k >= PAIR0 + PAIR_SLOTS ? 16 : ((k - PAIR0) * 16 + PAIR_SLOTS - 1) / PAIR_SLOTS);
+  }
+  static_assert(!(PV && QK) || PAIR_SLOTS >= 8, "softmax must fit in the MFMA slots");
 };
 
 // Operand i of a step: PV (ks = i / (D/32), cb = i % (D/32)), then QK (t = k/2, mb = k%2).
@@ -273,12 +284,12 @@ __device__ __forceinline__ void mfma_only(const u32x4* svp, const u32x4* skn,
 // sn (K tile in skn), and the online softmax of tile j (sc -> pc), interleaved.
 // Returns whether any row of the wave raised its reference max by more than tau;
 // then O must be multiplied by alpha before the next PV product.
-template <int D, bool CAUSAL, bool POLY, bool MASK>
+template <int D, bool CAUSAL, bool POLY, bool MASK, class Mid>
 __device__ __forceinline__ bool step(const u32x4* svp, const u32x4* skn, const bf16x8 (&pp)[4],
                                      f32x16 (&acc)[D / 32], const bf16x8 (&qf)[D / 16],
                                      f32x16 (&sc)[2], f32x16 (&sn)[2], bf16x8 (&pc)[4],
                                      RowState& st, float& alpha, int kv0, int qi, int N, float c,
-                                     float tau, int h, uint32_t vaddr, uint32_t kaddr) {
+                                     float tau, int h, uint32_t vaddr, uint32_t kaddr, Mid&& mid) {
   using SS = StepShape<D, true, true>;
   const float NEG_INF = -__builtin_inff();
   const char* vb = (const char*)svp;
@@ -313,24 +324,31 @@ __device__ __forceinline__ bool step(const u32x4* svp, const u32x4* skn, const b
       ring[k % kDepth] = load_operand<D, SS::NPV>(vb, kb, vaddr, kaddr, k + kDepth);
     issue_mfma<D, SS::NPV>(k, op, pp, acc, qf, sn);
 
-    if (k < 4) {                       // row max over 8 scores
-      const int mb = k >> 1, r0 = (k & 1) * 8;
+    if (k < SS::MAXS) {                // row max over this slot's share of the 32 scores
+      constexpr int per = 32 / SS::MAXS;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) mx = fmaxf(mx, sc[mb][r0 + r]);
-    } else if (k == 4) {               // whole row (other half-wave), threshold test
+      for (int u = 0; u < per; ++u) {
+        const int idx = k * per + u;
+        mx = fmaxf(mx, sc[idx >> 4][idx & 15]);
+      }
+    } else if (k == SS::TEST) {        // whole row (other half-wave), threshold test
       mx = half_swap_max(mx);
       mt = (mx == NEG_INF) ? NEG_INF : mx * c;
       any = __ballot(mt > st.m + tau) != 0;
-    } else if (k == 5) {               // thresholded update of the reference max
+    } else if (k == SS::MNEW) {        // thresholded update of the reference max
       const float m_new = any ? fmaxf(st.m, mt) : st.m;
       alpha = (m_new == NEG_INF) ? 1.f : exp2_sel<POLY>(st.m - m_new);
       st.m = m_new;
       mu = (m_new == NEG_INF) ? 0.f : m_new;
-    } else if (k >= SS::PAIR0 && k < SS::LSUM) {
+    } else if (k == SS::LSUM) {
+      st.l = __builtin_fmaf(st.l, alpha, (ls[0] + ls[1]) + (ls[2] + ls[3]));
+      asm volatile("" ::"v"(st.l));
+    }
+    if (k >= SS::PAIR0 && k < SS::LSUM) {
 #pragma unroll
-      for (int q = 0; q < SS::PAIRS_PER_SLOT; ++q) {
-        const int e = (k - SS::PAIR0) * SS::PAIRS_PER_SLOT + q;   // score pair 0..15
-        if (e < 16) {
+      for (int q = 0; q < 2; ++q) {    // score pairs scheduled in this slot
+        const int e = SS::pair_lo(k) + q;
+        if (e < SS::pair_lo(k + 1)) {
           const int mb = e >> 3, hf = (e >> 2) & 1, ee = e & 3;
           const float s0 = sc[mb][hf * 8 + 2 * ee], s1 = sc[mb][hf * 8 + 2 * ee + 1];
           float e0 = exp2_sel<POLY>(__builtin_fmaf(s0, c, -mu));
@@ -345,10 +363,8 @@ __device__ __forceinline__ bool step(const u32x4* svp, const u32x4* skn, const b
           asm volatile("" ::"v"(pk[mb * 2 + hf][ee]), "v"(ls[ee]));
         }
       }
-    } else if (k == SS::LSUM) {
-      st.l = __builtin_fmaf(st.l, alpha, (ls[0] + ls[1]) + (ls[2] + ls[3]));
-      asm volatile("" ::"v"(st.l));
     }
+    if (k == SS::MID) mid();
     __builtin_amdgcn_sched_barrier(0);
   }
   // S^T register r of block mb (next tile) holds key 32*mb + 16*(r/8) + 8*h + r%8
@@ -471,36 +487,63 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       }
       first = false;
     }
-    if (j + 1 <= n) {
-      store_stage(stg, j + 1);
-      if (j + 2 <= n) load_stage(stg, j + 2);
-    }
+    lds_barrier();
+  };
+  auto advance = [&]() {   // the next tile's S and this tile's P become current / previous
 #pragma unroll
     for (int i = 0; i < 2; ++i) s_cur[i] = s_nxt[i];
 #pragma unroll
     for (int i = 0; i < 4; ++i) p_prev[i] = p_cur[i];
-    lds_barrier();
+  };
+
+  // Staging inside step j (no branches, so it stays in the interleaved region):
+  // stage j+1 from registers to LDS (buffer (j+1)&1, last read in step j-1), then
+  // the loads of stage j+2.  Past the last tile the K part writes a buffer half
+  // that is never read and the loads are clamped to the last tile (in bounds,
+  // unused).
+  auto staging = [&](int j) {
+    store_k<D>(stg, sk[(j + 1) & 1], tid);
+    store_v<D>(stg, sv[(j + 1) & 1], tid);
+    load_k<D>(stg, tile_rsrc(Kh, min(j + 3, n - 1) * kBc), tid);
+    load_v<D>(stg, tile_rsrc(Vh, min(j + 1, n - 1) * kBc), tid);
   };
 
   // Tiles [0, n_full) need no element mask for any row of the workgroup: causal,
   // the keys below the workgroup's first query; otherwise the whole 64-key tiles.
   const int n_full = CAUSAL ? min(Q0, N) / kBc : N / kBc;
   int j = 0;
+  // Unmasked tiles two at a time, with the roles of the S and P registers swapped in
+  // the second step, so that no register copies are needed.
+  for (; j + 1 < n_full; j += 2) {
+    float alpha;
+    rescale();
+    bool any = step<D, CAUSAL, POLY, false>(
+        sv[j & 1], sk[j & 1], p_prev, acc, qf, s_cur, s_nxt, p_cur, st, alpha, j * kBc, qi, N, c,
+        tau, h, vaddr, kaddr, [&]() { staging(j); });
+    finish_step(j, any, alpha);
+    rescale();
+    any = step<D, CAUSAL, POLY, false>(
+        sv[(j + 1) & 1], sk[(j + 1) & 1], p_cur, acc, qf, s_nxt, s_cur, p_prev, st, alpha,
+        (j + 1) * kBc, qi, N, c, tau, h, vaddr, kaddr, [&]() { staging(j + 1); });
+    finish_step(j + 1, any, alpha);
+  }
   for (; j < n_full; ++j) {
     rescale();
     float alpha;
     const bool any = step<D, CAUSAL, POLY, false>(
         sv[j & 1], sk[j & 1], p_prev, acc, qf, s_cur, s_nxt, p_cur, st, alpha, j * kBc, qi, N, c,
-        tau, h, vaddr, kaddr);
+        tau, h, vaddr, kaddr, [&]() { staging(j); });
     finish_step(j, any, alpha);
+    advance();
   }
   for (; j < n; ++j) {
     rescale();
     float alpha;
     const bool any = step<D, CAUSAL, POLY, true>(
         sv[j & 1], sk[j & 1], p_prev, acc, qf, s_cur, s_nxt, p_cur, st, alpha, j * kBc, qi, N, c,
-        tau, h, vaddr, kaddr);
+        tau, h, vaddr, kaddr, [&]() { staging(j); });
     finish_step(j, any, alpha);
+    advance();
   }
   rescale();
 
