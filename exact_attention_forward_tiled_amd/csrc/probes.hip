@@ -12,6 +12,18 @@ using namespace attn;
 
 namespace {
 
+// One 512-thread workgroup per block, the attention kernels' shape: lane 0 of
+// every wave records the HW_ID hardware register (SIMD id in bits 5:4, CU id in
+// bits 11:8), out[block * 8 + wave].
+__global__ void __launch_bounds__(512) wave_place_probe(uint32_t* out) {
+  __shared__ uint32_t pad[16384];   // 64 KiB, as the attention kernels use
+  const int wave = threadIdx.x >> 6;
+  pad[threadIdx.x] = threadIdx.x;
+  __syncthreads();
+  const uint32_t id = __builtin_amdgcn_s_getreg(4 | (0 << 6) | (31 << 11)) + 0u * pad[threadIdx.x ^ 1];
+  if ((threadIdx.x & 63) == 0) out[blockIdx.x * 8 + wave] = id;
+}
+
 // a, b: 64 lanes x 8 bf16 each; c: 64 lanes x 16 fp32.
 __global__ void mfma_bf16_probe(const uint16_t* a, const uint16_t* b, float* c) {
   const int l = threadIdx.x;
@@ -293,6 +305,14 @@ int probe_mfma_fp4_sel2(const void* a, const void* b, const void* sa, const void
   hipLaunchKernelGGL(mfma_fp4_sel2_probe, dim3(1), dim3(64), 0, (hipStream_t)stream,
                      (const uint8_t*)a, (const uint8_t*)b, (const uint32_t*)sa,
                      (const uint32_t*)sb, c);
+  return (int)hipGetLastError();
+}
+
+// out must hold blocks * 8 uint32.
+int probe_wave_place(void* out, int blocks, void* stream) {
+  if (blocks < 1) return -1;
+  hipLaunchKernelGGL(wave_place_probe, dim3(blocks), dim3(512), 0, (hipStream_t)stream,
+                     (uint32_t*)out);
   return (int)hipGetLastError();
 }
 

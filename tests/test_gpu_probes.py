@@ -43,7 +43,8 @@ def lib():
                        "probe_lds_dma": [P, P, P], "probe_cvt_dot": [P, P, P, P],
                        "probe_mfma_fp4": [P, P, P, P, P, P],
                        "probe_mfma_fp4_sel2": [P, P, P, P, P, P],
-                       "probe_cvt_fp4": [P, P, P, P], "probe_dec_fp4": [P, P, P, P]}.items():
+                       "probe_cvt_fp4": [P, P, P, P], "probe_dec_fp4": [P, P, P, P],
+                       "probe_wave_place": [P, ctypes.c_int, P]}.items():
         fn = getattr(lib, name)
         fn.restype = I
         fn.argtypes = args
@@ -233,3 +234,24 @@ def test_fp4_decode(lib):
             byte = int(src[l, sel])
             assert got[l, sel, 0] == _fp4_value(byte & 15) * scale[l]
             assert got[l, sel, 1] == _fp4_value(byte >> 4) * scale[l]
+
+
+def test_wave_placement_pairs_waves_on_simds(lib):
+    """Wave placement of a 512-thread workgroup: waves w and w + 4 share a SIMD and
+    waves 0-3 sit on four different SIMDs.  The bf16 kernel's two waves of a SIMD
+    (w and w + 4) therefore compete for one matrix unit and one VALU, which is what
+    its per-SIMD instruction budget assumes (a speed, not a correctness, property:
+    every LDS hand-over in the kernel crosses a workgroup barrier)."""
+    import torch
+    blocks = 1024
+    out = torch.zeros(blocks * 8, dtype=torch.int32, device="cuda")
+    log("probe wave_place")
+    assert lib.probe_wave_place(out.data_ptr(), blocks, None) == 0
+    _sync()
+    hw = out.cpu().numpy().astype(np.uint32).reshape(blocks, 8)
+    simd = (hw >> 4) & 3
+    cu = (hw >> 8) & 15
+    log(f"  simd ids of the first blocks: {simd[:4].tolist()}")
+    assert np.all(cu == cu[:, :1]), "all waves of a workgroup on one CU"
+    assert np.all(simd[:, :4] == simd[:, 4:]), "wave w and w + 4 share a SIMD"
+    assert np.all(np.sort(simd[:, :4], axis=1) == np.arange(4)), "waves 0-3 on distinct SIMDs"
