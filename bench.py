@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attn fwd TFLOP/s (4·B·H·N²·d, causal halved) and % of MI355X MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6      # dense bf16 MFMA, 256 CUs x 2.4 GHz x 4096 flop/clk
 PEAK_FP4_TFLOPS = 10066.3      # dense MXFP4 MFMA, 256 CUs x 2.4 GHz x 16384 flop/clk
+PEAK_CLOCK_GHZ = 2.4           # the clock the published peaks assume
 KERNEL_SOURCES = {
     "bf16": ["exact_attention_forward_tiled_amd/csrc/attn_fwd_bf16.hip",
              "exact_attention_forward_tiled_amd/csrc/common.h",
@@ -168,14 +169,18 @@ def time_workload(wl, steps, warmup, warmup_seconds):
     return r
 
 
-def skip_ratio(wl):
-    """Fraction of (wave, tile) steps after each wave's first that skipped the O rescale."""
+def launch_stats(wl):
+    """One launch with the kernel's statistics counters: the fraction of (wave, tile) steps
+    after each wave's first that skipped the O rescale, and the mean shader clock over the
+    workgroups' lifetimes (shader cycles / 100 MHz reference ticks)."""
     import torch
-    stats = torch.zeros(2, dtype=torch.int64, device="cuda")
+    stats = torch.zeros(4, dtype=torch.int64, device="cuda")
     wl.launch(stats=stats)
     torch.cuda.synchronize()
-    s, r = (int(x) for x in stats.cpu())
-    return (1.0 - r / s) if s else None
+    s, r, cycles, ticks = (int(x) for x in stats.cpu())
+    skip = (1.0 - r / s) if s else None
+    ghz = (cycles / ticks * 0.1) if ticks else None
+    return skip, ghz
 
 
 def cpu_baseline(w, budget_s=10.0):
@@ -270,7 +275,7 @@ def main():
     log(f"timing {w.name}: ramp {args.warmup_seconds} s, warmup {args.warmup}, steps {args.steps}")
     wl = make_workload(w, args.exp, args.tau)
     t = time_workload(wl, args.steps, args.warmup, args.warmup_seconds)
-    skip = skip_ratio(wl)
+    skip, ghz = launch_stats(wl)
     del wl
     torch.cuda.empty_cache()
     kernel_tf = t["kernel_tflops"]
@@ -279,7 +284,10 @@ def main():
     extra = {"kernel_ms_avg": t["kernel_ms_avg"], "kernel_ms_median": t["kernel_ms_median"],
              "kernel_ms_min": t["kernel_ms_min"], "kernel_ms_max": t["kernel_ms_max"],
              "pct_of_bf16_peak": 100.0 * t["tflops"] / PEAK_BF16_TFLOPS,
-             "skip_ratio": skip, "exp_mode": args.exp if w.fmt == "bf16" else "directp",
+             "skip_ratio": skip, "clock_ghz": ghz,
+             "pct_of_bf16_peak_at_clock": (100.0 * t["tflops"] / (PEAK_BF16_TFLOPS * ghz / PEAK_CLOCK_GHZ)
+                                           if ghz else None),
+             "exp_mode": args.exp if w.fmt == "bf16" else "directp",
              "tau": args.tau, "kernel_hash": kernel_hash(w.fmt), "device": props.name,
              "compute_units": props.multi_processor_count, "workloads": {}}
     if w.fmt != "bf16":
@@ -299,14 +307,14 @@ def main():
         log(f"timing {wx.name}")
         wl = make_workload(wx, args.exp, args.tau)
         tx = time_workload(wl, max(5, args.steps // 2), args.warmup, args.warmup_seconds)
-        sx = skip_ratio(wl)
+        sx, gx = launch_stats(wl)
         del wl
         torch.cuda.empty_cache()
         extra["workloads"][wx.name] = {
             "tflops": round(tx["tflops"], 2), "ms": round(tx["ms_per_step"], 4),
             "kernel_ms_avg": round(tx["kernel_ms_avg"], 4),
             "pct_of_bf16_peak": round(100.0 * tx["tflops"] / PEAK_BF16_TFLOPS, 2),
-            "skip_ratio": sx}
+            "skip_ratio": sx, "clock_ghz": gx}
         if wx.fmt != "bf16":
             extra["workloads"][wx.name]["pct_of_fp4_peak"] = round(
                 100.0 * tx["tflops"] / PEAK_FP4_TFLOPS, 2)

@@ -122,6 +122,19 @@ def _stream(torch, device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
+STATS_COUNTERS = 4
+
+
+def _stats_ptr(torch, stats):
+    """Device pointer of the optional statistics buffer (int64 [>= STATS_COUNTERS], CUDA)."""
+    if stats is None:
+        return None
+    if stats.dtype != torch.int64 or not stats.is_cuda or not stats.is_contiguous() \
+            or stats.numel() < STATS_COUNTERS:
+        raise ValueError(f"stats must be a contiguous int64 CUDA tensor of {STATS_COUNTERS} counters")
+    return stats.data_ptr()
+
+
 def fwd(q, k, v, causal=False, scale=None, tau=8.0, exp_mode="hw", stats=None, out=None):
     """bf16 attention forward on the GPU: returns (O fp32 [B,Hq,N,d], LSE fp32 [B,Hq,N])."""
     torch = _torch()
@@ -139,7 +152,7 @@ def fwd(q, k, v, causal=False, scale=None, tau=8.0, exp_mode="hw", stats=None, o
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     else:
         o, lse = out
-    opts = make_opts(tau, exp_mode, stats.data_ptr() if stats is not None else None)
+    opts = make_opts(tau, exp_mode, _stats_ptr(torch, stats))
     check(attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                       B, Hq, Hkv, N, d, int(bool(causal)), float(scale), opts,
                       _stream(torch, q.device)))
@@ -191,7 +204,7 @@ def fwd_mxfp4(q4, qs, k4, ks, vt4, vts, causal=False, scale=None, tau=8.0, stats
     for t in (q4, qs, k4, ks, vt4, vts):
         if t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous():
             raise ValueError("codes and scales must be contiguous uint8 CUDA tensors")
-    opts = make_opts(tau, "hw", stats.data_ptr() if stats is not None else None)
+    opts = make_opts(tau, "hw", _stats_ptr(torch, stats))
     check(attn_fwd_mxfp4_ex(q4.data_ptr(), qs.data_ptr(), k4.data_ptr(), ks.data_ptr(),
                             vt4.data_ptr(), vts.data_ptr(), o.data_ptr(), lse.data_ptr(),
                             B, Hq, Hkv, N, d, int(bool(causal)), float(scale), opts,

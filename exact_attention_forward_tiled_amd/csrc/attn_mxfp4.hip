@@ -238,6 +238,9 @@ void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict_
   const int n32 = lane & 31, h = lane >> 5;
 
   const int group = Hq / Hkv;
+  // shader-clock and 100 MHz reference stamps, for the clock statistic
+  const unsigned long long clk0 = __builtin_amdgcn_s_memtime();
+  const unsigned long long ref0 = __builtin_amdgcn_s_memrealtime();
   const WorkItem wi = decode_workgroup(blockIdx.x, gridDim.x, Hkv, group, nqb, CAUSAL);
   const int b = wi.b, hkv = wi.hkv, g = wi.g;
   const int qb = CAUSAL ? (nqb - 1 - wi.qb_rank) : wi.qb_rank;
@@ -468,6 +471,10 @@ void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict_
   if (stats != nullptr && lane == 0 && wave_live) {
     atomicAdd(stats, (unsigned long long)n_steps);
     atomicAdd(stats + 1, (unsigned long long)n_rescales);
+  }
+  if (stats != nullptr && threadIdx.x == 0) {
+    atomicAdd(stats + 2, __builtin_amdgcn_s_memtime() - clk0);
+    atomicAdd(stats + 3, __builtin_amdgcn_s_memrealtime() - ref0);
   }
 }
 

@@ -57,9 +57,12 @@ typedef struct attn_opts {
     float tau;               /* rescale threshold in log2 units, >= 0 and finite; 0 rescales on
                                 every increase of the maximum (the textbook online softmax) */
     int exp_mode;            /* attn_exp_mode */
-    unsigned long long* stats; /* nullable DEVICE pointer to 2 counters, accumulated atomically:
+    unsigned long long* stats; /* nullable DEVICE pointer to 4 counters, accumulated atomically:
                                 [0] wave-tile steps after each wave's first tile,
-                                [1] rescale events among those steps.  Skip ratio = 1 - [1]/[0]. */
+                                [1] rescale events among those steps.  Skip ratio = 1 - [1]/[0].
+                                [2] shader-clock cycles and [3] 100 MHz reference-clock ticks
+                                from start to end of each workgroup (its first wave), summed:
+                                the mean shader clock is [2] / [3] * 100 MHz. */
 } attn_opts;
 
 /* Default options: tau = 8, hardware exp, no stats. */

@@ -169,13 +169,17 @@ def test_skip_ratio_stats():
     qb, kb, vb = random_case(37, 1, 2, 2, 4096, 128, sigma=w.sigma_qk)
     ratios = {}
     for tau in (0.0, 8.0):
-        stats = torch.zeros(2, dtype=torch.int64, device="cuda")
+        stats = torch.zeros(4, dtype=torch.int64, device="cuda")
         import exact_attention_forward_tiled_amd as fa
         fa.fwd(to_dev_bf16(qb), to_dev_bf16(kb), to_dev_bf16(vb), causal=False,
                scale=w.scale, tau=tau, stats=stats)
         torch.cuda.synchronize()
-        steps, resc = (int(x) for x in stats.cpu())
+        steps, resc, cycles, ticks = (int(x) for x in stats.cpu())
         assert steps == 2 * (4096 // 32) * (4096 // 64 - 1)
+        # shader clock over the workgroups' lifetimes (100 MHz reference ticks)
+        ghz = cycles / ticks * 0.1
+        log(f"  mean shader clock {ghz:.3f} GHz")
+        assert 0.3 < ghz < 3.0
         ratios[tau] = 1.0 - resc / steps
         log(f"  tau={tau}: steps={steps} rescales={resc} skip={ratios[tau]:.3f}")
     assert ratios[8.0] > ratios[0.0]
