@@ -19,6 +19,11 @@ Other modes (for rocprofv3 counter runs; they print nothing on stdout):
   --mode launch   run the workload's kernel --steps times, no timing, no oracle
   --mode copy     a plain device-to-device copy of --copy-mib MiB, --steps times
                   (calibrates the HBM byte counters against a known transfer)
+and one that prints its own JSON line:
+  --mode rates    issue-rate microbenchmarks from the test-only probe library:
+                  v_exp_f32 vs the VALU cubic exp2 vs a plain FMA, back-to-back
+                  v_mfma_f32_32x32x16_bf16, and LDS reads (ds_read_b128 and the
+                  transposing ds_read_b64_tr_b16), each at 2 and 4 waves per SIMD
 """
 
 import argparse
@@ -81,7 +86,7 @@ def device_inputs(w):
 class Workload:
     """Device buffers and one launch closure for a bf16 workload."""
 
-    def __init__(self, w, exp_mode, tau):
+    def __init__(self, w, exp_mode, tau, poly_frac=None):
         import torch
         import exact_attention_forward_tiled_amd as fa
         self.w = w
@@ -89,11 +94,12 @@ class Workload:
         self.o = torch.empty((w.B, w.Hq, w.N, w.d), dtype=torch.float32, device="cuda")
         self.lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device="cuda")
         self.fa = fa
-        self.exp_mode, self.tau = exp_mode, tau
+        self.exp_mode, self.tau, self.poly_frac = exp_mode, tau, poly_frac
 
     def launch(self, stats=None):
         self.fa.fwd(self.q, self.k, self.v, causal=self.w.causal, scale=self.w.scale, tau=self.tau,
-                    exp_mode=self.exp_mode, stats=stats, out=(self.o, self.lse))
+                    exp_mode=self.exp_mode, stats=stats, out=(self.o, self.lse),
+                    poly_frac=self.poly_frac)
 
 
 class Mxfp4Workload:
@@ -122,8 +128,8 @@ class Mxfp4Workload:
                           out=(self.o, self.lse))
 
 
-def make_workload(w, exp_mode, tau):
-    return Workload(w, exp_mode, tau) if w.fmt == "bf16" else Mxfp4Workload(w, tau)
+def make_workload(w, exp_mode, tau, poly_frac=None):
+    return Workload(w, exp_mode, tau, poly_frac) if w.fmt == "bf16" else Mxfp4Workload(w, tau)
 
 
 def time_workload(wl, steps, warmup, warmup_seconds):
@@ -183,6 +189,54 @@ def launch_stats(wl):
     return skip, ghz
 
 
+def rates():
+    """Issue rates of the softmax's exponential options, the MFMA and the LDS reads, as
+    nanoseconds per wave instruction per SIMD (best of 5 launches)."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "exact_attention_forward_tiled_amd", "libattn_probes.so"))
+    P, I = ctypes.c_void_p, ctypes.c_int
+    lib.probe_rate.argtypes = [P, I, I, I, P]
+    lib.probe_mfma_rate.argtypes = [P, I, I, P]
+    lib.probe_lds_rate.argtypes = [P, I, I, I, P]
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    simds = 4 * ncu
+
+    def best(fn):
+        assert fn() == 0
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t = 1e9
+        for _ in range(5):
+            a.record()
+            assert fn() == 0
+            b.record()
+            torch.cuda.synchronize()
+            t = min(t, a.elapsed_time(b) * 1e6)   # ns
+        return t
+
+    out_rates = {}
+    iters = 2048
+    for wps in (2, 4):                  # 256-thread blocks: 4 waves, one per SIMD
+        blocks = ncu * wps
+        out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+        waves_per_simd = blocks * 4 / simds
+        for mode, name in ((0, "exp2_hw_plus_sub"), (1, "exp2_cubic_plus_sub"), (2, "fma")):
+            ns = best(lambda: lib.probe_rate(out.data_ptr(), blocks, iters, mode, None))
+            out_rates[f"{name}/waves_per_simd={wps}"] = ns / (waves_per_simd * iters * 8)
+        ns = best(lambda: lib.probe_mfma_rate(out.data_ptr(), blocks, iters, None))
+        per = ns / (waves_per_simd * iters * 4)
+        out_rates[f"mfma_32x32x16_bf16/waves_per_simd={wps}"] = per
+        out_rates[f"mfma_tflops/waves_per_simd={wps}"] = 32768 / per * simds / 1e3
+        for mode, name, nbytes in ((0, "ds_read_b128_GBps_per_cu", 16),
+                                   (1, "ds_read_b64_tr_b16_GBps_per_cu", 8)):
+            ns = best(lambda: lib.probe_lds_rate(out.data_ptr(), blocks, iters, mode, None))
+            out_rates[f"{name}/waves_per_simd={wps}"] = blocks * 256 * iters * 8 * nbytes / ns / ncu
+        del out
+    return {"unit": "ns per wave instruction per SIMD (element-step for the exp2 rows)",
+            "rates": {k: round(v, 4) for k, v in out_rates.items()}}
+
+
 def cpu_baseline(w, budget_s=10.0):
     """The float64 oracle, as it stands, on whole (batch, head) slices of the same workload
     (the MXFP4 workload runs the Direct-P emulation on the quantised operands)."""
@@ -230,13 +284,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--warmup-seconds", type=float, default=0.5)
     ap.add_argument("--config", type=int, default=2)
-    ap.add_argument("--exp", default="hw", choices=["hw", "poly"])
+    ap.add_argument("--exp", default="hw", choices=["hw", "poly", "mix"])
+    ap.add_argument("--poly-frac", type=float, default=0.5,
+                    help="with --exp mix: fraction of the exponentials on the cubic")
     ap.add_argument("--tau", type=float, default=8.0)
     ap.add_argument("--extra", default="", help="other workloads to time (comma list), e.g. 3,4")
     ap.add_argument("--compare-exp", action="store_true",
-                    help="also time the headline workload with the other exp mode")
+                    help="also time the headline workload with the other exp modes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", default="bench", choices=["bench", "launch", "copy"])
+    ap.add_argument("--mode", default="bench", choices=["bench", "launch", "copy", "rates"])
     ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
 
@@ -252,6 +308,10 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
 
+    if args.mode == "rates":
+        print(json.dumps(rates()), flush=True)
+        return
+
     if args.mode == "copy":
         n = args.copy_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -265,7 +325,7 @@ def main():
     w = synth.workload(args.config)
 
     if args.mode == "launch":
-        wl = make_workload(w, args.exp, args.tau)
+        wl = make_workload(w, args.exp, args.tau, args.poly_frac)
         for _ in range(args.steps):
             wl.launch()
         torch.cuda.synchronize()
@@ -273,7 +333,7 @@ def main():
         return
 
     log(f"timing {w.name}: ramp {args.warmup_seconds} s, warmup {args.warmup}, steps {args.steps}")
-    wl = make_workload(w, args.exp, args.tau)
+    wl = make_workload(w, args.exp, args.tau, args.poly_frac)
     t = time_workload(wl, args.steps, args.warmup, args.warmup_seconds)
     skip, ghz = launch_stats(wl)
     del wl
@@ -288,24 +348,30 @@ def main():
              "pct_of_bf16_peak_at_clock": (100.0 * t["tflops"] / (PEAK_BF16_TFLOPS * ghz / PEAK_CLOCK_GHZ)
                                            if ghz else None),
              "exp_mode": args.exp if w.fmt == "bf16" else "directp",
+             "poly_frac": args.poly_frac if args.exp == "mix" else None,
              "tau": args.tau, "kernel_hash": kernel_hash(w.fmt), "device": props.name,
              "compute_units": props.multi_processor_count, "workloads": {}}
     if w.fmt != "bf16":
         extra["pct_of_fp4_peak"] = 100.0 * t["tflops"] / PEAK_FP4_TFLOPS
     if args.compare_exp and w.fmt == "bf16":
-        other = "poly" if args.exp == "hw" else "hw"
-        log(f"timing {w.name} with exp mode {other}")
-        wl = Workload(w, other, args.tau)
-        t2 = time_workload(wl, args.steps, args.warmup, args.warmup_seconds)
-        del wl
-        extra["workloads"][f"{w.name}/exp={other}"] = {
-            "tflops": round(t2["tflops"], 2), "ms": round(t2["ms_per_step"], 4)}
+        for other, frac in (("hw", None), ("poly", None), ("mix", 0.25), ("mix", 0.5), ("mix", 0.75)):
+            if other == args.exp and (other != "mix" or frac == args.poly_frac):
+                continue
+            tag = other if other != "mix" else f"mix{frac:g}"
+            log(f"timing {w.name} with exp mode {tag}")
+            wl = Workload(w, other, args.tau, frac)
+            t2 = time_workload(wl, args.steps, args.warmup, args.warmup_seconds)
+            _, g2 = launch_stats(wl)
+            del wl
+            extra["workloads"][f"{w.name}/exp={tag}"] = {
+                "tflops": round(t2["tflops"], 2), "ms": round(t2["ms_per_step"], 4),
+                "clock_ghz": g2}
     for idx in [int(x) for x in args.extra.split(",") if x.strip()]:
         wx = synth.workload(idx)
         if idx == args.config:
             continue
         log(f"timing {wx.name}")
-        wl = make_workload(wx, args.exp, args.tau)
+        wl = make_workload(wx, args.exp, args.tau, args.poly_frac)
         tx = time_workload(wl, max(5, args.steps // 2), args.warmup, args.warmup_seconds)
         sx, gx = launch_stats(wl)
         del wl

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libattn.so")
 
 ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, -1, -2, -3
-EXP_MODES = {"hw": 0, "poly": 1}
+EXP_MODES = {"hw": 0, "poly": 1, "mix": 2}
 
 # entry points declared in include/attn.h
 EXPORTS = ("attn_default_opts", "attn_fwd", "attn_fwd_ex", "attn_fwd_mxfp4", "attn_fwd_mxfp4_ex",
@@ -24,7 +24,7 @@ EXPORTS = ("attn_default_opts", "attn_fwd", "attn_fwd_ex", "attn_fwd_mxfp4", "at
 
 class AttnOpts(ctypes.Structure):
     _fields_ = [("tau", ctypes.c_float), ("exp_mode", ctypes.c_int),
-                ("stats", ctypes.c_void_p)]
+                ("poly_frac", ctypes.c_float), ("stats", ctypes.c_void_p)]
 
 
 def _load():
@@ -73,11 +73,13 @@ def check(status):
     raise AttnError(f"libattn: status {status}")
 
 
-def make_opts(tau=8.0, exp_mode="hw", stats_ptr=None):
+def make_opts(tau=8.0, exp_mode="hw", stats_ptr=None, poly_frac=None):
     o = AttnOpts()
     lib.attn_default_opts(ctypes.byref(o))
     o.tau = float(tau)
     o.exp_mode = EXP_MODES[exp_mode] if isinstance(exp_mode, str) else int(exp_mode)
+    if poly_frac is not None:
+        o.poly_frac = float(poly_frac)
     o.stats = stats_ptr
     return o
 
@@ -135,8 +137,10 @@ def _stats_ptr(torch, stats):
     return stats.data_ptr()
 
 
-def fwd(q, k, v, causal=False, scale=None, tau=8.0, exp_mode="hw", stats=None, out=None):
-    """bf16 attention forward on the GPU: returns (O fp32 [B,Hq,N,d], LSE fp32 [B,Hq,N])."""
+def fwd(q, k, v, causal=False, scale=None, tau=8.0, exp_mode="hw", stats=None, out=None,
+        poly_frac=None):
+    """bf16 attention forward on the GPU: returns (O fp32 [B,Hq,N,d], LSE fp32 [B,Hq,N]).
+    exp_mode "hw", "poly" or "mix" (poly_frac of the exponentials on the cubic)."""
     torch = _torch()
     for t in (q, k, v):
         if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
@@ -152,7 +156,7 @@ def fwd(q, k, v, causal=False, scale=None, tau=8.0, exp_mode="hw", stats=None, o
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     else:
         o, lse = out
-    opts = make_opts(tau, exp_mode, _stats_ptr(torch, stats))
+    opts = make_opts(tau, exp_mode, _stats_ptr(torch, stats), poly_frac)
     check(attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                       B, Hq, Hkv, N, d, int(bool(causal)), float(scale), opts,
                       _stream(torch, q.device)))

@@ -23,8 +23,18 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 int check_opts(const attn_opts* o) {
   if (!(o->tau >= 0.f) || !isfinite(o->tau)) return ATTN_EINVAL;
-  if (o->exp_mode != ATTN_EXP_HW && o->exp_mode != ATTN_EXP_POLY) return ATTN_EINVAL;
+  if (o->exp_mode != ATTN_EXP_HW && o->exp_mode != ATTN_EXP_POLY && o->exp_mode != ATTN_EXP_MIX)
+    return ATTN_EINVAL;
+  if (o->exp_mode == ATTN_EXP_MIX && !(o->poly_frac >= 0.f && o->poly_frac <= 1.f))
+    return ATTN_EINVAL;
   return ATTN_OK;
+}
+
+// Score pairs per lane and tile (of 16) whose exponential is the cubic.
+int poly_pairs(const attn_opts* o) {
+  if (o->exp_mode == ATTN_EXP_HW) return 0;
+  if (o->exp_mode == ATTN_EXP_POLY) return 16;
+  return 4 * (int)lrintf(o->poly_frac * 4.f);   // nearest quarter
 }
 
 int check_common(int B, int Hq, int Hkv, int N, int d, int causal, float scale) {
@@ -45,6 +55,7 @@ void attn_default_opts(attn_opts* opts) {
   if (opts == nullptr) return;
   opts->tau = 8.0f;
   opts->exp_mode = ATTN_EXP_HW;
+  opts->poly_frac = 0.5f;
   opts->stats = nullptr;
 }
 
@@ -82,7 +93,7 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, float* o, float* ls
   a.c = fabsf(scale) * 1.4426950408889634f;
   a.tau = op->tau;
   a.qsign = scale < 0.f ? 0x80008000u : 0u;
-  a.exp_mode = op->exp_mode;
+  a.poly_pairs = poly_pairs(op);
   a.stats = op->stats;
   a.stream = stream;
   return hip_status(attn::launch_fwd_bf16(a));

@@ -100,6 +100,20 @@ __device__ __forceinline__ float exp2_sel(float x) {
   else return __builtin_amdgcn_exp2f(x);
 }
 
+// Exponential split: NP of each lane's 16 score pairs per tile go to the cubic, the
+// rest to v_exp_f32 ("FlashAttention-4 de NVIDIA…", section "La ventaja técnica":
+// exponentials shared between the special-function unit and the FMA units).  The
+// cubic pairs are spread evenly over the tile (pair e is one when the running count
+// e*NP/16 steps up there).  NP = 0: hardware only; NP = 16: cubic only.
+__device__ __forceinline__ constexpr bool pair_on_poly(int np, int e) {
+  return (e + 1) * np / 16 > e * np / 16;
+}
+
+template <int NP>
+__device__ __forceinline__ float exp2_pair(float x, int e) {
+  return pair_on_poly(NP, e) ? exp2_poly(x) : __builtin_amdgcn_exp2f(x);
+}
+
 // Row of the K tile read by MFMA row m of a 32-row block: bits 2 and 3 swapped.
 __device__ __forceinline__ int perm_row(int m) {
   return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1);
@@ -284,7 +298,7 @@ __device__ __forceinline__ void mfma_only(const u32x4* svp, const u32x4* skn,
 // sn (K tile in skn), and the online softmax of tile j (sc -> pc), interleaved.
 // Returns whether any row of the wave raised its reference max by more than tau;
 // then O must be multiplied by alpha before the next PV product.
-template <int D, bool CAUSAL, bool POLY, bool MASK, class Mid>
+template <int D, bool CAUSAL, int NP, bool MASK, class Mid>
 __device__ __forceinline__ bool step(const u32x4* svp, const u32x4* skn, const bf16x8 (&pp)[4],
                                      f32x16 (&acc)[D / 32], const bf16x8 (&qf)[D / 16],
                                      f32x16 (&sc)[2], f32x16 (&sn)[2], bf16x8 (&pc)[4],
@@ -337,7 +351,7 @@ __device__ __forceinline__ bool step(const u32x4* svp, const u32x4* skn, const b
       any = __ballot(mt > st.m + tau) != 0;
     } else if (k == SS::MNEW) {        // thresholded update of the reference max
       const float m_new = any ? fmaxf(st.m, mt) : st.m;
-      alpha = (m_new == NEG_INF) ? 1.f : exp2_sel<POLY>(st.m - m_new);
+      alpha = (m_new == NEG_INF) ? 1.f : exp2_sel<NP == 16>(st.m - m_new);
       st.m = m_new;
       mu = (m_new == NEG_INF) ? 0.f : m_new;
     } else if (k == SS::LSUM) {
@@ -351,8 +365,8 @@ __device__ __forceinline__ bool step(const u32x4* svp, const u32x4* skn, const b
         if (e < SS::pair_lo(k + 1)) {
           const int mb = e >> 3, hf = (e >> 2) & 1, ee = e & 3;
           const float s0 = sc[mb][hf * 8 + 2 * ee], s1 = sc[mb][hf * 8 + 2 * ee + 1];
-          float e0 = exp2_sel<POLY>(__builtin_fmaf(s0, c, -mu));
-          float e1 = exp2_sel<POLY>(__builtin_fmaf(s1, c, -mu));
+          float e0 = exp2_pair<NP>(__builtin_fmaf(s0, c, -mu), e);
+          float e1 = exp2_pair<NP>(__builtin_fmaf(s1, c, -mu), e);
           if constexpr (MASK) {
             e0 = (s0 == NEG_INF) ? 0.f : e0;
             e1 = (s1 == NEG_INF) ? 0.f : e1;
@@ -373,7 +387,7 @@ __device__ __forceinline__ bool step(const u32x4* svp, const u32x4* skn, const b
   return any;
 }
 
-template <int D, bool CAUSAL, bool POLY>
+template <int D, bool CAUSAL, int NP>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE,
@@ -520,12 +534,12 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   for (; j + 1 < n_full; j += 2) {
     float alpha;
     rescale();
-    bool any = step<D, CAUSAL, POLY, false>(
+    bool any = step<D, CAUSAL, NP, false>(
         sv[j & 1], sk[j & 1], p_prev, acc, qf, s_cur, s_nxt, p_cur, st, alpha, j * kBc, qi, N, c,
         tau, h, vaddr, kaddr, [&]() { staging(j); });
     finish_step(j, any, alpha);
     rescale();
-    any = step<D, CAUSAL, POLY, false>(
+    any = step<D, CAUSAL, NP, false>(
         sv[(j + 1) & 1], sk[(j + 1) & 1], p_cur, acc, qf, s_nxt, s_cur, p_prev, st, alpha,
         (j + 1) * kBc, qi, N, c, tau, h, vaddr, kaddr, [&]() { staging(j + 1); });
     finish_step(j + 1, any, alpha);
@@ -533,7 +547,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   for (; j < n_full; ++j) {
     rescale();
     float alpha;
-    const bool any = step<D, CAUSAL, POLY, false>(
+    const bool any = step<D, CAUSAL, NP, false>(
         sv[j & 1], sk[j & 1], p_prev, acc, qf, s_cur, s_nxt, p_cur, st, alpha, j * kBc, qi, N, c,
         tau, h, vaddr, kaddr, [&]() { staging(j); });
     finish_step(j, any, alpha);
@@ -542,7 +556,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   for (; j < n; ++j) {
     rescale();
     float alpha;
-    const bool any = step<D, CAUSAL, POLY, true>(
+    const bool any = step<D, CAUSAL, NP, true>(
         sv[j & 1], sk[j & 1], p_prev, acc, qf, s_cur, s_nxt, p_cur, st, alpha, j * kBc, qi, N, c,
         tau, h, vaddr, kaddr, [&]() { staging(j); });
     finish_step(j, any, alpha);
@@ -580,28 +594,35 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   }
 }
 
-template <int D, bool CAUSAL, bool POLY>
+template <int D, bool CAUSAL, int NP>
 hipError_t launch_one(const FwdArgs& a) {
   const int nqb = (a.N + kBr - 1) / kBr;
   const long long grid = (long long)a.B * a.Hq * nqb;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, POLY>), dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NP>), dim3((unsigned)grid), dim3(kThreads), 0,
                      (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                      (const uint16_t*)a.v, a.o, a.lse, a.Hq, a.Hkv, a.N, nqb, a.c, a.tau, a.qsign,
                      a.stats);
   return hipGetLastError();
 }
 
+template <int D, bool CAUSAL>
+hipError_t launch_np(const FwdArgs& a) {
+  switch (a.poly_pairs) {
+    case 0: return launch_one<D, CAUSAL, 0>(a);
+    case 4: return launch_one<D, CAUSAL, 4>(a);
+    case 8: return launch_one<D, CAUSAL, 8>(a);
+    case 12: return launch_one<D, CAUSAL, 12>(a);
+    case 16: return launch_one<D, CAUSAL, 16>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
-  const bool poly = a.exp_mode == 1;
-  if (a.d == 128) {
-    if (a.causal) return poly ? launch_one<128, true, true>(a) : launch_one<128, true, false>(a);
-    return poly ? launch_one<128, false, true>(a) : launch_one<128, false, false>(a);
-  }
-  if (a.causal) return poly ? launch_one<64, true, true>(a) : launch_one<64, true, false>(a);
-  return poly ? launch_one<64, false, true>(a) : launch_one<64, false, false>(a);
+  if (a.d == 128) return a.causal ? launch_np<128, true>(a) : launch_np<128, false>(a);
+  return a.causal ? launch_np<64, true>(a) : launch_np<64, false>(a);
 }
 
 }  // namespace attn

@@ -17,7 +17,8 @@ struct FwdArgs {
   float c;          // |scale| * log2(e): scores to log2 units
   float tau;        // rescale threshold, log2 units
   uint32_t qsign;   // 0x80008000 flips the sign of every bf16 Q element (scale < 0)
-  int exp_mode;     // 0 hardware, 1 cubic
+  int poly_pairs;   // of each lane's 16 score pairs per tile, how many use the cubic exp2
+                    // (0, 4, 8, 12 or 16; the rest use v_exp_f32)
   unsigned long long* stats;
   void* stream;
 };

@@ -48,15 +48,22 @@ typedef enum attn_status {
 /* Exponential used for the softmax weights. */
 enum attn_exp_mode {
     ATTN_EXP_HW = 0,         /* hardware v_exp_f32 */
-    ATTN_EXP_POLY = 1        /* VALU cubic polynomial for 2^f on [0,1) plus exponent add
+    ATTN_EXP_POLY = 1,       /* VALU cubic polynomial for 2^f on [0,1) plus exponent add
                                 ("FlashAttention-4 de NVIDIA…", section "La ventaja técnica":
                                 exponentials approximated by cubic polynomials on the FMA units) */
+    ATTN_EXP_MIX = 2         /* a fraction poly_frac of the score elements on the cubic, the rest
+                                on v_exp_f32 (same section: the exponential work shared between
+                                the special-function unit and the FMA units) */
 };
 
 typedef struct attn_opts {
     float tau;               /* rescale threshold in log2 units, >= 0 and finite; 0 rescales on
                                 every increase of the maximum (the textbook online softmax) */
     int exp_mode;            /* attn_exp_mode */
+    float poly_frac;         /* ATTN_EXP_MIX only: fraction of the score elements whose
+                                exponential is the cubic, in [0, 1]; the kernel uses the nearest
+                                multiple of 1/4 (each lane's 16 score pairs of a 64-key tile are
+                                split 4 ways, the cubic pairs spread evenly); otherwise ignored */
     unsigned long long* stats; /* nullable DEVICE pointer to 4 counters, accumulated atomically:
                                 [0] wave-tile steps after each wave's first tile,
                                 [1] rescale events among those steps.  Skip ratio = 1 - [1]/[0].
@@ -65,7 +72,7 @@ typedef struct attn_opts {
                                 the mean shader clock is [2] / [3] * 100 MHz. */
 } attn_opts;
 
-/* Default options: tau = 8, hardware exp, no stats. */
+/* Default options: tau = 8, hardware exp (poly_frac 0.5 for ATTN_EXP_MIX), no stats. */
 void attn_default_opts(attn_opts* opts);
 
 /*

@@ -66,10 +66,21 @@ def test_fwd_validation(fa, args, code):
 
 
 def test_opts_validation(fa):
-    for tau, mode in [(-1.0, "hw"), (float("nan"), "hw"), (8.0, 7)]:
-        opts = fa.make_opts(tau, mode)
+    for tau, mode, frac in [(-1.0, "hw", None), (float("nan"), "hw", None), (8.0, 7, None),
+                            (8.0, "mix", -0.1), (8.0, "mix", 1.5), (8.0, "mix", float("nan"))]:
+        opts = fa.make_opts(tau, mode, poly_frac=frac)
         st = fa.attn_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 16, 64, 0, 0.1, opts, None)
         assert st == -1
+
+
+def test_default_opts_layout(fa):
+    """attn_default_opts fills every field of the C struct; reading them back through the
+    binding's mirror checks that the two layouts agree."""
+    from exact_attention_forward_tiled_amd.binding import AttnOpts, lib
+    o = AttnOpts()
+    o.tau, o.exp_mode, o.poly_frac, o.stats = -3.0, 9, -3.0, FAKE
+    lib.attn_default_opts(ctypes.byref(o))
+    assert (o.tau, o.exp_mode, o.poly_frac, o.stats) == (8.0, 0, 0.5, None)
 
 
 def test_mxfp4_validation(fa):

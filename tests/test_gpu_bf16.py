@@ -58,17 +58,31 @@ SMALL = [
 
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: "B%dHq%dHkv%dN%dd%d%s" % (
     c[0], c[1], c[2], c[3], c[4], "c" if c[5] else "n"))
-@pytest.mark.parametrize("mode", [("hw", 8.0), ("hw", 0.0), ("poly", 8.0)],
+@pytest.mark.parametrize("mode", [("hw", 8.0), ("hw", 0.0), ("poly", 8.0), ("mix", 8.0)],
                          ids=lambda m: f"{m[0]}-tau{m[1]:g}")
 def test_small_shapes(case, mode):
     B, Hq, Hkv, N, d, causal = case
     qb, kb, vb = random_case(sum(case[:5]) + 7, B, Hq, Hkv, N, d, sigma=1.5)
     scale = 1.0 / np.sqrt(d)
     log(f"case {case} mode {mode}")
-    o, lse = _run(qb, kb, vb, causal, scale, exp_mode=mode[0], tau=mode[1])
+    o, lse = _run(qb, kb, vb, causal, scale, exp_mode=mode[0], tau=mode[1],
+                  poly_frac=0.5 if mode[0] == "mix" else None)
     ro, rl = oracle.attention(synth.bf16_bits_to_f64(qb), synth.bf16_bits_to_f64(kb),
                               synth.bf16_bits_to_f64(vb), causal, scale)
     _check(o, lse, ro, rl, f"{case} {mode}")
+
+
+@pytest.mark.parametrize("frac", [0.25, 0.75])
+def test_mix_fractions(frac):
+    """The other two split points of the mixed exponential (0.5 runs in the shape sweep)."""
+    qb, kb, vb = random_case(91, 1, 4, 2, 700, 128, sigma=1.5)
+    scale = 1.0 / np.sqrt(128)
+    log(f"mix poly_frac {frac}")
+    for causal in (False, True):
+        o, lse = _run(qb, kb, vb, causal, scale, exp_mode="mix", poly_frac=frac)
+        ro, rl = oracle.attention(synth.bf16_bits_to_f64(qb), synth.bf16_bits_to_f64(kb),
+                                  synth.bf16_bits_to_f64(vb), causal, scale)
+        _check(o, lse, ro, rl, f"mix {frac} causal={causal}")
 
 
 def test_workload_1_full():
