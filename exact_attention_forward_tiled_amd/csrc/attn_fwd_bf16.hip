@@ -397,7 +397,10 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   __shared__ u32x4 sk[2][G::KUNITS];
   __shared__ u32x4 sv[2][G::VUNITS];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index through readfirstlane: the compiler then knows it is uniform, and the
+  // per-wave branches of the diagonal tiles (which contain barriers) are scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n32 = lane & 31, h = lane >> 5;
 
   const int group = Hq / Hkv;
@@ -441,6 +444,11 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const int wave_end = CAUSAL ? min(N, q0 + kRowsPerWave) : N;   // keys this wave can see
   const bool wave_live = q0 < N;
   auto active = [&](int j) { return wave_live && j * kBc < wave_end; };
+  // Per wave: tiles [0, n_vis) need no element mask, tiles [n_vis, n_w) do, and tiles
+  // [n_w, n) are entirely masked (causal: keys past the wave's last query), so the
+  // wave skips their products and only keeps up its share of the staging.
+  const int n_w = wave_live ? (wave_end + kBc - 1) / kBc : n;
+  const int n_vis = min(CAUSAL ? (q0 + 1) / kBc : n, N / kBc);
 
   auto tile_rsrc = [&](const uint16_t* head, int kv0) {
     return make_rsrc(head + (size_t)kv0 * D, (N - kv0) * G::ROW_BYTES);
@@ -553,7 +561,20 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     finish_step(j, any, alpha);
     advance();
   }
-  for (; j < n; ++j) {
+  // The diagonal tiles (and a ragged tail), in per-wave loops (wave-uniform bounds,
+  // each tile in exactly one loop, one barrier per tile): unmasked while the wave
+  // sees the whole tile, masked on its partial tiles, then its last PV product, then
+  // staging only for the tiles that are entirely masked for it.
+  for (; j < n_vis; ++j) {
+    rescale();
+    float alpha;
+    const bool any = step<D, CAUSAL, NP, false>(
+        sv[j & 1], sk[j & 1], p_prev, acc, qf, s_cur, s_nxt, p_cur, st, alpha, j * kBc, qi, N, c,
+        tau, h, vaddr, kaddr, [&]() { staging(j); });
+    finish_step(j, any, alpha);
+    advance();
+  }
+  for (; j < n_w; ++j) {
     rescale();
     float alpha;
     const bool any = step<D, CAUSAL, NP, true>(
@@ -562,10 +583,17 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     finish_step(j, any, alpha);
     advance();
   }
+  // ---- last PV product (tile n_w-1, V tile in stage n_w) ----
   rescale();
-
-  // ---- last PV product (tile n-1, V tile in stage n) ----
-  mfma_only<D, true, false>(sv[n & 1], sk[n & 1], p_prev, acc, qf, s_nxt, vaddr, kaddr);
+  mfma_only<D, true, false>(sv[j & 1], sk[j & 1], p_prev, acc, qf, s_nxt, vaddr, kaddr);
+  if (j < n) {
+    staging(j);
+    lds_barrier();
+    for (++j; j < n; ++j) {
+      staging(j);
+      lds_barrier();
+    }
+  }
 
   // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l) ----
   const float ltot = half_swap_sum(st.l);
