@@ -73,6 +73,10 @@ struct Geo {
   static constexpr int V_THREADS = CP * (kBc / 8);         // threads that stage V
   static constexpr int SW_SHIFT = (NCH == 16) ? 0 : 1;     // chunk swizzle granularity
   static constexpr int ROW_BYTES = D * 2;
+  // LDS: two K and two V^T tiles, reused after the last tile by the epilogue (8 KiB per wave)
+  static constexpr int STAGE_UNITS = 2 * KUNITS + 2 * VUNITS;
+  static constexpr int EPI_UNITS = kWaves * kRowsPerWave * 16;
+  static constexpr int LDS_UNITS = STAGE_UNITS > EPI_UNITS ? STAGE_UNITS : EPI_UNITS;
   static_assert(KUNITS % kThreads == 0, "K tile must split evenly over the workgroup");
   static_assert(V_THREADS <= kThreads, "V tile staging needs at most one thread per pair");
   static_assert(NCH == 8 || NCH == 16, "d = 64 or 128");
@@ -394,8 +398,9 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                      int Hq, int Hkv, int N, int nqb, float c, float tau, uint32_t qsign,
                      unsigned long long* __restrict__ stats) {
   using G = Geo<D>;
-  __shared__ u32x4 sk[2][G::KUNITS];
-  __shared__ u32x4 sv[2][G::VUNITS];
+  __shared__ u32x4 lds[G::LDS_UNITS];
+  u32x4 (*sk)[G::KUNITS] = reinterpret_cast<u32x4 (*)[G::KUNITS]>(lds);
+  u32x4 (*sv)[G::VUNITS] = reinterpret_cast<u32x4 (*)[G::VUNITS]>(lds + 2 * G::KUNITS);
 
   const int tid = threadIdx.x, lane = tid & 63;
   // wave index through readfirstlane: the compiler then knows it is uniform, and the
@@ -596,22 +601,40 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   }
 
   // ---- epilogue: O = acc / l, LSE = ln2 * (m + log2 l) ----
+  // O goes out through LDS so that every store instruction writes whole rows: each
+  // lane holds 16-byte pieces of one query row, so storing straight from registers
+  // would touch 32 rows per instruction.  After a barrier (every wave is done with
+  // the K/V buffers) each wave writes its 32 x 64 half tiles into its own 8 KiB of
+  // them, chunk c of row r at (c ^ (r % 16)) (conflict-free both ways), and reads
+  // them back as 4 rows x 256 B per instruction.
   const float ltot = half_swap_sum(st.l);
-  if (qi < N) {
-    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    float* Orow = O + ((size_t)(b * Hq + hq) * N + qi) * D;
+  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  lds_barrier();
+  {
+    u32x4* tb = lds + wave * (kRowsPerWave * 16);
+    float* Obase = O + ((size_t)(b * Hq + hq) * N + q0) * D;
 #pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb)
+    for (int half = 0; half < D / 64; ++half) {
 #pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        f32x4 out = {acc[cb][4 * a4] * inv, acc[cb][4 * a4 + 1] * inv, acc[cb][4 * a4 + 2] * inv,
-                     acc[cb][4 * a4 + 3] * inv};
-        *(f32x4*)(Orow + cb * 32 + 8 * a4 + 4 * h) = out;
+      for (int cbl = 0; cbl < 2; ++cbl)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int cb = 2 * half + cbl, c = 8 * cbl + 2 * a4 + h;
+          const f32x4 out = {acc[cb][4 * a4] * inv, acc[cb][4 * a4 + 1] * inv,
+                             acc[cb][4 * a4 + 2] * inv, acc[cb][4 * a4 + 3] * inv};
+          tb[n32 * 16 + (c ^ (n32 & 15))] = __builtin_bit_cast(u32x4, out);
+        }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int r = 4 * k + (lane >> 4), c = lane & 15;
+        const u32x4 val = tb[r * 16 + (c ^ (r & 15))];
+        if (q0 + r < N) *(u32x4*)(Obase + (size_t)r * D + 64 * half + 4 * c) = val;
       }
-    if (h == 0)
-      LSE[(size_t)(b * Hq + hq) * N + qi] =
-          ltot > 0.f ? (st.m + __builtin_log2f(ltot)) * kLn2 : -__builtin_inff();
+    }
   }
+  if (qi < N && h == 0)
+    LSE[(size_t)(b * Hq + hq) * N + qi] =
+        ltot > 0.f ? (st.m + __builtin_log2f(ltot)) * kLn2 : -__builtin_inff();
   if (stats != nullptr && lane == 0 && wave_live) {
     atomicAdd(stats, (unsigned long long)n_steps);
     atomicAdd(stats + 1, (unsigned long long)n_rescales);
