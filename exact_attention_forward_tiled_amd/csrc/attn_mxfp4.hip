@@ -234,7 +234,11 @@ void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict_
                       unsigned long long* __restrict__ stats) {
   __shared__ MBuf buf[2];
   const float NEG_INF = -__builtin_inff();
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index through readfirstlane: the staging roles below are whole waves (K codes:
+  // waves 0-3, V^T codes: 4-7, K scales: wave 0, V^T scales: waves 1-2), and the
+  // compiler then turns them into scalar branches instead of masked execution
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n32 = lane & 31, h = lane >> 5;
 
   const int group = Hq / Hkv;
@@ -288,43 +292,38 @@ void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict_
   auto active = [&](int j) { return wave_live && j * kMBc < wave_end; };
 
   // Stage t (read by pipeline step t from buffer t & 1) holds K tile t+1 and V tile t-1.
+  // The loads are unconditional, with the tile index clamped into [0, n) (in bounds;
+  // a stage past the tiles is loaded but never stored): a skipped load would make the
+  // compiler keep the old register values alive and wait for the new ones later.
   auto load_stage = [&](MStage& sg, int t) {
-    if (tid < 256) {
-      if (t + 1 < n) {
-        const int kv0 = (t + 1) * kMBc;
-        const __amdgpu_buffer_rsrc_t rk =
-            mrsrc(K4h + (size_t)kv0 * kCodeRow, (N - kv0) * kCodeRow);
-        sg.codes = __builtin_amdgcn_raw_buffer_load_b128(rk, (tid >> 2) * kCodeRow + (tid & 3) * 16,
-                                                         0, 0);
-      }
-    } else if (t >= 1 && t - 1 < n) {
-      const int kv0 = (t - 1) * kMBc, u = tid - 256;
+    const int kt = min(t + 1, n - 1), vt = max(min(t - 1, n - 1), 0);
+    if (wave < 4) {
+      const int kv0 = kt * kMBc;
+      const __amdgpu_buffer_rsrc_t rk = mrsrc(K4h + (size_t)kv0 * kCodeRow, (N - kv0) * kCodeRow);
+      sg.codes = __builtin_amdgcn_raw_buffer_load_b128(rk, (tid >> 2) * kCodeRow + (tid & 3) * 16,
+                                                       0, 0);
+    } else {
+      const int kv0 = vt * kMBc, u = tid - 256;
       sg.codes = __builtin_amdgcn_raw_buffer_load_b128(
           rvt, (u >> 1) * (N / 2) + kv0 / 2 + 16 * (u & 1), 0, 0);
     }
-    if (tid < 64) {
-      if (t + 1 < n) {
-        const int kv0 = (t + 1) * kMBc;
-        const __amdgpu_buffer_rsrc_t rs =
-            mrsrc(KSh + (size_t)kv0 * kScaleRow, (N - kv0) * kScaleRow);
-        sg.sc = __builtin_amdgcn_raw_buffer_load_b32(rs, tid * kScaleRow, 0, 0);
-      }
-    } else if (tid < 64 + kMD) {
-      if (t >= 1 && t - 1 < n) {
-        const int kv0 = (t - 1) * kMBc, col = tid - 64;
-        const uint32_t b0 = __builtin_amdgcn_raw_buffer_load_b8(rvs, col * nvb + kv0 / 32, 0, 0);
-        // a key block past N gets a neutral scale (its codes meet zero P codes)
-        const uint32_t b1 =
-            (kv0 + 32 < N) ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(
-                                 rvs, col * nvb + kv0 / 32 + 1, 0, 0)
-                           : 127u;
-        sg.sc = b0 | (b1 << 8);
-      }
+    if (wave == 0) {
+      const int kv0 = kt * kMBc;
+      const __amdgpu_buffer_rsrc_t rs = mrsrc(KSh + (size_t)kv0 * kScaleRow, (N - kv0) * kScaleRow);
+      sg.sc = __builtin_amdgcn_raw_buffer_load_b32(rs, tid * kScaleRow, 0, 0);
+    } else if (wave < 3) {
+      const int kv0 = vt * kMBc, col = tid - 64;
+      const uint32_t b0 = __builtin_amdgcn_raw_buffer_load_b8(rvs, col * nvb + kv0 / 32, 0, 0);
+      // a key block past N gets a neutral scale (its codes meet zero P codes); the load
+      // reads block 0 then, which is in range
+      const uint32_t b1 = __builtin_amdgcn_raw_buffer_load_b8(
+          rvs, col * nvb + (kv0 + 32 < N ? kv0 / 32 + 1 : 0), 0, 0);
+      sg.sc = b0 | ((kv0 + 32 < N ? b1 : 127u) << 8);
     }
   };
   auto store_stage = [&](const MStage& sg, int t) {
     MBuf& bb = buf[t & 1];
-    if (tid < 256) {
+    if (wave < 4) {
       if (t + 1 < n) {
         const int row = tid >> 2, cc = tid & 3;
         bb.kcode[row * 4 + (cc ^ kswz(row))] = sg.codes;
@@ -333,9 +332,9 @@ void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict_
       const int u = tid - 256, col = u >> 1, hh = u & 1;
       bb.vcode[col * 2 + (hh ^ ((col >> 3) & 1))] = sg.codes;
     }
-    if (tid < 64) {
+    if (wave == 0) {
       if (t + 1 < n) bb.kscale[tid] = sg.sc;
-    } else if (tid < 64 + kMD) {
+    } else if (wave < 3) {
       if (t >= 1 && t - 1 < n) {
         const int col = tid - 64;
         bb.vscale[col * 2] = (uint8_t)(sg.sc & 0xFF);
@@ -415,19 +414,25 @@ void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict_
   bool any_prev = false;
   float alpha_prev = 1.f;
   const int n_full = CAUSAL ? min(Q0, N) / kMBc : N / kMBc;
-  for (int j = 0; j < n; ++j) {
+  auto rescale = [&]() {
     if (any_prev) {
 #pragma unroll
       for (int i = 0; i < kMD / 32; ++i) acc[i] *= alpha_prev;
       lacc *= alpha_prev;
     }
-    mfmas(buf[j & 1], p_prev, e_prev, j >= 1, j + 1 < n, s_nxt);
+  };
+  // Pipeline step j: PV and row sum of tile j-1 (pp, ep), QK of tile j+1 into sn,
+  // Direct-P of tile j (sc -> pc, ec); then the staging of stage j+1 and the barrier.
+  auto step = [&](int j, bool pv, bool qk, bool masked, f32x16 (&sc)[2], f32x16 (&sn)[2],
+                  const u32x4& pp, uint32_t ep, u32x4& pc, uint32_t& ec) {
+    rescale();
+    mfmas(buf[j & 1], pp, ep, pv, qk, sn);
     float alpha;
     bool any;
-    if (j >= n_full)
-      any = directp_tile<CAUSAL, true>(s_cur, p_cur, e_cur, m, alpha, j * kMBc, qi, N, c, tau, h);
+    if (masked)
+      any = directp_tile<CAUSAL, true>(sc, pc, ec, m, alpha, j * kMBc, qi, N, c, tau, h);
     else
-      any = directp_tile<CAUSAL, false>(s_cur, p_cur, e_cur, m, alpha, j * kMBc, qi, N, c, tau, h);
+      any = directp_tile<CAUSAL, false>(sc, pc, ec, m, alpha, j * kMBc, qi, N, c, tau, h);
     any_prev = any;
     alpha_prev = alpha;
     if (active(j)) {
@@ -438,18 +443,36 @@ void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict_
       first = false;
     }
     store_stage(stg, j + 1);
-    if (j + 2 <= n) load_stage(stg, j + 2);
+    load_stage(stg, j + 2);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  auto advance = [&]() {
 #pragma unroll
     for (int i = 0; i < 2; ++i) s_cur[i] = s_nxt[i];
     p_prev = p_cur;
     e_prev = e_cur;
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+
+  // step 0 has no PV product (no tile before it)
+  step(0, false, n > 1, 0 >= n_full, s_cur, s_nxt, p_prev, e_prev, p_cur, e_cur);
+  advance();
+  int j = 1;
+  // unmasked steps with both products, two at a time with the S / P registers swapping
+  // roles (no copies)
+  for (; j + 1 < min(n_full, n - 1); j += 2) {
+    step(j, true, true, false, s_cur, s_nxt, p_prev, e_prev, p_cur, e_cur);
+    step(j + 1, true, true, false, s_nxt, s_cur, p_cur, e_cur, p_prev, e_prev);
   }
-  if (any_prev) {
-#pragma unroll
-    for (int i = 0; i < kMD / 32; ++i) acc[i] *= alpha_prev;
-    lacc *= alpha_prev;
+  for (; j < n - 1; ++j) {
+    step(j, true, true, j >= n_full, s_cur, s_nxt, p_prev, e_prev, p_cur, e_cur);
+    advance();
   }
+  // the last step has no QK product (no tile after it)
+  if (n > 1) {
+    step(n - 1, true, false, n - 1 >= n_full, s_cur, s_nxt, p_prev, e_prev, p_cur, e_cur);
+    advance();
+  }
+  rescale();
   mfmas(buf[n & 1], p_prev, e_prev, true, false, s_nxt);
 
   // ---- epilogue: O = acc / l, LSE = ln2 * m + ln l ----
