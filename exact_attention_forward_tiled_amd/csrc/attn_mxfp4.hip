@@ -178,14 +178,16 @@ __device__ __forceinline__ bool directp_tile(const f32x16 (&s)[2], u32x4& codes,
     const int key = kv0 + 32 * h + 16 * mb + r;
     return key < N && (!CAUSAL || key <= qi);
   };
-  float bm = NEG_INF;
+  // block max over this lane's 32 scores: four independent chains
+  float bq[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float v = (!MASK || visible(mb, r)) ? s[mb][r] : NEG_INF;
-      bm = fmaxf(bm, v);
+      bq[r & 3] = fmaxf(bq[r & 3], v);
     }
+  const float bm = fmaxf(fmaxf(bq[0], bq[1]), fmaxf(bq[2], bq[3]));
   const float Mb = (bm == NEG_INF) ? NEG_INF : bm * c;      // this lane's block max (log2)
   auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(Mb), __float_as_uint(Mb), false,
                                              false);
