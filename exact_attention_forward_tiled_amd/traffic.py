@@ -58,7 +58,8 @@ def main():
     ap.add_argument("--attn-write", required=True)
     ap.add_argument("--copy-fetch", required=True)
     ap.add_argument("--copy-write", required=True)
-    ap.add_argument("--kernel-filter", default="fwd_bf16_kernel")
+    ap.add_argument("--kernel-filter", default=None,
+                    help="kernel-name substring (default: the workload's forward kernel)")
     ap.add_argument("--copy-filter", default="copy")
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles", "traffic.json"))
     args = ap.parse_args()
@@ -66,22 +67,26 @@ def main():
     import bench
     import synth
     w = synth.workload(args.config)
+    kfilter = args.kernel_filter or ("fwd_bf16_kernel" if w.fmt == "bf16" else "fwd_mxfp4_kernel")
 
     copy_bytes = args.copy_mib * (1 << 20)
     cf = statistics.median(counter_values(args.copy_fetch, "FETCH_SIZE", args.copy_filter))
     cw = statistics.median(counter_values(args.copy_write, "WRITE_SIZE", args.copy_filter))
     f_fetch = copy_bytes / (cf * 1024.0)
     f_write = copy_bytes / (cw * 1024.0)
-    af = statistics.mean(counter_values(args.attn_fetch, "FETCH_SIZE", args.kernel_filter))
-    aw = statistics.mean(counter_values(args.attn_write, "WRITE_SIZE", args.kernel_filter))
+    af = statistics.mean(counter_values(args.attn_fetch, "FETCH_SIZE", kfilter))
+    aw = statistics.mean(counter_values(args.attn_write, "WRITE_SIZE", kfilter))
     fetch_b = af * 1024.0 * f_fetch
     write_b = aw * 1024.0 * f_write
 
-    # algorithmic bytes: one read of Q, K, V (bf16) and one write of O, LSE (fp32)
-    alg_in = 2 * (w.B * w.Hq * w.N * w.d + 2 * w.B * w.Hkv * w.N * w.d)
+    # algorithmic bytes: one read of the operands and one write of O, LSE (fp32).
+    # bf16: Q, K, V at 2 B per element.  mxfp4: E2M1 codes (0.5 B) plus one E8M0 scale
+    # byte per 32 elements, for Q, K and the transposed V.
+    elems = w.B * w.Hq * w.N * w.d + 2 * w.B * w.Hkv * w.N * w.d
+    alg_in = 2 * elems if w.fmt == "bf16" else elems // 2 + elems // 32
     alg_out = 4 * (w.B * w.Hq * w.N * w.d + w.B * w.Hq * w.N)
 
-    rec = {"kernel_hash": bench.kernel_hash(),
+    rec = {"kernel_hash": bench.kernel_hash(w.fmt), "kernel_filter": kfilter,
            "hbm_bytes_per_launch": round(fetch_b + write_b),
            "fetch_bytes_per_launch": round(fetch_b), "write_bytes_per_launch": round(write_b),
            "algorithmic_bytes_per_launch": alg_in + alg_out,
