@@ -176,6 +176,32 @@ def test_scale_sign_and_zero():
             _check(o, lse, ro, rl, f"scale={scale} causal={causal}")
 
 
+def test_extreme_logits():
+    """Logits far past 500 (the range-guard regime named in "Hardware-Aware FP4
+    FlashAttention-4", section "1. Direct-P para Inferencia Directa").  The online softmax
+    keeps every weight relative to the running max, so nothing under- or overflows and O
+    keeps its tolerance.  The LSE moves with the scores' own fp32 summation error, which
+    grows with their size: |dS| <= d u sum_k |q_k k_k| for any summation order (u = 2^-24),
+    and |dLSE| <= scale max |dS|, so the LSE bound adds that term to the usual 1e-3."""
+    qb, kb, vb = random_case(38, 1, 2, 2, 256, 128, sigma=6.0)
+    q64, k64, v64 = (synth.bf16_bits_to_f64(x) for x in (qb, kb, vb))
+    scale = 1.0
+    logits = np.einsum("bhid,bhjd->bhij", q64, k64) * scale
+    assert np.abs(logits).max() > 500
+    absum = np.einsum("bhid,bhjd->bhij", np.abs(q64), np.abs(k64))
+    bound = BF16_LSE_ABS + scale * 128 * 2.0 ** -24 * absum.max()
+    log(f"max |logit| {np.abs(logits).max():.0f}; LSE bound {bound:.3e}")
+    for causal in (False, True):
+        o, lse = _run(qb, kb, vb, causal, scale)
+        ro, rl = oracle.attention(q64, k64, v64, causal, scale)
+        assert np.isfinite(o).all() and np.isfinite(lse).all()
+        r = rel_rms(o, ro)
+        e = float(np.max(np.abs(lse - rl)))
+        log(f"  causal={causal}: relRMS(O)={r:.3e} max|dLSE|={e:.3e}")
+        assert r <= BF16_O_RELRMS
+        assert e <= bound
+
+
 def test_skip_ratio_stats():
     """The rescale counter: tau = 0 rescales on most steps, tau = 8 skips most of them."""
     import torch

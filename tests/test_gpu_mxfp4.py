@@ -129,6 +129,38 @@ def test_directp_scale_sign_and_large_logits():
         assert r <= MXFP4_O_RELRMS
 
 
+def test_directp_extreme_logits():
+    """Logits far past 500, the regime of the range guard in "Hardware-Aware FP4
+    FlashAttention-4", section "1. Direct-P para Inferencia Directa" (Protección de Rango).
+    Here the integer reference max follows the true running max, so the leading blocks of a
+    row never underflow.  Blocks more than about 125 binades below it have E < -127 and are
+    flushed to zero by the stated rule, in the kernel and in the emulation alike.  The inputs
+    are checked to be extreme (|logit| > 500) and to exercise the flush."""
+    q, k, v = _case(25, 1, 2, 2, 256, sigma=6.0)
+    scale = 1.0
+    t = mx.quantize_inputs(q, k, v)
+    logits = np.einsum("bhid,bhjd->bhij", t["q"], t["k"]) * scale
+    assert np.abs(logits).max() > 500
+    tl = logits * mx.LOG2E
+    m = np.ceil(tl.max(-1, keepdims=True))
+    e_blk = np.floor(tl.reshape(*tl.shape[:-1], -1, mx.BLOCK).max(-1) - m) - 2
+    log(f"max |logit| {np.abs(logits).max():.0f}; flushed (row, block) pairs "
+        f"{np.mean(e_blk < -127):.2f}")
+    assert np.mean(e_blk < -127) > 0.1
+    # fp32 summation error of the scores themselves (any order; u = 2^-24), in log units
+    absum = np.einsum("bhid,bhjd->bhij", np.abs(t["q"]), np.abs(t["k"]))
+    ds = scale * 128 * 2.0 ** -24 * absum.max()
+    for causal in (False, True):
+        o, lse = _run(q, k, v, causal, scale)
+        ro, rl = _reference(q, k, v, causal, scale)
+        assert np.isfinite(o).all() and np.isfinite(lse).all()
+        r = rel_rms(o, ro)
+        e = float(np.max(np.abs(lse - rl)))
+        log(f"  causal={causal}: relRMS(O)={r:.3e} max|dLSE|={e:.3e} (bound {0.05 + ds:.3e})")
+        assert r <= MXFP4_O_RELRMS
+        assert e <= 0.05 + ds
+
+
 def test_directp_constant_v_gives_one():
     q, k, _ = _case(22, 1, 4, 2, 256, sigma=2.0)
     v = np.ones((1, 2, 256, 128), np.float32)
