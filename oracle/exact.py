@@ -13,6 +13,12 @@ recomputation reach the same output without storing the N x N matrix):
     O[i,:] = sum_j exp(s_ij - m_i) * v[j, :] / l_i
     LSE_i  = m_i + ln(l_i)                      (natural log)
 
+Sliding window (the FlexAttention news page, body: sliding window attention is
+one of the patterns the FA4 backend serves; the page prints no definition).
+Reading: with a window W >= 1, key j is visible from query i only when
+i - W < j, and, without the causal mask, also j < i + W (a band of half-width
+W - 1 around the diagonal).  W = 0 means no window.
+
 Grouped-query attention (named in the same section's FlashAttention-2 entry)
 maps query head hq to key/value head hq // (Hq / Hkv).  A row whose keys are
 all masked (never reached with the causal mask when Q and K have the same
@@ -37,12 +43,26 @@ def scores(q_rows, k_head, scale):
     return scale * (q_rows @ k_head.T)
 
 
-def apply_mask(s, row_ids, causal):
-    """Additive -inf mask: key j is hidden from query i when causal and j > i."""
-    if not causal:
+def visible(row_ids, n_keys, causal, window=0):
+    """Boolean [rows, n_keys]: key j visible from query i (causal: j <= i; window W:
+    i - W < j, and j < i + W when not causal)."""
+    i = np.asarray(row_ids)[:, None]
+    j = np.arange(n_keys)[None, :]
+    ok = np.ones((i.shape[0], n_keys), dtype=bool)
+    if causal:
+        ok &= j <= i
+    if window:
+        ok &= j > i - window
+        if not causal:
+            ok &= j < i + window
+    return ok
+
+
+def apply_mask(s, row_ids, causal, window=0):
+    """Additive -inf mask on the keys that `visible` hides."""
+    if not causal and not window:
         return s
-    cols = np.arange(s.shape[1])
-    return np.where(cols[None, :] > row_ids[:, None], -np.inf, s)
+    return np.where(visible(row_ids, s.shape[1], causal, window), s, -np.inf)
 
 
 def softmax_parts(s):
@@ -65,29 +85,29 @@ def finish(m, e, l, v_head):
     return o, lse
 
 
-def attention_rows(q, k, v, causal, scale, b, hq, rows):
+def attention_rows(q, k, v, causal, scale, b, hq, rows, window=0):
     """O and LSE for the listed query rows of one (batch, query head) slice."""
     B, Hq, N, d = q.shape
     hk = kv_head(hq, Hq, k.shape[1])
     rows = np.asarray(rows, dtype=np.int64)
     s = scores(q[b, hq, rows, :], k[b, hk], scale)
-    s = apply_mask(s, rows, causal)
+    s = apply_mask(s, rows, causal, window)
     m, e, l = softmax_parts(s)
     return finish(m, e, l, v[b, hk])
 
 
-def attention_head(q, k, v, causal, scale, b, hq, chunk=512):
+def attention_head(q, k, v, causal, scale, b, hq, chunk=512, window=0):
     """All rows of one (batch, query head) slice, in chunks of whole rows."""
     N = q.shape[2]
     o = np.empty((N, v.shape[3]), dtype=np.float64)
     lse = np.empty((N,), dtype=np.float64)
     for r0 in range(0, N, chunk):
         rows = np.arange(r0, min(N, r0 + chunk))
-        o[rows], lse[rows] = attention_rows(q, k, v, causal, scale, b, hq, rows)
+        o[rows], lse[rows] = attention_rows(q, k, v, causal, scale, b, hq, rows, window)
     return o, lse
 
 
-def attention(q, k, v, causal, scale, chunk=512):
+def attention(q, k, v, causal, scale, chunk=512, window=0):
     """Exact forward over the whole [B, Hq, N, d] problem: returns (O, LSE)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -99,11 +119,11 @@ def attention(q, k, v, causal, scale, chunk=512):
     lse = np.empty(q.shape[:3], dtype=np.float64)
     for b in range(B):
         for hq in range(Hq):
-            o[b, hq], lse[b, hq] = attention_head(q, k, v, causal, scale, b, hq, chunk)
+            o[b, hq], lse[b, hq] = attention_head(q, k, v, causal, scale, b, hq, chunk, window)
     return o, lse
 
 
-def attention_brute(q, k, v, causal, scale):
+def attention_brute(q, k, v, causal, scale, window=0):
     """The same definition as scalar Python loops with math.exp (tiny inputs only)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -120,6 +140,8 @@ def attention_brute(q, k, v, causal, scale):
                 s = []
                 for j in range(Nk):
                     if causal and j > i:
+                        continue
+                    if window and (i - j >= window or (not causal and j - i >= window)):
                         continue
                     acc = 0.0
                     for c in range(d):

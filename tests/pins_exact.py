@@ -192,6 +192,80 @@ def pin_dominant_logit(attn):
     assert abs(lse[0, 0, 3] - 50.0) < 1e-12
 
 
+# ---- sliding window (attn(..., window=W)) -----------------------------------------------
+
+def _visible_range(i, N, causal, W):
+    """[lo, hi] of the keys query i sees under window W (W = 0: no window)."""
+    lo = max(0, i - W + 1) if W else 0
+    hi = i if causal else (min(N - 1, i + W - 1) if W else N - 1)
+    return lo, hi
+
+
+def pin_window_brute(attn):
+    """Agreement with the scalar loops on tiny shapes, windows 1..N+1, both masks."""
+    for n, (B, Hq, Hkv, N, d) in enumerate([(1, 2, 1, 7, 4), (1, 1, 1, 9, 3), (2, 2, 2, 5, 2)]):
+        q, k, v = _case(300 + n, B, Hq, Hkv, N, d, sigma=1.3)
+        for W in (1, 2, 3, N - 1, N + 1):
+            for causal in (False, True):
+                o, lse = attn(q, k, v, causal, 0.6, window=W)
+                ob, lseb = attention_brute(q, k, v, causal, 0.6, window=W)
+                assert np.max(np.abs(o - ob)) < TOL, ("window brute O", n, W, causal)
+                assert np.max(np.abs(lse - lseb)) < TOL, ("window brute LSE", n, W, causal)
+
+
+def pin_window_one(attn):
+    """W = 1: every query sees only its own key, so O_i = v_i and LSE_i = scale q_i.k_i."""
+    q, k, v = _case(310, 1, 4, 2, 12, 8)
+    for causal in (False, True):
+        o, lse = attn(q, k, v, causal, 0.45, window=1)
+        kk, vv = np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1)
+        assert np.max(np.abs(o - vv)) < TOL
+        assert np.max(np.abs(lse - 0.45 * np.sum(q * kk, axis=-1))) < TOL
+
+
+def pin_window_zero_query(attn):
+    """Q = 0: O_i is the mean of exactly the visible V rows and LSE_i = ln(their count)."""
+    N = 23
+    _, k, v = _case(311, 1, 2, 2, N, 4)
+    q = np.zeros((1, 2, N, 4))
+    for W in (1, 4, 9, 40):
+        for causal in (False, True):
+            o, lse = attn(q, k, v, causal, 0.8, window=W)
+            for i in range(N):
+                lo, hi = _visible_range(i, N, causal, W)
+                assert np.max(np.abs(o[0, :, i] - v[0, :, lo:hi + 1].mean(axis=1))) < TOL, (W, i)
+                assert abs(lse[0, 0, i] - np.log(hi - lo + 1)) < TOL, (W, i)
+
+
+def pin_window_torch(attn):
+    """Agreement with torch's CPU attention (float64) given the band as an explicit mask."""
+    q, k, v = _case(312, 1, 4, 4, 50, 16)
+    for W in (3, 17):
+        for causal in (False, True):
+            i = np.arange(50)[:, None]
+            j = np.arange(50)[None, :]
+            band = (j > i - W) & ((j <= i) if causal else (j < i + W))
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+                attn_mask=torch.from_numpy(band), scale=0.3)
+            o, _ = attn(q, k, v, causal, 0.3, window=W)
+            assert np.max(np.abs(o - ref.numpy())) < 1e-10, ("window torch", W, causal)
+
+
+def pin_window_wide_is_plain(attn):
+    """A window at least N wide hides nothing beyond the causal mask."""
+    q, k, v = _case(313, 1, 2, 1, 31, 8)
+    for causal in (False, True):
+        o0, l0 = attn(q, k, v, causal, 0.5)
+        for W in (31, 32, 1000):
+            o, l = attn(q, k, v, causal, 0.5, window=W)
+            assert np.max(np.abs(o - o0)) < TOL and np.max(np.abs(l - l0)) < TOL
+
+
+WINDOW_PINS = [pin_window_brute, pin_window_one, pin_window_zero_query, pin_window_torch,
+               pin_window_wide_is_plain]
+
+
 ALL_PINS = [pin_brute, pin_torch, pin_zero_query, pin_single_key, pin_two_keys,
             pin_constant_v, pin_identity_v, pin_shift, pin_permutations, pin_linear_in_v,
             pin_gqa, pin_causal_prefix, pin_dominant_logit]

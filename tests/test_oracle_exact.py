@@ -13,6 +13,52 @@ def test_oracle_pin(pin):
     pin(oracle.attention)
 
 
+@pytest.mark.parametrize("pin", pins_exact.WINDOW_PINS, ids=lambda p: p.__name__)
+def test_oracle_window_pin(pin):
+    pin(oracle.attention)
+
+
+# planted window mistakes: each must fail at least one window pin
+def _wmut_edge_off_by_one(monkeypatch):
+    orig = exact.visible
+
+    def bad(row_ids, n_keys, causal, window=0):
+        return orig(row_ids, n_keys, causal, window + 1 if window else 0)
+    monkeypatch.setattr(exact, "visible", bad)
+
+
+def _wmut_causal_band_both_sides(monkeypatch):
+    orig = exact.visible
+
+    def bad(row_ids, n_keys, causal, window=0):
+        ok = orig(row_ids, n_keys, causal, window)
+        if causal and window:   # forgets the causal side inside the band
+            i = np.asarray(row_ids)[:, None]
+            j = np.arange(n_keys)[None, :]
+            ok = ok | ((j > i) & (j < i + window))
+        return ok
+    monkeypatch.setattr(exact, "visible", bad)
+
+
+def _wmut_window_ignored(monkeypatch):
+    orig = exact.visible
+    monkeypatch.setattr(exact, "visible", lambda r, n, c, window=0: orig(r, n, c, 0))
+
+
+@pytest.mark.parametrize("mutant", [_wmut_edge_off_by_one, _wmut_causal_band_both_sides,
+                                    _wmut_window_ignored], ids=lambda m: m.__name__)
+def test_planted_window_mistake_is_caught(mutant, monkeypatch):
+    mutant(monkeypatch)
+    failures = []
+    for pin in pins_exact.WINDOW_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(oracle.attention)
+        except AssertionError:
+            failures.append(pin.__name__)
+    assert failures, "a planted window mistake passed every window pin"
+
+
 def test_rows_match_full():
     rng = np.random.default_rng(3)
     q = rng.standard_normal((1, 4, 40, 8))
@@ -39,7 +85,7 @@ def _mut_drop_scale(monkeypatch):
 
 
 def _mut_mask_diagonal(monkeypatch):
-    def bad(s, rows, causal):
+    def bad(s, rows, causal, window=0):
         if not causal:
             return s
         cols = np.arange(s.shape[1])
@@ -74,8 +120,8 @@ def _mut_sign(monkeypatch):
 def _mut_transposed_operand(monkeypatch):
     orig = exact.attention_rows
 
-    def bad(q, k, v, causal, scale, b, hq, rows):
-        return orig(q, k, k if k.shape == v.shape else v, causal, scale, b, hq, rows)
+    def bad(q, k, v, causal, scale, b, hq, rows, window=0):
+        return orig(q, k, k if k.shape == v.shape else v, causal, scale, b, hq, rows, window)
     monkeypatch.setattr(exact, "attention_rows", bad)
 
 
