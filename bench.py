@@ -86,10 +86,11 @@ def device_inputs(w):
 class Workload:
     """Device buffers and one launch closure for a bf16 workload."""
 
-    def __init__(self, w, exp_mode, tau, poly_frac=None):
+    def __init__(self, w, exp_mode, tau, poly_frac=None, window=0):
         import torch
         import exact_attention_forward_tiled_amd as fa
         self.w = w
+        self.window = window
         self.q, self.k, self.v = device_inputs(w)
         self.o = torch.empty((w.B, w.Hq, w.N, w.d), dtype=torch.float32, device="cuda")
         self.lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device="cuda")
@@ -99,7 +100,7 @@ class Workload:
     def launch(self, stats=None):
         self.fa.fwd(self.q, self.k, self.v, causal=self.w.causal, scale=self.w.scale, tau=self.tau,
                     exp_mode=self.exp_mode, stats=stats, out=(self.o, self.lse),
-                    poly_frac=self.poly_frac)
+                    poly_frac=self.poly_frac, window=self.window)
 
 
 class Mxfp4Workload:
@@ -126,6 +127,15 @@ class Mxfp4Workload:
         self.fa.fwd_mxfp4(self.q4, self.qs, self.k4, self.ks, self.vt4, self.vts,
                           causal=self.w.causal, scale=self.w.scale, tau=self.tau, stats=stats,
                           out=(self.o, self.lse))
+
+
+def visible_pairs(N, causal, window):
+    """(query, key) pairs a sliding window of width `window` shows (exact count)."""
+    import numpy as np
+    i = np.arange(N, dtype=np.int64)
+    lo = np.maximum(0, i - window + 1) if window else np.zeros_like(i)
+    hi = i if causal else (np.minimum(N - 1, i + window - 1) if window else np.full_like(i, N - 1))
+    return int((hi - lo + 1).sum())
 
 
 def make_workload(w, exp_mode, tau, poly_frac=None):
@@ -289,6 +299,9 @@ def main():
                     help="with --exp mix: fraction of the exponentials on the cubic")
     ap.add_argument("--tau", type=float, default=8.0)
     ap.add_argument("--extra", default="", help="other workloads to time (comma list), e.g. 3,4")
+    ap.add_argument("--window", type=int, default=0,
+                    help="also time the workload with this sliding window (bf16 only); its "
+                         "TFLOP/s count 4*d flop per visible (query, key) pair")
     ap.add_argument("--compare-exp", action="store_true",
                     help="also time the headline workload with the other exp modes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -384,6 +397,20 @@ def main():
         if wx.fmt != "bf16":
             extra["workloads"][wx.name]["pct_of_fp4_peak"] = round(
                 100.0 * tx["tflops"] / PEAK_FP4_TFLOPS, 2)
+
+    if args.window and w.fmt == "bf16":
+        log(f"timing {w.name} with window {args.window}")
+        wl = Workload(w, args.exp, args.tau, args.poly_frac, window=args.window)
+        tw = time_workload(wl, args.steps, args.warmup, args.warmup_seconds)
+        del wl
+        torch.cuda.empty_cache()
+        pairs = visible_pairs(w.N, w.causal, args.window)
+        fl = 4.0 * w.d * w.B * w.Hq * pairs
+        extra["workloads"][f"{w.name}/window={args.window}"] = {
+            "tflops_visible": round(fl / (tw["kernel_ms_avg"] * 1e-3) / 1e12, 2),
+            "kernel_ms_avg": round(tw["kernel_ms_avg"], 4),
+            "visible_pairs_per_head": pairs,
+            "time_vs_no_window": round(tw["kernel_ms_avg"] / t["kernel_ms_avg"], 4)}
 
     cpu = None
     if not args.no_cpu_baseline:

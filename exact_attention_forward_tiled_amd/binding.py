@@ -24,7 +24,8 @@ EXPORTS = ("attn_default_opts", "attn_fwd", "attn_fwd_ex", "attn_fwd_mxfp4", "at
 
 class AttnOpts(ctypes.Structure):
     _fields_ = [("tau", ctypes.c_float), ("exp_mode", ctypes.c_int),
-                ("poly_frac", ctypes.c_float), ("stats", ctypes.c_void_p)]
+                ("poly_frac", ctypes.c_float), ("stats", ctypes.c_void_p),
+                ("window", ctypes.c_int)]
 
 
 def _load():
@@ -73,7 +74,7 @@ def check(status):
     raise AttnError(f"libattn: status {status}")
 
 
-def make_opts(tau=8.0, exp_mode="hw", stats_ptr=None, poly_frac=None):
+def make_opts(tau=8.0, exp_mode="hw", stats_ptr=None, poly_frac=None, window=0):
     o = AttnOpts()
     lib.attn_default_opts(ctypes.byref(o))
     o.tau = float(tau)
@@ -81,6 +82,7 @@ def make_opts(tau=8.0, exp_mode="hw", stats_ptr=None, poly_frac=None):
     if poly_frac is not None:
         o.poly_frac = float(poly_frac)
     o.stats = stats_ptr
+    o.window = int(window)
     return o
 
 
@@ -138,9 +140,10 @@ def _stats_ptr(torch, stats):
 
 
 def fwd(q, k, v, causal=False, scale=None, tau=8.0, exp_mode="hw", stats=None, out=None,
-        poly_frac=None):
+        poly_frac=None, window=0):
     """bf16 attention forward on the GPU: returns (O fp32 [B,Hq,N,d], LSE fp32 [B,Hq,N]).
-    exp_mode "hw", "poly" or "mix" (poly_frac of the exponentials on the cubic)."""
+    exp_mode "hw", "poly" or "mix" (poly_frac of the exponentials on the cubic); window W:
+    key j visible from query i only when i - W < j (and j < i + W without the causal mask)."""
     torch = _torch()
     for t in (q, k, v):
         if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
@@ -156,7 +159,7 @@ def fwd(q, k, v, causal=False, scale=None, tau=8.0, exp_mode="hw", stats=None, o
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     else:
         o, lse = out
-    opts = make_opts(tau, exp_mode, _stats_ptr(torch, stats), poly_frac)
+    opts = make_opts(tau, exp_mode, _stats_ptr(torch, stats), poly_frac, window)
     check(attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                       B, Hq, Hkv, N, d, int(bool(causal)), float(scale), opts,
                       _stream(torch, q.device)))

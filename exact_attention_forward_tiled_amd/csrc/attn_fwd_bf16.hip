@@ -300,13 +300,16 @@ __device__ __forceinline__ void mfma_only(const u32x4* svp, const u32x4* skn,
 
 // One pipeline step: PV of tile j-1 (pp, V^T tile in svp), QK of tile j+1 into
 // sn (K tile in skn), and the online softmax of tile j (sc -> pc), interleaved.
+// MASK: keys outside [klo, khi] (this lane's visible range) or past N get -inf; klo
+// applies with WIN (a sliding window), khi when causal or with WIN.
 // Returns whether any row of the wave raised its reference max by more than tau;
 // then O must be multiplied by alpha before the next PV product.
-template <int D, bool CAUSAL, int NP, bool MASK, class Mid>
+template <int D, bool CAUSAL, int NP, bool MASK, bool WIN, class Mid>
 __device__ __forceinline__ bool step(const u32x4* svp, const u32x4* skn, const bf16x8 (&pp)[4],
                                      f32x16 (&acc)[D / 32], const bf16x8 (&qf)[D / 16],
                                      f32x16 (&sc)[2], f32x16 (&sn)[2], bf16x8 (&pc)[4],
-                                     RowState& st, float& alpha, int kv0, int qi, int N, float c,
+                                     RowState& st, float& alpha, int kv0, int klo, int khi, int N,
+                                     float c,
                                      float tau, int h, uint32_t vaddr, uint32_t kaddr, Mid&& mid) {
   using SS = StepShape<D, true, true>;
   const float NEG_INF = -__builtin_inff();
@@ -319,7 +322,8 @@ __device__ __forceinline__ bool step(const u32x4* svp, const u32x4* skn, const b
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kv0 + 32 * mb + 16 * (r >> 3) + 8 * h + (r & 7);
-        const bool ok = key < N && (!CAUSAL || key <= qi);
+        const bool ok = key < N && (!CAUSAL || key <= khi) &&
+                        (!WIN || (key >= klo && (CAUSAL || key <= khi)));
         sc[mb][r] = ok ? sc[mb][r] : NEG_INF;
       }
   }
@@ -391,12 +395,12 @@ __device__ __forceinline__ bool step(const u32x4* svp, const u32x4* skn, const b
   return any;
 }
 
-template <int D, bool CAUSAL, int NP>
+template <int D, bool CAUSAL, int NP, bool WIN>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE,
                      int Hq, int Hkv, int N, int nqb, float c, float tau, uint32_t qsign,
-                     unsigned long long* __restrict__ stats) {
+                     int window_arg, unsigned long long* __restrict__ stats) {
   using G = Geo<D>;
   __shared__ u32x4 lds[G::LDS_UNITS];
   u32x4 (*sk)[G::KUNITS] = reinterpret_cast<u32x4 (*)[G::KUNITS]>(lds);
@@ -443,25 +447,45 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   unsigned n_steps = 0, n_rescales = 0;
   bool first = true;
 
-  // Tiles of 64 keys this workgroup visits; per wave, which need element masks.
-  const int kv_end = CAUSAL ? min(N, Q0 + kBr) : N;
-  const int n = (kv_end + kBc - 1) / kBc;
-  const int wave_end = CAUSAL ? min(N, q0 + kRowsPerWave) : N;   // keys this wave can see
+  // Keys this lane sees: [klo, khi] (causal: up to its query; window W: from qi - W + 1,
+  // and up to qi + W - 1 without the causal mask).
+  constexpr int kNoBound = 0x7fffffff;
+  const int window = WIN ? window_arg : 0;   // 0 without the window instantiation
+  const int klo = window ? qi - window + 1 : -kNoBound;
+  const int khi = CAUSAL ? qi : (window ? qi + window - 1 : kNoBound);
+  // Tiles of 64 keys this workgroup visits, t0 .. t0 + n - 1 (local index j = tile - t0);
+  // the window skips the tiles below its lower edge.
+  const int t0 = window ? max(0, Q0 - window + 1) / kBc : 0;
+  const int kv_end = CAUSAL ? min(N, Q0 + kBr) : (window ? min(N, Q0 + kBr - 1 + window) : N);
+  const int n = (kv_end + kBc - 1) / kBc - t0;
+  const int wave_end = CAUSAL ? min(N, q0 + kRowsPerWave)            // keys this wave can see
+                              : (window ? min(N, q0 + kRowsPerWave - 1 + window) : N);
+  const int wave_lo = window ? q0 - window + 1 : 0;                   // the wave's lowest key
   const bool wave_live = q0 < N;
-  auto active = [&](int j) { return wave_live && j * kBc < wave_end; };
-  // Per wave: tiles [0, n_vis) need no element mask, tiles [n_vis, n_w) do, and tiles
-  // [n_w, n) are entirely masked (causal: keys past the wave's last query), so the
-  // wave skips their products and only keeps up its share of the staging.
-  const int n_w = wave_live ? (wave_end + kBc - 1) / kBc : n;
-  const int n_vis = min(CAUSAL ? (q0 + 1) / kBc : n, N / kBc);
+  auto active = [&](int j) {
+    return wave_live && (t0 + j) * kBc < wave_end && (!WIN || (t0 + j + 1) * kBc > wave_lo);
+  };
+  // Tiles [0, lo_wg) hold keys below some row's window: masked for every wave.
+  int lo_wg = 0;
+  if (window) {
+    const int x = Q0 + kBr - window;   // the largest lower edge of the workgroup's rows
+    lo_wg = x > t0 * kBc ? min(n, (x + kBc - 1) / kBc - t0) : 0;
+  }
+  // Per wave: tiles [lo_wg, n_vis) need no element mask, tiles [n_vis, n_w) do, and tiles
+  // [n_w, n) are entirely masked (keys past the wave's last visible key), so the wave
+  // skips their products and only keeps up its share of the staging.
+  const int n_w = wave_live ? (wave_end + kBc - 1) / kBc - t0 : n;
+  const int n_vis = max(0, min(CAUSAL ? (q0 + 1) / kBc : (window ? (q0 + window) / kBc : t0 + n),
+                               N / kBc) - t0);
 
   auto tile_rsrc = [&](const uint16_t* head, int kv0) {
     return make_rsrc(head + (size_t)kv0 * D, (N - kv0) * G::ROW_BYTES);
   };
-  // Stage t (read by pipeline step t from buffer t & 1) holds K tile t+1 and V tile t-1.
+  // Stage t (read by pipeline step t from buffer t & 1) holds K tile t+1 and V tile t-1
+  // (local indices).
   auto load_stage = [&](Stage<D>& s, int t) {
-    if (t + 1 < n) load_k<D>(s, tile_rsrc(Kh, (t + 1) * kBc), tid);
-    if (t >= 1 && t - 1 < n) load_v<D>(s, tile_rsrc(Vh, (t - 1) * kBc), tid);
+    if (t + 1 < n) load_k<D>(s, tile_rsrc(Kh, (t0 + t + 1) * kBc), tid);
+    if (t >= 1 && t - 1 < n) load_v<D>(s, tile_rsrc(Vh, (t0 + t - 1) * kBc), tid);
   };
   auto store_stage = [&](const Stage<D>& s, int t) {
     if (t + 1 < n) store_k<D>(s, sk[t & 1], tid);
@@ -478,7 +502,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   Stage<D> stg;
   {
     Stage<D> s0;
-    load_k<D>(s0, tile_rsrc(Kh, 0), tid);
+    load_k<D>(s0, tile_rsrc(Kh, t0 * kBc), tid);
     load_stage(stg, 0);
     store_k<D>(s0, sk[1], tid);
     store_stage(stg, 0);
@@ -534,34 +558,46 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   auto staging = [&](int j) {
     store_k<D>(stg, sk[(j + 1) & 1], tid);
     store_v<D>(stg, sv[(j + 1) & 1], tid);
-    load_k<D>(stg, tile_rsrc(Kh, min(j + 3, n - 1) * kBc), tid);
-    load_v<D>(stg, tile_rsrc(Vh, min(j + 1, n - 1) * kBc), tid);
+    load_k<D>(stg, tile_rsrc(Kh, (t0 + min(j + 3, n - 1)) * kBc), tid);
+    load_v<D>(stg, tile_rsrc(Vh, (t0 + min(j + 1, n - 1)) * kBc), tid);
   };
 
-  // Tiles [0, n_full) need no element mask for any row of the workgroup: causal,
-  // the keys below the workgroup's first query; otherwise the whole 64-key tiles.
-  const int n_full = CAUSAL ? min(Q0, N) / kBc : N / kBc;
+  // Tiles [lo_wg, n_full) need no element mask for any row of the workgroup: causal, the
+  // keys below the workgroup's first query; a non-causal window, the keys below its first
+  // query's upper edge; otherwise the whole 64-key tiles.
+  const int n_full =
+      max(0, (CAUSAL ? min(Q0, N) : (window ? min(Q0 + window, N) : N)) / kBc - t0);
   int j = 0;
+  // The window's lower edge: masked steps for every wave.
+  for (; j < lo_wg; ++j) {
+    rescale();
+    float alpha;
+    const bool any = step<D, CAUSAL, NP, true, WIN>(
+        sv[j & 1], sk[j & 1], p_prev, acc, qf, s_cur, s_nxt, p_cur, st, alpha, (t0 + j) * kBc,
+        klo, khi, N, c, tau, h, vaddr, kaddr, [&]() { staging(j); });
+    finish_step(j, any, alpha);
+    advance();
+  }
   // Unmasked tiles two at a time, with the roles of the S and P registers swapped in
   // the second step, so that no register copies are needed.
   for (; j + 1 < n_full; j += 2) {
     float alpha;
     rescale();
-    bool any = step<D, CAUSAL, NP, false>(
-        sv[j & 1], sk[j & 1], p_prev, acc, qf, s_cur, s_nxt, p_cur, st, alpha, j * kBc, qi, N, c,
+    bool any = step<D, CAUSAL, NP, false, WIN>(
+        sv[j & 1], sk[j & 1], p_prev, acc, qf, s_cur, s_nxt, p_cur, st, alpha, (t0 + j) * kBc, klo, khi, N, c,
         tau, h, vaddr, kaddr, [&]() { staging(j); });
     finish_step(j, any, alpha);
     rescale();
-    any = step<D, CAUSAL, NP, false>(
+    any = step<D, CAUSAL, NP, false, WIN>(
         sv[(j + 1) & 1], sk[(j + 1) & 1], p_cur, acc, qf, s_nxt, s_cur, p_prev, st, alpha,
-        (j + 1) * kBc, qi, N, c, tau, h, vaddr, kaddr, [&]() { staging(j + 1); });
+        (t0 + j + 1) * kBc, klo, khi, N, c, tau, h, vaddr, kaddr, [&]() { staging(j + 1); });
     finish_step(j + 1, any, alpha);
   }
   for (; j < n_full; ++j) {
     rescale();
     float alpha;
-    const bool any = step<D, CAUSAL, NP, false>(
-        sv[j & 1], sk[j & 1], p_prev, acc, qf, s_cur, s_nxt, p_cur, st, alpha, j * kBc, qi, N, c,
+    const bool any = step<D, CAUSAL, NP, false, WIN>(
+        sv[j & 1], sk[j & 1], p_prev, acc, qf, s_cur, s_nxt, p_cur, st, alpha, (t0 + j) * kBc, klo, khi, N, c,
         tau, h, vaddr, kaddr, [&]() { staging(j); });
     finish_step(j, any, alpha);
     advance();
@@ -573,8 +609,8 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   for (; j < n_vis; ++j) {
     rescale();
     float alpha;
-    const bool any = step<D, CAUSAL, NP, false>(
-        sv[j & 1], sk[j & 1], p_prev, acc, qf, s_cur, s_nxt, p_cur, st, alpha, j * kBc, qi, N, c,
+    const bool any = step<D, CAUSAL, NP, false, WIN>(
+        sv[j & 1], sk[j & 1], p_prev, acc, qf, s_cur, s_nxt, p_cur, st, alpha, (t0 + j) * kBc, klo, khi, N, c,
         tau, h, vaddr, kaddr, [&]() { staging(j); });
     finish_step(j, any, alpha);
     advance();
@@ -582,8 +618,8 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   for (; j < n_w; ++j) {
     rescale();
     float alpha;
-    const bool any = step<D, CAUSAL, NP, true>(
-        sv[j & 1], sk[j & 1], p_prev, acc, qf, s_cur, s_nxt, p_cur, st, alpha, j * kBc, qi, N, c,
+    const bool any = step<D, CAUSAL, NP, true, WIN>(
+        sv[j & 1], sk[j & 1], p_prev, acc, qf, s_cur, s_nxt, p_cur, st, alpha, (t0 + j) * kBc, klo, khi, N, c,
         tau, h, vaddr, kaddr, [&]() { staging(j); });
     finish_step(j, any, alpha);
     advance();
@@ -645,35 +681,40 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   }
 }
 
-template <int D, bool CAUSAL, int NP>
+template <int D, bool CAUSAL, int NP, bool WIN>
 hipError_t launch_one(const FwdArgs& a) {
   const int nqb = (a.N + kBr - 1) / kBr;
   const long long grid = (long long)a.B * a.Hq * nqb;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NP>), dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NP, WIN>), dim3((unsigned)grid), dim3(kThreads), 0,
                      (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                      (const uint16_t*)a.v, a.o, a.lse, a.Hq, a.Hkv, a.N, nqb, a.c, a.tau, a.qsign,
-                     a.stats);
+                     a.window, a.stats);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool WIN>
 hipError_t launch_np(const FwdArgs& a) {
   switch (a.poly_pairs) {
-    case 0: return launch_one<D, CAUSAL, 0>(a);
-    case 4: return launch_one<D, CAUSAL, 4>(a);
-    case 8: return launch_one<D, CAUSAL, 8>(a);
-    case 12: return launch_one<D, CAUSAL, 12>(a);
-    case 16: return launch_one<D, CAUSAL, 16>(a);
+    case 0: return launch_one<D, CAUSAL, 0, WIN>(a);
+    case 4: return launch_one<D, CAUSAL, 4, WIN>(a);
+    case 8: return launch_one<D, CAUSAL, 8, WIN>(a);
+    case 12: return launch_one<D, CAUSAL, 12, WIN>(a);
+    case 16: return launch_one<D, CAUSAL, 16, WIN>(a);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_win(const FwdArgs& a) {
+  return a.window ? launch_np<D, CAUSAL, true>(a) : launch_np<D, CAUSAL, false>(a);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
-  if (a.d == 128) return a.causal ? launch_np<128, true>(a) : launch_np<128, false>(a);
-  return a.causal ? launch_np<64, true>(a) : launch_np<64, false>(a);
+  if (a.d == 128) return a.causal ? launch_win<128, true>(a) : launch_win<128, false>(a);
+  return a.causal ? launch_win<64, true>(a) : launch_win<64, false>(a);
 }
 
 }  // namespace attn

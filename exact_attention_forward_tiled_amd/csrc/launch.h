@@ -19,6 +19,8 @@ struct FwdArgs {
   uint32_t qsign;   // 0x80008000 flips the sign of every bf16 Q element (scale < 0)
   int poly_pairs;   // of each lane's 16 score pairs per tile, how many use the cubic exp2
                     // (0, 4, 8, 12 or 16; the rest use v_exp_f32)
+  int window;       // sliding window W (0: none; 1 <= W < N): key j visible from query i
+                    // only when i - W < j, and j < i + W without the causal mask
   unsigned long long* stats;
   void* stream;
 };

@@ -70,9 +70,17 @@ typedef struct attn_opts {
                                 [2] shader-clock cycles and [3] 100 MHz reference-clock ticks
                                 from start to end of each workgroup (its first wave), summed:
                                 the mean shader clock is [2] / [3] * 100 MHz. */
+    int window;              /* sliding window W >= 0 (the FlexAttention news page names sliding
+                                window attention among the patterns the FA4 backend serves; it
+                                prints no definition).  W = 0: no window.  W >= 1: key j is
+                                visible from query i only when i - W < j, and, without the
+                                causal mask, also j < i + W.  Tiles wholly outside the band are
+                                skipped.  bf16 forward only: the MXFP4 forward returns
+                                ATTN_EUNSUPPORTED for W != 0. */
 } attn_opts;
 
-/* Default options: tau = 8, hardware exp (poly_frac 0.5 for ATTN_EXP_MIX), no stats. */
+/* Default options: tau = 8, hardware exp (poly_frac 0.5 for ATTN_EXP_MIX), no stats, no
+   window. */
 void attn_default_opts(attn_opts* opts);
 
 /*

@@ -71,6 +71,12 @@ def test_opts_validation(fa):
         opts = fa.make_opts(tau, mode, poly_frac=frac)
         st = fa.attn_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 16, 64, 0, 0.1, opts, None)
         assert st == -1
+    # a negative window is invalid for both forwards; any window is unsupported on MXFP4
+    opts = fa.make_opts(8.0, "hw", window=-1)
+    assert fa.attn_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 16, 64, 0, 0.1, opts, None) == -1
+    assert fa.attn_fwd_mxfp4_ex(*[FAKE] * 8, 1, 1, 1, 64, 128, 0, 0.1, opts, None) == -1
+    opts = fa.make_opts(8.0, "hw", window=16)
+    assert fa.attn_fwd_mxfp4_ex(*[FAKE] * 8, 1, 1, 1, 64, 128, 0, 0.1, opts, None) == -2
 
 
 def test_default_opts_layout(fa):
@@ -78,9 +84,9 @@ def test_default_opts_layout(fa):
     binding's mirror checks that the two layouts agree."""
     from exact_attention_forward_tiled_amd.binding import AttnOpts, lib
     o = AttnOpts()
-    o.tau, o.exp_mode, o.poly_frac, o.stats = -3.0, 9, -3.0, FAKE
+    o.tau, o.exp_mode, o.poly_frac, o.stats, o.window = -3.0, 9, -3.0, FAKE, -7
     lib.attn_default_opts(ctypes.byref(o))
-    assert (o.tau, o.exp_mode, o.poly_frac, o.stats) == (8.0, 0, 0.5, None)
+    assert (o.tau, o.exp_mode, o.poly_frac, o.stats, o.window) == (8.0, 0, 0.5, None, 0)
 
 
 def test_mxfp4_validation(fa):

@@ -202,6 +202,48 @@ def test_extreme_logits():
         assert e <= bound
 
 
+WINDOW_CASES = [
+    # B, Hq, Hkv, N, d, causal, window
+    (1, 2, 2, 256, 64, True, 1),
+    (1, 2, 2, 256, 128, False, 1),
+    (1, 2, 1, 333, 128, True, 31),
+    (1, 2, 2, 517, 128, False, 64),
+    (2, 4, 2, 700, 64, True, 100),
+    (1, 2, 2, 1000, 128, True, 200),
+    (1, 3, 3, 1000, 128, False, 257),
+    (1, 2, 2, 1100, 128, True, 1099),
+    (1, 1, 1, 2048, 128, True, 513),
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES, ids=lambda c: "B%dHq%dHkv%dN%dd%d%sW%d" % (
+    c[0], c[1], c[2], c[3], c[4], "c" if c[5] else "n", c[6]))
+def test_sliding_window(case):
+    """Sliding window against the oracle's band mask (key j visible from query i only when
+    i - W < j, and j < i + W without the causal mask)."""
+    B, Hq, Hkv, N, d, causal, W = case
+    qb, kb, vb = random_case(40 + W, B, Hq, Hkv, N, d)
+    log(f"case {case}")
+    o, lse = _run(qb, kb, vb, causal, d ** -0.5, window=W)
+    q64, k64, v64 = (synth.bf16_bits_to_f64(x) for x in (qb, kb, vb))
+    ro, rl = oracle.attention(q64, k64, v64, causal, d ** -0.5, window=W)
+    _check(o, lse, ro, rl, f"window {W}")
+
+
+def test_sliding_window_large_sampled_rows():
+    """A long causal GQA problem with a 1024-key window: sampled rows of several heads."""
+    B, Hq, Hkv, N, d, W = 1, 8, 2, 8192, 128, 1024
+    qb, kb, vb = random_case(49, B, Hq, Hkv, N, d)
+    o, lse = _run(qb, kb, vb, True, d ** -0.5, window=W)
+    q64, k64, v64 = (synth.bf16_bits_to_f64(x) for x in (qb, kb, vb))
+    rng = np.random.default_rng(49)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 1023, 1024, 1025, N - 1],
+                                     rng.integers(0, N, 24)]))
+    for h in (0, 3, Hq - 1):
+        ro, rl = oracle.attention_rows(q64, k64, v64, True, d ** -0.5, 0, h, rows, window=W)
+        _check(o[0, h, rows], lse[0, h, rows], ro, rl, f"head {h}")
+
+
 def test_skip_ratio_stats():
     """The rescale counter: tau = 0 rescales on most steps, tau = 8 skips most of them."""
     import torch
