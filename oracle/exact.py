@@ -19,6 +19,15 @@ Reading: with a window W >= 1, key j is visible from query i only when
 i - W < j, and, without the causal mask, also j < i + W (a band of half-width
 W - 1 around the diagonal).  W = 0 means no window.
 
+Score modifications (the same page names ALiBi and soft-capping among the patterns the
+FA4 backend serves, again without definitions).  Readings, applied to the scaled score
+before the mask, soft-capping first:
+
+    soft-capping with cap C > 0:    s_ij <- C * tanh(s_ij / C)
+    ALiBi with per-head slope a_h:  s_ij <- s_ij - a_h * |i - j|
+
+(|i - j| = i - j under the causal mask.)  The slopes are an input, one per query head.
+
 Grouped-query attention (named in the same section's FlashAttention-2 entry)
 maps query head hq to key/value head hq // (Hq / Hkv).  A row whose keys are
 all masked (never reached with the causal mask when Q and K have the same
@@ -41,6 +50,16 @@ def kv_head(hq, Hq, Hkv):
 def scores(q_rows, k_head, scale):
     """scale * q_rows @ k^T  ->  [rows, N_k]."""
     return scale * (q_rows @ k_head.T)
+
+
+def modify_scores(s, row_ids, softcap=0.0, alibi_slope=None):
+    """Soft-capping C*tanh(s/C) (C > 0), then the ALiBi bias -slope*|i - j|."""
+    if softcap:
+        s = softcap * np.tanh(s / softcap)
+    if alibi_slope is not None:
+        dist = np.abs(np.asarray(row_ids)[:, None] - np.arange(s.shape[1])[None, :])
+        s = s - alibi_slope * dist
+    return s
 
 
 def visible(row_ids, n_keys, causal, window=0):
@@ -85,29 +104,32 @@ def finish(m, e, l, v_head):
     return o, lse
 
 
-def attention_rows(q, k, v, causal, scale, b, hq, rows, window=0):
-    """O and LSE for the listed query rows of one (batch, query head) slice."""
+def attention_rows(q, k, v, causal, scale, b, hq, rows, window=0, softcap=0.0, alibi=None):
+    """O and LSE for the listed query rows of one (batch, query head) slice.  alibi: the
+    per-query-head slopes (length Hq) or None."""
     B, Hq, N, d = q.shape
     hk = kv_head(hq, Hq, k.shape[1])
     rows = np.asarray(rows, dtype=np.int64)
     s = scores(q[b, hq, rows, :], k[b, hk], scale)
+    s = modify_scores(s, rows, softcap, None if alibi is None else float(alibi[hq]))
     s = apply_mask(s, rows, causal, window)
     m, e, l = softmax_parts(s)
     return finish(m, e, l, v[b, hk])
 
 
-def attention_head(q, k, v, causal, scale, b, hq, chunk=512, window=0):
+def attention_head(q, k, v, causal, scale, b, hq, chunk=512, window=0, softcap=0.0, alibi=None):
     """All rows of one (batch, query head) slice, in chunks of whole rows."""
     N = q.shape[2]
     o = np.empty((N, v.shape[3]), dtype=np.float64)
     lse = np.empty((N,), dtype=np.float64)
     for r0 in range(0, N, chunk):
         rows = np.arange(r0, min(N, r0 + chunk))
-        o[rows], lse[rows] = attention_rows(q, k, v, causal, scale, b, hq, rows, window)
+        o[rows], lse[rows] = attention_rows(q, k, v, causal, scale, b, hq, rows, window,
+                                            softcap, alibi)
     return o, lse
 
 
-def attention(q, k, v, causal, scale, chunk=512, window=0):
+def attention(q, k, v, causal, scale, chunk=512, window=0, softcap=0.0, alibi=None):
     """Exact forward over the whole [B, Hq, N, d] problem: returns (O, LSE)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -119,11 +141,12 @@ def attention(q, k, v, causal, scale, chunk=512, window=0):
     lse = np.empty(q.shape[:3], dtype=np.float64)
     for b in range(B):
         for hq in range(Hq):
-            o[b, hq], lse[b, hq] = attention_head(q, k, v, causal, scale, b, hq, chunk, window)
+            o[b, hq], lse[b, hq] = attention_head(q, k, v, causal, scale, b, hq, chunk, window,
+                                                  softcap, alibi)
     return o, lse
 
 
-def attention_brute(q, k, v, causal, scale, window=0):
+def attention_brute(q, k, v, causal, scale, window=0, softcap=0.0, alibi=None):
     """The same definition as scalar Python loops with math.exp (tiny inputs only)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -146,7 +169,12 @@ def attention_brute(q, k, v, causal, scale, window=0):
                     acc = 0.0
                     for c in range(d):
                         acc += float(q[b, h, i, c]) * float(k[b, g, j, c])
-                    s.append((j, scale * acc))
+                    val = scale * acc
+                    if softcap:
+                        val = softcap * math.tanh(val / softcap)
+                    if alibi is not None:
+                        val -= float(alibi[h]) * abs(i - j)
+                    s.append((j, val))
                 if not s:
                     lse[b, h, i] = -math.inf
                     continue

@@ -266,6 +266,82 @@ WINDOW_PINS = [pin_window_brute, pin_window_one, pin_window_zero_query, pin_wind
                pin_window_wide_is_plain]
 
 
+# ---- score modifications (attn(..., softcap=C, alibi=slopes)) -----------------------------
+
+def _slopes(H):
+    return 0.5 ** (np.arange(1, H + 1) * 8.0 / H)   # a geometric sequence of per-head slopes
+
+
+def pin_mod_brute(attn):
+    """Agreement with the scalar loops: soft-capping, ALiBi, both, with the masks and a window."""
+    for n, (B, Hq, Hkv, N, d) in enumerate([(1, 2, 1, 7, 4), (1, 4, 2, 9, 3), (2, 2, 2, 5, 2)]):
+        q, k, v = _case(400 + n, B, Hq, Hkv, N, d, sigma=2.0)
+        for causal in (False, True):
+            for cap, alibi, W in ((3.0, None, 0), (0.0, _slopes(Hq), 0), (2.5, _slopes(Hq), 0),
+                                  (4.0, _slopes(Hq), 3)):
+                o, lse = attn(q, k, v, causal, 0.7, window=W, softcap=cap, alibi=alibi)
+                ob, lb = attention_brute(q, k, v, causal, 0.7, window=W, softcap=cap, alibi=alibi)
+                assert np.max(np.abs(o - ob)) < TOL and np.max(np.abs(lse - lb)) < TOL, \
+                    ("mod brute", n, causal, cap, alibi is not None, W)
+
+
+def pin_mod_torch(attn):
+    """torch's CPU attention (float64) fed the modified scores as an additive mask with
+    Q = 0 (ALiBi: the bias; soft-capping: the capped scores themselves)."""
+    q, k, v = _case(410, 1, 4, 4, 40, 8, sigma=2.0)
+    i = np.arange(40)[:, None]
+    j = np.arange(40)[None, :]
+    for causal in (False, True):
+        hide = (j > i) if causal else np.zeros((40, 40), bool)
+        for cap, alibi in ((3.0, None), (0.0, _slopes(4)), (2.0, _slopes(4))):
+            s = 0.5 * np.einsum("bhid,bhjd->bhij", q, k)
+            if cap:
+                s = cap * np.tanh(s / cap)
+            if alibi is not None:
+                s = s - alibi[None, :, None, None] * np.abs(i - j)[None, None]
+            s = np.where(hide[None, None], -np.inf, s)
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.zeros(1, 4, 40, 8, dtype=torch.float64), torch.from_numpy(k),
+                torch.from_numpy(v), attn_mask=torch.from_numpy(s))
+            o, _ = attn(q, k, v, causal, 0.5, softcap=cap, alibi=alibi)
+            assert np.max(np.abs(o - ref.numpy())) < 1e-10, ("mod torch", causal, cap)
+
+
+def pin_alibi_zero_query(attn):
+    """Q = 0 with ALiBi: the weights are exp(-a |i - j|), so O_i and LSE_i are explicit
+    geometric sums over the visible keys."""
+    N = 19
+    _, k, v = _case(411, 1, 2, 2, N, 4)
+    q = np.zeros((1, 2, N, 4))
+    slopes = np.array([0.3, 1.7])
+    for causal in (False, True):
+        o, lse = attn(q, k, v, causal, 0.9, alibi=slopes)
+        for h in range(2):
+            for r in range(N):
+                js = np.arange(0, r + 1 if causal else N)
+                w = np.exp(-slopes[h] * np.abs(r - js))
+                assert np.max(np.abs(o[0, h, r] - (w @ v[0, h, js]) / w.sum())) < TOL
+                assert abs(lse[0, h, r] - np.log(w.sum())) < TOL
+
+
+def pin_softcap_limits(attn):
+    """A cap far above every score leaves attention unchanged (to the cap's cubic term);
+    scores far above the cap saturate at it, so rows of huge equal logits become uniform."""
+    q, k, v = _case(412, 1, 2, 2, 17, 8)
+    for causal in (False, True):
+        o0, l0 = attn(q, k, v, causal, 0.3)
+        o, l = attn(q, k, v, causal, 0.3, softcap=1e6)   # |C tanh(s/C) - s| <= |s|^3 / (3 C^2)
+        assert np.max(np.abs(o - o0)) < 1e-9 and np.max(np.abs(l - l0)) < 1e-9
+    k2 = np.ones_like(k)
+    q2 = np.full_like(q, 50.0)                # every score 0.3 * 8 * 50 = 120 >> cap
+    o, l = attn(q2, k2, v, False, 0.3, softcap=2.0)
+    assert np.max(np.abs(o - v.mean(axis=2, keepdims=True))) < 1e-9
+    assert np.max(np.abs(l - (2.0 * np.tanh(60.0) + np.log(17)))) < 1e-9
+
+
+MOD_PINS = [pin_mod_brute, pin_mod_torch, pin_alibi_zero_query, pin_softcap_limits]
+
+
 ALL_PINS = [pin_brute, pin_torch, pin_zero_query, pin_single_key, pin_two_keys,
             pin_constant_v, pin_identity_v, pin_shift, pin_permutations, pin_linear_in_v,
             pin_gqa, pin_causal_prefix, pin_dominant_logit]

@@ -18,6 +18,63 @@ def test_oracle_window_pin(pin):
     pin(oracle.attention)
 
 
+@pytest.mark.parametrize("pin", pins_exact.MOD_PINS, ids=lambda p: p.__name__)
+def test_oracle_score_mod_pin(pin):
+    pin(oracle.attention)
+
+
+# planted score-modification mistakes: each must fail at least one score-mod pin
+def _smut_alibi_signed(monkeypatch):
+    orig = exact.modify_scores
+
+    def bad(s, row_ids, softcap=0.0, alibi_slope=None):
+        out = orig(s, row_ids, softcap, None)
+        if alibi_slope is not None:   # i - j instead of |i - j|
+            out = out - alibi_slope * (np.asarray(row_ids)[:, None] - np.arange(s.shape[1])[None, :])
+        return out
+    monkeypatch.setattr(exact, "modify_scores", bad)
+
+
+def _smut_alibi_sign(monkeypatch):
+    orig = exact.modify_scores
+    monkeypatch.setattr(exact, "modify_scores",
+                        lambda s, r, softcap=0.0, alibi_slope=None:
+                        orig(s, r, softcap, None if alibi_slope is None else -alibi_slope))
+
+
+def _smut_softcap_unscaled(monkeypatch):
+    orig = exact.modify_scores
+
+    def bad(s, row_ids, softcap=0.0, alibi_slope=None):
+        if softcap:
+            s = np.tanh(s / softcap) * softcap ** 0.5
+        return orig(s, row_ids, 0.0, alibi_slope)
+    monkeypatch.setattr(exact, "modify_scores", bad)
+
+
+def _smut_softcap_after_bias(monkeypatch):
+    orig = exact.modify_scores
+
+    def bad(s, row_ids, softcap=0.0, alibi_slope=None):
+        s = orig(s, row_ids, 0.0, alibi_slope)
+        return softcap * np.tanh(s / softcap) if softcap else s
+    monkeypatch.setattr(exact, "modify_scores", bad)
+
+
+@pytest.mark.parametrize("mutant", [_smut_alibi_signed, _smut_alibi_sign, _smut_softcap_unscaled,
+                                    _smut_softcap_after_bias], ids=lambda m: m.__name__)
+def test_planted_score_mod_mistake_is_caught(mutant, monkeypatch):
+    mutant(monkeypatch)
+    failures = []
+    for pin in pins_exact.MOD_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(oracle.attention)
+        except AssertionError:
+            failures.append(pin.__name__)
+    assert failures, "a planted score-modification mistake passed every pin"
+
+
 # planted window mistakes: each must fail at least one window pin
 def _wmut_edge_off_by_one(monkeypatch):
     orig = exact.visible
@@ -120,8 +177,8 @@ def _mut_sign(monkeypatch):
 def _mut_transposed_operand(monkeypatch):
     orig = exact.attention_rows
 
-    def bad(q, k, v, causal, scale, b, hq, rows, window=0):
-        return orig(q, k, k if k.shape == v.shape else v, causal, scale, b, hq, rows, window)
+    def bad(q, k, v, causal, scale, b, hq, rows, *mods):
+        return orig(q, k, k if k.shape == v.shape else v, causal, scale, b, hq, rows, *mods)
     monkeypatch.setattr(exact, "attention_rows", bad)
 
 
