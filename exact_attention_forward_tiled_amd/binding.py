@@ -25,7 +25,8 @@ EXPORTS = ("attn_default_opts", "attn_fwd", "attn_fwd_ex", "attn_fwd_mxfp4", "at
 class AttnOpts(ctypes.Structure):
     _fields_ = [("tau", ctypes.c_float), ("exp_mode", ctypes.c_int),
                 ("poly_frac", ctypes.c_float), ("stats", ctypes.c_void_p),
-                ("window", ctypes.c_int)]
+                ("window", ctypes.c_int), ("alibi_slopes", ctypes.c_void_p),
+                ("softcap", ctypes.c_float)]
 
 
 def _load():
@@ -74,7 +75,8 @@ def check(status):
     raise AttnError(f"libattn: status {status}")
 
 
-def make_opts(tau=8.0, exp_mode="hw", stats_ptr=None, poly_frac=None, window=0):
+def make_opts(tau=8.0, exp_mode="hw", stats_ptr=None, poly_frac=None, window=0, alibi_ptr=None,
+              softcap=0.0):
     o = AttnOpts()
     lib.attn_default_opts(ctypes.byref(o))
     o.tau = float(tau)
@@ -83,6 +85,8 @@ def make_opts(tau=8.0, exp_mode="hw", stats_ptr=None, poly_frac=None, window=0):
         o.poly_frac = float(poly_frac)
     o.stats = stats_ptr
     o.window = int(window)
+    o.alibi_slopes = alibi_ptr
+    o.softcap = float(softcap)
     return o
 
 
@@ -140,10 +144,12 @@ def _stats_ptr(torch, stats):
 
 
 def fwd(q, k, v, causal=False, scale=None, tau=8.0, exp_mode="hw", stats=None, out=None,
-        poly_frac=None, window=0):
+        poly_frac=None, window=0, alibi=None, softcap=0.0):
     """bf16 attention forward on the GPU: returns (O fp32 [B,Hq,N,d], LSE fp32 [B,Hq,N]).
     exp_mode "hw", "poly" or "mix" (poly_frac of the exponentials on the cubic); window W:
-    key j visible from query i only when i - W < j (and j < i + W without the causal mask)."""
+    key j visible from query i only when i - W < j (and j < i + W without the causal mask);
+    alibi: float32 CUDA tensor of Hq slopes a_h (score -= a_h |i - j|); softcap C > 0: score ->
+    C tanh(score / C)."""
     torch = _torch()
     for t in (q, k, v):
         if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
@@ -159,7 +165,14 @@ def fwd(q, k, v, causal=False, scale=None, tau=8.0, exp_mode="hw", stats=None, o
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     else:
         o, lse = out
-    opts = make_opts(tau, exp_mode, _stats_ptr(torch, stats), poly_frac, window)
+    alibi_ptr = None
+    if alibi is not None:
+        if (alibi.dtype != torch.float32 or not alibi.is_cuda or not alibi.is_contiguous()
+                or alibi.numel() != Hq):
+            raise ValueError("alibi must be a contiguous float32 CUDA tensor of Hq slopes")
+        alibi_ptr = alibi.data_ptr()
+    opts = make_opts(tau, exp_mode, _stats_ptr(torch, stats), poly_frac, window, alibi_ptr,
+                     softcap)
     check(attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                       B, Hq, Hkv, N, d, int(bool(causal)), float(scale), opts,
                       _stream(torch, q.device)))

@@ -28,6 +28,7 @@ int check_opts(const attn_opts* o) {
   if (o->exp_mode == ATTN_EXP_MIX && !(o->poly_frac >= 0.f && o->poly_frac <= 1.f))
     return ATTN_EINVAL;
   if (o->window < 0) return ATTN_EINVAL;
+  if (!(o->softcap >= 0.f) || !isfinite(o->softcap)) return ATTN_EINVAL;
   return ATTN_OK;
 }
 
@@ -59,6 +60,8 @@ void attn_default_opts(attn_opts* opts) {
   opts->poly_frac = 0.5f;
   opts->stats = nullptr;
   opts->window = 0;
+  opts->alibi_slopes = nullptr;
+  opts->softcap = 0.f;
 }
 
 const char* attn_strerror(int status) {
@@ -98,6 +101,10 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, float* o, float* ls
   a.poly_pairs = poly_pairs(op);
   // a window at least N wide hides nothing: run the plain mask
   a.window = op->window >= N ? 0 : op->window;
+  a.alibi = op->alibi_slopes;
+  a.softcap = op->softcap;
+  if ((a.alibi != nullptr || a.softcap > 0.f) && op->exp_mode != ATTN_EXP_HW)
+    return ATTN_EUNSUPPORTED;
   a.stats = op->stats;
   a.stream = stream;
   return hip_status(attn::launch_fwd_bf16(a));
@@ -123,7 +130,9 @@ int attn_fwd_mxfp4_ex(const uint8_t* q4, const uint8_t* qs, const uint8_t* k4, c
   const attn_opts* op = opts ? opts : &def;
   st = check_opts(op);
   if (st != ATTN_OK) return st;
-  if (d != 128 || N % 32 != 0 || op->window != 0) return ATTN_EUNSUPPORTED;
+  if (d != 128 || N % 32 != 0 || op->window != 0 || op->alibi_slopes != nullptr ||
+      op->softcap != 0.f)
+    return ATTN_EUNSUPPORTED;
 
   attn::Mxfp4Args a;
   a.q4 = q4; a.qs = qs; a.k4 = k4; a.ks = ks; a.vt4 = vt4; a.vts = vts;

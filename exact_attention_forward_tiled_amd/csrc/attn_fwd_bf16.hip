@@ -222,7 +222,7 @@ struct RowState {
   float l;       // this lane's partial row sum (its half of each 32-key block)
 };
 
-template <int D, bool PV, bool QK>
+template <int D, bool PV, bool QK, bool MODS = false>
 struct StepShape {
   static constexpr int NPV = PV ? 4 * (D / 32) : 0;
   static constexpr int NQK = QK ? 2 * (D / 16) : 0;
@@ -230,19 +230,22 @@ struct StepShape {
   // softmax slot plan, spread evenly over the MFMA slots: row max over 32 scores in
   // MAXS slots, threshold test, new reference max, the 16 score pairs over the
   // following slots, the row-sum update in the last slot; the staging of the next
-  // K/V stage sits in the middle slot.
-  static constexpr int MAXS = NOPS >= 32 ? 8 : 4;
+  // K/V stage sits in the middle slot.  With score modifications (MODS) the max phase
+  // also turns every score into its modified log2-domain value, so it gets more slots.
+  static constexpr int MAXS = MODS ? (NOPS >= 32 ? 16 : 8) : (NOPS >= 32 ? 8 : 4);
+  static_assert(32 % MAXS == 0, "every slot of the max phase takes the same share of the 32 scores");
   static constexpr int TEST = MAXS;
   static constexpr int MNEW = MAXS + 1;
   static constexpr int PAIR0 = MAXS + 2;
   static constexpr int PAIR_SLOTS = NOPS - 1 - PAIR0;
   static constexpr int LSUM = NOPS - 1;
   static constexpr int MID = NOPS / 2;
-  // score pairs [pair_lo(k), pair_lo(k + 1)) go to slot k (at most two per slot)
+  // score pairs [pair_lo(k), pair_lo(k + 1)) go to slot k (at most MAXQ per slot)
   static constexpr int pair_lo(int k) {
     return k <= PAIR0 ? 0 : (k >= PAIR0 + PAIR_SLOTS ? 16 : ((k - PAIR0) * 16 + PAIR_SLOTS - 1) / PAIR_SLOTS);
   }
-  static_assert(!(PV && QK) || PAIR_SLOTS >= 8, "softmax must fit in the MFMA slots");
+  static constexpr int MAXQ = (16 + PAIR_SLOTS - 1) / (PAIR_SLOTS > 0 ? PAIR_SLOTS : 1);
+  static_assert(!(PV && QK) || PAIR_SLOTS >= 4, "softmax must fit in the MFMA slots");
 };
 
 // Operand i of a step: PV (ks = i / (D/32), cb = i % (D/32)), then QK (t = k/2, mb = k%2).
@@ -298,20 +301,34 @@ __device__ __forceinline__ void mfma_only(const u32x4* svp, const u32x4* skn,
   }
 }
 
+// Score modifications (the FlexAttention news page, body: ALiBi and soft-capping among
+// the patterns the FA4 backend serves), switched at compile time; the values are per
+// lane.  In log2 units, on the scaled score s:
+//   soft-capping  t = C log2(e) tanh(s / C),  tanh(x) = 1 - 2 / (1 + 2^(2 x log2 e))
+//   ALiBi         t -= a_h log2(e) |i - j|
+struct ScoreMod {
+  float alibi;    // ALiBi slope of this query head, log2 units per key of distance
+  float k2;       // soft-capping: 2 |scale| log2(e) / C (raw MFMA score to 2 x log2 e)
+  float ccap;     // soft-capping: C log2(e)
+  int qi;         // this lane's query row
+};
+
 // One pipeline step: PV of tile j-1 (pp, V^T tile in svp), QK of tile j+1 into
 // sn (K tile in skn), and the online softmax of tile j (sc -> pc), interleaved.
 // MASK: keys outside [klo, khi] (this lane's visible range) or past N get -inf; klo
 // applies with WIN (a sliding window), khi when causal or with WIN.
 // Returns whether any row of the wave raised its reference max by more than tau;
 // then O must be multiplied by alpha before the next PV product.
-template <int D, bool CAUSAL, int NP, bool MASK, bool WIN, class Mid>
+template <int D, bool CAUSAL, int NP, bool MASK, bool WIN, bool ALIBI, bool SOFTCAP, class Mid>
 __device__ __forceinline__ bool step(const u32x4* svp, const u32x4* skn, const bf16x8 (&pp)[4],
                                      f32x16 (&acc)[D / 32], const bf16x8 (&qf)[D / 16],
                                      f32x16 (&sc)[2], f32x16 (&sn)[2], bf16x8 (&pc)[4],
                                      RowState& st, float& alpha, int kv0, int klo, int khi, int N,
                                      float c,
-                                     float tau, int h, uint32_t vaddr, uint32_t kaddr, Mid&& mid) {
-  using SS = StepShape<D, true, true>;
+                                     float tau, int h, uint32_t vaddr, uint32_t kaddr,
+                                     const ScoreMod& sm, Mid&& mid) {
+  constexpr bool MODS = ALIBI || SOFTCAP;
+  using SS = StepShape<D, true, true, MODS>;
   const float NEG_INF = -__builtin_inff();
   const char* vb = (const char*)svp;
   const char* kb = (const char*)skn;
@@ -336,6 +353,24 @@ __device__ __forceinline__ bool step(const u32x4* svp, const u32x4* skn, const b
 
   float mx = NEG_INF, mt = NEG_INF, mu = 0.f;
   bool any = false;
+  // ALiBi: key - query of register r of block mb is dbase + 32 mb + 16 (r / 8) + r % 8
+  const float dbase = ALIBI ? (float)(kv0 + 8 * h - sm.qi) : 0.f;
+  // the modified score, log2 units (masked scores stay -inf)
+  auto modified = [&](float s, int mb, int r) {
+    float t;
+    if constexpr (SOFTCAP) {
+      const float y = __builtin_amdgcn_exp2f(s * sm.k2);
+      t = __builtin_fmaf(-2.f * sm.ccap, __builtin_amdgcn_rcpf(y + 1.f), sm.ccap);
+      if constexpr (MASK) t = (s == NEG_INF) ? NEG_INF : t;
+    } else {
+      t = s * c;
+    }
+    if constexpr (ALIBI) {
+      const float dd = dbase + (float)(32 * mb + 16 * (r >> 3) + (r & 7));
+      t = __builtin_fmaf(-sm.alibi, __builtin_fabsf(dd), t);
+    }
+    return t;
+  };
   u32x4 pk[4];
   float ls[4] = {0.f, 0.f, 0.f, 0.f};
 
@@ -351,11 +386,16 @@ __device__ __forceinline__ bool step(const u32x4* svp, const u32x4* skn, const b
 #pragma unroll
       for (int u = 0; u < per; ++u) {
         const int idx = k * per + u;
+        if constexpr (MODS) {
+          sc[idx >> 4][idx & 15] = modified(sc[idx >> 4][idx & 15], idx >> 4, idx & 15);
+          // a use in this slot keeps the compiler from sinking the work out of it
+          asm volatile("" ::"v"(sc[idx >> 4][idx & 15]));
+        }
         mx = fmaxf(mx, sc[idx >> 4][idx & 15]);
       }
     } else if (k == SS::TEST) {        // whole row (other half-wave), threshold test
       mx = half_swap_max(mx);
-      mt = (mx == NEG_INF) ? NEG_INF : mx * c;
+      mt = (mx == NEG_INF) ? NEG_INF : (MODS ? mx : mx * c);
       any = __ballot(mt > st.m + tau) != 0;
     } else if (k == SS::MNEW) {        // thresholded update of the reference max
       const float m_new = any ? fmaxf(st.m, mt) : st.m;
@@ -368,13 +408,13 @@ __device__ __forceinline__ bool step(const u32x4* svp, const u32x4* skn, const b
     }
     if (k >= SS::PAIR0 && k < SS::LSUM) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {    // score pairs scheduled in this slot
+      for (int q = 0; q < SS::MAXQ; ++q) {   // score pairs scheduled in this slot
         const int e = SS::pair_lo(k) + q;
         if (e < SS::pair_lo(k + 1)) {
           const int mb = e >> 3, hf = (e >> 2) & 1, ee = e & 3;
           const float s0 = sc[mb][hf * 8 + 2 * ee], s1 = sc[mb][hf * 8 + 2 * ee + 1];
-          float e0 = exp2_pair<NP>(__builtin_fmaf(s0, c, -mu), e);
-          float e1 = exp2_pair<NP>(__builtin_fmaf(s1, c, -mu), e);
+          float e0 = exp2_pair<NP>(MODS ? s0 - mu : __builtin_fmaf(s0, c, -mu), e);
+          float e1 = exp2_pair<NP>(MODS ? s1 - mu : __builtin_fmaf(s1, c, -mu), e);
           if constexpr (MASK) {
             e0 = (s0 == NEG_INF) ? 0.f : e0;
             e1 = (s1 == NEG_INF) ? 0.f : e1;
@@ -395,12 +435,13 @@ __device__ __forceinline__ bool step(const u32x4* svp, const u32x4* skn, const b
   return any;
 }
 
-template <int D, bool CAUSAL, int NP, bool WIN>
+template <int D, bool CAUSAL, int NP, bool WIN, bool ALIBI, bool SOFTCAP>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE,
                      int Hq, int Hkv, int N, int nqb, float c, float tau, uint32_t qsign,
-                     int window_arg, unsigned long long* __restrict__ stats) {
+                     int window_arg, const float* __restrict__ alibi_slopes, float k2,
+                     float ccap, unsigned long long* __restrict__ stats) {
   using G = Geo<D>;
   __shared__ u32x4 lds[G::LDS_UNITS];
   u32x4 (*sk)[G::KUNITS] = reinterpret_cast<u32x4 (*)[G::KUNITS]>(lds);
@@ -439,6 +480,12 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       qf[t] = as_bf16x8(x);
     }
   }
+
+  ScoreMod sm;
+  sm.alibi = ALIBI ? alibi_slopes[hq] * kLog2e : 0.f;
+  sm.k2 = k2;
+  sm.ccap = ccap;
+  sm.qi = qi;
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -572,9 +619,9 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   for (; j < lo_wg; ++j) {
     rescale();
     float alpha;
-    const bool any = step<D, CAUSAL, NP, true, WIN>(
+    const bool any = step<D, CAUSAL, NP, true, WIN, ALIBI, SOFTCAP>(
         sv[j & 1], sk[j & 1], p_prev, acc, qf, s_cur, s_nxt, p_cur, st, alpha, (t0 + j) * kBc,
-        klo, khi, N, c, tau, h, vaddr, kaddr, [&]() { staging(j); });
+        klo, khi, N, c, tau, h, vaddr, kaddr, sm, [&]() { staging(j); });
     finish_step(j, any, alpha);
     advance();
   }
@@ -583,22 +630,22 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   for (; j + 1 < n_full; j += 2) {
     float alpha;
     rescale();
-    bool any = step<D, CAUSAL, NP, false, WIN>(
+    bool any = step<D, CAUSAL, NP, false, WIN, ALIBI, SOFTCAP>(
         sv[j & 1], sk[j & 1], p_prev, acc, qf, s_cur, s_nxt, p_cur, st, alpha, (t0 + j) * kBc, klo, khi, N, c,
-        tau, h, vaddr, kaddr, [&]() { staging(j); });
+        tau, h, vaddr, kaddr, sm, [&]() { staging(j); });
     finish_step(j, any, alpha);
     rescale();
-    any = step<D, CAUSAL, NP, false, WIN>(
+    any = step<D, CAUSAL, NP, false, WIN, ALIBI, SOFTCAP>(
         sv[(j + 1) & 1], sk[(j + 1) & 1], p_cur, acc, qf, s_nxt, s_cur, p_prev, st, alpha,
-        (t0 + j + 1) * kBc, klo, khi, N, c, tau, h, vaddr, kaddr, [&]() { staging(j + 1); });
+        (t0 + j + 1) * kBc, klo, khi, N, c, tau, h, vaddr, kaddr, sm, [&]() { staging(j + 1); });
     finish_step(j + 1, any, alpha);
   }
   for (; j < n_full; ++j) {
     rescale();
     float alpha;
-    const bool any = step<D, CAUSAL, NP, false, WIN>(
+    const bool any = step<D, CAUSAL, NP, false, WIN, ALIBI, SOFTCAP>(
         sv[j & 1], sk[j & 1], p_prev, acc, qf, s_cur, s_nxt, p_cur, st, alpha, (t0 + j) * kBc, klo, khi, N, c,
-        tau, h, vaddr, kaddr, [&]() { staging(j); });
+        tau, h, vaddr, kaddr, sm, [&]() { staging(j); });
     finish_step(j, any, alpha);
     advance();
   }
@@ -609,18 +656,18 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   for (; j < n_vis; ++j) {
     rescale();
     float alpha;
-    const bool any = step<D, CAUSAL, NP, false, WIN>(
+    const bool any = step<D, CAUSAL, NP, false, WIN, ALIBI, SOFTCAP>(
         sv[j & 1], sk[j & 1], p_prev, acc, qf, s_cur, s_nxt, p_cur, st, alpha, (t0 + j) * kBc, klo, khi, N, c,
-        tau, h, vaddr, kaddr, [&]() { staging(j); });
+        tau, h, vaddr, kaddr, sm, [&]() { staging(j); });
     finish_step(j, any, alpha);
     advance();
   }
   for (; j < n_w; ++j) {
     rescale();
     float alpha;
-    const bool any = step<D, CAUSAL, NP, true, WIN>(
+    const bool any = step<D, CAUSAL, NP, true, WIN, ALIBI, SOFTCAP>(
         sv[j & 1], sk[j & 1], p_prev, acc, qf, s_cur, s_nxt, p_cur, st, alpha, (t0 + j) * kBc, klo, khi, N, c,
-        tau, h, vaddr, kaddr, [&]() { staging(j); });
+        tau, h, vaddr, kaddr, sm, [&]() { staging(j); });
     finish_step(j, any, alpha);
     advance();
   }
@@ -681,33 +728,46 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   }
 }
 
-template <int D, bool CAUSAL, int NP, bool WIN>
+template <int D, bool CAUSAL, int NP, bool WIN, bool ALIBI, bool SOFTCAP>
 hipError_t launch_one(const FwdArgs& a) {
   const int nqb = (a.N + kBr - 1) / kBr;
   const long long grid = (long long)a.B * a.Hq * nqb;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NP, WIN>), dim3((unsigned)grid), dim3(kThreads), 0,
-                     (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                     (const uint16_t*)a.v, a.o, a.lse, a.Hq, a.Hkv, a.N, nqb, a.c, a.tau, a.qsign,
-                     a.window, a.stats);
+  const float k2 = SOFTCAP ? 2.f * a.c / a.softcap : 0.f;
+  const float ccap = SOFTCAP ? a.softcap * kLog2e : 0.f;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NP, WIN, ALIBI, SOFTCAP>), dim3((unsigned)grid),
+                     dim3(kThreads), 0, (hipStream_t)a.stream, (const uint16_t*)a.q,
+                     (const uint16_t*)a.k, (const uint16_t*)a.v, a.o, a.lse, a.Hq, a.Hkv, a.N, nqb,
+                     a.c, a.tau, a.qsign, a.window, a.alibi, k2, ccap, a.stats);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL, bool WIN>
 hipError_t launch_np(const FwdArgs& a) {
   switch (a.poly_pairs) {
-    case 0: return launch_one<D, CAUSAL, 0, WIN>(a);
-    case 4: return launch_one<D, CAUSAL, 4, WIN>(a);
-    case 8: return launch_one<D, CAUSAL, 8, WIN>(a);
-    case 12: return launch_one<D, CAUSAL, 12, WIN>(a);
-    case 16: return launch_one<D, CAUSAL, 16, WIN>(a);
+    case 0: return launch_one<D, CAUSAL, 0, WIN, false, false>(a);
+    case 4: return launch_one<D, CAUSAL, 4, WIN, false, false>(a);
+    case 8: return launch_one<D, CAUSAL, 8, WIN, false, false>(a);
+    case 12: return launch_one<D, CAUSAL, 12, WIN, false, false>(a);
+    case 16: return launch_one<D, CAUSAL, 16, WIN, false, false>(a);
     default: return hipErrorInvalidValue;
   }
 }
 
+// Score modifications run with the hardware exponential only.
+template <int D, bool CAUSAL, bool WIN>
+hipError_t launch_mod(const FwdArgs& a) {
+  const bool al = a.alibi != nullptr, cap = a.softcap > 0.f;
+  if (!al && !cap) return launch_np<D, CAUSAL, WIN>(a);
+  if (a.poly_pairs != 0) return hipErrorNotSupported;
+  if (al && cap) return launch_one<D, CAUSAL, 0, WIN, true, true>(a);
+  if (al) return launch_one<D, CAUSAL, 0, WIN, true, false>(a);
+  return launch_one<D, CAUSAL, 0, WIN, false, true>(a);
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_win(const FwdArgs& a) {
-  return a.window ? launch_np<D, CAUSAL, true>(a) : launch_np<D, CAUSAL, false>(a);
+  return a.window ? launch_mod<D, CAUSAL, true>(a) : launch_mod<D, CAUSAL, false>(a);
 }
 
 }  // namespace

@@ -21,6 +21,8 @@ struct FwdArgs {
                     // (0, 4, 8, 12 or 16; the rest use v_exp_f32)
   int window;       // sliding window W (0: none; 1 <= W < N): key j visible from query i
                     // only when i - W < j, and j < i + W without the causal mask
+  const float* alibi;   // device, Hq ALiBi slopes (natural-log units per key), or null
+  float softcap;    // soft-capping C (0: off)
   unsigned long long* stats;
   void* stream;
 };

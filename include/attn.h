@@ -77,10 +77,19 @@ typedef struct attn_opts {
                                 causal mask, also j < i + W.  Tiles wholly outside the band are
                                 skipped.  bf16 forward only: the MXFP4 forward returns
                                 ATTN_EUNSUPPORTED for W != 0. */
+    const float* alibi_slopes; /* nullable DEVICE pointer to Hq floats, one ALiBi slope a_h per
+                                query head (the same page names ALiBi; no definition printed):
+                                the scaled score of query i and key j gets -a_h |i - j| added
+                                before the mask.  Caller-owned, read during the call. */
+    float softcap;           /* soft-capping C >= 0 (same page): 0 = off; C > 0 replaces the
+                                scaled score s by C tanh(s / C), before the ALiBi bias and the
+                                mask.  Both modifications need the hardware exponential
+                                (ATTN_EUNSUPPORTED otherwise) and the bf16 forward (the MXFP4
+                                forward returns ATTN_EUNSUPPORTED). */
 } attn_opts;
 
 /* Default options: tau = 8, hardware exp (poly_frac 0.5 for ATTN_EXP_MIX), no stats, no
-   window. */
+   window, no ALiBi, no soft-capping. */
 void attn_default_opts(attn_opts* opts);
 
 /*

@@ -77,6 +77,18 @@ def test_opts_validation(fa):
     assert fa.attn_fwd_mxfp4_ex(*[FAKE] * 8, 1, 1, 1, 64, 128, 0, 0.1, opts, None) == -1
     opts = fa.make_opts(8.0, "hw", window=16)
     assert fa.attn_fwd_mxfp4_ex(*[FAKE] * 8, 1, 1, 1, 64, 128, 0, 0.1, opts, None) == -2
+    # soft-capping: C must be finite and >= 0; score modifications need the hardware exp
+    # and the bf16 forward
+    for cap in (-1.0, float("nan"), float("inf")):
+        opts = fa.make_opts(8.0, "hw", softcap=cap)
+        assert fa.attn_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 16, 64, 0, 0.1, opts,
+                              None) == -1
+    for kw in (dict(softcap=5.0), dict(alibi_ptr=FAKE)):
+        opts = fa.make_opts(8.0, "poly", **kw)
+        assert fa.attn_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 16, 64, 0, 0.1, opts,
+                              None) == -2
+        opts = fa.make_opts(8.0, "hw", **kw)
+        assert fa.attn_fwd_mxfp4_ex(*[FAKE] * 8, 1, 1, 1, 64, 128, 0, 0.1, opts, None) == -2
 
 
 def test_default_opts_layout(fa):
@@ -85,8 +97,10 @@ def test_default_opts_layout(fa):
     from exact_attention_forward_tiled_amd.binding import AttnOpts, lib
     o = AttnOpts()
     o.tau, o.exp_mode, o.poly_frac, o.stats, o.window = -3.0, 9, -3.0, FAKE, -7
+    o.alibi_slopes, o.softcap = FAKE, -2.0
     lib.attn_default_opts(ctypes.byref(o))
     assert (o.tau, o.exp_mode, o.poly_frac, o.stats, o.window) == (8.0, 0, 0.5, None, 0)
+    assert (o.alibi_slopes, o.softcap) == (None, 0.0)
 
 
 def test_mxfp4_validation(fa):

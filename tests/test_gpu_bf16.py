@@ -244,6 +244,39 @@ def test_sliding_window_large_sampled_rows():
         _check(o[0, h, rows], lse[0, h, rows], ro, rl, f"head {h}")
 
 
+MOD_CASES = [
+    # B, Hq, Hkv, N, d, causal, softcap, alibi, window
+    (1, 2, 2, 256, 128, False, 5.0, False, 0),
+    (1, 2, 2, 333, 128, True, 5.0, False, 0),
+    (1, 4, 2, 300, 128, True, 0.0, True, 0),
+    (1, 4, 4, 517, 128, False, 0.0, True, 0),
+    (1, 4, 1, 700, 64, True, 20.0, True, 0),
+    (2, 2, 2, 129, 64, False, 2.0, True, 0),
+    (1, 4, 2, 1000, 128, True, 30.0, True, 200),
+]
+
+
+@pytest.mark.parametrize("case", MOD_CASES, ids=lambda c: "B%dHq%dHkv%dN%dd%d%scap%gal%dW%d" % (
+    c[0], c[1], c[2], c[3], c[4], "c" if c[5] else "n", c[6], c[7], c[8]))
+def test_score_modifications(case):
+    """ALiBi (score - a_h |i - j|, one slope per query head) and soft-capping
+    (C tanh(score / C)) against the oracle, alone, together and with a window."""
+    import torch
+    B, Hq, Hkv, N, d, causal, cap, use_alibi, W = case
+    qb, kb, vb = random_case(60 + N, B, Hq, Hkv, N, d, sigma=2.0)
+    slopes = 0.5 ** (np.arange(1, Hq + 1) * 8.0 / Hq) if use_alibi else None
+    log(f"case {case}")
+    o, lse = _run(qb, kb, vb, causal, d ** -0.5, window=W, softcap=cap,
+                  alibi=None if slopes is None else
+                  torch.tensor(slopes, dtype=torch.float32, device="cuda"))
+    q64, k64, v64 = (synth.bf16_bits_to_f64(x) for x in (qb, kb, vb))
+    # the kernel reads the slopes in float32: the oracle gets the same values
+    ref_slopes = None if slopes is None else slopes.astype(np.float32).astype(np.float64)
+    ro, rl = oracle.attention(q64, k64, v64, causal, d ** -0.5, window=W, softcap=cap,
+                              alibi=ref_slopes)
+    _check(o, lse, ro, rl, f"softcap {cap} alibi {use_alibi} window {W}")
+
+
 def test_skip_ratio_stats():
     """The rescale counter: tau = 0 rescales on most steps, tau = 8 skips most of them."""
     import torch
