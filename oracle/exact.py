@@ -19,6 +19,12 @@ Reading: with a window W >= 1, key j is visible from query i only when
 i - W < j, and, without the causal mask, also j < i + W (a band of half-width
 W - 1 around the diagonal).  W = 0 means no window.
 
+Document masking (same page, same list; no definition printed).  Reading: the
+sequence holds documents packed back to back, given by offsets 0 = o_0 < o_1 < ... <
+o_D = N (document d is positions o_d .. o_{d+1} - 1, the same layout for every batch
+entry), and key j is visible from query i only when both lie in the same document.
+It combines with the causal mask and the window.
+
 Score modifications (the same page names ALiBi and soft-capping among the patterns the
 FA4 backend serves, again without definitions).  Readings, applied to the scaled score
 before the mask, soft-capping first:
@@ -62,9 +68,17 @@ def modify_scores(s, row_ids, softcap=0.0, alibi_slope=None):
     return s
 
 
-def visible(row_ids, n_keys, causal, window=0):
+def document_ids(doc_offsets, n):
+    """Document index of each of the n positions, from the offsets o_0 = 0 < ... < o_D = n."""
+    off = np.asarray(doc_offsets, dtype=np.int64)
+    if off[0] != 0 or off[-1] != n or np.any(np.diff(off) <= 0):
+        raise ValueError("document offsets must rise strictly from 0 to N")
+    return np.searchsorted(off, np.arange(n), side="right") - 1
+
+
+def visible(row_ids, n_keys, causal, window=0, docs=None):
     """Boolean [rows, n_keys]: key j visible from query i (causal: j <= i; window W:
-    i - W < j, and j < i + W when not causal)."""
+    i - W < j, and j < i + W when not causal; documents: same document)."""
     i = np.asarray(row_ids)[:, None]
     j = np.arange(n_keys)[None, :]
     ok = np.ones((i.shape[0], n_keys), dtype=bool)
@@ -74,14 +88,17 @@ def visible(row_ids, n_keys, causal, window=0):
         ok &= j > i - window
         if not causal:
             ok &= j < i + window
+    if docs is not None:
+        doc = document_ids(docs, n_keys)
+        ok &= doc[np.asarray(row_ids)][:, None] == doc[None, :]
     return ok
 
 
-def apply_mask(s, row_ids, causal, window=0):
+def apply_mask(s, row_ids, causal, window=0, docs=None):
     """Additive -inf mask on the keys that `visible` hides."""
-    if not causal and not window:
+    if not causal and not window and docs is None:
         return s
-    return np.where(visible(row_ids, s.shape[1], causal, window), s, -np.inf)
+    return np.where(visible(row_ids, s.shape[1], causal, window, docs), s, -np.inf)
 
 
 def softmax_parts(s):
@@ -104,7 +121,8 @@ def finish(m, e, l, v_head):
     return o, lse
 
 
-def attention_rows(q, k, v, causal, scale, b, hq, rows, window=0, softcap=0.0, alibi=None):
+def attention_rows(q, k, v, causal, scale, b, hq, rows, window=0, softcap=0.0, alibi=None,
+                   docs=None):
     """O and LSE for the listed query rows of one (batch, query head) slice.  alibi: the
     per-query-head slopes (length Hq) or None."""
     B, Hq, N, d = q.shape
@@ -112,12 +130,13 @@ def attention_rows(q, k, v, causal, scale, b, hq, rows, window=0, softcap=0.0, a
     rows = np.asarray(rows, dtype=np.int64)
     s = scores(q[b, hq, rows, :], k[b, hk], scale)
     s = modify_scores(s, rows, softcap, None if alibi is None else float(alibi[hq]))
-    s = apply_mask(s, rows, causal, window)
+    s = apply_mask(s, rows, causal, window, docs)
     m, e, l = softmax_parts(s)
     return finish(m, e, l, v[b, hk])
 
 
-def attention_head(q, k, v, causal, scale, b, hq, chunk=512, window=0, softcap=0.0, alibi=None):
+def attention_head(q, k, v, causal, scale, b, hq, chunk=512, window=0, softcap=0.0, alibi=None,
+                   docs=None):
     """All rows of one (batch, query head) slice, in chunks of whole rows."""
     N = q.shape[2]
     o = np.empty((N, v.shape[3]), dtype=np.float64)
@@ -125,11 +144,11 @@ def attention_head(q, k, v, causal, scale, b, hq, chunk=512, window=0, softcap=0
     for r0 in range(0, N, chunk):
         rows = np.arange(r0, min(N, r0 + chunk))
         o[rows], lse[rows] = attention_rows(q, k, v, causal, scale, b, hq, rows, window,
-                                            softcap, alibi)
+                                            softcap, alibi, docs)
     return o, lse
 
 
-def attention(q, k, v, causal, scale, chunk=512, window=0, softcap=0.0, alibi=None):
+def attention(q, k, v, causal, scale, chunk=512, window=0, softcap=0.0, alibi=None, docs=None):
     """Exact forward over the whole [B, Hq, N, d] problem: returns (O, LSE)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -142,11 +161,11 @@ def attention(q, k, v, causal, scale, chunk=512, window=0, softcap=0.0, alibi=No
     for b in range(B):
         for hq in range(Hq):
             o[b, hq], lse[b, hq] = attention_head(q, k, v, causal, scale, b, hq, chunk, window,
-                                                  softcap, alibi)
+                                                  softcap, alibi, docs)
     return o, lse
 
 
-def attention_brute(q, k, v, causal, scale, window=0, softcap=0.0, alibi=None):
+def attention_brute(q, k, v, causal, scale, window=0, softcap=0.0, alibi=None, docs=None):
     """The same definition as scalar Python loops with math.exp (tiny inputs only)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -154,6 +173,11 @@ def attention_brute(q, k, v, causal, scale, window=0, softcap=0.0, alibi=None):
     B, Hq, N, d = q.shape
     Hkv, Nk, dv = k.shape[1], k.shape[2], v.shape[3]
     group = Hq // Hkv
+    doc_of = None
+    if docs is not None:                  # position -> document, by walking the offsets
+        doc_of = []
+        for dd in range(len(docs) - 1):
+            doc_of += [dd] * (int(docs[dd + 1]) - int(docs[dd]))
     o = np.zeros((B, Hq, N, dv))
     lse = np.zeros((B, Hq, N))
     for b in range(B):
@@ -165,6 +189,8 @@ def attention_brute(q, k, v, causal, scale, window=0, softcap=0.0, alibi=None):
                     if causal and j > i:
                         continue
                     if window and (i - j >= window or (not causal and j - i >= window)):
+                        continue
+                    if doc_of is not None and doc_of[i] != doc_of[j]:
                         continue
                     acc = 0.0
                     for c in range(d):

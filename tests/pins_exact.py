@@ -342,6 +342,69 @@ def pin_softcap_limits(attn):
 MOD_PINS = [pin_mod_brute, pin_mod_torch, pin_alibi_zero_query, pin_softcap_limits]
 
 
+# ---- document masking (attn(..., docs=offsets)) -------------------------------------------
+
+def pin_docs_brute(attn):
+    """Agreement with the scalar loops, with the masks, a window and score modifications."""
+    q, k, v = _case(500, 1, 2, 1, 11, 4, sigma=1.5)
+    for docs in ([0, 11], [0, 4, 11], [0, 1, 2, 7, 11], [0, 5, 6, 11]):
+        for causal in (False, True):
+            for W, cap in ((0, 0.0), (3, 0.0), (0, 2.0)):
+                o, lse = attn(q, k, v, causal, 0.6, window=W, softcap=cap, docs=docs)
+                ob, lb = attention_brute(q, k, v, causal, 0.6, window=W, softcap=cap, docs=docs)
+                assert np.max(np.abs(o - ob)) < TOL and np.max(np.abs(lse - lb)) < TOL, \
+                    ("docs brute", docs, causal, W, cap)
+
+
+def pin_docs_are_independent_sequences(attn):
+    """Each document attends like a separate sequence: the result equals plain attention run
+    on every document's slice on its own."""
+    q, k, v = _case(501, 2, 4, 2, 40, 8)
+    docs = [0, 7, 8, 25, 40]
+    for causal in (False, True):
+        o, lse = attn(q, k, v, causal, 0.4, docs=docs)
+        for a, b in zip(docs[:-1], docs[1:]):
+            os_, ls_ = attn(q[:, :, a:b], k[:, :, a:b], v[:, :, a:b], causal, 0.4)
+            assert np.max(np.abs(o[:, :, a:b] - os_)) < TOL
+            assert np.max(np.abs(lse[:, :, a:b] - ls_)) < TOL
+
+
+def pin_docs_zero_query(attn):
+    """Q = 0: O_i is the mean of the V rows of i's document (causal: up to i), LSE_i the log
+    of their count."""
+    N = 21
+    _, k, v = _case(502, 1, 2, 2, N, 4)
+    q = np.zeros((1, 2, N, 4))
+    docs = [0, 3, 4, 13, 21]
+    for causal in (False, True):
+        o, lse = attn(q, k, v, causal, 0.8, docs=docs)
+        for a, b in zip(docs[:-1], docs[1:]):
+            for i in range(a, b):
+                hi = i if causal else b - 1
+                assert np.max(np.abs(o[0, :, i] - v[0, :, a:hi + 1].mean(axis=1))) < TOL
+                assert abs(lse[0, 1, i] - np.log(hi - a + 1)) < TOL
+
+
+def pin_docs_torch(attn):
+    """torch's CPU attention (float64) with the block-diagonal mask spelled out."""
+    q, k, v = _case(503, 1, 2, 2, 30, 16)
+    docs = [0, 10, 11, 30]
+    doc = np.repeat(np.arange(3), np.diff(docs))
+    for causal in (False, True):
+        m = doc[:, None] == doc[None, :]
+        if causal:
+            m &= np.arange(30)[None, :] <= np.arange(30)[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+            attn_mask=torch.from_numpy(m), scale=0.35)
+        o, _ = attn(q, k, v, causal, 0.35, docs=docs)
+        assert np.max(np.abs(o - ref.numpy())) < 1e-10
+
+
+DOC_PINS = [pin_docs_brute, pin_docs_are_independent_sequences, pin_docs_zero_query,
+            pin_docs_torch]
+
+
 ALL_PINS = [pin_brute, pin_torch, pin_zero_query, pin_single_key, pin_two_keys,
             pin_constant_v, pin_identity_v, pin_shift, pin_permutations, pin_linear_in_v,
             pin_gqa, pin_causal_prefix, pin_dominant_logit]

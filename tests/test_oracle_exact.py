@@ -23,6 +23,56 @@ def test_oracle_score_mod_pin(pin):
     pin(oracle.attention)
 
 
+@pytest.mark.parametrize("pin", pins_exact.DOC_PINS, ids=lambda p: p.__name__)
+def test_oracle_document_pin(pin):
+    pin(oracle.attention)
+
+
+def test_document_offsets_are_checked():
+    with pytest.raises(ValueError):
+        exact.document_ids([0, 5, 5, 10], 10)
+    with pytest.raises(ValueError):
+        exact.document_ids([0, 5, 9], 10)
+
+
+# planted document-mask mistakes: each must fail at least one document pin
+def _dmut_off_by_one(monkeypatch):
+    orig = exact.document_ids
+    monkeypatch.setattr(exact, "document_ids",
+                        lambda off, n: np.minimum(orig(off, n) + (np.arange(n) == np.asarray(off)[1] - 1),
+                                                  len(off) - 2))
+
+
+def _dmut_ignored(monkeypatch):
+    monkeypatch.setattr(exact, "document_ids", lambda off, n: np.zeros(n, dtype=np.int64))
+
+
+def _dmut_keys_only(monkeypatch):
+    orig = exact.visible
+
+    def bad(row_ids, n_keys, causal, window=0, docs=None):
+        ok = orig(row_ids, n_keys, causal, window, None)
+        if docs is not None:   # hides keys of other documents than the first, for every row
+            doc = exact.document_ids(docs, n_keys)
+            ok &= (doc == 0)[None, :]
+        return ok
+    monkeypatch.setattr(exact, "visible", bad)
+
+
+@pytest.mark.parametrize("mutant", [_dmut_off_by_one, _dmut_ignored, _dmut_keys_only],
+                         ids=lambda m: m.__name__)
+def test_planted_document_mistake_is_caught(mutant, monkeypatch):
+    mutant(monkeypatch)
+    failures = []
+    for pin in pins_exact.DOC_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(oracle.attention)
+        except AssertionError:
+            failures.append(pin.__name__)
+    assert failures, "a planted document-mask mistake passed every pin"
+
+
 # planted score-modification mistakes: each must fail at least one score-mod pin
 def _smut_alibi_signed(monkeypatch):
     orig = exact.modify_scores
@@ -79,16 +129,16 @@ def test_planted_score_mod_mistake_is_caught(mutant, monkeypatch):
 def _wmut_edge_off_by_one(monkeypatch):
     orig = exact.visible
 
-    def bad(row_ids, n_keys, causal, window=0):
-        return orig(row_ids, n_keys, causal, window + 1 if window else 0)
+    def bad(row_ids, n_keys, causal, window=0, docs=None):
+        return orig(row_ids, n_keys, causal, window + 1 if window else 0, docs)
     monkeypatch.setattr(exact, "visible", bad)
 
 
 def _wmut_causal_band_both_sides(monkeypatch):
     orig = exact.visible
 
-    def bad(row_ids, n_keys, causal, window=0):
-        ok = orig(row_ids, n_keys, causal, window)
+    def bad(row_ids, n_keys, causal, window=0, docs=None):
+        ok = orig(row_ids, n_keys, causal, window, docs)
         if causal and window:   # forgets the causal side inside the band
             i = np.asarray(row_ids)[:, None]
             j = np.arange(n_keys)[None, :]
@@ -99,7 +149,7 @@ def _wmut_causal_band_both_sides(monkeypatch):
 
 def _wmut_window_ignored(monkeypatch):
     orig = exact.visible
-    monkeypatch.setattr(exact, "visible", lambda r, n, c, window=0: orig(r, n, c, 0))
+    monkeypatch.setattr(exact, "visible", lambda r, n, c, window=0, docs=None: orig(r, n, c, 0, docs))
 
 
 @pytest.mark.parametrize("mutant", [_wmut_edge_off_by_one, _wmut_causal_band_both_sides,
@@ -142,7 +192,7 @@ def _mut_drop_scale(monkeypatch):
 
 
 def _mut_mask_diagonal(monkeypatch):
-    def bad(s, rows, causal, window=0):
+    def bad(s, rows, causal, window=0, docs=None):
         if not causal:
             return s
         cols = np.arange(s.shape[1])
