@@ -86,11 +86,13 @@ def device_inputs(w):
 class Workload:
     """Device buffers and one launch closure for a bf16 workload."""
 
-    def __init__(self, w, exp_mode, tau, poly_frac=None, window=0):
+    def __init__(self, w, exp_mode, tau, poly_frac=None, window=0, doc_offsets=None):
         import torch
         import exact_attention_forward_tiled_amd as fa
         self.w = w
         self.window = window
+        self.docs = (None if doc_offsets is None else
+                     torch.tensor(doc_offsets, dtype=torch.int32, device="cuda"))
         self.q, self.k, self.v = device_inputs(w)
         self.o = torch.empty((w.B, w.Hq, w.N, w.d), dtype=torch.float32, device="cuda")
         self.lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device="cuda")
@@ -100,7 +102,7 @@ class Workload:
     def launch(self, stats=None):
         self.fa.fwd(self.q, self.k, self.v, causal=self.w.causal, scale=self.w.scale, tau=self.tau,
                     exp_mode=self.exp_mode, stats=stats, out=(self.o, self.lse),
-                    poly_frac=self.poly_frac, window=self.window)
+                    poly_frac=self.poly_frac, window=self.window, docs=self.docs)
 
 
 class Mxfp4Workload:
@@ -129,12 +131,18 @@ class Mxfp4Workload:
                           out=(self.o, self.lse))
 
 
-def visible_pairs(N, causal, window):
-    """(query, key) pairs a sliding window of width `window` shows (exact count)."""
+def visible_pairs(N, causal, window, doc_offsets=None):
+    """(query, key) pairs a sliding window of width `window` and/or packed documents show
+    (exact count)."""
     import numpy as np
     i = np.arange(N, dtype=np.int64)
     lo = np.maximum(0, i - window + 1) if window else np.zeros_like(i)
     hi = i if causal else (np.minimum(N - 1, i + window - 1) if window else np.full_like(i, N - 1))
+    if doc_offsets is not None:
+        off = np.asarray(doc_offsets, dtype=np.int64)
+        d = np.searchsorted(off, i, side="right") - 1
+        lo = np.maximum(lo, off[d])
+        hi = np.minimum(hi, off[d + 1] - 1)
     return int((hi - lo + 1).sum())
 
 
@@ -299,6 +307,9 @@ def main():
                     help="with --exp mix: fraction of the exponentials on the cubic")
     ap.add_argument("--tau", type=float, default=8.0)
     ap.add_argument("--extra", default="", help="other workloads to time (comma list), e.g. 3,4")
+    ap.add_argument("--docs", type=int, default=0,
+                    help="also time the workload split into this many equal packed documents "
+                         "(bf16 only; TFLOP/s count 4*d flop per visible pair)")
     ap.add_argument("--window", type=int, default=0,
                     help="also time the workload with this sliding window (bf16 only); its "
                          "TFLOP/s count 4*d flop per visible (query, key) pair")
@@ -411,6 +422,21 @@ def main():
             "kernel_ms_avg": round(tw["kernel_ms_avg"], 4),
             "visible_pairs_per_head": pairs,
             "time_vs_no_window": round(tw["kernel_ms_avg"] / t["kernel_ms_avg"], 4)}
+
+    if args.docs and w.fmt == "bf16":
+        off = [round(x * w.N / args.docs) for x in range(args.docs + 1)]
+        log(f"timing {w.name} as {args.docs} documents")
+        wl = Workload(w, args.exp, args.tau, args.poly_frac, doc_offsets=off)
+        td = time_workload(wl, args.steps, args.warmup, args.warmup_seconds)
+        del wl
+        torch.cuda.empty_cache()
+        pairs = visible_pairs(w.N, w.causal, 0, off)
+        fl = 4.0 * w.d * w.B * w.Hq * pairs
+        extra["workloads"][f"{w.name}/docs={args.docs}"] = {
+            "tflops_visible": round(fl / (td["kernel_ms_avg"] * 1e-3) / 1e12, 2),
+            "kernel_ms_avg": round(td["kernel_ms_avg"], 4),
+            "visible_pairs_per_head": pairs,
+            "time_vs_one_document": round(td["kernel_ms_avg"] / t["kernel_ms_avg"], 4)}
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -26,7 +26,8 @@ class AttnOpts(ctypes.Structure):
     _fields_ = [("tau", ctypes.c_float), ("exp_mode", ctypes.c_int),
                 ("poly_frac", ctypes.c_float), ("stats", ctypes.c_void_p),
                 ("window", ctypes.c_int), ("alibi_slopes", ctypes.c_void_p),
-                ("softcap", ctypes.c_float)]
+                ("softcap", ctypes.c_float), ("doc_offsets", ctypes.c_void_p),
+                ("n_docs", ctypes.c_int)]
 
 
 def _load():
@@ -76,7 +77,7 @@ def check(status):
 
 
 def make_opts(tau=8.0, exp_mode="hw", stats_ptr=None, poly_frac=None, window=0, alibi_ptr=None,
-              softcap=0.0):
+              softcap=0.0, doc_ptr=None, n_docs=0):
     o = AttnOpts()
     lib.attn_default_opts(ctypes.byref(o))
     o.tau = float(tau)
@@ -87,6 +88,8 @@ def make_opts(tau=8.0, exp_mode="hw", stats_ptr=None, poly_frac=None, window=0, 
     o.window = int(window)
     o.alibi_slopes = alibi_ptr
     o.softcap = float(softcap)
+    o.doc_offsets = doc_ptr
+    o.n_docs = int(n_docs)
     return o
 
 
@@ -144,12 +147,13 @@ def _stats_ptr(torch, stats):
 
 
 def fwd(q, k, v, causal=False, scale=None, tau=8.0, exp_mode="hw", stats=None, out=None,
-        poly_frac=None, window=0, alibi=None, softcap=0.0):
+        poly_frac=None, window=0, alibi=None, softcap=0.0, docs=None):
     """bf16 attention forward on the GPU: returns (O fp32 [B,Hq,N,d], LSE fp32 [B,Hq,N]).
     exp_mode "hw", "poly" or "mix" (poly_frac of the exponentials on the cubic); window W:
     key j visible from query i only when i - W < j (and j < i + W without the causal mask);
     alibi: float32 CUDA tensor of Hq slopes a_h (score -= a_h |i - j|); softcap C > 0: score ->
-    C tanh(score / C)."""
+    C tanh(score / C); docs: int32 CUDA tensor of document offsets 0 < ... < N (packed
+    documents, keys visible only within the query's document)."""
     torch = _torch()
     for t in (q, k, v):
         if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
@@ -171,8 +175,14 @@ def fwd(q, k, v, causal=False, scale=None, tau=8.0, exp_mode="hw", stats=None, o
                 or alibi.numel() != Hq):
             raise ValueError("alibi must be a contiguous float32 CUDA tensor of Hq slopes")
         alibi_ptr = alibi.data_ptr()
+    doc_ptr, n_docs = None, 0
+    if docs is not None:
+        if docs.dtype != torch.int32 or not docs.is_cuda or not docs.is_contiguous() \
+                or docs.numel() < 2:
+            raise ValueError("docs must be a contiguous int32 CUDA tensor of document offsets")
+        doc_ptr, n_docs = docs.data_ptr(), docs.numel() - 1
     opts = make_opts(tau, exp_mode, _stats_ptr(torch, stats), poly_frac, window, alibi_ptr,
-                     softcap)
+                     softcap, doc_ptr, n_docs)
     check(attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                       B, Hq, Hkv, N, d, int(bool(causal)), float(scale), opts,
                       _stream(torch, q.device)))

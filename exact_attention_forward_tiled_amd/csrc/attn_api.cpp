@@ -29,6 +29,7 @@ int check_opts(const attn_opts* o) {
     return ATTN_EINVAL;
   if (o->window < 0) return ATTN_EINVAL;
   if (!(o->softcap >= 0.f) || !isfinite(o->softcap)) return ATTN_EINVAL;
+  if (o->doc_offsets != nullptr && o->n_docs < 1) return ATTN_EINVAL;
   return ATTN_OK;
 }
 
@@ -62,6 +63,8 @@ void attn_default_opts(attn_opts* opts) {
   opts->window = 0;
   opts->alibi_slopes = nullptr;
   opts->softcap = 0.f;
+  opts->doc_offsets = nullptr;
+  opts->n_docs = 0;
 }
 
 const char* attn_strerror(int status) {
@@ -103,6 +106,9 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, float* o, float* ls
   a.window = op->window >= N ? 0 : op->window;
   a.alibi = op->alibi_slopes;
   a.softcap = op->softcap;
+  a.doc_offsets = op->doc_offsets;
+  a.n_docs = op->doc_offsets != nullptr ? op->n_docs : 0;
+  if (a.n_docs > N) return ATTN_EINVAL;   // documents are non-empty
   if ((a.alibi != nullptr || a.softcap > 0.f) && op->exp_mode != ATTN_EXP_HW)
     return ATTN_EUNSUPPORTED;
   a.stats = op->stats;
@@ -131,7 +137,7 @@ int attn_fwd_mxfp4_ex(const uint8_t* q4, const uint8_t* qs, const uint8_t* k4, c
   st = check_opts(op);
   if (st != ATTN_OK) return st;
   if (d != 128 || N % 32 != 0 || op->window != 0 || op->alibi_slopes != nullptr ||
-      op->softcap != 0.f)
+      op->softcap != 0.f || op->doc_offsets != nullptr)
     return ATTN_EUNSUPPORTED;
 
   attn::Mxfp4Args a;

@@ -316,10 +316,10 @@ struct ScoreMod {
 // One pipeline step: PV of tile j-1 (pp, V^T tile in svp), QK of tile j+1 into
 // sn (K tile in skn), and the online softmax of tile j (sc -> pc), interleaved.
 // MASK: keys outside [klo, khi] (this lane's visible range) or past N get -inf; klo
-// applies with WIN (a sliding window), khi when causal or with WIN.
+// applies with BAND (a sliding window and/or documents), khi when causal or with BAND.
 // Returns whether any row of the wave raised its reference max by more than tau;
 // then O must be multiplied by alpha before the next PV product.
-template <int D, bool CAUSAL, int NP, bool MASK, bool WIN, bool ALIBI, bool SOFTCAP, class Mid>
+template <int D, bool CAUSAL, int NP, bool MASK, bool BAND, bool ALIBI, bool SOFTCAP, class Mid>
 __device__ __forceinline__ bool step(const u32x4* svp, const u32x4* skn, const bf16x8 (&pp)[4],
                                      f32x16 (&acc)[D / 32], const bf16x8 (&qf)[D / 16],
                                      f32x16 (&sc)[2], f32x16 (&sn)[2], bf16x8 (&pc)[4],
@@ -339,8 +339,7 @@ __device__ __forceinline__ bool step(const u32x4* svp, const u32x4* skn, const b
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kv0 + 32 * mb + 16 * (r >> 3) + 8 * h + (r & 7);
-        const bool ok = key < N && (!CAUSAL || key <= khi) &&
-                        (!WIN || (key >= klo && (CAUSAL || key <= khi)));
+        const bool ok = key < N && (!(CAUSAL || BAND) || key <= khi) && (!BAND || key >= klo);
         sc[mb][r] = ok ? sc[mb][r] : NEG_INF;
       }
   }
@@ -435,13 +434,14 @@ __device__ __forceinline__ bool step(const u32x4* svp, const u32x4* skn, const b
   return any;
 }
 
-template <int D, bool CAUSAL, int NP, bool WIN, bool ALIBI, bool SOFTCAP>
+template <int D, bool CAUSAL, int NP, bool BAND, bool ALIBI, bool SOFTCAP>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      const uint16_t* __restrict__ V, float* __restrict__ O, float* __restrict__ LSE,
                      int Hq, int Hkv, int N, int nqb, float c, float tau, uint32_t qsign,
-                     int window_arg, const float* __restrict__ alibi_slopes, float k2,
-                     float ccap, unsigned long long* __restrict__ stats) {
+                     int window_arg, const int* __restrict__ doc_off, int n_docs_arg,
+                     const float* __restrict__ alibi_slopes, float k2, float ccap,
+                     unsigned long long* __restrict__ stats) {
   using G = Geo<D>;
   __shared__ u32x4 lds[G::LDS_UNITS];
   u32x4 (*sk)[G::KUNITS] = reinterpret_cast<u32x4 (*)[G::KUNITS]>(lds);
@@ -494,36 +494,66 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   unsigned n_steps = 0, n_rescales = 0;
   bool first = true;
 
-  // Keys this lane sees: [klo, khi] (causal: up to its query; window W: from qi - W + 1,
-  // and up to qi + W - 1 without the causal mask).
+  // Keys this lane sees: [klo, khi].  Without BAND: up to its query when causal.  With
+  // BAND, row i sees [row_lo(i), row_hi(i)]: the causal limit, a window W (from i - W + 1,
+  // and up to i + W - 1 when not causal) and/or i's document (offsets doc_off[0..n_docs]).
+  // Both bounds are non-decreasing in i, so the first and last rows of a workgroup or a
+  // wave bound its keys.
   constexpr int kNoBound = 0x7fffffff;
-  const int window = WIN ? window_arg : 0;   // 0 without the window instantiation
-  const int klo = window ? qi - window + 1 : -kNoBound;
-  const int khi = CAUSAL ? qi : (window ? qi + window - 1 : kNoBound);
-  // Tiles of 64 keys this workgroup visits, t0 .. t0 + n - 1 (local index j = tile - t0);
-  // the window skips the tiles below its lower edge.
-  const int t0 = window ? max(0, Q0 - window + 1) / kBc : 0;
-  const int kv_end = CAUSAL ? min(N, Q0 + kBr) : (window ? min(N, Q0 + kBr - 1 + window) : N);
-  const int n = (kv_end + kBc - 1) / kBc - t0;
-  const int wave_end = CAUSAL ? min(N, q0 + kRowsPerWave)            // keys this wave can see
-                              : (window ? min(N, q0 + kRowsPerWave - 1 + window) : N);
-  const int wave_lo = window ? q0 - window + 1 : 0;                   // the wave's lowest key
-  const bool wave_live = q0 < N;
-  auto active = [&](int j) {
-    return wave_live && (t0 + j) * kBc < wave_end && (!WIN || (t0 + j + 1) * kBc > wave_lo);
+  const int window = BAND ? window_arg : 0;   // 0 without the band instantiation
+  const int n_docs = BAND ? n_docs_arg : 0;
+  // [lo, hi] of row i (0 <= i < N); the document search is clamped so that any offsets
+  // stay within doc_off[0..n_docs] and give lo <= i <= hi
+  auto row_bounds = [&](int i, int& lo, int& hi) {
+    lo = window ? max(0, i - window + 1) : 0;
+    hi = CAUSAL ? i : (window ? min(N - 1, i + window - 1) : N - 1);
+    if (n_docs > 0) {
+      int a = 0, z = n_docs;   // the document d with doc_off[d] <= i < doc_off[d + 1]
+      while (z - a > 1) {
+        const int m = (a + z) >> 1;
+        if (doc_off[m] <= i) a = m;
+        else z = m;
+      }
+      lo = max(lo, min(doc_off[a], i));
+      hi = min(hi, max(doc_off[a + 1] - 1, i));
+    }
   };
-  // Tiles [0, lo_wg) hold keys below some row's window: masked for every wave.
+  int klo = -kNoBound, khi = CAUSAL ? qi : kNoBound;
+  if (BAND) row_bounds(min(qi, N - 1), klo, khi);
+  // Tiles of 64 keys this workgroup visits, t0 .. t0 + n - 1 (local index j = tile - t0);
+  // a band skips the tiles below its lower edge.
+  int wg_lo_first = 0, wg_hi_first = 0, wg_lo_last = 0, wg_hi_last = 0;
+  if (BAND) {
+    row_bounds(Q0, wg_lo_first, wg_hi_first);
+    row_bounds(min(Q0 + kBr - 1, N - 1), wg_lo_last, wg_hi_last);
+  }
+  const int t0 = BAND ? wg_lo_first / kBc : 0;
+  const int kv_end = BAND ? wg_hi_last + 1 : (CAUSAL ? min(N, Q0 + kBr) : N);
+  const int n = (kv_end + kBc - 1) / kBc - t0;
+  const bool wave_live = q0 < N;
+  int w_lo_first = 0, w_hi_first = 0, w_lo_last = 0, w_hi_last = 0;
+  if (BAND) {
+    row_bounds(min(q0, N - 1), w_lo_first, w_hi_first);
+    row_bounds(min(q0 + kRowsPerWave - 1, N - 1), w_lo_last, w_hi_last);
+  }
+  const int wave_end = BAND ? w_hi_last + 1                          // keys this wave can see
+                            : (CAUSAL ? min(N, q0 + kRowsPerWave) : N);
+  const int wave_lo = BAND ? w_lo_first : 0;                          // the wave's lowest key
+  auto active = [&](int j) {
+    return wave_live && (t0 + j) * kBc < wave_end && (!BAND || (t0 + j + 1) * kBc > wave_lo);
+  };
+  // Tiles [0, lo_wg) hold keys below some row's lower edge: masked for every wave.
   int lo_wg = 0;
-  if (window) {
-    const int x = Q0 + kBr - window;   // the largest lower edge of the workgroup's rows
+  if (BAND) {
+    const int x = wg_lo_last;   // the largest lower edge of the workgroup's rows
     lo_wg = x > t0 * kBc ? min(n, (x + kBc - 1) / kBc - t0) : 0;
   }
   // Per wave: tiles [lo_wg, n_vis) need no element mask, tiles [n_vis, n_w) do, and tiles
   // [n_w, n) are entirely masked (keys past the wave's last visible key), so the wave
   // skips their products and only keeps up its share of the staging.
   const int n_w = wave_live ? (wave_end + kBc - 1) / kBc - t0 : n;
-  const int n_vis = max(0, min(CAUSAL ? (q0 + 1) / kBc : (window ? (q0 + window) / kBc : t0 + n),
-                               N / kBc) - t0);
+  const int n_vis = BAND ? max(0, min((w_hi_first + 1) / kBc, N / kBc) - t0)
+                         : min(CAUSAL ? (q0 + 1) / kBc : n, N / kBc);
 
   auto tile_rsrc = [&](const uint16_t* head, int kv0) {
     return make_rsrc(head + (size_t)kv0 * D, (N - kv0) * G::ROW_BYTES);
@@ -610,16 +640,16 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   };
 
   // Tiles [lo_wg, n_full) need no element mask for any row of the workgroup: causal, the
-  // keys below the workgroup's first query; a non-causal window, the keys below its first
-  // query's upper edge; otherwise the whole 64-key tiles.
-  const int n_full =
-      max(0, (CAUSAL ? min(Q0, N) : (window ? min(Q0 + window, N) : N)) / kBc - t0);
+  // keys below the workgroup's first query; with a band, the keys up to its first row's
+  // upper edge; otherwise the whole 64-key tiles.
+  const int n_full = BAND ? max(0, (wg_hi_first + 1) / kBc - t0)
+                          : (CAUSAL ? min(Q0, N) / kBc : N / kBc);
   int j = 0;
   // The window's lower edge: masked steps for every wave.
   for (; j < lo_wg; ++j) {
     rescale();
     float alpha;
-    const bool any = step<D, CAUSAL, NP, true, WIN, ALIBI, SOFTCAP>(
+    const bool any = step<D, CAUSAL, NP, true, BAND, ALIBI, SOFTCAP>(
         sv[j & 1], sk[j & 1], p_prev, acc, qf, s_cur, s_nxt, p_cur, st, alpha, (t0 + j) * kBc,
         klo, khi, N, c, tau, h, vaddr, kaddr, sm, [&]() { staging(j); });
     finish_step(j, any, alpha);
@@ -630,12 +660,12 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   for (; j + 1 < n_full; j += 2) {
     float alpha;
     rescale();
-    bool any = step<D, CAUSAL, NP, false, WIN, ALIBI, SOFTCAP>(
+    bool any = step<D, CAUSAL, NP, false, BAND, ALIBI, SOFTCAP>(
         sv[j & 1], sk[j & 1], p_prev, acc, qf, s_cur, s_nxt, p_cur, st, alpha, (t0 + j) * kBc, klo, khi, N, c,
         tau, h, vaddr, kaddr, sm, [&]() { staging(j); });
     finish_step(j, any, alpha);
     rescale();
-    any = step<D, CAUSAL, NP, false, WIN, ALIBI, SOFTCAP>(
+    any = step<D, CAUSAL, NP, false, BAND, ALIBI, SOFTCAP>(
         sv[(j + 1) & 1], sk[(j + 1) & 1], p_cur, acc, qf, s_nxt, s_cur, p_prev, st, alpha,
         (t0 + j + 1) * kBc, klo, khi, N, c, tau, h, vaddr, kaddr, sm, [&]() { staging(j + 1); });
     finish_step(j + 1, any, alpha);
@@ -643,7 +673,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   for (; j < n_full; ++j) {
     rescale();
     float alpha;
-    const bool any = step<D, CAUSAL, NP, false, WIN, ALIBI, SOFTCAP>(
+    const bool any = step<D, CAUSAL, NP, false, BAND, ALIBI, SOFTCAP>(
         sv[j & 1], sk[j & 1], p_prev, acc, qf, s_cur, s_nxt, p_cur, st, alpha, (t0 + j) * kBc, klo, khi, N, c,
         tau, h, vaddr, kaddr, sm, [&]() { staging(j); });
     finish_step(j, any, alpha);
@@ -656,7 +686,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   for (; j < n_vis; ++j) {
     rescale();
     float alpha;
-    const bool any = step<D, CAUSAL, NP, false, WIN, ALIBI, SOFTCAP>(
+    const bool any = step<D, CAUSAL, NP, false, BAND, ALIBI, SOFTCAP>(
         sv[j & 1], sk[j & 1], p_prev, acc, qf, s_cur, s_nxt, p_cur, st, alpha, (t0 + j) * kBc, klo, khi, N, c,
         tau, h, vaddr, kaddr, sm, [&]() { staging(j); });
     finish_step(j, any, alpha);
@@ -665,7 +695,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   for (; j < n_w; ++j) {
     rescale();
     float alpha;
-    const bool any = step<D, CAUSAL, NP, true, WIN, ALIBI, SOFTCAP>(
+    const bool any = step<D, CAUSAL, NP, true, BAND, ALIBI, SOFTCAP>(
         sv[j & 1], sk[j & 1], p_prev, acc, qf, s_cur, s_nxt, p_cur, st, alpha, (t0 + j) * kBc, klo, khi, N, c,
         tau, h, vaddr, kaddr, sm, [&]() { staging(j); });
     finish_step(j, any, alpha);
@@ -728,53 +758,54 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   }
 }
 
-template <int D, bool CAUSAL, int NP, bool WIN, bool ALIBI, bool SOFTCAP>
+template <int D, bool CAUSAL, int NP, bool BAND, bool ALIBI, bool SOFTCAP>
 hipError_t launch_one(const FwdArgs& a) {
   const int nqb = (a.N + kBr - 1) / kBr;
   const long long grid = (long long)a.B * a.Hq * nqb;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
   const float k2 = SOFTCAP ? 2.f * a.c / a.softcap : 0.f;
   const float ccap = SOFTCAP ? a.softcap * kLog2e : 0.f;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NP, WIN, ALIBI, SOFTCAP>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NP, BAND, ALIBI, SOFTCAP>), dim3((unsigned)grid),
                      dim3(kThreads), 0, (hipStream_t)a.stream, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, a.o, a.lse, a.Hq, a.Hkv, a.N, nqb,
-                     a.c, a.tau, a.qsign, a.window, a.alibi, k2, ccap, a.stats);
+                     a.c, a.tau, a.qsign, a.window, a.doc_offsets, a.n_docs, a.alibi, k2, ccap,
+                     a.stats);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, bool WIN>
+template <int D, bool CAUSAL, bool BAND>
 hipError_t launch_np(const FwdArgs& a) {
   switch (a.poly_pairs) {
-    case 0: return launch_one<D, CAUSAL, 0, WIN, false, false>(a);
-    case 4: return launch_one<D, CAUSAL, 4, WIN, false, false>(a);
-    case 8: return launch_one<D, CAUSAL, 8, WIN, false, false>(a);
-    case 12: return launch_one<D, CAUSAL, 12, WIN, false, false>(a);
-    case 16: return launch_one<D, CAUSAL, 16, WIN, false, false>(a);
+    case 0: return launch_one<D, CAUSAL, 0, BAND, false, false>(a);
+    case 4: return launch_one<D, CAUSAL, 4, BAND, false, false>(a);
+    case 8: return launch_one<D, CAUSAL, 8, BAND, false, false>(a);
+    case 12: return launch_one<D, CAUSAL, 12, BAND, false, false>(a);
+    case 16: return launch_one<D, CAUSAL, 16, BAND, false, false>(a);
     default: return hipErrorInvalidValue;
   }
 }
 
 // Score modifications run with the hardware exponential only.
-template <int D, bool CAUSAL, bool WIN>
+template <int D, bool CAUSAL, bool BAND>
 hipError_t launch_mod(const FwdArgs& a) {
   const bool al = a.alibi != nullptr, cap = a.softcap > 0.f;
-  if (!al && !cap) return launch_np<D, CAUSAL, WIN>(a);
+  if (!al && !cap) return launch_np<D, CAUSAL, BAND>(a);
   if (a.poly_pairs != 0) return hipErrorNotSupported;
-  if (al && cap) return launch_one<D, CAUSAL, 0, WIN, true, true>(a);
-  if (al) return launch_one<D, CAUSAL, 0, WIN, true, false>(a);
-  return launch_one<D, CAUSAL, 0, WIN, false, true>(a);
+  if (al && cap) return launch_one<D, CAUSAL, 0, BAND, true, true>(a);
+  if (al) return launch_one<D, CAUSAL, 0, BAND, true, false>(a);
+  return launch_one<D, CAUSAL, 0, BAND, false, true>(a);
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch_win(const FwdArgs& a) {
-  return a.window ? launch_mod<D, CAUSAL, true>(a) : launch_mod<D, CAUSAL, false>(a);
+hipError_t launch_band(const FwdArgs& a) {
+  return (a.window || a.n_docs > 0) ? launch_mod<D, CAUSAL, true>(a) : launch_mod<D, CAUSAL, false>(a);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
-  if (a.d == 128) return a.causal ? launch_win<128, true>(a) : launch_win<128, false>(a);
-  return a.causal ? launch_win<64, true>(a) : launch_win<64, false>(a);
+  if (a.d == 128) return a.causal ? launch_band<128, true>(a) : launch_band<128, false>(a);
+  return a.causal ? launch_band<64, true>(a) : launch_band<64, false>(a);
 }
 
 }  // namespace attn

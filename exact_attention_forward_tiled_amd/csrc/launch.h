@@ -23,6 +23,8 @@ struct FwdArgs {
                     // only when i - W < j, and j < i + W without the causal mask
   const float* alibi;   // device, Hq ALiBi slopes (natural-log units per key), or null
   float softcap;    // soft-capping C (0: off)
+  const int* doc_offsets;   // device, n_docs + 1 document offsets (0, ..., N), or null
+  int n_docs;       // documents (0: no document masking)
   unsigned long long* stats;
   void* stream;
 };

@@ -86,10 +86,20 @@ typedef struct attn_opts {
                                 mask.  Both modifications need the hardware exponential
                                 (ATTN_EUNSUPPORTED otherwise) and the bf16 forward (the MXFP4
                                 forward returns ATTN_EUNSUPPORTED). */
+    const int* doc_offsets;  /* nullable DEVICE pointer to n_docs + 1 ints: document masking (the
+                                same page names it; no definition printed).  The sequence holds
+                                n_docs documents packed back to back, 0 = o[0] < o[1] < ... <
+                                o[n_docs] = N, the same layout for every batch entry; key j is
+                                visible from query i only when both lie in one document (on top
+                                of the causal mask and the window).  Tiles outside a workgroup's
+                                documents are skipped.  Offsets that break the order give
+                                unspecified values but every read stays within the array.
+                                bf16 forward only. */
+    int n_docs;              /* number of documents (>= 1 when doc_offsets is set; else ignored) */
 } attn_opts;
 
 /* Default options: tau = 8, hardware exp (poly_frac 0.5 for ATTN_EXP_MIX), no stats, no
-   window, no ALiBi, no soft-capping. */
+   window, no ALiBi, no soft-capping, no documents. */
 void attn_default_opts(attn_opts* opts);
 
 /*

@@ -89,6 +89,13 @@ def test_opts_validation(fa):
                               None) == -2
         opts = fa.make_opts(8.0, "hw", **kw)
         assert fa.attn_fwd_mxfp4_ex(*[FAKE] * 8, 1, 1, 1, 64, 128, 0, 0.1, opts, None) == -2
+    # documents: at least one, at most N (documents are non-empty); bf16 forward only
+    for nd in (0, -1, 17):
+        opts = fa.make_opts(8.0, "hw", doc_ptr=FAKE, n_docs=nd)
+        assert fa.attn_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 16, 64, 0, 0.1, opts,
+                              None) == -1
+    opts = fa.make_opts(8.0, "hw", doc_ptr=FAKE, n_docs=2)
+    assert fa.attn_fwd_mxfp4_ex(*[FAKE] * 8, 1, 1, 1, 64, 128, 0, 0.1, opts, None) == -2
 
 
 def test_default_opts_layout(fa):
@@ -97,10 +104,10 @@ def test_default_opts_layout(fa):
     from exact_attention_forward_tiled_amd.binding import AttnOpts, lib
     o = AttnOpts()
     o.tau, o.exp_mode, o.poly_frac, o.stats, o.window = -3.0, 9, -3.0, FAKE, -7
-    o.alibi_slopes, o.softcap = FAKE, -2.0
+    o.alibi_slopes, o.softcap, o.doc_offsets, o.n_docs = FAKE, -2.0, FAKE, -5
     lib.attn_default_opts(ctypes.byref(o))
     assert (o.tau, o.exp_mode, o.poly_frac, o.stats, o.window) == (8.0, 0, 0.5, None, 0)
-    assert (o.alibi_slopes, o.softcap) == (None, 0.0)
+    assert (o.alibi_slopes, o.softcap, o.doc_offsets, o.n_docs) == (None, 0.0, None, 0)
 
 
 def test_mxfp4_validation(fa):

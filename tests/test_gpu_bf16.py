@@ -277,6 +277,54 @@ def test_score_modifications(case):
     _check(o, lse, ro, rl, f"softcap {cap} alibi {use_alibi} window {W}")
 
 
+DOC_CASES = [
+    # B, Hq, Hkv, N, d, causal, offsets, window, alibi
+    (1, 2, 2, 256, 128, False, [0, 256], 0, False),
+    (1, 2, 2, 333, 128, True, [0, 100, 101, 333], 0, False),
+    (2, 4, 2, 700, 64, False, [0, 64, 128, 511, 700], 0, False),
+    (1, 2, 1, 1000, 128, True, [0, 17, 300, 301, 302, 900, 1000], 0, False),
+    (1, 4, 4, 1000, 128, False, [0, 250, 520, 1000], 100, False),
+    (1, 4, 2, 777, 128, True, [0, 5, 400, 777], 0, True),
+]
+
+
+@pytest.mark.parametrize("case", DOC_CASES, ids=lambda c: "B%dHq%dHkv%dN%dd%d%sD%dW%dal%d" % (
+    c[0], c[1], c[2], c[3], c[4], "c" if c[5] else "n", len(c[6]) - 1, c[7], c[8]))
+def test_document_masking(case):
+    """Packed documents (keys visible only within the query's document) against the
+    oracle, with the masks, a window and ALiBi."""
+    import torch
+    B, Hq, Hkv, N, d, causal, off, W, use_alibi = case
+    qb, kb, vb = random_case(70 + N, B, Hq, Hkv, N, d)
+    slopes = 0.5 ** (np.arange(1, Hq + 1) * 8.0 / Hq) if use_alibi else None
+    log(f"case {case}")
+    o, lse = _run(qb, kb, vb, causal, d ** -0.5, window=W,
+                  docs=torch.tensor(off, dtype=torch.int32, device="cuda"),
+                  alibi=None if slopes is None else
+                  torch.tensor(slopes, dtype=torch.float32, device="cuda"))
+    q64, k64, v64 = (synth.bf16_bits_to_f64(x) for x in (qb, kb, vb))
+    ref_slopes = None if slopes is None else slopes.astype(np.float32).astype(np.float64)
+    ro, rl = oracle.attention(q64, k64, v64, causal, d ** -0.5, window=W, docs=off,
+                              alibi=ref_slopes)
+    _check(o, lse, ro, rl, f"documents {off} window {W}")
+
+
+def test_document_masking_large_sampled_rows():
+    """N = 8192 holding 7 documents of mixed lengths, causal: sampled rows of several heads."""
+    import torch
+    B, Hq, Hkv, N, d = 1, 4, 2, 8192, 128
+    off = [0, 1000, 1001, 3000, 4096, 4200, 7777, 8192]
+    qb, kb, vb = random_case(79, B, Hq, Hkv, N, d)
+    o, lse = _run(qb, kb, vb, True, d ** -0.5,
+                  docs=torch.tensor(off, dtype=torch.int32, device="cuda"))
+    q64, k64, v64 = (synth.bf16_bits_to_f64(x) for x in (qb, kb, vb))
+    rng = np.random.default_rng(79)
+    rows = np.unique(np.concatenate([off[:-1], [x - 1 for x in off[1:]], rng.integers(0, N, 16)]))
+    for h in (0, Hq - 1):
+        ro, rl = oracle.attention_rows(q64, k64, v64, True, d ** -0.5, 0, h, rows, docs=off)
+        _check(o[0, h, rows], lse[0, h, rows], ro, rl, f"head {h}")
+
+
 def test_skip_ratio_stats():
     """The rescale counter: tau = 0 rescales on most steps, tau = 8 skips most of them."""
     import torch
