@@ -18,14 +18,18 @@ check), written from the definitions so that a reader can check it by eye:
 * ``mx``     -- OCP MXFP4 quantisation (E2M1 payload, E8M0 block scale) and a
   step-by-step emulation of Direct-P ("Hardware-Aware FP4 FlashAttention-4",
   section "1. Direct-P para Inferencia Directa").
+* ``mxfp8``  -- OCP MXFP8 (E4M3 payload, E8M0 block scale) quantisation and a
+  step-by-step emulation of the FP8 forward (P rounded to E4M3 with one
+  power-of-two scale per 32 keys; the same page's "Resultados" compares an FP8
+  path, and its section "2. Causal Backward Cuantizado" keeps P and V in FP8).
 
 Parity status: every function is pinned by tests under ``tests/`` against
 brute force, a library routine (torch's CPU attention in float64), closed
-forms and invariants; see the test modules ``test_oracle_exact.py`` and
-``test_oracle_mx.py``.
+forms and invariants; see the test modules ``test_oracle_exact.py``,
+``test_oracle_mx.py`` and ``test_oracle_mxfp8.py``.
 """
 
 from .exact import attention, attention_brute, attention_head, attention_rows, kv_head
-from . import mx
+from . import mx, mxfp8
 
-__all__ = ["attention", "attention_brute", "attention_head", "attention_rows", "kv_head", "mx"]
+__all__ = ["attention", "attention_brute", "attention_head", "attention_rows", "kv_head", "mx", "mxfp8"]

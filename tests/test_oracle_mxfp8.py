@@ -1,0 +1,301 @@
+"""Pins for the MXFP8 (E4M3) quantiser and the FP8 forward emulation in oracle.mxfp8."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import mxfp8 as m8
+
+
+# ---- E4M3 / E8M0 encodings ---------------------------------------------------------
+
+def test_e4m3_table_matches_torch_decode():
+    """All 256 bytes decode as torch's float8_e4m3fn does (an independent implementation),
+    NaN at 0x7F and 0xFF only."""
+    got = m8.e4m3_value(np.arange(256))
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)].astype(np.float64))
+    assert set(np.flatnonzero(np.isnan(got))) == {0x7F, 0xFF}
+
+
+def test_e4m3_landmarks():
+    """Closed forms of the format: largest 448, smallest normal 2^-6, smallest subnormal 2^-9,
+    strictly increasing magnitudes."""
+    mags = m8.E4M3_MAGNITUDES
+    assert mags[-1] == 448.0 and mags[1] == 2.0 ** -9 and mags[8] == 2.0 ** -6
+    assert np.all(np.diff(mags) > 0)
+    assert m8.e4m3_value(0x38) == 1.0 and m8.e4m3_value(0xB8) == -1.0
+
+
+def test_round_matches_brute_force_nearest():
+    """Away from ties the code is the nearest magnitude (scan of all 127); ties go to the even
+    code; values past 448 saturate."""
+    mags = m8.E4M3_MAGNITUDES
+    rng = np.random.default_rng(3)
+    y = np.concatenate([rng.uniform(0, 500, 4000), np.exp2(rng.uniform(-12, 9, 4000))])
+    codes = m8.e4m3_round(y)
+    for yy, c in zip(y, codes):
+        d = np.abs(mags - yy)
+        best = np.flatnonzero(d == d.min())
+        want = best[0] if len(best) == 1 else best[best % 2 == 0][0]
+        assert c == want, yy
+    # exact midpoints between neighbours: the even code wins
+    mids = (mags[:-1] + mags[1:]) / 2
+    got = m8.e4m3_round(mids)
+    lo = np.arange(126)
+    assert np.array_equal(got, np.where(lo % 2 == 0, lo, lo + 1))
+    assert np.all(m8.e4m3_round([448.0, 463.9, 1e6]) == 126)
+
+
+def test_round_matches_torch_cast_in_range():
+    """torch's fp32 -> float8_e4m3fn cast rounds to nearest even; below 464 it agrees code for
+    code (above, torch gives NaN where the MX rule saturates)."""
+    rng = np.random.default_rng(4)
+    y = np.concatenate([rng.uniform(0, 463, 20000), np.exp2(rng.uniform(-14, 8.8, 20000))])
+    y = y.astype(np.float32)
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(m8.e4m3_round(y.astype(np.float64)), ref)
+
+
+def _floor_log2(a):
+    k = 0
+    while 2.0 ** k > a:
+        k -= 1
+    while 2.0 ** (k + 1) <= a:
+        k += 1
+    return k
+
+
+def test_shared_exponent():
+    for a in [1.0, 2.0, 0.5, 3.999, 448.0, 1e-3, 6.1e4, 2.0 ** -100, 7.0]:
+        assert m8.shared_exponent(a) == _floor_log2(a) - 8, a
+    assert m8.shared_exponent(0.0) == 0
+    assert m8.shared_exponent(2.0 ** 300) == 127 and m8.shared_exponent(2.0 ** -300) == -127
+    for k in range(-20, 21):
+        want = torch.tensor([2.0 ** (k - 8)]).to(torch.float8_e8m0fnu).view(torch.uint8).item()
+        assert int(m8.shared_exponent(2.0 ** k)) + 127 == want
+
+
+def test_quantize_round_trip_exact_values():
+    """Blocks of representable values times 2^E, whose amax fixes that E, come back bit-exact."""
+    rng = np.random.default_rng(5)
+    mags = m8.E4M3_MAGNITUDES
+    for E in (-9, -1, 0, 4):
+        vals = rng.choice(np.concatenate([mags, -mags[1:]]), 32)
+        vals[5] = 320.0                     # amax in [256, 512) -> shared exponent E
+        vals = np.clip(vals, -320.0, 320.0)
+        x = np.ldexp(vals, E)
+        codes, sc = m8.quantize(x[None, :], axis=-1)
+        assert sc[0, 0] == E + 127
+        assert np.array_equal(m8.dequantize(codes, sc, axis=-1)[0], x)
+
+
+def test_quantize_error_bound_and_layout():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((3, 64, 96)).astype(np.float32).astype(np.float64)
+    for axis in (-1, -2):
+        codes, sc = m8.quantize(x, axis=axis)
+        xt = m8.dequantize(codes, sc, axis=axis)
+        xm = np.moveaxis(x, axis, -1).reshape(-1, 32)
+        tm = np.moveaxis(xt, axis, -1).reshape(-1, 32)
+        e = np.moveaxis(sc.astype(np.int64) - 127, axis, -1).reshape(-1)
+        scale = np.ldexp(1.0, e)[:, None]
+        a = np.abs(xm) / scale
+        # half the spacing of the binade holding a (subnormal spacing 2^-9 below 2^-6);
+        # past 448 the error is the clip
+        binade = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+        half_gap = np.ldexp(1.0, (binade - 4).astype(np.int64))
+        bound = np.where(a > 448, a - 448, half_gap) * scale
+        assert np.all(np.abs(xm - tm) <= bound + 1e-15)
+        assert np.all(np.sign(tm) * np.sign(xm) >= 0)
+        amax = np.abs(xm).max(axis=1)
+        assert np.all((amax / scale[:, 0] >= 256) & (amax / scale[:, 0] < 512))
+    # the block max of [256, 512) above 448 saturates
+    blk = np.full((1, 32), 1.0)
+    blk[0, 0] = 1.95
+    codes, sc = m8.quantize(blk, axis=-1)
+    assert sc[0, 0] == 127 - 8 and codes[0, 0] == 0x7E
+
+
+def test_zero_block_and_zero_sign():
+    x = np.zeros((1, 32))
+    x[0, 3] = -0.0
+    codes, sc = m8.quantize(x, axis=-1)
+    assert sc[0, 0] == 127 and np.all(codes == 0)
+    y = np.full((1, 32), 1e-9)
+    y[0, 0] = 4.0
+    y[0, 1] = -1e-9
+    codes, _ = m8.quantize(y, axis=-1)
+    assert codes[0, 1] == 0                  # magnitude 0 is stored as +0
+
+
+# ---- FP8 forward emulation ----------------------------------------------------------
+
+def _case(seed, B, H, N, d):
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.standard_normal((B, H, N, d)).astype(np.float32) for _ in range(3))
+    return m8.quantize_inputs(q, k, v)
+
+
+def test_fp8p_constant_v_gives_one():
+    """The denominator is the sum of the same rounded weights PV uses, so V = 1 gives 1."""
+    t = _case(20, 1, 2, 96, 32)
+    v = np.ones_like(t["v"])
+    for causal in (False, True):
+        o, _ = m8.fp8_attention(t["q"], t["k"], v, causal, 0.5)
+        assert np.allclose(o, 1.0, atol=1e-14)
+
+
+def test_fp8p_zero_query():
+    """Q = 0: t = 0, m = 0, E = -7, every weight is 2^7 * 2^-7 = 1, so O is the mean of V~."""
+    t = _case(21, 1, 2, 64, 32)
+    q = np.zeros_like(t["q"])
+    o, lse = m8.fp8_attention(q, t["k"], t["v"], False, 0.5)
+    assert np.allclose(o, t["v"].mean(axis=2, keepdims=True), atol=1e-14)
+    assert np.allclose(lse, math.log(64), atol=1e-14)
+    _, _, p = m8.fp8p_rows(q[0, 0], t["k"][0, 0], t["v"][0, 0], np.arange(64), False, 0.5)
+    assert np.all(p == 1.0)
+
+
+def test_fp8p_single_visible_key():
+    t = _case(22, 1, 1, 32, 32)
+    o, lse = m8.fp8_attention(t["q"], t["k"], t["v"], True, 0.5)
+    assert np.allclose(o[0, 0, 0], t["v"][0, 0, 0], atol=1e-15)
+    # the one weight is 2^(t - m) rounded to E4M3 in the binade [128, 256) * 2^-7:
+    # LSE = ln2 * m + ln(p~), within ln(1 + 2^-4) of the exact logit
+    s = 0.5 * t["q"][0, 0, 0] @ t["k"][0, 0, 0]
+    tl = s * m8.LOG2E
+    m = math.ceil(tl)
+    y = 2.0 ** (tl - m + 7)
+    k = round(y / 2.0 ** (math.floor(math.log2(y)) - 3))   # multiple of the binade's spacing
+    p = k * 2.0 ** (math.floor(math.log2(y)) - 3) * 2.0 ** -7
+    assert abs(lse[0, 0, 0] - (math.log(2) * m + math.log(p))) < 1e-12
+    assert abs(lse[0, 0, 0] - s) <= math.log1p(2.0 ** -4)
+
+
+def test_fp8p_exact_when_weights_are_representable():
+    """When every 2^(t - m) is a power of two within E4M3's range of the block max, the FP8
+    forward equals the exact oracle."""
+    N, d = 64, 1
+    rng = np.random.default_rng(23)
+    t_vals = -rng.integers(0, 12, size=N).astype(np.float64)
+    t_vals[0] = 0.0
+    t_vals[32] = -3.0
+    q = np.ones((1, 1, 1, d))
+    k = (t_vals / m8.LOG2E).reshape(1, 1, N, d)
+    v = rng.standard_normal((1, 1, N, 5))
+    o, lse, p = m8.fp8p_rows(q[0, 0], k[0, 0], v[0, 0], np.array([0]), False, 1.0)
+    oe, le = oracle.attention(q, k, v, False, 1.0)
+    assert np.allclose(p[0], 2.0 ** t_vals, rtol=1e-12)
+    assert np.allclose(o[0], oe[0, 0, 0], atol=1e-12)
+    assert abs(lse[0] - le[0, 0, 0]) < 1e-12
+
+
+def test_fp8p_independent_of_integer_reference():
+    """Shifting the integer reference max by any integer scales every weight by the same power
+    of two and leaves O and LSE unchanged."""
+    t = _case(24, 1, 1, 128, 64)
+    qr, kh, vh = t["q"][0, 0, :16], t["k"][0, 0], t["v"][0, 0]
+    rows = np.arange(16)
+    o0, l0, p0 = m8.fp8p_rows(qr, kh, vh, rows, False, 0.3)
+    m0 = np.ceil((0.3 * qr @ kh.T * m8.LOG2E).max(axis=1))
+    for shift in (-3, 2, 7):
+        o1, l1, p1 = m8.fp8p_rows(qr, kh, vh, rows, False, 0.3, ref_max=m0 + shift)
+        assert np.array_equal(p1 * 2.0 ** shift, p0)
+        assert np.allclose(o1, o0, atol=1e-15) and np.allclose(l1, l0, atol=1e-12)
+
+
+def test_fp8p_weights_within_rounding_bound():
+    """Each weight is within half an E4M3 spacing (of the block-scaled value) of 2^(t - m), and
+    the block max sits in [128, 256) * 2^E."""
+    t = _case(25, 1, 1, 64, 32)
+    qr, kh = t["q"][0, 0, :8], t["k"][0, 0]
+    _, _, p = m8.fp8p_rows(qr, kh, t["v"][0, 0], np.arange(8), False, 0.5)
+    tt = 0.5 * qr @ kh.T * m8.LOG2E
+    m = np.ceil(tt.max(axis=1))
+    exact = 2.0 ** (tt - m[:, None])
+    for b0 in range(0, 64, 32):
+        blk = exact[:, b0:b0 + 32]
+        E = np.floor(np.log2(blk.max(axis=1))) - 7
+        y = blk / 2.0 ** E[:, None]
+        assert np.all((y.max(axis=1) >= 128) & (y.max(axis=1) < 256))
+        binade = np.floor(np.log2(np.maximum(y, 2.0 ** -6)))
+        half_gap = 2.0 ** (binade - 4)
+        err = np.abs(p[:, b0:b0 + 32] / 2.0 ** E[:, None] - y)
+        assert np.all(err <= half_gap + 1e-12)
+
+
+def test_fp8p_close_to_exact_on_gaussian_inputs():
+    """Gaussian softmax test: three mantissa bits per weight keep the output within about 1 %
+    of exact attention on the same operands (the explainer page quotes a mean cosine of about
+    0.990 against BF16 for its FP8 path; here the cosine is against the exact result)."""
+    t = _case(26, 1, 2, 256, 64)
+    o, lse = m8.fp8_attention(t["q"], t["k"], t["v"], False, 0.125)
+    oe, le = oracle.attention(t["q"], t["k"], t["v"], False, 0.125)
+    rel = np.linalg.norm(o - oe) / np.linalg.norm(oe)
+    cos = (o * oe).sum(-1) / np.linalg.norm(o, axis=-1) / np.linalg.norm(oe, axis=-1)
+    assert rel < 0.03 and cos.mean() > 0.999
+    assert np.max(np.abs(lse - le)) < 0.05
+
+
+def test_fp8p_gqa_matches_repeated_heads():
+    t = _case(27, 1, 4, 64, 32)
+    k2, v2 = t["k"][:, :2], t["v"][:, :2]
+    o, lse = m8.fp8_attention(t["q"], k2, v2, True, 0.3)
+    om, lm = m8.fp8_attention(t["q"], np.repeat(k2, 2, axis=1), np.repeat(v2, 2, axis=1),
+                              True, 0.3)
+    assert np.array_equal(o, om) and np.array_equal(lse, lm)
+
+
+@pytest.mark.parametrize("bad", ["no_consistent_norm", "float_ref_max", "offset_8",
+                                 "round_down", "no_subnormals"])
+def test_planted_fp8p_mistakes_are_caught(bad, monkeypatch):
+    """Planted mistakes in the emulation or the rounding fail at least one pin above."""
+    orig_rows = m8.fp8p_rows
+    orig_round = m8.e4m3_round
+
+    def mutated_rows(qt_rows, kt, vt, row_ids, causal, scale, ref_max=None):
+        if bad == "no_consistent_norm":
+            o, lse, p = orig_rows(qt_rows, kt, vt, row_ids, causal, scale, ref_max)
+            t = scale * qt_rows @ kt.T * m8.LOG2E
+            if causal:
+                t = np.where(np.arange(kt.shape[0])[None] > np.asarray(row_ids)[:, None],
+                             -np.inf, t)
+            m = np.ceil(t.max(axis=1))
+            l_exact = np.exp2(t - m[:, None]).sum(axis=1)
+            return (p @ vt) / l_exact[:, None], lse, p
+        if bad == "float_ref_max":
+            t = scale * qt_rows @ kt.T * m8.LOG2E
+            m = t.max(axis=1) if ref_max is None else np.asarray(ref_max) + 0.37
+            return orig_rows(qt_rows, kt, vt, row_ids, causal, scale, ref_max=m)
+        return orig_rows(qt_rows, kt, vt, row_ids, causal, scale, ref_max)
+
+    def mutated_round(y):
+        y = np.asarray(y, dtype=np.float64)
+        if bad == "round_down":
+            c = orig_round(y)
+            return np.where(m8.E4M3_MAGNITUDES[c] > y, np.maximum(c.astype(int) - 1, 0),
+                            c).astype(np.uint8)
+        if bad == "no_subnormals":
+            return np.where(y < 2.0 ** -6, 0, orig_round(y)).astype(np.uint8)
+        return orig_round(y)
+
+    monkeypatch.setattr(m8, "fp8p_rows", mutated_rows)
+    monkeypatch.setattr(m8, "e4m3_round", mutated_round)
+    if bad == "offset_8":
+        monkeypatch.setattr(m8, "P_EXP_OFFSET", 8)
+    pins = [test_round_matches_brute_force_nearest, test_round_matches_torch_cast_in_range,
+            test_fp8p_constant_v_gives_one, test_fp8p_zero_query,
+            test_fp8p_independent_of_integer_reference, test_fp8p_weights_within_rounding_bound,
+            test_fp8p_exact_when_weights_are_representable]
+    failed = 0
+    for pin in pins:
+        try:
+            pin()
+        except AssertionError:
+            failed += 1
+    assert failed > 0
