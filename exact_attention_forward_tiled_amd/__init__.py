@@ -11,8 +11,10 @@ import importlib
 
 _BINDING_NAMES = ("AttnError", "EXPORTS", "attn_fwd", "attn_fwd_ex", "attn_fwd_mxfp4",
                   "attn_fwd_mxfp4_ex", "attn_quantize_mxfp4_cols_t", "attn_quantize_mxfp4_rows",
-                  "check", "fwd", "fwd_mxfp4", "make_opts", "quantize_mxfp4_cols_t",
-                  "quantize_mxfp4_rows", "STATS_COUNTERS", "lib")
+                  "attn_fwd_mxfp8", "attn_fwd_mxfp8_ex", "attn_quantize_mxfp8_cols_t",
+                  "attn_quantize_mxfp8_rows", "check", "fwd", "fwd_mxfp4", "fwd_mxfp8",
+                  "make_opts", "quantize_mxfp4_cols_t", "quantize_mxfp4_rows",
+                  "quantize_mxfp8_cols_t", "quantize_mxfp8_rows", "STATS_COUNTERS", "lib")
 
 __all__ = list(_BINDING_NAMES)
 

@@ -18,8 +18,9 @@ EXP_MODES = {"hw": 0, "poly": 1, "mix": 2}
 
 # entry points declared in include/attn.h
 EXPORTS = ("attn_default_opts", "attn_fwd", "attn_fwd_ex", "attn_fwd_mxfp4", "attn_fwd_mxfp4_ex",
-           "attn_quantize_mxfp4_rows", "attn_quantize_mxfp4_cols_t", "attn_strerror",
-           "attn_last_hip_error")
+           "attn_quantize_mxfp4_rows", "attn_quantize_mxfp4_cols_t", "attn_fwd_mxfp8",
+           "attn_fwd_mxfp8_ex", "attn_quantize_mxfp8_rows", "attn_quantize_mxfp8_cols_t",
+           "attn_strerror", "attn_last_hip_error")
 
 
 class AttnOpts(ctypes.Structure):
@@ -45,6 +46,10 @@ def _load():
         "attn_fwd_mxfp4_ex": (I, [P] * 8 + [I] * 6 + [F, OP, P]),
         "attn_quantize_mxfp4_rows": (I, [P, P, P, LL, I, P]),
         "attn_quantize_mxfp4_cols_t": (I, [P, P, P, I, I, I, P]),
+        "attn_fwd_mxfp8": (I, [P] * 8 + [I] * 6 + [F]),
+        "attn_fwd_mxfp8_ex": (I, [P] * 8 + [I] * 6 + [F, OP, P]),
+        "attn_quantize_mxfp8_rows": (I, [P, P, P, LL, I, P]),
+        "attn_quantize_mxfp8_cols_t": (I, [P, P, P, I, I, I, P]),
         "attn_strerror": (ctypes.c_char_p, [I]),
         "attn_last_hip_error": (I, []),
     }
@@ -112,6 +117,24 @@ def attn_fwd_mxfp4_ex(q4, qs, k4, ks, vt4, vts, o, lse, B, Hq, Hkv, N, d, causal
 
 def attn_fwd_mxfp4(q4, qs, k4, ks, vt4, vts, o, lse, B, Hq, Hkv, N, d, causal, scale):
     return lib.attn_fwd_mxfp4(q4, qs, k4, ks, vt4, vts, o, lse, B, Hq, Hkv, N, d, causal, scale)
+
+
+def attn_fwd_mxfp8_ex(q8, qs, k8, ks, vt8, vts, o, lse, B, Hq, Hkv, N, d, causal, scale,
+                      opts=None, stream=None):
+    return lib.attn_fwd_mxfp8_ex(q8, qs, k8, ks, vt8, vts, o, lse, B, Hq, Hkv, N, d, causal,
+                                 scale, ctypes.byref(opts) if opts is not None else None, stream)
+
+
+def attn_fwd_mxfp8(q8, qs, k8, ks, vt8, vts, o, lse, B, Hq, Hkv, N, d, causal, scale):
+    return lib.attn_fwd_mxfp8(q8, qs, k8, ks, vt8, vts, o, lse, B, Hq, Hkv, N, d, causal, scale)
+
+
+def attn_quantize_mxfp8_rows(x, codes, scales, rows, cols, stream=None):
+    return lib.attn_quantize_mxfp8_rows(x, codes, scales, rows, cols, stream)
+
+
+def attn_quantize_mxfp8_cols_t(x, codes, scales, batch, rows, cols, stream=None):
+    return lib.attn_quantize_mxfp8_cols_t(x, codes, scales, batch, rows, cols, stream)
 
 
 def attn_quantize_mxfp4_rows(x, codes, scales, rows, cols, stream=None):
@@ -239,4 +262,60 @@ def fwd_mxfp4(q4, qs, k4, ks, vt4, vts, causal=False, scale=None, tau=8.0, stats
                             vt4.data_ptr(), vts.data_ptr(), o.data_ptr(), lse.data_ptr(),
                             B, Hq, Hkv, N, d, int(bool(causal)), float(scale), opts,
                             _stream(torch, q4.device)))
+    return o, lse
+
+
+def quantize_mxfp8_rows(x):
+    """fp32 [..., cols] -> (E4M3 codes uint8 [..., cols], E8M0 scales uint8 [..., cols/32])."""
+    torch = _torch()
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous fp32 CUDA tensor")
+    cols = x.shape[-1]
+    rows = x.numel() // cols
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(x.shape[:-1] + (cols // 32,), dtype=torch.uint8, device=x.device)
+    check(attn_quantize_mxfp8_rows(x.data_ptr(), codes.data_ptr(), scales.data_ptr(), rows, cols,
+                                   _stream(torch, x.device)))
+    return codes, scales
+
+
+def quantize_mxfp8_cols_t(x):
+    """fp32 [..., rows, cols] -> transposed (codes [..., cols, rows], scales [..., cols, rows/32])."""
+    torch = _torch()
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous fp32 CUDA tensor")
+    rows, cols = x.shape[-2], x.shape[-1]
+    batch = x.numel() // (rows * cols)
+    lead = x.shape[:-2]
+    codes = torch.empty(lead + (cols, rows), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(lead + (cols, rows // 32), dtype=torch.uint8, device=x.device)
+    check(attn_quantize_mxfp8_cols_t(x.data_ptr(), codes.data_ptr(), scales.data_ptr(), batch,
+                                     rows, cols, _stream(torch, x.device)))
+    return codes, scales
+
+
+def fwd_mxfp8(q8, qs, k8, ks, vt8, vts, causal=False, scale=None, tau=8.0, stats=None, out=None):
+    """MXFP8 forward: returns (O fp32 [B,Hq,N,d], LSE fp32 [B,Hq,N])."""
+    torch = _torch()
+    B, Hq, N, d = q8.shape
+    Hkv = k8.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    for t in (q8, qs, k8, ks, vt8, vts):
+        if t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("codes and scales must be contiguous uint8 CUDA tensors")
+    if (k8.shape != (B, Hkv, N, d) or qs.shape != (B, Hq, N, d // 32)
+            or ks.shape != (B, Hkv, N, d // 32) or vt8.shape != (B, Hkv, d, N)
+            or vts.shape != (B, Hkv, d, N // 32)):
+        raise ValueError("MXFP8 operand shapes do not match q8 [B, Hq, N, d]")
+    if out is None:
+        o = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q8.device)
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q8.device)
+    else:
+        o, lse = out
+    opts = make_opts(tau, "hw", _stats_ptr(torch, stats))
+    check(attn_fwd_mxfp8_ex(q8.data_ptr(), qs.data_ptr(), k8.data_ptr(), ks.data_ptr(),
+                            vt8.data_ptr(), vts.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                            B, Hq, Hkv, N, d, int(bool(causal)), float(scale), opts,
+                            _stream(torch, q8.device)))
     return o, lse

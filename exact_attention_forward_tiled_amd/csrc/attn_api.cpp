@@ -50,6 +50,40 @@ int check_common(int B, int Hq, int Hkv, int N, int d, int causal, float scale) 
   return ATTN_OK;
 }
 
+// Shared validation and launch of the block-scaled forwards (MXFP4 and MXFP8).
+int mx_fwd(hipError_t (*launch)(const attn::MxArgs&), uint32_t qsign, const uint8_t* qc,
+           const uint8_t* qs, const uint8_t* kc, const uint8_t* ks, const uint8_t* vtc,
+           const uint8_t* vts, float* o, float* lse, int B, int Hq, int Hkv, int N, int d,
+           int causal, float scale, const attn_opts* opts, void* stream) {
+  if (!qc || !qs || !kc || !ks || !vtc || !vts || !o || !lse) return ATTN_EINVAL;
+  if (!aligned(qc, 16) || !aligned(kc, 16) || !aligned(vtc, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4) || !aligned(ks, 4))
+    return ATTN_EINVAL;
+  int st = check_common(B, Hq, Hkv, N, d, causal, scale);
+  if (st != ATTN_OK) return st;
+  attn_opts def;
+  attn_default_opts(&def);
+  const attn_opts* op = opts ? opts : &def;
+  st = check_opts(op);
+  if (st != ATTN_OK) return st;
+  if (d != 128 || N % 32 != 0 || op->window != 0 || op->alibi_slopes != nullptr ||
+      op->softcap != 0.f || op->doc_offsets != nullptr)
+    return ATTN_EUNSUPPORTED;
+
+  attn::MxArgs a;
+  a.qc = qc; a.qs = qs; a.kc = kc; a.ks = ks; a.vtc = vtc; a.vts = vts;
+  a.o = o; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N = N; a.d = d; a.causal = causal;
+  a.c = fabsf(scale) * 1.4426950408889634f;
+  a.qsign = scale < 0.f ? qsign : 0u;
+  a.tau = op->tau;
+  a.stats = op->stats;
+  a.stream = stream;
+  hipError_t e = launch(a);
+  if (e == hipErrorNotSupported) return ATTN_EUNSUPPORTED;
+  return hip_status(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -125,33 +159,8 @@ int attn_fwd_mxfp4_ex(const uint8_t* q4, const uint8_t* qs, const uint8_t* k4, c
                       const uint8_t* vt4, const uint8_t* vts, float* o, float* lse, int B, int Hq,
                       int Hkv, int N, int d, int causal, float scale, const attn_opts* opts,
                       void* stream) {
-  if (!q4 || !qs || !k4 || !ks || !vt4 || !vts || !o || !lse) return ATTN_EINVAL;
-  if (!aligned(q4, 16) || !aligned(k4, 16) || !aligned(vt4, 16) || !aligned(o, 16) ||
-      !aligned(lse, 4) || !aligned(ks, 4))
-    return ATTN_EINVAL;
-  int st = check_common(B, Hq, Hkv, N, d, causal, scale);
-  if (st != ATTN_OK) return st;
-  attn_opts def;
-  attn_default_opts(&def);
-  const attn_opts* op = opts ? opts : &def;
-  st = check_opts(op);
-  if (st != ATTN_OK) return st;
-  if (d != 128 || N % 32 != 0 || op->window != 0 || op->alibi_slopes != nullptr ||
-      op->softcap != 0.f || op->doc_offsets != nullptr)
-    return ATTN_EUNSUPPORTED;
-
-  attn::Mxfp4Args a;
-  a.q4 = q4; a.qs = qs; a.k4 = k4; a.ks = ks; a.vt4 = vt4; a.vts = vts;
-  a.o = o; a.lse = lse;
-  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N = N; a.d = d; a.causal = causal;
-  a.c = fabsf(scale) * 1.4426950408889634f;
-  a.qsign = scale < 0.f ? 0x88888888u : 0u;
-  a.tau = op->tau;
-  a.stats = op->stats;
-  a.stream = stream;
-  hipError_t e = attn::launch_fwd_mxfp4(a);
-  if (e == hipErrorNotSupported) return ATTN_EUNSUPPORTED;
-  return hip_status(e);
+  return mx_fwd(attn::launch_fwd_mxfp4, 0x88888888u, q4, qs, k4, ks, vt4, vts, o, lse, B, Hq, Hkv,
+                N, d, causal, scale, opts, stream);
 }
 
 int attn_fwd_mxfp4(const uint8_t* q4, const uint8_t* qs, const uint8_t* k4, const uint8_t* ks,
@@ -175,6 +184,38 @@ int attn_quantize_mxfp4_cols_t(const float* x, uint8_t* codes, uint8_t* scales, 
   if (batch < 1 || rows < 32 || rows % 32 != 0 || cols < 1) return ATTN_EINVAL;
   if ((long long)batch * rows * cols >= (1LL << 40)) return ATTN_EUNSUPPORTED;
   return hip_status(attn::launch_quantize_cols_t(x, codes, scales, batch, rows, cols, stream));
+}
+
+int attn_fwd_mxfp8_ex(const uint8_t* q8, const uint8_t* qs, const uint8_t* k8, const uint8_t* ks,
+                      const uint8_t* vt8, const uint8_t* vts, float* o, float* lse, int B, int Hq,
+                      int Hkv, int N, int d, int causal, float scale, const attn_opts* opts,
+                      void* stream) {
+  return mx_fwd(attn::launch_fwd_mxfp8, 0x80808080u, q8, qs, k8, ks, vt8, vts, o, lse, B, Hq, Hkv,
+                N, d, causal, scale, opts, stream);
+}
+
+int attn_fwd_mxfp8(const uint8_t* q8, const uint8_t* qs, const uint8_t* k8, const uint8_t* ks,
+                   const uint8_t* vt8, const uint8_t* vts, float* o, float* lse, int B, int Hq,
+                   int Hkv, int N, int d, int causal, float scale) {
+  return attn_fwd_mxfp8_ex(q8, qs, k8, ks, vt8, vts, o, lse, B, Hq, Hkv, N, d, causal, scale,
+                           nullptr, nullptr);
+}
+
+int attn_quantize_mxfp8_rows(const float* x, uint8_t* codes, uint8_t* scales, long long rows,
+                             int cols, void* stream) {
+  if (!x || !codes || !scales) return ATTN_EINVAL;
+  if (rows < 1 || cols < 32 || cols % 32 != 0) return ATTN_EINVAL;
+  if (!aligned(x, 16) || !aligned(codes, 16)) return ATTN_EINVAL;
+  return hip_status(attn::launch_quantize8_rows(x, codes, scales, rows, cols, stream));
+}
+
+int attn_quantize_mxfp8_cols_t(const float* x, uint8_t* codes, uint8_t* scales, int batch,
+                               int rows, int cols, void* stream) {
+  if (!x || !codes || !scales) return ATTN_EINVAL;
+  if (batch < 1 || rows < 32 || rows % 32 != 0 || cols < 1) return ATTN_EINVAL;
+  if (!aligned(codes, 16)) return ATTN_EINVAL;
+  if ((long long)batch * rows * cols >= (1LL << 40)) return ATTN_EUNSUPPORTED;
+  return hip_status(attn::launch_quantize8_cols_t(x, codes, scales, batch, rows, cols, stream));
 }
 
 }  // extern "C"

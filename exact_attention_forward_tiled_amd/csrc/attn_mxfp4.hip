@@ -504,12 +504,12 @@ void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict_
 }
 
 template <bool CAUSAL>
-hipError_t launch_mxfp4(const Mxfp4Args& a) {
+hipError_t launch_mxfp4(const MxArgs& a) {
   const int nqb = (a.N + kMBr - 1) / kMBr;
   const long long grid = (long long)a.B * a.Hq * nqb;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((fwd_mxfp4_kernel<CAUSAL>), dim3((unsigned)grid), dim3(kMThreads), 0,
-                     (hipStream_t)a.stream, a.q4, a.qs, a.k4, a.ks, a.vt4, a.vts, a.o, a.lse,
+                     (hipStream_t)a.stream, a.qc, a.qs, a.kc, a.ks, a.vtc, a.vts, a.o, a.lse,
                      a.Hq, a.Hkv, a.N, nqb, a.c, a.tau, a.qsign, a.stats);
   return hipGetLastError();
 }
@@ -538,7 +538,7 @@ hipError_t launch_quantize_cols_t(const float* x, uint8_t* codes, uint8_t* scale
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_mxfp4(const Mxfp4Args& a) {
+hipError_t launch_fwd_mxfp4(const MxArgs& a) {
   if (a.d != kMD) return hipErrorNotSupported;
   return a.causal ? launch_mxfp4<true>(a) : launch_mxfp4<false>(a);
 }

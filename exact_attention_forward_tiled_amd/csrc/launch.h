@@ -29,23 +29,30 @@ struct FwdArgs {
   void* stream;
 };
 
-struct Mxfp4Args {
-  const uint8_t *q4, *qs, *k4, *ks, *vt4, *vts;
+// Block-scaled (MXFP4 / MXFP8) forward: element codes and E8M0 scales.
+struct MxArgs {
+  const uint8_t *qc, *qs, *kc, *ks, *vtc, *vts;
   float* o;
   float* lse;
   int B, Hq, Hkv, N, d, causal;
   float c;          // |scale| * log2(e): scores to log2 units
   float tau;
-  uint32_t qsign;   // 0x88888888 flips the sign of every E2M1 Q element (scale < 0)
+  uint32_t qsign;   // flips the sign bit of every Q element (scale < 0): 0x88888888 for E2M1
+                    // nibbles, 0x80808080 for E4M3 bytes
   unsigned long long* stats;
   void* stream;
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a);
-hipError_t launch_fwd_mxfp4(const Mxfp4Args& a);
+hipError_t launch_fwd_mxfp4(const MxArgs& a);
+hipError_t launch_fwd_mxfp8(const MxArgs& a);
 hipError_t launch_quantize_rows(const float* x, uint8_t* codes, uint8_t* scales, long long rows,
                                 int cols, void* stream);
 hipError_t launch_quantize_cols_t(const float* x, uint8_t* codes, uint8_t* scales, int batch,
                                   int rows, int cols, void* stream);
+hipError_t launch_quantize8_rows(const float* x, uint8_t* codes, uint8_t* scales, long long rows,
+                                 int cols, void* stream);
+hipError_t launch_quantize8_cols_t(const float* x, uint8_t* codes, uint8_t* scales, int batch,
+                                   int rows, int cols, void* stream);
 
 }  // namespace attn

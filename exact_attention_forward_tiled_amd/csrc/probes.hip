@@ -3,7 +3,7 @@
 // Each probe runs one fixed-size wave (or a fixed grid for the rate probes)
 // and writes raw per-lane results, so the tests can check on the host the
 // register layouts the kernels rely on: MFMA operand / accumulator lane maps,
-// the LDS transposing read, the half-wave swap, and the fp4 scaled MFMA.  All
+// the LDS transposing read, the half-wave swap, and the fp4 / fp8 scaled MFMA.  All
 // buffers are sized by the caller exactly as documented per function.
 
 #include "common.h"
@@ -218,6 +218,37 @@ __global__ void mfma_fp4_sel2_probe(const uint8_t* a, const uint8_t* b, const ui
   for (int i = 0; i < 16; ++i) c[16 * l + i] = acc[i];
 }
 
+// fp8 (E4M3) scaled MFMA.  a, b: 64 lanes x 32 bytes of E4M3 codes; sa, sb: 64 scale
+// bytes; c: 64 lanes x 16 fp32.
+__global__ void mfma_fp8_probe(const uint8_t* a, const uint8_t* b, const uint8_t* sa,
+                               const uint8_t* sb, float* c) {
+  const int l = threadIdx.x;
+  const u32x4 a0 = *(const u32x4*)(a + 32 * l), a1 = *(const u32x4*)(a + 32 * l + 16);
+  const u32x4 b0 = *(const u32x4*)(b + 32 * l), b1 = *(const u32x4*)(b + 32 * l + 16);
+  i32x8 av = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+              (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+  i32x8 bv = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+              (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  f32x16 acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, zero16(), 0, 0, 0,
+                                                                (int)sa[l], 0, (int)sb[l]);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) c[16 * l + i] = acc[i];
+}
+
+// fp8 (E4M3) convert probe.  x: 64 lanes x 2 floats; out: 64 lanes x 2 u32,
+// out[2l + sel] = v_cvt_scalef32_pk_fp8_f32 of (x[2l], x[2l+1]) with scale 1 into
+// 16-bit half `sel` of 0xFFFFFFFF.
+__global__ void cvt_fp8_probe(const float* x, uint32_t* out) {
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+  const int l = threadIdx.x;
+  const float a = x[2 * l], b = x[2 * l + 1];
+  const s16x2 ones = {-1, -1};
+  out[2 * l + 0] = __builtin_bit_cast(
+      uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(ones, a, b, 1.0f, false));
+  out[2 * l + 1] = __builtin_bit_cast(
+      uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(ones, a, b, 1.0f, true));
+}
+
 }  // namespace
 
 extern "C" {
@@ -312,6 +343,20 @@ int probe_mfma_fp4_sel2(const void* a, const void* b, const void* sa, const void
 int probe_wave_place(void* out, int blocks, void* stream) {
   if (blocks < 1) return -1;
   hipLaunchKernelGGL(wave_place_probe, dim3(blocks), dim3(512), 0, (hipStream_t)stream,
+                     (uint32_t*)out);
+  return (int)hipGetLastError();
+}
+
+int probe_mfma_fp8(const void* a, const void* b, const void* sa, const void* sb, float* c,
+                   void* stream) {
+  hipLaunchKernelGGL(mfma_fp8_probe, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                     (const uint8_t*)a, (const uint8_t*)b, (const uint8_t*)sa,
+                     (const uint8_t*)sb, c);
+  return (int)hipGetLastError();
+}
+
+int probe_cvt_fp8(const void* x, void* out, void* stream) {
+  hipLaunchKernelGGL(cvt_fp8_probe, dim3(1), dim3(64), 0, (hipStream_t)stream, (const float*)x,
                      (uint32_t*)out);
   return (int)hipGetLastError();
 }

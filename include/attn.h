@@ -157,6 +157,51 @@ int attn_quantize_mxfp4_rows(const float* x, uint8_t* codes, uint8_t* scales,
 int attn_quantize_mxfp4_cols_t(const float* x, uint8_t* codes, uint8_t* scales,
                                int batch, int rows, int cols, void* stream);
 
+/*
+ * MXFP8 forward ("Hardware-Aware FP4 FlashAttention-4", section "Resultados",
+ * sets its FP4 path beside an FP8 one; section "2. Causal Backward Cuantizado"
+ * keeps P and V in FP8; the aigc.bar page, section "从V1到V4", credits
+ * FlashAttention-3 with FP8).  Operands are OCP MXFP8: E4M3 elements, one E8M0
+ * scale per 32.  QK^T and PV run on the scaled FP8 MFMA; the softmax weights,
+ * taken relative to an integer running maximum m, are rounded to E4M3 with one
+ * power-of-two scale per 32 keys, E = floor(block max of t - m) - 7 with
+ * t = scale * q.k * log2(e), and the denominator is summed from those same
+ * rounded weights.
+ *   q8, k8   E4M3 codes [B, H*, N, d]  (one byte per element)
+ *   qs, ks   E8M0 scales [B, H*, N, d/32] (block of 32 along d)
+ *   vt8      E4M3 codes of V transposed [B, Hkv, d, N] (block of 32 along keys)
+ *   vts      E8M0 scales [B, Hkv, d, N/32]
+ *   o fp32 [B, Hq, N, d], lse fp32 [B, Hq, N]  (natural log)
+ *   d = 128; N a multiple of 32 (else ATTN_EUNSUPPORTED); codes must not hold the NaN
+ *   patterns 0x7F / 0xFF (the quantisers below never write them).  Options: tau and
+ *   stats as for the bf16 forward; window, ALiBi, soft-capping and documents are
+ *   ATTN_EUNSUPPORTED.
+ */
+int attn_fwd_mxfp8(const uint8_t* q8, const uint8_t* qs, const uint8_t* k8, const uint8_t* ks,
+                   const uint8_t* vt8, const uint8_t* vts, float* o, float* lse,
+                   int B, int Hq, int Hkv, int N, int d, int causal, float scale);
+
+int attn_fwd_mxfp8_ex(const uint8_t* q8, const uint8_t* qs, const uint8_t* k8, const uint8_t* ks,
+                      const uint8_t* vt8, const uint8_t* vts, float* o, float* lse,
+                      int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                      const attn_opts* opts, void* stream);
+
+/*
+ * MXFP8 quantisation of fp32 inputs (OCP MX v1.0 rule for E4M3: shared exponent
+ * floor(log2(amax)) - 8 per block of 32, clamped to [-127, 127]; elements rounded to
+ * the nearest E4M3 value with ties to even, saturating at +-448; an all-zero block gets
+ * exponent 0; a value that rounds to 0 is stored as +0).
+ *
+ * attn_quantize_mxfp8_rows: x fp32 [rows, cols] -> codes [rows, cols], scales [rows, cols/32].
+ * attn_quantize_mxfp8_cols_t: x fp32 [batch, rows, cols] -> codes [batch, cols, rows],
+ *   scales [batch, cols, rows/32] (blocks along rows, output transposed; used for V).
+ * cols (resp. rows) must be a positive multiple of 32; codes 16-byte aligned.
+ */
+int attn_quantize_mxfp8_rows(const float* x, uint8_t* codes, uint8_t* scales,
+                             long long rows, int cols, void* stream);
+int attn_quantize_mxfp8_cols_t(const float* x, uint8_t* codes, uint8_t* scales,
+                               int batch, int rows, int cols, void* stream);
+
 /* Static description of a status code; never NULL. */
 const char* attn_strerror(int status);
 

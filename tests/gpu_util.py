@@ -40,3 +40,30 @@ BF16_O_RELRMS = 5e-3
 BF16_LSE_ABS = 1e-3
 # tolerance for the MXFP4 Direct-P path against the emulating oracle
 MXFP4_O_RELRMS = 0.1
+# tolerances for the MXFP8 path against the emulating oracle (no stated figure).  Both sides
+# apply the same quantisation.  The E4M3 form of the scaled MFMA does not round its
+# 64-product sums once in fp32: the layout probe measures errors up to 2^-11.4 of the
+# largest single product on random codes, and on attention inputs the scores move by up
+# to 2^-9.1 of scale * (sum over the two 64-wide d chunks of the largest |q~_d k~_d|).
+# That shift moves the LSE directly, and flips a weight's E4M3 code where a score lies
+# near a rounding boundary (relRMS(O) measured 5e-4 .. 1.5e-3).  Gates: relRMS(O) <= 5e-3,
+# which FP8's own ~2e-2 error against exact attention would fail, and
+# |dLSE| <= 1e-3 + 2^-8 * scale * that sum (twice the worst shift measured).
+MXFP8_O_RELRMS = 5e-3
+MXFP8_LSE_ABS = 1e-3
+MXFP8_MFMA_REL = 2.0 ** -8
+
+
+def mxfp8_lse_tol(qt, kt, scale):
+    """LSE gate of the MXFP8 path for dequantised operands qt [B,Hq,N,d], kt [B,Hkv,N,d]."""
+    group = qt.shape[1] // kt.shape[1]
+    qa = np.abs(qt)
+    ka = np.repeat(np.abs(kt), group, axis=1)
+    worst = 0.0
+    for c0 in range(0, qt.shape[-1], 64):
+        # the largest |q_id k_jd| of the chunk, per (b, h): max over d of
+        # (max_i |q_id|) * (max_j |k_jd|)
+        mq = qa[..., c0:c0 + 64].max(axis=-2)
+        mk = ka[..., c0:c0 + 64].max(axis=-2)
+        worst = worst + (mq * mk).max(axis=-1)
+    return MXFP8_LSE_ABS + MXFP8_MFMA_REL * abs(scale) * float(np.max(worst))

@@ -119,6 +119,19 @@ def test_mxfp4_validation(fa):
     assert fa.attn_quantize_mxfp4_cols_t(FAKE, FAKE, FAKE, 1, 40, 8) == -1
 
 
+def test_mxfp8_validation(fa):
+    base = [FAKE] * 8
+    assert fa.attn_fwd_mxfp8(*base, 1, 2, 2, 64, 64, 0, 0.1) == -2      # d must be 128
+    assert fa.attn_fwd_mxfp8(*base, 1, 2, 2, 48, 128, 0, 0.1) == -2     # N % 32
+    assert fa.attn_fwd_mxfp8(*base, 1, 3, 2, 64, 128, 0, 0.1) == -1     # Hq % Hkv
+    assert fa.attn_fwd_mxfp8(*base, 1, 2, 2, 64, 128, 2, 0.1) == -1     # causal in {0, 1}
+    assert fa.attn_fwd_mxfp8(0, *base[1:], 1, 2, 2, 64, 128, 0, 0.1) == -1
+    assert fa.attn_fwd_mxfp8_ex(*base, 1, 2, 2, 64, 128, 0, 0.1, fa.make_opts(window=16),
+                                None) == -2
+    assert fa.attn_quantize_mxfp8_rows(FAKE, FAKE, FAKE, 4, 48) == -1
+    assert fa.attn_quantize_mxfp8_cols_t(FAKE, FAKE, FAKE, 1, 40, 8) == -1
+
+
 def test_strerror(fa):
     from exact_attention_forward_tiled_amd.binding import lib
     assert lib.attn_strerror(0) == b"success"

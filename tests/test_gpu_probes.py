@@ -19,6 +19,18 @@ CDNA3/CDNA4 operand layouts:
 * v_cvt_scalef32_pk_fp4_f32 writes RNE(x / scale) onto the E2M1 grid (ties to
   the even code, saturating at +-6) into the selected byte, keeping the others;
   v_cvt_scalef32_pk_f32_fp4 decodes a selected byte times the scale.
+* the same MFMA with fp8 (E4M3) operands: lane l holds row (A) or column (B)
+  l % 32 in 32 bytes (8 registers); bytes 0-15 belong to k-block 0 (k 0..31)
+  and bytes 16-31 to k-block 1 (k 32..63), each k-block being the 16-byte
+  halves of lanes l % 32 and l % 32 + 32; the E8M0 byte of lane
+  (l % 32) + 32*b scales k-block b of that row or column.  (The order of the
+  elements inside a k-block is the same for A and B, so it does not show in
+  the product; the model below takes byte i of lane half h as k = 16h + i.)
+  The product of E4M3 operands is not rounded once in fp32: its error reaches
+  about 2^-11 of the largest single product.
+* v_cvt_scalef32_pk_fp8_f32 with scale 1 rounds to the nearest E4M3 value
+  (ties to even, subnormals kept) and writes the two codes into the selected
+  16-bit half, keeping the other.
 """
 
 import ctypes
@@ -44,6 +56,7 @@ def lib():
                        "probe_mfma_fp4": [P, P, P, P, P, P],
                        "probe_mfma_fp4_sel2": [P, P, P, P, P, P],
                        "probe_cvt_fp4": [P, P, P, P], "probe_dec_fp4": [P, P, P, P],
+                       "probe_mfma_fp8": [P, P, P, P, P, P], "probe_cvt_fp8": [P, P, P],
                        "probe_wave_place": [P, ctypes.c_int, P]}.items():
         fn = getattr(lib, name)
         fn.restype = I
@@ -255,3 +268,73 @@ def test_wave_placement_pairs_waves_on_simds(lib):
     assert np.all(cu == cu[:, :1]), "all waves of a workgroup on one CU"
     assert np.all(simd[:, :4] == simd[:, 4:]), "wave w and w + 4 share a SIMD"
     assert np.all(np.sort(simd[:, :4], axis=1) == np.arange(4)), "waves 0-3 on distinct SIMDs"
+
+
+def _e4m3_decode(codes):
+    """E4M3 byte -> value through torch's float8_e4m3fn (an independent decoder)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8))
+    return t.view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+
+
+def test_mfma_fp8_layout_and_scales(lib):
+    import torch
+    rng = np.random.default_rng(8)
+    ca = rng.integers(0, 256, size=(64, 32)).astype(np.uint8)
+    cb = rng.integers(0, 256, size=(64, 32)).astype(np.uint8)
+    ca[(ca & 0x7F) == 0x7F] = 0x12          # no NaN codes
+    cb[(cb & 0x7F) == 0x7F] = 0x34
+    sa = rng.integers(120, 135, size=64).astype(np.uint8)
+    sb = rng.integers(120, 135, size=64).astype(np.uint8)
+    va, vb = _e4m3_decode(ca), _e4m3_decode(cb)
+
+    def k_of(l, i):
+        h = l // 32
+        return 16 * h + i if i < 16 else 32 + 16 * h + (i - 16)
+
+    A = np.zeros((32, 64))
+    B = np.zeros((64, 32))
+    for l in range(64):
+        for i in range(32):
+            k = k_of(l, i)
+            blk = k // 32          # the scale of k-block blk comes from lane (l % 32) + 32*blk
+            A[l % 32, k] = va[l, i] * 2.0 ** (int(sa[l % 32 + 32 * blk]) - 127)
+            B[k, l % 32] = vb[l, i] * 2.0 ** (int(sb[l % 32 + 32 * blk]) - 127)
+    C = A @ B
+    want = np.array([[C[8 * (r // 4) + 4 * (l // 32) + r % 4, l % 32] for r in range(16)]
+                     for l in range(64)])
+    # bound of the hardware's accumulation error: 2^-10 of the largest product
+    pmax = np.array([[np.max(np.abs(A[8 * (r // 4) + 4 * (l // 32) + r % 4] *
+                                    B[:, l % 32])) for r in range(16)] for l in range(64)])
+    bufs = [_dev(ca), _dev(cb), _dev(sa), _dev(sb)]
+    c = torch.zeros((64, 16), dtype=torch.float32, device="cuda")
+    log("probe mfma_fp8")
+    assert lib.probe_mfma_fp8(*[t.data_ptr() for t in bufs], c.data_ptr(), None) == 0
+    _sync()
+    got = c.cpu().numpy().astype(np.float64)
+    # a scale misapplied to a k-block (e.g. each lane's own byte for all its 32 elements)
+    # is off by far more than this on these inputs
+    assert np.all(np.abs(got - want) <= 2.0 ** -10 * pmax)
+
+
+def test_fp8_convert_rounding_and_half_select(lib):
+    import torch
+    rng = np.random.default_rng(9)
+    mags = _e4m3_decode(np.arange(127))
+    mids = ((mags[:-1] + mags[1:]) / 2)[rng.permutation(126)[:40]]     # exact ties
+    x = np.concatenate([mags[rng.integers(0, 127, 24)], mids,
+                        np.exp2(rng.uniform(-12, 8.7, 40)), rng.uniform(0, 300, 24)])
+    x = x.astype(np.float32)
+    assert x.shape == (128,)             # the probe reads 64 lanes x 2 floats
+    x[::3] = -x[::3]
+    bufs = [_dev(x)]
+    out = torch.zeros(128, dtype=torch.int32, device="cuda")
+    log("probe cvt_fp8")
+    assert lib.probe_cvt_fp8(bufs[0].data_ptr(), out.data_ptr(), None) == 0
+    _sync()
+    got = out.cpu().numpy().view(np.uint32).reshape(64, 2)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy().astype(np.uint32)
+    for l in range(64):
+        pair = ref[2 * l] | (ref[2 * l + 1] << 8)
+        assert got[l, 0] == (0xFFFF0000 | pair), (l, x[2 * l], x[2 * l + 1], hex(got[l, 0]))
+        assert got[l, 1] == (0x0000FFFF | (pair << 16)), (l, hex(got[l, 1]))
