@@ -40,12 +40,16 @@ sys.path.insert(0, ROOT)
 METRIC = "attn fwd TFLOP/s (4·B·H·N²·d, causal halved) and % of MI355X MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6      # dense bf16 MFMA, 256 CUs x 2.4 GHz x 4096 flop/clk
 PEAK_FP4_TFLOPS = 10066.3      # dense MXFP4 MFMA, 256 CUs x 2.4 GHz x 16384 flop/clk
+PEAK_FP8_TFLOPS = 5033.2       # dense FP8 MFMA, 256 CUs x 2.4 GHz x 8192 flop/clk
+PEAKS = {"bf16": PEAK_BF16_TFLOPS, "mxfp4": PEAK_FP4_TFLOPS, "mxfp8": PEAK_FP8_TFLOPS}
 PEAK_CLOCK_GHZ = 2.4           # the clock the published peaks assume
 KERNEL_SOURCES = {
     "bf16": ["exact_attention_forward_tiled_amd/csrc/attn_fwd_bf16.hip",
              "exact_attention_forward_tiled_amd/csrc/common.h",
              "exact_attention_forward_tiled_amd/csrc/exp2_poly.h"],
     "mxfp4": ["exact_attention_forward_tiled_amd/csrc/attn_mxfp4.hip",
+              "exact_attention_forward_tiled_amd/csrc/common.h"],
+    "mxfp8": ["exact_attention_forward_tiled_amd/csrc/attn_mxfp8.hip",
               "exact_attention_forward_tiled_amd/csrc/common.h"],
 }
 
@@ -131,6 +135,32 @@ class Mxfp4Workload:
                           out=(self.o, self.lse))
 
 
+class Mxfp8Workload:
+    """MXFP8 workload: fp32 draws quantised on the GPU once (untimed), then the forward on
+    the resident codes and scales."""
+
+    def __init__(self, w, tau):
+        import numpy as np
+        import torch
+        import exact_attention_forward_tiled_amd as fa
+        self.w = w
+        q, k, v = (torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in w.make())
+        self.q8, self.qs = fa.quantize_mxfp8_rows(q)
+        self.k8, self.ks = fa.quantize_mxfp8_rows(k)
+        self.vt8, self.vts = fa.quantize_mxfp8_cols_t(v)
+        torch.cuda.synchronize()
+        del q, k, v
+        self.o = torch.empty((w.B, w.Hq, w.N, w.d), dtype=torch.float32, device="cuda")
+        self.lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device="cuda")
+        self.fa = fa
+        self.tau = tau
+
+    def launch(self, stats=None):
+        self.fa.fwd_mxfp8(self.q8, self.qs, self.k8, self.ks, self.vt8, self.vts,
+                          causal=self.w.causal, scale=self.w.scale, tau=self.tau, stats=stats,
+                          out=(self.o, self.lse))
+
+
 def visible_pairs(N, causal, window, doc_offsets=None):
     """(query, key) pairs a sliding window of width `window` and/or packed documents show
     (exact count)."""
@@ -147,7 +177,11 @@ def visible_pairs(N, causal, window, doc_offsets=None):
 
 
 def make_workload(w, exp_mode, tau, poly_frac=None):
-    return Workload(w, exp_mode, tau, poly_frac) if w.fmt == "bf16" else Mxfp4Workload(w, tau)
+    if w.fmt == "mxfp4":
+        return Mxfp4Workload(w, tau)
+    if w.fmt == "mxfp8":
+        return Mxfp8Workload(w, tau)
+    return Workload(w, exp_mode, tau, poly_frac)
 
 
 def time_workload(wl, steps, warmup, warmup_seconds):
@@ -257,7 +291,7 @@ def rates():
 
 def cpu_baseline(w, budget_s=10.0):
     """The float64 oracle, as it stands, on whole (batch, head) slices of the same workload
-    (the MXFP4 workload runs the Direct-P emulation on the quantised operands)."""
+    (the block-scaled workloads run the oracle's emulation of their quantisation)."""
     import oracle
     import synth
     from threadpoolctl import threadpool_info
@@ -272,14 +306,15 @@ def cpu_baseline(w, budget_s=10.0):
         import numpy as np
         q, k, v = w.make()
         group = w.Hq // w.Hkv
+        mod, rows_fn = ((oracle.mx, oracle.mx.directp_rows) if w.fmt == "mxfp4"
+                        else (oracle.mxfp8, oracle.mxfp8.fp8p_rows))
 
         def one(b, h):
-            t = oracle.mx.quantize_inputs(q[b:b + 1, h:h + 1], k[b:b + 1, h // group:h // group + 1],
-                                          v[b:b + 1, h // group:h // group + 1])
+            t = mod.quantize_inputs(q[b:b + 1, h:h + 1], k[b:b + 1, h // group:h // group + 1],
+                                    v[b:b + 1, h // group:h // group + 1])
             for r0 in range(0, w.N, 256):
                 rows = np.arange(r0, min(w.N, r0 + 256))
-                oracle.mx.directp_rows(t["q"][0, 0, rows], t["k"][0, 0], t["v"][0, 0], rows,
-                                       w.causal, w.scale)
+                rows_fn(t["q"][0, 0, rows], t["k"][0, 0], t["v"][0, 0], rows, w.causal, w.scale)
     done, t0 = 0, time.perf_counter()
     while time.perf_counter() - t0 < budget_s:
         b, h = heads[done % len(heads)]
@@ -371,12 +406,12 @@ def main():
              "skip_ratio": skip, "clock_ghz": ghz,
              "pct_of_bf16_peak_at_clock": (100.0 * t["tflops"] / (PEAK_BF16_TFLOPS * ghz / PEAK_CLOCK_GHZ)
                                            if ghz else None),
-             "exp_mode": args.exp if w.fmt == "bf16" else "directp",
+             "exp_mode": {"bf16": args.exp, "mxfp4": "directp", "mxfp8": "hw"}[w.fmt],
              "poly_frac": args.poly_frac if args.exp == "mix" else None,
              "tau": args.tau, "kernel_hash": kernel_hash(w.fmt), "device": props.name,
              "compute_units": props.multi_processor_count, "workloads": {}}
     if w.fmt != "bf16":
-        extra["pct_of_fp4_peak"] = 100.0 * t["tflops"] / PEAK_FP4_TFLOPS
+        extra[f"pct_of_{w.fmt[2:]}_peak"] = 100.0 * t["tflops"] / PEAKS[w.fmt]
     if args.compare_exp and w.fmt == "bf16":
         for other, frac in (("hw", None), ("poly", None), ("mix", 0.25), ("mix", 0.5), ("mix", 0.75)):
             if other == args.exp and (other != "mix" or frac == args.poly_frac):
@@ -406,8 +441,8 @@ def main():
             "pct_of_bf16_peak": round(100.0 * tx["tflops"] / PEAK_BF16_TFLOPS, 2),
             "skip_ratio": sx, "clock_ghz": gx}
         if wx.fmt != "bf16":
-            extra["workloads"][wx.name]["pct_of_fp4_peak"] = round(
-                100.0 * tx["tflops"] / PEAK_FP4_TFLOPS, 2)
+            extra["workloads"][wx.name][f"pct_of_{wx.fmt[2:]}_peak"] = round(
+                100.0 * tx["tflops"] / PEAKS[wx.fmt], 2)
 
     if args.window and w.fmt == "bf16":
         log(f"timing {w.name} with window {args.window}")
@@ -443,7 +478,7 @@ def main():
         log("timing the float64 oracle on the host")
         cpu = cpu_baseline(w)
 
-    peak = PEAK_BF16_TFLOPS if w.fmt == "bf16" else PEAK_FP4_TFLOPS
+    peak = PEAKS[w.fmt]
     line = {
         "metric": METRIC,
         "value": round(t["tflops"], 3),
@@ -455,7 +490,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.fmt == "bf16" else "mxfp4",
+        "dtype": w.fmt,
         "data": "synthetic",
         "config": dict(w.describe()),
         "roofline": {"bound": "mfma", "achieved": round(kernel_tf, 3), "peak": peak,

@@ -67,7 +67,7 @@ def main():
     import bench
     import synth
     w = synth.workload(args.config)
-    kfilter = args.kernel_filter or ("fwd_bf16_kernel" if w.fmt == "bf16" else "fwd_mxfp4_kernel")
+    kfilter = args.kernel_filter or f"fwd_{w.fmt}_kernel"
 
     copy_bytes = args.copy_mib * (1 << 20)
     cf = statistics.median(counter_values(args.copy_fetch, "FETCH_SIZE", args.copy_filter))
@@ -80,10 +80,11 @@ def main():
     write_b = aw * 1024.0 * f_write
 
     # algorithmic bytes: one read of the operands and one write of O, LSE (fp32).
-    # bf16: Q, K, V at 2 B per element.  mxfp4: E2M1 codes (0.5 B) plus one E8M0 scale
-    # byte per 32 elements, for Q, K and the transposed V.
+    # bf16: Q, K, V at 2 B per element.  mxfp4 / mxfp8: E2M1 codes (0.5 B) or E4M3 codes
+    # (1 B) plus one E8M0 scale byte per 32 elements, for Q, K and the transposed V.
     elems = w.B * w.Hq * w.N * w.d + 2 * w.B * w.Hkv * w.N * w.d
-    alg_in = 2 * elems if w.fmt == "bf16" else elems // 2 + elems // 32
+    alg_in = {"bf16": 2 * elems, "mxfp4": elems // 2 + elems // 32,
+              "mxfp8": elems + elems // 32}[w.fmt]
     alg_out = 4 * (w.B * w.Hq * w.N * w.d + w.B * w.Hq * w.N)
 
     rec = {"kernel_hash": bench.kernel_hash(w.fmt), "kernel_filter": kfilter,

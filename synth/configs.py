@@ -23,7 +23,7 @@ class Workload:
     N: int
     d: int
     causal: bool
-    fmt: str            # "bf16" or "mxfp4"
+    fmt: str            # "bf16", "mxfp4" or "mxfp8"
     sigma_qk: float = 1.0
     sigma_v: float = 1.0
 
@@ -51,7 +51,8 @@ class Workload:
                 "N": self.N, "d": self.d, "causal": self.causal, "format": self.fmt}
 
     def make(self):
-        """Returns (q, k, v): uint16 bf16 bits for bf16 workloads, fp32 for mxfp4."""
+        """Returns (q, k, v): uint16 bf16 bits for bf16 workloads, fp32 for the block-scaled
+        formats (quantised by the consumer)."""
         sq, sk, sv = self.seeds()
         shq, shk, shv = self.shapes()
         if self.fmt == "bf16":
@@ -71,6 +72,10 @@ CONFIGS = {
                 "bf16", sigma_qk=3.0),
     5: Workload(5, "noncausal_mxfp4_directp_B1_H24_N16384_d128", 1, 24, 24, 16384, 128, False,
                 "mxfp4"),
+    # MXFP8 forward on the shapes of workloads 5 and 3 (FP8 path; not one of the five above)
+    6: Workload(6, "noncausal_mxfp8_B1_H24_N16384_d128", 1, 24, 24, 16384, 128, False, "mxfp8"),
+    7: Workload(7, "causal_gqa_mxfp8_B1_Hq32_Hkv8_N8192_d128", 1, 32, 8, 8192, 128, True,
+                "mxfp8"),
 }
 
 

@@ -183,29 +183,36 @@ def test_fp8_gqa_equals_repeated_heads():
         assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
-def test_fp8_workload_sampled_rows():
-    """B1 H24 N16384 d128 non-causal (the MXFP4 workload's shape, in MXFP8): sampled rows of
-    several heads against the emulation, and the cosine against exact attention on the
-    unquantised inputs (the explainer page quotes about 0.990 for its FP8 path; context)."""
-    w = synth.workload(5)
+@pytest.mark.parametrize("idx", [6, 7])
+def test_fp8_workload_sampled_rows(idx):
+    """The MXFP8 bench workloads at full size (B1 H24 N16384 non-causal; causal GQA B1 Hq32
+    Hkv8 N8192), in the bench's launch configuration: sampled rows of several heads against
+    the emulation, and the cosine against exact attention on the unquantised inputs (the
+    explainer page quotes about 0.990 for its FP8 path; context only)."""
+    w = synth.workload(idx)
     q, k, v = w.make()
-    log(f"mxfp8 on workload shape {w.name}")
+    log(f"mxfp8 workload {w.name}")
     o, lse = _run(q, k, v, w.causal, w.scale)
     assert not np.isnan(o).any() and not np.isnan(lse).any()
-    rng = np.random.default_rng(6)
+    rng = np.random.default_rng(idx)
+    group = w.Hq // w.Hkv
     heads = [0, w.Hq - 1, int(rng.integers(w.Hq))]
-    rows = np.unique(np.concatenate([[0, 1, 31, 32, 63, 64, w.N - 1], rng.integers(0, w.N, 29)]))
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 63, 64, 255, 256, w.N - 1],
+                                     rng.integers(0, w.N, 27)]))
     got, ref, exact = [], [], []
     for h in heads:
-        t = m8.quantize_inputs(q[:, h:h + 1, rows], k[:, h:h + 1], v[:, h:h + 1])
+        g = h // group
+        t = m8.quantize_inputs(q[:, h:h + 1, rows], k[:, g:g + 1], v[:, g:g + 1])
         tol = mxfp8_lse_tol(t["q"], t["k"], w.scale)
-        ro, rl, _ = m8.fp8p_rows(t["q"][0, 0], t["k"][0, 0], t["v"][0, 0], rows, False, w.scale)
+        ro, rl, _ = m8.fp8p_rows(t["q"][0, 0], t["k"][0, 0], t["v"][0, 0], rows, w.causal,
+                                 w.scale)
         got.append(o[0, h, rows])
         ref.append(ro)
-        eo, _ = oracle.attention(q[:, h:h + 1, rows].astype(np.float64),
-                                 k[:, h:h + 1].astype(np.float64),
-                                 v[:, h:h + 1].astype(np.float64), False, w.scale)
-        exact.append(eo[0, 0])
+        eo, _ = oracle.attention_rows(q[:, h:h + 1].astype(np.float64),
+                                      k[:, g:g + 1].astype(np.float64),
+                                      v[:, g:g + 1].astype(np.float64), w.causal, w.scale,
+                                      0, 0, rows)
+        exact.append(eo)
         e = float(np.max(np.abs(lse[0, h, rows] - rl)))
         log(f"  head {h}: max|dLSE|={e:.3e} (gate {tol:.3e})")
         assert e <= tol
