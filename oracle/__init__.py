@@ -22,14 +22,19 @@ check), written from the definitions so that a reader can check it by eye:
   step-by-step emulation of the FP8 forward (P rounded to E4M3 with one
   power-of-two scale per 32 keys; the same page's "Resultados" compares an FP8
   path, and its section "2. Causal Backward Cuantizado" keeps P and V in FP8).
+* ``backward`` -- the gradients dQ, dK, dV of the exact forward, with P rebuilt
+  from the saved log-sum-exp ("Hardware-Aware FP4 FlashAttention-4", section
+  "2. Causal Backward Cuantizado": the forward saves the LSE and the backward
+  rebuilds the probabilities from it).
 
 Parity status: every function is pinned by tests under ``tests/`` against
 brute force, a library routine (torch's CPU attention in float64), closed
 forms and invariants; see the test modules ``test_oracle_exact.py``,
-``test_oracle_mx.py`` and ``test_oracle_mxfp8.py``.
+``test_oracle_mx.py``, ``test_oracle_mxfp8.py`` and ``test_oracle_backward.py``.
 """
 
 from .exact import attention, attention_brute, attention_head, attention_rows, kv_head
-from . import mx, mxfp8
+from . import backward, mx, mxfp8
 
-__all__ = ["attention", "attention_brute", "attention_head", "attention_rows", "kv_head", "mx", "mxfp8"]
+__all__ = ["attention", "attention_brute", "attention_head", "attention_rows", "kv_head", "backward", "mx",
+           "mxfp8"]

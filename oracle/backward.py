@@ -1,0 +1,90 @@
+"""Exact attention backward in float64: the gradients of the forward's plain definition.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+What the pages give.  The series keeps memory linear by not storing the N x N
+matrix and recomputing it in the backward pass ("FlashAttention-4发布：原生支持
+Blackwell…", section "从V1到V4", FlashAttention (2022) entry: tiling plus
+recomputation); "Hardware-Aware FP4 FlashAttention-4", section "2. Causal
+Backward Cuantizado", saves the log-sum-exp in the forward so that the backward
+rebuilds the probabilities from it.  The pages print no formula, so this is the
+chain rule applied to the forward's definition (oracle.exact), with P rebuilt
+from the saved LSE:
+
+    s_ij   = scale * q_i . k_j            (-inf where masked)
+    P_ij   = exp(s_ij - LSE_i)            the forward's probabilities
+    dV_j   = sum_i P_ij dO_i
+    dP_ij  = dO_i . v_j
+    D_i    = sum_j P_ij dP_ij = dO_i . O_i
+    dS_ij  = P_ij (dP_ij - D_i)           gradient of the loss w.r.t. s_ij
+    dQ_i   = scale * sum_j dS_ij k_j
+    dK_j   = scale * sum_i dS_ij q_i
+
+With grouped-query attention the key/value head hk serves query heads
+hk*g .. hk*g + g - 1 (g = Hq / Hkv), so dK and dV of hk are the sums of those
+query heads' contributions.  A row whose keys are all masked contributes
+nothing.  Inputs: float64 q [B, Hq, N, d], k, v [B, Hkv, N, d], dO like q; O
+and LSE are the forward's (recomputed here from the definition unless given).
+"""
+
+import numpy as np
+
+from .exact import apply_mask, attention, scores
+
+
+def backward_head(q, k, v, do, causal, scale, o=None, lse=None):
+    """Gradients for one (batch, query head) slice: q, do [N, d]; k, v [Nk, d].
+
+    Returns (dq [N, d], dk [Nk, d], dv [Nk, d]) of that query head alone.
+    """
+    n = q.shape[0]
+    rows = np.arange(n)
+    s = apply_mask(scores(q, k, scale), rows, causal)
+    if lse is None or o is None:
+        m = s.max(axis=1)
+        m_safe = np.where(np.isfinite(m), m, 0.0)
+        e = np.exp(s - m_safe[:, None])
+        l = e.sum(axis=1)
+        live = l > 0
+        lse = np.where(live, m_safe + np.log(np.where(live, l, 1.0)), -np.inf)
+        o = np.where(live[:, None], (e @ v) / np.where(live, l, 1.0)[:, None], 0.0)
+    live = np.isfinite(lse)
+    p = np.where(live[:, None], np.exp(s - np.where(live, lse, 0.0)[:, None]), 0.0)
+    dv = p.T @ do
+    dp = do @ v.T
+    delta = np.sum(do * o, axis=1)
+    ds = p * (dp - delta[:, None])
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    return dq, dk, dv
+
+
+def attention_backward(q, k, v, do, causal, scale, o=None, lse=None):
+    """Gradients over [B, H, N, d] operands: returns (dq, dk, dv) in float64.
+
+    o and lse, when given, are the forward's outputs [B, Hq, N, d] and [B, Hq, N];
+    otherwise they are recomputed from the definition.
+    """
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    g = Hq // Hkv
+    if o is None or lse is None:
+        o, lse = attention(q, k, v, causal, scale)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // g
+            gq, gk, gv = backward_head(q[b, h], k[b, hk], v[b, hk], do[b, h], causal, scale,
+                                       o[b, h], lse[b, h])
+            dq[b, h] = gq
+            dk[b, hk] += gk
+            dv[b, hk] += gv
+    return dq, dk, dv
+
+
+def delta(o, do):
+    """D_i = dO_i . O_i per row: [B, Hq, N]."""
+    return np.sum(np.asarray(o, dtype=np.float64) * np.asarray(do, dtype=np.float64), axis=-1)

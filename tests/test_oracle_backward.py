@@ -1,0 +1,142 @@
+"""Pins for the float64 attention backward in oracle.backward."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import backward as bw
+
+
+def _case(seed, B, Hq, Hkv, N, d, sigma=1.0):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, N, d)) * sigma
+    k = rng.standard_normal((B, Hkv, N, d)) * sigma
+    v = rng.standard_normal((B, Hkv, N, d))
+    do = rng.standard_normal((B, Hq, N, d))
+    return q, k, v, do
+
+
+def _torch_grads(q, k, v, do, causal, scale):
+    """Autograd of a plain float64 softmax attention (GQA by repeating K/V heads)."""
+    g = q.shape[1] // k.shape[1]
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    kk = tk.repeat_interleave(g, dim=1)
+    vv = tv.repeat_interleave(g, dim=1)
+    s = scale * torch.matmul(tq, kk.transpose(-1, -2).contiguous())
+    if causal:
+        n = q.shape[2]
+        mask = torch.ones(n, n, dtype=torch.bool).tril()
+        s = s.masked_fill(~mask, float("-inf"))
+    o = torch.matmul(torch.softmax(s, dim=-1), vv)
+    o.backward(torch.tensor(do, dtype=torch.float64))
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 2, 9, 4), (2, 4, 2, 16, 8), (1, 6, 2, 33, 16),
+                                   (1, 1, 1, 1, 3)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_matches_torch_autograd(shape, causal):
+    B, Hq, Hkv, N, d = shape
+    q, k, v, do = _case(sum(shape), B, Hq, Hkv, N, d)
+    scale = 0.7
+    got = bw.attention_backward(q, k, v, do, causal, scale)
+    ref = _torch_grads(q, k, v, do, causal, scale)
+    for a, b in zip(got, ref):
+        assert np.allclose(a, b, atol=1e-12, rtol=1e-10)
+
+
+def test_finite_differences():
+    """Central differences of L = sum(O * dO) against the gradients, element by element on a
+    tiny causal GQA case (the forward is the pinned oracle.exact)."""
+    q, k, v, do = _case(7, 1, 2, 1, 5, 3)
+    scale = 0.9
+    dq, dk, dv = bw.attention_backward(q, k, v, do, True, scale)
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.attention(qq, kk, vv, True, scale)
+        return float(np.sum(o * do))
+
+    h = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = [xp if y is x else y for y in (q, k, v)]
+            args_m = [xm if y is x else y for y in (q, k, v)]
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            assert abs(fd - g[idx]) < 1e-7, (idx, fd, g[idx])
+
+
+def test_shift_and_sum_invariants():
+    """Closed forms: adding a constant vector to every key leaves the loss unchanged, so the dK
+    rows of each kv head sum to 0 (also under the causal mask, every row keeps its keys);
+    the softmax rows sum to 1, so the dV rows of a kv head sum to the dO rows of its query
+    heads."""
+    q, k, v, do = _case(8, 2, 4, 2, 24, 8)
+    for causal in (False, True):
+        dq, dk, dv = bw.attention_backward(q, k, v, do, causal, 0.5)
+        assert np.allclose(dk.sum(axis=2), 0.0, atol=1e-12)
+        want = do.reshape(2, 2, 2, 24, 8).sum(axis=(2, 3))
+        assert np.allclose(dv.sum(axis=2), want, atol=1e-12)
+
+
+def test_single_key_row_gets_no_q_gradient():
+    """Causal row 0 sees one key: its output is v_0 whatever q_0 is, so dQ_0 = 0."""
+    q, k, v, do = _case(9, 1, 2, 2, 12, 4)
+    dq, _, _ = bw.attention_backward(q, k, v, do, True, 0.8)
+    assert np.allclose(dq[:, :, 0], 0.0, atol=1e-14)
+
+
+def test_given_forward_outputs_equal_recomputed():
+    q, k, v, do = _case(10, 1, 2, 2, 20, 6)
+    o, lse = oracle.attention(q, k, v, True, 0.4)
+    a = bw.attention_backward(q, k, v, do, True, 0.4, o=o, lse=lse)
+    b = bw.attention_backward(q, k, v, do, True, 0.4)
+    for x, y in zip(a, b):
+        assert np.allclose(x, y, atol=1e-14)
+    assert np.allclose(bw.delta(o, do), np.sum(o * do, axis=-1))
+
+
+@pytest.mark.parametrize("bad", ["no_delta", "no_scale_dk", "gqa_last_head", "p_unnormalised"])
+def test_planted_mistakes_are_caught(bad, monkeypatch):
+    orig = bw.backward_head
+
+    def mutated(q, k, v, do, causal, scale, o=None, lse=None):
+        dq, dk, dv = orig(q, k, v, do, causal, scale, o, lse)
+        if bad == "no_delta":
+            rows = np.arange(q.shape[0])
+            s = oracle.exact.apply_mask(scale * q @ k.T, rows, causal)
+            p = np.exp(s - lse[:, None])
+            ds = p * (do @ v.T)
+            return scale * ds @ k, scale * ds.T @ q, dv
+        if bad == "no_scale_dk":
+            return dq, dk / scale, dv
+        if bad == "p_unnormalised":
+            return dq, dk, dv * 1.5
+        return dq, dk, dv
+
+    monkeypatch.setattr(bw, "backward_head", mutated)
+    if bad == "gqa_last_head":
+        orig_all = bw.attention_backward
+
+        def keep_last(q, k, v, do, causal, scale, o=None, lse=None):
+            dq, dk, dv = orig_all(q, k, v, do, causal, scale, o, lse)
+            g = q.shape[1] // k.shape[1]
+            if g > 1:   # as if only the group's last query head were counted
+                for hk in range(k.shape[1]):
+                    _, dk1, dv1 = orig(q[0, hk * g + g - 1], k[0, hk], v[0, hk],
+                                       do[0, hk * g + g - 1], causal, scale)
+                    dk[0, hk], dv[0, hk] = dk1, dv1
+            return dq, dk, dv
+        monkeypatch.setattr(bw, "attention_backward", keep_last)
+    pins = [lambda: test_matches_torch_autograd((2, 4, 2, 16, 8), True),
+            test_shift_and_sum_invariants]
+    failed = 0
+    for pin in pins:
+        try:
+            pin()
+        except AssertionError:
+            failed += 1
+    assert failed > 0
