@@ -9,12 +9,13 @@ ImportError (there is no fallback path).
 
 import importlib
 
-_BINDING_NAMES = ("AttnError", "EXPORTS", "attn_fwd", "attn_fwd_ex", "attn_fwd_mxfp4",
-                  "attn_fwd_mxfp4_ex", "attn_quantize_mxfp4_cols_t", "attn_quantize_mxfp4_rows",
-                  "attn_fwd_mxfp8", "attn_fwd_mxfp8_ex", "attn_quantize_mxfp8_cols_t",
-                  "attn_quantize_mxfp8_rows", "check", "fwd", "fwd_mxfp4", "fwd_mxfp8",
-                  "make_opts", "quantize_mxfp4_cols_t", "quantize_mxfp4_rows",
-                  "quantize_mxfp8_cols_t", "quantize_mxfp8_rows", "STATS_COUNTERS", "lib")
+_BINDING_NAMES = ("AttnError", "EXPORTS", "attn_bwd", "attn_fwd", "attn_fwd_ex",
+                  "attn_fwd_mxfp4", "attn_fwd_mxfp4_ex", "attn_fwd_mxfp8", "attn_fwd_mxfp8_ex",
+                  "attn_quantize_mxfp4_cols_t", "attn_quantize_mxfp4_rows",
+                  "attn_quantize_mxfp8_cols_t", "attn_quantize_mxfp8_rows", "bwd", "check",
+                  "fwd", "fwd_mxfp4", "fwd_mxfp8", "make_opts", "quantize_mxfp4_cols_t",
+                  "quantize_mxfp4_rows", "quantize_mxfp8_cols_t", "quantize_mxfp8_rows",
+                  "STATS_COUNTERS", "lib")
 
 __all__ = list(_BINDING_NAMES)
 

@@ -20,7 +20,7 @@ EXP_MODES = {"hw": 0, "poly": 1, "mix": 2}
 EXPORTS = ("attn_default_opts", "attn_fwd", "attn_fwd_ex", "attn_fwd_mxfp4", "attn_fwd_mxfp4_ex",
            "attn_quantize_mxfp4_rows", "attn_quantize_mxfp4_cols_t", "attn_fwd_mxfp8",
            "attn_fwd_mxfp8_ex", "attn_quantize_mxfp8_rows", "attn_quantize_mxfp8_cols_t",
-           "attn_strerror", "attn_last_hip_error")
+           "attn_bwd", "attn_strerror", "attn_last_hip_error")
 
 
 class AttnOpts(ctypes.Structure):
@@ -50,6 +50,7 @@ def _load():
         "attn_fwd_mxfp8_ex": (I, [P] * 8 + [I] * 6 + [F, OP, P]),
         "attn_quantize_mxfp8_rows": (I, [P, P, P, LL, I, P]),
         "attn_quantize_mxfp8_cols_t": (I, [P, P, P, I, I, I, P]),
+        "attn_bwd": (I, [P] * 10 + [I] * 6 + [F, P]),
         "attn_strerror": (ctypes.c_char_p, [I]),
         "attn_last_hip_error": (I, []),
     }
@@ -135,6 +136,12 @@ def attn_quantize_mxfp8_rows(x, codes, scales, rows, cols, stream=None):
 
 def attn_quantize_mxfp8_cols_t(x, codes, scales, batch, rows, cols, stream=None):
     return lib.attn_quantize_mxfp8_cols_t(x, codes, scales, batch, rows, cols, stream)
+
+
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, N, d, causal, scale,
+             stream=None):
+    return lib.attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, N, d, causal,
+                        scale, stream)
 
 
 def attn_quantize_mxfp4_rows(x, codes, scales, rows, cols, stream=None):
@@ -319,3 +326,37 @@ def fwd_mxfp8(q8, qs, k8, ks, vt8, vts, causal=False, scale=None, tau=8.0, stats
                             B, Hq, Hkv, N, d, int(bool(causal)), float(scale), opts,
                             _stream(torch, q8.device)))
     return o, lse
+
+
+def bwd(q, k, v, o, lse, dout, causal=False, scale=None, out=None, delta=None):
+    """bf16 attention backward: returns (dQ fp32 [B,Hq,N,d], dK, dV fp32 [B,Hkv,N,d]).
+    o, lse: the forward's outputs for the same q, k, v (fp32); dout: bf16 like q.
+    delta: optional fp32 CUDA workspace of B*Hq*N floats."""
+    torch = _torch()
+    for t in (q, k, v, dout):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v, dout must be contiguous bf16 CUDA tensors")
+    for t in (o, lse):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("o, lse must be contiguous fp32 CUDA tensors")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if (k.shape != (B, Hkv, N, d) or v.shape != k.shape or dout.shape != q.shape
+            or o.shape != q.shape or lse.shape != (B, Hq, N)):
+        raise ValueError("shapes do not match q [B, Hq, N, d]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        dq = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device)
+        dk = torch.empty((B, Hkv, N, d), dtype=torch.float32, device=q.device)
+        dv = torch.empty((B, Hkv, N, d), dtype=torch.float32, device=q.device)
+    else:
+        dq, dk, dv = out
+    if delta is None:
+        delta = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    elif delta.dtype != torch.float32 or not delta.is_cuda or delta.numel() < B * Hq * N:
+        raise ValueError("delta must be an fp32 CUDA tensor of at least B*Hq*N floats")
+    check(attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                   dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                   B, Hq, Hkv, N, d, int(bool(causal)), float(scale), _stream(torch, q.device)))
+    return dq, dk, dv

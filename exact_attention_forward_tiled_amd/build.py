@@ -25,7 +25,8 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           "-Wno-unused-command-line-argument", "-I", CSRC, "-I", os.path.join(ROOT, "include")]
 
 LIBS = {
-    "libattn.so": ["attn_api.cpp", "attn_fwd_bf16.hip", "attn_mxfp4.hip", "attn_mxfp8.hip"],
+    "libattn.so": ["attn_api.cpp", "attn_fwd_bf16.hip", "attn_mxfp4.hip", "attn_mxfp8.hip",
+                   "attn_bwd_bf16.hip"],
     "libattn_probes.so": ["probes.hip"],
 }
 

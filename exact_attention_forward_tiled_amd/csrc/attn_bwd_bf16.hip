@@ -1,0 +1,363 @@
+// bf16 attention backward: dQ, dK, dV from the saved LSE.
+//
+// The forward keeps only O and the row log-sum-exp; the backward recomputes the
+// probabilities from them instead of storing the N x N matrix ("FlashAttention-4
+// 发布：原生支持Blackwell…", section "从V1到V4", FlashAttention (2022) entry:
+// tiling plus recomputation; "Hardware-Aware FP4 FlashAttention-4", section
+// "2. Causal Backward Cuantizado": the forward saves the LSE and the backward
+// rebuilds the probabilities from it).  With s = scale q.k and P = exp(s - LSE):
+//   D_i  = dO_i . O_i                         (delta_kernel)
+//   dS   = P * (dO V^T - D)
+//   dV   = P^T dO,  dK = scale dS^T Q          (dkdv_kernel, one workgroup per key block)
+//   dQ   = scale dS K                          (dq_kernel, one workgroup per query block)
+// Each kernel recomputes S and dP for its own orientation, so every output is
+// written once by one workgroup: no atomics, deterministic results.
+//
+// All products run on v_mfma_f32_32x32x16_bf16.  Operand layouts (probed): lane l
+// holds A[l % 32][8*(l / 32) + i] and B[8*(l / 32) + i][l % 32], i = 0..7;
+// accumulator register r of lane l is C[8*(r / 4) + 4*(l / 32) + r % 4][l % 32].
+// Reading the A rows in the order pi(m) (bits 2 and 3 of m swapped) makes
+// register r of the product hold row 16*(r / 8) + 8*(l / 32) + r % 8 of the
+// 32-row block, which is exactly the k index the B operand of the next product
+// expects from that lane: the probabilities go from one MFMA to the next
+// without any data movement.
+
+#include "common.h"
+#include "launch.h"
+
+namespace attn {
+namespace {
+
+constexpr int kBD = 128;                 // head dimension of this path
+constexpr int kBWaves = 4;
+constexpr int kBThreads = kBWaves * 64;
+constexpr int kBBlock = kBWaves * 32;    // keys (dK/dV) or queries (dQ) per workgroup
+constexpr int kBTile = 32;               // queries (dK/dV) or keys (dQ) per loop step
+constexpr int kRowStride = kBD * 2 + 16; // bytes per staged row (padded)
+constexpr int kColStride = kBTile * 2 + 16;  // bytes per staged transposed column (padded)
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int perm_row(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+// row of the 32-row block held by accumulator register r of lane half h (after pi)
+__device__ __forceinline__ int acc_row(int r, int h) { return 16 * (r >> 3) + 8 * h + (r & 7); }
+
+__device__ __forceinline__ f32x16 mfma_bf16(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// bf16 B operand (8 k values) from accumulator registers 8c .. 8c + 7.
+__device__ __forceinline__ u32x4 pack_chunk(const f32x16& x, int c) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = pack_bf16x2(x[8 * c + 2 * i], x[8 * c + 2 * i + 1]);
+  return r;
+}
+
+// Staged tile: 32 rows x 128 bf16 of two tensors, row-major and transposed.
+struct BTile {
+  uint8_t a[kBTile * kRowStride];     // tensor A, row r at r * kRowStride
+  uint8_t b[kBTile * kRowStride];     // tensor B
+  uint8_t at[kBD * kColStride];       // A transposed: column d at d * kColStride, 32 rows
+  uint8_t bt[kBD * kColStride];       // B transposed
+  float s0[kBTile];                   // per-row scalars (LSE, D) of the dK/dV tile
+  float s1[kBTile];
+};
+
+// Stage rows r0 .. r0 + 31 of two [N, 128] bf16 tensors (rows past N read as row N - 1:
+// in bounds; their contributions are masked by the caller).
+__device__ __forceinline__ void stage_pair(BTile& t, const uint16_t* A, const uint16_t* B,
+                                           int r0, int N, bool transposed_a, bool transposed_b) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int unit = tid + u * kBThreads;     // 512 units of 16 bytes per tensor
+    const int row = unit >> 4, c16 = unit & 15;
+    const int gr = min(r0 + row, N - 1);
+    const u32x4 va = *(const u32x4*)(A + (size_t)gr * kBD + 8 * c16);
+    const u32x4 vb = *(const u32x4*)(B + (size_t)gr * kBD + 8 * c16);
+    *(u32x4*)(t.a + row * kRowStride + 16 * c16) = va;
+    *(u32x4*)(t.b + row * kRowStride + 16 * c16) = vb;
+    if (transposed_a) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        *(uint16_t*)(t.at + (8 * c16 + i) * kColStride + 2 * row) =
+            (uint16_t)(va[i >> 1] >> (16 * (i & 1)));
+    }
+    if (transposed_b) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        *(uint16_t*)(t.bt + (8 * c16 + i) * kColStride + 2 * row) =
+            (uint16_t)(vb[i >> 1] >> (16 * (i & 1)));
+    }
+  }
+}
+
+__device__ __forceinline__ u32x4 lds_u32x4(const uint8_t* p) { return *(const u32x4*)p; }
+
+// D_i = dO_i . O_i, 16 threads per row.
+__global__ void delta_kernel(const float* __restrict__ O, const uint16_t* __restrict__ dO,
+                             float* __restrict__ D, long long rows) {
+  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int part = threadIdx.x & 15;
+  float acc = 0.f;
+  if (row < rows) {
+    const f32x4* o = (const f32x4*)(O + row * kBD + 8 * part);
+    const u32x4 g = *(const u32x4*)(dO + row * kBD + 8 * part);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const f32x4 ov = o[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w = g[2 * i + (e >> 1)];
+        const float gv = __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+        acc = __builtin_fmaf(ov[e], gv, acc);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
+  if (row < rows && part == 0) D[row] = acc;
+}
+
+// dK, dV for 128 keys of one (batch, kv head): each wave owns 32 keys; the loop runs
+// over the group's query heads and their 32-query blocks (causal: only blocks that
+// reach the workgroup's keys).
+template <bool CAUSAL>
+__global__ __launch_bounds__(kBThreads) void dkdv_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    const float* __restrict__ LSE, const float* __restrict__ D, float* __restrict__ dK,
+    float* __restrict__ dV, int Hq, int Hkv, int N, int nkb, float c, float scale) {
+  __shared__ BTile tile;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n32 = lane & 31, h = lane >> 5;
+  const int kb = blockIdx.x % nkb;
+  const int bh = blockIdx.x / nkb;          // b * Hkv + hkv
+  const int hkv = bh % Hkv, b = bh / Hkv;
+  const int group = Hq / Hkv;
+  const int K0 = kb * kBBlock;
+  const int kw0 = K0 + wave * 32;           // this wave's keys
+  const int key = kw0 + n32;                // this lane's key (accumulator column)
+
+  const size_t khead = (size_t)(b * Hkv + hkv) * N;
+  // K^T and V^T as B operands: lane holds K[key][16c + 8h .. +7] for each d chunk c
+  u32x4 kop[kBD / 16], vop[kBD / 16];
+  {
+    const int kr = min(key, N - 1);
+    const uint16_t* krow = K + (khead + kr) * kBD;
+    const uint16_t* vrow = V + (khead + kr) * kBD;
+#pragma unroll
+    for (int cc = 0; cc < kBD / 16; ++cc) {
+      kop[cc] = *(const u32x4*)(krow + 16 * cc + 8 * h);
+      vop[cc] = *(const u32x4*)(vrow + 16 * cc + 8 * h);
+    }
+  }
+  f32x16 dk[kBD / 32], dv[kBD / 32];
+#pragma unroll
+  for (int i = 0; i < kBD / 32; ++i) {
+    dk[i] = zero16();
+    dv[i] = zero16();
+  }
+
+  const int nqt = (N + kBTile - 1) / kBTile;
+  const int qt0 = CAUSAL ? K0 / kBTile : 0;
+  const int pm = perm_row(n32);
+  for (int g = 0; g < group; ++g) {
+    const int hq = hkv * group + g;
+    const size_t qhead = (size_t)(b * Hq + hq) * N;
+    for (int qt = qt0; qt < nqt; ++qt) {
+      const int q0 = qt * kBTile;
+      __syncthreads();
+      stage_pair(tile, Q + qhead * kBD, dO + qhead * kBD, q0, N, true, true);
+      if (tid < kBTile) {
+        const int qr = q0 + tid;
+        const float l = qr < N ? LSE[qhead + qr] : -__builtin_inff();
+        // rows past N or without visible keys: +inf makes their weights 0
+        tile.s0[tid] = (l == -__builtin_inff()) ? __builtin_inff() : l * kLog2e;
+        tile.s1[tid] = qr < N ? D[qhead + qr] : 0.f;
+      }
+      __syncthreads();
+      // this wave's keys all lie after the block's last query: nothing visible
+      if (CAUSAL && kw0 > q0 + kBTile - 1) continue;
+      // S = Q_pi K^T and dP = dO_pi V^T (queries x keys; rows permuted)
+      f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+      for (int cc = 0; cc < kBD / 16; ++cc) {
+        const u32x4 qa = lds_u32x4(tile.a + pm * kRowStride + 32 * cc + 16 * h);
+        const u32x4 ga = lds_u32x4(tile.b + pm * kRowStride + 32 * cc + 16 * h);
+        s = mfma_bf16(qa, kop[cc], s);
+        dp = mfma_bf16(ga, vop[cc], dp);
+      }
+      // P and dS; register r holds query q0 + acc_row(r, h) for this lane's key
+      f32x16 p, ds;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qi = acc_row(r, h);
+        const float lse2 = tile.s0[qi];
+        float x = __builtin_fmaf(s[r], c, -lse2);
+        const bool vis = key < N && (!CAUSAL || key <= q0 + qi);
+        const float pr = vis ? __builtin_amdgcn_exp2f(x) : 0.f;
+        p[r] = pr;
+        ds[r] = pr * (dp[r] - tile.s1[qi]);
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS (d x keys), over the two 16-query chunks
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        const u32x4 pb = pack_chunk(p, q2), db = pack_chunk(ds, q2);
+#pragma unroll
+        for (int dbk = 0; dbk < kBD / 32; ++dbk) {
+          const int dcol = 32 * dbk + n32;
+          const u32x4 gta = lds_u32x4(tile.bt + dcol * kColStride + 32 * q2 + 16 * h);
+          const u32x4 qta = lds_u32x4(tile.at + dcol * kColStride + 32 * q2 + 16 * h);
+          dv[dbk] = mfma_bf16(gta, pb, dv[dbk]);
+          dk[dbk] = mfma_bf16(qta, db, dk[dbk]);
+        }
+      }
+    }
+  }
+  // dK = scale * (dK^T)^T, dV = (dV^T)^T: lane holds d 32dbk + 8a + 4h + 0..3 of its key
+  if (key < N) {
+    float* dkrow = dK + (khead + key) * kBD;
+    float* dvrow = dV + (khead + key) * kBD;
+#pragma unroll
+    for (int dbk = 0; dbk < kBD / 32; ++dbk)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int col = 32 * dbk + 8 * a4 + 4 * h;
+        f32x4 kv = {dk[dbk][4 * a4] * scale, dk[dbk][4 * a4 + 1] * scale,
+                    dk[dbk][4 * a4 + 2] * scale, dk[dbk][4 * a4 + 3] * scale};
+        f32x4 vv = {dv[dbk][4 * a4], dv[dbk][4 * a4 + 1], dv[dbk][4 * a4 + 2],
+                    dv[dbk][4 * a4 + 3]};
+        *(f32x4*)(dkrow + col) = kv;
+        *(f32x4*)(dvrow + col) = vv;
+      }
+  }
+}
+
+// dQ for 128 queries of one (batch, query head): each wave owns 32 queries; the loop
+// runs over 32-key blocks (causal: up to the workgroup's last query).
+template <bool CAUSAL>
+__global__ __launch_bounds__(kBThreads) void dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    const float* __restrict__ LSE, const float* __restrict__ D, float* __restrict__ dQ,
+    int Hq, int Hkv, int N, int nqb, float c, float scale) {
+  __shared__ BTile tile;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n32 = lane & 31, h = lane >> 5;
+  const int qb = blockIdx.x % nqb;
+  const int bh = blockIdx.x / nqb;          // b * Hq + hq
+  const int hq = bh % Hq, b = bh / Hq;
+  const int hkv = hq / (Hq / Hkv);
+  const int Q0 = qb * kBBlock;
+  const int qw0 = Q0 + wave * 32;
+  const int qi = qw0 + n32;                 // this lane's query (accumulator column)
+
+  const size_t qhead = (size_t)(b * Hq + hq) * N;
+  const size_t khead = (size_t)(b * Hkv + hkv) * N;
+  // Q^T and dO^T as B operands: lane holds Q[qi][16c + 8h .. +7]
+  u32x4 qop[kBD / 16], gop[kBD / 16];
+  float lse2 = __builtin_inff(), dlt = 0.f;
+  {
+    const int qr = min(qi, N - 1);
+    const uint16_t* qrow = Q + (qhead + qr) * kBD;
+    const uint16_t* grow = dO + (qhead + qr) * kBD;
+#pragma unroll
+    for (int cc = 0; cc < kBD / 16; ++cc) {
+      qop[cc] = *(const u32x4*)(qrow + 16 * cc + 8 * h);
+      gop[cc] = *(const u32x4*)(grow + 16 * cc + 8 * h);
+    }
+    if (qi < N) {
+      const float l = LSE[qhead + qi];
+      lse2 = (l == -__builtin_inff()) ? __builtin_inff() : l * kLog2e;
+      dlt = D[qhead + qi];
+    }
+  }
+  f32x16 dq[kBD / 32];
+#pragma unroll
+  for (int i = 0; i < kBD / 32; ++i) dq[i] = zero16();
+
+  const int kend = CAUSAL ? min(N, Q0 + kBBlock) : N;
+  const int nkt = (kend + kBTile - 1) / kBTile;
+  const int pm = perm_row(n32);
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int k0 = kt * kBTile;
+    __syncthreads();
+    stage_pair(tile, K + khead * kBD, V + khead * kBD, k0, N, true, false);
+    __syncthreads();
+    if (CAUSAL && k0 > qw0 + 31) continue;
+    // S^T = K_pi Q^T and dP^T = V_pi dO^T (keys x queries; rows permuted)
+    f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+    for (int cc = 0; cc < kBD / 16; ++cc) {
+      const u32x4 ka = lds_u32x4(tile.a + pm * kRowStride + 32 * cc + 16 * h);
+      const u32x4 va = lds_u32x4(tile.b + pm * kRowStride + 32 * cc + 16 * h);
+      s = mfma_bf16(ka, qop[cc], s);
+      dp = mfma_bf16(va, gop[cc], dp);
+    }
+    // dS^T; register r holds key k0 + acc_row(r, h) for this lane's query
+    f32x16 ds;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kj = k0 + acc_row(r, h);
+      const bool vis = kj < N && qi < N && (!CAUSAL || kj <= qi);
+      const float pr = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2)) : 0.f;
+      ds[r] = pr * (dp[r] - dlt);
+    }
+    // dQ^T += K^T dS^T (d x queries), over the two 16-key chunks
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const u32x4 db = pack_chunk(ds, k2);
+#pragma unroll
+      for (int dbk = 0; dbk < kBD / 32; ++dbk) {
+        const int dcol = 32 * dbk + n32;
+        const u32x4 kta = lds_u32x4(tile.at + dcol * kColStride + 32 * k2 + 16 * h);
+        dq[dbk] = mfma_bf16(kta, db, dq[dbk]);
+      }
+    }
+  }
+  if (qi < N) {
+    float* row = dQ + (qhead + qi) * kBD;
+#pragma unroll
+    for (int dbk = 0; dbk < kBD / 32; ++dbk)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        f32x4 v = {dq[dbk][4 * a4] * scale, dq[dbk][4 * a4 + 1] * scale,
+                   dq[dbk][4 * a4 + 2] * scale, dq[dbk][4 * a4 + 3] * scale};
+        *(f32x4*)(row + 32 * dbk + 8 * a4 + 4 * h) = v;
+      }
+  }
+}
+
+template <bool CAUSAL>
+hipError_t launch_bwd_t(const BwdArgs& a) {
+  const long long rows = (long long)a.B * a.Hq * a.N;
+  hipLaunchKernelGGL(delta_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0,
+                     (hipStream_t)a.stream, a.o, (const uint16_t*)a.dout, a.delta, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nb = (a.N + kBBlock - 1) / kBBlock;
+  hipLaunchKernelGGL((dkdv_kernel<CAUSAL>), dim3((unsigned)(a.B * a.Hkv * nb)), dim3(kBThreads),
+                     0, (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                     (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta, a.dk, a.dv,
+                     a.Hq, a.Hkv, a.N, nb, a.c, a.scale);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((dq_kernel<CAUSAL>), dim3((unsigned)(a.B * a.Hq * nb)), dim3(kBThreads), 0,
+                     (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                     (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta, a.dq,
+                     a.Hq, a.Hkv, a.N, nb, a.c, a.scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdArgs& a) {
+  if (a.d != kBD) return hipErrorNotSupported;
+  return a.causal ? launch_bwd_t<true>(a) : launch_bwd_t<false>(a);
+}
+
+}  // namespace attn

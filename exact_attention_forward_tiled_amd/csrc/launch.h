@@ -43,7 +43,26 @@ struct MxArgs {
   void* stream;
 };
 
+// bf16 backward (d = 128): gradients of the forward from its saved O and LSE.
+struct BwdArgs {
+  const void* q;        // bf16 [B, Hq, N, d]
+  const void* k;        // bf16 [B, Hkv, N, d]
+  const void* v;        // bf16 [B, Hkv, N, d]
+  const float* o;       // fp32 [B, Hq, N, d], the forward's output
+  const float* lse;     // fp32 [B, Hq, N], the forward's LSE (natural log)
+  const void* dout;     // bf16 [B, Hq, N, d]
+  float* dq;            // fp32 [B, Hq, N, d]
+  float* dk;            // fp32 [B, Hkv, N, d]
+  float* dv;            // fp32 [B, Hkv, N, d]
+  float* delta;         // fp32 [B, Hq, N] workspace (D_i = dO_i . O_i)
+  int B, Hq, Hkv, N, d, causal;
+  float c;              // scale * log2(e)
+  float scale;
+  void* stream;
+};
+
 hipError_t launch_fwd_bf16(const FwdArgs& a);
+hipError_t launch_bwd_bf16(const BwdArgs& a);
 hipError_t launch_fwd_mxfp4(const MxArgs& a);
 hipError_t launch_fwd_mxfp8(const MxArgs& a);
 hipError_t launch_quantize_rows(const float* x, uint8_t* codes, uint8_t* scales, long long rows,

@@ -202,6 +202,28 @@ int attn_quantize_mxfp8_rows(const float* x, uint8_t* codes, uint8_t* scales,
 int attn_quantize_mxfp8_cols_t(const float* x, uint8_t* codes, uint8_t* scales,
                                int batch, int rows, int cols, void* stream);
 
+/*
+ * bf16 backward: the gradients of the bf16 forward (same masks, scale and GQA map), with
+ * the probabilities rebuilt from the forward's saved LSE instead of a stored N x N matrix
+ * ("FlashAttention-4发布：原生支持Blackwell…", section "从V1到V4", FlashAttention (2022)
+ * entry: tiling plus recomputation; "Hardware-Aware FP4 FlashAttention-4", section
+ * "2. Causal Backward Cuantizado": the forward saves the LSE for the backward).  With
+ * s = scale q.k (masked: -inf) and P = exp(s - LSE):
+ *     D = rowsum(dO * O),  dS = P * (dO V^T - D)
+ *     dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO   (dK, dV summed over the query
+ *                                                          heads that share a kv head)
+ *   q bf16 [B, Hq, N, d]; k, v bf16 [B, Hkv, N, d]; o fp32 [B, Hq, N, d] and lse fp32
+ *   [B, Hq, N] as written by attn_fwd on the same inputs; dout bf16 [B, Hq, N, d];
+ *   dq fp32 [B, Hq, N, d], dk, dv fp32 [B, Hkv, N, d] (outputs, every element written);
+ *   delta: caller-owned device workspace of B*Hq*N floats (overwritten; holds D afterwards).
+ *   d = 128 (else ATTN_EUNSUPPORTED); any N >= 1; causal in {0, 1}; scale finite.
+ *   Three kernels are queued on `stream` (null: the null stream); no atomics, so the
+ *   results are deterministic.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse,
+             const void* dout, float* dq, float* dk, float* dv, float* delta,
+             int B, int Hq, int Hkv, int N, int d, int causal, float scale, void* stream);
+
 /* Static description of a status code; never NULL. */
 const char* attn_strerror(int status);
 

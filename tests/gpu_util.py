@@ -67,3 +67,11 @@ def mxfp8_lse_tol(qt, kt, scale):
         mk = ka[..., c0:c0 + 64].max(axis=-2)
         worst = worst + (mq * mk).max(axis=-1)
     return MXFP8_LSE_ABS + MXFP8_MFMA_REL * abs(scale) * float(np.max(worst))
+# tolerances for the bf16 backward against the float64 oracle (no stated figure).  The kernel
+# rounds P and dS to bf16 (unit roundoff 2^-9) before the products that consume them, as the
+# forward rounds P; dV = P^T dO then carries about 2^-9 relative error per term, averaged
+# down over the keys, as O does (forward gate 5e-3).  dS's rows sum to zero, so dQ = scale
+# dS K and dK = scale dS^T Q are sums with cancellation: their relative error is the
+# rounding of dS times the ratio of sum |dS_ij k_j| to |sum dS_ij k_j|, a few times larger.
+BWD_DV_RELRMS = 5e-3
+BWD_DQK_RELRMS = 1e-2

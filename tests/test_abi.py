@@ -132,6 +132,22 @@ def test_mxfp8_validation(fa):
     assert fa.attn_quantize_mxfp8_cols_t(FAKE, FAKE, FAKE, 1, 40, 8) == -1
 
 
+def test_bwd_validation(fa):
+    base = [FAKE] * 10
+    assert fa.attn_bwd(*base, 1, 2, 2, 64, 64, 0, 0.1) == -2            # d must be 128
+    assert fa.attn_bwd(*base, 1, 3, 2, 64, 128, 0, 0.1) == -1           # Hq % Hkv
+    assert fa.attn_bwd(*base, 1, 2, 2, 0, 128, 0, 0.1) == -1            # N >= 1
+    assert fa.attn_bwd(*base, 1, 2, 2, 64, 128, 3, 0.1) == -1           # causal in {0, 1}
+    assert fa.attn_bwd(*base, 1, 2, 2, 64, 128, 0, float("inf")) == -1  # finite scale
+    for i in range(10):                                                 # every pointer
+        args = list(base)
+        args[i] = 0
+        assert fa.attn_bwd(*args, 1, 2, 2, 64, 128, 0, 0.1) == -1
+    args = list(base)
+    args[6] = FAKE + 4                                                  # dq 16-byte aligned
+    assert fa.attn_bwd(*args, 1, 2, 2, 64, 128, 0, 0.1) == -1
+
+
 def test_strerror(fa):
     from exact_attention_forward_tiled_amd.binding import lib
     assert lib.attn_strerror(0) == b"success"

@@ -1,0 +1,121 @@
+"""bf16 backward on the GPU (through the C ABI) against the float64 oracle.
+
+The backward takes the forward's O and LSE.  Two feeds are tested: the oracle's own O and
+LSE (the backward kernels alone) and the GPU forward's (the forward + backward pair as a
+caller runs it).  Gates: relRMS(dV) <= 5e-3, relRMS(dQ), relRMS(dK) <= 1e-2 (gpu_util
+states the arithmetic); invariants from the definition (the dK rows of a kv head sum to 0,
+the dV rows sum to the group's dO rows); bitwise determinism (no atomics).
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import backward as bw
+from gpu_util import BWD_DQK_RELRMS, BWD_DV_RELRMS, cuda_ok, log, rel_rms, to_dev_bf16, to_dev_f32
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not cuda_ok(), reason="needs a GPU")]
+
+
+def _case(seed, B, Hq, Hkv, N, d=128):
+    """bf16 bits of q, k, v, dO and their exact float64 values."""
+    qb, kb, vb = synth.configs.random_case(seed, B, Hq, Hkv, N, d)
+    gb = synth.normal_bf16((B, Hq, N, d), 7919 + seed, 1.0)
+    return (qb, kb, vb, gb), tuple(synth.bf16_bits_to_f64(x) for x in (qb, kb, vb, gb))
+
+
+def _run(bits, causal, scale, o=None, lse=None):
+    """GPU backward; o, lse: float64 arrays to feed, else the GPU forward's outputs."""
+    import torch
+    import exact_attention_forward_tiled_amd as fa
+    q, k, v, g = (to_dev_bf16(x) for x in bits)
+    if o is None:
+        od, ld = fa.fwd(q, k, v, causal=causal, scale=scale)
+    else:
+        od, ld = to_dev_f32(o), to_dev_f32(lse)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    nan = float("nan")
+    dq = torch.full((B, Hq, N, d), nan, dtype=torch.float32, device="cuda")
+    dk = torch.full((B, Hkv, N, d), nan, dtype=torch.float32, device="cuda")
+    dv = torch.full((B, Hkv, N, d), nan, dtype=torch.float32, device="cuda")
+    fa.bwd(q, k, v, od, ld, g, causal=causal, scale=scale, out=(dq, dk, dv))
+    torch.cuda.synchronize()
+    return dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
+
+
+def _check(got, ref, tag):
+    rq, rk, rv = (rel_rms(a, b) for a, b in zip(got, ref))
+    log(f"  {tag}: relRMS dQ={rq:.2e} dK={rk:.2e} dV={rv:.2e}")
+    for a in got:
+        assert not np.isnan(a).any()
+    assert rv <= BWD_DV_RELRMS, rv
+    assert rq <= BWD_DQK_RELRMS and rk <= BWD_DQK_RELRMS, (rq, rk)
+
+
+SMALL = [
+    # B, Hq, Hkv, N, causal
+    (1, 2, 2, 128, False),
+    (1, 2, 2, 128, True),
+    (1, 1, 1, 1, False),
+    (1, 1, 1, 1, True),
+    (1, 2, 2, 33, True),
+    (2, 4, 2, 200, False),
+    (1, 8, 2, 256, True),
+    (1, 2, 2, 300, False),
+    (1, 2, 1, 161, True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "B%dHq%dHkv%dN%d%s" % (
+    c[0], c[1], c[2], c[3], "c" if c[4] else "n"))
+def test_bwd_small(case):
+    B, Hq, Hkv, N, causal = case
+    bits, (q, k, v, g) = _case(sum(case[:4]) + 11, B, Hq, Hkv, N)
+    scale = 1.0 / math.sqrt(128)
+    o, lse = oracle.attention(q, k, v, causal, scale)
+    ref = bw.attention_backward(q, k, v, g, causal, scale, o=o, lse=lse)
+    log(f"bwd case {case}")
+    _check(_run(bits, causal, scale, o, lse), ref, "oracle O/LSE")
+    _check(_run(bits, causal, scale), ref, "GPU forward O/LSE")
+
+
+def test_bwd_negative_scale_and_large_logits():
+    bits, (q, k, v, g) = _case(51, 1, 2, 2, 192)
+    for scale in (-0.2, 0.3):
+        o, lse = oracle.attention(q, k, v, False, scale)
+        ref = bw.attention_backward(q, k, v, g, False, scale, o=o, lse=lse)
+        log(f"bwd scale {scale}")
+        _check(_run(bits, False, scale, o, lse), ref, f"scale {scale}")
+
+
+def test_bwd_deterministic_and_invariants():
+    bits, (q, k, v, g) = _case(52, 1, 4, 2, 256)
+    scale = 1.0 / math.sqrt(128)
+    log("bwd determinism")
+    a = _run(bits, True, scale)
+    b = _run(bits, True, scale)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    dq, dk, dv = a
+    # dK rows of each kv head sum to ~0; dV rows sum to the group's dO rows
+    assert np.abs(dk.sum(axis=2)).max() <= 1e-2 * np.abs(dk).sum(axis=2).max()
+    want = g.reshape(1, 2, 2, 256, 128).sum(axis=(2, 3))
+    assert np.allclose(dv.sum(axis=2), want, rtol=1e-2, atol=1e-2 * np.abs(want).max())
+
+
+def test_bwd_headline_shape_two_heads():
+    """Causal B4 H16 N2048 d128 (the forward's headline shape) in the launch configuration a
+    caller uses: all heads run on the GPU, two heads are checked against the oracle in full."""
+    w = synth.workload(2)
+    qb, kb, vb = w.make()
+    gb = synth.normal_bf16((w.B, w.Hq, w.N, w.d), 2917, 1.0)
+    log(f"bwd on {w.name}")
+    dq, dk, dv = _run((qb, kb, vb, gb), w.causal, w.scale)
+    for b, h in ((0, 0), (w.B - 1, w.Hq - 1)):
+        q, k, v, g = (synth.bf16_bits_to_f64(x[b, h]) for x in (qb, kb, vb, gb))
+        ref = bw.backward_head(q, k, v, g, w.causal, w.scale)
+        _check((dq[b, h], dk[b, h], dv[b, h]), ref, f"(b, h) = ({b}, {h})")
