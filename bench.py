@@ -17,6 +17,7 @@ FLOPs follow the metric: 4*B*H*N^2*d, halved for causal.
 
 Other modes (for rocprofv3 counter runs; they print nothing on stdout):
   --mode launch   run the workload's kernel --steps times, no timing, no oracle
+                  (with --bwd: the three backward kernels instead)
   --mode copy     a plain device-to-device copy of --copy-mib MiB, --steps times
                   (calibrates the HBM byte counters against a known transfer)
 and one that prints its own JSON line:
@@ -159,6 +160,37 @@ class Mxfp8Workload:
         self.fa.fwd_mxfp8(self.q8, self.qs, self.k8, self.ks, self.vt8, self.vts,
                           causal=self.w.causal, scale=self.w.scale, tau=self.tau, stats=stats,
                           out=(self.o, self.lse))
+
+
+class BwdWorkload:
+    """bf16 backward on a bf16 workload: the forward's O and LSE computed once (untimed),
+    a seeded dO, then the three backward kernels per step."""
+
+    def __init__(self, w):
+        import torch
+        import exact_attention_forward_tiled_amd as fa
+        import synth
+        self.w = w
+        self.q, self.k, self.v = device_inputs(w)
+        self.o, self.lse = fa.fwd(self.q, self.k, self.v, causal=w.causal, scale=w.scale)
+        gb = synth.normal_bf16((w.B, w.Hq, w.N, w.d), 1000 * w.index + 4, 1.0)
+        self.do = device_inputs_bits(gb)
+        self.dq = torch.empty((w.B, w.Hq, w.N, w.d), dtype=torch.float32, device="cuda")
+        self.dk = torch.empty((w.B, w.Hkv, w.N, w.d), dtype=torch.float32, device="cuda")
+        self.dv = torch.empty_like(self.dk)
+        self.delta = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        self.fa = fa
+
+    def launch(self, stats=None):
+        self.fa.bwd(self.q, self.k, self.v, self.o, self.lse, self.do, causal=self.w.causal,
+                    scale=self.w.scale, out=(self.dq, self.dk, self.dv), delta=self.delta)
+
+
+def device_inputs_bits(bits):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
 def visible_pairs(N, causal, window, doc_offsets=None):
@@ -348,6 +380,9 @@ def main():
     ap.add_argument("--window", type=int, default=0,
                     help="also time the workload with this sliding window (bf16 only); its "
                          "TFLOP/s count 4*d flop per visible (query, key) pair")
+    ap.add_argument("--bwd", action="store_true",
+                    help="also time the bf16 backward (dQ, dK, dV) on the workload; TFLOP/s "
+                         "count 2.5x the forward's FLOPs (five products)")
     ap.add_argument("--compare-exp", action="store_true",
                     help="also time the headline workload with the other exp modes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -384,7 +419,7 @@ def main():
     w = synth.workload(args.config)
 
     if args.mode == "launch":
-        wl = make_workload(w, args.exp, args.tau, args.poly_frac)
+        wl = BwdWorkload(w) if args.bwd else make_workload(w, args.exp, args.tau, args.poly_frac)
         for _ in range(args.steps):
             wl.launch()
         torch.cuda.synchronize()
@@ -472,6 +507,21 @@ def main():
             "kernel_ms_avg": round(td["kernel_ms_avg"], 4),
             "visible_pairs_per_head": pairs,
             "time_vs_one_document": round(td["kernel_ms_avg"] / t["kernel_ms_avg"], 4)}
+
+    if args.bwd and w.fmt == "bf16":
+        log(f"timing the backward on {w.name}")
+        wl = BwdWorkload(w)
+        tb = time_workload(wl, args.steps, args.warmup, args.warmup_seconds)
+        del wl
+        torch.cuda.empty_cache()
+        fl = 2.5 * w.flops
+        extra["workloads"][f"{w.name}/bwd"] = {
+            "tflops": round(fl / (tb["kernel_ms_avg"] * 1e-3) / 1e12, 2),
+            "ms": round(tb["kernel_ms_avg"], 4),
+            "pct_of_bf16_peak": round(100.0 * fl / (tb["kernel_ms_avg"] * 1e-3) / 1e12
+                                      / PEAK_BF16_TFLOPS, 2),
+            "flop_convention": "2.5x forward (dQ, dK, dV, S, dP); the kernels execute 3.5x "
+                               "(S and dP recomputed in both the dK/dV and the dQ kernel)"}
 
     cpu = None
     if not args.no_cpu_baseline:

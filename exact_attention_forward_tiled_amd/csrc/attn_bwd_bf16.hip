@@ -66,32 +66,47 @@ struct BTile {
   float s1[kBTile];
 };
 
-// Stage rows r0 .. r0 + 31 of two [N, 128] bf16 tensors (rows past N read as row N - 1:
-// in bounds; their contributions are masked by the caller).
-__device__ __forceinline__ void stage_pair(BTile& t, const uint16_t* A, const uint16_t* B,
-                                           int r0, int N, bool transposed_a, bool transposed_b) {
+// One thread's share of a staged tile pair: 2 units of 16 bytes of each tensor.  Unit u
+// is row u % 32, bytes 16 * (u / 32) .. + 15, so the 32 lanes of a half-wave take 32
+// consecutive rows: their 2-byte writes into the transposed copy fall on 32 distinct
+// dwords of one column instead of piling onto two banks.
+struct StageRegs {
+  u32x4 a[2], b[2];
+};
+
+// Fetch rows r0 .. r0 + 31 of two [N, 128] bf16 tensors into registers (rows past N read
+// as row N - 1: in bounds; their contributions are masked by the caller).
+__device__ __forceinline__ void stage_load(StageRegs& sr, const uint16_t* A, const uint16_t* B,
+                                           int r0, int N) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int unit = tid + u * kBThreads;     // 512 units of 16 bytes per tensor
-    const int row = unit >> 4, c16 = unit & 15;
+    const int unit = tid + u * kBThreads;
+    const int row = unit & 31, c16 = unit >> 5;
     const int gr = min(r0 + row, N - 1);
-    const u32x4 va = *(const u32x4*)(A + (size_t)gr * kBD + 8 * c16);
-    const u32x4 vb = *(const u32x4*)(B + (size_t)gr * kBD + 8 * c16);
-    *(u32x4*)(t.a + row * kRowStride + 16 * c16) = va;
-    *(u32x4*)(t.b + row * kRowStride + 16 * c16) = vb;
-    if (transposed_a) {
+    sr.a[u] = *(const u32x4*)(A + (size_t)gr * kBD + 8 * c16);
+    sr.b[u] = *(const u32x4*)(B + (size_t)gr * kBD + 8 * c16);
+  }
+}
+
+__device__ __forceinline__ void put_transposed(uint8_t* t, const u32x4& v, int row, int c16) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *(uint16_t*)(t.at + (8 * c16 + i) * kColStride + 2 * row) =
-            (uint16_t)(va[i >> 1] >> (16 * (i & 1)));
-    }
-    if (transposed_b) {
+  for (int i = 0; i < 8; ++i)
+    *(uint16_t*)(t + (8 * c16 + i) * kColStride + 2 * row) = (uint16_t)(v[i >> 1] >> (16 * (i & 1)));
+}
+
+// Write the fetched rows into LDS: both tensors row-major, and transposed where asked.
+__device__ __forceinline__ void stage_store(BTile& t, const StageRegs& sr, bool transposed_a,
+                                            bool transposed_b) {
+  const int tid = threadIdx.x;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *(uint16_t*)(t.bt + (8 * c16 + i) * kColStride + 2 * row) =
-            (uint16_t)(vb[i >> 1] >> (16 * (i & 1)));
-    }
+  for (int u = 0; u < 2; ++u) {
+    const int unit = tid + u * kBThreads;
+    const int row = unit & 31, c16 = unit >> 5;
+    *(u32x4*)(t.a + row * kRowStride + 16 * c16) = sr.a[u];
+    *(u32x4*)(t.b + row * kRowStride + 16 * c16) = sr.b[u];
+    if (transposed_a) put_transposed(t.at, sr.a[u], row, c16);
+    if (transposed_b) put_transposed(t.bt, sr.b[u], row, c16);
   }
 }
 
@@ -165,21 +180,43 @@ __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
   const int nqt = (N + kBTile - 1) / kBTile;
   const int qt0 = CAUSAL ? K0 / kBTile : 0;
   const int pm = perm_row(n32);
-  for (int g = 0; g < group; ++g) {
-    const int hq = hkv * group + g;
-    const size_t qhead = (size_t)(b * Hq + hq) * N;
-    for (int qt = qt0; qt < nqt; ++qt) {
-      const int q0 = qt * kBTile;
+  // (query head, query tile) steps in order; the next step's rows are fetched into
+  // registers while the current one computes
+  const int steps_per_head = nqt - qt0;
+  const int nsteps = group * steps_per_head;
+  auto step_rows = [&](int st, size_t& qh, int& q0) {
+    const int g = st / steps_per_head;
+    q0 = (qt0 + st % steps_per_head) * kBTile;
+    qh = (size_t)(b * Hq + hkv * group + g) * N;
+  };
+  StageRegs sr;
+  float lse_next = 0.f, d_next = 0.f;
+  auto fetch = [&](int st) {
+    size_t qh;
+    int q0;
+    step_rows(st, qh, q0);
+    stage_load(sr, Q + qh * kBD, dO + qh * kBD, q0, N);
+    if (tid < kBTile) {
+      const int qr = q0 + tid;
+      lse_next = qr < N ? LSE[qh + qr] : -__builtin_inff();
+      d_next = qr < N ? D[qh + qr] : 0.f;
+    }
+  };
+  if (nsteps > 0) fetch(0);
+  for (int st = 0; st < nsteps; ++st) {
+    size_t qh_unused;
+    int q0;
+    step_rows(st, qh_unused, q0);
+    {
       __syncthreads();
-      stage_pair(tile, Q + qhead * kBD, dO + qhead * kBD, q0, N, true, true);
+      stage_store(tile, sr, true, true);
       if (tid < kBTile) {
-        const int qr = q0 + tid;
-        const float l = qr < N ? LSE[qhead + qr] : -__builtin_inff();
         // rows past N or without visible keys: +inf makes their weights 0
-        tile.s0[tid] = (l == -__builtin_inff()) ? __builtin_inff() : l * kLog2e;
-        tile.s1[tid] = qr < N ? D[qhead + qr] : 0.f;
+        tile.s0[tid] = (lse_next == -__builtin_inff()) ? __builtin_inff() : lse_next * kLog2e;
+        tile.s1[tid] = d_next;
       }
       __syncthreads();
+      if (st + 1 < nsteps) fetch(st + 1);
       // this wave's keys all lie after the block's last query: nothing visible
       if (CAUSAL && kw0 > q0 + kBTile - 1) continue;
       // S = Q_pi K^T and dP = dO_pi V^T (queries x keys; rows permuted)
@@ -283,11 +320,15 @@ __global__ __launch_bounds__(kBThreads) void dq_kernel(
   const int kend = CAUSAL ? min(N, Q0 + kBBlock) : N;
   const int nkt = (kend + kBTile - 1) / kBTile;
   const int pm = perm_row(n32);
+  // the next key tile is fetched into registers while the current one computes
+  StageRegs sr;
+  if (nkt > 0) stage_load(sr, K + khead * kBD, V + khead * kBD, 0, N);
   for (int kt = 0; kt < nkt; ++kt) {
     const int k0 = kt * kBTile;
     __syncthreads();
-    stage_pair(tile, K + khead * kBD, V + khead * kBD, k0, N, true, false);
+    stage_store(tile, sr, true, false);
     __syncthreads();
+    if (kt + 1 < nkt) stage_load(sr, K + khead * kBD, V + khead * kBD, k0 + kBTile, N);
     if (CAUSAL && k0 > qw0 + 31) continue;
     // S^T = K_pi Q^T and dP^T = V_pi dO^T (keys x queries; rows permuted)
     f32x16 s = zero16(), dp = zero16();
