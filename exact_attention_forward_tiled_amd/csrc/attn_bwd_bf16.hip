@@ -57,13 +57,13 @@ __device__ __forceinline__ u32x4 pack_chunk(const f32x16& x, int c) {
 }
 
 // Staged tile: 32 rows x 128 bf16 of two tensors, row-major and transposed.
-struct BTile {
+struct alignas(16) BTile {
+  float s0[kBTile];                   // per-row scalars (LSE, D) of the dK/dV tile
+  float s1[kBTile];
   uint8_t a[kBTile * kRowStride];     // tensor A, row r at r * kRowStride
   uint8_t b[kBTile * kRowStride];     // tensor B
   uint8_t at[kBD * kColStride];       // A transposed: column d at d * kColStride, 32 rows
   uint8_t bt[kBD * kColStride];       // B transposed
-  float s0[kBTile];                   // per-row scalars (LSE, D) of the dK/dV tile
-  float s1[kBTile];
 };
 
 // One thread's share of a staged tile pair: 2 units of 16 bytes of each tensor.  Unit u
@@ -219,26 +219,36 @@ __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
       if (st + 1 < nsteps) fetch(st + 1);
       // this wave's keys all lie after the block's last query: nothing visible
       if (CAUSAL && kw0 > q0 + kBTile - 1) continue;
-      // S = Q_pi K^T and dP = dO_pi V^T (queries x keys; rows permuted)
-      f32x16 s = zero16(), dp = zero16();
+      // S = Q_pi K^T and dP = dO_pi V^T (queries x keys; rows permuted), each as two
+      // accumulation chains over alternate d chunks so that four MFMA chains overlap
+      f32x16 s = zero16(), dp = zero16(), s2 = zero16(), dp2 = zero16();
 #pragma unroll
-      for (int cc = 0; cc < kBD / 16; ++cc) {
-        const u32x4 qa = lds_u32x4(tile.a + pm * kRowStride + 32 * cc + 16 * h);
-        const u32x4 ga = lds_u32x4(tile.b + pm * kRowStride + 32 * cc + 16 * h);
-        s = mfma_bf16(qa, kop[cc], s);
-        dp = mfma_bf16(ga, vop[cc], dp);
+      for (int cc = 0; cc < kBD / 16; cc += 2) {
+        const uint8_t* qr = tile.a + pm * kRowStride + 32 * cc + 16 * h;
+        const uint8_t* gr = tile.b + pm * kRowStride + 32 * cc + 16 * h;
+        s = mfma_bf16(lds_u32x4(qr), kop[cc], s);
+        dp = mfma_bf16(lds_u32x4(gr), vop[cc], dp);
+        s2 = mfma_bf16(lds_u32x4(qr + 32), kop[cc + 1], s2);
+        dp2 = mfma_bf16(lds_u32x4(gr + 32), vop[cc + 1], dp2);
+      }
+      // this lane's 16 query rows: acc_row(r, h) = 8h + r (r < 8), 16 + 8h + r - 8
+      f32x4 l4[4], d4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r0 = 16 * (i >> 1) + 8 * h + 4 * (i & 1);
+        l4[i] = *(const f32x4*)(tile.s0 + r0);
+        d4[i] = *(const f32x4*)(tile.s1 + r0);
       }
       // P and dS; register r holds query q0 + acc_row(r, h) for this lane's key
       f32x16 p, ds;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qi = acc_row(r, h);
-        const float lse2 = tile.s0[qi];
-        float x = __builtin_fmaf(s[r], c, -lse2);
+        const float x = __builtin_fmaf(s[r] + s2[r], c, -l4[r >> 2][r & 3]);
         const bool vis = key < N && (!CAUSAL || key <= q0 + qi);
         const float pr = vis ? __builtin_amdgcn_exp2f(x) : 0.f;
         p[r] = pr;
-        ds[r] = pr * (dp[r] - tile.s1[qi]);
+        ds[r] = pr * (dp[r] + dp2[r] - d4[r >> 2][r & 3]);
       }
       // dV^T += dO^T P and dK^T += Q^T dS (d x keys), over the two 16-query chunks
 #pragma unroll
@@ -330,14 +340,16 @@ __global__ __launch_bounds__(kBThreads) void dq_kernel(
     __syncthreads();
     if (kt + 1 < nkt) stage_load(sr, K + khead * kBD, V + khead * kBD, k0 + kBTile, N);
     if (CAUSAL && k0 > qw0 + 31) continue;
-    // S^T = K_pi Q^T and dP^T = V_pi dO^T (keys x queries; rows permuted)
-    f32x16 s = zero16(), dp = zero16();
+    // S^T = K_pi Q^T and dP^T = V_pi dO^T (keys x queries; rows permuted), two chains each
+    f32x16 s = zero16(), dp = zero16(), s2 = zero16(), dp2 = zero16();
 #pragma unroll
-    for (int cc = 0; cc < kBD / 16; ++cc) {
-      const u32x4 ka = lds_u32x4(tile.a + pm * kRowStride + 32 * cc + 16 * h);
-      const u32x4 va = lds_u32x4(tile.b + pm * kRowStride + 32 * cc + 16 * h);
-      s = mfma_bf16(ka, qop[cc], s);
-      dp = mfma_bf16(va, gop[cc], dp);
+    for (int cc = 0; cc < kBD / 16; cc += 2) {
+      const uint8_t* kr = tile.a + pm * kRowStride + 32 * cc + 16 * h;
+      const uint8_t* vr = tile.b + pm * kRowStride + 32 * cc + 16 * h;
+      s = mfma_bf16(lds_u32x4(kr), qop[cc], s);
+      dp = mfma_bf16(lds_u32x4(vr), gop[cc], dp);
+      s2 = mfma_bf16(lds_u32x4(kr + 32), qop[cc + 1], s2);
+      dp2 = mfma_bf16(lds_u32x4(vr + 32), gop[cc + 1], dp2);
     }
     // dS^T; register r holds key k0 + acc_row(r, h) for this lane's query
     f32x16 ds;
@@ -345,8 +357,9 @@ __global__ __launch_bounds__(kBThreads) void dq_kernel(
     for (int r = 0; r < 16; ++r) {
       const int kj = k0 + acc_row(r, h);
       const bool vis = kj < N && qi < N && (!CAUSAL || kj <= qi);
-      const float pr = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2)) : 0.f;
-      ds[r] = pr * (dp[r] - dlt);
+      const float pr =
+          vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r] + s2[r], c, -lse2)) : 0.f;
+      ds[r] = pr * (dp[r] + dp2[r] - dlt);
     }
     // dQ^T += K^T dS^T (d x queries), over the two 16-key chunks
 #pragma unroll
