@@ -165,7 +165,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const float* o, const 
     return ATTN_EINVAL;
   int st = check_common(B, Hq, Hkv, N, d, causal, scale);
   if (st != ATTN_OK) return st;
-  if (d != 128) return ATTN_EUNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_EUNSUPPORTED;
   if ((long long)B * Hkv * ((N + 127) / 128) >= (1LL << 31) ||
       (long long)B * Hq * ((N + 127) / 128) >= (1LL << 31))
     return ATTN_EUNSUPPORTED;

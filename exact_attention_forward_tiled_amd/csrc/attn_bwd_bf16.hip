@@ -28,15 +28,11 @@
 namespace attn {
 namespace {
 
-constexpr int kBD = 128;                 // head dimension of this path
 constexpr int kBWaves = 4;
 constexpr int kBThreads = kBWaves * 64;
 constexpr int kBBlock = kBWaves * 32;    // keys (dK/dV) or queries (dQ) per workgroup
 constexpr int kBTile = 32;               // queries (dK/dV) or keys (dQ) per loop step
-constexpr int kRowStride = kBD * 2 + 16; // bytes per staged row (padded)
 constexpr int kColStride = kBTile * 2 + 16;  // bytes per staged transposed column (padded)
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int perm_row(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
@@ -56,36 +52,42 @@ __device__ __forceinline__ u32x4 pack_chunk(const f32x16& x, int c) {
   return r;
 }
 
-// Staged tile: 32 rows x 128 bf16 of two tensors, row-major and transposed.
+// Staged tile: 32 rows x D bf16 of two tensors, row-major (rows padded by 16 bytes: the
+// 16 rows read together start 4 banks apart) and transposed.
+template <int D>
 struct alignas(16) BTile {
+  static constexpr int kRow = D * 2 + 16;   // bytes per staged row
   float s0[kBTile];                   // per-row scalars (LSE, D) of the dK/dV tile
   float s1[kBTile];
-  uint8_t a[kBTile * kRowStride];     // tensor A, row r at r * kRowStride
-  uint8_t b[kBTile * kRowStride];     // tensor B
-  uint8_t at[kBD * kColStride];       // A transposed: column d at d * kColStride, 32 rows
-  uint8_t bt[kBD * kColStride];       // B transposed
+  uint8_t a[kBTile * kRow];           // tensor A, row r at r * kRow
+  uint8_t b[kBTile * kRow];           // tensor B
+  uint8_t at[D * kColStride];         // A transposed: column d at d * kColStride, 32 rows
+  uint8_t bt[D * kColStride];         // B transposed
 };
 
-// One thread's share of a staged tile pair: 2 units of 16 bytes of each tensor.  Unit u
-// is row u % 32, bytes 16 * (u / 32) .. + 15, so the 32 lanes of a half-wave take 32
-// consecutive rows: their 2-byte writes into the transposed copy fall on 32 distinct
+// One thread's share of a staged tile pair: D / 64 units of 16 bytes of each tensor.
+// Unit u is row u % 32, bytes 16 * (u / 32) .. + 15, so the 32 lanes of a half-wave take
+// 32 consecutive rows: their 2-byte writes into the transposed copy fall on 32 distinct
 // dwords of one column instead of piling onto two banks.
+template <int D>
 struct StageRegs {
-  u32x4 a[2], b[2];
+  static constexpr int kUnits = D / 64;
+  u32x4 a[kUnits], b[kUnits];
 };
 
-// Fetch rows r0 .. r0 + 31 of two [N, 128] bf16 tensors into registers (rows past N read
+// Fetch rows r0 .. r0 + 31 of two [N, D] bf16 tensors into registers (rows past N read
 // as row N - 1: in bounds; their contributions are masked by the caller).
-__device__ __forceinline__ void stage_load(StageRegs& sr, const uint16_t* A, const uint16_t* B,
-                                           int r0, int N) {
+template <int D>
+__device__ __forceinline__ void stage_load(StageRegs<D>& sr, const uint16_t* A,
+                                           const uint16_t* B, int r0, int N) {
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < StageRegs<D>::kUnits; ++u) {
     const int unit = tid + u * kBThreads;
     const int row = unit & 31, c16 = unit >> 5;
     const int gr = min(r0 + row, N - 1);
-    sr.a[u] = *(const u32x4*)(A + (size_t)gr * kBD + 8 * c16);
-    sr.b[u] = *(const u32x4*)(B + (size_t)gr * kBD + 8 * c16);
+    sr.a[u] = *(const u32x4*)(A + (size_t)gr * D + 8 * c16);
+    sr.b[u] = *(const u32x4*)(B + (size_t)gr * D + 8 * c16);
   }
 }
 
@@ -96,15 +98,16 @@ __device__ __forceinline__ void put_transposed(uint8_t* t, const u32x4& v, int r
 }
 
 // Write the fetched rows into LDS: both tensors row-major, and transposed where asked.
-__device__ __forceinline__ void stage_store(BTile& t, const StageRegs& sr, bool transposed_a,
-                                            bool transposed_b) {
+template <int D>
+__device__ __forceinline__ void stage_store(BTile<D>& t, const StageRegs<D>& sr,
+                                            bool transposed_a, bool transposed_b) {
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < StageRegs<D>::kUnits; ++u) {
     const int unit = tid + u * kBThreads;
     const int row = unit & 31, c16 = unit >> 5;
-    *(u32x4*)(t.a + row * kRowStride + 16 * c16) = sr.a[u];
-    *(u32x4*)(t.b + row * kRowStride + 16 * c16) = sr.b[u];
+    *(u32x4*)(t.a + row * BTile<D>::kRow + 16 * c16) = sr.a[u];
+    *(u32x4*)(t.b + row * BTile<D>::kRow + 16 * c16) = sr.b[u];
     if (transposed_a) put_transposed(t.at, sr.a[u], row, c16);
     if (transposed_b) put_transposed(t.bt, sr.b[u], row, c16);
   }
@@ -112,15 +115,17 @@ __device__ __forceinline__ void stage_store(BTile& t, const StageRegs& sr, bool 
 
 __device__ __forceinline__ u32x4 lds_u32x4(const uint8_t* p) { return *(const u32x4*)p; }
 
-// D_i = dO_i . O_i, 16 threads per row.
+// D_i = dO_i . O_i, HD / 8 threads per row (8 elements each).
+template <int HD>
 __global__ void delta_kernel(const float* __restrict__ O, const uint16_t* __restrict__ dO,
                              float* __restrict__ D, long long rows) {
-  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int part = threadIdx.x & 15;
+  constexpr int kParts = HD / 8;
+  const long long row = (long long)blockIdx.x * (256 / kParts) + (threadIdx.x / kParts);
+  const int part = threadIdx.x % kParts;
   float acc = 0.f;
   if (row < rows) {
-    const f32x4* o = (const f32x4*)(O + row * kBD + 8 * part);
-    const u32x4 g = *(const u32x4*)(dO + row * kBD + 8 * part);
+    const f32x4* o = (const f32x4*)(O + row * HD + 8 * part);
+    const u32x4 g = *(const u32x4*)(dO + row * HD + 8 * part);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const f32x4 ov = o[i];
@@ -133,20 +138,20 @@ __global__ void delta_kernel(const float* __restrict__ O, const uint16_t* __rest
     }
   }
 #pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
+  for (int off = kParts / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, kParts);
   if (row < rows && part == 0) D[row] = acc;
 }
 
 // dK, dV for 128 keys of one (batch, kv head): each wave owns 32 keys; the loop runs
 // over the group's query heads and their 32-query blocks (causal: only blocks that
 // reach the workgroup's keys).
-template <bool CAUSAL>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ D, float* __restrict__ dK,
+    const float* __restrict__ LSE, const float* __restrict__ Delta, float* __restrict__ dK,
     float* __restrict__ dV, int Hq, int Hkv, int N, int nkb, float c, float scale) {
-  __shared__ BTile tile;
+  __shared__ BTile<D> tile;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n32 = lane & 31, h = lane >> 5;
   const int kb = blockIdx.x % nkb;
@@ -159,20 +164,20 @@ __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
 
   const size_t khead = (size_t)(b * Hkv + hkv) * N;
   // K^T and V^T as B operands: lane holds K[key][16c + 8h .. +7] for each d chunk c
-  u32x4 kop[kBD / 16], vop[kBD / 16];
+  u32x4 kop[D / 16], vop[D / 16];
   {
     const int kr = min(key, N - 1);
-    const uint16_t* krow = K + (khead + kr) * kBD;
-    const uint16_t* vrow = V + (khead + kr) * kBD;
+    const uint16_t* krow = K + (khead + kr) * D;
+    const uint16_t* vrow = V + (khead + kr) * D;
 #pragma unroll
-    for (int cc = 0; cc < kBD / 16; ++cc) {
+    for (int cc = 0; cc < D / 16; ++cc) {
       kop[cc] = *(const u32x4*)(krow + 16 * cc + 8 * h);
       vop[cc] = *(const u32x4*)(vrow + 16 * cc + 8 * h);
     }
   }
-  f32x16 dk[kBD / 32], dv[kBD / 32];
+  f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
-  for (int i = 0; i < kBD / 32; ++i) {
+  for (int i = 0; i < D / 32; ++i) {
     dk[i] = zero16();
     dv[i] = zero16();
   }
@@ -189,17 +194,17 @@ __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
     q0 = (qt0 + st % steps_per_head) * kBTile;
     qh = (size_t)(b * Hq + hkv * group + g) * N;
   };
-  StageRegs sr;
+  StageRegs<D> sr;
   float lse_next = 0.f, d_next = 0.f;
   auto fetch = [&](int st) {
     size_t qh;
     int q0;
     step_rows(st, qh, q0);
-    stage_load(sr, Q + qh * kBD, dO + qh * kBD, q0, N);
+    stage_load(sr, Q + qh * D, dO + qh * D, q0, N);
     if (tid < kBTile) {
       const int qr = q0 + tid;
       lse_next = qr < N ? LSE[qh + qr] : -__builtin_inff();
-      d_next = qr < N ? D[qh + qr] : 0.f;
+      d_next = qr < N ? Delta[qh + qr] : 0.f;
     }
   };
   if (nsteps > 0) fetch(0);
@@ -223,9 +228,9 @@ __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
       // accumulation chains over alternate d chunks so that four MFMA chains overlap
       f32x16 s = zero16(), dp = zero16(), s2 = zero16(), dp2 = zero16();
 #pragma unroll
-      for (int cc = 0; cc < kBD / 16; cc += 2) {
-        const uint8_t* qr = tile.a + pm * kRowStride + 32 * cc + 16 * h;
-        const uint8_t* gr = tile.b + pm * kRowStride + 32 * cc + 16 * h;
+      for (int cc = 0; cc < D / 16; cc += 2) {
+        const uint8_t* qr = tile.a + pm * BTile<D>::kRow + 32 * cc + 16 * h;
+        const uint8_t* gr = tile.b + pm * BTile<D>::kRow + 32 * cc + 16 * h;
         s = mfma_bf16(lds_u32x4(qr), kop[cc], s);
         dp = mfma_bf16(lds_u32x4(gr), vop[cc], dp);
         s2 = mfma_bf16(lds_u32x4(qr + 32), kop[cc + 1], s2);
@@ -255,7 +260,7 @@ __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
       for (int q2 = 0; q2 < 2; ++q2) {
         const u32x4 pb = pack_chunk(p, q2), db = pack_chunk(ds, q2);
 #pragma unroll
-        for (int dbk = 0; dbk < kBD / 32; ++dbk) {
+        for (int dbk = 0; dbk < D / 32; ++dbk) {
           const int dcol = 32 * dbk + n32;
           const u32x4 gta = lds_u32x4(tile.bt + dcol * kColStride + 32 * q2 + 16 * h);
           const u32x4 qta = lds_u32x4(tile.at + dcol * kColStride + 32 * q2 + 16 * h);
@@ -267,10 +272,10 @@ __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
   }
   // dK = scale * (dK^T)^T, dV = (dV^T)^T: lane holds d 32dbk + 8a + 4h + 0..3 of its key
   if (key < N) {
-    float* dkrow = dK + (khead + key) * kBD;
-    float* dvrow = dV + (khead + key) * kBD;
+    float* dkrow = dK + (khead + key) * D;
+    float* dvrow = dV + (khead + key) * D;
 #pragma unroll
-    for (int dbk = 0; dbk < kBD / 32; ++dbk)
+    for (int dbk = 0; dbk < D / 32; ++dbk)
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         const int col = 32 * dbk + 8 * a4 + 4 * h;
@@ -286,13 +291,13 @@ __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
 
 // dQ for 128 queries of one (batch, query head): each wave owns 32 queries; the loop
 // runs over 32-key blocks (causal: up to the workgroup's last query).
-template <bool CAUSAL>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBThreads) void dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ D, float* __restrict__ dQ,
+    const float* __restrict__ LSE, const float* __restrict__ Delta, float* __restrict__ dQ,
     int Hq, int Hkv, int N, int nqb, float c, float scale) {
-  __shared__ BTile tile;
+  __shared__ BTile<D> tile;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n32 = lane & 31, h = lane >> 5;
   const int qb = blockIdx.x % nqb;
@@ -306,46 +311,46 @@ __global__ __launch_bounds__(kBThreads) void dq_kernel(
   const size_t qhead = (size_t)(b * Hq + hq) * N;
   const size_t khead = (size_t)(b * Hkv + hkv) * N;
   // Q^T and dO^T as B operands: lane holds Q[qi][16c + 8h .. +7]
-  u32x4 qop[kBD / 16], gop[kBD / 16];
+  u32x4 qop[D / 16], gop[D / 16];
   float lse2 = __builtin_inff(), dlt = 0.f;
   {
     const int qr = min(qi, N - 1);
-    const uint16_t* qrow = Q + (qhead + qr) * kBD;
-    const uint16_t* grow = dO + (qhead + qr) * kBD;
+    const uint16_t* qrow = Q + (qhead + qr) * D;
+    const uint16_t* grow = dO + (qhead + qr) * D;
 #pragma unroll
-    for (int cc = 0; cc < kBD / 16; ++cc) {
+    for (int cc = 0; cc < D / 16; ++cc) {
       qop[cc] = *(const u32x4*)(qrow + 16 * cc + 8 * h);
       gop[cc] = *(const u32x4*)(grow + 16 * cc + 8 * h);
     }
     if (qi < N) {
       const float l = LSE[qhead + qi];
       lse2 = (l == -__builtin_inff()) ? __builtin_inff() : l * kLog2e;
-      dlt = D[qhead + qi];
+      dlt = Delta[qhead + qi];
     }
   }
-  f32x16 dq[kBD / 32];
+  f32x16 dq[D / 32];
 #pragma unroll
-  for (int i = 0; i < kBD / 32; ++i) dq[i] = zero16();
+  for (int i = 0; i < D / 32; ++i) dq[i] = zero16();
 
   const int kend = CAUSAL ? min(N, Q0 + kBBlock) : N;
   const int nkt = (kend + kBTile - 1) / kBTile;
   const int pm = perm_row(n32);
   // the next key tile is fetched into registers while the current one computes
-  StageRegs sr;
-  if (nkt > 0) stage_load(sr, K + khead * kBD, V + khead * kBD, 0, N);
+  StageRegs<D> sr;
+  if (nkt > 0) stage_load(sr, K + khead * D, V + khead * D, 0, N);
   for (int kt = 0; kt < nkt; ++kt) {
     const int k0 = kt * kBTile;
     __syncthreads();
     stage_store(tile, sr, true, false);
     __syncthreads();
-    if (kt + 1 < nkt) stage_load(sr, K + khead * kBD, V + khead * kBD, k0 + kBTile, N);
+    if (kt + 1 < nkt) stage_load(sr, K + khead * D, V + khead * D, k0 + kBTile, N);
     if (CAUSAL && k0 > qw0 + 31) continue;
     // S^T = K_pi Q^T and dP^T = V_pi dO^T (keys x queries; rows permuted), two chains each
     f32x16 s = zero16(), dp = zero16(), s2 = zero16(), dp2 = zero16();
 #pragma unroll
-    for (int cc = 0; cc < kBD / 16; cc += 2) {
-      const uint8_t* kr = tile.a + pm * kRowStride + 32 * cc + 16 * h;
-      const uint8_t* vr = tile.b + pm * kRowStride + 32 * cc + 16 * h;
+    for (int cc = 0; cc < D / 16; cc += 2) {
+      const uint8_t* kr = tile.a + pm * BTile<D>::kRow + 32 * cc + 16 * h;
+      const uint8_t* vr = tile.b + pm * BTile<D>::kRow + 32 * cc + 16 * h;
       s = mfma_bf16(lds_u32x4(kr), qop[cc], s);
       dp = mfma_bf16(lds_u32x4(vr), gop[cc], dp);
       s2 = mfma_bf16(lds_u32x4(kr + 32), qop[cc + 1], s2);
@@ -366,7 +371,7 @@ __global__ __launch_bounds__(kBThreads) void dq_kernel(
     for (int k2 = 0; k2 < 2; ++k2) {
       const u32x4 db = pack_chunk(ds, k2);
 #pragma unroll
-      for (int dbk = 0; dbk < kBD / 32; ++dbk) {
+      for (int dbk = 0; dbk < D / 32; ++dbk) {
         const int dcol = 32 * dbk + n32;
         const u32x4 kta = lds_u32x4(tile.at + dcol * kColStride + 32 * k2 + 16 * h);
         dq[dbk] = mfma_bf16(kta, db, dq[dbk]);
@@ -374,9 +379,9 @@ __global__ __launch_bounds__(kBThreads) void dq_kernel(
     }
   }
   if (qi < N) {
-    float* row = dQ + (qhead + qi) * kBD;
+    float* row = dQ + (qhead + qi) * D;
 #pragma unroll
-    for (int dbk = 0; dbk < kBD / 32; ++dbk)
+    for (int dbk = 0; dbk < D / 32; ++dbk)
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         f32x4 v = {dq[dbk][4 * a4] * scale, dq[dbk][4 * a4 + 1] * scale,
@@ -386,22 +391,24 @@ __global__ __launch_bounds__(kBThreads) void dq_kernel(
   }
 }
 
-template <bool CAUSAL>
+template <int D, bool CAUSAL>
 hipError_t launch_bwd_t(const BwdArgs& a) {
   const long long rows = (long long)a.B * a.Hq * a.N;
-  hipLaunchKernelGGL(delta_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0,
-                     (hipStream_t)a.stream, a.o, (const uint16_t*)a.dout, a.delta, rows);
+  constexpr int kRowsPerBlock = 256 / (D / 8);
+  hipLaunchKernelGGL(delta_kernel<D>, dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)),
+                     dim3(256), 0, (hipStream_t)a.stream, a.o, (const uint16_t*)a.dout, a.delta,
+                     rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nb = (a.N + kBBlock - 1) / kBBlock;
-  hipLaunchKernelGGL((dkdv_kernel<CAUSAL>), dim3((unsigned)(a.B * a.Hkv * nb)), dim3(kBThreads),
-                     0, (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                     (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta, a.dk, a.dv,
-                     a.Hq, a.Hkv, a.N, nb, a.c, a.scale);
+  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL>), dim3((unsigned)(a.B * a.Hkv * nb)),
+                     dim3(kBThreads), 0, (hipStream_t)a.stream, (const uint16_t*)a.q,
+                     (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse,
+                     a.delta, a.dk, a.dv, a.Hq, a.Hkv, a.N, nb, a.c, a.scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((dq_kernel<CAUSAL>), dim3((unsigned)(a.B * a.Hq * nb)), dim3(kBThreads), 0,
-                     (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+  hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3((unsigned)(a.B * a.Hq * nb)), dim3(kBThreads),
+                     0, (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                      (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta, a.dq,
                      a.Hq, a.Hkv, a.N, nb, a.c, a.scale);
   return hipGetLastError();
@@ -410,8 +417,9 @@ hipError_t launch_bwd_t(const BwdArgs& a) {
 }  // namespace
 
 hipError_t launch_bwd_bf16(const BwdArgs& a) {
-  if (a.d != kBD) return hipErrorNotSupported;
-  return a.causal ? launch_bwd_t<true>(a) : launch_bwd_t<false>(a);
+  if (a.d == 128) return a.causal ? launch_bwd_t<128, true>(a) : launch_bwd_t<128, false>(a);
+  if (a.d == 64) return a.causal ? launch_bwd_t<64, true>(a) : launch_bwd_t<64, false>(a);
+  return hipErrorNotSupported;
 }
 
 }  // namespace attn

@@ -43,7 +43,7 @@ struct MxArgs {
   void* stream;
 };
 
-// bf16 backward (d = 128): gradients of the forward from its saved O and LSE.
+// bf16 backward (d = 64 or 128): gradients of the forward from its saved O and LSE.
 struct BwdArgs {
   const void* q;        // bf16 [B, Hq, N, d]
   const void* k;        // bf16 [B, Hkv, N, d]

@@ -216,7 +216,7 @@ int attn_quantize_mxfp8_cols_t(const float* x, uint8_t* codes, uint8_t* scales,
  *   [B, Hq, N] as written by attn_fwd on the same inputs; dout bf16 [B, Hq, N, d];
  *   dq fp32 [B, Hq, N, d], dk, dv fp32 [B, Hkv, N, d] (outputs, every element written);
  *   delta: caller-owned device workspace of B*Hq*N floats (overwritten; holds D afterwards).
- *   d = 128 (else ATTN_EUNSUPPORTED); any N >= 1; causal in {0, 1}; scale finite.
+ *   d in {64, 128} (else ATTN_EUNSUPPORTED); any N >= 1; causal in {0, 1}; scale finite.
  *   Three kernels are queued on `stream` (null: the null stream); no atomics, so the
  *   results are deterministic.
  */

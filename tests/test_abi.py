@@ -134,7 +134,7 @@ def test_mxfp8_validation(fa):
 
 def test_bwd_validation(fa):
     base = [FAKE] * 10
-    assert fa.attn_bwd(*base, 1, 2, 2, 64, 64, 0, 0.1) == -2            # d must be 128
+    assert fa.attn_bwd(*base, 1, 2, 2, 64, 96, 0, 0.1) == -2            # d in {64, 128}
     assert fa.attn_bwd(*base, 1, 3, 2, 64, 128, 0, 0.1) == -1           # Hq % Hkv
     assert fa.attn_bwd(*base, 1, 2, 2, 0, 128, 0, 0.1) == -1            # N >= 1
     assert fa.attn_bwd(*base, 1, 2, 2, 64, 128, 3, 0.1) == -1           # causal in {0, 1}

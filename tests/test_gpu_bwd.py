@@ -57,8 +57,11 @@ def _check(got, ref, tag):
 
 
 SMALL = [
-    # B, Hq, Hkv, N, causal
+    # B, Hq, Hkv, N, causal[, d]
     (1, 2, 2, 128, False),
+    (1, 2, 2, 256, False, 64),
+    (1, 4, 2, 190, True, 64),
+    (1, 1, 1, 1, True, 64),
     (1, 2, 2, 128, True),
     (1, 1, 1, 1, False),
     (1, 1, 1, 1, True),
@@ -70,12 +73,13 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("case", SMALL, ids=lambda c: "B%dHq%dHkv%dN%d%s" % (
-    c[0], c[1], c[2], c[3], "c" if c[4] else "n"))
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "B%dHq%dHkv%dN%d%sd%d" % (
+    c[0], c[1], c[2], c[3], "c" if c[4] else "n", c[5] if len(c) > 5 else 128))
 def test_bwd_small(case):
-    B, Hq, Hkv, N, causal = case
-    bits, (q, k, v, g) = _case(sum(case[:4]) + 11, B, Hq, Hkv, N)
-    scale = 1.0 / math.sqrt(128)
+    B, Hq, Hkv, N, causal = case[:5]
+    d = case[5] if len(case) > 5 else 128
+    bits, (q, k, v, g) = _case(sum(case[:4]) + 11, B, Hq, Hkv, N, d)
+    scale = 1.0 / math.sqrt(d)
     o, lse = oracle.attention(q, k, v, causal, scale)
     ref = bw.attention_backward(q, k, v, g, causal, scale, o=o, lse=lse)
     log(f"bwd case {case}")
