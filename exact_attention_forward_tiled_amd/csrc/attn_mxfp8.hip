@@ -173,8 +173,9 @@ __device__ __forceinline__ i32x8 fp8_operand(const u32x4& lo, const u32x4& hi) {
 struct F8Buf {
   uint8_t kcode[k8Bc * k8KStride];   // K row r at kpos8(r) * 144, 128 code bytes
   uint8_t vcode[k8D * k8VStride];    // V^T column c at c * 80, 64 code bytes (keys)
-  uint32_t kscale[k8Bc];             // 4 scale bytes per key row
-  uint8_t vscale[k8D * 2];           // byte (col*2 + h): scale of key block h of column col
+  // scale bytes: [0, 256) K, byte 4r + b = scale of d block b of key row r;
+  // [256, 512) V^T, byte 256 + 2c + h = scale of key block h of column c
+  uint8_t scale[4 * k8Bc + 2 * k8D];
 };
 
 __device__ __forceinline__ u32x4 lds16(const uint8_t* p) { return *(const u32x4*)p; }
@@ -183,7 +184,7 @@ __device__ __forceinline__ void sts16(uint8_t* p, const u32x4& v) { *(u32x4*)p =
 struct F8Stage {
   u32x4 k;       // K codes: row tid/8, chunk tid%8
   u32x4 v;       // V^T codes: column tid/4, chunk tid%4
-  uint32_t sc;   // tid < 64: K scales of row tid; 64 <= tid < 192: V scales of col tid-64
+  uint32_t sc;   // scale byte tid of the tile (F8Buf::scale layout)
 };
 
 // Weights of one 64-key tile for this lane (32 keys: its P scale block).  Returns
@@ -336,6 +337,10 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict_
   // Stage t (read by pipeline step t from buffer t & 1) holds K tile t+1 and V tile t-1.
   // The loads are unconditional, with the tile index clamped into [0, n) (in bounds;
   // a stage past the tiles is loaded but never stored).
+  // Every thread stages one code unit of K, one of V^T and one scale byte; the loads are
+  // unconditional, with the tile index clamped into [0, n) (in bounds), and so are the
+  // stores: a stage past the tiles lands in a buffer half no later product reads.  The
+  // scale's source (K or V^T) is a wave-uniform select, so the step has no branches.
   auto load_stage = [&](F8Stage& sg, int t) {
     const int kt = min(t + 1, n - 1), vt = max(min(t - 1, n - 1), 0);
     const int kk0 = kt * k8Bc, vk0 = vt * k8Bc;
@@ -344,31 +349,21 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict_
     // keys past N in the last tile read the next column's codes (finite; they meet zero
     // weights) or, past the head, zeros from the range check
     sg.v = __builtin_amdgcn_raw_buffer_load_b128(rvt, vcs * N + vk0 + 16 * vch, 0, 0);
-    if (wave == 0) {
-      const __amdgpu_buffer_rsrc_t rs = rsrc8(KSh + (size_t)kk0 * k8ScaleRow, (N - kk0) * k8ScaleRow);
-      sg.sc = __builtin_amdgcn_raw_buffer_load_b32(rs, tid * k8ScaleRow, 0, 0);
-    } else if (wave < 3) {
-      const int col = tid - 64;
-      const uint32_t b0 = __builtin_amdgcn_raw_buffer_load_b8(rvs, col * nvb + vk0 / 32, 0, 0);
-      // a key block past N gets a neutral scale; the load reads block 0 then (in range)
-      const uint32_t b1 = __builtin_amdgcn_raw_buffer_load_b8(
-          rvs, col * nvb + (vk0 + 32 < N ? vk0 / 32 + 1 : 0), 0, 0);
-      sg.sc = b0 | ((vk0 + 32 < N ? b1 : 127u) << 8);
-    }
+    const bool kpart = wave < 4;                      // tid < 256: a K scale byte
+    const int u = tid - 256, col = u >> 1, hb = u & 1;
+    // a V key block past N gets a neutral scale; the load reads block 0 then (in range)
+    const bool past = vk0 + 32 * hb >= N;
+    const __amdgpu_buffer_rsrc_t rs =
+        kpart ? rsrc8(KSh + (size_t)kk0 * k8ScaleRow, (N - kk0) * k8ScaleRow) : rvs;
+    const int off = kpart ? tid : col * nvb + (past ? 0 : vk0 / 32 + hb);
+    const uint32_t byte = __builtin_amdgcn_raw_buffer_load_b8(rs, off, 0, 0);
+    sg.sc = (!kpart && past) ? 127u : byte;
   };
   auto store_stage = [&](const F8Stage& sg, int t) {
     F8Buf& bb = buf[t & 1];
-    if (t + 1 < n) sts16(bb.kcode + kpos8(krs) * k8KStride + 16 * kcs, sg.k);
-    if (t >= 1 && t - 1 < n) sts16(bb.vcode + vcs * k8VStride + 16 * vch, sg.v);
-    if (wave == 0) {
-      if (t + 1 < n) bb.kscale[tid] = sg.sc;
-    } else if (wave < 3) {
-      if (t >= 1 && t - 1 < n) {
-        const int col = tid - 64;
-        bb.vscale[col * 2] = (uint8_t)(sg.sc & 0xFF);
-        bb.vscale[col * 2 + 1] = (uint8_t)(sg.sc >> 8);
-      }
-    }
+    sts16(bb.kcode + kpos8(krs) * k8KStride + 16 * kcs, sg.k);
+    sts16(bb.vcode + vcs * k8VStride + 16 * vch, sg.v);
+    bb.scale[tid] = (uint8_t)sg.sc;
   };
 
   // per-lane LDS byte offsets of the operand reads (chunk and column-block offsets
@@ -389,7 +384,7 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict_
         const int col = 32 * cb + n32;
         const uint8_t* vp = bb.vcode + va + 32 * cb * k8VStride;
         const u32x4 v0 = lds16(vp), v1 = lds16(vp + 32);
-        const int vs = bb.vscale[col * 2 + h];
+        const int vs = bb.scale[4 * k8Bc + col * 2 + h];
         acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp8_operand(v0, v1), bp,
                                                                   acc[cb], 0, 0, 0, vs, 0,
                                                                   (int)ep);
@@ -403,7 +398,7 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict_
       for (int mb = 0; mb < 2; ++mb) {
         const int row = mb ? kr1 : kr0;
         const uint8_t* kp = bb.kcode + (mb ? ka1 : ka0);
-        const int ksc = (int)(bb.kscale[row] >> (8 * h));
+        const int ksc = (int)(*(const uint32_t*)(bb.scale + 4 * row) >> (8 * h));
         // d elements 0..63 (scale byte 0 of the shifted scale words), then 64..127 (byte 2)
         const u32x4 a00 = lds16(kp), a01 = lds16(kp + 32);
         const u32x4 a10 = lds16(kp + 64), a11 = lds16(kp + 96);
@@ -419,18 +414,15 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict_
   // ---- prologue: K tile 0 -> buffer 1; stage 0 -> buffer 0; stage 1 in registers ----
   F8Stage stg;
   {
-    const __amdgpu_buffer_rsrc_t rk = rsrc8(K8h, N * k8CodeRow);
-    const u32x4 k0 = __builtin_amdgcn_raw_buffer_load_b128(rk, krs * k8CodeRow + kcs * 16, 0, 0);
-    uint32_t ks0 = 0;
-    if (wave == 0)
-      ks0 = __builtin_amdgcn_raw_buffer_load_b32(rsrc8(KSh, N * k8ScaleRow), tid * k8ScaleRow, 0, 0);
+    F8Stage s0;
+    load_stage(s0, -1);            // K tile 0 (its V half is overwritten below)
     load_stage(stg, 0);
-    sts16(buf[1].kcode + kpos8(krs) * k8KStride + 16 * kcs, k0);
-    if (wave == 0) buf[1].kscale[tid] = ks0;
-    store_stage(stg, 0);
-    // no V tile precedes tile 0: zero codes, neutral scales
+    store_stage(s0, 1);            // buffer 1: K tile 0 and its scales
+    store_stage(stg, 0);           // buffer 0: K tile 1
+    // no V tile precedes tile 0: zero codes and neutral scales, written by the same
+    // threads that stored this half just above
     sts16(buf[0].vcode + vcs * k8VStride + 16 * vch, u32x4{0u, 0u, 0u, 0u});
-    if (tid < k8D * 2) buf[0].vscale[tid] = 127;
+    if (!(wave < 4)) buf[0].scale[tid] = 127;
   }
   load_stage(stg, 1);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -465,13 +457,10 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict_
       any = fp8p_tile<CAUSAL, false>(sc, pc, ec, m, alpha, j * k8Bc, qi, N, c, tau, h);
     any_prev = any;
     alpha_prev = alpha;
-    if (active(j)) {
-      if (!first) {
-        ++n_steps;
-        n_rescales += any ? 1u : 0u;
-      }
-      first = false;
-    }
+    const bool counted = active(j) && !first;   // branch-free: uniform selects
+    n_steps += counted ? 1u : 0u;
+    n_rescales += (counted && any) ? 1u : 0u;
+    first = first && !active(j);
     store_stage(stg, j + 1);
     load_stage(stg, j + 2);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
