@@ -155,15 +155,17 @@ __device__ __forceinline__ i32x8 fp4_operand(u32x4 v) {
 }
 
 struct MBuf {
-  u32x4 kcode[kMBc * kCodeRow / 16];     // 256 units: unit(row, c) = row*4 + (c ^ kswz(row))
-  u32x4 vcode[kMD * 2];                  // 256 units: unit(col, h) = col*2 + (h ^ ((col>>3)&1))
-  uint32_t kscale[kMBc];                 // 4 scale bytes per key row
-  uint8_t vscale[kMD * 2];               // byte (col*2 + h): scale of key block h of column col
+  // code units: [0, 256) K, unit(row, c) = row*4 + (c ^ kswz(row));
+  //             [256, 512) V^T, 256 + unit(col, h) = 256 + col*2 + (h ^ ((col>>3)&1))
+  u32x4 code[2 * 256];
+  // scale bytes: [0, 256) K, byte 4r + b = scale of d block b of key row r;
+  //              [256, 512) V^T, byte 256 + 2c + h = scale of key block h of column c
+  uint8_t scale[4 * kMBc + 2 * kMD];
 };
 
 struct MStage {
   u32x4 codes;     // tid < 256: K codes (row tid/4, chunk tid%4); else V^T codes (col, half)
-  uint32_t sc;     // tid < 64: K scales of row tid; 64 <= tid < 192: V scales of col tid-64
+  uint32_t sc;     // scale byte tid of the tile (MBuf::scale layout)
 };
 
 // Direct-P mapping of one 64-key tile for this lane (32 keys: its P scale block).
@@ -237,9 +239,8 @@ void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict_
   __shared__ MBuf buf[2];
   const float NEG_INF = -__builtin_inff();
   const int tid = threadIdx.x, lane = tid & 63;
-  // wave index through readfirstlane: the staging roles below are whole waves (K codes:
-  // waves 0-3, V^T codes: 4-7, K scales: wave 0, V^T scales: waves 1-2), and the
-  // compiler then turns them into scalar branches instead of masked execution
+  // wave index through readfirstlane: the staging roles below (K codes: waves 0-3, V^T
+  // codes: 4-7) are whole waves, so their selects are scalar
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n32 = lane & 31, h = lane >> 5;
 
@@ -294,55 +295,35 @@ void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict_
   auto active = [&](int j) { return wave_live && j * kMBc < wave_end; };
 
   // Stage t (read by pipeline step t from buffer t & 1) holds K tile t+1 and V tile t-1.
-  // The loads are unconditional, with the tile index clamped into [0, n) (in bounds;
-  // a stage past the tiles is loaded but never stored): a skipped load would make the
-  // compiler keep the old register values alive and wait for the new ones later.
+  // Every thread stages one code unit (K for waves 0-3, V^T for waves 4-7) and one scale
+  // byte, choosing the source by wave-uniform selects, so a pipeline step has no branches
+  // and is one scheduling region.  The loads are unconditional, with the tile index
+  // clamped into [0, n) (in bounds), and so are the stores: a stage past the tiles lands
+  // in a buffer half that no later product reads.
+  const bool kpart = wave < 4;
+  const int su = tid - 256, scol = su >> 1, shh = su & 1;        // V^T unit of waves 4-7
+  const int code_slot = kpart ? (tid >> 2) * 4 + ((tid & 3) ^ kswz(tid >> 2))
+                              : 256 + scol * 2 + (shh ^ ((scol >> 3) & 1));
   auto load_stage = [&](MStage& sg, int t) {
     const int kt = min(t + 1, n - 1), vt = max(min(t - 1, n - 1), 0);
-    if (wave < 4) {
-      const int kv0 = kt * kMBc;
-      const __amdgpu_buffer_rsrc_t rk = mrsrc(K4h + (size_t)kv0 * kCodeRow, (N - kv0) * kCodeRow);
-      sg.codes = __builtin_amdgcn_raw_buffer_load_b128(rk, (tid >> 2) * kCodeRow + (tid & 3) * 16,
-                                                       0, 0);
-    } else {
-      const int kv0 = vt * kMBc, u = tid - 256;
-      sg.codes = __builtin_amdgcn_raw_buffer_load_b128(
-          rvt, (u >> 1) * (N / 2) + kv0 / 2 + 16 * (u & 1), 0, 0);
-    }
-    if (wave == 0) {
-      const int kv0 = kt * kMBc;
-      const __amdgpu_buffer_rsrc_t rs = mrsrc(KSh + (size_t)kv0 * kScaleRow, (N - kv0) * kScaleRow);
-      sg.sc = __builtin_amdgcn_raw_buffer_load_b32(rs, tid * kScaleRow, 0, 0);
-    } else if (wave < 3) {
-      const int kv0 = vt * kMBc, col = tid - 64;
-      const uint32_t b0 = __builtin_amdgcn_raw_buffer_load_b8(rvs, col * nvb + kv0 / 32, 0, 0);
-      // a key block past N gets a neutral scale (its codes meet zero P codes); the load
-      // reads block 0 then, which is in range
-      const uint32_t b1 = __builtin_amdgcn_raw_buffer_load_b8(
-          rvs, col * nvb + (kv0 + 32 < N ? kv0 / 32 + 1 : 0), 0, 0);
-      sg.sc = b0 | ((kv0 + 32 < N ? b1 : 127u) << 8);
-    }
+    const int kk0 = kt * kMBc, vk0 = vt * kMBc;
+    const __amdgpu_buffer_rsrc_t rk = mrsrc(K4h + (size_t)kk0 * kCodeRow, (N - kk0) * kCodeRow);
+    sg.codes = __builtin_amdgcn_raw_buffer_load_b128(
+        kpart ? rk : rvt,
+        kpart ? (tid >> 2) * kCodeRow + (tid & 3) * 16 : scol * (N / 2) + vk0 / 2 + 16 * shh,
+        0, 0);
+    // a V key block past N gets a neutral scale; the load reads block 0 then (in range)
+    const bool past = vk0 + 32 * shh >= N;
+    const __amdgpu_buffer_rsrc_t rs =
+        kpart ? mrsrc(KSh + (size_t)kk0 * kScaleRow, (N - kk0) * kScaleRow) : rvs;
+    const int off = kpart ? tid : scol * nvb + (past ? 0 : vk0 / 32 + shh);
+    const uint32_t byte = __builtin_amdgcn_raw_buffer_load_b8(rs, off, 0, 0);
+    sg.sc = (!kpart && past) ? 127u : byte;
   };
   auto store_stage = [&](const MStage& sg, int t) {
     MBuf& bb = buf[t & 1];
-    if (wave < 4) {
-      if (t + 1 < n) {
-        const int row = tid >> 2, cc = tid & 3;
-        bb.kcode[row * 4 + (cc ^ kswz(row))] = sg.codes;
-      }
-    } else if (t >= 1 && t - 1 < n) {
-      const int u = tid - 256, col = u >> 1, hh = u & 1;
-      bb.vcode[col * 2 + (hh ^ ((col >> 3) & 1))] = sg.codes;
-    }
-    if (wave == 0) {
-      if (t + 1 < n) bb.kscale[tid] = sg.sc;
-    } else if (wave < 3) {
-      if (t >= 1 && t - 1 < n) {
-        const int col = tid - 64;
-        bb.vscale[col * 2] = (uint8_t)(sg.sc & 0xFF);
-        bb.vscale[col * 2 + 1] = (uint8_t)(sg.sc >> 8);
-      }
-    }
+    bb.code[code_slot] = sg.codes;
+    bb.scale[tid] = (uint8_t)sg.sc;
   };
 
   const int kr0 = krow(0, n32), kr1 = krow(1, n32);
@@ -357,8 +338,8 @@ void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict_
 #pragma unroll
       for (int cb = 0; cb < kMD / 32; ++cb) {
         const int col = 32 * cb + n32;
-        const u32x4 va = bb.vcode[col * 2 + (h ^ ((col >> 3) & 1))];
-        const int vs = bb.vscale[col * 2 + h];
+        const u32x4 va = bb.code[256 + col * 2 + (h ^ ((col >> 3) & 1))];
+        const int vs = bb.scale[4 * kMBc + col * 2 + h];
         acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp4_operand(va), bp, acc[cb], 4,
                                                                   4, 0, vs, 0, (int)ep);
       }
@@ -369,10 +350,10 @@ void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict_
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const int row = mb ? kr1 : kr0;
-        const int ksc = (int)(bb.kscale[row] >> (8 * h));
+        const int ksc = (int)(*(const uint32_t*)(bb.scale + 4 * row) >> (8 * h));
         // d elements 0..63 (scale byte 0 of the shifted scale words), then 64..127 (byte 2)
-        const u32x4 ka0 = bb.kcode[row * 4 + ((0 + h) ^ kswz(row))];
-        const u32x4 ka1 = bb.kcode[row * 4 + ((2 + h) ^ kswz(row))];
+        const u32x4 ka0 = bb.code[row * 4 + ((0 + h) ^ kswz(row))];
+        const u32x4 ka1 = bb.code[row * 4 + ((2 + h) ^ kswz(row))];
         f32x16 a = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
             fp4_operand(ka0), fp4_operand(qc[0]), zero16(), 4, 4, 0, ksc, 0, (int)qsc);
         a = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp4_operand(ka1), fp4_operand(qc[1]), a,
@@ -386,23 +367,16 @@ void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict_
   MStage stg;
   {
     MStage s0;
-    if (tid < 256) {
-      const __amdgpu_buffer_rsrc_t rk = mrsrc(K4h, N * kCodeRow);
-      s0.codes = __builtin_amdgcn_raw_buffer_load_b128(rk, (tid >> 2) * kCodeRow + (tid & 3) * 16,
-                                                       0, 0);
-    }
-    if (tid < 64)
-      s0.sc = __builtin_amdgcn_raw_buffer_load_b32(mrsrc(KSh, N * kScaleRow), tid * kScaleRow, 0, 0);
+    load_stage(s0, -1);            // K tile 0 (its V half is overwritten later)
     load_stage(stg, 0);
-    if (tid < 256) {
-      const int row = tid >> 2, cc = tid & 3;
-      buf[1].kcode[row * 4 + (cc ^ kswz(row))] = s0.codes;
+    store_stage(s0, 1);            // buffer 1: K tile 0 and its scales
+    store_stage(stg, 0);           // buffer 0: K tile 1
+    // no V tile precedes tile 0: zero codes and neutral scales, written by the same
+    // threads (same slots) that stored this half just above
+    if (!kpart) {
+      buf[0].code[code_slot] = u32x4{0u, 0u, 0u, 0u};
+      buf[0].scale[tid] = 127;
     }
-    if (tid < 64) buf[1].kscale[tid] = s0.sc;
-    store_stage(stg, 0);
-    // no V tile precedes tile 0: zero codes, neutral scales
-    if (tid >= 256) buf[0].vcode[tid - 256] = u32x4{0u, 0u, 0u, 0u};
-    else buf[0].vscale[tid] = 127;
   }
   load_stage(stg, 1);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -437,13 +411,10 @@ void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict_
       any = directp_tile<CAUSAL, false>(sc, pc, ec, m, alpha, j * kMBc, qi, N, c, tau, h);
     any_prev = any;
     alpha_prev = alpha;
-    if (active(j)) {
-      if (!first) {
-        ++n_steps;
-        n_rescales += any ? 1u : 0u;
-      }
-      first = false;
-    }
+    const bool counted = active(j) && !first;   // branch-free: uniform selects
+    n_steps += counted ? 1u : 0u;
+    n_rescales += (counted && any) ? 1u : 0u;
+    first = first && !active(j);
     store_stage(stg, j + 1);
     load_stage(stg, j + 2);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
