@@ -103,11 +103,13 @@ __global__ void quantize8_cols_t_kernel(const float* __restrict__ x, uint8_t* __
 // ---------------------------------------------------------------------------
 // FP8 forward.
 //
-// Work split, staging and the software pipeline are those of the MXFP4 forward:
-// one workgroup = 8 waves x 32 query rows; 64-key tiles of K codes/scales and V^T
-// codes/scales are staged through registers into double-buffered LDS; pipeline
-// step j issues the PV product of tile j-1, the QK product of tile j+1 and the
-// weights of tile j.  All three products run on v_mfma_scale_f32_32x32x64_f8f6f4
+// Work split and staging are those of the MXFP4 forward: one workgroup = 8 waves x
+// 32 query rows; 64-key tiles of K codes/scales and V^T codes/scales are staged
+// through registers into double-buffered LDS.  Pipeline step j issues the QK
+// product of tile j, then the PV product of tile j-1 (which covers the QK latency),
+// then the weights of tile j: the scores live only within a step and the P codes
+// pass from one step to the next in the same registers, so the loop needs no
+// register copies and stays well inside the 256 registers a wave has here.  All three products run on v_mfma_scale_f32_32x32x64_f8f6f4
 // with E4M3 operands (format 0) and E8M0 block scales:
 //   S^T  = K Q^T       A = K codes (32 keys x 64 d), B = Q codes (registers)
 //   O^T += V^T P^T     A = V^T codes (32 d x 64 keys), B = P codes (registers)
@@ -334,15 +336,13 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict_
   const int krs = tid >> 3, kcs = tid & 7;     // K staging unit of this thread
   const int vcs = tid >> 2, vch = tid & 3;     // V^T staging unit of this thread
 
-  // Stage t (read by pipeline step t from buffer t & 1) holds K tile t+1 and V tile t-1.
-  // The loads are unconditional, with the tile index clamped into [0, n) (in bounds;
-  // a stage past the tiles is loaded but never stored).
+  // Stage t (read by pipeline step t from buffer t & 1) holds K tile t and V tile t-1.
   // Every thread stages one code unit of K, one of V^T and one scale byte; the loads are
   // unconditional, with the tile index clamped into [0, n) (in bounds), and so are the
   // stores: a stage past the tiles lands in a buffer half no later product reads.  The
   // scale's source (K or V^T) is a wave-uniform select, so the step has no branches.
   auto load_stage = [&](F8Stage& sg, int t) {
-    const int kt = min(t + 1, n - 1), vt = max(min(t - 1, n - 1), 0);
+    const int kt = min(t, n - 1), vt = max(min(t - 1, n - 1), 0);
     const int kk0 = kt * k8Bc, vk0 = vt * k8Bc;
     const __amdgpu_buffer_rsrc_t rk = rsrc8(K8h + (size_t)kk0 * k8CodeRow, (N - kk0) * k8CodeRow);
     sg.k = __builtin_amdgcn_raw_buffer_load_b128(rk, krs * k8CodeRow + kcs * 16, 0, 0);
@@ -373,26 +373,11 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict_
   const int va = n32 * k8VStride + 16 * h;
   const uint32_t ONES = 0x38383838u;           // E4M3 1.0 in every byte
 
-  // MFMAs of one pipeline step: PV + row sum of the previous tile (P codes pp, P scale
-  // byte ep, V^T from bb), then QK of the next tile into sn (K from bb).
+  // MFMAs of one pipeline step: QK of this step's tile into sn (K from bb), then PV and
+  // row sum of the previous tile (P codes pp, P scale byte ep, V^T from bb).  The PV
+  // products cover the latency of the QK results the weights wait for.
   auto mfmas = [&](const F8Buf& bb, const u32x4 (&pp)[2], uint32_t ep, bool pv, bool qk,
                    f32x16 (&sn)[2]) {
-    if (pv) {
-      const i32x8 bp = fp8_operand(pp[0], pp[1]);
-#pragma unroll
-      for (int cb = 0; cb < k8D / 32; ++cb) {
-        const int col = 32 * cb + n32;
-        const uint8_t* vp = bb.vcode + va + 32 * cb * k8VStride;
-        const u32x4 v0 = lds16(vp), v1 = lds16(vp + 32);
-        const int vs = bb.scale[4 * k8Bc + col * 2 + h];
-        acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp8_operand(v0, v1), bp,
-                                                                  acc[cb], 0, 0, 0, vs, 0,
-                                                                  (int)ep);
-      }
-      const u32x4 ones = {ONES, ONES, ONES, ONES};
-      lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp8_operand(ones, ones), bp, lacc,
-                                                             0, 0, 0, 127, 0, (int)ep);
-    }
     if (qk) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
@@ -409,29 +394,39 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict_
         sn[mb] = a;
       }
     }
+    if (pv) {
+      const i32x8 bp = fp8_operand(pp[0], pp[1]);
+#pragma unroll
+      for (int cb = 0; cb < k8D / 32; ++cb) {
+        const int col = 32 * cb + n32;
+        const uint8_t* vp = bb.vcode + va + 32 * cb * k8VStride;
+        const u32x4 v0 = lds16(vp), v1 = lds16(vp + 32);
+        const int vs = bb.scale[4 * k8Bc + col * 2 + h];
+        acc[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp8_operand(v0, v1), bp,
+                                                                  acc[cb], 0, 0, 0, vs, 0,
+                                                                  (int)ep);
+      }
+      const u32x4 ones = {ONES, ONES, ONES, ONES};
+      lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp8_operand(ones, ones), bp, lacc,
+                                                             0, 0, 0, 127, 0, (int)ep);
+    }
   };
 
-  // ---- prologue: K tile 0 -> buffer 1; stage 0 -> buffer 0; stage 1 in registers ----
+  // ---- prologue: stage 0 (K tile 0; no V tile precedes it) -> buffer 0; stage 1 in
+  //      registers ----
   F8Stage stg;
-  {
-    F8Stage s0;
-    load_stage(s0, -1);            // K tile 0 (its V half is overwritten below)
-    load_stage(stg, 0);
-    store_stage(s0, 1);            // buffer 1: K tile 0 and its scales
-    store_stage(stg, 0);           // buffer 0: K tile 1
-    // no V tile precedes tile 0: zero codes and neutral scales, written by the same
-    // threads that stored this half just above
-    sts16(buf[0].vcode + vcs * k8VStride + 16 * vch, u32x4{0u, 0u, 0u, 0u});
-    if (!(wave < 4)) buf[0].scale[tid] = 127;
-  }
+  load_stage(stg, 0);
+  store_stage(stg, 0);
+  // zero V codes and neutral V scales, written by the same threads that stored this half
+  sts16(buf[0].vcode + vcs * k8VStride + 16 * vch, u32x4{0u, 0u, 0u, 0u});
+  if (!(wave < 4)) buf[0].scale[tid] = 127;
   load_stage(stg, 1);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-  f32x16 s_cur[2], s_nxt[2];
-  u32x4 p_prev[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}}, p_cur[2];
-  uint32_t e_prev = 127u, e_cur = 127u;
-  mfmas(buf[1], p_prev, e_prev, false, true, s_cur);
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // P codes and scale of the latest tile: written by the weights of step j, read by the
+  // PV product of step j + 1 before the weights of that step overwrite them
+  u32x4 p[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+  uint32_t ep = 127u;
 
   bool any_prev = false;
   float alpha_prev = 1.f;
@@ -443,18 +438,18 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict_
       lacc *= alpha_prev;
     }
   };
-  // Pipeline step j: PV and row sum of tile j-1 (pp, ep), QK of tile j+1 into sn,
-  // weights of tile j (sc -> pc, ec); then the staging of stage j+1 and the barrier.
-  auto step = [&](int j, bool pv, bool qk, bool masked, f32x16 (&sc)[2], f32x16 (&sn)[2],
-                  const u32x4 (&pp)[2], uint32_t ep, u32x4 (&pc)[2], uint32_t& ec) {
+  // Pipeline step j: QK of tile j, PV and row sum of tile j-1, weights of tile j; then
+  // the staging of stage j+1 and the barrier.  S lives only within the step.
+  auto step = [&](int j, bool pv, bool masked) {
     rescale();
-    mfmas(buf[j & 1], pp, ep, pv, qk, sn);
+    f32x16 s[2];
+    mfmas(buf[j & 1], p, ep, pv, true, s);
     float alpha;
     bool any;
     if (masked)
-      any = fp8p_tile<CAUSAL, true>(sc, pc, ec, m, alpha, j * k8Bc, qi, N, c, tau, h);
+      any = fp8p_tile<CAUSAL, true>(s, p, ep, m, alpha, j * k8Bc, qi, N, c, tau, h);
     else
-      any = fp8p_tile<CAUSAL, false>(sc, pc, ec, m, alpha, j * k8Bc, qi, N, c, tau, h);
+      any = fp8p_tile<CAUSAL, false>(s, p, ep, m, alpha, j * k8Bc, qi, N, c, tau, h);
     any_prev = any;
     alpha_prev = alpha;
     const bool counted = active(j) && !first;   // branch-free: uniform selects
@@ -465,37 +460,19 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict_
     load_stage(stg, j + 2);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
-  auto advance = [&]() {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      s_cur[i] = s_nxt[i];
-      p_prev[i] = p_cur[i];
-    }
-    e_prev = e_cur;
-  };
 
-  // step 0 has no PV product (no tile before it)
-  step(0, false, n > 1, 0 >= n_full, s_cur, s_nxt, p_prev, e_prev, p_cur, e_cur);
-  advance();
+  // step 0 has no PV product (no tile before it); then the unmasked steps, then the
+  // masked ones (causal diagonal, ragged tail)
+  step(0, false, 0 >= n_full);
   int j = 1;
-  // unmasked steps with both products, then the masked ones (causal diagonal, ragged
-  // tail), one per iteration: unrolling two steps with the S / P registers swapping
-  // roles (as the MXFP4 forward does) needs more than the 256 registers a wave has here
-  for (; j < min(n_full, n - 1); ++j) {
-    step(j, true, true, false, s_cur, s_nxt, p_prev, e_prev, p_cur, e_cur);
-    advance();
-  }
-  for (; j < n - 1; ++j) {
-    step(j, true, true, true, s_cur, s_nxt, p_prev, e_prev, p_cur, e_cur);
-    advance();
-  }
-  // the last step has no QK product (no tile after it)
-  if (n > 1) {
-    step(n - 1, true, false, n - 1 >= n_full, s_cur, s_nxt, p_prev, e_prev, p_cur, e_cur);
-    advance();
-  }
+  for (; j < min(n_full, n); ++j) step(j, true, false);
+  for (; j < n; ++j) step(j, true, true);
+  // PV and row sum of the last tile (its V^T was staged by the last step into buffer n&1)
   rescale();
-  mfmas(buf[n & 1], p_prev, e_prev, true, false, s_nxt);
+  {
+    f32x16 unused[2];
+    mfmas(buf[n & 1], p, ep, true, false, unused);
+  }
 
   // ---- epilogue: O = acc / l, LSE = ln2 * m + ln l ----
   const float l = lacc[0];
