@@ -154,9 +154,10 @@ __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
   __shared__ BTile<D> tile;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n32 = lane & 31, h = lane >> 5;
-  const int kb = blockIdx.x % nkb;
-  const int bh = blockIdx.x / nkb;          // b * Hkv + hkv
-  const int hkv = bh % Hkv, b = bh / Hkv;
+  // the key blocks of one kv head run on one XCD (its Q / dO tiles stay in that L2);
+  // causal: the blocks with the most query tiles (the lowest keys) first
+  const WorkItem wi = decode_workgroup(blockIdx.x, gridDim.x, Hkv, 1, nkb, CAUSAL);
+  const int kb = wi.qb_rank, hkv = wi.hkv, b = wi.b;
   const int group = Hq / Hkv;
   const int K0 = kb * kBBlock;
   const int kw0 = K0 + wave * 32;           // this wave's keys
@@ -300,10 +301,12 @@ __global__ __launch_bounds__(kBThreads) void dq_kernel(
   __shared__ BTile<D> tile;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n32 = lane & 31, h = lane >> 5;
-  const int qb = blockIdx.x % nqb;
-  const int bh = blockIdx.x / nqb;          // b * Hq + hq
-  const int hq = bh % Hq, b = bh / Hq;
-  const int hkv = hq / (Hq / Hkv);
+  // the query blocks of one kv head's query heads run on one XCD (its K / V tiles stay
+  // in that L2); causal: the longest (highest) query blocks first
+  const int group = Hq / Hkv;
+  const WorkItem wi = decode_workgroup(blockIdx.x, gridDim.x, Hkv, group, nqb, CAUSAL);
+  const int qb = CAUSAL ? nqb - 1 - wi.qb_rank : wi.qb_rank;
+  const int hkv = wi.hkv, b = wi.b, hq = hkv * group + wi.g;
   const int Q0 = qb * kBBlock;
   const int qw0 = Q0 + wave * 32;
   const int qi = qw0 + n32;                 // this lane's query (accumulator column)
