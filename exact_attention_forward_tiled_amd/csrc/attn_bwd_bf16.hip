@@ -31,7 +31,8 @@ namespace {
 constexpr int kBWaves = 4;
 constexpr int kBThreads = kBWaves * 64;
 constexpr int kBBlock = kBWaves * 32;    // keys (dK/dV) or queries (dQ) per workgroup
-constexpr int kBTile = 32;               // queries (dK/dV) or keys (dQ) per loop step
+constexpr int kBTile = 64;               // queries (dK/dV) or keys (dQ) staged per loop step
+constexpr int kSub = 32;                 // rows per MFMA block: a step is two such halves
 constexpr int kColStride = kBTile * 2 + 16;  // bytes per staged transposed column (padded)
 
 __device__ __forceinline__ int perm_row(int m) {
@@ -52,7 +53,7 @@ __device__ __forceinline__ u32x4 pack_chunk(const f32x16& x, int c) {
   return r;
 }
 
-// Staged tile: 32 rows x D bf16 of two tensors, row-major (rows padded by 16 bytes: the
+// Staged tile: 64 rows x D bf16 of two tensors, row-major (rows padded by 16 bytes: the
 // 16 rows read together start 4 banks apart) and transposed.
 template <int D>
 struct alignas(16) BTile {
@@ -61,21 +62,21 @@ struct alignas(16) BTile {
   float s1[kBTile];
   uint8_t a[kBTile * kRow];           // tensor A, row r at r * kRow
   uint8_t b[kBTile * kRow];           // tensor B
-  uint8_t at[D * kColStride];         // A transposed: column d at d * kColStride, 32 rows
+  uint8_t at[D * kColStride];         // A transposed: column d at d * kColStride, 64 rows
   uint8_t bt[D * kColStride];         // B transposed
 };
 
-// One thread's share of a staged tile pair: D / 64 units of 16 bytes of each tensor.
-// Unit u is row u % 32, bytes 16 * (u / 32) .. + 15, so the 32 lanes of a half-wave take
-// 32 consecutive rows: their 2-byte writes into the transposed copy fall on 32 distinct
+// One thread's share of a staged tile pair: D / 32 units of 16 bytes of each tensor.
+// Unit u is row u % 64, bytes 16 * (u / 64) .. + 15, so the lanes of a wave take 64
+// consecutive rows: their 2-byte writes into the transposed copy fall on 32 distinct
 // dwords of one column instead of piling onto two banks.
 template <int D>
 struct StageRegs {
-  static constexpr int kUnits = D / 64;
+  static constexpr int kUnits = kBTile * D * 2 / 16 / kBThreads;
   u32x4 a[kUnits], b[kUnits];
 };
 
-// Fetch rows r0 .. r0 + 31 of two [N, D] bf16 tensors into registers (rows past N read
+// Fetch rows r0 .. r0 + 63 of two [N, D] bf16 tensors into registers (rows past N read
 // as row N - 1: in bounds; their contributions are masked by the caller).
 template <int D>
 __device__ __forceinline__ void stage_load(StageRegs<D>& sr, const uint16_t* A,
@@ -84,7 +85,7 @@ __device__ __forceinline__ void stage_load(StageRegs<D>& sr, const uint16_t* A,
 #pragma unroll
   for (int u = 0; u < StageRegs<D>::kUnits; ++u) {
     const int unit = tid + u * kBThreads;
-    const int row = unit & 31, c16 = unit >> 5;
+    const int row = unit % kBTile, c16 = unit / kBTile;
     const int gr = min(r0 + row, N - 1);
     sr.a[u] = *(const u32x4*)(A + (size_t)gr * D + 8 * c16);
     sr.b[u] = *(const u32x4*)(B + (size_t)gr * D + 8 * c16);
@@ -105,7 +106,7 @@ __device__ __forceinline__ void stage_store(BTile<D>& t, const StageRegs<D>& sr,
 #pragma unroll
   for (int u = 0; u < StageRegs<D>::kUnits; ++u) {
     const int unit = tid + u * kBThreads;
-    const int row = unit & 31, c16 = unit >> 5;
+    const int row = unit % kBTile, c16 = unit / kBTile;
     *(u32x4*)(t.a + row * BTile<D>::kRow + 16 * c16) = sr.a[u];
     *(u32x4*)(t.b + row * BTile<D>::kRow + 16 * c16) = sr.b[u];
     if (transposed_a) put_transposed(t.at, sr.a[u], row, c16);
@@ -143,8 +144,8 @@ __global__ void delta_kernel(const float* __restrict__ O, const uint16_t* __rest
 }
 
 // dK, dV for 128 keys of one (batch, kv head): each wave owns 32 keys; the loop runs
-// over the group's query heads and their 32-query blocks (causal: only blocks that
-// reach the workgroup's keys).
+// over the group's query heads and their 64-query tiles (causal: only tiles that reach
+// the workgroup's keys).
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -223,50 +224,55 @@ __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
       }
       __syncthreads();
       if (st + 1 < nsteps) fetch(st + 1);
-      // this wave's keys all lie after the block's last query: nothing visible
+      // this wave's keys all lie after the tile's last query: nothing visible
       if (CAUSAL && kw0 > q0 + kBTile - 1) continue;
-      // S = Q_pi K^T and dP = dO_pi V^T (queries x keys; rows permuted), each as two
-      // accumulation chains over alternate d chunks so that four MFMA chains overlap
-      f32x16 s = zero16(), dp = zero16(), s2 = zero16(), dp2 = zero16();
+      // the two 32-query halves are independent until they meet in dK / dV, so the
+      // compiler can overlap one half's exponentials with the other half's products
 #pragma unroll
-      for (int cc = 0; cc < D / 16; cc += 2) {
-        const uint8_t* qr = tile.a + pm * BTile<D>::kRow + 32 * cc + 16 * h;
-        const uint8_t* gr = tile.b + pm * BTile<D>::kRow + 32 * cc + 16 * h;
-        s = mfma_bf16(lds_u32x4(qr), kop[cc], s);
-        dp = mfma_bf16(lds_u32x4(gr), vop[cc], dp);
-        s2 = mfma_bf16(lds_u32x4(qr + 32), kop[cc + 1], s2);
-        dp2 = mfma_bf16(lds_u32x4(gr + 32), vop[cc + 1], dp2);
-      }
-      // this lane's 16 query rows: acc_row(r, h) = 8h + r (r < 8), 16 + 8h + r - 8
-      f32x4 l4[4], d4[4];
+      for (int sub = 0; sub < kBTile / kSub; ++sub) {
+        const int qs = q0 + kSub * sub;
+        // S = Q_pi K^T and dP = dO_pi V^T (queries x keys; rows permuted), each as two
+        // accumulation chains over alternate d chunks
+        f32x16 s = zero16(), dp = zero16(), s2 = zero16(), dp2 = zero16();
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r0 = 16 * (i >> 1) + 8 * h + 4 * (i & 1);
-        l4[i] = *(const f32x4*)(tile.s0 + r0);
-        d4[i] = *(const f32x4*)(tile.s1 + r0);
-      }
-      // P and dS; register r holds query q0 + acc_row(r, h) for this lane's key
-      f32x16 p, ds;
+        for (int cc = 0; cc < D / 16; cc += 2) {
+          const uint8_t* qr = tile.a + (kSub * sub + pm) * BTile<D>::kRow + 32 * cc + 16 * h;
+          const uint8_t* gr = tile.b + (kSub * sub + pm) * BTile<D>::kRow + 32 * cc + 16 * h;
+          s = mfma_bf16(lds_u32x4(qr), kop[cc], s);
+          dp = mfma_bf16(lds_u32x4(gr), vop[cc], dp);
+          s2 = mfma_bf16(lds_u32x4(qr + 32), kop[cc + 1], s2);
+          dp2 = mfma_bf16(lds_u32x4(gr + 32), vop[cc + 1], dp2);
+        }
+        // this lane's 16 query rows: acc_row(r, h) = 8h + r (r < 8), 16 + 8h + r - 8
+        f32x4 l4[4], d4[4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = acc_row(r, h);
-        const float x = __builtin_fmaf(s[r] + s2[r], c, -l4[r >> 2][r & 3]);
-        const bool vis = key < N && (!CAUSAL || key <= q0 + qi);
-        const float pr = vis ? __builtin_amdgcn_exp2f(x) : 0.f;
-        p[r] = pr;
-        ds[r] = pr * (dp[r] + dp2[r] - d4[r >> 2][r & 3]);
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS (d x keys), over the two 16-query chunks
+        for (int i = 0; i < 4; ++i) {
+          const int r0 = kSub * sub + 16 * (i >> 1) + 8 * h + 4 * (i & 1);
+          l4[i] = *(const f32x4*)(tile.s0 + r0);
+          d4[i] = *(const f32x4*)(tile.s1 + r0);
+        }
+        // P and dS; register r holds query qs + acc_row(r, h) for this lane's key
+        f32x16 p, ds;
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
-        const u32x4 pb = pack_chunk(p, q2), db = pack_chunk(ds, q2);
+        for (int r = 0; r < 16; ++r) {
+          const int qi = acc_row(r, h);
+          const float x = __builtin_fmaf(s[r] + s2[r], c, -l4[r >> 2][r & 3]);
+          const bool vis = key < N && (!CAUSAL || key <= qs + qi);
+          const float pr = vis ? __builtin_amdgcn_exp2f(x) : 0.f;
+          p[r] = pr;
+          ds[r] = pr * (dp[r] + dp2[r] - d4[r >> 2][r & 3]);
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS (d x keys), over the two 16-query chunks
 #pragma unroll
-        for (int dbk = 0; dbk < D / 32; ++dbk) {
-          const int dcol = 32 * dbk + n32;
-          const u32x4 gta = lds_u32x4(tile.bt + dcol * kColStride + 32 * q2 + 16 * h);
-          const u32x4 qta = lds_u32x4(tile.at + dcol * kColStride + 32 * q2 + 16 * h);
-          dv[dbk] = mfma_bf16(gta, pb, dv[dbk]);
-          dk[dbk] = mfma_bf16(qta, db, dk[dbk]);
+        for (int q2 = 0; q2 < 2; ++q2) {
+          const u32x4 pb = pack_chunk(p, q2), db = pack_chunk(ds, q2);
+#pragma unroll
+          for (int dbk = 0; dbk < D / 32; ++dbk) {
+            const int dcol = 32 * dbk + n32;
+            const int off = dcol * kColStride + 2 * kSub * sub + 32 * q2 + 16 * h;
+            dv[dbk] = mfma_bf16(lds_u32x4(tile.bt + off), pb, dv[dbk]);
+            dk[dbk] = mfma_bf16(lds_u32x4(tile.at + off), db, dk[dbk]);
+          }
         }
       }
     }
@@ -291,7 +297,7 @@ __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
 }
 
 // dQ for 128 queries of one (batch, query head): each wave owns 32 queries; the loop
-// runs over 32-key blocks (causal: up to the workgroup's last query).
+// runs over 64-key tiles (causal: up to the workgroup's last query).
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBThreads) void dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -348,36 +354,40 @@ __global__ __launch_bounds__(kBThreads) void dq_kernel(
     __syncthreads();
     if (kt + 1 < nkt) stage_load(sr, K + khead * D, V + khead * D, k0 + kBTile, N);
     if (CAUSAL && k0 > qw0 + 31) continue;
-    // S^T = K_pi Q^T and dP^T = V_pi dO^T (keys x queries; rows permuted), two chains each
-    f32x16 s = zero16(), dp = zero16(), s2 = zero16(), dp2 = zero16();
 #pragma unroll
-    for (int cc = 0; cc < D / 16; cc += 2) {
-      const uint8_t* kr = tile.a + pm * BTile<D>::kRow + 32 * cc + 16 * h;
-      const uint8_t* vr = tile.b + pm * BTile<D>::kRow + 32 * cc + 16 * h;
-      s = mfma_bf16(lds_u32x4(kr), qop[cc], s);
-      dp = mfma_bf16(lds_u32x4(vr), gop[cc], dp);
-      s2 = mfma_bf16(lds_u32x4(kr + 32), qop[cc + 1], s2);
-      dp2 = mfma_bf16(lds_u32x4(vr + 32), gop[cc + 1], dp2);
-    }
-    // dS^T; register r holds key k0 + acc_row(r, h) for this lane's query
-    f32x16 ds;
+    for (int sub = 0; sub < kBTile / kSub; ++sub) {
+      const int ks = k0 + kSub * sub;
+      // S^T = K_pi Q^T and dP^T = V_pi dO^T (keys x queries; rows permuted), two chains each
+      f32x16 s = zero16(), dp = zero16(), s2 = zero16(), dp2 = zero16();
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kj = k0 + acc_row(r, h);
-      const bool vis = kj < N && qi < N && (!CAUSAL || kj <= qi);
-      const float pr =
-          vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r] + s2[r], c, -lse2)) : 0.f;
-      ds[r] = pr * (dp[r] + dp2[r] - dlt);
-    }
-    // dQ^T += K^T dS^T (d x queries), over the two 16-key chunks
+      for (int cc = 0; cc < D / 16; cc += 2) {
+        const uint8_t* kr = tile.a + (kSub * sub + pm) * BTile<D>::kRow + 32 * cc + 16 * h;
+        const uint8_t* vr = tile.b + (kSub * sub + pm) * BTile<D>::kRow + 32 * cc + 16 * h;
+        s = mfma_bf16(lds_u32x4(kr), qop[cc], s);
+        dp = mfma_bf16(lds_u32x4(vr), gop[cc], dp);
+        s2 = mfma_bf16(lds_u32x4(kr + 32), qop[cc + 1], s2);
+        dp2 = mfma_bf16(lds_u32x4(vr + 32), gop[cc + 1], dp2);
+      }
+      // dS^T; register r holds key ks + acc_row(r, h) for this lane's query
+      f32x16 ds;
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      const u32x4 db = pack_chunk(ds, k2);
+      for (int r = 0; r < 16; ++r) {
+        const int kj = ks + acc_row(r, h);
+        const bool vis = kj < N && qi < N && (!CAUSAL || kj <= qi);
+        const float pr =
+            vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r] + s2[r], c, -lse2)) : 0.f;
+        ds[r] = pr * (dp[r] + dp2[r] - dlt);
+      }
+      // dQ^T += K^T dS^T (d x queries), over the two 16-key chunks
 #pragma unroll
-      for (int dbk = 0; dbk < D / 32; ++dbk) {
-        const int dcol = 32 * dbk + n32;
-        const u32x4 kta = lds_u32x4(tile.at + dcol * kColStride + 32 * k2 + 16 * h);
-        dq[dbk] = mfma_bf16(kta, db, dq[dbk]);
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const u32x4 db = pack_chunk(ds, k2);
+#pragma unroll
+        for (int dbk = 0; dbk < D / 32; ++dbk) {
+          const int dcol = 32 * dbk + n32;
+          const int off = dcol * kColStride + 2 * kSub * sub + 32 * k2 + 16 * h;
+          dq[dbk] = mfma_bf16(lds_u32x4(tile.at + off), db, dq[dbk]);
+        }
       }
     }
   }
