@@ -298,8 +298,10 @@ __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
 
 // dQ for 128 queries of one (batch, query head): each wave owns 32 queries; the loop
 // runs over 64-key tiles (causal: up to the workgroup's last query).
+// Two waves per SIMD (at most 256 registers each; two workgroups' tiles fit the CU's LDS),
+// so one workgroup's products overlap the other's exponentials and staging.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBThreads) void dq_kernel(
+__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Delta, float* __restrict__ dQ,
