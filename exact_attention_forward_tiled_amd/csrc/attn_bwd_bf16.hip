@@ -191,17 +191,15 @@ __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
   // registers while the current one computes
   const int steps_per_head = nqt - qt0;
   const int nsteps = group * steps_per_head;
-  auto step_rows = [&](int st, size_t& qh, int& q0) {
-    const int g = st / steps_per_head;
-    q0 = (qt0 + st % steps_per_head) * kBTile;
-    qh = (size_t)(b * Hq + hkv * group + g) * N;
+  auto step_q0 = [&](int st) { return (qt0 + st % steps_per_head) * kBTile; };
+  auto step_qhead = [&](int st) {
+    return (size_t)(b * Hq + hkv * group + st / steps_per_head) * N;
   };
   StageRegs<D> sr;
   float lse_next = 0.f, d_next = 0.f;
   auto fetch = [&](int st) {
-    size_t qh;
-    int q0;
-    step_rows(st, qh, q0);
+    const size_t qh = step_qhead(st);
+    const int q0 = step_q0(st);
     stage_load(sr, Q + qh * D, dO + qh * D, q0, N);
     if (tid < kBTile) {
       const int qr = q0 + tid;
@@ -211,9 +209,7 @@ __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
   };
   if (nsteps > 0) fetch(0);
   for (int st = 0; st < nsteps; ++st) {
-    size_t qh_unused;
-    int q0;
-    step_rows(st, qh_unused, q0);
+    const int q0 = step_q0(st);
     {
       __syncthreads();
       stage_store(tile, sr, true, true);
