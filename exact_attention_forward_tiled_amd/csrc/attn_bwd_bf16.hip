@@ -222,10 +222,8 @@ __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
       if (st + 1 < nsteps) fetch(st + 1);
       // this wave's keys all lie after the tile's last query: nothing visible
       if (CAUSAL && kw0 > q0 + kBTile - 1) continue;
-      // the two 32-query halves are independent until they meet in dK / dV, so the
-      // compiler can overlap one half's exponentials with the other half's products
-#pragma unroll
-      for (int sub = 0; sub < kBTile / kSub; ++sub) {
+      // one 32-query half: S and dP, then P and dS, then the dK / dV products
+      auto half = [&](int sub) {
         const int qs = q0 + kSub * sub;
         // S = Q_pi K^T and dP = dO_pi V^T (queries x keys; rows permuted), each as two
         // accumulation chains over alternate d chunks
@@ -270,6 +268,18 @@ __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
             dk[dbk] = mfma_bf16(lds_u32x4(tile.at + off), db, dk[dbk]);
           }
         }
+      };
+      // The two halves are independent until they meet in dK / dV.  Unrolled (non-causal),
+      // the compiler overlaps one half's exponentials with the other's products; in the
+      // causal form, with its masks, both halves' scores live at once push the K / V
+      // operands into AGPRs (415 register moves per step against 128), so the halves run
+      // one after the other.
+      if constexpr (CAUSAL) {
+#pragma unroll 1
+        for (int sub = 0; sub < kBTile / kSub; ++sub) half(sub);
+      } else {
+#pragma unroll
+        for (int sub = 0; sub < kBTile / kSub; ++sub) half(sub);
       }
     }
   }
