@@ -41,7 +41,7 @@ typedef enum attn_status {
     ATTN_OK = 0,
     ATTN_EINVAL = -1,        /* null pointer, non-positive size, Hq % Hkv != 0, causal not 0/1,
                                 non-finite scale, bad option value */
-    ATTN_EUNSUPPORTED = -2,  /* valid request this build does not implement (e.g. d not 64/128) */
+    ATTN_EUNSUPPORTED = -2,  /* valid request the library does not implement (e.g. d not 64/128) */
     ATTN_EHIP = -3           /* a HIP runtime call or kernel launch failed; see attn_last_hip_error */
 } attn_status;
 
