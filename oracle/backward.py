@@ -20,6 +20,10 @@ from the saved LSE:
     dQ_i   = scale * sum_j dS_ij k_j
     dK_j   = scale * sum_i dS_ij q_i
 
+The masks are the forward's (oracle.exact.visible): causal, sliding window,
+packed documents; a hidden key has s_ij = -inf, so P_ij = 0 and it gets no
+gradient from that query.
+
 With grouped-query attention the key/value head hk serves query heads
 hk*g .. hk*g + g - 1 (g = Hq / Hkv), so dK and dV of hk are the sums of those
 query heads' contributions.  A row whose keys are all masked contributes
@@ -32,14 +36,14 @@ import numpy as np
 from .exact import apply_mask, attention, scores
 
 
-def backward_head(q, k, v, do, causal, scale, o=None, lse=None):
+def backward_head(q, k, v, do, causal, scale, o=None, lse=None, window=0, docs=None):
     """Gradients for one (batch, query head) slice: q, do [N, d]; k, v [Nk, d].
 
     Returns (dq [N, d], dk [Nk, d], dv [Nk, d]) of that query head alone.
     """
     n = q.shape[0]
     rows = np.arange(n)
-    s = apply_mask(scores(q, k, scale), rows, causal)
+    s = apply_mask(scores(q, k, scale), rows, causal, window, docs)
     if lse is None or o is None:
         m = s.max(axis=1)
         m_safe = np.where(np.isfinite(m), m, 0.0)
@@ -59,18 +63,18 @@ def backward_head(q, k, v, do, causal, scale, o=None, lse=None):
     return dq, dk, dv
 
 
-def attention_backward(q, k, v, do, causal, scale, o=None, lse=None):
+def attention_backward(q, k, v, do, causal, scale, o=None, lse=None, window=0, docs=None):
     """Gradients over [B, H, N, d] operands: returns (dq, dk, dv) in float64.
 
     o and lse, when given, are the forward's outputs [B, Hq, N, d] and [B, Hq, N];
-    otherwise they are recomputed from the definition.
+    otherwise they are recomputed from the definition (with the same masks).
     """
     q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
     g = Hq // Hkv
     if o is None or lse is None:
-        o, lse = attention(q, k, v, causal, scale)
+        o, lse = attention(q, k, v, causal, scale, window=window, docs=docs)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
@@ -78,7 +82,7 @@ def attention_backward(q, k, v, do, causal, scale, o=None, lse=None):
         for h in range(Hq):
             hk = h // g
             gq, gk, gv = backward_head(q[b, h], k[b, hk], v[b, hk], do[b, h], causal, scale,
-                                       o[b, h], lse[b, h])
+                                       o[b, h], lse[b, h], window, docs)
             dq[b, h] = gq
             dk[b, hk] += gk
             dv[b, hk] += gv

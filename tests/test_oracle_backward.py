@@ -17,17 +17,35 @@ def _case(seed, B, Hq, Hkv, N, d, sigma=1.0):
     return q, k, v, do
 
 
-def _torch_grads(q, k, v, do, causal, scale):
+def _mask(n, causal, window, docs):
+    """Boolean [n, n] visibility written out from the mask rules (independent of the oracle):
+    causal j <= i; window i - W < j (and j < i + W when not causal); same document."""
+    m = torch.ones(n, n, dtype=torch.bool)
+    i = torch.arange(n)[:, None]
+    j = torch.arange(n)[None, :]
+    if causal:
+        m &= j <= i
+    if window:
+        m &= j > i - window
+        if not causal:
+            m &= j < i + window
+    if docs is not None:
+        doc = torch.zeros(n, dtype=torch.long)
+        for d_idx in range(len(docs) - 1):
+            doc[docs[d_idx]:docs[d_idx + 1]] = d_idx
+        m &= doc[:, None] == doc[None, :]
+    return m
+
+
+def _torch_grads(q, k, v, do, causal, scale, window=0, docs=None):
     """Autograd of a plain float64 softmax attention (GQA by repeating K/V heads)."""
     g = q.shape[1] // k.shape[1]
     tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
     kk = tk.repeat_interleave(g, dim=1)
     vv = tv.repeat_interleave(g, dim=1)
     s = scale * torch.matmul(tq, kk.transpose(-1, -2).contiguous())
-    if causal:
-        n = q.shape[2]
-        mask = torch.ones(n, n, dtype=torch.bool).tril()
-        s = s.masked_fill(~mask, float("-inf"))
+    if causal or window or docs is not None:
+        s = s.masked_fill(~_mask(q.shape[2], causal, window, docs), float("-inf"))
     o = torch.matmul(torch.softmax(s, dim=-1), vv)
     o.backward(torch.tensor(do, dtype=torch.float64))
     return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
@@ -44,6 +62,45 @@ def test_matches_torch_autograd(shape, causal):
     ref = _torch_grads(q, k, v, do, causal, scale)
     for a, b in zip(got, ref):
         assert np.allclose(a, b, atol=1e-12, rtol=1e-10)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("window,docs", [(3, None), (0, [0, 5, 6, 13, 20]), (4, [0, 9, 20])])
+def test_masked_matches_torch_autograd(causal, window, docs):
+    """Sliding window and packed documents: the same masks as the forward, against autograd."""
+    q, k, v, do = _case(31, 1, 4, 2, 20, 8)
+    got = bw.attention_backward(q, k, v, do, causal, 0.6, window=window, docs=docs)
+    ref = _torch_grads(q, k, v, do, causal, 0.6, window, docs)
+    for a, b in zip(got, ref):
+        assert np.allclose(a, b, atol=1e-12, rtol=1e-10)
+
+
+def test_masked_finite_differences_and_isolation():
+    """Central differences on a tiny windowed, documented case; and a key outside every
+    query's window and document band gets no gradient at all."""
+    q, k, v, do = _case(32, 1, 1, 1, 7, 2)
+    docs = [0, 3, 7]
+    dq, dk, dv = bw.attention_backward(q, k, v, do, False, 0.8, window=2, docs=docs)
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.attention(qq, kk, vv, False, 0.8, window=2, docs=docs)
+        return float(np.sum(o * do))
+
+    h = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            fd = (loss(*[xp if y is x else y for y in (q, k, v)]) -
+                  loss(*[xm if y is x else y for y in (q, k, v)])) / (2 * h)
+            assert abs(fd - g[idx]) < 1e-7, (idx, fd, g[idx])
+    # documents of one position see only themselves: their dQ is 0 and their K row is
+    # reached by no other query
+    q2, k2, v2, do2 = _case(33, 1, 1, 1, 6, 3)
+    dq2, dk2, dv2 = bw.attention_backward(q2, k2, v2, do2, False, 0.5, docs=[0, 2, 3, 6])
+    assert np.allclose(dq2[0, 0, 2], 0.0, atol=1e-15) and np.allclose(dk2[0, 0, 2], 0.0)
+    assert np.allclose(dv2[0, 0, 2], do2[0, 0, 2], atol=1e-14)
 
 
 def test_finite_differences():
@@ -103,11 +160,11 @@ def test_given_forward_outputs_equal_recomputed():
 def test_planted_mistakes_are_caught(bad, monkeypatch):
     orig = bw.backward_head
 
-    def mutated(q, k, v, do, causal, scale, o=None, lse=None):
-        dq, dk, dv = orig(q, k, v, do, causal, scale, o, lse)
+    def mutated(q, k, v, do, causal, scale, o=None, lse=None, window=0, docs=None):
+        dq, dk, dv = orig(q, k, v, do, causal, scale, o, lse, window, docs)
         if bad == "no_delta":
             rows = np.arange(q.shape[0])
-            s = oracle.exact.apply_mask(scale * q @ k.T, rows, causal)
+            s = oracle.exact.apply_mask(scale * q @ k.T, rows, causal, window, docs)
             p = np.exp(s - lse[:, None])
             ds = p * (do @ v.T)
             return scale * ds @ k, scale * ds.T @ q, dv
@@ -121,8 +178,8 @@ def test_planted_mistakes_are_caught(bad, monkeypatch):
     if bad == "gqa_last_head":
         orig_all = bw.attention_backward
 
-        def keep_last(q, k, v, do, causal, scale, o=None, lse=None):
-            dq, dk, dv = orig_all(q, k, v, do, causal, scale, o, lse)
+        def keep_last(q, k, v, do, causal, scale, o=None, lse=None, window=0, docs=None):
+            dq, dk, dv = orig_all(q, k, v, do, causal, scale, o, lse, window, docs)
             g = q.shape[1] // k.shape[1]
             if g > 1:   # as if only the group's last query head were counted
                 for hk in range(k.shape[1]):
