@@ -164,15 +164,20 @@ class Mxfp8Workload:
 
 class BwdWorkload:
     """bf16 backward on a bf16 workload: the forward's O and LSE computed once (untimed),
-    a seeded dO, then the three backward kernels per step."""
+    a seeded dO, then the three backward kernels per step (with the forward's sliding window
+    and / or documents when given)."""
 
-    def __init__(self, w):
+    def __init__(self, w, window=0, doc_offsets=None):
         import torch
         import exact_attention_forward_tiled_amd as fa
         import synth
         self.w = w
+        self.window = window
+        self.docs = (None if doc_offsets is None else
+                     torch.tensor(doc_offsets, dtype=torch.int32, device="cuda"))
         self.q, self.k, self.v = device_inputs(w)
-        self.o, self.lse = fa.fwd(self.q, self.k, self.v, causal=w.causal, scale=w.scale)
+        self.o, self.lse = fa.fwd(self.q, self.k, self.v, causal=w.causal, scale=w.scale,
+                                  window=window, docs=self.docs)
         gb = synth.normal_bf16((w.B, w.Hq, w.N, w.d), 1000 * w.index + 4, 1.0)
         self.do = device_inputs_bits(gb)
         self.dq = torch.empty((w.B, w.Hq, w.N, w.d), dtype=torch.float32, device="cuda")
@@ -184,7 +189,8 @@ class BwdWorkload:
 
     def launch(self, stats=None):
         self.fa.bwd(self.q, self.k, self.v, self.o, self.lse, self.do, causal=self.w.causal,
-                    scale=self.w.scale, out=(self.dq, self.dk, self.dv), delta=self.delta)
+                    scale=self.w.scale, out=(self.dq, self.dk, self.dv), delta=self.delta,
+                    window=self.window, docs=self.docs)
 
 
 def device_inputs_bits(bits):
@@ -522,6 +528,25 @@ def main():
                                       / PEAK_BF16_TFLOPS, 2),
             "flop_convention": "2.5x forward (dQ, dK, dV, S, dP); the kernels execute 3.5x "
                                "(S and dP recomputed in both the dK/dV and the dQ kernel)"}
+        masked = []
+        if args.window:
+            masked.append((f"bwd/window={args.window}", args.window, None))
+        if args.docs:
+            masked.append((f"bwd/docs={args.docs}", 0,
+                           [round(x * w.N / args.docs) for x in range(args.docs + 1)]))
+        for tag, win, off in masked:
+            log(f"timing the backward on {w.name} with {tag[4:]}")
+            wl = BwdWorkload(w, window=win, doc_offsets=off)
+            tm = time_workload(wl, args.steps, args.warmup, args.warmup_seconds)
+            del wl
+            torch.cuda.empty_cache()
+            pairs = visible_pairs(w.N, w.causal, win, off)
+            fl = 2.5 * 4.0 * w.d * w.B * w.Hq * pairs
+            extra["workloads"][f"{w.name}/{tag}"] = {
+                "tflops_visible": round(fl / (tm["kernel_ms_avg"] * 1e-3) / 1e12, 2),
+                "ms": round(tm["kernel_ms_avg"], 4),
+                "visible_pairs_per_head": pairs,
+                "time_vs_unmasked_bwd": round(tm["kernel_ms_avg"] / tb["kernel_ms_avg"], 4)}
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -20,7 +20,7 @@ EXP_MODES = {"hw": 0, "poly": 1, "mix": 2}
 EXPORTS = ("attn_default_opts", "attn_fwd", "attn_fwd_ex", "attn_fwd_mxfp4", "attn_fwd_mxfp4_ex",
            "attn_quantize_mxfp4_rows", "attn_quantize_mxfp4_cols_t", "attn_fwd_mxfp8",
            "attn_fwd_mxfp8_ex", "attn_quantize_mxfp8_rows", "attn_quantize_mxfp8_cols_t",
-           "attn_bwd", "attn_strerror", "attn_last_hip_error")
+           "attn_bwd", "attn_bwd_ex", "attn_strerror", "attn_last_hip_error")
 
 
 class AttnOpts(ctypes.Structure):
@@ -51,6 +51,7 @@ def _load():
         "attn_quantize_mxfp8_rows": (I, [P, P, P, LL, I, P]),
         "attn_quantize_mxfp8_cols_t": (I, [P, P, P, I, I, I, P]),
         "attn_bwd": (I, [P] * 10 + [I] * 6 + [F, P]),
+        "attn_bwd_ex": (I, [P] * 10 + [I] * 6 + [F, OP, P]),
         "attn_strerror": (ctypes.c_char_p, [I]),
         "attn_last_hip_error": (I, []),
     }
@@ -142,6 +143,12 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, N, d, causal,
              stream=None):
     return lib.attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, N, d, causal,
                         scale, stream)
+
+
+def attn_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, N, d, causal, scale,
+                opts=None, stream=None):
+    return lib.attn_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, N, d, causal,
+                           scale, ctypes.byref(opts) if opts is not None else None, stream)
 
 
 def attn_quantize_mxfp4_rows(x, codes, scales, rows, cols, stream=None):
@@ -328,10 +335,12 @@ def fwd_mxfp8(q8, qs, k8, ks, vt8, vts, causal=False, scale=None, tau=8.0, stats
     return o, lse
 
 
-def bwd(q, k, v, o, lse, dout, causal=False, scale=None, out=None, delta=None):
+def bwd(q, k, v, o, lse, dout, causal=False, scale=None, out=None, delta=None, window=0,
+        docs=None):
     """bf16 attention backward: returns (dQ fp32 [B,Hq,N,d], dK, dV fp32 [B,Hkv,N,d]).
     o, lse: the forward's outputs for the same q, k, v (fp32); dout: bf16 like q.
-    delta: optional fp32 CUDA workspace of B*Hq*N floats."""
+    delta: optional fp32 CUDA workspace of B*Hq*N floats.  window, docs: the forward's
+    sliding window and document offsets (as for fwd)."""
     torch = _torch()
     for t in (q, k, v, dout):
         if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
@@ -356,7 +365,15 @@ def bwd(q, k, v, o, lse, dout, causal=False, scale=None, out=None, delta=None):
         delta = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     elif delta.dtype != torch.float32 or not delta.is_cuda or delta.numel() < B * Hq * N:
         raise ValueError("delta must be an fp32 CUDA tensor of at least B*Hq*N floats")
-    check(attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                   dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
-                   B, Hq, Hkv, N, d, int(bool(causal)), float(scale), _stream(torch, q.device)))
+    doc_ptr, n_docs = None, 0
+    if docs is not None:
+        if docs.dtype != torch.int32 or not docs.is_cuda or not docs.is_contiguous() \
+                or docs.numel() < 2:
+            raise ValueError("docs must be a contiguous int32 CUDA tensor of document offsets")
+        doc_ptr, n_docs = docs.data_ptr(), docs.numel() - 1
+    opts = make_opts(window=window, doc_ptr=doc_ptr, n_docs=n_docs)
+    check(attn_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                      dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                      delta.data_ptr(), B, Hq, Hkv, N, d, int(bool(causal)), float(scale), opts,
+                      _stream(torch, q.device)))
     return dq, dk, dv

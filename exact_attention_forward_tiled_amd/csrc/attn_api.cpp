@@ -155,9 +155,10 @@ int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse, 
   return attn_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, nullptr, nullptr);
 }
 
-int attn_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse,
-             const void* dout, float* dq, float* dk, float* dv, float* delta, int B, int Hq,
-             int Hkv, int N, int d, int causal, float scale, void* stream) {
+int attn_bwd_ex(const void* q, const void* k, const void* v, const float* o, const float* lse,
+                const void* dout, float* dq, float* dk, float* dv, float* delta, int B, int Hq,
+                int Hkv, int N, int d, int causal, float scale, const attn_opts* opts,
+                void* stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return ATTN_EINVAL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
@@ -165,6 +166,12 @@ int attn_bwd(const void* q, const void* k, const void* v, const float* o, const 
     return ATTN_EINVAL;
   int st = check_common(B, Hq, Hkv, N, d, causal, scale);
   if (st != ATTN_OK) return st;
+  attn_opts def;
+  attn_default_opts(&def);
+  const attn_opts* op = opts ? opts : &def;
+  st = check_opts(op);
+  if (st != ATTN_OK) return st;
+  if (op->alibi_slopes != nullptr || op->softcap != 0.f) return ATTN_EUNSUPPORTED;
   if (d != 64 && d != 128) return ATTN_EUNSUPPORTED;
   if ((long long)B * Hkv * ((N + 127) / 128) >= (1LL << 31) ||
       (long long)B * Hq * ((N + 127) / 128) >= (1LL << 31))
@@ -173,12 +180,24 @@ int attn_bwd(const void* q, const void* k, const void* v, const float* o, const 
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
   a.dq = dq; a.dk = dk; a.dv = dv; a.delta = delta;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N = N; a.d = d; a.causal = causal;
+  // a window at least N wide hides nothing: run the plain mask
+  a.window = op->window >= N ? 0 : op->window;
+  a.doc_offsets = op->doc_offsets;
+  a.n_docs = op->doc_offsets != nullptr ? op->n_docs : 0;
+  if (a.n_docs > N) return ATTN_EINVAL;   // documents are non-empty
   a.c = scale * 1.4426950408889634f;
   a.scale = scale;
   a.stream = stream;
   hipError_t e = attn::launch_bwd_bf16(a);
   if (e == hipErrorNotSupported) return ATTN_EUNSUPPORTED;
   return hip_status(e);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse,
+             const void* dout, float* dq, float* dk, float* dv, float* delta, int B, int Hq,
+             int Hkv, int N, int d, int causal, float scale, void* stream) {
+  return attn_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, N, d, causal, scale,
+                     nullptr, stream);
 }
 
 int attn_fwd_mxfp4_ex(const uint8_t* q4, const uint8_t* qs, const uint8_t* k4, const uint8_t* ks,

@@ -116,6 +116,52 @@ __device__ __forceinline__ void stage_store(BTile<D>& t, const StageRegs<D>& sr,
 
 __device__ __forceinline__ u32x4 lds_u32x4(const uint8_t* p) { return *(const u32x4*)p; }
 
+// The masks beyond the causal one, as in the forward: a sliding window W (key j visible
+// from query i when i - W < j, and j < i + W without the causal mask) and packed documents
+// (both in one document).  Key j is visible from query i iff lo(i) <= j <= hi(i) (keys()),
+// equivalently qlo(j) <= i <= qhi(j) (queries()); all four bounds are non-decreasing, so
+// the first and last rows of a block bound the band of the whole block.
+struct Band {
+  int N, window, n_docs;
+  const int* doc_off;
+  // the document [s, e) holding position i; the search reads only doc_off[0 .. n_docs],
+  // and the clamps keep s <= i < e whatever the offsets hold
+  __device__ void doc_of(int i, int& s, int& e) const {
+    int a = 0, z = n_docs;
+    while (z - a > 1) {
+      const int m = (a + z) >> 1;
+      if (doc_off[m] <= i) a = m;
+      else z = m;
+    }
+    s = min(doc_off[a], i);
+    e = max(doc_off[a + 1], i + 1);
+  }
+  // keys seen by query i (0 <= i < N)
+  template <bool CAUSAL>
+  __device__ void keys(int i, int& lo, int& hi) const {
+    lo = window ? max(0, i - window + 1) : 0;
+    hi = CAUSAL ? i : (window ? min(N - 1, i + window - 1) : N - 1);
+    if (n_docs > 0) {
+      int ds, de;
+      doc_of(i, ds, de);
+      lo = max(lo, ds);
+      hi = min(hi, de - 1);
+    }
+  }
+  // queries that see key j (0 <= j < N)
+  template <bool CAUSAL>
+  __device__ void queries(int j, int& lo, int& hi) const {
+    lo = CAUSAL ? j : (window ? max(0, j - window + 1) : 0);
+    hi = window ? min(N - 1, j + window - 1) : N - 1;
+    if (n_docs > 0) {
+      int ds, de;
+      doc_of(j, ds, de);
+      lo = max(lo, ds);
+      hi = min(hi, de - 1);
+    }
+  }
+};
+
 // D_i = dO_i . O_i, HD / 8 threads per row (8 elements each).
 template <int HD>
 __global__ void delta_kernel(const float* __restrict__ O, const uint16_t* __restrict__ dO,
@@ -145,13 +191,13 @@ __global__ void delta_kernel(const float* __restrict__ O, const uint16_t* __rest
 
 // dK, dV for 128 keys of one (batch, kv head): each wave owns 32 keys; the loop runs
 // over the group's query heads and their 64-query tiles (causal: only tiles that reach
-// the workgroup's keys).
-template <int D, bool CAUSAL>
+// the workgroup's keys; BAND: only tiles within the keys' window and documents).
+template <int D, bool CAUSAL, bool BAND>
 __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Delta, float* __restrict__ dK,
-    float* __restrict__ dV, int Hq, int Hkv, int N, int nkb, float c, float scale) {
+    float* __restrict__ dV, int Hq, int Hkv, int N, int nkb, float c, float scale, Band band) {
   __shared__ BTile<D> tile;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n32 = lane & 31, h = lane >> 5;
@@ -184,12 +230,27 @@ __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
     dv[i] = zero16();
   }
 
-  const int nqt = (N + kBTile - 1) / kBTile;
-  const int qt0 = CAUSAL ? K0 / kBTile : 0;
+  // query tiles [qt0, qt1) reach the workgroup's keys; BAND: this lane's key is seen by
+  // queries [kq_lo, kq_hi], this wave's keys by [wq_lo, wq_hi]
+  int qt0 = CAUSAL ? K0 / kBTile : 0, qt1 = (N + kBTile - 1) / kBTile;
+  int kq_lo = 0, kq_hi = 0, wq_lo = 0, wq_hi = 0;
+  if (BAND) {
+    int lo, hi, lo2, hi2;
+    band.queries<CAUSAL>(K0, lo, hi);
+    band.queries<CAUSAL>(min(K0 + kBBlock - 1, N - 1), lo2, hi2);
+    qt0 = lo / kBTile;
+    qt1 = hi2 / kBTile + 1;
+    band.queries<CAUSAL>(min(key, N - 1), kq_lo, kq_hi);
+    band.queries<CAUSAL>(min(kw0, N - 1), wq_lo, hi);
+    band.queries<CAUSAL>(min(kw0 + 31, N - 1), lo, wq_hi);
+    // the same in every lane of the wave: kept in scalar registers
+    wq_lo = __builtin_amdgcn_readfirstlane(wq_lo);
+    wq_hi = __builtin_amdgcn_readfirstlane(wq_hi);
+  }
   const int pm = perm_row(n32);
   // (query head, query tile) steps in order; the next step's rows are fetched into
   // registers while the current one computes
-  const int steps_per_head = nqt - qt0;
+  const int steps_per_head = qt1 - qt0;
   const int nsteps = group * steps_per_head;
   auto step_q0 = [&](int st) { return (qt0 + st % steps_per_head) * kBTile; };
   auto step_qhead = [&](int st) {
@@ -220,8 +281,10 @@ __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
       }
       __syncthreads();
       if (st + 1 < nsteps) fetch(st + 1);
-      // this wave's keys all lie after the tile's last query: nothing visible
-      if (CAUSAL && kw0 > q0 + kBTile - 1) continue;
+      // this wave's keys all lie after the tile's last query (or outside its band):
+      // nothing visible
+      if (!BAND && CAUSAL && kw0 > q0 + kBTile - 1) continue;
+      if (BAND && (kw0 >= N || q0 > wq_hi || q0 + kBTile - 1 < wq_lo)) continue;
       // one 32-query half: S and dP, then P and dS, then the dK / dV products
       auto half = [&](int sub) {
         const int qs = q0 + kSub * sub;
@@ -251,7 +314,9 @@ __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
         for (int r = 0; r < 16; ++r) {
           const int qi = acc_row(r, h);
           const float x = __builtin_fmaf(s[r] + s2[r], c, -l4[r >> 2][r & 3]);
-          const bool vis = key < N && (!CAUSAL || key <= qs + qi);
+          // non-short-circuit: evaluated whole, so no branch per element
+          const bool vis = BAND ? ((key < N) & (qs + qi >= kq_lo) & (qs + qi <= kq_hi))
+                                : (key < N && (!CAUSAL || key <= qs + qi));
           const float pr = vis ? __builtin_amdgcn_exp2f(x) : 0.f;
           p[r] = pr;
           ds[r] = pr * (dp[r] + dp2[r] - d4[r >> 2][r & 3]);
@@ -271,10 +336,10 @@ __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
       };
       // The two halves are independent until they meet in dK / dV.  Unrolled (non-causal),
       // the compiler overlaps one half's exponentials with the other's products; in the
-      // causal form, with its masks, both halves' scores live at once push the K / V
-      // operands into AGPRs (415 register moves per step against 128), so the halves run
-      // one after the other.
-      if constexpr (CAUSAL) {
+      // causal and band forms, with their masks, both halves' scores live at once push the
+      // K / V operands into AGPRs (415 register moves per step against 128), so the halves
+      // run one after the other.
+      if constexpr (CAUSAL || BAND) {
 #pragma unroll 1
         for (int sub = 0; sub < kBTile / kSub; ++sub) half(sub);
       } else {
@@ -303,15 +368,16 @@ __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
 }
 
 // dQ for 128 queries of one (batch, query head): each wave owns 32 queries; the loop
-// runs over 64-key tiles (causal: up to the workgroup's last query).
+// runs over 64-key tiles (causal: up to the workgroup's last query; BAND: the tiles within
+// the queries' window and documents).
 // Two waves per SIMD (at most 256 registers each; two workgroups' tiles fit the CU's LDS),
 // so one workgroup's products overlap the other's exponentials and staging.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool BAND>
 __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Delta, float* __restrict__ dQ,
-    int Hq, int Hkv, int N, int nqb, float c, float scale) {
+    int Hq, int Hkv, int N, int nqb, float c, float scale, Band band) {
   __shared__ BTile<D> tile;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n32 = lane & 31, h = lane >> 5;
@@ -349,23 +415,41 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) dq[i] = zero16();
 
-  const int kend = CAUSAL ? min(N, Q0 + kBBlock) : N;
-  const int nkt = (kend + kBTile - 1) / kBTile;
+  // key tiles [kt0, kt1) reach the workgroup's queries; BAND: this lane's query sees keys
+  // [q_lo, q_hi], this wave's queries see [w_lo, w_hi]
+  int kt0 = 0, kt1 = ((CAUSAL ? min(N, Q0 + kBBlock) : N) + kBTile - 1) / kBTile;
+  int q_lo = 0, q_hi = 0, w_lo = 0, w_hi = 0;
+  if (BAND) {
+    int lo, hi, lo2, hi2;
+    band.keys<CAUSAL>(Q0, lo, hi);
+    band.keys<CAUSAL>(min(Q0 + kBBlock - 1, N - 1), lo2, hi2);
+    kt0 = lo / kBTile;
+    kt1 = hi2 / kBTile + 1;
+    band.keys<CAUSAL>(min(qi, N - 1), q_lo, q_hi);
+    band.keys<CAUSAL>(min(qw0, N - 1), w_lo, hi);
+    band.keys<CAUSAL>(min(qw0 + 31, N - 1), lo, w_hi);
+    // the same in every lane of the wave: kept in scalar registers
+    w_lo = __builtin_amdgcn_readfirstlane(w_lo);
+    w_hi = __builtin_amdgcn_readfirstlane(w_hi);
+  }
   const int pm = perm_row(n32);
   // the next key tile is fetched into registers while the current one computes
   StageRegs<D> sr;
-  if (nkt > 0) stage_load(sr, K + khead * D, V + khead * D, 0, N);
-  for (int kt = 0; kt < nkt; ++kt) {
+  if (kt1 > kt0) stage_load(sr, K + khead * D, V + khead * D, kt0 * kBTile, N);
+  for (int kt = kt0; kt < kt1; ++kt) {
     const int k0 = kt * kBTile;
     __syncthreads();
     stage_store(tile, sr, true, false);
     __syncthreads();
-    if (kt + 1 < nkt) stage_load(sr, K + khead * D, V + khead * D, k0 + kBTile, N);
-    if (CAUSAL && k0 > qw0 + 31) continue;
-#pragma unroll
-    for (int sub = 0; sub < kBTile / kSub; ++sub) {
+    if (kt + 1 < kt1) stage_load(sr, K + khead * D, V + khead * D, k0 + kBTile, N);
+    if (!BAND && CAUSAL && k0 > qw0 + 31) continue;
+    if (BAND && (qw0 >= N || k0 > w_hi || k0 + kBTile - 1 < w_lo)) continue;
+    // one 32-key half: S^T and dP^T, then dS^T, then the dQ products
+    constexpr bool kTwoChains = !(BAND && D == 128);
+    auto half = [&](int sub) {
       const int ks = k0 + kSub * sub;
-      // S^T = K_pi Q^T and dP^T = V_pi dO^T (keys x queries; rows permuted), two chains each
+      // S^T = K_pi Q^T and dP^T = V_pi dO^T (keys x queries; rows permuted), two chains
+      // each; one each in the band form at d = 128, whose bounds leave no room for four
       f32x16 s = zero16(), dp = zero16(), s2 = zero16(), dp2 = zero16();
 #pragma unroll
       for (int cc = 0; cc < D / 16; cc += 2) {
@@ -373,18 +457,29 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         const uint8_t* vr = tile.b + (kSub * sub + pm) * BTile<D>::kRow + 32 * cc + 16 * h;
         s = mfma_bf16(lds_u32x4(kr), qop[cc], s);
         dp = mfma_bf16(lds_u32x4(vr), gop[cc], dp);
-        s2 = mfma_bf16(lds_u32x4(kr + 32), qop[cc + 1], s2);
-        dp2 = mfma_bf16(lds_u32x4(vr + 32), gop[cc + 1], dp2);
+        if constexpr (kTwoChains) {
+          s2 = mfma_bf16(lds_u32x4(kr + 32), qop[cc + 1], s2);
+          dp2 = mfma_bf16(lds_u32x4(vr + 32), gop[cc + 1], dp2);
+        } else {
+          s = mfma_bf16(lds_u32x4(kr + 32), qop[cc + 1], s);
+          dp = mfma_bf16(lds_u32x4(vr + 32), gop[cc + 1], dp);
+        }
       }
       // dS^T; register r holds key ks + acc_row(r, h) for this lane's query
       f32x16 ds;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kj = ks + acc_row(r, h);
-        const bool vis = kj < N && qi < N && (!CAUSAL || kj <= qi);
-        const float pr =
-            vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r] + s2[r], c, -lse2)) : 0.f;
-        ds[r] = pr * (dp[r] + dp2[r] - dlt);
+        // non-short-circuit: evaluated whole, so no branch per element (causal: kj <= qi
+        // < N implies kj < N)
+        const bool vis = BAND     ? ((qi < N) & (kj >= q_lo) & (kj <= q_hi))
+                         : CAUSAL ? ((qi < N) & (kj <= qi))
+                                  : ((kj < N) & (qi < N));
+        const float sv = kTwoChains ? s[r] + s2[r] : s[r];
+        const float dpv = kTwoChains ? dp[r] + dp2[r] : dp[r];
+        // hidden: 2^-inf = 0 (a select, not a branch around the exponential)
+        const float x = vis ? __builtin_fmaf(sv, c, -lse2) : -__builtin_inff();
+        ds[r] = __builtin_amdgcn_exp2f(x) * (dpv - dlt);
       }
       // dQ^T += K^T dS^T (d x queries), over the two 16-key chunks
 #pragma unroll
@@ -397,6 +492,15 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
           dq[dbk] = mfma_bf16(lds_u32x4(tile.at + off), db, dq[dbk]);
         }
       }
+    };
+    // unrolled, one half's exponentials overlap the other's products; the band form's
+    // extra bounds would push that past the 256 registers of two waves per SIMD
+    if constexpr (BAND) {
+#pragma unroll 1
+      for (int sub = 0; sub < kBTile / kSub; ++sub) half(sub);
+    } else {
+#pragma unroll
+      for (int sub = 0; sub < kBTile / kSub; ++sub) half(sub);
     }
   }
   if (qi < N) {
@@ -412,7 +516,7 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool BAND>
 hipError_t launch_bwd_t(const BwdArgs& a) {
   const long long rows = (long long)a.B * a.Hq * a.N;
   constexpr int kRowsPerBlock = 256 / (D / 8);
@@ -422,24 +526,32 @@ hipError_t launch_bwd_t(const BwdArgs& a) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nb = (a.N + kBBlock - 1) / kBBlock;
-  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL>), dim3((unsigned)(a.B * a.Hkv * nb)),
+  const Band band{a.N, a.window, a.n_docs, a.doc_offsets};
+  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, BAND>), dim3((unsigned)(a.B * a.Hkv * nb)),
                      dim3(kBThreads), 0, (hipStream_t)a.stream, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse,
-                     a.delta, a.dk, a.dv, a.Hq, a.Hkv, a.N, nb, a.c, a.scale);
+                     a.delta, a.dk, a.dv, a.Hq, a.Hkv, a.N, nb, a.c, a.scale, band);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3((unsigned)(a.B * a.Hq * nb)), dim3(kBThreads),
+  hipLaunchKernelGGL((dq_kernel<D, CAUSAL, BAND>), dim3((unsigned)(a.B * a.Hq * nb)), dim3(kBThreads),
                      0, (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                      (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta, a.dq,
-                     a.Hq, a.Hkv, a.N, nb, a.c, a.scale);
+                     a.Hq, a.Hkv, a.N, nb, a.c, a.scale, band);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdArgs& a) {
+  const bool band = a.window > 0 || a.n_docs > 0;
+  if (a.causal) return band ? launch_bwd_t<D, true, true>(a) : launch_bwd_t<D, true, false>(a);
+  return band ? launch_bwd_t<D, false, true>(a) : launch_bwd_t<D, false, false>(a);
 }
 
 }  // namespace
 
 hipError_t launch_bwd_bf16(const BwdArgs& a) {
-  if (a.d == 128) return a.causal ? launch_bwd_t<128, true>(a) : launch_bwd_t<128, false>(a);
-  if (a.d == 64) return a.causal ? launch_bwd_t<64, true>(a) : launch_bwd_t<64, false>(a);
+  if (a.d == 128) return launch_bwd_d<128>(a);
+  if (a.d == 64) return launch_bwd_d<64>(a);
   return hipErrorNotSupported;
 }
 

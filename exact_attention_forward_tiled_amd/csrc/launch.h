@@ -56,6 +56,9 @@ struct BwdArgs {
   float* dv;            // fp32 [B, Hkv, N, d]
   float* delta;         // fp32 [B, Hq, N] workspace (D_i = dO_i . O_i)
   int B, Hq, Hkv, N, d, causal;
+  int window;           // sliding window W (0: none; 1 <= W < N), as in FwdArgs
+  const int* doc_offsets;   // device, n_docs + 1 document offsets (0, ..., N), or null
+  int n_docs;           // documents (0: no document masking)
   float c;              // scale * log2(e)
   float scale;
   void* stream;

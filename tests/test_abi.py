@@ -148,6 +148,22 @@ def test_bwd_validation(fa):
     assert fa.attn_bwd(*args, 1, 2, 2, 64, 128, 0, 0.1) == -1
 
 
+def test_bwd_ex_validation(fa):
+    """The masking options of the backward: rejected before any launch."""
+    base = [FAKE] * 10
+    shape = (1, 2, 2, 64, 128, 0, 0.1)
+    assert fa.attn_bwd_ex(*base, *shape, fa.make_opts(window=-1)) == -1
+    assert fa.attn_bwd_ex(*base, *shape, fa.make_opts(doc_ptr=FAKE, n_docs=0)) == -1
+    assert fa.attn_bwd_ex(*base, *shape, fa.make_opts(doc_ptr=FAKE, n_docs=65)) == -1
+    assert fa.attn_bwd_ex(*base, *shape, fa.make_opts(alibi_ptr=FAKE)) == -2
+    assert fa.attn_bwd_ex(*base, *shape, fa.make_opts(softcap=5.0)) == -2
+    assert fa.attn_bwd_ex(*base, *shape, fa.make_opts(tau=-1.0)) == -1
+    assert fa.attn_bwd_ex(*base, 1, 2, 2, 64, 96, 0, 0.1, fa.make_opts(window=8)) == -2
+    args = list(base)
+    args[9] = 0                                                         # delta
+    assert fa.attn_bwd_ex(*args, *shape, fa.make_opts(window=8)) == -1
+
+
 def test_strerror(fa):
     from exact_attention_forward_tiled_amd.binding import lib
     assert lib.attn_strerror(0) == b"success"

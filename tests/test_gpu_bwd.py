@@ -27,13 +27,15 @@ def _case(seed, B, Hq, Hkv, N, d=128):
     return (qb, kb, vb, gb), tuple(synth.bf16_bits_to_f64(x) for x in (qb, kb, vb, gb))
 
 
-def _run(bits, causal, scale, o=None, lse=None):
-    """GPU backward; o, lse: float64 arrays to feed, else the GPU forward's outputs."""
+def _run(bits, causal, scale, o=None, lse=None, window=0, docs=None):
+    """GPU backward; o, lse: float64 arrays to feed, else the GPU forward's outputs (with the
+    same window and documents)."""
     import torch
     import exact_attention_forward_tiled_amd as fa
     q, k, v, g = (to_dev_bf16(x) for x in bits)
+    dd = None if docs is None else torch.tensor(docs, dtype=torch.int32, device="cuda")
     if o is None:
-        od, ld = fa.fwd(q, k, v, causal=causal, scale=scale)
+        od, ld = fa.fwd(q, k, v, causal=causal, scale=scale, window=window, docs=dd)
     else:
         od, ld = to_dev_f32(o), to_dev_f32(lse)
     B, Hq, N, d = q.shape
@@ -42,9 +44,16 @@ def _run(bits, causal, scale, o=None, lse=None):
     dq = torch.full((B, Hq, N, d), nan, dtype=torch.float32, device="cuda")
     dk = torch.full((B, Hkv, N, d), nan, dtype=torch.float32, device="cuda")
     dv = torch.full((B, Hkv, N, d), nan, dtype=torch.float32, device="cuda")
-    fa.bwd(q, k, v, od, ld, g, causal=causal, scale=scale, out=(dq, dk, dv))
+    fa.bwd(q, k, v, od, ld, g, causal=causal, scale=scale, out=(dq, dk, dv), window=window,
+           docs=dd)
     torch.cuda.synchronize()
     return dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
+
+
+# Where every query sees a single key (a window of 1, one-token documents everywhere) dQ and
+# dK are exactly 0: P = 1 and dP - D cancels.  The kernels compute dP and D in fp32 from
+# unit-scale bf16 operands, so the residue is a few fp32 ulps of dP (~1e-6), far below this.
+ZERO_GRAD_ABS = 1e-4
 
 
 def _check(got, ref, tag):
@@ -53,7 +62,11 @@ def _check(got, ref, tag):
     for a in got:
         assert not np.isnan(a).any()
     assert rv <= BWD_DV_RELRMS, rv
-    assert rq <= BWD_DQK_RELRMS and rk <= BWD_DQK_RELRMS, (rq, rk)
+    for a, b, r in ((got[0], ref[0], rq), (got[1], ref[1], rk)):
+        if np.sqrt(np.mean(np.square(b))) < 1e-9:    # an exactly zero gradient
+            assert np.abs(a).max() <= ZERO_GRAD_ABS, np.abs(a).max()
+        else:
+            assert r <= BWD_DQK_RELRMS, (rq, rk)
 
 
 SMALL = [
@@ -123,3 +136,48 @@ def test_bwd_headline_shape_two_heads():
         q, k, v, g = (synth.bf16_bits_to_f64(x[b, h]) for x in (qb, kb, vb, gb))
         ref = bw.backward_head(q, k, v, g, w.causal, w.scale)
         _check((dq[b, h], dk[b, h], dv[b, h]), ref, f"(b, h) = ({b}, {h})")
+
+
+MASKED = [
+    # B, Hq, Hkv, N, causal, window, docs, d
+    (1, 4, 2, 300, True, 70, None, 128),
+    (1, 2, 2, 257, False, 100, None, 128),
+    (1, 2, 2, 150, True, 1, None, 128),
+    (1, 2, 2, 150, False, 1, None, 64),
+    (1, 2, 2, 100, True, 100, None, 128),           # a window N wide hides nothing
+    (1, 2, 1, 400, True, 0, [0, 37, 170, 171, 400], 128),
+    (2, 4, 2, 333, False, 0, [0, 100, 333], 64),
+    (1, 2, 2, 512, True, 50, [0, 200, 512], 128),
+    (1, 2, 2, 260, False, 33, [0, 129, 260], 64),
+    (1, 2, 2, 64, False, 0, [0, 1, 2, 64], 128),    # one-token documents
+]
+
+
+@pytest.mark.parametrize("case", MASKED, ids=lambda c: "Hq%dHkv%dN%d%sW%d%sd%d" % (
+    c[1], c[2], c[3], "c" if c[4] else "n", c[5], "docs" if c[6] else "", c[7]))
+def test_bwd_masked(case):
+    """Sliding window and packed documents: the band kernels (tiles outside the band are
+    skipped) against the oracle under the same masks, fed the oracle's and the GPU
+    forward's O / LSE."""
+    B, Hq, Hkv, N, causal, window, docs, d = case
+    bits, (q, k, v, g) = _case(N + 7 * Hq + window, B, Hq, Hkv, N, d)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = oracle.attention(q, k, v, causal, scale, window=window, docs=docs)
+    ref = bw.attention_backward(q, k, v, g, causal, scale, o=o, lse=lse, window=window,
+                                docs=docs)
+    log(f"bwd masked case {case}")
+    _check(_run(bits, causal, scale, o, lse, window, docs), ref, "oracle O/LSE")
+    _check(_run(bits, causal, scale, window=window, docs=docs), ref, "GPU forward O/LSE")
+
+
+def test_bwd_masked_long_sequence():
+    """Causal GQA N 2048 with a 256 window over three documents: most tiles lie outside
+    the band; every head checked against the oracle."""
+    B, Hq, Hkv, N = 1, 4, 2, 2048
+    docs = [0, 700, 1500, 2048]
+    bits, (q, k, v, g) = _case(77, B, Hq, Hkv, N)
+    scale = 1.0 / math.sqrt(128)
+    log("bwd masked N2048 W256 docs")
+    got = _run(bits, True, scale, window=256, docs=docs)
+    ref = bw.attention_backward(q, k, v, g, True, scale, window=256, docs=docs)
+    _check(got, ref, "N2048 W256 docs")
