@@ -425,7 +425,15 @@ def main():
     w = synth.workload(args.config)
 
     if args.mode == "launch":
-        wl = BwdWorkload(w) if args.bwd else make_workload(w, args.exp, args.tau, args.poly_frac)
+        off = ([round(x * w.N / args.docs) for x in range(args.docs + 1)] if args.docs
+               else None)
+        if args.bwd:
+            wl = BwdWorkload(w, window=args.window, doc_offsets=off)
+        elif (args.window or off) and w.fmt == "bf16":
+            wl = Workload(w, args.exp, args.tau, args.poly_frac, window=args.window,
+                          doc_offsets=off)
+        else:
+            wl = make_workload(w, args.exp, args.tau, args.poly_frac)
         for _ in range(args.steps):
             wl.launch()
         torch.cuda.synchronize()
