@@ -24,6 +24,14 @@ The masks are the forward's (oracle.exact.visible): causal, sliding window,
 packed documents; a hidden key has s_ij = -inf, so P_ij = 0 and it gets no
 gradient from that query.
 
+The score modifications are the forward's too (oracle.exact.modify_scores:
+soft-capping t = C tanh(s / C), then the ALiBi bias u = t - a_h |i - j|), and P
+is built from the modified score u.  The softmax gives the gradient w.r.t. u,
+dU = P (dP - D); the bias does not depend on q or k, and the chain rule through
+the cap multiplies by dt/ds = 1 - tanh(s / C)^2:
+
+    dS_ij  = dU_ij (1 - tanh(s_ij / C)^2)     (dS = dU without soft-capping)
+
 With grouped-query attention the key/value head hk serves query heads
 hk*g .. hk*g + g - 1 (g = Hq / Hkv), so dK and dV of hk are the sums of those
 query heads' contributions.  A row whose keys are all masked contributes
@@ -33,17 +41,19 @@ and LSE are the forward's (recomputed here from the definition unless given).
 
 import numpy as np
 
-from .exact import apply_mask, attention, scores
+from .exact import apply_mask, attention, modify_scores, scores
 
 
-def backward_head(q, k, v, do, causal, scale, o=None, lse=None, window=0, docs=None):
+def backward_head(q, k, v, do, causal, scale, o=None, lse=None, window=0, docs=None,
+                  softcap=0.0, alibi_slope=None):
     """Gradients for one (batch, query head) slice: q, do [N, d]; k, v [Nk, d].
 
     Returns (dq [N, d], dk [Nk, d], dv [Nk, d]) of that query head alone.
     """
     n = q.shape[0]
     rows = np.arange(n)
-    s = apply_mask(scores(q, k, scale), rows, causal, window, docs)
+    raw = scores(q, k, scale)
+    s = apply_mask(modify_scores(raw, rows, softcap, alibi_slope), rows, causal, window, docs)
     if lse is None or o is None:
         m = s.max(axis=1)
         m_safe = np.where(np.isfinite(m), m, 0.0)
@@ -58,23 +68,28 @@ def backward_head(q, k, v, do, causal, scale, o=None, lse=None, window=0, docs=N
     dp = do @ v.T
     delta = np.sum(do * o, axis=1)
     ds = p * (dp - delta[:, None])
+    if softcap:
+        ds = ds * (1.0 - np.tanh(raw / softcap) ** 2)
     dq = scale * (ds @ k)
     dk = scale * (ds.T @ q)
     return dq, dk, dv
 
 
-def attention_backward(q, k, v, do, causal, scale, o=None, lse=None, window=0, docs=None):
+def attention_backward(q, k, v, do, causal, scale, o=None, lse=None, window=0, docs=None,
+                       softcap=0.0, alibi=None):
     """Gradients over [B, H, N, d] operands: returns (dq, dk, dv) in float64.
 
     o and lse, when given, are the forward's outputs [B, Hq, N, d] and [B, Hq, N];
-    otherwise they are recomputed from the definition (with the same masks).
+    otherwise they are recomputed from the definition (with the same masks and
+    modifications).  alibi: Hq slopes or None; softcap: C (0 = off).
     """
     q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
     g = Hq // Hkv
     if o is None or lse is None:
-        o, lse = attention(q, k, v, causal, scale, window=window, docs=docs)
+        o, lse = attention(q, k, v, causal, scale, window=window, docs=docs, softcap=softcap,
+                           alibi=alibi)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
@@ -82,7 +97,8 @@ def attention_backward(q, k, v, do, causal, scale, o=None, lse=None, window=0, d
         for h in range(Hq):
             hk = h // g
             gq, gk, gv = backward_head(q[b, h], k[b, hk], v[b, hk], do[b, h], causal, scale,
-                                       o[b, h], lse[b, h], window, docs)
+                                       o[b, h], lse[b, h], window, docs, softcap,
+                                       None if alibi is None else float(alibi[h]))
             dq[b, h] = gq
             dk[b, hk] += gk
             dv[b, hk] += gv

@@ -37,13 +37,20 @@ def _mask(n, causal, window, docs):
     return m
 
 
-def _torch_grads(q, k, v, do, causal, scale, window=0, docs=None):
-    """Autograd of a plain float64 softmax attention (GQA by repeating K/V heads)."""
+def _torch_grads(q, k, v, do, causal, scale, window=0, docs=None, softcap=0.0, alibi=None):
+    """Autograd of a plain float64 softmax attention (GQA by repeating K/V heads), with the
+    soft-capping C tanh(s / C) and the ALiBi bias -a_h |i - j| written out."""
     g = q.shape[1] // k.shape[1]
     tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
     kk = tk.repeat_interleave(g, dim=1)
     vv = tv.repeat_interleave(g, dim=1)
     s = scale * torch.matmul(tq, kk.transpose(-1, -2).contiguous())
+    if softcap:
+        s = softcap * torch.tanh(s / softcap)
+    if alibi is not None:
+        n = q.shape[2]
+        dist = (torch.arange(n)[:, None] - torch.arange(n)[None, :]).abs().to(torch.float64)
+        s = s - torch.tensor(alibi, dtype=torch.float64)[None, :, None, None] * dist
     if causal or window or docs is not None:
         s = s.masked_fill(~_mask(q.shape[2], causal, window, docs), float("-inf"))
     o = torch.matmul(torch.softmax(s, dim=-1), vv)
@@ -73,6 +80,67 @@ def test_masked_matches_torch_autograd(causal, window, docs):
     ref = _torch_grads(q, k, v, do, causal, 0.6, window, docs)
     for a, b in zip(got, ref):
         assert np.allclose(a, b, atol=1e-12, rtol=1e-10)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("softcap,alibi,window", [(2.5, None, 0), (0.0, [0.3, 0.05, 0.7, 0.0], 0),
+                                                  (1.5, [0.2, 0.4, 0.1, 0.9], 5)])
+def test_modified_scores_match_torch_autograd(causal, softcap, alibi, window):
+    """Soft-capping and ALiBi (with a window too): the chain rule through the cap, against
+    autograd; large logits (sigma 2) so that the cap bends the scores."""
+    q, k, v, do = _case(41, 1, 4, 2, 18, 8, sigma=2.0)
+    got = bw.attention_backward(q, k, v, do, causal, 0.5, window=window, softcap=softcap,
+                                alibi=alibi)
+    ref = _torch_grads(q, k, v, do, causal, 0.5, window, None, softcap, alibi)
+    for a, b in zip(got, ref):
+        assert np.allclose(a, b, atol=1e-12, rtol=1e-10)
+
+
+def test_modified_scores_finite_differences():
+    """Central differences through the cap and the bias on a tiny case."""
+    q, k, v, do = _case(42, 1, 1, 1, 6, 2, sigma=2.0)
+    alibi = [0.25]
+    dq, dk, dv = bw.attention_backward(q, k, v, do, True, 0.9, softcap=1.2, alibi=alibi)
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.attention(qq, kk, vv, True, 0.9, softcap=1.2, alibi=alibi)
+        return float(np.sum(o * do))
+
+    h = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            fd = (loss(*[xp if y is x else y for y in (q, k, v)]) -
+                  loss(*[xm if y is x else y for y in (q, k, v)])) / (2 * h)
+            assert abs(fd - g[idx]) < 1e-7, (idx, fd, g[idx])
+
+
+def test_dropped_cap_derivative_is_caught(monkeypatch):
+    """A backward that forgets the 1 - tanh^2 factor fails the autograd pin."""
+    orig = bw.backward_head
+
+    def no_cap_factor(q, k, v, do, causal, scale, o=None, lse=None, window=0, docs=None,
+                      softcap=0.0, alibi_slope=None):
+        dq, dk, dv = orig(q, k, v, do, causal, scale, o, lse, window, docs, softcap,
+                          alibi_slope)
+        if softcap:   # undo the factor: recompute with the cap only in P
+            rows = np.arange(q.shape[0])
+            raw = oracle.exact.scores(q, k, scale)
+            fac = 1.0 - np.tanh(raw / softcap) ** 2
+            s = oracle.exact.apply_mask(oracle.exact.modify_scores(raw, rows, softcap,
+                                                                   alibi_slope),
+                                        rows, causal, window, docs)
+            p = np.exp(s - lse[:, None])
+            ds = p * (do @ v.T - np.sum(do * o, axis=1)[:, None])
+            assert np.all(fac > 0)
+            return scale * ds @ k, scale * ds.T @ q, dv
+        return dq, dk, dv
+
+    monkeypatch.setattr(bw, "backward_head", no_cap_factor)
+    with pytest.raises(AssertionError):
+        test_modified_scores_match_torch_autograd(False, 2.5, None, 0)
 
 
 def test_masked_finite_differences_and_isolation():
@@ -160,8 +228,10 @@ def test_given_forward_outputs_equal_recomputed():
 def test_planted_mistakes_are_caught(bad, monkeypatch):
     orig = bw.backward_head
 
-    def mutated(q, k, v, do, causal, scale, o=None, lse=None, window=0, docs=None):
-        dq, dk, dv = orig(q, k, v, do, causal, scale, o, lse, window, docs)
+    def mutated(q, k, v, do, causal, scale, o=None, lse=None, window=0, docs=None,
+                softcap=0.0, alibi_slope=None):
+        dq, dk, dv = orig(q, k, v, do, causal, scale, o, lse, window, docs, softcap,
+                          alibi_slope)
         if bad == "no_delta":
             rows = np.arange(q.shape[0])
             s = oracle.exact.apply_mask(scale * q @ k.T, rows, causal, window, docs)
@@ -178,8 +248,10 @@ def test_planted_mistakes_are_caught(bad, monkeypatch):
     if bad == "gqa_last_head":
         orig_all = bw.attention_backward
 
-        def keep_last(q, k, v, do, causal, scale, o=None, lse=None, window=0, docs=None):
-            dq, dk, dv = orig_all(q, k, v, do, causal, scale, o, lse, window, docs)
+        def keep_last(q, k, v, do, causal, scale, o=None, lse=None, window=0, docs=None,
+                      softcap=0.0, alibi=None):
+            dq, dk, dv = orig_all(q, k, v, do, causal, scale, o, lse, window, docs, softcap,
+                                  alibi)
             g = q.shape[1] // k.shape[1]
             if g > 1:   # as if only the group's last query head were counted
                 for hk in range(k.shape[1]):
