@@ -336,11 +336,12 @@ def fwd_mxfp8(q8, qs, k8, ks, vt8, vts, causal=False, scale=None, tau=8.0, stats
 
 
 def bwd(q, k, v, o, lse, dout, causal=False, scale=None, out=None, delta=None, window=0,
-        docs=None):
+        docs=None, alibi=None, softcap=0.0):
     """bf16 attention backward: returns (dQ fp32 [B,Hq,N,d], dK, dV fp32 [B,Hkv,N,d]).
     o, lse: the forward's outputs for the same q, k, v (fp32); dout: bf16 like q.
-    delta: optional fp32 CUDA workspace of B*Hq*N floats.  window, docs: the forward's
-    sliding window and document offsets (as for fwd)."""
+    delta: optional fp32 CUDA workspace of B*Hq*N floats.  window, docs, alibi, softcap:
+    the forward's sliding window, document offsets, ALiBi slopes and soft-capping (as for
+    fwd)."""
     torch = _torch()
     for t in (q, k, v, dout):
         if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
@@ -371,7 +372,14 @@ def bwd(q, k, v, o, lse, dout, causal=False, scale=None, out=None, delta=None, w
                 or docs.numel() < 2:
             raise ValueError("docs must be a contiguous int32 CUDA tensor of document offsets")
         doc_ptr, n_docs = docs.data_ptr(), docs.numel() - 1
-    opts = make_opts(window=window, doc_ptr=doc_ptr, n_docs=n_docs)
+    alibi_ptr = None
+    if alibi is not None:
+        if (alibi.dtype != torch.float32 or not alibi.is_cuda or not alibi.is_contiguous()
+                or alibi.numel() != Hq):
+            raise ValueError("alibi must be a contiguous float32 CUDA tensor of Hq slopes")
+        alibi_ptr = alibi.data_ptr()
+    opts = make_opts(window=window, doc_ptr=doc_ptr, n_docs=n_docs, alibi_ptr=alibi_ptr,
+                     softcap=softcap)
     check(attn_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                       dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                       delta.data_ptr(), B, Hq, Hkv, N, d, int(bool(causal)), float(scale), opts,

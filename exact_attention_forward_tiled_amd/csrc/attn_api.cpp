@@ -171,7 +171,6 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const float* o, con
   const attn_opts* op = opts ? opts : &def;
   st = check_opts(op);
   if (st != ATTN_OK) return st;
-  if (op->alibi_slopes != nullptr || op->softcap != 0.f) return ATTN_EUNSUPPORTED;
   if (d != 64 && d != 128) return ATTN_EUNSUPPORTED;
   if ((long long)B * Hkv * ((N + 127) / 128) >= (1LL << 31) ||
       (long long)B * Hq * ((N + 127) / 128) >= (1LL << 31))
@@ -185,6 +184,8 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const float* o, con
   a.doc_offsets = op->doc_offsets;
   a.n_docs = op->doc_offsets != nullptr ? op->n_docs : 0;
   if (a.n_docs > N) return ATTN_EINVAL;   // documents are non-empty
+  a.alibi = op->alibi_slopes;
+  a.softcap = op->softcap;
   a.c = scale * 1.4426950408889634f;
   a.scale = scale;
   a.stream = stream;

@@ -22,6 +22,8 @@
 // expects from that lane: the probabilities go from one MFMA to the next
 // without any data movement.
 
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -189,15 +191,25 @@ __global__ void delta_kernel(const float* __restrict__ O, const uint16_t* __rest
   if (row < rows && part == 0) D[row] = acc;
 }
 
+// The forward's score modifications, on the scaled score s (log2 units below): soft-capping
+// t = C tanh(s / C), then the ALiBi bias t -= a_h |i - j|.  P is rebuilt from the modified
+// score, and the cap's chain rule multiplies dS by dt/ds = 1 - tanh(s / C)^2.
+struct Mods {
+  const float* alibi;   // Hq slopes (natural units), or null
+  float k2;             // soft-capping: 2 scale log2(e) / C (raw q.k to 2 s log2(e) / C); 0 = off
+  float ccap;           // soft-capping: C log2(e)
+};
+
 // dK, dV for 128 keys of one (batch, kv head): each wave owns 32 keys; the loop runs
 // over the group's query heads and their 64-query tiles (causal: only tiles that reach
 // the workgroup's keys; BAND: only tiles within the keys' window and documents).
-template <int D, bool CAUSAL, bool BAND>
+template <int D, bool CAUSAL, bool BAND, bool MODS>
 __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Delta, float* __restrict__ dK,
-    float* __restrict__ dV, int Hq, int Hkv, int N, int nkb, float c, float scale, Band band) {
+    float* __restrict__ dV, int Hq, int Hkv, int N, int nkb, float c, float scale, Band band,
+    Mods mods) {
   __shared__ BTile<D> tile;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n32 = lane & 31, h = lane >> 5;
@@ -271,6 +283,10 @@ __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
   if (nsteps > 0) fetch(0);
   for (int st = 0; st < nsteps; ++st) {
     const int q0 = step_q0(st);
+    // ALiBi slope of this step's query head, log2 units (0: no bias)
+    const float slope2 =
+        (MODS && mods.alibi != nullptr)
+            ? mods.alibi[hkv * group + st / steps_per_head] * kLog2e : 0.f;
     {
       __syncthreads();
       stage_store(tile, sr, true, true);
@@ -308,18 +324,53 @@ __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
           l4[i] = *(const f32x4*)(tile.s0 + r0);
           d4[i] = *(const f32x4*)(tile.s1 + r0);
         }
-        // P and dS; register r holds query qs + acc_row(r, h) for this lane's key
+        // P and dS; register r holds query qs + acc_row(r, h) for this lane's key.  CAP:
+        // soft-capping (a uniform choice, made once around the loop)
         f32x16 p, ds;
+        auto elements = [&](auto cap_tag) {
+          constexpr bool CAP = decltype(cap_tag)::value;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = acc_row(r, h);
-          const float x = __builtin_fmaf(s[r] + s2[r], c, -l4[r >> 2][r & 3]);
-          // non-short-circuit: evaluated whole, so no branch per element
-          const bool vis = BAND ? ((key < N) & (qs + qi >= kq_lo) & (qs + qi <= kq_hi))
-                                : (key < N && (!CAUSAL || key <= qs + qi));
-          const float pr = vis ? __builtin_amdgcn_exp2f(x) : 0.f;
-          p[r] = pr;
-          ds[r] = pr * (dp[r] + dp2[r] - d4[r >> 2][r & 3]);
+          for (int r = 0; r < 16; ++r) {
+            const int qi = acc_row(r, h);
+            float x, dfac = 1.f;
+            if constexpr (MODS) {
+              const float raw = s[r] + s2[r];
+              float t = raw * c;
+              if constexpr (CAP) {
+                const float y = __builtin_amdgcn_exp2f(raw * mods.k2);
+                const float th = __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(y + 1.f), 1.f);
+                t = mods.ccap * th;
+                dfac = __builtin_fmaf(-th, th, 1.f);
+              }
+              t = __builtin_fmaf(-slope2, __builtin_fabsf((float)(key - (qs + qi))), t);
+              x = t - l4[r >> 2][r & 3];
+            } else {
+              x = __builtin_fmaf(s[r] + s2[r], c, -l4[r >> 2][r & 3]);
+            }
+            // non-short-circuit: evaluated whole, so no branch per element
+            const bool vis = BAND ? ((key < N) & (qs + qi >= kq_lo) & (qs + qi <= kq_hi))
+                                  : (key < N && (!CAUSAL || key <= qs + qi));
+            const float pr = vis ? __builtin_amdgcn_exp2f(x) : 0.f;
+            p[r] = pr;
+            const float g = pr * (dp[r] + dp2[r] - d4[r >> 2][r & 3]);
+            ds[r] = CAP ? g * dfac : g;
+          }
+        };
+        if constexpr (MODS) {
+          if (mods.k2 != 0.f) elements(std::true_type{});
+          else elements(std::false_type{});
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qi = acc_row(r, h);
+            const float x = __builtin_fmaf(s[r] + s2[r], c, -l4[r >> 2][r & 3]);
+            // non-short-circuit: evaluated whole, so no branch per element
+            const bool vis = BAND ? ((key < N) & (qs + qi >= kq_lo) & (qs + qi <= kq_hi))
+                                  : (key < N && (!CAUSAL || key <= qs + qi));
+            const float pr = vis ? __builtin_amdgcn_exp2f(x) : 0.f;
+            p[r] = pr;
+            ds[r] = pr * (dp[r] + dp2[r] - d4[r >> 2][r & 3]);
+          }
         }
         // dV^T += dO^T P and dK^T += Q^T dS (d x keys), over the two 16-query chunks
 #pragma unroll
@@ -339,7 +390,7 @@ __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
       // causal and band forms, with their masks, both halves' scores live at once push the
       // K / V operands into AGPRs (415 register moves per step against 128), so the halves
       // run one after the other.
-      if constexpr (CAUSAL || BAND) {
+      if constexpr (CAUSAL || BAND || MODS) {
 #pragma unroll 1
         for (int sub = 0; sub < kBTile / kSub; ++sub) half(sub);
       } else {
@@ -372,12 +423,12 @@ __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
 // the queries' window and documents).
 // Two waves per SIMD (at most 256 registers each; two workgroups' tiles fit the CU's LDS),
 // so one workgroup's products overlap the other's exponentials and staging.
-template <int D, bool CAUSAL, bool BAND>
-__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(
+template <int D, bool CAUSAL, bool BAND, bool MODS>
+__device__ __forceinline__ void dq_body(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Delta, float* __restrict__ dQ,
-    int Hq, int Hkv, int N, int nqb, float c, float scale, Band band) {
+    int Hq, int Hkv, int N, int nqb, float c, float scale, Band band, Mods mods) {
   __shared__ BTile<D> tile;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n32 = lane & 31, h = lane >> 5;
@@ -445,7 +496,9 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     if (!BAND && CAUSAL && k0 > qw0 + 31) continue;
     if (BAND && (qw0 >= N || k0 > w_hi || k0 + kBTile - 1 < w_lo)) continue;
     // one 32-key half: S^T and dP^T, then dS^T, then the dQ products
-    constexpr bool kTwoChains = !(BAND && D == 128);
+    constexpr bool kTwoChains = !((BAND || MODS) && D == 128);
+    // ALiBi slope of this query head, log2 units (0: no bias)
+    const float slope2 = (MODS && mods.alibi != nullptr) ? mods.alibi[hq] * kLog2e : 0.f;
     auto half = [&](int sub) {
       const int ks = k0 + kSub * sub;
       // S^T = K_pi Q^T and dP^T = V_pi dO^T (keys x queries; rows permuted), two chains
@@ -465,8 +518,11 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
           dp = mfma_bf16(lds_u32x4(vr + 32), gop[cc + 1], dp);
         }
       }
-      // dS^T; register r holds key ks + acc_row(r, h) for this lane's query
+      // dS^T; register r holds key ks + acc_row(r, h) for this lane's query.  CAP:
+      // soft-capping (a uniform choice, made once around the loop)
       f32x16 ds;
+      auto elements = [&](auto cap_tag) {
+      constexpr bool CAP = decltype(cap_tag)::value;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kj = ks + acc_row(r, h);
@@ -478,9 +534,26 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         const float sv = kTwoChains ? s[r] + s2[r] : s[r];
         const float dpv = kTwoChains ? dp[r] + dp2[r] : dp[r];
         // hidden: 2^-inf = 0 (a select, not a branch around the exponential)
-        const float x = vis ? __builtin_fmaf(sv, c, -lse2) : -__builtin_inff();
-        ds[r] = __builtin_amdgcn_exp2f(x) * (dpv - dlt);
+        if constexpr (MODS) {
+          float t = sv * c, dfac = 1.f;
+          if constexpr (CAP) {
+            const float y = __builtin_amdgcn_exp2f(sv * mods.k2);
+            const float th = __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(y + 1.f), 1.f);
+            t = mods.ccap * th;
+            dfac = __builtin_fmaf(-th, th, 1.f);
+          }
+          t = __builtin_fmaf(-slope2, __builtin_fabsf((float)(kj - qi)), t);
+          const float x = vis ? t - lse2 : -__builtin_inff();
+          const float g = __builtin_amdgcn_exp2f(x) * (dpv - dlt);
+          ds[r] = CAP ? g * dfac : g;
+        } else {
+          const float x = vis ? __builtin_fmaf(sv, c, -lse2) : -__builtin_inff();
+          ds[r] = __builtin_amdgcn_exp2f(x) * (dpv - dlt);
+        }
       }
+      };
+      if (MODS && mods.k2 != 0.f) elements(std::true_type{});
+      else elements(std::false_type{});
       // dQ^T += K^T dS^T (d x queries), over the two 16-key chunks
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
@@ -493,9 +566,9 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         }
       }
     };
-    // unrolled, one half's exponentials overlap the other's products; the band form's
-    // extra bounds would push that past the 256 registers of two waves per SIMD
-    if constexpr (BAND) {
+    // unrolled, one half's exponentials overlap the other's products; the band and
+    // modified forms' extra work would push that past the 256 registers of two waves per SIMD
+    if constexpr (BAND || MODS) {
 #pragma unroll 1
       for (int sub = 0; sub < kBTile / kSub; ++sub) half(sub);
     } else {
@@ -516,7 +589,29 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   }
 }
 
-template <int D, bool CAUSAL, bool BAND>
+template <int D, bool CAUSAL, bool BAND, bool MODS>
+__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    const float* __restrict__ LSE, const float* __restrict__ Delta, float* __restrict__ dQ,
+    int Hq, int Hkv, int N, int nqb, float c, float scale, Band band, Mods mods) {
+  dq_body<D, CAUSAL, BAND, MODS>(Q, K, V, dO, LSE, Delta, dQ, Hq, Hkv, N, nqb, c, scale, band,
+                                 mods);
+}
+
+// The same at one wave per SIMD (up to 512 registers): the soft-capping and ALiBi form at
+// d = 128, whose per-element work does not fit the 256 registers of two waves per SIMD.
+template <int D, bool CAUSAL, bool BAND, bool MODS>
+__global__ __launch_bounds__(kBThreads) void dq_kernel_1w(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    const float* __restrict__ LSE, const float* __restrict__ Delta, float* __restrict__ dQ,
+    int Hq, int Hkv, int N, int nqb, float c, float scale, Band band, Mods mods) {
+  dq_body<D, CAUSAL, BAND, MODS>(Q, K, V, dO, LSE, Delta, dQ, Hq, Hkv, N, nqb, c, scale, band,
+                                 mods);
+}
+
+template <int D, bool CAUSAL, bool BAND, bool MODS>
 hipError_t launch_bwd_t(const BwdArgs& a) {
   const long long rows = (long long)a.B * a.Hq * a.N;
   constexpr int kRowsPerBlock = 256 / (D / 8);
@@ -527,24 +622,40 @@ hipError_t launch_bwd_t(const BwdArgs& a) {
   if (e != hipSuccess) return e;
   const int nb = (a.N + kBBlock - 1) / kBBlock;
   const Band band{a.N, a.window, a.n_docs, a.doc_offsets};
-  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, BAND>), dim3((unsigned)(a.B * a.Hkv * nb)),
+  const Mods mods{a.alibi, a.softcap > 0.f ? 2.f * a.c / a.softcap : 0.f,
+                  a.softcap * kLog2e};
+  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, BAND, MODS>), dim3((unsigned)(a.B * a.Hkv * nb)),
                      dim3(kBThreads), 0, (hipStream_t)a.stream, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse,
-                     a.delta, a.dk, a.dv, a.Hq, a.Hkv, a.N, nb, a.c, a.scale, band);
+                     a.delta, a.dk, a.dv, a.Hq, a.Hkv, a.N, nb, a.c, a.scale, band, mods);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((dq_kernel<D, CAUSAL, BAND>), dim3((unsigned)(a.B * a.Hq * nb)), dim3(kBThreads),
-                     0, (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                     (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta, a.dq,
-                     a.Hq, a.Hkv, a.N, nb, a.c, a.scale, band);
+  const dim3 grid((unsigned)(a.B * a.Hq * nb));
+  if constexpr (MODS && D == 128)
+    hipLaunchKernelGGL((dq_kernel_1w<D, CAUSAL, BAND, MODS>), grid, dim3(kBThreads), 0,
+                       (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                       (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta, a.dq,
+                       a.Hq, a.Hkv, a.N, nb, a.c, a.scale, band, mods);
+  else
+    hipLaunchKernelGGL((dq_kernel<D, CAUSAL, BAND, MODS>), grid, dim3(kBThreads), 0,
+                       (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                       (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta, a.dq,
+                       a.Hq, a.Hkv, a.N, nb, a.c, a.scale, band, mods);
   return hipGetLastError();
+}
+
+template <int D, bool MODS>
+hipError_t launch_bwd_dm(const BwdArgs& a) {
+  const bool band = a.window > 0 || a.n_docs > 0;
+  if (a.causal)
+    return band ? launch_bwd_t<D, true, true, MODS>(a) : launch_bwd_t<D, true, false, MODS>(a);
+  return band ? launch_bwd_t<D, false, true, MODS>(a) : launch_bwd_t<D, false, false, MODS>(a);
 }
 
 template <int D>
 hipError_t launch_bwd_d(const BwdArgs& a) {
-  const bool band = a.window > 0 || a.n_docs > 0;
-  if (a.causal) return band ? launch_bwd_t<D, true, true>(a) : launch_bwd_t<D, true, false>(a);
-  return band ? launch_bwd_t<D, false, true>(a) : launch_bwd_t<D, false, false>(a);
+  return (a.alibi != nullptr || a.softcap > 0.f) ? launch_bwd_dm<D, true>(a)
+                                                 : launch_bwd_dm<D, false>(a);
 }
 
 }  // namespace

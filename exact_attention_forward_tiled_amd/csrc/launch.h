@@ -59,6 +59,8 @@ struct BwdArgs {
   int window;           // sliding window W (0: none; 1 <= W < N), as in FwdArgs
   const int* doc_offsets;   // device, n_docs + 1 document offsets (0, ..., N), or null
   int n_docs;           // documents (0: no document masking)
+  const float* alibi;   // device, Hq ALiBi slopes, or null
+  float softcap;        // soft-capping C (0: off)
   float c;              // scale * log2(e)
   float scale;
   void* stream;

@@ -225,13 +225,15 @@ int attn_bwd(const void* q, const void* k, const void* v, const float* o, const 
              int B, int Hq, int Hkv, int N, int d, int causal, float scale, void* stream);
 
 /*
- * bf16 backward with the forward's masking options: opts->window and opts->doc_offsets /
- * n_docs (the same meaning, ranges and errors as for attn_fwd_ex; pass the options the
- * forward ran with).  A window at least N wide is no window.  The tiles wholly outside a
- * block's band are skipped in both gradient kernels.  ALiBi or soft-capping
- * (alibi_slopes != NULL, softcap != 0): ATTN_EUNSUPPORTED.  tau, exp_mode, poly_frac and
- * stats are forward-only and ignored (still validated).  opts NULL = attn_bwd.  The
- * document offsets are read on `stream` during the call.
+ * bf16 backward with the forward's options: opts->window, opts->doc_offsets / n_docs,
+ * opts->alibi_slopes and opts->softcap (the same meaning, ranges and errors as for
+ * attn_fwd_ex; pass the options the forward ran with).  A window at least N wide is no
+ * window; the tiles wholly outside a block's band are skipped in both gradient kernels.
+ * With the score modifications P is rebuilt from the modified score, and soft-capping
+ * multiplies dS by its derivative 1 - tanh(s / C)^2 (the ALiBi bias does not depend on
+ * q or k).  tau, exp_mode, poly_frac and stats are forward-only and ignored (still
+ * validated).  opts NULL = attn_bwd.  The document offsets and slopes are read on
+ * `stream` during the call.
  */
 int attn_bwd_ex(const void* q, const void* k, const void* v, const float* o, const float* lse,
                 const void* dout, float* dq, float* dk, float* dv, float* delta,

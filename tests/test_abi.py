@@ -155,8 +155,9 @@ def test_bwd_ex_validation(fa):
     assert fa.attn_bwd_ex(*base, *shape, fa.make_opts(window=-1)) == -1
     assert fa.attn_bwd_ex(*base, *shape, fa.make_opts(doc_ptr=FAKE, n_docs=0)) == -1
     assert fa.attn_bwd_ex(*base, *shape, fa.make_opts(doc_ptr=FAKE, n_docs=65)) == -1
-    assert fa.attn_bwd_ex(*base, *shape, fa.make_opts(alibi_ptr=FAKE)) == -2
-    assert fa.attn_bwd_ex(*base, *shape, fa.make_opts(softcap=5.0)) == -2
+    assert fa.attn_bwd_ex(*base, *shape, fa.make_opts(softcap=-1.0)) == -1
+    assert fa.attn_bwd_ex(*base, *shape, fa.make_opts(softcap=float("inf"))) == -1
+    assert fa.attn_bwd_ex(*base, 1, 2, 2, 64, 96, 0, 0.1, fa.make_opts(softcap=5.0)) == -2
     assert fa.attn_bwd_ex(*base, *shape, fa.make_opts(tau=-1.0)) == -1
     assert fa.attn_bwd_ex(*base, 1, 2, 2, 64, 96, 0, 0.1, fa.make_opts(window=8)) == -2
     args = list(base)

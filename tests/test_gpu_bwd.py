@@ -27,15 +27,17 @@ def _case(seed, B, Hq, Hkv, N, d=128):
     return (qb, kb, vb, gb), tuple(synth.bf16_bits_to_f64(x) for x in (qb, kb, vb, gb))
 
 
-def _run(bits, causal, scale, o=None, lse=None, window=0, docs=None):
+def _run(bits, causal, scale, o=None, lse=None, window=0, docs=None, alibi=None, softcap=0.0):
     """GPU backward; o, lse: float64 arrays to feed, else the GPU forward's outputs (with the
-    same window and documents)."""
+    same window, documents, ALiBi slopes and soft-capping)."""
     import torch
     import exact_attention_forward_tiled_amd as fa
     q, k, v, g = (to_dev_bf16(x) for x in bits)
     dd = None if docs is None else torch.tensor(docs, dtype=torch.int32, device="cuda")
+    al = None if alibi is None else torch.tensor(alibi, dtype=torch.float32, device="cuda")
     if o is None:
-        od, ld = fa.fwd(q, k, v, causal=causal, scale=scale, window=window, docs=dd)
+        od, ld = fa.fwd(q, k, v, causal=causal, scale=scale, window=window, docs=dd, alibi=al,
+                        softcap=softcap)
     else:
         od, ld = to_dev_f32(o), to_dev_f32(lse)
     B, Hq, N, d = q.shape
@@ -45,7 +47,7 @@ def _run(bits, causal, scale, o=None, lse=None, window=0, docs=None):
     dk = torch.full((B, Hkv, N, d), nan, dtype=torch.float32, device="cuda")
     dv = torch.full((B, Hkv, N, d), nan, dtype=torch.float32, device="cuda")
     fa.bwd(q, k, v, od, ld, g, causal=causal, scale=scale, out=(dq, dk, dv), window=window,
-           docs=dd)
+           docs=dd, alibi=al, softcap=softcap)
     torch.cuda.synchronize()
     return dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
 
@@ -181,3 +183,34 @@ def test_bwd_masked_long_sequence():
     got = _run(bits, True, scale, window=256, docs=docs)
     ref = bw.attention_backward(q, k, v, g, True, scale, window=256, docs=docs)
     _check(got, ref, "N2048 W256 docs")
+
+
+MODIFIED = [
+    # B, Hq, Hkv, N, causal, window, docs, d, softcap, ALiBi (slopes 2^(-8 h / Hq) * a)
+    (1, 4, 2, 300, True, 0, None, 128, 2.0, 0.0),
+    (1, 2, 2, 257, False, 0, None, 128, 0.0, 1.0),
+    (1, 4, 2, 200, True, 0, None, 128, 1.5, 0.5),
+    (1, 2, 2, 190, False, 64, None, 64, 3.0, 1.0),
+    (1, 2, 1, 300, True, 0, [0, 100, 300], 128, 2.0, 0.0),
+    (2, 2, 2, 130, False, 0, None, 64, 1.0, 0.0),
+    (1, 2, 2, 96, True, 0, None, 64, 0.0, 2.0),
+]
+
+
+@pytest.mark.parametrize("case", MODIFIED, ids=lambda c: "Hq%dHkv%dN%d%sW%d%sd%dC%gA%g" % (
+    c[1], c[2], c[3], "c" if c[4] else "n", c[5], "docs" if c[6] else "", c[7], c[8], c[9]))
+def test_bwd_score_modifications(case):
+    """Soft-capping and ALiBi (alone, together, with a window or documents): P rebuilt from
+    the modified score and dS times the cap's derivative, against the oracle."""
+    B, Hq, Hkv, N, causal, window, docs, d, softcap, a = case
+    bits, (q, k, v, g) = _case(3 * N + Hq + d, B, Hq, Hkv, N, d)
+    scale = 1.0 / math.sqrt(d)
+    alibi = [a * 2.0 ** (-8.0 * (h + 1) / Hq) for h in range(Hq)] if a else None
+    o, lse = oracle.attention(q, k, v, causal, scale, window=window, docs=docs, softcap=softcap,
+                              alibi=alibi)
+    ref = bw.attention_backward(q, k, v, g, causal, scale, o=o, lse=lse, window=window,
+                                docs=docs, softcap=softcap, alibi=alibi)
+    log(f"bwd modified case {case}")
+    _check(_run(bits, causal, scale, o, lse, window, docs, alibi, softcap), ref, "oracle O/LSE")
+    _check(_run(bits, causal, scale, window=window, docs=docs, alibi=alibi, softcap=softcap),
+           ref, "GPU forward O/LSE")
