@@ -11,7 +11,10 @@
 //   dV   = P^T dO,  dK = scale dS^T Q          (dkdv_kernel, one workgroup per key block)
 //   dQ   = scale dS K                          (dq_kernel, one workgroup per query block)
 // Each kernel recomputes S and dP for its own orientation, so every output is
-// written once by one workgroup: no atomics, deterministic results.
+// written once by one workgroup: no atomics, deterministic results.  The forward's
+// masks (causal, sliding window, documents) and score modifications (soft-capping,
+// ALiBi) apply unchanged: P comes from the modified, masked score, and soft-capping
+// multiplies dS by its derivative.
 //
 // All products run on v_mfma_f32_32x32x16_bf16.  Operand layouts (probed): lane l
 // holds A[l % 32][8*(l / 32) + i] and B[8*(l / 32) + i][l % 32], i = 0..7;
@@ -421,8 +424,7 @@ __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
 // dQ for 128 queries of one (batch, query head): each wave owns 32 queries; the loop
 // runs over 64-key tiles (causal: up to the workgroup's last query; BAND: the tiles within
 // the queries' window and documents).
-// Two waves per SIMD (at most 256 registers each; two workgroups' tiles fit the CU's LDS),
-// so one workgroup's products overlap the other's exponentials and staging.
+// (The body; the kernels below set the waves per SIMD.)
 template <int D, bool CAUSAL, bool BAND, bool MODS>
 __device__ __forceinline__ void dq_body(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -589,6 +591,8 @@ __device__ __forceinline__ void dq_body(
   }
 }
 
+// Two waves per SIMD (at most 256 registers each; two workgroups' tiles fit the CU's LDS),
+// so one workgroup's products overlap the other's exponentials and staging.
 template <int D, bool CAUSAL, bool BAND, bool MODS>
 __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
