@@ -91,13 +91,16 @@ def device_inputs(w):
 class Workload:
     """Device buffers and one launch closure for a bf16 workload."""
 
-    def __init__(self, w, exp_mode, tau, poly_frac=None, window=0, doc_offsets=None):
+    def __init__(self, w, exp_mode, tau, poly_frac=None, window=0, doc_offsets=None,
+                 alibi=False, softcap=0.0):
         import torch
         import exact_attention_forward_tiled_amd as fa
         self.w = w
         self.window = window
         self.docs = (None if doc_offsets is None else
                      torch.tensor(doc_offsets, dtype=torch.int32, device="cuda"))
+        self.alibi = alibi_slopes(w.Hq) if alibi else None
+        self.softcap = softcap
         self.q, self.k, self.v = device_inputs(w)
         self.o = torch.empty((w.B, w.Hq, w.N, w.d), dtype=torch.float32, device="cuda")
         self.lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device="cuda")
@@ -107,7 +110,15 @@ class Workload:
     def launch(self, stats=None):
         self.fa.fwd(self.q, self.k, self.v, causal=self.w.causal, scale=self.w.scale, tau=self.tau,
                     exp_mode=self.exp_mode, stats=stats, out=(self.o, self.lse),
-                    poly_frac=self.poly_frac, window=self.window, docs=self.docs)
+                    poly_frac=self.poly_frac, window=self.window, docs=self.docs,
+                    alibi=self.alibi, softcap=self.softcap)
+
+
+def alibi_slopes(H):
+    """The usual geometric ALiBi slopes 2^(-8 h / H), h = 1 .. H (float32 on the device)."""
+    import torch
+    return torch.tensor([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=torch.float32,
+                        device="cuda")
 
 
 class Mxfp4Workload:
@@ -167,7 +178,7 @@ class BwdWorkload:
     a seeded dO, then the three backward kernels per step (with the forward's sliding window
     and / or documents when given)."""
 
-    def __init__(self, w, window=0, doc_offsets=None):
+    def __init__(self, w, window=0, doc_offsets=None, alibi=False, softcap=0.0):
         import torch
         import exact_attention_forward_tiled_amd as fa
         import synth
@@ -175,9 +186,12 @@ class BwdWorkload:
         self.window = window
         self.docs = (None if doc_offsets is None else
                      torch.tensor(doc_offsets, dtype=torch.int32, device="cuda"))
+        self.alibi = alibi_slopes(w.Hq) if alibi else None
+        self.softcap = softcap
         self.q, self.k, self.v = device_inputs(w)
         self.o, self.lse = fa.fwd(self.q, self.k, self.v, causal=w.causal, scale=w.scale,
-                                  window=window, docs=self.docs)
+                                  window=window, docs=self.docs, alibi=self.alibi,
+                                  softcap=softcap)
         gb = synth.normal_bf16((w.B, w.Hq, w.N, w.d), 1000 * w.index + 4, 1.0)
         self.do = device_inputs_bits(gb)
         self.dq = torch.empty((w.B, w.Hq, w.N, w.d), dtype=torch.float32, device="cuda")
@@ -190,7 +204,7 @@ class BwdWorkload:
     def launch(self, stats=None):
         self.fa.bwd(self.q, self.k, self.v, self.o, self.lse, self.do, causal=self.w.causal,
                     scale=self.w.scale, out=(self.dq, self.dk, self.dv), delta=self.delta,
-                    window=self.window, docs=self.docs)
+                    window=self.window, docs=self.docs, alibi=self.alibi, softcap=self.softcap)
 
 
 def device_inputs_bits(bits):
@@ -386,6 +400,10 @@ def main():
     ap.add_argument("--window", type=int, default=0,
                     help="also time the workload with this sliding window (bf16 only); its "
                          "TFLOP/s count 4*d flop per visible (query, key) pair")
+    ap.add_argument("--softcap", type=float, default=0.0,
+                    help="also time the workload with soft-capping C (bf16 only)")
+    ap.add_argument("--alibi", action="store_true",
+                    help="also time the workload with ALiBi slopes 2^(-8h/H) (bf16 only)")
     ap.add_argument("--bwd", action="store_true",
                     help="also time the bf16 backward (dQ, dK, dV) on the workload; TFLOP/s "
                          "count 2.5x the forward's FLOPs (five products)")
@@ -522,6 +540,25 @@ def main():
             "visible_pairs_per_head": pairs,
             "time_vs_one_document": round(td["kernel_ms_avg"] / t["kernel_ms_avg"], 4)}
 
+    mods = []
+    if args.softcap:
+        mods.append((f"softcap={args.softcap:g}", {"softcap": args.softcap}))
+    if args.alibi:
+        mods.append(("alibi", {"alibi": True}))
+    if args.softcap and args.alibi:
+        mods.append((f"softcap={args.softcap:g}+alibi", {"softcap": args.softcap, "alibi": True}))
+    if w.fmt == "bf16":
+        for tag, kw in mods:
+            log(f"timing {w.name} with {tag}")
+            wl = Workload(w, "hw", args.tau, None, **kw)
+            tm = time_workload(wl, args.steps, args.warmup, args.warmup_seconds)
+            del wl
+            torch.cuda.empty_cache()
+            extra["workloads"][f"{w.name}/{tag}"] = {
+                "tflops": round(tm["tflops"], 2),
+                "kernel_ms_avg": round(tm["kernel_ms_avg"], 4),
+                "time_vs_plain": round(tm["kernel_ms_avg"] / t["kernel_ms_avg"], 4)}
+
     if args.bwd and w.fmt == "bf16":
         log(f"timing the backward on {w.name}")
         wl = BwdWorkload(w)
@@ -542,6 +579,16 @@ def main():
         if args.docs:
             masked.append((f"bwd/docs={args.docs}", 0,
                            [round(x * w.N / args.docs) for x in range(args.docs + 1)]))
+        for tag, kw in mods:
+            log(f"timing the backward on {w.name} with {tag}")
+            wl = BwdWorkload(w, **kw)
+            tm = time_workload(wl, args.steps, args.warmup, args.warmup_seconds)
+            del wl
+            torch.cuda.empty_cache()
+            extra["workloads"][f"{w.name}/bwd/{tag}"] = {
+                "tflops": round(2.5 * w.flops / (tm["kernel_ms_avg"] * 1e-3) / 1e12, 2),
+                "ms": round(tm["kernel_ms_avg"], 4),
+                "time_vs_plain_bwd": round(tm["kernel_ms_avg"] / tb["kernel_ms_avg"], 4)}
         for tag, win, off in masked:
             log(f"timing the backward on {w.name} with {tag[4:]}")
             wl = BwdWorkload(w, window=win, doc_offsets=off)
