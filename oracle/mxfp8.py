@@ -48,6 +48,8 @@ import math
 
 import numpy as np
 
+from .exact import visible
+
 BLOCK = 32
 E4M3_EMAX = 8          # exponent of the largest normal binade (448 = 1.75 * 2^8)
 E4M3_MAX = 448.0
@@ -154,19 +156,21 @@ def quantize_inputs(q, k, v):
     }
 
 
-def fp8p_rows(qt_rows, kt, vt, row_ids, causal, scale, ref_max=None):
+def fp8p_rows(qt_rows, kt, vt, row_ids, causal, scale, ref_max=None, window=0, docs=None):
     """FP8 forward for some query rows of one head, on dequantised operands.
 
     qt_rows [r, d], kt and vt [N, d] (float64).  ref_max optionally overrides
-    the integer reference max (a test hook).  Returns (O, LSE, p~).
+    the integer reference max (a test hook).  window, docs: the exact forward's
+    sliding window and packed documents (oracle.exact.visible); a hidden key's
+    score is -inf before the block maxima, as with the causal mask.  Returns
+    (O, LSE, p~).
     """
     n_keys = kt.shape[0]
     if n_keys % BLOCK:
         raise ValueError("the key count must be a multiple of 32")
     t = (scale * (qt_rows @ kt.T)) * LOG2E
-    if causal:
-        cols = np.arange(n_keys)
-        t = np.where(cols[None, :] > np.asarray(row_ids)[:, None], -np.inf, t)
+    if causal or window or docs is not None:
+        t = np.where(visible(row_ids, n_keys, causal, window, docs), t, -np.inf)
     row_max = t.max(axis=1)
     live_row = np.isfinite(row_max)
     m = np.where(live_row, np.ceil(np.where(live_row, row_max, 0.0)), 0.0)
@@ -195,7 +199,7 @@ def fp8p_rows(qt_rows, kt, vt, row_ids, causal, scale, ref_max=None):
     return o, lse, p
 
 
-def fp8_attention(qt, kt, vt, causal, scale, chunk=256):
+def fp8_attention(qt, kt, vt, causal, scale, chunk=256, window=0, docs=None):
     """FP8 forward over [B, H, N, d] dequantised operands: returns (O, LSE)."""
     qt = np.asarray(qt, dtype=np.float64)
     B, Hq, N, d = qt.shape
@@ -208,5 +212,6 @@ def fp8_attention(qt, kt, vt, causal, scale, chunk=256):
             for r0 in range(0, N, chunk):
                 rows = np.arange(r0, min(N, r0 + chunk))
                 o[b, h, rows], lse[b, h, rows], _ = fp8p_rows(
-                    qt[b, h, rows], kt[b, g], vt[b, g], rows, causal, scale)
+                    qt[b, h, rows], kt[b, g], vt[b, g], rows, causal, scale, window=window,
+                    docs=docs)
     return o, lse

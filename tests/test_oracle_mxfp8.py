@@ -258,7 +258,9 @@ def test_planted_fp8p_mistakes_are_caught(bad, monkeypatch):
     orig_rows = m8.fp8p_rows
     orig_round = m8.e4m3_round
 
-    def mutated_rows(qt_rows, kt, vt, row_ids, causal, scale, ref_max=None):
+    def mutated_rows(qt_rows, kt, vt, row_ids, causal, scale, ref_max=None, window=0,
+                     docs=None):
+        assert window == 0 and docs is None   # the pins below use neither
         if bad == "no_consistent_norm":
             o, lse, p = orig_rows(qt_rows, kt, vt, row_ids, causal, scale, ref_max)
             t = scale * qt_rows @ kt.T * m8.LOG2E
@@ -299,3 +301,38 @@ def test_planted_fp8p_mistakes_are_caught(bad, monkeypatch):
         except AssertionError:
             failed += 1
     assert failed > 0
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8p_documents_are_independent_sequences(causal):
+    """Packed documents whose offsets are multiples of 32 (the P blocks then coincide): each
+    document's rows equal the emulation run on that document alone."""
+    t = _case(31, 1, 2, 256, 32)
+    docs = [0, 64, 160, 256]
+    o, lse = m8.fp8_attention(t["q"], t["k"], t["v"], causal, 0.2, docs=docs)
+    for a, b in zip(docs[:-1], docs[1:]):
+        oa, la = m8.fp8_attention(t["q"][:, :, a:b], t["k"][:, :, a:b], t["v"][:, :, a:b],
+                                  causal, 0.2)
+        assert np.array_equal(o[:, :, a:b], oa) and np.array_equal(lse[:, :, a:b], la)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8p_window_edges(causal):
+    """A narrow window W = 8: the emulation stays within its quantisation error of the exact
+    windowed attention, and is far from the exact attention with W - 1 or W + 1 (one key more
+    or less per row), so the window's edges are where the definition puts them.  A window of
+    N or more is no window."""
+    t = _case(32, 1, 2, 128, 32)
+    o, _ = m8.fp8_attention(t["q"], t["k"], t["v"], causal, 0.2, window=8)
+
+    def rel(x, y):
+        return np.linalg.norm(x - y) / np.linalg.norm(y)
+
+    oe, _ = oracle.attention(t["q"], t["k"], t["v"], causal, 0.2, window=8)
+    assert rel(o, oe) < 0.03
+    for w in (7, 9):
+        ow, _ = oracle.attention(t["q"], t["k"], t["v"], causal, 0.2, window=w)
+        assert rel(o, ow) > 0.1
+    o_all, l_all = m8.fp8_attention(t["q"], t["k"], t["v"], causal, 0.2, window=128)
+    o_none, l_none = m8.fp8_attention(t["q"], t["k"], t["v"], causal, 0.2)
+    assert np.array_equal(o_all, o_none) and np.array_equal(l_all, l_none)
