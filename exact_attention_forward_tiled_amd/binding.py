@@ -308,8 +308,10 @@ def quantize_mxfp8_cols_t(x):
     return codes, scales
 
 
-def fwd_mxfp8(q8, qs, k8, ks, vt8, vts, causal=False, scale=None, tau=8.0, stats=None, out=None):
-    """MXFP8 forward: returns (O fp32 [B,Hq,N,d], LSE fp32 [B,Hq,N])."""
+def fwd_mxfp8(q8, qs, k8, ks, vt8, vts, causal=False, scale=None, tau=8.0, stats=None, out=None,
+              window=0, docs=None):
+    """MXFP8 forward: returns (O fp32 [B,Hq,N,d], LSE fp32 [B,Hq,N]).  window, docs: sliding
+    window and document offsets (int32 CUDA tensor), as for fwd."""
     torch = _torch()
     B, Hq, N, d = q8.shape
     Hkv = k8.shape[1]
@@ -327,7 +329,14 @@ def fwd_mxfp8(q8, qs, k8, ks, vt8, vts, causal=False, scale=None, tau=8.0, stats
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q8.device)
     else:
         o, lse = out
-    opts = make_opts(tau, "hw", _stats_ptr(torch, stats))
+    doc_ptr, n_docs = None, 0
+    if docs is not None:
+        if docs.dtype != torch.int32 or not docs.is_cuda or not docs.is_contiguous() \
+                or docs.numel() < 2:
+            raise ValueError("docs must be a contiguous int32 CUDA tensor of document offsets")
+        doc_ptr, n_docs = docs.data_ptr(), docs.numel() - 1
+    opts = make_opts(tau, "hw", _stats_ptr(torch, stats), window=window, doc_ptr=doc_ptr,
+                     n_docs=n_docs)
     check(attn_fwd_mxfp8_ex(q8.data_ptr(), qs.data_ptr(), k8.data_ptr(), ks.data_ptr(),
                             vt8.data_ptr(), vts.data_ptr(), o.data_ptr(), lse.data_ptr(),
                             B, Hq, Hkv, N, d, int(bool(causal)), float(scale), opts,

@@ -51,10 +51,11 @@ int check_common(int B, int Hq, int Hkv, int N, int d, int causal, float scale) 
 }
 
 // Shared validation and launch of the block-scaled forwards (MXFP4 and MXFP8).
-int mx_fwd(hipError_t (*launch)(const attn::MxArgs&), uint32_t qsign, const uint8_t* qc,
-           const uint8_t* qs, const uint8_t* kc, const uint8_t* ks, const uint8_t* vtc,
-           const uint8_t* vts, float* o, float* lse, int B, int Hq, int Hkv, int N, int d,
-           int causal, float scale, const attn_opts* opts, void* stream) {
+// band_ok: the forward takes a sliding window and document offsets (MXFP8).
+int mx_fwd(hipError_t (*launch)(const attn::MxArgs&), uint32_t qsign, bool band_ok,
+           const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+           const uint8_t* vtc, const uint8_t* vts, float* o, float* lse, int B, int Hq, int Hkv,
+           int N, int d, int causal, float scale, const attn_opts* opts, void* stream) {
   if (!qc || !qs || !kc || !ks || !vtc || !vts || !o || !lse) return ATTN_EINVAL;
   if (!aligned(qc, 16) || !aligned(kc, 16) || !aligned(vtc, 16) || !aligned(o, 16) ||
       !aligned(lse, 4) || !aligned(ks, 4))
@@ -66,9 +67,9 @@ int mx_fwd(hipError_t (*launch)(const attn::MxArgs&), uint32_t qsign, const uint
   const attn_opts* op = opts ? opts : &def;
   st = check_opts(op);
   if (st != ATTN_OK) return st;
-  if (d != 128 || N % 32 != 0 || op->window != 0 || op->alibi_slopes != nullptr ||
-      op->softcap != 0.f || op->doc_offsets != nullptr)
+  if (d != 128 || N % 32 != 0 || op->alibi_slopes != nullptr || op->softcap != 0.f)
     return ATTN_EUNSUPPORTED;
+  if (!band_ok && (op->window != 0 || op->doc_offsets != nullptr)) return ATTN_EUNSUPPORTED;
 
   attn::MxArgs a;
   a.qc = qc; a.qs = qs; a.kc = kc; a.ks = ks; a.vtc = vtc; a.vts = vts;
@@ -77,6 +78,11 @@ int mx_fwd(hipError_t (*launch)(const attn::MxArgs&), uint32_t qsign, const uint
   a.c = fabsf(scale) * 1.4426950408889634f;
   a.qsign = scale < 0.f ? qsign : 0u;
   a.tau = op->tau;
+  // a window at least N wide hides nothing: run the plain mask
+  a.window = op->window >= N ? 0 : op->window;
+  a.doc_offsets = op->doc_offsets;
+  a.n_docs = op->doc_offsets != nullptr ? op->n_docs : 0;
+  if (a.n_docs > N) return ATTN_EINVAL;   // documents are non-empty
   a.stats = op->stats;
   a.stream = stream;
   hipError_t e = launch(a);
@@ -205,7 +211,7 @@ int attn_fwd_mxfp4_ex(const uint8_t* q4, const uint8_t* qs, const uint8_t* k4, c
                       const uint8_t* vt4, const uint8_t* vts, float* o, float* lse, int B, int Hq,
                       int Hkv, int N, int d, int causal, float scale, const attn_opts* opts,
                       void* stream) {
-  return mx_fwd(attn::launch_fwd_mxfp4, 0x88888888u, q4, qs, k4, ks, vt4, vts, o, lse, B, Hq, Hkv,
+  return mx_fwd(attn::launch_fwd_mxfp4, 0x88888888u, false, q4, qs, k4, ks, vt4, vts, o, lse, B, Hq, Hkv,
                 N, d, causal, scale, opts, stream);
 }
 
@@ -236,7 +242,7 @@ int attn_fwd_mxfp8_ex(const uint8_t* q8, const uint8_t* qs, const uint8_t* k8, c
                       const uint8_t* vt8, const uint8_t* vts, float* o, float* lse, int B, int Hq,
                       int Hkv, int N, int d, int causal, float scale, const attn_opts* opts,
                       void* stream) {
-  return mx_fwd(attn::launch_fwd_mxfp8, 0x80808080u, q8, qs, k8, ks, vt8, vts, o, lse, B, Hq, Hkv,
+  return mx_fwd(attn::launch_fwd_mxfp8, 0x80808080u, true, q8, qs, k8, ks, vt8, vts, o, lse, B, Hq, Hkv,
                 N, d, causal, scale, opts, stream);
 }
 

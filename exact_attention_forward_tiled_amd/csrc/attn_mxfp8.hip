@@ -192,14 +192,17 @@ struct F8Stage {
 // Weights of one 64-key tile for this lane (32 keys: its P scale block).  Returns
 // whether any row of the wave moved its reference max (then O and the row sum
 // must be multiplied by alpha before the next PV product).
-template <bool CAUSAL, bool MASK>
+// BAND: the lane sees keys [klo, khi] only (a sliding window and / or its document; the
+// bounds already hold the causal limit and N).
+template <bool CAUSAL, bool MASK, bool BAND>
 __device__ __forceinline__ bool fp8p_tile(const f32x16 (&s)[2], u32x4 (&codes)[2],
                                           uint32_t& sbyte, float& m, float& alpha, int kv0,
-                                          int qi, int N, float c, float tau, int h) {
+                                          int qi, int N, float c, float tau, int h, int klo,
+                                          int khi) {
   const float NEG_INF = -__builtin_inff();
   auto visible = [&](int mb, int r) {
     const int key = kv0 + 32 * mb + 16 * h + r;
-    return key < N && (!CAUSAL || key <= qi);
+    return BAND ? (key >= klo) & (key <= khi) : key < N && (!CAUSAL || key <= qi);
   };
   // this lane's maxima over its 16 scores of each 32-key block (two chains each)
   float bq[2][2] = {{NEG_INF, NEG_INF}, {NEG_INF, NEG_INF}};
@@ -264,13 +267,14 @@ __device__ __forceinline__ bool fp8p_tile(const f32x16 (&s)[2], u32x4 (&codes)[2
   return any;
 }
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool BAND>
 __global__ __attribute__((amdgpu_flat_work_group_size(k8Threads, k8Threads), amdgpu_waves_per_eu(2, 2)))
 void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ QS,
                       const uint8_t* __restrict__ K8, const uint8_t* __restrict__ KS,
                       const uint8_t* __restrict__ VT8, const uint8_t* __restrict__ VTS,
                       float* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int N,
-                      int nqb, float c, float tau, uint32_t qsign,
+                      int nqb, float c, float tau, uint32_t qsign, int window,
+                      const int* __restrict__ doc_off, int n_docs,
                       unsigned long long* __restrict__ stats) {
   __shared__ F8Buf buf[2];
   const float NEG_INF = -__builtin_inff();
@@ -327,11 +331,42 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict_
   unsigned n_steps = 0, n_rescales = 0;
   bool first = true;
 
-  const int kv_end = CAUSAL ? min(N, Q0 + k8Br) : N;
-  const int n = (kv_end + k8Bc - 1) / k8Bc;
-  const int wave_end = CAUSAL ? min(N, q0 + k8Rows) : N;
+  // BAND (the bf16 forward's rules): row i sees keys [lo(i), hi(i)], from a window W
+  // (i - W < j, and j < i + W without the causal mask) and / or its document; both
+  // bounds are non-decreasing in i, so a block's first and last rows bound its keys.
+  // The document search reads only doc_off[0 .. n_docs] and keeps lo <= i <= hi.
+  auto row_bounds = [&](int i, int& lo, int& hi) {
+    lo = window ? max(0, i - window + 1) : 0;
+    hi = CAUSAL ? i : (window ? min(N - 1, i + window - 1) : N - 1);
+    if (n_docs > 0) {
+      int a = 0, z = n_docs;
+      while (z - a > 1) {
+        const int mid = (a + z) >> 1;
+        if (doc_off[mid] <= i) a = mid;
+        else z = mid;
+      }
+      lo = max(lo, min(doc_off[a], i));
+      hi = min(hi, max(doc_off[a + 1] - 1, i));
+    }
+  };
+  int klo = 0, khi = 0, wg_lo_first = 0, wg_hi_first = 0, wg_lo_last = 0, wg_hi_last = 0;
+  int w_lo = 0, w_hi = 0, unused = 0;
+  if (BAND) {
+    row_bounds(min(qi, N - 1), klo, khi);
+    row_bounds(Q0, wg_lo_first, wg_hi_first);
+    row_bounds(min(Q0 + k8Br - 1, N - 1), wg_lo_last, wg_hi_last);
+    row_bounds(min(q0, N - 1), w_lo, unused);
+    row_bounds(min(q0 + k8Rows - 1, N - 1), unused, w_hi);
+  }
+  // tiles t0 .. t0 + n - 1 (local index j = tile - t0)
+  const int t0 = BAND ? wg_lo_first / k8Bc : 0;
+  const int kv_end = BAND ? wg_hi_last + 1 : (CAUSAL ? min(N, Q0 + k8Br) : N);
+  const int n = (kv_end + k8Bc - 1) / k8Bc - t0;
+  const int wave_end = BAND ? w_hi + 1 : (CAUSAL ? min(N, q0 + k8Rows) : N);
   const bool wave_live = q0 < N;
-  auto active = [&](int j) { return wave_live && j * k8Bc < wave_end; };
+  auto active = [&](int j) {
+    return wave_live && (t0 + j) * k8Bc < wave_end && (!BAND || (t0 + j + 1) * k8Bc > w_lo);
+  };
 
   const int krs = tid >> 3, kcs = tid & 7;     // K staging unit of this thread
   const int vcs = tid >> 2, vch = tid & 3;     // V^T staging unit of this thread
@@ -343,7 +378,7 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict_
   // scale's source (K or V^T) is a wave-uniform select, so the step has no branches.
   auto load_stage = [&](F8Stage& sg, int t) {
     const int kt = min(t, n - 1), vt = max(min(t - 1, n - 1), 0);
-    const int kk0 = kt * k8Bc, vk0 = vt * k8Bc;
+    const int kk0 = (t0 + kt) * k8Bc, vk0 = (t0 + vt) * k8Bc;
     const __amdgpu_buffer_rsrc_t rk = rsrc8(K8h + (size_t)kk0 * k8CodeRow, (N - kk0) * k8CodeRow);
     sg.k = __builtin_amdgcn_raw_buffer_load_b128(rk, krs * k8CodeRow + kcs * 16, 0, 0);
     // keys past N in the last tile read the next column's codes (finite; they meet zero
@@ -430,7 +465,9 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict_
 
   bool any_prev = false;
   float alpha_prev = 1.f;
-  const int n_full = CAUSAL ? min(Q0, N) / k8Bc : N / k8Bc;
+  // unmasked tiles [lo_full, n_full): every row of the workgroup sees all their keys
+  const int n_full = BAND ? (wg_hi_first + 1) / k8Bc - t0 : (CAUSAL ? min(Q0, N) / k8Bc : N / k8Bc);
+  const int lo_full = BAND ? min(n, (wg_lo_last + k8Bc - 1) / k8Bc - t0) : 0;
   auto rescale = [&]() {
     if (any_prev) {
 #pragma unroll
@@ -447,9 +484,11 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict_
     float alpha;
     bool any;
     if (masked)
-      any = fp8p_tile<CAUSAL, true>(s, p, ep, m, alpha, j * k8Bc, qi, N, c, tau, h);
+      any = fp8p_tile<CAUSAL, true, BAND>(s, p, ep, m, alpha, (t0 + j) * k8Bc, qi, N, c, tau, h,
+                                          klo, khi);
     else
-      any = fp8p_tile<CAUSAL, false>(s, p, ep, m, alpha, j * k8Bc, qi, N, c, tau, h);
+      any = fp8p_tile<CAUSAL, false, BAND>(s, p, ep, m, alpha, (t0 + j) * k8Bc, qi, N, c, tau,
+                                           h, klo, khi);
     any_prev = any;
     alpha_prev = alpha;
     const bool counted = active(j) && !first;   // branch-free: uniform selects
@@ -463,10 +502,16 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict_
 
   // step 0 has no PV product (no tile before it); then the unmasked steps, then the
   // masked ones (causal diagonal, ragged tail)
-  step(0, false, 0 >= n_full);
-  int j = 1;
-  for (; j < min(n_full, n); ++j) step(j, true, false);
-  for (; j < n; ++j) step(j, true, true);
+  if constexpr (BAND) {
+    // masked below lo_full (some row's lower edge) and from n_full on
+    step(0, false, 0 < lo_full || 0 >= n_full);
+    for (int j = 1; j < n; ++j) step(j, true, j < lo_full || j >= n_full);
+  } else {
+    step(0, false, 0 >= n_full);
+    int j = 1;
+    for (; j < min(n_full, n); ++j) step(j, true, false);
+    for (; j < n; ++j) step(j, true, true);
+  }
   // PV and row sum of the last tile (its V^T was staged by the last step into buffer n&1)
   rescale();
   {
@@ -500,14 +545,15 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict_
   }
 }
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool BAND>
 hipError_t launch_mxfp8(const MxArgs& a) {
   const int nqb = (a.N + k8Br - 1) / k8Br;
   const long long grid = (long long)a.B * a.Hq * nqb;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_mxfp8_kernel<CAUSAL>), dim3((unsigned)grid), dim3(k8Threads), 0,
+  hipLaunchKernelGGL((fwd_mxfp8_kernel<CAUSAL, BAND>), dim3((unsigned)grid), dim3(k8Threads), 0,
                      (hipStream_t)a.stream, a.qc, a.qs, a.kc, a.ks, a.vtc, a.vts, a.o, a.lse,
-                     a.Hq, a.Hkv, a.N, nqb, a.c, a.tau, a.qsign, a.stats);
+                     a.Hq, a.Hkv, a.N, nqb, a.c, a.tau, a.qsign, a.window, a.doc_offsets,
+                     a.n_docs, a.stats);
   return hipGetLastError();
 }
 
@@ -537,7 +583,9 @@ hipError_t launch_quantize8_cols_t(const float* x, uint8_t* codes, uint8_t* scal
 
 hipError_t launch_fwd_mxfp8(const MxArgs& a) {
   if (a.d != k8D) return hipErrorNotSupported;
-  return a.causal ? launch_mxfp8<true>(a) : launch_mxfp8<false>(a);
+  const bool band = a.window > 0 || a.n_docs > 0;
+  if (a.causal) return band ? launch_mxfp8<true, true>(a) : launch_mxfp8<true, false>(a);
+  return band ? launch_mxfp8<false, true>(a) : launch_mxfp8<false, false>(a);
 }
 
 }  // namespace attn

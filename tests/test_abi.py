@@ -126,7 +126,18 @@ def test_mxfp8_validation(fa):
     assert fa.attn_fwd_mxfp8(*base, 1, 3, 2, 64, 128, 0, 0.1) == -1     # Hq % Hkv
     assert fa.attn_fwd_mxfp8(*base, 1, 2, 2, 64, 128, 2, 0.1) == -1     # causal in {0, 1}
     assert fa.attn_fwd_mxfp8(0, *base[1:], 1, 2, 2, 64, 128, 0, 0.1) == -1
-    assert fa.attn_fwd_mxfp8_ex(*base, 1, 2, 2, 64, 128, 0, 0.1, fa.make_opts(window=16),
+    # masks are taken, but still validated before any launch; score modifications are not
+    assert fa.attn_fwd_mxfp8_ex(*base, 1, 2, 2, 64, 64, 0, 0.1, fa.make_opts(window=16),
+                                None) == -2
+    assert fa.attn_fwd_mxfp8_ex(*base, 1, 2, 2, 64, 128, 0, 0.1, fa.make_opts(window=-1),
+                                None) == -1
+    assert fa.attn_fwd_mxfp8_ex(*base, 1, 2, 2, 64, 128, 0, 0.1,
+                                fa.make_opts(doc_ptr=FAKE, n_docs=65), None) == -1
+    assert fa.attn_fwd_mxfp8_ex(*base, 1, 2, 2, 64, 128, 0, 0.1, fa.make_opts(alibi_ptr=FAKE),
+                                None) == -2
+    assert fa.attn_fwd_mxfp8_ex(*base, 1, 2, 2, 64, 128, 0, 0.1, fa.make_opts(softcap=2.0),
+                                None) == -2
+    assert fa.attn_fwd_mxfp4_ex(*base, 1, 2, 2, 64, 128, 0, 0.1, fa.make_opts(window=16),
                                 None) == -2
     assert fa.attn_quantize_mxfp8_rows(FAKE, FAKE, FAKE, 4, 48) == -1
     assert fa.attn_quantize_mxfp8_cols_t(FAKE, FAKE, FAKE, 1, 40, 8) == -1

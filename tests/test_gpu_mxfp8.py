@@ -222,3 +222,63 @@ def test_fp8_workload_sampled_rows(idx):
                   np.linalg.norm(exact, axis=-1))
     log(f"  relRMS(O) vs emulation {r:.3e}; mean row cosine vs unquantised exact {cos:.5f}")
     assert r <= MXFP8_O_RELRMS
+
+
+MASKED = [
+    # B, Hq, Hkv, N, causal, window, docs
+    (1, 2, 2, 512, True, 100, None),
+    (1, 2, 2, 320, False, 64, None),
+    (1, 4, 2, 256, True, 0, [0, 100, 101, 256]),
+    (1, 2, 2, 384, False, 0, [0, 64, 200, 384]),
+    (1, 2, 2, 512, True, 130, [0, 300, 512]),
+    (1, 2, 2, 128, True, 1, None),       # a window of 1: every row sees only itself
+    (1, 2, 2, 256, False, 256, None),    # a window N wide hides nothing
+]
+
+
+def _masked_check(q, k, v, causal, scale, window, docs, rows=None):
+    import torch
+    dd = None if docs is None else torch.tensor(docs, dtype=torch.int32, device="cuda")
+    o, lse = _run(q, k, v, causal, scale, window=window, docs=dd)
+    t = m8.quantize_inputs(q, k, v)
+    tol = mxfp8_lse_tol(t["q"], t["k"], scale)
+    assert not np.isnan(o).any() and not np.isnan(lse).any()
+    if rows is None:
+        ro, rl = m8.fp8_attention(t["q"], t["k"], t["v"], causal, scale, window=window,
+                                  docs=docs)
+    else:   # sampled rows of every head
+        B, Hq = q.shape[:2]
+        group = Hq // k.shape[1]
+        ro = np.empty((B, Hq, len(rows), q.shape[3]))
+        rl = np.empty((B, Hq, len(rows)))
+        for b in range(B):
+            for h in range(Hq):
+                ro[b, h], rl[b, h], _ = m8.fp8p_rows(t["q"][b, h, rows], t["k"][b, h // group],
+                                                     t["v"][b, h // group], rows, causal, scale,
+                                                     window=window, docs=docs)
+        o, lse = o[:, :, rows], lse[:, :, rows]
+    r = rel_rms(o, ro)
+    e = float(np.max(np.abs(lse - rl)))
+    log(f"  relRMS(O)={r:.3e} max|dLSE|={e:.3e} (gate {tol:.3e})")
+    assert r <= MXFP8_O_RELRMS, r
+    assert e <= tol, e
+
+
+@pytest.mark.parametrize("case", MASKED, ids=lambda c: "Hq%dHkv%dN%d%sW%d%s" % (
+    c[1], c[2], c[3], "c" if c[4] else "n", c[5], "docs" if c[6] else ""))
+def test_fp8_masked(case):
+    """Sliding window and packed documents on the MXFP8 forward (tiles outside a block's band
+    skipped) against the emulation under the same masks."""
+    B, Hq, Hkv, N, causal, window, docs = case
+    q, k, v = _case(N + window + 3 * Hq, B, Hq, Hkv, N)
+    log(f"mxfp8 masked case {case}")
+    _masked_check(q, k, v, causal, 1.0 / math.sqrt(128), window, docs)
+
+
+def test_fp8_masked_long_sampled_rows():
+    """Causal GQA N 4096 with a 1024 window over two documents: sampled rows (both document
+    edges, the window's reach, the last rows) of every head."""
+    q, k, v = _case(61, 1, 4, 2, 4096)
+    rows = np.array([0, 1, 31, 1023, 1024, 1500, 2047, 2048, 2049, 3071, 3072, 4094, 4095])
+    log("mxfp8 masked N4096 W1024 docs")
+    _masked_check(q, k, v, True, 1.0 / math.sqrt(128), 1024, [0, 2048, 4096], rows=rows)
