@@ -151,11 +151,14 @@ class Mxfp8Workload:
     """MXFP8 workload: fp32 draws quantised on the GPU once (untimed), then the forward on
     the resident codes and scales."""
 
-    def __init__(self, w, tau):
+    def __init__(self, w, tau, window=0, doc_offsets=None):
         import numpy as np
         import torch
         import exact_attention_forward_tiled_amd as fa
         self.w = w
+        self.window = window
+        self.docs = (None if doc_offsets is None else
+                     torch.tensor(doc_offsets, dtype=torch.int32, device="cuda"))
         q, k, v = (torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in w.make())
         self.q8, self.qs = fa.quantize_mxfp8_rows(q)
         self.k8, self.ks = fa.quantize_mxfp8_rows(k)
@@ -170,7 +173,7 @@ class Mxfp8Workload:
     def launch(self, stats=None):
         self.fa.fwd_mxfp8(self.q8, self.qs, self.k8, self.ks, self.vt8, self.vts,
                           causal=self.w.causal, scale=self.w.scale, tau=self.tau, stats=stats,
-                          out=(self.o, self.lse))
+                          out=(self.o, self.lse), window=self.window, docs=self.docs)
 
 
 class BwdWorkload:
@@ -396,9 +399,9 @@ def main():
     ap.add_argument("--extra", default="", help="other workloads to time (comma list), e.g. 3,4")
     ap.add_argument("--docs", type=int, default=0,
                     help="also time the workload split into this many equal packed documents "
-                         "(bf16 only; TFLOP/s count 4*d flop per visible pair)")
+                         "(bf16, mxfp8; TFLOP/s count 4*d flop per visible pair)")
     ap.add_argument("--window", type=int, default=0,
-                    help="also time the workload with this sliding window (bf16 only); its "
+                    help="also time the workload with this sliding window (bf16, mxfp8); its "
                          "TFLOP/s count 4*d flop per visible (query, key) pair")
     ap.add_argument("--softcap", type=float, default=0.0,
                     help="also time the workload with soft-capping C (bf16 only)")
@@ -511,9 +514,10 @@ def main():
             extra["workloads"][wx.name][f"pct_of_{wx.fmt[2:]}_peak"] = round(
                 100.0 * tx["tflops"] / PEAKS[wx.fmt], 2)
 
-    if args.window and w.fmt == "bf16":
+    if args.window and w.fmt in ("bf16", "mxfp8"):
         log(f"timing {w.name} with window {args.window}")
-        wl = Workload(w, args.exp, args.tau, args.poly_frac, window=args.window)
+        wl = (Workload(w, args.exp, args.tau, args.poly_frac, window=args.window)
+              if w.fmt == "bf16" else Mxfp8Workload(w, args.tau, window=args.window))
         tw = time_workload(wl, args.steps, args.warmup, args.warmup_seconds)
         del wl
         torch.cuda.empty_cache()
@@ -525,10 +529,11 @@ def main():
             "visible_pairs_per_head": pairs,
             "time_vs_no_window": round(tw["kernel_ms_avg"] / t["kernel_ms_avg"], 4)}
 
-    if args.docs and w.fmt == "bf16":
+    if args.docs and w.fmt in ("bf16", "mxfp8"):
         off = [round(x * w.N / args.docs) for x in range(args.docs + 1)]
         log(f"timing {w.name} as {args.docs} documents")
-        wl = Workload(w, args.exp, args.tau, args.poly_frac, doc_offsets=off)
+        wl = (Workload(w, args.exp, args.tau, args.poly_frac, doc_offsets=off)
+              if w.fmt == "bf16" else Mxfp8Workload(w, args.tau, doc_offsets=off))
         td = time_workload(wl, args.steps, args.warmup, args.warmup_seconds)
         del wl
         torch.cuda.empty_cache()
