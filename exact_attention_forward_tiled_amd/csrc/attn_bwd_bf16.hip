@@ -425,7 +425,8 @@ __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
 // runs over 64-key tiles (causal: up to the workgroup's last query; BAND: the tiles within
 // the queries' window and documents).
 // (The body; the kernels below set the waves per SIMD.)
-template <int D, bool CAUSAL, bool BAND, bool MODS>
+// CAP: the soft-capping path is compiled in (MODS with ALiBi only leaves it out).
+template <int D, bool CAUSAL, bool BAND, bool MODS, bool CAP_ON = MODS>
 __device__ __forceinline__ void dq_body(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -554,7 +555,7 @@ __device__ __forceinline__ void dq_body(
         }
       }
       };
-      if (MODS && mods.k2 != 0.f) elements(std::true_type{});
+      if (CAP_ON && mods.k2 != 0.f) elements(std::true_type{});
       else elements(std::false_type{});
       // dQ^T += K^T dS^T (d x queries), over the two 16-key chunks
 #pragma unroll
@@ -593,18 +594,18 @@ __device__ __forceinline__ void dq_body(
 
 // Two waves per SIMD (at most 256 registers each; two workgroups' tiles fit the CU's LDS),
 // so one workgroup's products overlap the other's exponentials and staging.
-template <int D, bool CAUSAL, bool BAND, bool MODS>
+template <int D, bool CAUSAL, bool BAND, bool MODS, bool CAP_ON = MODS>
 __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Delta, float* __restrict__ dQ,
     int Hq, int Hkv, int N, int nqb, float c, float scale, Band band, Mods mods) {
-  dq_body<D, CAUSAL, BAND, MODS>(Q, K, V, dO, LSE, Delta, dQ, Hq, Hkv, N, nqb, c, scale, band,
-                                 mods);
+  dq_body<D, CAUSAL, BAND, MODS, CAP_ON>(Q, K, V, dO, LSE, Delta, dQ, Hq, Hkv, N, nqb, c, scale,
+                                         band, mods);
 }
 
-// The same at one wave per SIMD (up to 512 registers): the soft-capping and ALiBi form at
-// d = 128, whose per-element work does not fit the 256 registers of two waves per SIMD.
+// The same at one wave per SIMD (up to 512 registers): the soft-capping form at d = 128,
+// whose per-element work does not fit the 256 registers of two waves per SIMD.
 template <int D, bool CAUSAL, bool BAND, bool MODS>
 __global__ __launch_bounds__(kBThreads) void dq_kernel_1w(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -635,16 +636,18 @@ hipError_t launch_bwd_t(const BwdArgs& a) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)(a.B * a.Hq * nb));
-  if constexpr (MODS && D == 128)
-    hipLaunchKernelGGL((dq_kernel_1w<D, CAUSAL, BAND, MODS>), grid, dim3(kBThreads), 0,
-                       (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                       (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta, a.dq,
-                       a.Hq, a.Hkv, a.N, nb, a.c, a.scale, band, mods);
-  else
-    hipLaunchKernelGGL((dq_kernel<D, CAUSAL, BAND, MODS>), grid, dim3(kBThreads), 0,
-                       (hipStream_t)a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                       (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta, a.dq,
-                       a.Hq, a.Hkv, a.N, nb, a.c, a.scale, band, mods);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(kBThreads), 0, (hipStream_t)a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, a.lse, a.delta, a.dq, a.Hq, a.Hkv, a.N, nb, a.c,
+                       a.scale, band, mods);
+  };
+  if constexpr (MODS && D == 128) {
+    if (a.softcap > 0.f) go(dq_kernel_1w<D, CAUSAL, BAND, MODS>);
+    else go(dq_kernel<D, CAUSAL, BAND, MODS, false>);   // ALiBi only: two waves per SIMD
+  } else {
+    go(dq_kernel<D, CAUSAL, BAND, MODS>);
+  }
   return hipGetLastError();
 }
 
