@@ -25,16 +25,21 @@ check), written from the definitions so that a reader can check it by eye:
 * ``backward`` -- the gradients dQ, dK, dV of the exact forward, with P rebuilt
   from the saved log-sum-exp ("Hardware-Aware FP4 FlashAttention-4", section
   "2. Causal Backward Cuantizado": the forward saves the LSE and the backward
-  rebuilds the probabilities from it).
+  rebuilds the probabilities from it); also for sampled rows at full sizes.
+* ``skipsim`` -- a diagnostic model of how often the thresholded rescale fires
+  (the aigc.bar page, section "FlashAttention-4：为Blackwell而生的性能猛兽",
+  item 1); not part of the parity definition, since the output does not depend
+  on the threshold in exact arithmetic.
 
 Parity status: every function is pinned by tests under ``tests/`` against
 brute force, a library routine (torch's CPU attention in float64), closed
 forms and invariants; see the test modules ``test_oracle_exact.py``,
-``test_oracle_mx.py``, ``test_oracle_mxfp8.py`` and ``test_oracle_backward.py``.
+``test_oracle_mx.py``, ``test_oracle_mxfp8.py``, ``test_oracle_backward.py`` and
+``test_oracle_skipsim.py``.
 """
 
 from .exact import attention, attention_brute, attention_head, attention_rows, kv_head
-from . import backward, mx, mxfp8
+from . import backward, mx, mxfp8, skipsim
 
 __all__ = ["attention", "attention_brute", "attention_head", "attention_rows", "kv_head", "backward", "mx",
-           "mxfp8"]
+           "mxfp8", "skipsim"]

@@ -41,7 +41,7 @@ and LSE are the forward's (recomputed here from the definition unless given).
 
 import numpy as np
 
-from .exact import apply_mask, attention, modify_scores, scores
+from .exact import apply_mask, attention, modify_scores, scores, visible
 
 
 def backward_head(q, k, v, do, causal, scale, o=None, lse=None, window=0, docs=None,
@@ -106,5 +106,53 @@ def attention_backward(q, k, v, do, causal, scale, o=None, lse=None, window=0, d
 
 
 def delta(o, do):
-    """D_i = dO_i . O_i per row: [B, Hq, N]."""
+    """D_i = dO_i . O_i per row: [B, Hq, N].  Equal to sum_j P_ij dP_ij, because
+    O_i = sum_j P_ij v_j and dP_ij = dO_i . v_j."""
     return np.sum(np.asarray(o, dtype=np.float64) * np.asarray(do, dtype=np.float64), axis=-1)
+
+
+def backward_rows(q, k, v, do, causal, scale, o, lse, qrows, krows, window=0, docs=None,
+                  softcap=0.0, alibi_slope=None):
+    """The same gradients as backward_head, for listed rows only, at sizes where the N x N
+    matrices do not fit: dQ of the query rows `qrows` and dK, dV of the key rows `krows`,
+    for one (batch, query head) slice.  q, do [N, d]; k, v [Nk, d]; o [N, d] and lse [N]
+    are the forward's outputs for every query row of the slice (D_i and P_ij need them).
+
+    dQ_i needs row i of P and dP (all keys); dK_j and dV_j need column j of P and dP (all
+    queries), so only those rows and columns of the score matrix are formed.  Returns
+    (dq [len(qrows), d], dk [len(krows), d], dv [len(krows), d])."""
+    qrows = np.asarray(qrows, dtype=np.int64)
+    krows = np.asarray(krows, dtype=np.int64)
+    n, nk = q.shape[0], k.shape[0]
+    all_rows = np.arange(n)
+    live = np.isfinite(lse)
+    lse0 = np.where(live, lse, 0.0)
+    dlt = np.sum(do * o, axis=1)                 # D_i for every query row
+
+    def masked(raw, rows, cols):
+        s = modify_scores(raw, rows, softcap, None)
+        if alibi_slope is not None:
+            s = s - alibi_slope * np.abs(rows[:, None] - cols[None, :])
+        if not causal and not window and docs is None:
+            return s
+        return np.where(visible(rows, nk, causal, window, docs)[:, cols], s, -np.inf)
+
+    # rows of the score matrix: dQ
+    raw_r = scale * (q[qrows] @ k.T)
+    cols_all = np.arange(nk)
+    p_r = np.where(live[qrows, None],
+                   np.exp(masked(raw_r, qrows, cols_all) - lse0[qrows, None]), 0.0)
+    ds_r = p_r * (do[qrows] @ v.T - dlt[qrows, None])
+    if softcap:
+        ds_r = ds_r * (1.0 - np.tanh(raw_r / softcap) ** 2)
+    dq = scale * (ds_r @ k)
+    # columns of the score matrix: dK, dV
+    raw_c = scale * (q @ k[krows].T)
+    p_c = np.where(live[:, None],
+                   np.exp(masked(raw_c, all_rows, krows) - lse0[:, None]), 0.0)
+    dv = p_c.T @ do
+    ds_c = p_c * (do @ v[krows].T - dlt[:, None])
+    if softcap:
+        ds_c = ds_c * (1.0 - np.tanh(raw_c / softcap) ** 2)
+    dk = scale * (ds_c.T @ q)
+    return dq, dk, dv

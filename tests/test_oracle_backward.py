@@ -269,3 +269,66 @@ def test_planted_mistakes_are_caught(bad, monkeypatch):
         except AssertionError:
             failed += 1
     assert failed > 0
+
+
+def test_delta_is_sum_of_p_times_dp_brute_force():
+    """D_i = dO_i . O_i equals sum_j P_ij dP_ij with P the softmax of the scores and
+    dP_ij = dO_i . v_j, both written out as scalar loops (math.exp), independent of how
+    the oracle forms O."""
+    import math
+    q, k, v, do = _case(21, 1, 2, 1, 9, 5)
+    for causal in (False, True):
+        scale = 0.7
+        o, _ = oracle.attention(q, k, v, causal, scale)
+        got = bw.delta(o, do)
+        for h in range(2):
+            for i in range(9):
+                keys = [j for j in range(9) if not (causal and j > i)]
+                s = [scale * sum(q[0, h, i, c] * k[0, 0, j, c] for c in range(5)) for j in keys]
+                mx = max(s)
+                e = [math.exp(x - mx) for x in s]
+                tot = sum(e)
+                want = sum(e[n] / tot * sum(do[0, h, i, c] * v[0, 0, j, c] for c in range(5))
+                           for n, j in enumerate(keys))
+                assert abs(got[0, h, i] - want) <= 1e-12 * max(1.0, abs(want))
+
+
+def test_planted_delta_mistakes_are_caught(monkeypatch):
+    """A sign flip or a missing row of the product in delta fails the brute-force pin."""
+    orig = bw.delta
+    for bad in ("sign", "drop_last_column"):
+        def mutated(o, do, bad=bad):
+            if bad == "sign":
+                return -orig(o, do)
+            return orig(o[..., :-1], do[..., :-1])
+        monkeypatch.setattr(bw, "delta", mutated)
+        with pytest.raises(AssertionError):
+            test_delta_is_sum_of_p_times_dp_brute_force()
+    monkeypatch.setattr(bw, "delta", orig)
+
+
+@pytest.mark.parametrize("mask", ["none", "causal", "window", "docs_mods"])
+def test_backward_rows_equal_full_backward(mask):
+    """Sampled rows and columns of the gradients equal the full backward's, under every mask
+    and the score modifications (the row function forms only those rows and columns)."""
+    q, k, v, do = _case(22, 1, 1, 1, 40, 6)
+    kw = dict(causal=False, window=0, docs=None, softcap=0.0, alibi_slope=None)
+    if mask == "causal":
+        kw["causal"] = True
+    elif mask == "window":
+        kw.update(causal=True, window=7)
+    elif mask == "docs_mods":
+        kw.update(docs=[0, 13, 14, 40], softcap=1.5, alibi_slope=0.3)
+    scale = 0.6
+    alibi = None if kw["alibi_slope"] is None else [kw["alibi_slope"]]
+    o, lse = oracle.attention(q, k, v, kw["causal"], scale, window=kw["window"], docs=kw["docs"],
+                              softcap=kw["softcap"], alibi=alibi)
+    full = bw.backward_head(q[0, 0], k[0, 0], v[0, 0], do[0, 0], kw["causal"], scale, o[0, 0],
+                            lse[0, 0], kw["window"], kw["docs"], kw["softcap"], kw["alibi_slope"])
+    qrows, krows = np.array([0, 5, 13, 39]), np.array([1, 13, 14, 38, 39])
+    dq, dk, dv = bw.backward_rows(q[0, 0], k[0, 0], v[0, 0], do[0, 0], kw["causal"], scale,
+                                  o[0, 0], lse[0, 0], qrows, krows, kw["window"], kw["docs"],
+                                  kw["softcap"], kw["alibi_slope"])
+    assert np.allclose(dq, full[0][qrows], rtol=1e-12, atol=1e-14)
+    assert np.allclose(dk, full[1][krows], rtol=1e-12, atol=1e-14)
+    assert np.allclose(dv, full[2][krows], rtol=1e-12, atol=1e-14)
