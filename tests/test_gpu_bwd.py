@@ -15,7 +15,8 @@ import pytest
 import oracle
 import synth
 from oracle import backward as bw
-from gpu_util import BWD_DQK_RELRMS, BWD_DV_RELRMS, cuda_ok, log, rel_rms, to_dev_bf16, to_dev_f32
+from gpu_util import (BWD_DQK_RELRMS, BWD_DQK_ROW, BWD_DV_RELRMS, BWD_DV_ROW, cuda_ok, log,
+                      rel_rms, row_rel_max, to_dev_bf16, to_dev_f32)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not cuda_ok(), reason="needs a GPU")]
 
@@ -59,16 +60,21 @@ ZERO_GRAD_ABS = 1e-4
 
 
 def _check(got, ref, tag):
+    """relRMS and the per-row gate on each gradient (rows: the last axis)."""
     rq, rk, rv = (rel_rms(a, b) for a, b in zip(got, ref))
-    log(f"  {tag}: relRMS dQ={rq:.2e} dK={rk:.2e} dV={rv:.2e}")
+    wq, wk, wv = (row_rel_max(a, b) for a, b in zip(got, ref))
+    log(f"  {tag}: relRMS dQ={rq:.2e} dK={rk:.2e} dV={rv:.2e}; "
+        f"rowmax dQ={wq:.2e} dK={wk:.2e} dV={wv:.2e}")
     for a in got:
         assert not np.isnan(a).any()
     assert rv <= BWD_DV_RELRMS, rv
-    for a, b, r in ((got[0], ref[0], rq), (got[1], ref[1], rk)):
+    assert wv <= BWD_DV_ROW, wv
+    for a, b, r, w in ((got[0], ref[0], rq, wq), (got[1], ref[1], rk, wk)):
         if np.sqrt(np.mean(np.square(b))) < 1e-9:    # an exactly zero gradient
             assert np.abs(a).max() <= ZERO_GRAD_ABS, np.abs(a).max()
         else:
             assert r <= BWD_DQK_RELRMS, (rq, rk)
+            assert w <= BWD_DQK_ROW, (wq, wk)
 
 
 SMALL = [
@@ -194,6 +200,11 @@ MODIFIED = [
     (1, 2, 1, 300, True, 0, [0, 100, 300], 128, 2.0, 0.0),
     (2, 2, 2, 130, False, 0, None, 64, 1.0, 0.0),
     (1, 2, 2, 96, True, 0, None, 64, 0.0, 2.0),
+    # ALiBi alone at d = 128 (the two-wave dQ kernel with the cap path compiled out): causal
+    # GQA, a window, documents
+    (1, 4, 2, 300, True, 0, None, 128, 0.0, 1.0),
+    (1, 2, 2, 333, False, 90, None, 128, 0.0, 0.7),
+    (1, 4, 2, 290, True, 0, [0, 120, 121, 290], 128, 0.0, 1.5),
 ]
 
 
@@ -214,3 +225,64 @@ def test_bwd_score_modifications(case):
     _check(_run(bits, causal, scale, o, lse, window, docs, alibi, softcap), ref, "oracle O/LSE")
     _check(_run(bits, causal, scale, window=window, docs=docs, alibi=alibi, softcap=softcap),
            ref, "GPU forward O/LSE")
+
+
+def test_bwd_delta_workspace():
+    """The caller's workspace ends holding D_i = dO_i . O_i (the first kernel's output), which
+    the oracle pins as sum_j P_ij dP_ij."""
+    import torch
+    import exact_attention_forward_tiled_amd as fa
+    bits, (q, k, v, g) = _case(53, 1, 4, 2, 300)
+    scale = 1.0 / math.sqrt(128)
+    o, lse = oracle.attention(q, k, v, True, scale)
+    qd, kd, vd, gd = (to_dev_bf16(x) for x in bits)
+    delta = torch.full((1, 4, 300), float("nan"), dtype=torch.float32, device="cuda")
+    log("bwd delta workspace")
+    fa.bwd(qd, kd, vd, to_dev_f32(o), to_dev_f32(lse), gd, causal=True, scale=scale, delta=delta)
+    torch.cuda.synchronize()
+    got = delta.cpu().numpy()
+    # O is fed in fp32 and dO is exact in bf16: D is an fp32 dot product of 128 terms
+    want = bw.delta(o.astype(np.float32).astype(np.float64), g)
+    bound = 128 * 2.0 ** -24 * np.sum(np.abs(o * g), axis=-1) + 1e-7
+    assert np.all(np.abs(got - want) <= bound)
+
+
+def _full_size_sampled(idx, seed):
+    """Backward at a full workload size, all heads on the GPU (from the GPU forward's O and
+    LSE, as a caller runs it); two (batch, kv head) groups checked on sampled query rows
+    (dQ) and key rows (dK, dV, summed over the group's query heads) against the oracle."""
+    w = synth.workload(idx)
+    qb, kb, vb = w.make()
+    gb = synth.normal_bf16((w.B, w.Hq, w.N, w.d), seed, 1.0)
+    log(f"bwd on {w.name}")
+    dq, dk, dv = _run((qb, kb, vb, gb), w.causal, w.scale)
+    group = w.Hq // w.Hkv
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, w.N - 2, w.N - 1],
+                                     rng.integers(0, w.N, 24)]))
+    for b, hk in ((0, 0), (w.B - 1, w.Hkv - 1)):
+        k, v = (synth.bf16_bits_to_f64(x[b, hk]) for x in (kb, vb))
+        got_q, ref_q = [], []
+        ref_k = np.zeros((len(rows), w.d))
+        ref_v = np.zeros((len(rows), w.d))
+        for h in range(hk * group, (hk + 1) * group):
+            q, g = (synth.bf16_bits_to_f64(x[b, h]) for x in (qb, gb))
+            o, lse = oracle.attention_head(q[None, None], k[None, None], v[None, None],
+                                           w.causal, w.scale, 0, 0)
+            rq, rk, rv = bw.backward_rows(q, k, v, g, w.causal, w.scale, o, lse, rows, rows)
+            got_q.append(dq[b, h, rows])
+            ref_q.append(rq)
+            ref_k += rk
+            ref_v += rv
+        _check((np.concatenate(got_q), dk[b, hk, rows], dv[b, hk, rows]),
+               (np.concatenate(ref_q), ref_k, ref_v), f"(b, kv head) = ({b}, {hk})")
+
+
+def test_bwd_full_size_noncausal_long():
+    """Non-causal B2 H16 N16384 d128 (the unrolled non-causal dK/dV path)."""
+    _full_size_sampled(4, 4917)
+
+
+def test_bwd_full_size_causal_gqa():
+    """Causal GQA B1 Hq32 Hkv8 N8192 d128 (dK, dV summed over four query heads)."""
+    _full_size_sampled(3, 3917)

@@ -20,7 +20,8 @@ import pytest
 import oracle
 import synth
 from oracle import mxfp8 as m8
-from gpu_util import MXFP8_O_RELRMS, cuda_ok, log, mxfp8_lse_tol, rel_rms, to_dev_f32
+from gpu_util import (MXFP8_O_RELRMS, MXFP8_O_ROW, cuda_ok, gate, log, mxfp8_lse_tol, rel_rms,
+                      to_dev_f32)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not cuda_ok(), reason="needs a GPU")]
 
@@ -113,10 +114,9 @@ def test_fp8_small(case, tau):
     o, lse = _run(q, k, v, causal, scale, tau=tau)
     ro, rl, tol = _reference(q, k, v, causal, scale)
     assert not np.isnan(o).any() and not np.isnan(lse).any()
-    r = rel_rms(o, ro)
+    gate(o, ro, MXFP8_O_RELRMS, MXFP8_O_ROW, f"{case} tau {tau} O")
     e = float(np.max(np.abs(lse - rl)))
-    log(f"  relRMS(O)={r:.3e} max|dLSE|={e:.3e} (gate {tol:.3e})")
-    assert r <= MXFP8_O_RELRMS, r
+    log(f"  max|dLSE|={e:.3e} (gate {tol:.3e})")
     assert e <= tol, e
 
 
@@ -126,10 +126,10 @@ def test_fp8_scale_sign_and_large_logits():
         log(f"mxfp8 scale {scale}")
         o, lse = _run(q, k, v, False, scale)
         ro, rl, tol = _reference(q, k, v, False, scale)
-        r = rel_rms(o, ro)
+        gate(o, ro, MXFP8_O_RELRMS, MXFP8_O_ROW, f"scale {scale} O")
         e = float(np.max(np.abs(lse - rl)))
-        log(f"  relRMS(O)={r:.3e} max|dLSE|={e:.3e} (gate {tol:.3e})")
-        assert r <= MXFP8_O_RELRMS and e <= tol
+        log(f"  max|dLSE|={e:.3e} (gate {tol:.3e})")
+        assert e <= tol
 
 
 def test_fp8_extreme_logits():
@@ -147,10 +147,9 @@ def test_fp8_extreme_logits():
         o, lse = _run(q, k, v, causal, scale)
         ro, rl, tol = _reference(q, k, v, causal, scale)
         assert np.isfinite(o).all() and np.isfinite(lse).all()
-        r = rel_rms(o, ro)
+        gate(o, ro, MXFP8_O_RELRMS, MXFP8_O_ROW, f"extreme causal={causal} O")
         e = float(np.max(np.abs(lse - rl)))
-        log(f"  relRMS(O)={r:.3e} max|dLSE|={e:.3e} (gate {tol:.3e})")
-        assert r <= MXFP8_O_RELRMS
+        log(f"  max|dLSE|={e:.3e} (gate {tol:.3e})")
         assert e <= tol
 
 
@@ -217,11 +216,10 @@ def test_fp8_workload_sampled_rows(idx):
         log(f"  head {h}: max|dLSE|={e:.3e} (gate {tol:.3e})")
         assert e <= tol
     got, ref, exact = (np.concatenate(x) for x in (got, ref, exact))
-    r = rel_rms(got, ref)
+    gate(got, ref, MXFP8_O_RELRMS, MXFP8_O_ROW, "sampled rows vs emulation O")
     cos = np.mean(np.sum(got * exact, -1) / np.linalg.norm(got, axis=-1) /
                   np.linalg.norm(exact, axis=-1))
-    log(f"  relRMS(O) vs emulation {r:.3e}; mean row cosine vs unquantised exact {cos:.5f}")
-    assert r <= MXFP8_O_RELRMS
+    log(f"  mean row cosine vs unquantised exact {cos:.5f}")
 
 
 MASKED = [
@@ -257,10 +255,9 @@ def _masked_check(q, k, v, causal, scale, window, docs, rows=None):
                                                      t["v"][b, h // group], rows, causal, scale,
                                                      window=window, docs=docs)
         o, lse = o[:, :, rows], lse[:, :, rows]
-    r = rel_rms(o, ro)
+    gate(o, ro, MXFP8_O_RELRMS, MXFP8_O_ROW, "masked O")
     e = float(np.max(np.abs(lse - rl)))
-    log(f"  relRMS(O)={r:.3e} max|dLSE|={e:.3e} (gate {tol:.3e})")
-    assert r <= MXFP8_O_RELRMS, r
+    log(f"  max|dLSE|={e:.3e} (gate {tol:.3e})")
     assert e <= tol, e
 
 
