@@ -3,9 +3,12 @@
 
 A step is one fused attention forward (QK^T, mask, online softmax with
 thresholded rescale, PV, LSE) over one batch of synthetic inputs already
-resident in HBM.  The headline workload is causal B=4, H=16, N=2048, d=128
-bf16; `--config` picks another workload and `--extra` times more of them
-(reported under "extra", never in the headline fields).
+resident in HBM.  The headline workload is the largest bf16 one that fits a
+GPU: non-causal B=2, H=16, N=16384, d=128 with q, k ~ N(0, 3^2) (the running
+max moves often, so the rescale skip ratio is exercised).  The causal GQA
+workload B=1, Hq=32, Hkv=8, N=8192 is always timed beside it (reported under
+"extra"); `--config` picks another headline and `--extra` times more
+workloads (never in the headline fields).
 
 Timing: the GPU is first driven with untimed launches for `--warmup-seconds`
 (clocks ramp up under load), then W untimed warm-up steps, then K timed steps
@@ -78,6 +81,17 @@ def load_traffic(workload_name, fmt="bf16"):
     if rec.get("kernel_hash") != kernel_hash(fmt):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def skip_ratio_model(workload_name):
+    """The skip ratio the tau rule gives in float64 over 32-row groups and 64-key tiles on
+    every head of the workload (stored by tests/golden/make_skip_ratio.py), or None."""
+    path = os.path.join(ROOT, "tests", "golden", "skip_ratio.json")
+    try:
+        with open(path) as fh:
+            return json.load(fh)[workload_name]["skip_ratio"]
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def device_inputs(w):
@@ -391,12 +405,13 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--warmup-seconds", type=float, default=0.5)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--exp", default="hw", choices=["hw", "poly", "mix"])
     ap.add_argument("--poly-frac", type=float, default=0.5,
                     help="with --exp mix: fraction of the exponentials on the cubic")
     ap.add_argument("--tau", type=float, default=8.0)
-    ap.add_argument("--extra", default="", help="other workloads to time (comma list), e.g. 3,4")
+    ap.add_argument("--extra", default="3",
+                    help="other workloads to time (comma list, '' for none), e.g. 2,3,5")
     ap.add_argument("--docs", type=int, default=0,
                     help="also time the workload split into this many equal packed documents "
                          "(bf16, mxfp8; TFLOP/s count 4*d flop per visible pair)")
@@ -473,7 +488,9 @@ def main():
     extra = {"kernel_ms_avg": t["kernel_ms_avg"], "kernel_ms_median": t["kernel_ms_median"],
              "kernel_ms_min": t["kernel_ms_min"], "kernel_ms_max": t["kernel_ms_max"],
              "pct_of_bf16_peak": 100.0 * t["tflops"] / PEAK_BF16_TFLOPS,
-             "skip_ratio": skip, "clock_ghz": ghz,
+             "skip_ratio": skip, "skip_ratio_model": skip_ratio_model(w.name)
+                                   if args.tau == 8.0 else None,
+             "clock_ghz": ghz,
              "pct_of_bf16_peak_at_clock": (100.0 * t["tflops"] / (PEAK_BF16_TFLOPS * ghz / PEAK_CLOCK_GHZ)
                                            if ghz else None),
              "exp_mode": {"bf16": args.exp, "mxfp4": "directp", "mxfp8": "hw"}[w.fmt],
@@ -509,7 +526,9 @@ def main():
             "tflops": round(tx["tflops"], 2), "ms": round(tx["ms_per_step"], 4),
             "kernel_ms_avg": round(tx["kernel_ms_avg"], 4),
             "pct_of_bf16_peak": round(100.0 * tx["tflops"] / PEAK_BF16_TFLOPS, 2),
-            "skip_ratio": sx, "clock_ghz": gx}
+            "skip_ratio": sx,
+            "skip_ratio_model": skip_ratio_model(wx.name) if args.tau == 8.0 else None,
+            "clock_ghz": gx}
         if wx.fmt != "bf16":
             extra["workloads"][wx.name][f"pct_of_{wx.fmt[2:]}_peak"] = round(
                 100.0 * tx["tflops"] / PEAKS[wx.fmt], 2)

@@ -173,6 +173,38 @@ def _stream(torch, device):
 STATS_COUNTERS = 4
 
 
+def require(t, name, shape, dtype, device):
+    """Raise ValueError unless t is a contiguous tensor of this exact shape and dtype on this
+    device.  The C ABI sees only pointers, so a wrong buffer would mean out-of-bounds device
+    accesses: every caller tensor is checked here, before any launch."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _on_gpu(t):
+    """The kernels read and write device memory only."""
+    if not t.is_cuda:
+        raise ValueError("the operands must be CUDA tensors")
+
+
+def _outputs(torch, out, shapes, names, device):
+    """Caller-given output tensors (checked) or new fp32 ones."""
+    if out is None:
+        return tuple(torch.empty(sh, dtype=torch.float32, device=device) for sh in shapes)
+    out = tuple(out)
+    if len(out) != len(shapes):
+        raise ValueError(f"out must hold {len(shapes)} tensors ({', '.join(names)})")
+    for t, sh, nm in zip(out, shapes, names):
+        require(t, nm, sh, torch.float32, device)
+    return out
+
+
 def _stats_ptr(torch, stats):
     """Device pointer of the optional statistics buffer (int64 [>= STATS_COUNTERS], CUDA)."""
     if stats is None:
@@ -192,20 +224,17 @@ def fwd(q, k, v, causal=False, scale=None, tau=8.0, exp_mode="hw", stats=None, o
     C tanh(score / C); docs: int32 CUDA tensor of document offsets 0 < ... < N (packed
     documents, keys visible only within the query's document)."""
     torch = _torch()
-    for t in (q, k, v):
-        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous bf16 CUDA tensors")
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d] tensors")
     B, Hq, N, d = q.shape
-    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
-        raise ValueError("k and v must be [B, Hkv, N, d] matching q")
     Hkv = k.shape[1]
+    require(q, "q", (B, Hq, N, d), torch.bfloat16, q.device)
+    require(k, "k", (B, Hkv, N, d), torch.bfloat16, q.device)
+    require(v, "v", (B, Hkv, N, d), torch.bfloat16, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        o = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device)
-        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
-    else:
-        o, lse = out
+    o, lse = _outputs(torch, out, ((B, Hq, N, d), (B, Hq, N)), ("o", "lse"), q.device)
+    _on_gpu(q)
     alibi_ptr = None
     if alibi is not None:
         if (alibi.dtype != torch.float32 or not alibi.is_cuda or not alibi.is_contiguous()
@@ -258,19 +287,22 @@ def quantize_mxfp4_cols_t(x):
 def fwd_mxfp4(q4, qs, k4, ks, vt4, vts, causal=False, scale=None, tau=8.0, stats=None, out=None):
     """MXFP4 Direct-P forward: returns (O fp32 [B,Hq,N,d], LSE fp32 [B,Hq,N])."""
     torch = _torch()
+    if q4.dim() != 4 or k4.dim() != 4:
+        raise ValueError("MXFP4 codes must be [B, H, N, d/2] tensors")
     B, Hq, N, half_d = q4.shape
     d = 2 * half_d
     Hkv = k4.shape[1]
+    u8, dev = torch.uint8, q4.device
+    require(q4, "q4", (B, Hq, N, d // 2), u8, dev)
+    require(qs, "qs", (B, Hq, N, d // 32), u8, dev)
+    require(k4, "k4", (B, Hkv, N, d // 2), u8, dev)
+    require(ks, "ks", (B, Hkv, N, d // 32), u8, dev)
+    require(vt4, "vt4", (B, Hkv, d, N // 2), u8, dev)
+    require(vts, "vts", (B, Hkv, d, N // 32), u8, dev)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        o = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q4.device)
-        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q4.device)
-    else:
-        o, lse = out
-    for t in (q4, qs, k4, ks, vt4, vts):
-        if t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous():
-            raise ValueError("codes and scales must be contiguous uint8 CUDA tensors")
+    o, lse = _outputs(torch, out, ((B, Hq, N, d), (B, Hq, N)), ("o", "lse"), dev)
+    _on_gpu(q4)
     opts = make_opts(tau, "hw", _stats_ptr(torch, stats))
     check(attn_fwd_mxfp4_ex(q4.data_ptr(), qs.data_ptr(), k4.data_ptr(), ks.data_ptr(),
                             vt4.data_ptr(), vts.data_ptr(), o.data_ptr(), lse.data_ptr(),
@@ -313,22 +345,21 @@ def fwd_mxfp8(q8, qs, k8, ks, vt8, vts, causal=False, scale=None, tau=8.0, stats
     """MXFP8 forward: returns (O fp32 [B,Hq,N,d], LSE fp32 [B,Hq,N]).  window, docs: sliding
     window and document offsets (int32 CUDA tensor), as for fwd."""
     torch = _torch()
+    if q8.dim() != 4 or k8.dim() != 4:
+        raise ValueError("MXFP8 codes must be [B, H, N, d] tensors")
     B, Hq, N, d = q8.shape
     Hkv = k8.shape[1]
+    u8, dev = torch.uint8, q8.device
+    require(q8, "q8", (B, Hq, N, d), u8, dev)
+    require(qs, "qs", (B, Hq, N, d // 32), u8, dev)
+    require(k8, "k8", (B, Hkv, N, d), u8, dev)
+    require(ks, "ks", (B, Hkv, N, d // 32), u8, dev)
+    require(vt8, "vt8", (B, Hkv, d, N), u8, dev)
+    require(vts, "vts", (B, Hkv, d, N // 32), u8, dev)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    for t in (q8, qs, k8, ks, vt8, vts):
-        if t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous():
-            raise ValueError("codes and scales must be contiguous uint8 CUDA tensors")
-    if (k8.shape != (B, Hkv, N, d) or qs.shape != (B, Hq, N, d // 32)
-            or ks.shape != (B, Hkv, N, d // 32) or vt8.shape != (B, Hkv, d, N)
-            or vts.shape != (B, Hkv, d, N // 32)):
-        raise ValueError("MXFP8 operand shapes do not match q8 [B, Hq, N, d]")
-    if out is None:
-        o = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q8.device)
-        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q8.device)
-    else:
-        o, lse = out
+    o, lse = _outputs(torch, out, ((B, Hq, N, d), (B, Hq, N)), ("o", "lse"), dev)
+    _on_gpu(q8)
     doc_ptr, n_docs = None, 0
     if docs is not None:
         if docs.dtype != torch.int32 or not docs.is_cuda or not docs.is_contiguous() \
@@ -352,29 +383,28 @@ def bwd(q, k, v, o, lse, dout, causal=False, scale=None, out=None, delta=None, w
     the forward's sliding window, document offsets, ALiBi slopes and soft-capping (as for
     fwd)."""
     torch = _torch()
-    for t in (q, k, v, dout):
-        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
-            raise ValueError("q, k, v, dout must be contiguous bf16 CUDA tensors")
-    for t in (o, lse):
-        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
-            raise ValueError("o, lse must be contiguous fp32 CUDA tensors")
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d] tensors")
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
-    if (k.shape != (B, Hkv, N, d) or v.shape != k.shape or dout.shape != q.shape
-            or o.shape != q.shape or lse.shape != (B, Hq, N)):
-        raise ValueError("shapes do not match q [B, Hq, N, d]")
+    bf, f32, dev = torch.bfloat16, torch.float32, q.device
+    require(q, "q", (B, Hq, N, d), bf, dev)
+    require(k, "k", (B, Hkv, N, d), bf, dev)
+    require(v, "v", (B, Hkv, N, d), bf, dev)
+    require(dout, "dout", (B, Hq, N, d), bf, dev)
+    require(o, "o", (B, Hq, N, d), f32, dev)
+    require(lse, "lse", (B, Hq, N), f32, dev)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if out is None:
-        dq = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device)
-        dk = torch.empty((B, Hkv, N, d), dtype=torch.float32, device=q.device)
-        dv = torch.empty((B, Hkv, N, d), dtype=torch.float32, device=q.device)
-    else:
-        dq, dk, dv = out
+    dq, dk, dv = _outputs(torch, out, ((B, Hq, N, d), (B, Hkv, N, d), (B, Hkv, N, d)),
+                          ("dq", "dk", "dv"), dev)
     if delta is None:
-        delta = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
-    elif delta.dtype != torch.float32 or not delta.is_cuda or delta.numel() < B * Hq * N:
-        raise ValueError("delta must be an fp32 CUDA tensor of at least B*Hq*N floats")
+        delta = torch.empty((B, Hq, N), dtype=f32, device=dev)
+    elif (delta.dtype != f32 or delta.device != dev or not delta.is_contiguous()
+          or delta.numel() < B * Hq * N):
+        raise ValueError("delta must be a contiguous fp32 tensor of at least B*Hq*N floats "
+                         "on the inputs' device")
+    _on_gpu(q)
     doc_ptr, n_docs = None, 0
     if docs is not None:
         if docs.dtype != torch.int32 or not docs.is_cuda or not docs.is_contiguous() \

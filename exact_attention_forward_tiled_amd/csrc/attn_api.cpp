@@ -22,7 +22,7 @@ int hip_status(hipError_t e) {
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 int check_opts(const attn_opts* o) {
-  if (!(o->tau >= 0.f) || !isfinite(o->tau)) return ATTN_EINVAL;
+  if (!(o->tau >= 0.f && o->tau <= ATTN_TAU_MAX)) return ATTN_EINVAL;   // also rejects NaN
   if (o->exp_mode != ATTN_EXP_HW && o->exp_mode != ATTN_EXP_POLY && o->exp_mode != ATTN_EXP_MIX)
     return ATTN_EINVAL;
   if (o->exp_mode == ATTN_EXP_MIX && !(o->poly_frac >= 0.f && o->poly_frac <= 1.f))

@@ -56,9 +56,17 @@ enum attn_exp_mode {
                                 the special-function unit and the FMA units) */
 };
 
+/* Largest accepted rescale threshold (log2 units): weights up to 2^64 times the row sum
+ * stay far inside fp32, and the MXFP4 / MXFP8 weight scale exponents (tau - 2, tau - 7)
+ * stay below the E8M0 NaN code. */
+#define ATTN_TAU_MAX 64.0f
+
 typedef struct attn_opts {
-    float tau;               /* rescale threshold in log2 units, >= 0 and finite; 0 rescales on
-                                every increase of the maximum (the textbook online softmax) */
+    float tau;               /* rescale threshold in log2 units, 0 <= tau <= ATTN_TAU_MAX
+                                (else ATTN_EINVAL); 0 rescales on every increase of the
+                                maximum (the textbook online softmax).  Stale weights reach
+                                2^tau, so the bound keeps the fp32 sums and the E8M0 weight
+                                scales of the block-scaled forwards far from overflow. */
     int exp_mode;            /* attn_exp_mode */
     float poly_frac;         /* ATTN_EXP_MIX only: fraction of the score elements whose
                                 exponential is the cubic, in [0, 1]; the kernel uses the nearest
@@ -174,9 +182,9 @@ int attn_quantize_mxfp4_cols_t(const float* x, uint8_t* codes, uint8_t* scales,
  *   vts      E8M0 scales [B, Hkv, d, N/32]
  *   o fp32 [B, Hq, N, d], lse fp32 [B, Hq, N]  (natural log)
  *   d = 128; N a multiple of 32 (else ATTN_EUNSUPPORTED); codes must not hold the NaN
- *   patterns 0x7F / 0xFF (the quantisers below never write them).  Options: tau and
- *   stats as for the bf16 forward; window, ALiBi, soft-capping and documents are
- *   ATTN_EUNSUPPORTED.
+ *   patterns 0x7F / 0xFF (the quantisers below never write them).  Options: tau,
+ *   stats, the sliding window and the document offsets as for the bf16 forward; ALiBi
+ *   and soft-capping are ATTN_EUNSUPPORTED.
  */
 int attn_fwd_mxfp8(const uint8_t* q8, const uint8_t* qs, const uint8_t* k8, const uint8_t* ks,
                    const uint8_t* vt8, const uint8_t* vts, float* o, float* lse,

@@ -98,6 +98,22 @@ def test_opts_validation(fa):
     assert fa.attn_fwd_mxfp4_ex(*[FAKE] * 8, 1, 1, 1, 64, 128, 0, 0.1, opts, None) == -2
 
 
+def test_tau_bound(fa):
+    """tau above ATTN_TAU_MAX (64) is rejected by every forward and the backward; 64 itself
+    passes the option check (the call then stops at the unsupported head dimension)."""
+    for tau in (64.5, 200.0, float("inf")):
+        opts = fa.make_opts(tau, "hw")
+        assert fa.attn_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 16, 64, 0, 0.1, opts,
+                              None) == -1
+        assert fa.attn_fwd_mxfp4_ex(*[FAKE] * 8, 1, 1, 1, 64, 128, 0, 0.1, opts, None) == -1
+        assert fa.attn_fwd_mxfp8_ex(*[FAKE] * 8, 1, 1, 1, 64, 128, 0, 0.1, opts, None) == -1
+        assert fa.attn_bwd_ex(*[FAKE] * 10, 1, 1, 1, 16, 64, 0, 0.1, opts, None) == -1
+    opts = fa.make_opts(64.0, "hw")
+    assert fa.attn_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 16, 96, 0, 0.1, opts,
+                          None) == -2
+    assert fa.attn_fwd_mxfp4_ex(*[FAKE] * 8, 1, 1, 1, 64, 64, 0, 0.1, opts, None) == -2
+
+
 def test_default_opts_layout(fa):
     """attn_default_opts fills every field of the C struct; reading them back through the
     binding's mirror checks that the two layouts agree."""
