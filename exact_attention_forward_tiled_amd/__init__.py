@@ -9,7 +9,8 @@ ImportError (there is no fallback path).
 
 import importlib
 
-_BINDING_NAMES = ("AttnError", "EXPORTS", "attn_bwd", "attn_bwd_ex", "attn_fwd", "attn_fwd_ex",
+_BINDING_NAMES = ("AttnError", "EXPORTS", "attn_bwd", "attn_bwd_ex", "attn_bwd_noalloc", "attn_fwd",
+                  "attn_fwd_ex",
                   "attn_fwd_mxfp4", "attn_fwd_mxfp4_ex", "attn_fwd_mxfp8", "attn_fwd_mxfp8_ex",
                   "attn_quantize_mxfp4_cols_t", "attn_quantize_mxfp4_rows",
                   "attn_quantize_mxfp8_cols_t", "attn_quantize_mxfp8_rows", "bwd", "check",

@@ -20,7 +20,7 @@ EXP_MODES = {"hw": 0, "poly": 1, "mix": 2}
 EXPORTS = ("attn_default_opts", "attn_fwd", "attn_fwd_ex", "attn_fwd_mxfp4", "attn_fwd_mxfp4_ex",
            "attn_quantize_mxfp4_rows", "attn_quantize_mxfp4_cols_t", "attn_fwd_mxfp8",
            "attn_fwd_mxfp8_ex", "attn_quantize_mxfp8_rows", "attn_quantize_mxfp8_cols_t",
-           "attn_bwd", "attn_bwd_ex", "attn_strerror", "attn_last_hip_error")
+           "attn_bwd", "attn_bwd_ex", "attn_bwd_noalloc", "attn_strerror", "attn_last_hip_error")
 
 
 class AttnOpts(ctypes.Structure):
@@ -52,6 +52,7 @@ def _load():
         "attn_quantize_mxfp8_cols_t": (I, [P, P, P, I, I, I, P]),
         "attn_bwd": (I, [P] * 10 + [I] * 6 + [F, P]),
         "attn_bwd_ex": (I, [P] * 10 + [I] * 6 + [F, OP, P]),
+        "attn_bwd_noalloc": (I, [P] * 9 + [I] * 6 + [F, OP, P]),
         "attn_strerror": (ctypes.c_char_p, [I]),
         "attn_last_hip_error": (I, []),
     }
@@ -149,6 +150,12 @@ def attn_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, N, d, caus
                 opts=None, stream=None):
     return lib.attn_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, N, d, causal,
                            scale, ctypes.byref(opts) if opts is not None else None, stream)
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale,
+                     opts=None, stream=None):
+    return lib.attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, causal,
+                                scale, ctypes.byref(opts) if opts is not None else None, stream)
 
 
 def attn_quantize_mxfp4_rows(x, codes, scales, rows, cols, stream=None):

@@ -90,6 +90,43 @@ int mx_fwd(hipError_t (*launch)(const attn::MxArgs&), uint32_t qsign, bool band_
   return hip_status(e);
 }
 
+// Validation of the backward's arguments and the kernel arguments; nothing is launched.
+int bwd_args(attn::BwdArgs& a, const void* q, const void* k, const void* v, const float* o,
+             const float* lse, const void* dout, float* dq, float* dk, float* dv, float* delta,
+             int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+             const attn_opts* opts, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return ATTN_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4) || !aligned(delta, 4))
+    return ATTN_EINVAL;
+  int st = check_common(B, Hq, Hkv, N, d, causal, scale);
+  if (st != ATTN_OK) return st;
+  attn_opts def;
+  attn_default_opts(&def);
+  const attn_opts* op = opts ? opts : &def;
+  st = check_opts(op);
+  if (st != ATTN_OK) return st;
+  if (d != 64 && d != 128) return ATTN_EUNSUPPORTED;
+  if ((long long)B * Hkv * ((N + 127) / 128) >= (1LL << 31) ||
+      (long long)B * Hq * ((N + 127) / 128) >= (1LL << 31))
+    return ATTN_EUNSUPPORTED;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.delta = delta;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N = N; a.d = d; a.causal = causal;
+  // a window at least N wide hides nothing: run the plain mask
+  a.window = op->window >= N ? 0 : op->window;
+  a.doc_offsets = op->doc_offsets;
+  a.n_docs = op->doc_offsets != nullptr ? op->n_docs : 0;
+  if (a.n_docs > N) return ATTN_EINVAL;   // documents are non-empty
+  a.alibi = op->alibi_slopes;
+  a.softcap = op->softcap;
+  a.c = scale * 1.4426950408889634f;
+  a.scale = scale;
+  a.stream = stream;
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -165,36 +202,10 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const float* o, con
                 const void* dout, float* dq, float* dk, float* dv, float* delta, int B, int Hq,
                 int Hkv, int N, int d, int causal, float scale, const attn_opts* opts,
                 void* stream) {
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return ATTN_EINVAL;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
-      !aligned(lse, 4) || !aligned(delta, 4))
-    return ATTN_EINVAL;
-  int st = check_common(B, Hq, Hkv, N, d, causal, scale);
-  if (st != ATTN_OK) return st;
-  attn_opts def;
-  attn_default_opts(&def);
-  const attn_opts* op = opts ? opts : &def;
-  st = check_opts(op);
-  if (st != ATTN_OK) return st;
-  if (d != 64 && d != 128) return ATTN_EUNSUPPORTED;
-  if ((long long)B * Hkv * ((N + 127) / 128) >= (1LL << 31) ||
-      (long long)B * Hq * ((N + 127) / 128) >= (1LL << 31))
-    return ATTN_EUNSUPPORTED;
   attn::BwdArgs a;
-  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
-  a.dq = dq; a.dk = dk; a.dv = dv; a.delta = delta;
-  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N = N; a.d = d; a.causal = causal;
-  // a window at least N wide hides nothing: run the plain mask
-  a.window = op->window >= N ? 0 : op->window;
-  a.doc_offsets = op->doc_offsets;
-  a.n_docs = op->doc_offsets != nullptr ? op->n_docs : 0;
-  if (a.n_docs > N) return ATTN_EINVAL;   // documents are non-empty
-  a.alibi = op->alibi_slopes;
-  a.softcap = op->softcap;
-  a.c = scale * 1.4426950408889634f;
-  a.scale = scale;
-  a.stream = stream;
+  const int st = bwd_args(a, q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, N, d, causal,
+                          scale, opts, stream);
+  if (st != ATTN_OK) return st;
   hipError_t e = attn::launch_bwd_bf16(a);
   if (e == hipErrorNotSupported) return ATTN_EUNSUPPORTED;
   return hip_status(e);
@@ -205,6 +216,23 @@ int attn_bwd(const void* q, const void* k, const void* v, const float* o, const 
              int Hkv, int N, int d, int causal, float scale, void* stream) {
   return attn_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, delta, B, Hq, Hkv, N, d, causal, scale,
                      nullptr, stream);
+}
+
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const float* o,
+                     const float* lse, const void* dout, float* dq, float* dk, float* dv, int B,
+                     int Hq, int Hkv, int N, int d, int causal, float scale,
+                     const attn_opts* opts, void* stream) {
+  attn::BwdArgs a;
+  // validate everything first (dq stands in for the workspace pointer: non-null, aligned)
+  const int st = bwd_args(a, q, k, v, o, lse, dout, dq, dk, dv, dq, B, Hq, Hkv, N, d, causal,
+                          scale, opts, stream);
+  if (st != ATTN_OK) return st;
+  if ((long long)B * Hq * N > ATTN_NOALLOC_MAX_ROWS) return ATTN_EUNSUPPORTED;
+  hipError_t e = attn::noalloc_scratch(&a.delta);
+  if (e != hipSuccess) return hip_status(e);
+  e = attn::launch_bwd_bf16(a);
+  if (e == hipErrorNotSupported) return ATTN_EUNSUPPORTED;
+  return hip_status(e);
 }
 
 int attn_fwd_mxfp4_ex(const uint8_t* q4, const uint8_t* qs, const uint8_t* k4, const uint8_t* ks,

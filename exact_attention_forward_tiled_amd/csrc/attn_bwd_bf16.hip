@@ -25,8 +25,10 @@
 // expects from that lane: the probabilities go from one MFMA to the next
 // without any data movement.
 
+#include <mutex>
 #include <type_traits>
 
+#include "../../include/attn.h"
 #include "common.h"
 #include "launch.h"
 
@@ -671,6 +673,36 @@ hipError_t launch_bwd_bf16(const BwdArgs& a) {
   if (a.d == 128) return launch_bwd_d<128>(a);
   if (a.d == 64) return launch_bwd_d<64>(a);
   return hipErrorNotSupported;
+}
+
+}  // namespace attn
+
+// Workspace of the allocation-free backward (attn_bwd_noalloc): D_i for up to
+// ATTN_NOALLOC_MAX_ROWS rows.  Each GPU holds its own copy for the life of the process;
+// every call on a GPU shares it.  In host code this name is a stand-in, not a device
+// address: the kernels get the address resolved by noalloc_scratch below.
+static __device__ __align__(256) float scratch[ATTN_NOALLOC_MAX_ROWS];
+
+namespace attn {
+
+// Device address of `scratch` on the current device, resolved once per device.
+hipError_t noalloc_scratch(float** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<float*>(p);
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace attn

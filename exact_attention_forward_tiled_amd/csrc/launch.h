@@ -71,6 +71,8 @@ struct BwdArgs {
 
 hipError_t launch_fwd_bf16(const FwdArgs& a);
 hipError_t launch_bwd_bf16(const BwdArgs& a);
+// Device address of the allocation-free backward's static workspace on the current device.
+hipError_t noalloc_scratch(float** out);
 hipError_t launch_fwd_mxfp4(const MxArgs& a);
 hipError_t launch_fwd_mxfp8(const MxArgs& a);
 hipError_t launch_quantize_rows(const float* x, uint8_t* codes, uint8_t* scales, long long rows,

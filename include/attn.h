@@ -249,6 +249,25 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const float* o, con
                 int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                 const attn_opts* opts, void* stream);
 
+/*
+ * The bf16 backward without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments, meaning and errors as attn_bwd_ex, except that D (B*Hq*N
+ * floats) goes to a static device array of the library, ATTN_NOALLOC_MAX_ROWS floats
+ * (8 MiB) on each GPU, held until the process ends.  B*Hq*N > ATTN_NOALLOC_MAX_ROWS ->
+ * ATTN_EUNSUPPORTED.  Nothing is allocated: not by the library, not through any other
+ * library.  The array's device address is looked up once per device (on the first call
+ * with that device current).  Every call overwrites all of D before reading it, so nothing
+ * carries over between calls; but calls on one GPU share the array, so calls that overlap
+ * in time on one GPU (other streams, other threads) race and must be serialised by the
+ * caller.
+ */
+#define ATTN_NOALLOC_MAX_ROWS (1 << 21)
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const float* o,
+                     const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                     int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                     const attn_opts* opts, void* stream);
+
 /* Static description of a status code; never NULL. */
 const char* attn_strerror(int status);
 

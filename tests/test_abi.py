@@ -114,6 +114,18 @@ def test_tau_bound(fa):
     assert fa.attn_fwd_mxfp4_ex(*[FAKE] * 8, 1, 1, 1, 64, 64, 0, 0.1, opts, None) == -2
 
 
+def test_bwd_noalloc_validation(fa):
+    """The allocation-free backward validates like attn_bwd_ex before touching the device,
+    and rejects problems whose D does not fit its static workspace (B*Hq*N > 2^21)."""
+    base = [FAKE] * 9
+    assert fa.attn_bwd_noalloc(0, *base[1:], 1, 2, 1, 16, 64, 0, 0.1) == -1
+    assert fa.attn_bwd_noalloc(*base, 1, 2, 1, 0, 64, 0, 0.1) == -1
+    assert fa.attn_bwd_noalloc(*base, 1, 2, 1, 16, 96, 0, 0.1) == -2
+    assert fa.attn_bwd_noalloc(*base, 1, 2, 1, 16, 64, 0, 0.1, fa.make_opts(tau=-1.0)) == -1
+    assert fa.attn_bwd_noalloc(*base, 1, 64, 8, (1 << 21) // 64 + 1, 128, 0, 0.1) == -2
+    assert fa.attn_bwd_noalloc(*base, 2, 16, 16, 65537, 128, 1, 0.1) == -2
+
+
 def test_default_opts_layout(fa):
     """attn_default_opts fills every field of the C struct; reading them back through the
     binding's mirror checks that the two layouts agree."""
