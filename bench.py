@@ -354,8 +354,56 @@ def rates():
             ns = best(lambda: lib.probe_lds_rate(out.data_ptr(), blocks, iters, mode, None))
             out_rates[f"{name}/waves_per_simd={wps}"] = blocks * 256 * iters * 8 * nbytes / ns / ncu
         del out
+    power = clock_under_load(lib, ncu)
     return {"unit": "ns per wave instruction per SIMD (element-step for the exp2 rows)",
-            "rates": {k: round(v, 4) for k, v in out_rates.items()}}
+            "rates": {k: round(v, 4) for k, v in out_rates.items()},
+            "clock_under_load": power}
+
+
+def clock_under_load(lib, ncu, seconds=1.0, iters=8000):
+    """The bf16 MFMA rate and the clock the chip holds with two waves per SIMD issuing MFMAs
+    back to back on random-data operands (mode 0), with every A operand read from LDS
+    (mode 1), and with about 5 softmax-like VALU instructions per MFMA on top (mode 2)."""
+    import ctypes
+    import numpy as np
+    import torch
+    import synth
+    P, I = ctypes.c_void_p, ctypes.c_int
+    lib.probe_power.argtypes = [P, P, P, I, I, I, P]
+    src = torch.from_numpy(synth.normal_bf16((16384,), 77, 1.0).view(np.int16)).cuda()
+    out = torch.empty(ncu * 512, dtype=torch.float32, device="cuda")
+    stats = torch.zeros(2, dtype=torch.int64, device="cuda")
+    flops = ncu * 8 * iters * 8 * 32768.0
+    res = {}
+    for mode, name in ((0, "mfma_random_operands"), (1, "mfma_lds_operands"),
+                       (2, "mfma_lds_operands_plus_5_valu")):
+        def go(st=None):
+            assert lib.probe_power(src.data_ptr(), out.data_ptr(),
+                                   (st if st is not None else stats).data_ptr(), ncu, iters,
+                                   mode, None) == 0
+        t_end = time.perf_counter() + seconds
+        while time.perf_counter() < t_end:
+            for _ in range(4):
+                go()
+            torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(10):
+            go()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / 10
+        st = torch.zeros(2, dtype=torch.int64, device="cuda")
+        go(st)
+        torch.cuda.synchronize()
+        cyc, ticks = (int(x) for x in st.cpu())
+        ghz = cyc / ticks * 0.1
+        tf = flops / (ms * 1e-3) / 1e12
+        res[name] = {"tflops": round(tf, 1), "clock_ghz": round(ghz, 3),
+                     "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 1),
+                     "pct_of_peak_at_clock": round(100 * tf / (PEAK_BF16_TFLOPS * ghz /
+                                                                PEAK_CLOCK_GHZ), 1)}
+    return res
 
 
 def cpu_baseline(w, budget_s=10.0):

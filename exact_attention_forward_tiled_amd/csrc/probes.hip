@@ -119,6 +119,63 @@ __global__ void mfma_rate_probe(float* out, int iters) {
   out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// Clock-under-load probe, in the attention kernels' shape: 512-thread blocks (8 waves, two
+// per SIMD), one block per CU.  Each wave runs `iters` iterations of 8
+// v_mfma_f32_32x32x16_bf16 on operands taken from random data (src: 2048 x 16 bytes):
+//   MODE 0  operands cycle through 4 register-held pairs;
+//   MODE 1  every A operand is read from LDS (ds_read_b128, 16 B per lane per MFMA, as the
+//           attention kernel reads its K and V^T operands);
+//   MODE 2  MODE 1 plus about 5 VALU instructions per MFMA (fma, exp, max, bf16 pack, add:
+//           the softmax's share per MFMA).
+// stats (2 x u64, summed atomically): shader-clock cycles and 100 MHz ticks over each
+// block's lifetime (wave 0), whose ratio is the clock the block ran at.
+template <int MODE>
+__global__ void __launch_bounds__(512) power_probe(const u32x4* __restrict__ src,
+                                                   float* __restrict__ out,
+                                                   unsigned long long* __restrict__ stats,
+                                                   int iters) {
+  __shared__ u32x4 buf[2048];
+  const unsigned long long c0 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  const int t = threadIdx.x, l = t & 63, w = t >> 6;
+  for (int i = t; i < 2048; i += 512) buf[i] = src[i];
+  __syncthreads();
+  u32x4 a[4], b[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    a[k] = src[(64 * (w + k) + l) & 2047];
+    b[k] = src[(64 * (w + k + 8) + l) & 2047];
+  }
+  f32x16 acc[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) acc[k] = zero16();
+  float x = __uint_as_float(0x3f000000u | (src[l][0] & 0x7fffffu)), mx = 0.f, sum = 0.f;
+  uint32_t pk = 0;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const u32x4 av = MODE >= 1 ? buf[((it * 8 + u) * 64 + l) & 2047] : a[u & 3];
+      acc[u & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(b[u & 3]),
+                                                          acc[u & 3], 0, 0, 0);
+      if constexpr (MODE == 2) {
+        x = __builtin_fmaf(x, 0.999f, 0.0007f);
+        const float e = __builtin_amdgcn_exp2f(-x);
+        mx = fmaxf(mx, e);
+        pk ^= pack_bf16x2(e, mx);
+        sum += e;
+      }
+    }
+  }
+  float s = sum + mx + (float)(pk & 1u);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s += acc[0][i] + acc[1][i] + acc[2][i] + acc[3][i];
+  out[blockIdx.x * 512 + t] = s;
+  if (t == 0) {
+    atomicAdd(stats, __builtin_amdgcn_s_memtime() - c0);
+    atomicAdd(stats + 1, __builtin_amdgcn_s_memrealtime() - r0);
+  }
+}
+
 // LDS read-rate probe: 256 threads, each wave reads 16 B (mode 0, ds_read_b128) or
 // 8 B with the transposing read (mode 1) per lane per step from a 32 KiB buffer.
 template <int MODE>
@@ -294,6 +351,20 @@ int probe_rate(float* out, int blocks, int iters, int mode, void* stream) {
 int probe_mfma_rate(float* out, int blocks, int iters, void* stream) {
   if (blocks < 1 || iters < 1) return -1;
   hipLaunchKernelGGL(mfma_rate_probe, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters);
+  return (int)hipGetLastError();
+}
+
+// src: 2048 x 16 bytes of operand data; out: blocks * 512 floats; stats: 2 x u64.
+int probe_power(const void* src, float* out, unsigned long long* stats, int blocks, int iters,
+                int mode, void* stream) {
+  if (blocks < 1 || iters < 1 || mode < 0 || mode > 2) return -1;
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(blocks), dim3(512), 0, (hipStream_t)stream,
+                       (const u32x4*)src, out, stats, iters);
+  };
+  if (mode == 0) go(power_probe<0>);
+  else if (mode == 1) go(power_probe<1>);
+  else go(power_probe<2>);
   return (int)hipGetLastError();
 }
 

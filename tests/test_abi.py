@@ -235,3 +235,59 @@ def test_exp2_cubic_error_bound():
     got = bits.view(np.float32).astype(np.float64)
     rel = np.abs(got / np.exp2(x.astype(np.float64)) - 1.0)
     assert rel.max() < 1.2e-4
+
+
+def test_exp2_cubic_exhaustive_scan(tmp_path):
+    """Every fp32 x in [-126, 8] (2,214,330,370 values) through the kernel's fp32 steps of the
+    cubic (fused multiply-adds, exponent-bit add), against 2^x in double: the largest
+    relative error stays at the fit's 1.03e-4 (the fp32 evaluation adds under 1e-6)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    exe = str(tmp_path / "exp2_scan")
+    subprocess.run([gcc, "-O2", "-fopenmp", "-ffp-contract=off", "-I",
+                    os.path.join(PKG, "csrc"), os.path.join(ROOT, "tests", "exp2_scan.c"),
+                    "-lm", "-o", exe], check=True)
+    count, worst = subprocess.run([exe], check=True, capture_output=True,
+                                  text=True).stdout.split()
+    assert int(count) == 0x41000000 + 1 + 0x42FC0000 + 1
+    assert float(worst) <= 1.04e-4
+
+
+def test_abi_under_address_sanitizer(fa, tmp_path):
+    """The host code of the C ABI built with AddressSanitizer and UndefinedBehaviorSanitizer
+    (g++, host code only; the kernels' objects are linked unchanged), driven through every
+    entry point's argument checks by tests/abi_asan.c.  Nothing is launched."""
+    import glob
+    import shutil
+    import subprocess
+    gxx, gcc = shutil.which("g++"), shutil.which("gcc")
+    if gxx is None or gcc is None:
+        pytest.skip("no host C/C++ compiler")
+    objs = sorted(glob.glob(os.path.join(ROOT, "_build", "obj", "attn_*.hip.o")))
+    if len(objs) < 4:
+        from exact_attention_forward_tiled_amd.build import build
+        build()
+        objs = sorted(glob.glob(os.path.join(ROOT, "_build", "obj", "attn_*.hip.o")))
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    san = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-g", "-O1"]
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
+           "-I", os.path.join(rocm, "include"), "-D__HIP_PLATFORM_AMD__"]
+    api_o = str(tmp_path / "attn_api_asan.o")
+    drv_o = str(tmp_path / "abi_asan.o")
+    exe = str(tmp_path / "abi_asan")
+    subprocess.run([gxx, "-std=c++17", "-fPIC", "-c", *san, *inc,
+                    os.path.join(PKG, "csrc", "attn_api.cpp"), "-o", api_o], check=True)
+    subprocess.run([gcc, "-c", *san, *inc, os.path.join(ROOT, "tests", "abi_asan.c"), "-o",
+                    drv_o], check=True)
+    subprocess.run([gxx, *san, drv_o, api_o, *objs, "-L", os.path.join(rocm, "lib"),
+                    "-Wl,-rpath," + os.path.join(rocm, "lib"), "-lamdhip64", "-o", exe],
+                   check=True)
+    # verify_asan_link_order=0: the environment may preload a library of its own ahead of
+    # the sanitizer runtime
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:verify_asan_link_order=0",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    res = subprocess.run([exe], capture_output=True, text=True, env=env)
+    assert res.returncode == 0 and res.stdout.strip() == "ok", res.stdout + res.stderr
