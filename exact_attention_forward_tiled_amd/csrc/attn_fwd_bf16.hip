@@ -123,9 +123,18 @@ __device__ __forceinline__ int perm_row(int m) {
   return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
+// max of two floats as one v_max_f32.  fmaxf on values the compiler cannot prove canonical
+// (a lane swap's output, a loop-carried maximum) adds a quieting max per operand; the
+// operands here are scores or -inf, never signalling NaNs.
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 __device__ __forceinline__ float half_swap_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float half_swap_sum(float x) {
@@ -371,7 +380,9 @@ __device__ __forceinline__ bool step(const u32x4* svp, const u32x4* skn, const b
     return t;
   };
   u32x4 pk[4];
-  float ls[4] = {0.f, 0.f, 0.f, 0.f};
+  // -0 is the additive identity the compiler may fold, so the first add to each partial sum
+  // disappears (+0 is not: +0 + -0 = +0)
+  float ls[4] = {-0.f, -0.f, -0.f, -0.f};
 
 #pragma unroll
   for (int k = 0; k < SS::NOPS; ++k) {
@@ -394,13 +405,22 @@ __device__ __forceinline__ bool step(const u32x4* svp, const u32x4* skn, const b
       }
     } else if (k == SS::TEST) {        // whole row (other half-wave), threshold test
       mx = half_swap_max(mx);
-      mt = (mx == NEG_INF) ? NEG_INF : (MODS ? mx : mx * c);
+      // an unmasked tile holds a finite score for every row: the -inf guard is for masks
+      if constexpr (MASK) mt = (mx == NEG_INF) ? NEG_INF : (MODS ? mx : mx * c);
+      else mt = MODS ? mx : mx * c;
       any = __ballot(mt > st.m + tau) != 0;
     } else if (k == SS::MNEW) {        // thresholded update of the reference max
-      const float m_new = any ? fmaxf(st.m, mt) : st.m;
-      alpha = (m_new == NEG_INF) ? 1.f : exp2_sel<NP == 16>(st.m - m_new);
+      const float m_up = vmax(st.m, mt);   // unconditional, so the choice is a select
+      const float m_new = any ? m_up : st.m;
+      if constexpr (MASK) {
+        alpha = (m_new == NEG_INF) ? 1.f : exp2_sel<NP == 16>(st.m - m_new);
+        mu = (m_new == NEG_INF) ? 0.f : m_new;
+      } else {
+        // m_new is finite; on a row's first tile st.m = -inf and alpha = 2^-inf = 0
+        alpha = exp2_sel<NP == 16>(st.m - m_new);
+        mu = m_new;
+      }
       st.m = m_new;
-      mu = (m_new == NEG_INF) ? 0.f : m_new;
     } else if (k == SS::LSUM) {
       st.l = __builtin_fmaf(st.l, alpha, (ls[0] + ls[1]) + (ls[2] + ls[3]));
       asm volatile("" ::"v"(st.l));

@@ -154,6 +154,14 @@ __device__ __forceinline__ i32x8 fp4_operand(u32x4 v) {
   return i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
 }
 
+// max of two floats as one v_max_f32 (fmaxf on a lane swap's output or a loop-carried value
+// adds a quieting max per operand; the operands are scores, integers or -inf)
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 struct MBuf {
   // code units: [0, 256) K, unit(row, c) = row*4 + (c ^ kswz(row));
   //             [256, 512) V^T, 256 + unit(col, h) = 256 + col*2 + (h ^ ((col>>3)&1))
@@ -190,18 +198,26 @@ __device__ __forceinline__ bool directp_tile(const f32x16 (&s)[2], u32x4& codes,
       bq[r & 3] = fmaxf(bq[r & 3], v);
     }
   const float bm = fmaxf(fmaxf(bq[0], bq[1]), fmaxf(bq[2], bq[3]));
-  const float Mb = (bm == NEG_INF) ? NEG_INF : bm * c;      // this lane's block max (log2)
+  // this lane's block max (log2); without a mask every score, so the maximum, is finite
+  const float Mb = (MASK && bm == NEG_INF) ? NEG_INF : bm * c;
   auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(Mb), __float_as_uint(Mb), false,
                                              false);
-  const float mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));   // tile row max
+  const float mx = vmax(__uint_as_float(sw[0]), __uint_as_float(sw[1]));   // tile row max
 
   const bool any = __ballot(mx > m + tau) != 0;
-  const float m_new = any ? fmaxf(m, __builtin_ceilf(mx)) : m;
-  alpha = (m_new == NEG_INF) ? 1.f
-          : (m == NEG_INF ? 0.f : __builtin_ldexpf(1.f, (int)(m - m_new)));
+  const float m_up = vmax(m, __builtin_ceilf(mx));   // unconditional: the choice is a select
+  const float m_new = any ? m_up : m;
+  if constexpr (MASK) {
+    alpha = (m_new == NEG_INF) ? 1.f
+            : (m == NEG_INF ? 0.f : __builtin_ldexpf(1.f, (int)(m - m_new)));
+  } else {
+    // m_new is a finite integer; m is an integer or -inf, whose conversion saturates, so
+    // alpha = 2^(m - m_new) is 0 on a row's first tile
+    alpha = __builtin_ldexpf(1.f, (int)(m - m_new));
+  }
   m = m_new;
 
-  bool flush = (Mb == NEG_INF) || (m_new == NEG_INF);
+  bool flush = MASK && ((Mb == NEG_INF) || (m_new == NEG_INF));
   float e = flush ? 0.f : __builtin_floorf(Mb - m_new) - 2.f;
   flush = flush || e < -127.f;
   e = flush ? 0.f : e;
@@ -219,7 +235,9 @@ __device__ __forceinline__ bool directp_tile(const f32x16 (&s)[2], u32x4& codes,
       if constexpr (MASK) x = visible(mb, r) ? x : NEG_INF;
       y[q] = __builtin_amdgcn_exp2f(x);
     }
-    uint32_t word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[0], y[1], 1.0f, 0);
+    // the four converts write all four bytes, so the first one starts from the register's
+    // old contents rather than a zeroed register
+    uint32_t word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes[w], y[0], y[1], 1.0f, 0);
     word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, y[2], y[3], 1.0f, 1);
     word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, y[4], y[5], 1.0f, 2);
     word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, y[6], y[7], 1.0f, 3);
@@ -285,14 +303,11 @@ void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict_
   for (int i = 0; i < kMD / 32; ++i) acc[i] = zero16();
   lacc = zero16();
   float m = NEG_INF;
-  unsigned n_steps = 0, n_rescales = 0;
-  bool first = true;
 
   const int kv_end = CAUSAL ? min(N, Q0 + kMBr) : N;
   const int n = (kv_end + kMBc - 1) / kMBc;
   const int wave_end = CAUSAL ? min(N, q0 + kMRows) : N;
   const bool wave_live = q0 < N;
-  auto active = [&](int j) { return wave_live && j * kMBc < wave_end; };
 
   // Stage t (read by pipeline step t from buffer t & 1) holds K tile t+1 and V tile t-1.
   // Every thread stages one code unit (K for waves 0-3, V^T for waves 4-7) and one scale
@@ -390,11 +405,14 @@ void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict_
   bool any_prev = false;
   float alpha_prev = 1.f;
   const int n_full = CAUSAL ? min(Q0, N) / kMBc : N / kMBc;
+  // rescale decisions that fired; every step's decision passes through rescale() once
+  unsigned n_fires = 0;
   auto rescale = [&]() {
     if (any_prev) {
 #pragma unroll
       for (int i = 0; i < kMD / 32; ++i) acc[i] *= alpha_prev;
       lacc *= alpha_prev;
+      ++n_fires;
     }
   };
   // Pipeline step j: PV and row sum of tile j-1 (pp, ep), QK of tile j+1 into sn,
@@ -411,10 +429,6 @@ void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict_
       any = directp_tile<CAUSAL, false>(sc, pc, ec, m, alpha, j * kMBc, qi, N, c, tau, h);
     any_prev = any;
     alpha_prev = alpha;
-    const bool counted = active(j) && !first;   // branch-free: uniform selects
-    n_steps += counted ? 1u : 0u;
-    n_rescales += (counted && any) ? 1u : 0u;
-    first = first && !active(j);
     store_stage(stg, j + 1);
     load_stage(stg, j + 2);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -464,9 +478,13 @@ void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict_
     if (h == 0)
       LSE[qhead + qi] = l > 0.f ? (m + __builtin_log2f(l)) * kLn2 : -__builtin_inff();
   }
+  // Statistics without per-step bookkeeping: the wave's visible tiles are
+  // [0, ceil(wave_end / 64)); the first always fires (the reference max starts at -inf) and
+  // the rest are the counted steps; tiles past them hold no visible key and never fire.
   if (stats != nullptr && lane == 0 && wave_live) {
-    atomicAdd(stats, (unsigned long long)n_steps);
-    atomicAdd(stats + 1, (unsigned long long)n_rescales);
+    const int n_act = min(n, (wave_end + kMBc - 1) / kMBc);
+    atomicAdd(stats, (unsigned long long)(n_act - 1));
+    atomicAdd(stats + 1, (unsigned long long)(n_fires - 1u));
   }
   if (stats != nullptr && threadIdx.x == 0) {
     atomicAdd(stats + 2, __builtin_amdgcn_s_memtime() - clk0);

@@ -22,6 +22,10 @@ visited tile always fires and is not counted; the skip ratio is 1 - (fires after
 tile) / (tiles visited after the first), summed over groups.  Rows past N (a ragged last
 group) repeat row N - 1, as the kernel's clamped row loads do.
 
+With integer_ref (the block-scaled forwards' rule, "Hardware-Aware FP4 FlashAttention-4",
+section "1. Direct-P para Inferencia Directa": the reference the weights are taken against
+is an integer), a firing group sets m_i = max(m_i, ceil(M_i)) instead.
+
 Only the non-causal and causal masks are modelled.  Scores are float64 here and fp32 in
 the kernel, so a decision can differ where M_i - m_i sits within rounding of tau.
 """
@@ -53,7 +57,7 @@ def tile_maxima(q, k, scale, causal, rows=32, keys=64, chunk=256):
     return out
 
 
-def count_rescales(m_tiles, n, tau, causal, rows=32, keys=64):
+def count_rescales(m_tiles, n, tau, causal, rows=32, keys=64, integer_ref=False):
     """(steps, fires) for the rule above, from tile_maxima's output."""
     n_groups = m_tiles.shape[0] // rows
     n_tiles = m_tiles.shape[1]
@@ -72,20 +76,21 @@ def count_rescales(m_tiles, n, tau, causal, rows=32, keys=64):
             break
         tile = mt[:, :, j]
         fire = np.any(tile > m + tau, axis=1) & live
-        m = np.where(fire[:, None], np.maximum(m, tile), m)
+        up = np.ceil(tile) if integer_ref else tile
+        m = np.where(fire[:, None], np.maximum(m, up), m)
         if j > 0:
             steps += int(live.sum())
             fires += int(fire.sum())
     return steps, fires
 
 
-def skip_counts(q, k, scale, tau, causal, rows=32, keys=64):
+def skip_counts(q, k, scale, tau, causal, rows=32, keys=64, integer_ref=False):
     """(steps, fires) of one head: q [N, d], k [N, d] float64."""
     return count_rescales(tile_maxima(q, k, scale, causal, rows, keys), q.shape[0], tau,
-                          causal, rows, keys)
+                          causal, rows, keys, integer_ref)
 
 
-def skip_counts_brute(q, k, scale, tau, causal, rows=32, keys=64):
+def skip_counts_brute(q, k, scale, tau, causal, rows=32, keys=64, integer_ref=False):
     """The same rule as scalar Python loops (tiny inputs only)."""
     n, nk = q.shape[0], k.shape[0]
     steps = fires = 0
@@ -107,7 +112,8 @@ def skip_counts_brute(q, k, scale, tau, causal, rows=32, keys=64):
                 tile_m.append(best)
             fire = any(tile_m[r] > m[r] + tau for r in range(rows))
             if fire:
-                m = [max(m[r], tile_m[r]) for r in range(rows)]
+                m = [max(m[r], math.ceil(tile_m[r]) if integer_ref and tile_m[r] > -math.inf
+                         else tile_m[r]) for r in range(rows)]
             if not first:
                 steps += 1
                 fires += int(fire)

@@ -211,3 +211,29 @@ def test_directp_workload_sampled_rows():
     cos = np.mean(np.sum(got * exact, -1) / np.linalg.norm(got, axis=-1) /
                   np.linalg.norm(exact, axis=-1))
     log(f"  mean row cosine vs unquantised exact {cos:.4f}")
+
+
+def test_directp_skip_ratio_stats():
+    """The MXFP4 kernel's counters (steps in closed form, rescales counted where they are
+    applied) against the skip-ratio model with the integer reference rule, on the
+    dequantised operands: the step count exactly, the rescale count within a few
+    decisions (scores are fp32 sums in the kernel)."""
+    import torch
+    from oracle import skipsim
+    for causal in (False, True):
+        q, k, v = _case(26, 1, 2, 2, 2048, sigma=3.0)
+        t = mx.quantize_inputs(q, k, v)
+        for tau in (0.0, 8.0):
+            stats = torch.zeros(4, dtype=torch.int64, device="cuda")
+            log(f"mxfp4 stats causal={causal} tau={tau}")
+            _run(q, k, v, causal, 1.0 / math.sqrt(128), tau=tau, stats=stats)
+            steps, resc = (int(x) for x in stats.cpu()[:2])
+            m_steps = m_fires = 0
+            for h in range(2):
+                st, fi = skipsim.skip_counts(t["q"][0, h], t["k"][0, h], 1.0 / math.sqrt(128),
+                                             tau, causal, integer_ref=True)
+                m_steps += st
+                m_fires += fi
+            log(f"  steps {steps} rescales {resc}; model {m_steps} {m_fires}")
+            assert steps == m_steps
+            assert abs(resc - m_fires) <= max(3, 0.002 * steps)

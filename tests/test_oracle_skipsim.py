@@ -13,10 +13,22 @@ def _qk(seed, n, d, sigma):
 
 @pytest.mark.parametrize("n,causal,tau", [(70, False, 0.0), (70, True, 0.0), (96, False, 1.0),
                                           (130, True, 2.0), (33, True, 0.5)])
-def test_matches_scalar_loops(n, causal, tau):
+@pytest.mark.parametrize("integer_ref", [False, True])
+def test_matches_scalar_loops(n, causal, tau, integer_ref):
     q, k = _qk(n, n, 4, 2.0)
-    got = skipsim.skip_counts(q, k, 0.7, tau, causal, rows=8, keys=16)
-    assert got == skipsim.skip_counts_brute(q, k, 0.7, tau, causal, rows=8, keys=16)
+    got = skipsim.skip_counts(q, k, 0.7, tau, causal, rows=8, keys=16, integer_ref=integer_ref)
+    assert got == skipsim.skip_counts_brute(q, k, 0.7, tau, causal, rows=8, keys=16,
+                                            integer_ref=integer_ref)
+
+
+def test_integer_reference_fires_less_or_equal():
+    """Raising the reference to the ceiling of the tile maximum leaves more headroom, so the
+    integer rule never fires more often than the plain one on the same scores."""
+    q, k = _qk(4, 700, 8, 3.0)
+    for tau in (0.0, 2.0, 8.0):
+        plain = skipsim.skip_counts(q, k, 0.3, tau, False)[1]
+        integer = skipsim.skip_counts(q, k, 0.3, tau, False, integer_ref=True)[1]
+        assert integer <= plain
 
 
 def test_step_count_closed_form():
