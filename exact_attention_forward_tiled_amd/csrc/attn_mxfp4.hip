@@ -483,8 +483,10 @@ void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict_
   // the rest are the counted steps; tiles past them hold no visible key and never fire.
   if (stats != nullptr && lane == 0 && wave_live) {
     const int n_act = min(n, (wave_end + kMBc - 1) / kMBc);
-    atomicAdd(stats, (unsigned long long)(n_act - 1));
-    atomicAdd(stats + 1, (unsigned long long)(n_fires - 1u));
+    if (n_act > 0) {
+      atomicAdd(stats, (unsigned long long)(n_act - 1));
+      atomicAdd(stats + 1, (unsigned long long)(n_fires - 1u));
+    }
   }
   if (stats != nullptr && threadIdx.x == 0) {
     atomicAdd(stats + 2, __builtin_amdgcn_s_memtime() - clk0);

@@ -172,6 +172,14 @@ __device__ __forceinline__ i32x8 fp8_operand(const u32x4& lo, const u32x4& hi) {
                (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
+// max of two floats as one v_max_f32 (fmaxf on a lane swap's output or a loop-carried value
+// adds a quieting max per operand; the operands are scores, integers or -inf)
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 struct F8Buf {
   uint8_t kcode[k8Bc * k8KStride];   // K row r at kpos8(r) * 144, 128 code bytes
   uint8_t vcode[k8D * k8VStride];    // V^T column c at c * 80, 64 code bytes (keys)
@@ -217,22 +225,30 @@ __device__ __forceinline__ bool fp8p_tile(const f32x16 (&s)[2], u32x4 (&codes)[2
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     const float bm = fmaxf(bq[mb][0], bq[mb][1]);
-    ml[mb] = (bm == NEG_INF) ? NEG_INF : bm * c;             // log2 units
+    // log2 units; without a mask every score, so the maximum, is finite
+    ml[mb] = (MASK && bm == NEG_INF) ? NEG_INF : bm * c;
   }
   // block b's 32 keys sit in lanes (n, 0) and (n, 1): the first swap leaves lane half h
   // with both halves' maxima of block h, the second hands both block maxima to every lane
   auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(ml[0]), __float_as_uint(ml[1]),
                                              false, false);
-  const float own = fmaxf(__uint_as_float(s1[0]), __uint_as_float(s1[1]));   // block h max
+  const float own = vmax(__uint_as_float(s1[0]), __uint_as_float(s1[1]));   // block h max
   auto s2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(own), __float_as_uint(own), false,
                                              false);
   const float B0 = __uint_as_float(s2[0]), B1 = __uint_as_float(s2[1]);
-  const float mx = fmaxf(B0, B1);                             // tile row max
+  const float mx = vmax(B0, B1);                              // tile row max
 
   const bool any = __ballot(mx > m + tau) != 0;
-  const float m_new = any ? fmaxf(m, __builtin_ceilf(mx)) : m;
-  alpha = (m_new == NEG_INF) ? 1.f
-          : (m == NEG_INF ? 0.f : __builtin_ldexpf(1.f, (int)(m - m_new)));
+  const float m_up = vmax(m, __builtin_ceilf(mx));   // unconditional: the choice is a select
+  const float m_new = any ? m_up : m;
+  if constexpr (MASK) {
+    alpha = (m_new == NEG_INF) ? 1.f
+            : (m == NEG_INF ? 0.f : __builtin_ldexpf(1.f, (int)(m - m_new)));
+  } else {
+    // m_new is a finite integer; m is an integer or -inf, whose conversion saturates, so
+    // alpha = 2^(m - m_new) is 0 on a row's first tile
+    alpha = __builtin_ldexpf(1.f, (int)(m - m_new));
+  }
   m = m_new;
 
   // per block: E = floor(block max - m) - 7, or flushed (fully masked, or E < -127)
@@ -240,7 +256,7 @@ __device__ __forceinline__ bool fp8p_tile(const f32x16 (&s)[2], u32x4 (&codes)[2
   const float Bm[2] = {B0, B1};
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
-    bool flush = (Bm[b] == NEG_INF) || (m_new == NEG_INF);
+    bool flush = MASK && ((Bm[b] == NEG_INF) || (m_new == NEG_INF));
     float e = flush ? 0.f : __builtin_floorf(Bm[b] - m_new) - (float)k8PExp;
     flush = flush || e < -127.f;
     eb[b] = flush ? 0.f : e;
@@ -248,7 +264,6 @@ __device__ __forceinline__ bool fp8p_tile(const f32x16 (&s)[2], u32x4 (&codes)[2
   }
   sbyte = (uint32_t)((int)(h ? eb[1] : eb[0]) + 127);    // this lane scales block h
 
-  const s16x2 zero = {0, 0};
 #pragma unroll
   for (int w = 0; w < 8; ++w) {
     float y[4];
@@ -260,7 +275,10 @@ __device__ __forceinline__ bool fp8p_tile(const f32x16 (&s)[2], u32x4 (&codes)[2
       if constexpr (MASK) x = visible(mb, r) ? x : NEG_INF;
       y[q] = __builtin_amdgcn_exp2f(x);
     }
-    const s16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(zero, y[0], y[1], 1.0f, false);
+    // the second convert overwrites the high half, so the first one starts from the
+    // word's old contents rather than a zeroed register
+    const s16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(
+        __builtin_bit_cast(s16x2, codes[w >> 2][w & 3]), y[0], y[1], 1.0f, false);
     codes[w >> 2][w & 3] = __builtin_bit_cast(
         uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, y[2], y[3], 1.0f, true));
   }
@@ -328,8 +346,6 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict_
   for (int i = 0; i < k8D / 32; ++i) acc[i] = zero16();
   lacc = zero16();
   float m = NEG_INF;
-  unsigned n_steps = 0, n_rescales = 0;
-  bool first = true;
 
   // BAND (the bf16 forward's rules): row i sees keys [lo(i), hi(i)], from a window W
   // (i - W < j, and j < i + W without the causal mask) and / or its document; both
@@ -364,9 +380,6 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict_
   const int n = (kv_end + k8Bc - 1) / k8Bc - t0;
   const int wave_end = BAND ? w_hi + 1 : (CAUSAL ? min(N, q0 + k8Rows) : N);
   const bool wave_live = q0 < N;
-  auto active = [&](int j) {
-    return wave_live && (t0 + j) * k8Bc < wave_end && (!BAND || (t0 + j + 1) * k8Bc > w_lo);
-  };
 
   const int krs = tid >> 3, kcs = tid & 7;     // K staging unit of this thread
   const int vcs = tid >> 2, vch = tid & 3;     // V^T staging unit of this thread
@@ -468,11 +481,14 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict_
   // unmasked tiles [lo_full, n_full): every row of the workgroup sees all their keys
   const int n_full = BAND ? (wg_hi_first + 1) / k8Bc - t0 : (CAUSAL ? min(Q0, N) / k8Bc : N / k8Bc);
   const int lo_full = BAND ? min(n, (wg_lo_last + k8Bc - 1) / k8Bc - t0) : 0;
+  // rescale decisions that fired; every step's decision passes through rescale() once
+  unsigned n_fires = 0;
   auto rescale = [&]() {
     if (any_prev) {
 #pragma unroll
       for (int i = 0; i < k8D / 32; ++i) acc[i] *= alpha_prev;
       lacc *= alpha_prev;
+      ++n_fires;
     }
   };
   // Pipeline step j: QK of tile j, PV and row sum of tile j-1, weights of tile j; then
@@ -491,10 +507,6 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict_
                                            h, klo, khi);
     any_prev = any;
     alpha_prev = alpha;
-    const bool counted = active(j) && !first;   // branch-free: uniform selects
-    n_steps += counted ? 1u : 0u;
-    n_rescales += (counted && any) ? 1u : 0u;
-    first = first && !active(j);
     store_stage(stg, j + 1);
     load_stage(stg, j + 2);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -535,9 +547,16 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict_
     if (h == 0)
       LSE[qhead + qi] = l > 0.f ? (m + __builtin_log2f(l)) * kLn2 : -__builtin_inff();
   }
+  // Statistics without per-step bookkeeping: the wave's visible tiles are the local
+  // indices [j_lo, j_hi); the first always fires (the reference max starts at -inf) and
+  // the rest are the counted steps; the other tiles hold no visible key and never fire.
   if (stats != nullptr && lane == 0 && wave_live) {
-    atomicAdd(stats, (unsigned long long)n_steps);
-    atomicAdd(stats + 1, (unsigned long long)n_rescales);
+    const int j_hi = min(n, (wave_end + k8Bc - 1) / k8Bc - t0);
+    const int j_lo = BAND ? max(0, w_lo / k8Bc - t0) : 0;
+    if (j_hi > j_lo) {
+      atomicAdd(stats, (unsigned long long)(j_hi - j_lo - 1));
+      atomicAdd(stats + 1, (unsigned long long)(n_fires - 1u));
+    }
   }
   if (stats != nullptr && threadIdx.x == 0) {
     atomicAdd(stats + 2, __builtin_amdgcn_s_memtime() - clk0);

@@ -279,3 +279,44 @@ def test_fp8_masked_long_sampled_rows():
     rows = np.array([0, 1, 31, 1023, 1024, 1500, 2047, 2048, 2049, 3071, 3072, 4094, 4095])
     log("mxfp8 masked N4096 W1024 docs")
     _masked_check(q, k, v, True, 1.0 / math.sqrt(128), 1024, [0, 2048, 4096], rows=rows)
+
+
+def _visible_tile_steps(N, causal, window=0, docs=None):
+    """Steps the counters report: per 32-row wave, the 64-key tiles holding a key visible to
+    one of its rows, minus the wave's first (from the oracle's visibility definition)."""
+    vis = oracle.exact.visible(np.arange(N), N, causal, window, docs)
+    steps = 0
+    for r0 in range(0, N, 32):
+        w = vis[r0:r0 + 32]
+        tiles = [bool(w[:, t0:t0 + 64].any()) for t0 in range(0, N, 64)]
+        steps += max(0, sum(tiles) - 1)
+    return steps
+
+
+@pytest.mark.parametrize("causal,window,docs", [(False, 0, None), (True, 0, None),
+                                                (True, 300, None), (False, 200, [0, 700, 1024])])
+def test_fp8_skip_ratio_stats(causal, window, docs):
+    """The MXFP8 kernel's counters (steps in closed form, rescales counted where they are
+    applied): the step count exactly against the visible tiles of every wave, and, without
+    a band, the rescale count against the skip-ratio model with the integer reference rule
+    on the dequantised operands (within a few decisions: fp32 scores in the kernel)."""
+    import torch
+    from oracle import skipsim
+    N, H = 1024, 2
+    q, k, v = _case(27, 1, H, H, N, sigma=3.0)
+    t = m8.quantize_inputs(q, k, v)
+    dd = None if docs is None else torch.tensor(docs, dtype=torch.int32, device="cuda")
+    for tau in (0.0, 8.0):
+        stats = torch.zeros(4, dtype=torch.int64, device="cuda")
+        log(f"mxfp8 stats causal={causal} window={window} docs={docs} tau={tau}")
+        _run(q, k, v, causal, 1.0 / math.sqrt(128), tau=tau, stats=stats, window=window,
+             docs=dd)
+        steps, resc = (int(x) for x in stats.cpu()[:2])
+        want_steps = H * _visible_tile_steps(N, causal, window, docs)
+        log(f"  steps {steps} (visible tiles {want_steps}) rescales {resc}")
+        assert steps == want_steps
+        if window == 0 and docs is None:
+            m_fires = sum(skipsim.skip_counts(t["q"][0, h], t["k"][0, h], 1.0 / math.sqrt(128),
+                                              tau, causal, integer_ref=True)[1] for h in range(H))
+            log(f"  model rescales {m_fires}")
+            assert abs(resc - m_fires) <= max(3, 0.002 * steps)
