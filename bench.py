@@ -23,7 +23,9 @@ Other modes (for rocprofv3 counter runs; they print nothing on stdout):
                   (with --bwd: the three backward kernels instead)
   --mode copy     a plain device-to-device copy of --copy-mib MiB, --steps times
                   (calibrates the HBM byte counters against a known transfer)
-and one that prints its own JSON line:
+and ones that print their own JSON line:
+  --mode lds-patterns  LDS access patterns of the MXFP8 kernel and alternatives, one
+                  dispatch each, for a run under the LDS bank-conflict counter
   --mode rates    issue-rate microbenchmarks from the test-only probe library:
                   v_exp_f32 vs the VALU cubic exp2 vs a plain FMA, back-to-back
                   v_mfma_f32_32x32x16_bf16, and LDS reads (ds_read_b128 and the
@@ -406,6 +408,53 @@ def clock_under_load(lib, ncu, seconds=1.0, iters=8000):
     return res
 
 
+def lds_patterns():
+    """Runs the LDS access-pattern probe (one wave, 4096 accesses each) over the MXFP8
+    kernel's operand-read and staging-write maps, and over alternative layouts, one dispatch
+    per pattern in the printed order.  Under `rocprofv3 --pmc SQ_LDS_BANK_CONFLICT` the
+    counter of each dispatch / 4096 is the conflict cycles of one access."""
+    import ctypes
+    import numpy as np
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "exact_attention_forward_tiled_amd", "libattn_probes.so"))
+    lib.probe_lds_pattern.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_void_p]
+    lanes = np.arange(64)
+    n32, half = lanes % 32, lanes // 32
+
+    def krow8(mb, m):       # K row read by MFMA row m of key block mb (MXFP8 kernel)
+        return 32 * mb + 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3)
+
+    def kpos8(r):           # the MXFP8 kernel's reordered K row position
+        return r ^ (((r >> 4) & 1) << 3)
+
+    layouts = {"rows_reordered_144": lambda r, c: kpos8(r) * 144 + 16 * c,
+               "rows_natural_144": lambda r, c: r * 144 + 16 * c}
+    pats = [("linear", 0, 16 * lanes)]
+    for name, f in layouts.items():
+        for mb in (0, 1):
+            for c0 in (0, 2, 4, 6):
+                pats.append((f"K_read_{name}_block{mb}_chunk{c0}", 0,
+                             np.array([f(krow8(mb, int(n)), c0 + int(hh))
+                                       for n, hh in zip(n32, half)])))
+        pats.append((f"K_write_{name}", 1, np.array([f(int(t >> 3), int(t & 7)) for t in lanes])))
+    pats.append(("V_read_80", 0, n32 * 80 + 16 * half))
+    pats.append(("V_write_80_consecutive_columns", 1,
+                 np.array([(t >> 2) * 80 + 16 * (t & 3) for t in lanes])))
+    pats.append(("V_write_80_columns_four_apart", 1,
+                 np.array([(((t >> 4) & 3) + 4 * ((t >> 2) & 3) + 16 * (t >> 6)) * 80 +
+                           16 * (t & 3) for t in lanes])))
+    out = torch.zeros(64, dtype=torch.float32, device="cuda")
+    for name, write, a in pats:
+        a = np.asarray(a, dtype=np.int64)
+        assert a.shape == (64,) and (a % 16 == 0).all() and a.min() >= 0 and a.max() < 32768
+        at = torch.from_numpy(a.astype(np.int32)).cuda()
+        assert lib.probe_lds_pattern(at.data_ptr(), out.data_ptr(), 4096, write, None) == 0
+        torch.cuda.synchronize()
+    return {"dispatch_order": [(name, "write" if w else "read") for name, w, _ in pats],
+            "accesses_per_dispatch": 4096}
+
+
 def cpu_baseline(w, budget_s=10.0):
     """The float64 oracle, as it stands, on whole (batch, head) slices of the same workload
     (the block-scaled workloads run the oracle's emulation of their quantisation)."""
@@ -476,7 +525,8 @@ def main():
     ap.add_argument("--compare-exp", action="store_true",
                     help="also time the headline workload with the other exp modes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", default="bench", choices=["bench", "launch", "copy", "rates"])
+    ap.add_argument("--mode", default="bench",
+                    choices=["bench", "launch", "copy", "rates", "lds-patterns"])
     ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
 
@@ -494,6 +544,10 @@ def main():
 
     if args.mode == "rates":
         print(json.dumps(rates()), flush=True)
+        return
+
+    if args.mode == "lds-patterns":
+        print(json.dumps(lds_patterns()), flush=True)
         return
 
     if args.mode == "copy":

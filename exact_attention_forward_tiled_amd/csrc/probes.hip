@@ -176,6 +176,33 @@ __global__ void __launch_bounds__(512) power_probe(const u32x4* __restrict__ src
   }
 }
 
+// LDS access-pattern probe: one wave; lane l reads (WRITE = 0) or writes (WRITE = 1) the
+// 16 bytes at byte offset addr[l] of a 32 KiB LDS buffer, `iters` times.  Run under the
+// LDS bank-conflict counter, it gives the conflict cycles of one ds_read_b128 /
+// ds_write_b128 with that lane-to-address map.  addr[l] must be a multiple of 16 below
+// 32768 (the host checks).
+template <int WRITE>
+__global__ void __launch_bounds__(64) lds_pattern_probe(const uint32_t* __restrict__ addr,
+                                                        float* __restrict__ out, int iters) {
+  __shared__ u32x4 buf[2048];
+  const int l = threadIdx.x;
+  for (int i = l; i < 2048; i += 64) buf[i] = u32x4{(uint32_t)i, 1u, 2u, 3u};
+  __syncthreads();
+  const uint32_t a = addr[l] >> 4;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int it = 0; it < iters; ++it) {
+    if constexpr (WRITE) {
+      buf[a] = u32x4{(uint32_t)it, (uint32_t)l, 0u, 0u};
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    } else {
+      acc += buf[a];
+      asm volatile("" ::"v"(acc));
+    }
+  }
+  __syncthreads();
+  out[l] = (float)(acc[0] + acc[1] + buf[l][0]);
+}
+
 // LDS read-rate probe: 256 threads, each wave reads 16 B (mode 0, ds_read_b128) or
 // 8 B with the transposing read (mode 1) per lane per step from a 32 KiB buffer.
 template <int MODE>
@@ -365,6 +392,18 @@ int probe_power(const void* src, float* out, unsigned long long* stats, int bloc
   if (mode == 0) go(power_probe<0>);
   else if (mode == 1) go(power_probe<1>);
   else go(power_probe<2>);
+  return (int)hipGetLastError();
+}
+
+// addr: 64 byte offsets (multiples of 16, below 32768); out: 64 floats.
+int probe_lds_pattern(const void* addr, float* out, int iters, int write, void* stream) {
+  if (iters < 1) return -1;
+  if (write)
+    hipLaunchKernelGGL(lds_pattern_probe<1>, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                       (const uint32_t*)addr, out, iters);
+  else
+    hipLaunchKernelGGL(lds_pattern_probe<0>, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                       (const uint32_t*)addr, out, iters);
   return (int)hipGetLastError();
 }
 
