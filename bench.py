@@ -5,10 +5,12 @@ A step is one fused attention forward (QK^T, mask, online softmax with
 thresholded rescale, PV, LSE) over one batch of synthetic inputs already
 resident in HBM.  The headline workload is the largest bf16 one that fits a
 GPU: non-causal B=2, H=16, N=16384, d=128 with q, k ~ N(0, 3^2) (the running
-max moves often, so the rescale skip ratio is exercised).  The causal GQA
-workload B=1, Hq=32, Hkv=8, N=8192 is always timed beside it (reported under
-"extra"); `--config` picks another headline and `--extra` times more
-workloads (never in the headline fields).
+max moves often, so the rescale skip ratio is exercised).  By default the
+causal GQA workload B=1, Hq=32, Hkv=8, N=8192 and the MXFP4 Direct-P and
+MXFP8 workloads (B=1, H=24, N=16384) are timed beside it, reported under
+"extra" (the block-scaled ones with their accuracy on stored reference rows);
+`--config` picks another headline and `--extra` another list of workloads
+(never in the headline fields).
 
 Timing: the GPU is first driven with untimed launches for `--warmup-seconds`
 (clocks ramp up under load), then W untimed warm-up steps, then K timed steps
@@ -94,6 +96,30 @@ def skip_ratio_model(workload_name):
             return json.load(fh)[workload_name]["skip_ratio"]
     except (OSError, KeyError, ValueError):
         return None
+
+
+def mx_accuracy(wl):
+    """Accuracy of a block-scaled workload's last output on stored reference rows (written
+    by tests/golden/make_mx_reference_rows.py from the oracle): the mean row cosine against
+    exact attention on the unquantised inputs (the explainer page quotes about 0.944 for
+    Direct-P and 0.990 for its FP8 path), and the largest per-row relative error against
+    the emulation of the same quantisation; None when no rows are stored for it."""
+    import numpy as np
+    path = os.path.join(ROOT, "tests", "golden", "mx_reference_rows.npz")
+    name = wl.w.name
+    try:
+        ref = np.load(path)
+        heads, rows = ref[f"{name}/heads"], ref[f"{name}/rows"]
+        exact, emul = ref[f"{name}/exact"], ref[f"{name}/emulated"]
+    except (OSError, KeyError, ValueError):
+        return None
+    got = wl.o[0][heads][:, rows].cpu().numpy().astype(np.float64)
+    cos = np.sum(got * exact, -1) / (np.linalg.norm(got, axis=-1) * np.linalg.norm(exact, axis=-1))
+    row_err = np.linalg.norm(got - emul, axis=-1) / np.linalg.norm(emul, axis=-1)
+    return {"rows": int(cos.size), "mean_row_cosine_vs_exact": round(float(cos.mean()), 5),
+            "min_row_cosine_vs_exact": round(float(cos.min()), 5),
+            "max_row_relerr_vs_emulation": float(row_err.max()),
+            "rows_matching_emulation_within_1e-5": round(float(np.mean(row_err < 1e-5)), 4)}
 
 
 def device_inputs(w):
@@ -507,7 +533,7 @@ def main():
     ap.add_argument("--poly-frac", type=float, default=0.5,
                     help="with --exp mix: fraction of the exponentials on the cubic")
     ap.add_argument("--tau", type=float, default=8.0)
-    ap.add_argument("--extra", default="3",
+    ap.add_argument("--extra", default="3,5,6",
                     help="other workloads to time (comma list, '' for none), e.g. 2,3,5")
     ap.add_argument("--docs", type=int, default=0,
                     help="also time the workload split into this many equal packed documents "
@@ -582,6 +608,7 @@ def main():
     wl = make_workload(w, args.exp, args.tau, args.poly_frac)
     t = time_workload(wl, args.steps, args.warmup, args.warmup_seconds)
     skip, ghz = launch_stats(wl)
+    acc = mx_accuracy(wl) if w.fmt != "bf16" else None
     del wl
     torch.cuda.empty_cache()
     kernel_tf = t["kernel_tflops"]
@@ -601,6 +628,7 @@ def main():
              "compute_units": props.multi_processor_count, "workloads": {}}
     if w.fmt != "bf16":
         extra[f"pct_of_{w.fmt[2:]}_peak"] = 100.0 * t["tflops"] / PEAKS[w.fmt]
+        extra["accuracy"] = acc
     if args.compare_exp and w.fmt == "bf16":
         for other, frac in (("hw", None), ("poly", None), ("mix", 0.25), ("mix", 0.5), ("mix", 0.75)):
             if other == args.exp and (other != "mix" or frac == args.poly_frac):
@@ -622,6 +650,7 @@ def main():
         wl = make_workload(wx, args.exp, args.tau, args.poly_frac)
         tx = time_workload(wl, max(5, args.steps // 2), args.warmup, args.warmup_seconds)
         sx, gx = launch_stats(wl)
+        ax = mx_accuracy(wl) if wx.fmt != "bf16" else None
         del wl
         torch.cuda.empty_cache()
         extra["workloads"][wx.name] = {
@@ -634,6 +663,7 @@ def main():
         if wx.fmt != "bf16":
             extra["workloads"][wx.name][f"pct_of_{wx.fmt[2:]}_peak"] = round(
                 100.0 * tx["tflops"] / PEAKS[wx.fmt], 2)
+            extra["workloads"][wx.name]["accuracy"] = ax
 
     if args.window and w.fmt in ("bf16", "mxfp8"):
         log(f"timing {w.name} with window {args.window}")
