@@ -8,7 +8,8 @@
 // rebuilds the probabilities from it).  With s = scale q.k and P = exp(s - LSE):
 //   D_i  = dO_i . O_i                         (delta_kernel)
 //   dS   = P * (dO V^T - D)
-//   dV   = P^T dO,  dK = scale dS^T Q          (dkdv_kernel, one workgroup per key block)
+//   dV   = P^T dO,  dK = scale dS^T Q          (dkdv_kernel, one workgroup per key block,
+//                                              two waves of different roles per 32 keys)
 //   dQ   = scale dS K                          (dq_kernel, one workgroup per query block)
 // Each kernel recomputes S and dP for its own orientation, so every output is
 // written once by one workgroup: no atomics, deterministic results.  The forward's
@@ -205,18 +206,75 @@ struct Mods {
   float ccap;           // soft-capping: C log2(e)
 };
 
-// dK, dV for 128 keys of one (batch, kv head): each wave owns 32 keys; the loop runs
-// over the group's query heads and their 64-query tiles (causal: only tiles that reach
-// the workgroup's keys; BAND: only tiles within the keys' window and documents).
+// One query tile of the dK/dV loop in LDS, with its per-row scalars.  Each tensor is
+// stored by 16-byte column chunks: chunk c of row r at (c * 68 + r) * 16, the 64 rows of a
+// chunk followed by 4 units of padding.  Three access patterns then touch every bank once
+// per pass: 16 lanes reading one chunk of 16 different rows (the row operands), 32 lanes
+// reading 8 bytes of 4 chunks x 4 rows (the transposing reads), and 16 lanes writing
+// consecutive rows of one chunk (the staging).
+template <int D>
+struct alignas(16) QTile {
+  static constexpr int kChunk = (kBTile + 4) * 16;   // bytes per column chunk
+  float l2[kBTile];                   // LSE in log2 units (+inf: the row has no weight)
+  float dl[kBTile];                   // D_i
+  uint8_t q[D / 8 * kChunk];
+  uint8_t g[D / 8 * kChunk];          // dO
+};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes, lane t
+// returns element t % 4 of the 8-byte words addressed by lanes t / 4, t / 4 + 4, t / 4 + 8,
+// t / 4 + 12 (probed).  When lane a of the group addresses the 8 bytes holding columns
+// 4 (a % 4) .. + 3 of row a / 4 of a bf16 tile, lane t receives column t of four
+// consecutive rows.
+__device__ __forceinline__ uint2 lds_tr16(const uint8_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  return __builtin_bit_cast(uint2, v);
+}
+
+// A operand (8 consecutive k = rows of the tile, one m = column per lane) from a QTile
+// tensor: lane l holds rows r0 + 8 (l / 32) + 0..7 of column c0 + l % 32, when p is the
+// lane's address of row r0 + 8 (l / 32) + (l % 16) / 4, column c0 + 16 ((l / 16) % 2) +
+// 4 (l % 4) (rows r + 4 lie 64 bytes further on in a chunk).
+__device__ __forceinline__ u32x4 lds_tr_operand(const uint8_t* p) {
+  const uint2 lo = lds_tr16(p), hi = lds_tr16(p + 64);
+  return u32x4{lo.x, lo.y, hi.x, hi.y};
+}
+
+constexpr int kKVThreads = 2 * kBThreads;    // dK/dV workgroup: two waves per 32 keys
+
+// dK, dV for 128 keys of one (batch, kv head).  The loop runs over the group's query
+// heads and their 64-query tiles (causal: only tiles that reach the workgroup's keys;
+// BAND: only tiles within the keys' window and documents).
+//
+// Two waves own each 32 keys, with different roles, so that each needs half the
+// registers and two waves share every SIMD (one's elementwise work runs beside the
+// other's products):
+//   P wave  (waves 0-3): S = Q K^T, P; dV^T += dO^T P
+//   dS wave (waves 4-7): dP = dO V^T; dS = P (dP - D); dK^T += Q^T dS
+// P crosses from one to the other through LDS in fp32 (with soft-capping, P times the
+// cap's derivative, which is all dS needs of it).  The query tiles are double-buffered:
+// the next tile is fetched into registers at the top of a step and written to the other
+// buffer after the middle barrier.  Q^T and dO^T come from the row-major tile through
+// transposing reads.
 template <int D, bool CAUSAL, bool BAND, bool MODS>
-__global__ __launch_bounds__(kBThreads) void dkdv_kernel(
+__global__ __launch_bounds__(kKVThreads) void dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Delta, float* __restrict__ dK,
     float* __restrict__ dV, int Hq, int Hkv, int N, int nkb, float c, float scale, Band band,
     Mods mods) {
-  __shared__ BTile<D> tile;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  using Tile = QTile<D>;
+  constexpr int kChunk = Tile::kChunk;
+  constexpr int kUnits = kBTile * D * 2 / 16 / kKVThreads;   // 16-byte units per thread
+  __shared__ Tile tiles[2];
+  __shared__ f32x4 xchg[kBWaves][kBTile / 8][64];            // P: [pair][register quad][lane]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave & (kBWaves - 1);
+  const bool p_role = wave < kBWaves;
   const int n32 = lane & 31, h = lane >> 5;
   // the key blocks of one kv head run on one XCD (its Q / dO tiles stay in that L2);
   // causal: the blocks with the most query tiles (the lowest keys) first
@@ -224,33 +282,15 @@ __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
   const int kb = wi.qb_rank, hkv = wi.hkv, b = wi.b;
   const int group = Hq / Hkv;
   const int K0 = kb * kBBlock;
-  const int kw0 = K0 + wave * 32;           // this wave's keys
+  const int kw0 = K0 + pair * 32;           // this wave's keys
   const int key = kw0 + n32;                // this lane's key (accumulator column)
-
   const size_t khead = (size_t)(b * Hkv + hkv) * N;
-  // K^T and V^T as B operands: lane holds K[key][16c + 8h .. +7] for each d chunk c
-  u32x4 kop[D / 16], vop[D / 16];
-  {
-    const int kr = min(key, N - 1);
-    const uint16_t* krow = K + (khead + kr) * D;
-    const uint16_t* vrow = V + (khead + kr) * D;
-#pragma unroll
-    for (int cc = 0; cc < D / 16; ++cc) {
-      kop[cc] = *(const u32x4*)(krow + 16 * cc + 8 * h);
-      vop[cc] = *(const u32x4*)(vrow + 16 * cc + 8 * h);
-    }
-  }
-  f32x16 dk[D / 32], dv[D / 32];
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i) {
-    dk[i] = zero16();
-    dv[i] = zero16();
-  }
 
   // query tiles [qt0, qt1) reach the workgroup's keys; BAND: this lane's key is seen by
-  // queries [kq_lo, kq_hi], this wave's keys by [wq_lo, wq_hi]
+  // queries [kq_lo, kq_hi], this wave's keys by [wq_lo, wq_hi], every key of the wave by
+  // [fq_lo, fq_hi]
   int qt0 = CAUSAL ? K0 / kBTile : 0, qt1 = (N + kBTile - 1) / kBTile;
-  int kq_lo = 0, kq_hi = 0, wq_lo = 0, wq_hi = 0;
+  int kq_lo = 0, kq_hi = 0, wq_lo = 0, wq_hi = 0, fq_lo = 0, fq_hi = -1;
   if (BAND) {
     int lo, hi, lo2, hi2;
     band.queries<CAUSAL>(K0, lo, hi);
@@ -258,174 +298,277 @@ __global__ __launch_bounds__(kBThreads) void dkdv_kernel(
     qt0 = lo / kBTile;
     qt1 = hi2 / kBTile + 1;
     band.queries<CAUSAL>(min(key, N - 1), kq_lo, kq_hi);
-    band.queries<CAUSAL>(min(kw0, N - 1), wq_lo, hi);
-    band.queries<CAUSAL>(min(kw0 + 31, N - 1), lo, wq_hi);
+    band.queries<CAUSAL>(min(kw0, N - 1), wq_lo, fq_hi);
+    band.queries<CAUSAL>(min(kw0 + 31, N - 1), fq_lo, wq_hi);
     // the same in every lane of the wave: kept in scalar registers
     wq_lo = __builtin_amdgcn_readfirstlane(wq_lo);
     wq_hi = __builtin_amdgcn_readfirstlane(wq_hi);
+    fq_lo = __builtin_amdgcn_readfirstlane(fq_lo);
+    fq_hi = __builtin_amdgcn_readfirstlane(fq_hi);
   }
-  const int pm = perm_row(n32);
-  // (query head, query tile) steps in order; the next step's rows are fetched into
-  // registers while the current one computes
+  // lane offsets: S / dP A operands (rows in the order pi, chunk 2 cc + h) and the
+  // transposed operands (row 8 h + (lane % 16) / 4, column 16 ((lane / 16) % 2) +
+  // 4 (lane % 4): chunk 2 ((lane / 16) % 2) + (lane % 4) / 2, byte 8 (lane % 2))
+  const int a_off = h * kChunk + perm_row(n32) * 16;
+  const int t_off = (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) * kChunk +
+                    (8 * h + ((lane & 15) >> 2)) * 16 + 8 * (lane & 1);
+  // (query head, query tile) steps in order
   const int steps_per_head = qt1 - qt0;
   const int nsteps = group * steps_per_head;
   auto step_q0 = [&](int st) { return (qt0 + st % steps_per_head) * kBTile; };
   auto step_qhead = [&](int st) {
     return (size_t)(b * Hq + hkv * group + st / steps_per_head) * N;
   };
-  StageRegs<D> sr;
+  // staging: unit u of a thread is row unit % 64, bytes 16 (unit / 64) .. + 15 (rows past
+  // N read as row N - 1: in bounds; their LSE of +inf gives them no weight)
+  u32x4 sq[kUnits], sg[kUnits];
   float lse_next = 0.f, d_next = 0.f;
   auto fetch = [&](int st) {
     const size_t qh = step_qhead(st);
     const int q0 = step_q0(st);
-    stage_load(sr, Q + qh * D, dO + qh * D, q0, N);
+    const uint16_t* qb = Q + qh * D;
+    const uint16_t* gb = dO + qh * D;
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+      const int unit = tid + u * kKVThreads;
+      const int gr = min(q0 + unit % kBTile, N - 1);
+      sq[u] = *(const u32x4*)(qb + (size_t)gr * D + 8 * (unit / kBTile));
+      sg[u] = *(const u32x4*)(gb + (size_t)gr * D + 8 * (unit / kBTile));
+    }
     if (tid < kBTile) {
       const int qr = q0 + tid;
       lse_next = qr < N ? LSE[qh + qr] : -__builtin_inff();
       d_next = qr < N ? Delta[qh + qr] : 0.f;
     }
   };
-  if (nsteps > 0) fetch(0);
-  for (int st = 0; st < nsteps; ++st) {
-    const int q0 = step_q0(st);
-    // ALiBi slope of this step's query head, log2 units (0: no bias)
-    const float slope2 =
-        (MODS && mods.alibi != nullptr)
-            ? mods.alibi[hkv * group + st / steps_per_head] * kLog2e : 0.f;
-    {
-      __syncthreads();
-      stage_store(tile, sr, true, true);
-      if (tid < kBTile) {
-        // rows past N or without visible keys: +inf makes their weights 0
-        tile.s0[tid] = (lse_next == -__builtin_inff()) ? __builtin_inff() : lse_next * kLog2e;
-        tile.s1[tid] = d_next;
-      }
-      __syncthreads();
-      if (st + 1 < nsteps) fetch(st + 1);
-      // this wave's keys all lie after the tile's last query (or outside its band):
-      // nothing visible
-      if (!BAND && CAUSAL && kw0 > q0 + kBTile - 1) continue;
-      if (BAND && (kw0 >= N || q0 > wq_hi || q0 + kBTile - 1 < wq_lo)) continue;
-      // one 32-query half: S and dP, then P and dS, then the dK / dV products
-      auto half = [&](int sub) {
-        const int qs = q0 + kSub * sub;
-        // S = Q_pi K^T and dP = dO_pi V^T (queries x keys; rows permuted), each as two
-        // accumulation chains over alternate d chunks
-        f32x16 s = zero16(), dp = zero16(), s2 = zero16(), dp2 = zero16();
+  auto store = [&](Tile& t) {
 #pragma unroll
-        for (int cc = 0; cc < D / 16; cc += 2) {
-          const uint8_t* qr = tile.a + (kSub * sub + pm) * BTile<D>::kRow + 32 * cc + 16 * h;
-          const uint8_t* gr = tile.b + (kSub * sub + pm) * BTile<D>::kRow + 32 * cc + 16 * h;
-          s = mfma_bf16(lds_u32x4(qr), kop[cc], s);
-          dp = mfma_bf16(lds_u32x4(gr), vop[cc], dp);
-          s2 = mfma_bf16(lds_u32x4(qr + 32), kop[cc + 1], s2);
-          dp2 = mfma_bf16(lds_u32x4(gr + 32), vop[cc + 1], dp2);
-        }
-        // this lane's 16 query rows: acc_row(r, h) = 8h + r (r < 8), 16 + 8h + r - 8
-        f32x4 l4[4], d4[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r0 = kSub * sub + 16 * (i >> 1) + 8 * h + 4 * (i & 1);
-          l4[i] = *(const f32x4*)(tile.s0 + r0);
-          d4[i] = *(const f32x4*)(tile.s1 + r0);
-        }
-        // P and dS; register r holds query qs + acc_row(r, h) for this lane's key.  CAP:
-        // soft-capping (a uniform choice, made once around the loop)
-        f32x16 p, ds;
-        auto elements = [&](auto cap_tag) {
-          constexpr bool CAP = decltype(cap_tag)::value;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int qi = acc_row(r, h);
-            float x, dfac = 1.f;
-            if constexpr (MODS) {
-              const float raw = s[r] + s2[r];
-              float t = raw * c;
-              if constexpr (CAP) {
-                const float y = __builtin_amdgcn_exp2f(raw * mods.k2);
-                const float th = __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(y + 1.f), 1.f);
-                t = mods.ccap * th;
-                dfac = __builtin_fmaf(-th, th, 1.f);
-              }
-              t = __builtin_fmaf(-slope2, __builtin_fabsf((float)(key - (qs + qi))), t);
-              x = t - l4[r >> 2][r & 3];
-            } else {
-              x = __builtin_fmaf(s[r] + s2[r], c, -l4[r >> 2][r & 3]);
-            }
-            // non-short-circuit: evaluated whole, so no branch per element
-            const bool vis = BAND ? ((key < N) & (qs + qi >= kq_lo) & (qs + qi <= kq_hi))
-                                  : (key < N && (!CAUSAL || key <= qs + qi));
-            const float pr = vis ? __builtin_amdgcn_exp2f(x) : 0.f;
-            p[r] = pr;
-            const float g = pr * (dp[r] + dp2[r] - d4[r >> 2][r & 3]);
-            ds[r] = CAP ? g * dfac : g;
-          }
-        };
-        if constexpr (MODS) {
-          if (mods.k2 != 0.f) elements(std::true_type{});
-          else elements(std::false_type{});
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int qi = acc_row(r, h);
-            const float x = __builtin_fmaf(s[r] + s2[r], c, -l4[r >> 2][r & 3]);
-            // non-short-circuit: evaluated whole, so no branch per element
-            const bool vis = BAND ? ((key < N) & (qs + qi >= kq_lo) & (qs + qi <= kq_hi))
-                                  : (key < N && (!CAUSAL || key <= qs + qi));
-            const float pr = vis ? __builtin_amdgcn_exp2f(x) : 0.f;
-            p[r] = pr;
-            ds[r] = pr * (dp[r] + dp2[r] - d4[r >> 2][r & 3]);
-          }
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS (d x keys), over the two 16-query chunks
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) {
-          const u32x4 pb = pack_chunk(p, q2), db = pack_chunk(ds, q2);
-#pragma unroll
-          for (int dbk = 0; dbk < D / 32; ++dbk) {
-            const int dcol = 32 * dbk + n32;
-            const int off = dcol * kColStride + 2 * kSub * sub + 32 * q2 + 16 * h;
-            dv[dbk] = mfma_bf16(lds_u32x4(tile.bt + off), pb, dv[dbk]);
-            dk[dbk] = mfma_bf16(lds_u32x4(tile.at + off), db, dk[dbk]);
-          }
-        }
-      };
-      // The two halves are independent until they meet in dK / dV.  Unrolled (non-causal),
-      // the compiler overlaps one half's exponentials with the other's products; in the
-      // causal and band forms, with their masks, both halves' scores live at once push the
-      // K / V operands into AGPRs (415 register moves per step against 128), so the halves
-      // run one after the other.
-      if constexpr (CAUSAL || BAND || MODS) {
-#pragma unroll 1
-        for (int sub = 0; sub < kBTile / kSub; ++sub) half(sub);
-      } else {
-#pragma unroll
-        for (int sub = 0; sub < kBTile / kSub; ++sub) half(sub);
-      }
+    for (int u = 0; u < kUnits; ++u) {
+      const int unit = tid + u * kKVThreads;
+      const int off = (unit / kBTile) * kChunk + (unit % kBTile) * 16;
+      *(u32x4*)(t.q + off) = sq[u];
+      *(u32x4*)(t.g + off) = sg[u];
     }
+    if (tid < kBTile) {
+      // rows past N or without visible keys: +inf makes their weights 0
+      t.l2[tid] = (lse_next == -__builtin_inff()) ? __builtin_inff() : lse_next * kLog2e;
+      t.dl[tid] = d_next;
+    }
+  };
+  // this wave's keys all lie after the tile's last query (or outside its band): nothing
+  // visible in the step
+  auto idle_at = [&](int q0) {
+    return BAND ? (kw0 >= N || q0 > wq_hi || q0 + kBTile - 1 < wq_lo)
+                : (CAUSAL && kw0 > q0 + kBTile - 1);
+  };
+  // one 32 x 32 product set: acc = X_pi Y^T over d, X rows from the tile, Y^T in registers
+  auto rows_product = [&](const uint8_t* x, const u32x4 (&y)[D / 16], int sub) {
+    f32x16 acc = zero16();
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc)
+      acc = mfma_bf16(lds_u32x4(x + 2 * cc * kChunk + kSub * sub * 16 + a_off), y[cc], acc);
+    return acc;
+  };
+  // acc[dbk] += X^T B over one 32-query half: X^T from the tile by transposing reads
+  auto cols_product = [&](f32x16 (&acc)[D / 32], const uint8_t* x, const u32x4 (&bop)[2],
+                          int sub) {
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+      for (int dbk = 0; dbk < D / 32; ++dbk)
+        acc[dbk] = mfma_bf16(
+            lds_tr_operand(x + 4 * dbk * kChunk + (kSub * sub + 16 * q2) * 16 + t_off), bop[q2],
+            acc[dbk]);
+  };
+  auto write_out = [&](float* dst, const f32x16 (&acc)[D / 32], float mul) {
+    if (key < N) {
+      float* row = dst + (khead + key) * D;
+#pragma unroll
+      for (int dbk = 0; dbk < D / 32; ++dbk)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          f32x4 v = {acc[dbk][4 * a4] * mul, acc[dbk][4 * a4 + 1] * mul,
+                     acc[dbk][4 * a4 + 2] * mul, acc[dbk][4 * a4 + 3] * mul};
+          *(f32x4*)(row + 32 * dbk + 8 * a4 + 4 * h) = v;
+        }
+    }
+  };
+
+  if (nsteps > 0) {
+    fetch(0);
+    store(tiles[0]);
   }
-  // dK = scale * (dK^T)^T, dV = (dV^T)^T: lane holds d 32dbk + 8a + 4h + 0..3 of its key
-  if (key < N) {
-    float* dkrow = dK + (khead + key) * D;
-    float* dvrow = dV + (khead + key) * D;
+  __syncthreads();
+  if (p_role) {
+    // K^T as B operand: lane holds K[key][16c + 8h .. +7] for each d chunk c
+    u32x4 kop[D / 16];
+    {
+      const uint16_t* krow = K + (khead + min(key, N - 1)) * D;
 #pragma unroll
-    for (int dbk = 0; dbk < D / 32; ++dbk)
+      for (int cc = 0; cc < D / 16; ++cc) kop[cc] = *(const u32x4*)(krow + 16 * cc + 8 * h);
+      // wait for the operands here: left pending into the loop, they would make every
+      // step wait for its own prefetch of the next tile as well
 #pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const int col = 32 * dbk + 8 * a4 + 4 * h;
-        f32x4 kv = {dk[dbk][4 * a4] * scale, dk[dbk][4 * a4 + 1] * scale,
-                    dk[dbk][4 * a4 + 2] * scale, dk[dbk][4 * a4 + 3] * scale};
-        f32x4 vv = {dv[dbk][4 * a4], dv[dbk][4 * a4 + 1], dv[dbk][4 * a4 + 2],
-                    dv[dbk][4 * a4 + 3]};
-        *(f32x4*)(dkrow + col) = kv;
-        *(f32x4*)(dvrow + col) = vv;
+      for (int cc = 0; cc < D / 16; ++cc) asm volatile("" ::"v"(kop[cc]));
+    }
+    f32x16 dv[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) dv[i] = zero16();
+    for (int st = 0; st < nsteps; ++st) {
+      const Tile& tl = tiles[st & 1];
+      const int q0 = step_q0(st);
+      if (st + 1 < nsteps) fetch(st + 1);
+      const bool idle = idle_at(q0);
+      // ALiBi slope of this step's query head, log2 units (0: no bias)
+      const float slope2 =
+          (MODS && mods.alibi != nullptr)
+              ? mods.alibi[hkv * group + st / steps_per_head] * kLog2e : 0.f;
+      u32x4 pb[2][2];
+      // P of one half; register r holds query q0 + 32 sub + acc_row(r, h) for this lane's
+      // key.  CAP: soft-capping; MASKED: some pair of the step is hidden (uniform choices)
+      auto half = [&](auto cap_tag, auto mask_tag, int sub) {
+        constexpr bool CAP = decltype(cap_tag)::value;
+        constexpr bool MASKED = decltype(mask_tag)::value;
+        const f32x16 s = rows_product(tl.q, kop, sub);
+        // register r holds query qs + c(r), c(r) = 16 (r / 8) + r % 8: the masks and the
+        // ALiBi distance compare per-lane differences with these constants
+        const int qs = q0 + kSub * sub + 8 * h;
+        const int kd = key - qs;
+        f32x4 l4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          l4[i] = *(const f32x4*)(tl.l2 + kSub * sub + 16 * (i >> 1) + 8 * h + 4 * (i & 1));
+        f32x16 p, pd;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          constexpr int kC[16] = {0, 1, 2, 3, 4, 5, 6, 7, 16, 17, 18, 19, 20, 21, 22, 23};
+          const int cr = kC[r];
+          float x, dfac = 1.f;
+          if constexpr (MODS) {
+            float t = s[r] * c;
+            if constexpr (CAP) {
+              const float y = __builtin_amdgcn_exp2f(s[r] * mods.k2);
+              const float th = __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(y + 1.f), 1.f);
+              t = mods.ccap * th;
+              dfac = __builtin_fmaf(-th, th, 1.f);
+            }
+            t = __builtin_fmaf(-slope2, __builtin_fabsf((float)(kd - cr)), t);
+            x = t - l4[r >> 2][r & 3];
+          } else {
+            x = __builtin_fmaf(s[r], c, -l4[r >> 2][r & 3]);
+          }
+          float pr;
+          if constexpr (MASKED) {
+            // non-short-circuit: evaluated whole, so no branch per element
+            const bool vis = BAND ? ((key < N) & (cr >= kq_lo - qs) & (cr <= kq_hi - qs))
+                                  : (key < N && (!CAUSAL || kd <= cr));
+            pr = vis ? __builtin_amdgcn_exp2f(x) : 0.f;
+          } else {
+            pr = __builtin_amdgcn_exp2f(x);
+          }
+          p[r] = pr;
+          pd[r] = CAP ? pr * dfac : pr;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          xchg[pair][4 * sub + i][lane] = f32x4{pd[4 * i], pd[4 * i + 1], pd[4 * i + 2], pd[4 * i + 3]};
+        pb[sub][0] = pack_chunk(p, 0);
+        pb[sub][1] = pack_chunk(p, 1);
+      };
+      auto phase1 = [&](auto cap_tag, auto mask_tag) {
+        half(cap_tag, mask_tag, 0);
+        half(cap_tag, mask_tag, 1);
+      };
+      if (!idle) {
+        // every key of the wave is visible from every query of the step (query rows past
+        // N need no mask: their LSE of +inf gives them weight 0)
+        const bool full = BAND ? (kw0 + 31 < N && q0 >= fq_lo && q0 + kBTile - 1 <= fq_hi)
+                               : (kw0 + 31 < N && (!CAUSAL || kw0 + 31 <= q0));
+        if constexpr (MODS) {
+          if (mods.k2 != 0.f) {
+            if (full) phase1(std::true_type{}, std::false_type{});
+            else phase1(std::true_type{}, std::true_type{});
+          } else {
+            if (full) phase1(std::false_type{}, std::false_type{});
+            else phase1(std::false_type{}, std::true_type{});
+          }
+        } else {
+          if (full) phase1(std::false_type{}, std::false_type{});
+          else phase1(std::false_type{}, std::true_type{});
+        }
       }
+      __syncthreads();
+      // dV^T += dO^T P
+      if (!idle) {
+        cols_product(dv, tl.g, pb[0], 0);
+        cols_product(dv, tl.g, pb[1], 1);
+      }
+      if (st + 1 < nsteps) store(tiles[(st + 1) & 1]);
+      __syncthreads();
+    }
+    write_out(dV, dv, 1.f);
+  } else {
+    // V^T as B operand
+    u32x4 vop[D / 16];
+    {
+      const uint16_t* vrow = V + (khead + min(key, N - 1)) * D;
+#pragma unroll
+      for (int cc = 0; cc < D / 16; ++cc) vop[cc] = *(const u32x4*)(vrow + 16 * cc + 8 * h);
+#pragma unroll
+      for (int cc = 0; cc < D / 16; ++cc) asm volatile("" ::"v"(vop[cc]));
+    }
+    f32x16 dk[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) dk[i] = zero16();
+    for (int st = 0; st < nsteps; ++st) {
+      const Tile& tl = tiles[st & 1];
+      const int q0 = step_q0(st);
+      if (st + 1 < nsteps) fetch(st + 1);
+      const bool idle = idle_at(q0);
+      f32x16 dp0, dp1;
+      if (!idle) {
+        dp0 = rows_product(tl.g, vop, 0);
+        dp1 = rows_product(tl.g, vop, 1);
+      }
+      __syncthreads();
+      if (!idle) {
+        // dS = P (dP - D), then dK^T += Q^T dS, one half at a time
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          const f32x16& dp = sub ? dp1 : dp0;
+          f32x16 ds;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const f32x4 pd = xchg[pair][4 * sub + i][lane];
+            const f32x4 d4 =
+                *(const f32x4*)(tl.dl + kSub * sub + 16 * (i >> 1) + 8 * h + 4 * (i & 1));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ds[4 * i + e] = pd[e] * (dp[4 * i + e] - d4[e]);
+          }
+          const u32x4 db[2] = {pack_chunk(ds, 0), pack_chunk(ds, 1)};
+          cols_product(dk, tl.q, db, sub);
+        }
+      }
+      if (st + 1 < nsteps) store(tiles[(st + 1) & 1]);
+      __syncthreads();
+    }
+    write_out(dK, dk, scale);
   }
 }
 
+// One key tile of the dQ loop in LDS: K and V stored by 16-byte column chunks, as QTile.
+template <int D>
+struct alignas(16) KVTile {
+  static constexpr int kChunk = (kBTile + 4) * 16;   // bytes per column chunk
+  uint8_t k[D / 8 * kChunk];
+  uint8_t v[D / 8 * kChunk];
+};
+
 // dQ for 128 queries of one (batch, query head): each wave owns 32 queries; the loop
 // runs over 64-key tiles (causal: up to the workgroup's last query; BAND: the tiles within
-// the queries' window and documents).
+// the queries' window and documents).  The key tiles are double-buffered: the next tile is
+// fetched into registers at the top of a step and written to the other buffer at its end,
+// one barrier per step.  K^T comes from the stored K rows through transposing reads.
 // (The body; the kernels below set the waves per SIMD.)
 // CAP: the soft-capping path is compiled in (MODS with ALiBi only leaves it out).
 template <int D, bool CAUSAL, bool BAND, bool MODS, bool CAP_ON = MODS>
@@ -434,8 +577,12 @@ __device__ __forceinline__ void dq_body(
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Delta, float* __restrict__ dQ,
     int Hq, int Hkv, int N, int nqb, float c, float scale, Band band, Mods mods) {
-  __shared__ BTile<D> tile;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  using Tile = KVTile<D>;
+  constexpr int kChunk = Tile::kChunk;
+  constexpr int kUnits = kBTile * D * 2 / 16 / kBThreads;    // 16-byte units per thread
+  __shared__ Tile tiles[2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n32 = lane & 31, h = lane >> 5;
   // the query blocks of one kv head's query heads run on one XCD (its K / V tiles stay
   // in that L2); causal: the longest (highest) query blocks first
@@ -466,15 +613,20 @@ __device__ __forceinline__ void dq_body(
       lse2 = (l == -__builtin_inff()) ? __builtin_inff() : l * kLog2e;
       dlt = Delta[qhead + qi];
     }
+    // wait for the operands here: left pending into the loop, they would make every step
+    // wait for its own prefetch of the next tile as well
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc) asm volatile("" ::"v"(qop[cc]), "v"(gop[cc]));
+    asm volatile("" ::"v"(lse2), "v"(dlt));
   }
   f32x16 dq[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) dq[i] = zero16();
 
   // key tiles [kt0, kt1) reach the workgroup's queries; BAND: this lane's query sees keys
-  // [q_lo, q_hi], this wave's queries see [w_lo, w_hi]
+  // [q_lo, q_hi], this wave's queries see [w_lo, w_hi] together and [f_lo, f_hi] each
   int kt0 = 0, kt1 = ((CAUSAL ? min(N, Q0 + kBBlock) : N) + kBTile - 1) / kBTile;
-  int q_lo = 0, q_hi = 0, w_lo = 0, w_hi = 0;
+  int q_lo = 0, q_hi = 0, w_lo = 0, w_hi = 0, f_lo = 0, f_hi = -1;
   if (BAND) {
     int lo, hi, lo2, hi2;
     band.keys<CAUSAL>(Q0, lo, hi);
@@ -482,104 +634,143 @@ __device__ __forceinline__ void dq_body(
     kt0 = lo / kBTile;
     kt1 = hi2 / kBTile + 1;
     band.keys<CAUSAL>(min(qi, N - 1), q_lo, q_hi);
-    band.keys<CAUSAL>(min(qw0, N - 1), w_lo, hi);
-    band.keys<CAUSAL>(min(qw0 + 31, N - 1), lo, w_hi);
+    band.keys<CAUSAL>(min(qw0, N - 1), w_lo, f_hi);
+    band.keys<CAUSAL>(min(qw0 + 31, N - 1), f_lo, w_hi);
     // the same in every lane of the wave: kept in scalar registers
     w_lo = __builtin_amdgcn_readfirstlane(w_lo);
     w_hi = __builtin_amdgcn_readfirstlane(w_hi);
+    f_lo = __builtin_amdgcn_readfirstlane(f_lo);
+    f_hi = __builtin_amdgcn_readfirstlane(f_hi);
   }
-  const int pm = perm_row(n32);
-  // the next key tile is fetched into registers while the current one computes
-  StageRegs<D> sr;
-  if (kt1 > kt0) stage_load(sr, K + khead * D, V + khead * D, kt0 * kBTile, N);
-  for (int kt = kt0; kt < kt1; ++kt) {
+  // lane offsets: S^T / dP^T A operands (rows in the order pi, chunk 2 cc + h) and the
+  // transposed K operand (as in the dK/dV kernel)
+  const int a_off = h * kChunk + perm_row(n32) * 16;
+  const int t_off = (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) * kChunk +
+                    (8 * h + ((lane & 15) >> 2)) * 16 + 8 * (lane & 1);
+  // staging: unit u of a thread is row unit % 64, chunk unit / 64 (rows past N read as row
+  // N - 1: in bounds; their keys are masked)
+  u32x4 sk[kUnits], sv[kUnits];
+  auto fetch = [&](int kt) {
     const int k0 = kt * kBTile;
-    __syncthreads();
-    stage_store(tile, sr, true, false);
-    __syncthreads();
-    if (kt + 1 < kt1) stage_load(sr, K + khead * D, V + khead * D, k0 + kBTile, N);
-    if (!BAND && CAUSAL && k0 > qw0 + 31) continue;
-    if (BAND && (qw0 >= N || k0 > w_hi || k0 + kBTile - 1 < w_lo)) continue;
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+      const int unit = tid + u * kBThreads;
+      const size_t gr = khead + min(k0 + unit % kBTile, N - 1);
+      sk[u] = *(const u32x4*)(K + gr * D + 8 * (unit / kBTile));
+      sv[u] = *(const u32x4*)(V + gr * D + 8 * (unit / kBTile));
+    }
+  };
+  auto store = [&](Tile& t) {
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+      const int unit = tid + u * kBThreads;
+      const int off = (unit / kBTile) * kChunk + (unit % kBTile) * 16;
+      *(u32x4*)(t.k + off) = sk[u];
+      *(u32x4*)(t.v + off) = sv[u];
+    }
+  };
+  // ALiBi slope of this query head, log2 units (0: no bias)
+  const float slope2 = (MODS && mods.alibi != nullptr) ? mods.alibi[hq] * kLog2e : 0.f;
+  if (kt1 > kt0) {
+    fetch(kt0);
+    store(tiles[0]);
+  }
+  __syncthreads();
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const Tile& tl = tiles[(kt - kt0) & 1];
+    const int k0 = kt * kBTile;
+    if (kt + 1 < kt1) fetch(kt + 1);
+    // this wave's queries see none of the tile's keys: nothing to do in this step
+    const bool idle = BAND ? (qw0 >= N || k0 > w_hi || k0 + kBTile - 1 < w_lo)
+                           : (CAUSAL && k0 > qw0 + 31);
     // one 32-key half: S^T and dP^T, then dS^T, then the dQ products
-    constexpr bool kTwoChains = !((BAND || MODS) && D == 128);
-    // ALiBi slope of this query head, log2 units (0: no bias)
-    const float slope2 = (MODS && mods.alibi != nullptr) ? mods.alibi[hq] * kLog2e : 0.f;
     auto half = [&](int sub) {
-      const int ks = k0 + kSub * sub;
-      // S^T = K_pi Q^T and dP^T = V_pi dO^T (keys x queries; rows permuted), two chains
-      // each; one each in the band form at d = 128, whose bounds leave no room for four
-      f32x16 s = zero16(), dp = zero16(), s2 = zero16(), dp2 = zero16();
+      // register r holds key ks + c(r), c(r) = 16 (r / 8) + r % 8, for this lane's query
+      const int ks = k0 + kSub * sub + 8 * h;
+      const int qd = qi - ks;
+      // S^T = K_pi Q^T and dP^T = V_pi dO^T (keys x queries; rows permuted); the two
+      // chains alternate, so neither product waits on its own previous one
+      f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-      for (int cc = 0; cc < D / 16; cc += 2) {
-        const uint8_t* kr = tile.a + (kSub * sub + pm) * BTile<D>::kRow + 32 * cc + 16 * h;
-        const uint8_t* vr = tile.b + (kSub * sub + pm) * BTile<D>::kRow + 32 * cc + 16 * h;
-        s = mfma_bf16(lds_u32x4(kr), qop[cc], s);
-        dp = mfma_bf16(lds_u32x4(vr), gop[cc], dp);
-        if constexpr (kTwoChains) {
-          s2 = mfma_bf16(lds_u32x4(kr + 32), qop[cc + 1], s2);
-          dp2 = mfma_bf16(lds_u32x4(vr + 32), gop[cc + 1], dp2);
-        } else {
-          s = mfma_bf16(lds_u32x4(kr + 32), qop[cc + 1], s);
-          dp = mfma_bf16(lds_u32x4(vr + 32), gop[cc + 1], dp);
-        }
+      for (int cc = 0; cc < D / 16; ++cc) {
+        const int off = 2 * cc * kChunk + kSub * sub * 16 + a_off;
+        s = mfma_bf16(lds_u32x4(tl.k + off), qop[cc], s);
+        dp = mfma_bf16(lds_u32x4(tl.v + off), gop[cc], dp);
       }
-      // dS^T; register r holds key ks + acc_row(r, h) for this lane's query.  CAP:
-      // soft-capping (a uniform choice, made once around the loop)
+      // dS^T.  CAP: soft-capping; MASKED: some (key, query) pair of the half is hidden
+      // (uniform choices)
       f32x16 ds;
-      auto elements = [&](auto cap_tag) {
-      constexpr bool CAP = decltype(cap_tag)::value;
+      auto elements = [&](auto cap_tag, auto mask_tag) {
+        constexpr bool CAP = decltype(cap_tag)::value;
+        constexpr bool MASKED = decltype(mask_tag)::value;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kj = ks + acc_row(r, h);
-        // non-short-circuit: evaluated whole, so no branch per element (causal: kj <= qi
-        // < N implies kj < N)
-        const bool vis = BAND     ? ((qi < N) & (kj >= q_lo) & (kj <= q_hi))
-                         : CAUSAL ? ((qi < N) & (kj <= qi))
-                                  : ((kj < N) & (qi < N));
-        const float sv = kTwoChains ? s[r] + s2[r] : s[r];
-        const float dpv = kTwoChains ? dp[r] + dp2[r] : dp[r];
-        // hidden: 2^-inf = 0 (a select, not a branch around the exponential)
-        if constexpr (MODS) {
-          float t = sv * c, dfac = 1.f;
-          if constexpr (CAP) {
-            const float y = __builtin_amdgcn_exp2f(sv * mods.k2);
-            const float th = __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(y + 1.f), 1.f);
-            t = mods.ccap * th;
-            dfac = __builtin_fmaf(-th, th, 1.f);
+        for (int r = 0; r < 16; ++r) {
+          constexpr int kC[16] = {0, 1, 2, 3, 4, 5, 6, 7, 16, 17, 18, 19, 20, 21, 22, 23};
+          const int cr = kC[r];
+          float x;
+          float dfac = 1.f;
+          if constexpr (MODS) {
+            float t = s[r] * c;
+            if constexpr (CAP) {
+              const float y = __builtin_amdgcn_exp2f(s[r] * mods.k2);
+              const float th = __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(y + 1.f), 1.f);
+              t = mods.ccap * th;
+              dfac = __builtin_fmaf(-th, th, 1.f);
+            }
+            t = __builtin_fmaf(-slope2, __builtin_fabsf((float)(cr - qd)), t);
+            x = t - lse2;
+          } else {
+            x = __builtin_fmaf(s[r], c, -lse2);
           }
-          t = __builtin_fmaf(-slope2, __builtin_fabsf((float)(kj - qi)), t);
-          const float x = vis ? t - lse2 : -__builtin_inff();
-          const float g = __builtin_amdgcn_exp2f(x) * (dpv - dlt);
+          if constexpr (MASKED) {
+            // non-short-circuit: evaluated whole, so no branch per element (causal:
+            // key <= query < N implies key < N); hidden: 2^-inf = 0
+            const bool vis = BAND     ? ((qi < N) & (cr >= q_lo - ks) & (cr <= q_hi - ks))
+                             : CAUSAL ? ((qi < N) & (cr <= qd))
+                                      : ((cr < N - ks) & (qi < N));
+            x = vis ? x : -__builtin_inff();
+          }
+          const float g = __builtin_amdgcn_exp2f(x) * (dp[r] - dlt);
           ds[r] = CAP ? g * dfac : g;
-        } else {
-          const float x = vis ? __builtin_fmaf(sv, c, -lse2) : -__builtin_inff();
-          ds[r] = __builtin_amdgcn_exp2f(x) * (dpv - dlt);
         }
-      }
       };
-      if (CAP_ON && mods.k2 != 0.f) elements(std::true_type{});
-      else elements(std::false_type{});
-      // dQ^T += K^T dS^T (d x queries), over the two 16-key chunks
+      // every key of the half is visible from every query of the wave
+      const int kh = k0 + kSub * sub;
+      const bool full = BAND ? (qw0 + 31 < N && kh >= f_lo && kh + kSub - 1 <= f_hi)
+                             : (qw0 + 31 < N && kh + kSub - 1 < N &&
+                                (!CAUSAL || kh + kSub - 1 <= qw0));
+      if constexpr (MODS) {
+        // (the modified forms take the masked path only: two copies would not fit)
+        if (CAP_ON && mods.k2 != 0.f) elements(std::true_type{}, std::true_type{});
+        else elements(std::false_type{}, std::true_type{});
+      } else {
+        if (full) elements(std::false_type{}, std::false_type{});
+        else elements(std::false_type{}, std::true_type{});
+      }
+      // dQ^T += K^T dS^T (d x queries), over the two 16-key chunks; K^T by transposing reads
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
         const u32x4 db = pack_chunk(ds, k2);
 #pragma unroll
-        for (int dbk = 0; dbk < D / 32; ++dbk) {
-          const int dcol = 32 * dbk + n32;
-          const int off = dcol * kColStride + 2 * kSub * sub + 32 * k2 + 16 * h;
-          dq[dbk] = mfma_bf16(lds_u32x4(tile.at + off), db, dq[dbk]);
-        }
+        for (int dbk = 0; dbk < D / 32; ++dbk)
+          dq[dbk] = mfma_bf16(
+              lds_tr_operand(tl.k + 4 * dbk * kChunk + (kSub * sub + 16 * k2) * 16 + t_off), db,
+              dq[dbk]);
       }
     };
-    // unrolled, one half's exponentials overlap the other's products; the band and
-    // modified forms' extra work would push that past the 256 registers of two waves per SIMD
-    if constexpr (BAND || MODS) {
+    if (!idle) {
+      // the band and modified forms' extra work would not fit two halves at once in the
+      // 256 registers of two waves per SIMD
+      if constexpr (BAND || MODS) {
 #pragma unroll 1
-      for (int sub = 0; sub < kBTile / kSub; ++sub) half(sub);
-    } else {
+        for (int sub = 0; sub < kBTile / kSub; ++sub) half(sub);
+      } else {
 #pragma unroll
-      for (int sub = 0; sub < kBTile / kSub; ++sub) half(sub);
+        for (int sub = 0; sub < kBTile / kSub; ++sub) half(sub);
+      }
     }
+    if (kt + 1 < kt1) store(tiles[(kt + 1 - kt0) & 1]);
+    __syncthreads();
   }
   if (qi < N) {
     float* row = dQ + (qhead + qi) * D;
@@ -632,7 +823,7 @@ hipError_t launch_bwd_t(const BwdArgs& a) {
   const Mods mods{a.alibi, a.softcap > 0.f ? 2.f * a.c / a.softcap : 0.f,
                   a.softcap * kLog2e};
   hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, BAND, MODS>), dim3((unsigned)(a.B * a.Hkv * nb)),
-                     dim3(kBThreads), 0, (hipStream_t)a.stream, (const uint16_t*)a.q,
+                     dim3(kKVThreads), 0, (hipStream_t)a.stream, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse,
                      a.delta, a.dk, a.dv, a.Hq, a.Hkv, a.N, nb, a.c, a.scale, band, mods);
   e = hipGetLastError();
