@@ -36,14 +36,17 @@ __global__ void mfma_bf16_probe(const uint16_t* a, const uint16_t* b, float* c) 
 
 // out: 64 lanes x 4 u16.  LDS holds u16 values 0..1023 (value = element index);
 // lane l reads the 8 bytes at element 4*l with the transposing read.
-__global__ void tr16_probe(uint16_t* out) {
+// Transposing LDS read probe: LDS word i (16 bits) holds i; lane l reads 8 bytes at word
+// addr[l] (a multiple of 4, at most 1020) with ds_read_b64_tr_b16.  out: 64 lanes x 4 words.
+__global__ void tr16_probe(const int* addr, uint16_t* out) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[1024];
   const int l = threadIdx.x;
   for (int i = l; i < 1024; i += 64) lds[i] = (uint16_t)i;
   __syncthreads();
   typedef short i16x4 __attribute__((ext_vector_type(4)));
+  const int a = addr[l] & 1020;   // in bounds whatever the caller passes
   i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4*)(lds + 4 * l));
+      (__attribute__((address_space(3))) i16x4*)(lds + a));
 #pragma unroll
   for (int i = 0; i < 4; ++i) out[4 * l + i] = (uint16_t)t[i];
 }
@@ -343,8 +346,9 @@ int probe_mfma_bf16(const void* a, const void* b, float* c, void* stream) {
   return (int)hipGetLastError();
 }
 
-int probe_tr16(void* out, void* stream) {
-  hipLaunchKernelGGL(tr16_probe, dim3(1), dim3(64), 0, (hipStream_t)stream, (uint16_t*)out);
+int probe_tr16(const void* addr, void* out, void* stream) {
+  hipLaunchKernelGGL(tr16_probe, dim3(1), dim3(64), 0, (hipStream_t)stream, (const int*)addr,
+                     (uint16_t*)out);
   return (int)hipGetLastError();
 }
 

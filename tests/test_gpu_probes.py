@@ -10,6 +10,9 @@ CDNA3/CDNA4 operand layouts:
 * v_permlane32_swap: swaps the upper half of the first operand with the lower
   half of the second.
 * 16-byte direct-to-LDS loads: lane l's 16 bytes land at LDS base + 16*l.
+* ds_read_b64_tr_b16 (the transposing read of the backward kernels): within each
+  group of 16 lanes, lane t returns element t % 4 of the 8-byte words addressed
+  by lanes t // 4, t // 4 + 4, t // 4 + 8, t // 4 + 12 of the group.
 * the packed fp32 -> bf16 convert rounds to nearest even.
 * v_mfma_scale_f32_32x32x64_f8f6f4 with fp4 (E2M1) operands: lane l holds row
   (A) or column (B) l % 32 and the 32 k-elements 32*(l // 32) .. +31, element i
@@ -57,7 +60,7 @@ def lib():
                        "probe_mfma_fp4_sel2": [P, P, P, P, P, P],
                        "probe_cvt_fp4": [P, P, P, P], "probe_dec_fp4": [P, P, P, P],
                        "probe_mfma_fp8": [P, P, P, P, P, P], "probe_cvt_fp8": [P, P, P],
-                       "probe_wave_place": [P, ctypes.c_int, P]}.items():
+                       "probe_wave_place": [P, ctypes.c_int, P], "probe_tr16": [P, P, P]}.items():
         fn = getattr(lib, name)
         fn.restype = I
         fn.argtypes = args
@@ -129,6 +132,39 @@ def test_direct_to_lds_lane_map(lib):
     got = out.cpu().numpy().view(np.uint32).reshape(64, 4)
     want = np.array([[4 * (63 - l) + i for i in range(4)] for l in range(64)], np.uint32)
     assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("pattern", ["contiguous", "rows_of_a_tile"])
+def test_transposing_lds_read_lane_map(lib, pattern):
+    import torch
+    lanes = np.arange(64)
+    if pattern == "contiguous":
+        addr = 4 * lanes
+    else:
+        # as the backward kernels address a tile of 64-word rows: lane a of a 16-lane group
+        # reads row a // 4 (plus 8 per lane half), column quad a % 4 (plus 16 for odd groups)
+        g, t = lanes // 16, lanes % 16
+        addr = (8 * (g // 2) + t // 4) * 64 + 16 * (g % 2) + 4 * (t % 4)
+    assert (addr % 4 == 0).all() and addr.min() >= 0 and addr.max() <= 1020
+    a = _dev(addr.astype(np.int32))
+    out = torch.zeros(256, dtype=torch.int16, device="cuda")
+    log(f"probe tr16 {pattern}")
+    assert lib.probe_tr16(a.data_ptr(), out.data_ptr(), None) == 0
+    _sync()
+    got = out.cpu().numpy().view(np.uint16).reshape(64, 4).astype(np.int64)
+    want = np.zeros((64, 4), np.int64)
+    for l in range(64):
+        g, t = l // 16, l % 16
+        for j in range(4):
+            want[l, j] = addr[16 * g + 4 * j + t // 4] + t % 4
+    assert np.array_equal(got, want)
+    if pattern == "rows_of_a_tile":
+        # lane t of each group gets column 16 (g % 2) + t of four consecutive rows
+        for l in range(64):
+            g, t = l // 16, l % 16
+            rows = got[l] // 64
+            cols = got[l] % 64
+            assert (cols == 16 * (g % 2) + t).all() and (rows == 8 * (g // 2) + np.arange(4)).all()
 
 
 def test_bf16_convert_rounds_to_nearest_even(lib):
