@@ -27,7 +27,10 @@ normalised log-scores are mapped straight onto the eight E2M1 magnitudes
 rounded codes and block scales that the PV product consumes (Normalización
 Consistente).  Emulated here as:
 
-    t_ij  = scale * q~_i . k~_j * log2(e)           (-inf where masked)
+    t_ij  = scale * q~_i . k~_j * log2(e)           (-inf where masked: causal, and
+                                                     the sliding window and packed
+                                                     documents of the FlexAttention
+                                                     patterns, oracle.exact.visible)
     m_i   = ceil(max_j t_ij)                        integer reference max
     per row i and 32-key block b:
       M_ib = max of t_ij over the block
@@ -47,6 +50,8 @@ any tile order and any rescale threshold (pinned by a test).
 import math
 
 import numpy as np
+
+from .exact import visible
 
 BLOCK = 32
 E2M1_EMAX = 2
@@ -109,20 +114,22 @@ def dequantize(codes, scale_bytes, axis):
     return np.moveaxis(val.reshape(codes.shape), -1, axis)
 
 
-def directp_rows(qt_rows, kt, vt, row_ids, causal, scale, ref_max=None):
+def directp_rows(qt_rows, kt, vt, row_ids, causal, scale, ref_max=None, window=0, docs=None):
     """Direct-P output for some query rows of one head, on dequantised operands.
 
     qt_rows [r, d], kt and vt [N, d] (float64, already dequantised).
     ref_max optionally overrides the integer reference max m_i (a test hook
-    showing that the result does not depend on it).  Returns (O, LSE, p~).
+    showing that the result does not depend on it).  window, docs: the exact
+    forward's sliding window and packed documents (oracle.exact.visible); a
+    hidden key's score is -inf before the block maxima, as with the causal
+    mask.  Returns (O, LSE, p~).
     """
     n_keys = kt.shape[0]
     if n_keys % BLOCK:
         raise ValueError("the key count must be a multiple of 32")
     t = (scale * (qt_rows @ kt.T)) * LOG2E
-    if causal:
-        cols = np.arange(n_keys)
-        t = np.where(cols[None, :] > np.asarray(row_ids)[:, None], -np.inf, t)
+    if causal or window or docs is not None:
+        t = np.where(visible(np.asarray(row_ids), n_keys, causal, window, docs), t, -np.inf)
     row_max = t.max(axis=1)
     live_row = np.isfinite(row_max)
     m = np.where(live_row, np.ceil(np.where(live_row, row_max, 0.0)), 0.0)
@@ -151,8 +158,9 @@ def directp_rows(qt_rows, kt, vt, row_ids, causal, scale, ref_max=None):
     return o, lse, p
 
 
-def directp_attention(qt, kt, vt, causal, scale, chunk=256):
-    """Direct-P forward over [B, H, N, d] dequantised operands: returns (O, LSE)."""
+def directp_attention(qt, kt, vt, causal, scale, chunk=256, window=0, docs=None):
+    """Direct-P forward over [B, H, N, d] dequantised operands: returns (O, LSE).  window,
+    docs: as for directp_rows."""
     qt = np.asarray(qt, dtype=np.float64)
     B, Hq, N, d = qt.shape
     group = Hq // kt.shape[1]
@@ -164,7 +172,8 @@ def directp_attention(qt, kt, vt, causal, scale, chunk=256):
             for r0 in range(0, N, chunk):
                 rows = np.arange(r0, min(N, r0 + chunk))
                 o[b, h, rows], lse[b, h, rows], _ = directp_rows(
-                    qt[b, h, rows], kt[b, g], vt[b, g], rows, causal, scale)
+                    qt[b, h, rows], kt[b, g], vt[b, g], rows, causal, scale, window=window,
+                    docs=docs)
     return o, lse
 
 

@@ -213,7 +213,8 @@ def test_planted_directp_mistakes_are_caught(bad, monkeypatch):
     """Planted mistakes in the Direct-P emulation fail the pins above."""
     orig_rows = mx.directp_rows
 
-    def mutated(qt_rows, kt, vt, row_ids, causal, scale, ref_max=None):
+    def mutated(qt_rows, kt, vt, row_ids, causal, scale, ref_max=None, window=0, docs=None):
+        assert window == 0 and docs is None   # the pins below use neither
         if bad == "no_consistent_norm":
             o, lse, p = orig_rows(qt_rows, kt, vt, row_ids, causal, scale, ref_max)
             t = scale * qt_rows @ kt.T * mx.LOG2E
@@ -241,3 +242,77 @@ def test_planted_directp_mistakes_are_caught(bad, monkeypatch):
         except AssertionError:
             failed += 1
     assert failed > 0
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_directp_documents_are_independent_sequences(causal):
+    """Packed documents whose offsets are multiples of 32 (the P blocks then coincide): each
+    document's rows equal the emulation run on that document alone."""
+    t = _mx_case(31, 1, 2, 256, 32)
+    docs = [0, 64, 160, 256]
+    o, lse = mx.directp_attention(t["q"], t["k"], t["v"], causal, 0.2, docs=docs)
+    for a, b in zip(docs[:-1], docs[1:]):
+        oa, la = mx.directp_attention(t["q"][:, :, a:b], t["k"][:, :, a:b], t["v"][:, :, a:b],
+                                      causal, 0.2)
+        assert np.array_equal(o[:, :, a:b], oa) and np.array_equal(lse[:, :, a:b], la)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_directp_window_edges(causal):
+    """A narrow window W = 8: the emulation stays within its quantisation error of the exact
+    windowed attention, and is far from the exact attention with W - 1 or W + 1 (one key more
+    or less per row), so the window's edges are where the definition puts them.  A window of
+    N or more is no window."""
+    t = _mx_case(32, 1, 2, 128, 32)
+    o, _ = mx.directp_attention(t["q"], t["k"], t["v"], causal, 0.2, window=8)
+
+    def rel(x, y):
+        return np.linalg.norm(x - y) / np.linalg.norm(y)
+
+    oe, _ = oracle.attention(t["q"], t["k"], t["v"], causal, 0.2, window=8)
+    assert rel(o, oe) < 0.12
+    for w in (7, 9):
+        ow, _ = oracle.attention(t["q"], t["k"], t["v"], causal, 0.2, window=w)
+        assert rel(o, ow) > 2 * rel(o, oe)
+    o_all, l_all = mx.directp_attention(t["q"], t["k"], t["v"], causal, 0.2, window=128)
+    o_none, l_none = mx.directp_attention(t["q"], t["k"], t["v"], causal, 0.2)
+    assert np.array_equal(o_all, o_none) and np.array_equal(l_all, l_none)
+
+
+def test_directp_window_of_one_returns_v():
+    """Causal with a window of 1: each row sees only its own key, whose block maximum is its
+    score, so x = t - m - E lies in [2, 3), the code is 4 or 6 and O_i = v~_i exactly; the
+    LSE is ln 2 (m_i + E_i) + ln code."""
+    t = _mx_case(33, 1, 2, 96, 32)
+    o, lse = mx.directp_attention(t["q"], t["k"], t["v"], True, 0.3, window=1)
+    assert np.array_equal(o, t["v"])
+    s = 0.3 * np.einsum("bhnd,bhnd->bhn", t["q"], t["k"]) * mx.LOG2E
+    m = np.ceil(s)
+    e = np.floor(s - m) - 2.0
+    code_val = mx.E2M1_MAGNITUDES[mx.e2m1_round(np.exp2(s - m - e))]
+    assert np.all((code_val == 4.0) | (code_val == 6.0))
+    assert np.allclose(lse, math.log(2.0) * (m + e) + np.log(code_val), atol=1e-12)
+
+
+@pytest.mark.parametrize("bad", ["window_one_wider", "documents_ignored"])
+def test_planted_mask_mistakes_are_caught(bad, monkeypatch):
+    """Planted mistakes in the emulation's masks fail the mask pins above."""
+    orig_rows = mx.directp_rows
+
+    def mutated(qt_rows, kt, vt, row_ids, causal, scale, ref_max=None, window=0, docs=None):
+        if bad == "window_one_wider" and window:
+            window += 1
+        if bad == "documents_ignored":
+            docs = None
+        return orig_rows(qt_rows, kt, vt, row_ids, causal, scale, ref_max, window, docs)
+    monkeypatch.setattr(mx, "directp_rows", mutated)
+    pins = [lambda: test_directp_documents_are_independent_sequences(True),
+            lambda: test_directp_window_edges(True), test_directp_window_of_one_returns_v]
+    failed = 0
+    for pin in pins:
+        try:
+            pin()
+        except AssertionError:
+            failed += 1
+    assert failed > 0
+
