@@ -167,11 +167,14 @@ class Mxfp4Workload:
     """MXFP4 Direct-P workload: fp32 draws quantised on the GPU once (untimed), then the
     forward on the resident codes and scales."""
 
-    def __init__(self, w, tau):
+    def __init__(self, w, tau, window=0, doc_offsets=None):
         import numpy as np
         import torch
         import exact_attention_forward_tiled_amd as fa
         self.w = w
+        self.window = window
+        self.docs = (None if doc_offsets is None else
+                     torch.tensor(doc_offsets, dtype=torch.int32, device="cuda"))
         q, k, v = (torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in w.make())
         self.q4, self.qs = fa.quantize_mxfp4_rows(q)
         self.k4, self.ks = fa.quantize_mxfp4_rows(k)
@@ -186,7 +189,7 @@ class Mxfp4Workload:
     def launch(self, stats=None):
         self.fa.fwd_mxfp4(self.q4, self.qs, self.k4, self.ks, self.vt4, self.vts,
                           causal=self.w.causal, scale=self.w.scale, tau=self.tau, stats=stats,
-                          out=(self.o, self.lse))
+                          out=(self.o, self.lse), window=self.window, docs=self.docs)
 
 
 class Mxfp8Workload:
@@ -537,9 +540,9 @@ def main():
                     help="other workloads to time (comma list, '' for none), e.g. 2,3,5")
     ap.add_argument("--docs", type=int, default=0,
                     help="also time the workload split into this many equal packed documents "
-                         "(bf16, mxfp8; TFLOP/s count 4*d flop per visible pair)")
+                         "(every format; TFLOP/s count 4*d flop per visible pair)")
     ap.add_argument("--window", type=int, default=0,
-                    help="also time the workload with this sliding window (bf16, mxfp8); its "
+                    help="also time the workload with this sliding window (every format); its "
                          "TFLOP/s count 4*d flop per visible (query, key) pair")
     ap.add_argument("--softcap", type=float, default=0.0,
                     help="also time the workload with soft-capping C (bf16 only)")
@@ -665,10 +668,11 @@ def main():
                 100.0 * tx["tflops"] / PEAKS[wx.fmt], 2)
             extra["workloads"][wx.name]["accuracy"] = ax
 
-    if args.window and w.fmt in ("bf16", "mxfp8"):
+    masked_mx = {"mxfp4": Mxfp4Workload, "mxfp8": Mxfp8Workload}
+    if args.window:
         log(f"timing {w.name} with window {args.window}")
         wl = (Workload(w, args.exp, args.tau, args.poly_frac, window=args.window)
-              if w.fmt == "bf16" else Mxfp8Workload(w, args.tau, window=args.window))
+              if w.fmt == "bf16" else masked_mx[w.fmt](w, args.tau, window=args.window))
         tw = time_workload(wl, args.steps, args.warmup, args.warmup_seconds)
         del wl
         torch.cuda.empty_cache()
@@ -680,11 +684,11 @@ def main():
             "visible_pairs_per_head": pairs,
             "time_vs_no_window": round(tw["kernel_ms_avg"] / t["kernel_ms_avg"], 4)}
 
-    if args.docs and w.fmt in ("bf16", "mxfp8"):
+    if args.docs:
         off = [round(x * w.N / args.docs) for x in range(args.docs + 1)]
         log(f"timing {w.name} as {args.docs} documents")
         wl = (Workload(w, args.exp, args.tau, args.poly_frac, doc_offsets=off)
-              if w.fmt == "bf16" else Mxfp8Workload(w, args.tau, doc_offsets=off))
+              if w.fmt == "bf16" else masked_mx[w.fmt](w, args.tau, doc_offsets=off))
         td = time_workload(wl, args.steps, args.warmup, args.warmup_seconds)
         del wl
         torch.cuda.empty_cache()

@@ -291,8 +291,10 @@ def quantize_mxfp4_cols_t(x):
     return codes, scales
 
 
-def fwd_mxfp4(q4, qs, k4, ks, vt4, vts, causal=False, scale=None, tau=8.0, stats=None, out=None):
-    """MXFP4 Direct-P forward: returns (O fp32 [B,Hq,N,d], LSE fp32 [B,Hq,N])."""
+def fwd_mxfp4(q4, qs, k4, ks, vt4, vts, causal=False, scale=None, tau=8.0, stats=None, out=None,
+              window=0, docs=None):
+    """MXFP4 Direct-P forward: returns (O fp32 [B,Hq,N,d], LSE fp32 [B,Hq,N]).  window, docs:
+    sliding window and document offsets (int32 CUDA tensor), as for fwd."""
     torch = _torch()
     if q4.dim() != 4 or k4.dim() != 4:
         raise ValueError("MXFP4 codes must be [B, H, N, d/2] tensors")
@@ -310,7 +312,14 @@ def fwd_mxfp4(q4, qs, k4, ks, vt4, vts, causal=False, scale=None, tau=8.0, stats
         scale = 1.0 / math.sqrt(d)
     o, lse = _outputs(torch, out, ((B, Hq, N, d), (B, Hq, N)), ("o", "lse"), dev)
     _on_gpu(q4)
-    opts = make_opts(tau, "hw", _stats_ptr(torch, stats))
+    doc_ptr, n_docs = None, 0
+    if docs is not None:
+        if docs.dtype != torch.int32 or not docs.is_cuda or not docs.is_contiguous() \
+                or docs.numel() < 2:
+            raise ValueError("docs must be a contiguous int32 CUDA tensor of document offsets")
+        doc_ptr, n_docs = docs.data_ptr(), docs.numel() - 1
+    opts = make_opts(tau, "hw", _stats_ptr(torch, stats), window=window, doc_ptr=doc_ptr,
+                     n_docs=n_docs)
     check(attn_fwd_mxfp4_ex(q4.data_ptr(), qs.data_ptr(), k4.data_ptr(), ks.data_ptr(),
                             vt4.data_ptr(), vts.data_ptr(), o.data_ptr(), lse.data_ptr(),
                             B, Hq, Hkv, N, d, int(bool(causal)), float(scale), opts,

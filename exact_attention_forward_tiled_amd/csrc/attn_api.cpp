@@ -51,7 +51,7 @@ int check_common(int B, int Hq, int Hkv, int N, int d, int causal, float scale) 
 }
 
 // Shared validation and launch of the block-scaled forwards (MXFP4 and MXFP8).
-// band_ok: the forward takes a sliding window and document offsets (MXFP8).
+// band_ok: the forward takes a sliding window and document offsets (both forwards do).
 int mx_fwd(hipError_t (*launch)(const attn::MxArgs&), uint32_t qsign, bool band_ok,
            const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
            const uint8_t* vtc, const uint8_t* vts, float* o, float* lse, int B, int Hq, int Hkv,
@@ -239,7 +239,7 @@ int attn_fwd_mxfp4_ex(const uint8_t* q4, const uint8_t* qs, const uint8_t* k4, c
                       const uint8_t* vt4, const uint8_t* vts, float* o, float* lse, int B, int Hq,
                       int Hkv, int N, int d, int causal, float scale, const attn_opts* opts,
                       void* stream) {
-  return mx_fwd(attn::launch_fwd_mxfp4, 0x88888888u, false, q4, qs, k4, ks, vt4, vts, o, lse, B, Hq, Hkv,
+  return mx_fwd(attn::launch_fwd_mxfp4, 0x88888888u, true, q4, qs, k4, ks, vt4, vts, o, lse, B, Hq, Hkv,
                 N, d, causal, scale, opts, stream);
 }
 

@@ -179,14 +179,17 @@ struct MStage {
 // Direct-P mapping of one 64-key tile for this lane (32 keys: its P scale block).
 // Returns whether any row of the wave moved its reference max (then O and the
 // row sum must be multiplied by alpha before the next PV product).
-template <bool CAUSAL, bool MASK>
+// BAND: the lane sees keys [klo, khi] only (a sliding window and / or its document;
+// khi < N), which replaces the causal and ragged-tail tests.
+template <bool CAUSAL, bool MASK, bool BAND>
 __device__ __forceinline__ bool directp_tile(const f32x16 (&s)[2], u32x4& codes, uint32_t& sbyte,
                                              float& m, float& alpha, int kv0, int qi, int N,
-                                             float c, float tau, int h) {
+                                             float c, float tau, int h, int klo, int khi) {
   const float NEG_INF = -__builtin_inff();
   auto visible = [&](int mb, int r) {
     const int key = kv0 + 32 * h + 16 * mb + r;
-    return key < N && (!CAUSAL || key <= qi);
+    // non-short-circuit in the band form: evaluated whole, no branch per element
+    return BAND ? (key >= klo) & (key <= khi) : key < N && (!CAUSAL || key <= qi);
   };
   // block max over this lane's 32 scores: four independent chains
   float bq[4] = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
@@ -246,13 +249,14 @@ __device__ __forceinline__ bool directp_tile(const f32x16 (&s)[2], u32x4& codes,
   return any;
 }
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool BAND>
 __global__ __attribute__((amdgpu_flat_work_group_size(kMThreads, kMThreads), amdgpu_waves_per_eu(2, 2)))
 void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict__ QS,
                       const uint8_t* __restrict__ K4, const uint8_t* __restrict__ KS,
                       const uint8_t* __restrict__ VT4, const uint8_t* __restrict__ VTS,
                       float* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int N,
-                      int nqb, float c, float tau, uint32_t qsign,
+                      int nqb, float c, float tau, uint32_t qsign, int window,
+                      const int* __restrict__ doc_off, int n_docs,
                       unsigned long long* __restrict__ stats) {
   __shared__ MBuf buf[2];
   const float NEG_INF = -__builtin_inff();
@@ -304,9 +308,38 @@ void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict_
   lacc = zero16();
   float m = NEG_INF;
 
-  const int kv_end = CAUSAL ? min(N, Q0 + kMBr) : N;
-  const int n = (kv_end + kMBc - 1) / kMBc;
-  const int wave_end = CAUSAL ? min(N, q0 + kMRows) : N;
+  // BAND (the bf16 forward's rules): row i sees keys [lo(i), hi(i)], from a window W
+  // (i - W < j, and j < i + W without the causal mask) and / or its document; both
+  // bounds are non-decreasing in i, so a block's first and last rows bound its keys.
+  // The document search reads only doc_off[0 .. n_docs] and keeps lo <= i <= hi.
+  auto row_bounds = [&](int i, int& lo, int& hi) {
+    lo = window ? max(0, i - window + 1) : 0;
+    hi = CAUSAL ? i : (window ? min(N - 1, i + window - 1) : N - 1);
+    if (n_docs > 0) {
+      int a = 0, z = n_docs;
+      while (z - a > 1) {
+        const int mid = (a + z) >> 1;
+        if (doc_off[mid] <= i) a = mid;
+        else z = mid;
+      }
+      lo = max(lo, min(doc_off[a], i));
+      hi = min(hi, max(doc_off[a + 1] - 1, i));
+    }
+  };
+  int klo = 0, khi = 0, wg_lo_first = 0, wg_hi_first = 0, wg_lo_last = 0, wg_hi_last = 0;
+  int w_lo = 0, w_hi = 0, unused = 0;
+  if (BAND) {
+    row_bounds(min(qi, N - 1), klo, khi);
+    row_bounds(Q0, wg_lo_first, wg_hi_first);
+    row_bounds(min(Q0 + kMBr - 1, N - 1), wg_lo_last, wg_hi_last);
+    row_bounds(min(q0, N - 1), w_lo, unused);
+    row_bounds(min(q0 + kMRows - 1, N - 1), unused, w_hi);
+  }
+  // tiles t0 .. t0 + n - 1 (local index j = tile - t0)
+  const int t0 = BAND ? wg_lo_first / kMBc : 0;
+  const int kv_end = BAND ? wg_hi_last + 1 : (CAUSAL ? min(N, Q0 + kMBr) : N);
+  const int n = (kv_end + kMBc - 1) / kMBc - t0;
+  const int wave_end = BAND ? w_hi + 1 : (CAUSAL ? min(N, q0 + kMRows) : N);
   const bool wave_live = q0 < N;
 
   // Stage t (read by pipeline step t from buffer t & 1) holds K tile t+1 and V tile t-1.
@@ -321,7 +354,7 @@ void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict_
                               : 256 + scol * 2 + (shh ^ ((scol >> 3) & 1));
   auto load_stage = [&](MStage& sg, int t) {
     const int kt = min(t + 1, n - 1), vt = max(min(t - 1, n - 1), 0);
-    const int kk0 = kt * kMBc, vk0 = vt * kMBc;
+    const int kk0 = (t0 + kt) * kMBc, vk0 = (t0 + vt) * kMBc;
     const __amdgpu_buffer_rsrc_t rk = mrsrc(K4h + (size_t)kk0 * kCodeRow, (N - kk0) * kCodeRow);
     sg.codes = __builtin_amdgcn_raw_buffer_load_b128(
         kpart ? rk : rvt,
@@ -404,7 +437,9 @@ void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict_
 
   bool any_prev = false;
   float alpha_prev = 1.f;
-  const int n_full = CAUSAL ? min(Q0, N) / kMBc : N / kMBc;
+  // unmasked tiles [lo_full, n_full): every row of the workgroup sees all their keys
+  const int n_full = BAND ? (wg_hi_first + 1) / kMBc - t0 : (CAUSAL ? min(Q0, N) / kMBc : N / kMBc);
+  const int lo_full = BAND ? min(n, (wg_lo_last + kMBc - 1) / kMBc - t0) : 0;
   // rescale decisions that fired; every step's decision passes through rescale() once
   unsigned n_fires = 0;
   auto rescale = [&]() {
@@ -424,9 +459,11 @@ void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict_
     float alpha;
     bool any;
     if (masked)
-      any = directp_tile<CAUSAL, true>(sc, pc, ec, m, alpha, j * kMBc, qi, N, c, tau, h);
+      any = directp_tile<CAUSAL, true, BAND>(sc, pc, ec, m, alpha, (t0 + j) * kMBc, qi, N, c,
+                                             tau, h, klo, khi);
     else
-      any = directp_tile<CAUSAL, false>(sc, pc, ec, m, alpha, j * kMBc, qi, N, c, tau, h);
+      any = directp_tile<CAUSAL, false, BAND>(sc, pc, ec, m, alpha, (t0 + j) * kMBc, qi, N, c,
+                                              tau, h, klo, khi);
     any_prev = any;
     alpha_prev = alpha;
     store_stage(stg, j + 1);
@@ -440,10 +477,17 @@ void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict_
     e_prev = e_cur;
   };
 
+  // masked tiles: below lo_full (some row's lower edge, BAND) and from n_full on
+  auto masked_at = [&](int jj) { return jj < lo_full || jj >= n_full; };
   // step 0 has no PV product (no tile before it)
-  step(0, false, n > 1, 0 >= n_full, s_cur, s_nxt, p_prev, e_prev, p_cur, e_cur);
+  step(0, false, n > 1, masked_at(0), s_cur, s_nxt, p_prev, e_prev, p_cur, e_cur);
   advance();
   int j = 1;
+  // masked steps below the band's lower edge
+  for (; j < min(lo_full, n - 1); ++j) {
+    step(j, true, true, true, s_cur, s_nxt, p_prev, e_prev, p_cur, e_cur);
+    advance();
+  }
   // unmasked steps with both products, two at a time with the S / P registers swapping
   // roles (no copies)
   for (; j + 1 < min(n_full, n - 1); j += 2) {
@@ -451,12 +495,12 @@ void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict_
     step(j + 1, true, true, false, s_nxt, s_cur, p_cur, e_cur, p_prev, e_prev);
   }
   for (; j < n - 1; ++j) {
-    step(j, true, true, j >= n_full, s_cur, s_nxt, p_prev, e_prev, p_cur, e_cur);
+    step(j, true, true, masked_at(j), s_cur, s_nxt, p_prev, e_prev, p_cur, e_cur);
     advance();
   }
   // the last step has no QK product (no tile after it)
   if (n > 1) {
-    step(n - 1, true, false, n - 1 >= n_full, s_cur, s_nxt, p_prev, e_prev, p_cur, e_cur);
+    step(n - 1, true, false, masked_at(n - 1), s_cur, s_nxt, p_prev, e_prev, p_cur, e_cur);
     advance();
   }
   rescale();
@@ -478,13 +522,14 @@ void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict_
     if (h == 0)
       LSE[qhead + qi] = l > 0.f ? (m + __builtin_log2f(l)) * kLn2 : -__builtin_inff();
   }
-  // Statistics without per-step bookkeeping: the wave's visible tiles are
-  // [0, ceil(wave_end / 64)); the first always fires (the reference max starts at -inf) and
-  // the rest are the counted steps; tiles past them hold no visible key and never fire.
+  // Statistics without per-step bookkeeping: the wave's visible tiles are the local
+  // indices [j_lo, j_hi); the first always fires (the reference max starts at -inf) and
+  // the rest are the counted steps; the other tiles hold no visible key and never fire.
   if (stats != nullptr && lane == 0 && wave_live) {
-    const int n_act = min(n, (wave_end + kMBc - 1) / kMBc);
-    if (n_act > 0) {
-      atomicAdd(stats, (unsigned long long)(n_act - 1));
+    const int j_hi = min(n, (wave_end + kMBc - 1) / kMBc - t0);
+    const int j_lo = BAND ? max(0, w_lo / kMBc - t0) : 0;
+    if (j_hi > j_lo) {
+      atomicAdd(stats, (unsigned long long)(j_hi - j_lo - 1));
       atomicAdd(stats + 1, (unsigned long long)(n_fires - 1u));
     }
   }
@@ -494,14 +539,15 @@ void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict_
   }
 }
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool BAND>
 hipError_t launch_mxfp4(const MxArgs& a) {
   const int nqb = (a.N + kMBr - 1) / kMBr;
   const long long grid = (long long)a.B * a.Hq * nqb;
   if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_mxfp4_kernel<CAUSAL>), dim3((unsigned)grid), dim3(kMThreads), 0,
+  hipLaunchKernelGGL((fwd_mxfp4_kernel<CAUSAL, BAND>), dim3((unsigned)grid), dim3(kMThreads), 0,
                      (hipStream_t)a.stream, a.qc, a.qs, a.kc, a.ks, a.vtc, a.vts, a.o, a.lse,
-                     a.Hq, a.Hkv, a.N, nqb, a.c, a.tau, a.qsign, a.stats);
+                     a.Hq, a.Hkv, a.N, nqb, a.c, a.tau, a.qsign, a.window, a.doc_offsets,
+                     a.n_docs, a.stats);
   return hipGetLastError();
 }
 
@@ -531,7 +577,9 @@ hipError_t launch_quantize_cols_t(const float* x, uint8_t* codes, uint8_t* scale
 
 hipError_t launch_fwd_mxfp4(const MxArgs& a) {
   if (a.d != kMD) return hipErrorNotSupported;
-  return a.causal ? launch_mxfp4<true>(a) : launch_mxfp4<false>(a);
+  const bool band = a.window > 0 || a.n_docs > 0;
+  if (a.causal) return band ? launch_mxfp4<true, true>(a) : launch_mxfp4<true, false>(a);
+  return band ? launch_mxfp4<false, true>(a) : launch_mxfp4<false, false>(a);
 }
 
 }  // namespace attn

@@ -39,8 +39,8 @@ struct MxArgs {
   float tau;
   uint32_t qsign;   // flips the sign bit of every Q element (scale < 0): 0x88888888 for E2M1
                     // nibbles, 0x80808080 for E4M3 bytes
-  int window;       // MXFP8 only: sliding window W (0: none; 1 <= W < N)
-  const int* doc_offsets;   // MXFP8 only: device, n_docs + 1 document offsets, or null
+  int window;       // sliding window W (0: none; 1 <= W < N)
+  const int* doc_offsets;   // device, n_docs + 1 document offsets, or null
   int n_docs;       // documents (0: no document masking)
   unsigned long long* stats;
   void* stream;

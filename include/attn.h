@@ -83,8 +83,7 @@ typedef struct attn_opts {
                                 prints no definition).  W = 0: no window.  W >= 1: key j is
                                 visible from query i only when i - W < j, and, without the
                                 causal mask, also j < i + W.  Tiles wholly outside the band are
-                                skipped.  bf16 and MXFP8 forwards and the backward: the
-                                MXFP4 forward returns ATTN_EUNSUPPORTED for W != 0. */
+                                skipped.  All three forwards and the backward. */
     const float* alibi_slopes; /* nullable DEVICE pointer to Hq floats, one ALiBi slope a_h per
                                 query head (the same page names ALiBi; no definition printed):
                                 the scaled score of query i and key j gets -a_h |i - j| added
@@ -102,8 +101,7 @@ typedef struct attn_opts {
                                 of the causal mask and the window).  Tiles outside a workgroup's
                                 documents are skipped.  Offsets that break the order give
                                 unspecified values but every read stays within the array.
-                                bf16 and MXFP8 forwards and the backward (MXFP4:
-                                ATTN_EUNSUPPORTED). */
+                                All three forwards and the backward. */
     int n_docs;              /* number of documents (>= 1 when doc_offsets is set; else ignored) */
 } attn_opts;
 

@@ -59,7 +59,11 @@ int main(void) {
   EXPECT(attn_fwd_mxfp4(u, u, u, u, u, NULL, f, f, 1, 1, 1, 64, 128, 0, 0.1f), ATTN_EINVAL);
   EXPECT(attn_fwd_mxfp4(u, u, u, u, u, u, f, f, 1, 1, 1, 48, 128, 0, 0.1f), ATTN_EUNSUPPORTED);
   bad = o;
-  bad.window = 8;
+  bad.window = -8;
+  EXPECT(attn_fwd_mxfp4_ex(u, u, u, u, u, u, f, f, 1, 1, 1, 64, 128, 0, 0.1f, &bad, NULL),
+         ATTN_EINVAL);
+  bad = o;
+  bad.softcap = 2.0f;
   EXPECT(attn_fwd_mxfp4_ex(u, u, u, u, u, u, f, f, 1, 1, 1, 64, 128, 0, 0.1f, &bad, NULL),
          ATTN_EUNSUPPORTED);
   EXPECT(attn_fwd_mxfp8(u, u, u, u, u, u, f, f, 1, 1, 1, 64, 64, 0, 0.1f), ATTN_EUNSUPPORTED);

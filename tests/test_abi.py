@@ -71,12 +71,10 @@ def test_opts_validation(fa):
         opts = fa.make_opts(tau, mode, poly_frac=frac)
         st = fa.attn_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 16, 64, 0, 0.1, opts, None)
         assert st == -1
-    # a negative window is invalid for both forwards; any window is unsupported on MXFP4
+    # a negative window is invalid for both forwards
     opts = fa.make_opts(8.0, "hw", window=-1)
     assert fa.attn_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 16, 64, 0, 0.1, opts, None) == -1
     assert fa.attn_fwd_mxfp4_ex(*[FAKE] * 8, 1, 1, 1, 64, 128, 0, 0.1, opts, None) == -1
-    opts = fa.make_opts(8.0, "hw", window=16)
-    assert fa.attn_fwd_mxfp4_ex(*[FAKE] * 8, 1, 1, 1, 64, 128, 0, 0.1, opts, None) == -2
     # soft-capping: C must be finite and >= 0; score modifications need the hardware exp
     # and the bf16 forward
     for cap in (-1.0, float("nan"), float("inf")):
@@ -89,13 +87,14 @@ def test_opts_validation(fa):
                               None) == -2
         opts = fa.make_opts(8.0, "hw", **kw)
         assert fa.attn_fwd_mxfp4_ex(*[FAKE] * 8, 1, 1, 1, 64, 128, 0, 0.1, opts, None) == -2
-    # documents: at least one, at most N (documents are non-empty); bf16 forward only
+    # documents: at least one, at most N (documents are non-empty), for every forward
     for nd in (0, -1, 17):
         opts = fa.make_opts(8.0, "hw", doc_ptr=FAKE, n_docs=nd)
         assert fa.attn_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 16, 64, 0, 0.1, opts,
                               None) == -1
-    opts = fa.make_opts(8.0, "hw", doc_ptr=FAKE, n_docs=2)
-    assert fa.attn_fwd_mxfp4_ex(*[FAKE] * 8, 1, 1, 1, 64, 128, 0, 0.1, opts, None) == -2
+    for nd in (0, -1, 65):
+        opts = fa.make_opts(8.0, "hw", doc_ptr=FAKE, n_docs=nd)
+        assert fa.attn_fwd_mxfp4_ex(*[FAKE] * 8, 1, 1, 1, 64, 128, 0, 0.1, opts, None) == -1
 
 
 def test_tau_bound(fa):
@@ -165,7 +164,12 @@ def test_mxfp8_validation(fa):
                                 None) == -2
     assert fa.attn_fwd_mxfp8_ex(*base, 1, 2, 2, 64, 128, 0, 0.1, fa.make_opts(softcap=2.0),
                                 None) == -2
-    assert fa.attn_fwd_mxfp4_ex(*base, 1, 2, 2, 64, 128, 0, 0.1, fa.make_opts(window=16),
+    # the MXFP4 forward takes the masks too, validated the same way before any launch
+    assert fa.attn_fwd_mxfp4_ex(*base, 1, 2, 2, 64, 128, 0, 0.1, fa.make_opts(window=-1),
+                                None) == -1
+    assert fa.attn_fwd_mxfp4_ex(*base, 1, 2, 2, 64, 128, 0, 0.1,
+                                fa.make_opts(doc_ptr=FAKE, n_docs=65), None) == -1
+    assert fa.attn_fwd_mxfp4_ex(*base, 1, 2, 2, 64, 128, 0, 0.1, fa.make_opts(alibi_ptr=FAKE),
                                 None) == -2
     assert fa.attn_quantize_mxfp8_rows(FAKE, FAKE, FAKE, 4, 48) == -1
     assert fa.attn_quantize_mxfp8_cols_t(FAKE, FAKE, FAKE, 1, 40, 8) == -1

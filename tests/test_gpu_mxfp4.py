@@ -10,6 +10,8 @@
   measured error is printed.
 * Exact invariants: V = 1 gives O = 1 (the normaliser is summed from the same
   codes and scales as PV); Q = 0 gives the mean of the dequantised V rows.
+* Sliding window and packed documents against the emulation under the same
+  masks, and the step counter against the visible tiles of every wave.
 """
 
 import math
@@ -237,3 +239,91 @@ def test_directp_skip_ratio_stats():
             log(f"  steps {steps} rescales {resc}; model {m_steps} {m_fires}")
             assert steps == m_steps
             assert abs(resc - m_fires) <= max(3, 0.002 * steps)
+
+
+MASKED = [
+    # B, Hq, Hkv, N, causal, window, docs
+    (1, 2, 2, 512, True, 100, None),
+    (1, 2, 2, 320, False, 64, None),
+    (1, 4, 2, 256, True, 0, [0, 100, 101, 256]),
+    (1, 2, 2, 384, False, 0, [0, 64, 200, 384]),
+    (1, 2, 2, 512, True, 130, [0, 300, 512]),
+    (1, 2, 2, 128, True, 1, None),       # a window of 1: every row sees only itself
+    (1, 2, 2, 256, False, 256, None),    # a window N wide hides nothing
+]
+
+
+def _masked_check(q, k, v, causal, scale, window, docs, rows=None):
+    import torch
+    dd = None if docs is None else torch.tensor(docs, dtype=torch.int32, device="cuda")
+    o, lse = _run(q, k, v, causal, scale, window=window, docs=dd)
+    t = mx.quantize_inputs(q, k, v)
+    assert not np.isnan(o).any() and not np.isnan(lse).any()
+    if rows is None:
+        ro, rl = mx.directp_attention(t["q"], t["k"], t["v"], causal, scale, window=window,
+                                      docs=docs)
+    else:   # sampled rows of every head
+        B, Hq = q.shape[:2]
+        group = Hq // k.shape[1]
+        ro = np.empty((B, Hq, len(rows), q.shape[3]))
+        rl = np.empty((B, Hq, len(rows)))
+        for b in range(B):
+            for h in range(Hq):
+                ro[b, h], rl[b, h], _ = mx.directp_rows(t["q"][b, h, rows], t["k"][b, h // group],
+                                                        t["v"][b, h // group], rows, causal, scale,
+                                                        window=window, docs=docs)
+        o, lse = o[:, :, rows], lse[:, :, rows]
+    gate(o, ro, MXFP4_O_RELRMS, MXFP4_O_ROW, "masked O")
+    e = float(np.max(np.abs(lse - rl)))
+    log(f"  max|dLSE|={e:.3e}")
+    assert e <= 0.05, e
+
+
+@pytest.mark.parametrize("case", MASKED, ids=lambda c: "Hq%dHkv%dN%d%sW%d%s" % (
+    c[1], c[2], c[3], "c" if c[4] else "n", c[5], "docs" if c[6] else ""))
+def test_directp_masked(case):
+    """Sliding window and packed documents on the MXFP4 Direct-P forward (tiles outside a
+    block's band skipped) against the emulation under the same masks."""
+    B, Hq, Hkv, N, causal, window, docs = case
+    q, k, v = _case(N + window + 5 * Hq, B, Hq, Hkv, N)
+    log(f"mxfp4 masked case {case}")
+    _masked_check(q, k, v, causal, 1.0 / math.sqrt(128), window, docs)
+
+
+def test_directp_masked_long_sampled_rows():
+    """Causal GQA N 4096 with a 1024 window over two documents: sampled rows (both document
+    edges, the window's reach, the last rows) of every head."""
+    q, k, v = _case(62, 1, 4, 2, 4096)
+    rows = np.array([0, 1, 31, 1023, 1024, 1500, 2047, 2048, 2049, 3071, 3072, 4094, 4095])
+    log("mxfp4 masked N4096 W1024 docs")
+    _masked_check(q, k, v, True, 1.0 / math.sqrt(128), 1024, [0, 2048, 4096], rows=rows)
+
+
+def _visible_tile_steps(N, causal, window=0, docs=None):
+    """Steps the counters report: per 32-row wave, the 64-key tiles holding a key visible to
+    one of its rows, minus the wave's first (from the oracle's visibility definition)."""
+    vis = oracle.exact.visible(np.arange(N), N, causal, window, docs)
+    steps = 0
+    for r0 in range(0, N, 32):
+        w = vis[r0:r0 + 32]
+        tiles = [bool(w[:, t0:t0 + 64].any()) for t0 in range(0, N, 64)]
+        steps += max(0, sum(tiles) - 1)
+    return steps
+
+
+@pytest.mark.parametrize("causal,window,docs", [(True, 300, None), (False, 200, [0, 700, 1024])])
+def test_directp_masked_step_counter(causal, window, docs):
+    """With a band the kernel's step counter (closed form) equals the visible tiles of every
+    wave."""
+    import torch
+    N, H = 1024, 2
+    q, k, v = _case(28, 1, H, H, N, sigma=3.0)
+    dd = None if docs is None else torch.tensor(docs, dtype=torch.int32, device="cuda")
+    stats = torch.zeros(4, dtype=torch.int64, device="cuda")
+    log(f"mxfp4 stats causal={causal} window={window} docs={docs}")
+    _run(q, k, v, causal, 1.0 / math.sqrt(128), stats=stats, window=window, docs=dd)
+    steps = int(stats.cpu()[0])
+    want = H * _visible_tile_steps(N, causal, window, docs)
+    log(f"  steps {steps} (visible tiles {want})")
+    assert steps == want
+
