@@ -244,6 +244,7 @@ __device__ __forceinline__ u32x4 lds_tr_operand(const uint8_t* p) {
 }
 
 constexpr int kKVThreads = 2 * kBThreads;    // dK/dV workgroup: two waves per 32 keys
+constexpr int kRing = 4;                     // dK/dV: LDS operand reads in flight per product
 
 // dK, dV for 128 keys of one (batch, kv head).  The loop runs over the group's query
 // heads and their 64-query tiles (causal: only tiles that reach the workgroup's keys;
@@ -369,16 +370,50 @@ __global__ __launch_bounds__(kKVThreads) void dkdv_kernel(
       acc = mfma_bf16(lds_u32x4(x + 2 * cc * kChunk + kSub * sub * 16 + a_off), y[cc], acc);
     return acc;
   };
-  // acc[dbk] += X^T B over one 32-query half: X^T from the tile by transposing reads
-  auto cols_product = [&](f32x16 (&acc)[D / 32], const uint8_t* x, const u32x4 (&bop)[2],
-                          int sub) {
+  // Both 32-query halves of a product, as one sequence of MFMAs whose LDS operands are read
+  // kRing products ahead (one read and one product per scheduling slot); left to itself the
+  // compiler reads each operand just before its product and waits for it.
+  // a0 / a1 = X_pi Y^T over d for the two halves, the halves' products interleaved:
+  auto rows_product_pair = [&](const uint8_t* x, const u32x4 (&y)[D / 16], f32x16& a0,
+                               f32x16& a1) {
+    constexpr int NK = 2 * (D / 16);
+    auto rd = [&](int k) {
+      return lds_u32x4(x + 2 * (k >> 1) * kChunk + kSub * (k & 1) * 16 + a_off);
+    };
+    u32x4 ring[kRing];
 #pragma unroll
-    for (int q2 = 0; q2 < 2; ++q2)
+    for (int i = 0; i < kRing; ++i) ring[i] = rd(i);
+    a0 = zero16();
+    a1 = zero16();
 #pragma unroll
-      for (int dbk = 0; dbk < D / 32; ++dbk)
-        acc[dbk] = mfma_bf16(
-            lds_tr_operand(x + 4 * dbk * kChunk + (kSub * sub + 16 * q2) * 16 + t_off), bop[q2],
-            acc[dbk]);
+    for (int k = 0; k < NK; ++k) {
+      const u32x4 op = ring[k % kRing];
+      if (k + kRing < NK) ring[k % kRing] = rd(k + kRing);
+      if (k & 1) a1 = mfma_bf16(op, y[k >> 1], a1);
+      else a0 = mfma_bf16(op, y[k >> 1], a0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // acc[dbk] += X^T B over both halves (B = b0 for queries 0-31, b1 for 32-63), X^T from the
+  // tile by transposing reads, each accumulator's products in query order:
+  auto cols_product_pair = [&](f32x16 (&acc)[D / 32], const uint8_t* x, const u32x4 (&b0)[2],
+                               const u32x4 (&b1)[2]) {
+    constexpr int NK = 4 * (D / 32);
+    auto rd = [&](int k) {
+      const int sub = k / (2 * (D / 32)), q2 = (k / (D / 32)) & 1, dbk = k % (D / 32);
+      return lds_tr_operand(x + 4 * dbk * kChunk + (kSub * sub + 16 * q2) * 16 + t_off);
+    };
+    u32x4 ring[kRing];
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) ring[i] = rd(i);
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      const int sub = k / (2 * (D / 32)), q2 = (k / (D / 32)) & 1, dbk = k % (D / 32);
+      const u32x4 op = ring[k % kRing];
+      if (k + kRing < NK) ring[k % kRing] = rd(k + kRing);
+      acc[dbk] = mfma_bf16(op, sub ? b1[q2] : b0[q2], acc[dbk]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
   auto write_out = [&](float* dst, const f32x16 (&acc)[D / 32], float mul) {
     if (key < N) {
@@ -499,10 +534,7 @@ __global__ __launch_bounds__(kKVThreads) void dkdv_kernel(
       }
       __syncthreads();
       // dV^T += dO^T P
-      if (!idle) {
-        cols_product(dv, tl.g, pb[0], 0);
-        cols_product(dv, tl.g, pb[1], 1);
-      }
+      if (!idle) cols_product_pair(dv, tl.g, pb[0], pb[1]);
       if (st + 1 < nsteps) store(tiles[(st + 1) & 1]);
       __syncthreads();
     }
@@ -526,13 +558,11 @@ __global__ __launch_bounds__(kKVThreads) void dkdv_kernel(
       if (st + 1 < nsteps) fetch(st + 1);
       const bool idle = idle_at(q0);
       f32x16 dp0, dp1;
-      if (!idle) {
-        dp0 = rows_product(tl.g, vop, 0);
-        dp1 = rows_product(tl.g, vop, 1);
-      }
+      if (!idle) rows_product_pair(tl.g, vop, dp0, dp1);
       __syncthreads();
       if (!idle) {
-        // dS = P (dP - D), then dK^T += Q^T dS, one half at a time
+        // dS = P (dP - D) for both halves, then dK^T += Q^T dS
+        u32x4 db[2][2];
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
           const f32x16& dp = sub ? dp1 : dp0;
@@ -545,9 +575,10 @@ __global__ __launch_bounds__(kKVThreads) void dkdv_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) ds[4 * i + e] = pd[e] * (dp[4 * i + e] - d4[e]);
           }
-          const u32x4 db[2] = {pack_chunk(ds, 0), pack_chunk(ds, 1)};
-          cols_product(dk, tl.q, db, sub);
+          db[sub][0] = pack_chunk(ds, 0);
+          db[sub][1] = pack_chunk(ds, 1);
         }
+        cols_product_pair(dk, tl.q, db[0], db[1]);
       }
       if (st + 1 < nsteps) store(tiles[(st + 1) & 1]);
       __syncthreads();
