@@ -388,7 +388,44 @@ def rates():
     power = clock_under_load(lib, ncu)
     return {"unit": "ns per wave instruction per SIMD (element-step for the exp2 rows)",
             "rates": {k: round(v, 4) for k, v in out_rates.items()},
-            "clock_under_load": power}
+            "clock_under_load": power,
+            "mfma_valu_overlap": mfma_valu_overlap(lib, ncu)}
+
+
+def mfma_valu_overlap(lib, ncu, iters=20000):
+    """SIMD cycles per bf16 MFMA (32x32x16) when each MFMA is followed by V independent fp32
+    FMAs, at one and at two waves per SIMD: how much VALU work hides under the matrix unit.
+    An MFMA alone takes 32 cycles; the FMAs alone take 4 cycles each."""
+    import ctypes
+    import torch
+    P, I = ctypes.c_void_p, ctypes.c_int
+    lib.probe_overlap.argtypes = [P, P, I, I, I, I, P]
+    out = torch.empty(ncu * 512, dtype=torch.float32, device="cuda")
+    res = {}
+    for threads in (256, 512):
+        for v in (0, 4, 8, 12, 16):
+            stats = torch.zeros(2, dtype=torch.int64, device="cuda")
+
+            def go(st):
+                assert lib.probe_overlap(out.data_ptr(), st.data_ptr(), ncu, threads, iters, v,
+                                         None) == 0
+            go(stats)
+            torch.cuda.synchronize()
+            best = 1e30
+            for _ in range(3):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                go(stats)
+                b.record()
+                torch.cuda.synchronize()
+                best = min(best, a.elapsed_time(b))
+            cyc, ticks = (int(x) for x in stats.cpu())
+            ghz = cyc / ticks * 0.1
+            per_simd = (threads // 256) * iters * 4
+            res[f"waves_per_simd={threads // 256}/fma_per_mfma={v}"] = {
+                "simd_cycles_per_mfma": round(best * 1e-3 * ghz * 1e9 / per_simd, 1),
+                "clock_ghz": round(ghz, 3)}
+    return res
 
 
 def clock_under_load(lib, ncu, seconds=1.0, iters=8000):

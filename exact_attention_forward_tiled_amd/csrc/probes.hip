@@ -122,6 +122,52 @@ __global__ void mfma_rate_probe(float* out, int iters) {
   out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// MFMA / VALU co-issue probe: one block per CU (the 96 KiB LDS pad keeps a second one off),
+// 256 threads (one wave per SIMD) or 512 (two).  Each wave runs `iters` rounds of 4
+// v_mfma_f32_32x32x16_bf16 on 4 independent accumulators, each MFMA followed by V fp32 FMAs
+// on 8 independent loop-carried chains.  The SIMD's cycles per (MFMA + V FMAs) over all its
+// waves is the event-timed launch span times the clock, divided by its MFMAs.
+// stats (2 x u64, summed atomically): shader-clock cycles and 100 MHz ticks of wave 0 of
+// each block, whose ratio is the clock.
+template <int V>
+__global__ void __launch_bounds__(512) overlap_probe(float* __restrict__ out,
+                                                     unsigned long long* __restrict__ stats,
+                                                     int iters) {
+  __shared__ float pad[24576];
+  pad[threadIdx.x] = (float)threadIdx.x;
+  const int l = threadIdx.x & 63;
+  u32x4 av = {(uint32_t)l, 1u, 2u, 3u}, bv = {3u, 2u, 1u, (uint32_t)l};
+  const bf16x8 a = as_bf16x8(av), b = as_bf16x8(bv);
+  f32x16 c[4] = {zero16(), zero16(), zero16(), zero16()};
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = (float)(threadIdx.x + i) * 1e-3f;
+  __syncthreads();
+  const float y = 0.999f + 1e-9f * pad[threadIdx.x ^ 1], z = 1e-7f;
+  const unsigned long long c0 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      c[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[k], 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < V; ++v) x[v & 7] = __builtin_fmaf(x[v & 7], y, z);
+    }
+  }
+  const unsigned long long c1 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) s += c[k][0] + c[k][15];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += x[i];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+  if (threadIdx.x == 0) {
+    atomicAdd(stats, c1 - c0);
+    atomicAdd(stats + 1, r1 - r0);
+  }
+}
+
 // Clock-under-load probe, in the attention kernels' shape: 512-thread blocks (8 waves, two
 // per SIMD), one block per CU.  Each wave runs `iters` iterations of 8
 // v_mfma_f32_32x32x16_bf16 on operands taken from random data (src: 2048 x 16 bytes):
@@ -396,6 +442,26 @@ int probe_power(const void* src, float* out, unsigned long long* stats, int bloc
   if (mode == 0) go(power_probe<0>);
   else if (mode == 1) go(power_probe<1>);
   else go(power_probe<2>);
+  return (int)hipGetLastError();
+}
+
+// out: blocks * threads floats; stats: 2 x u64 (added to); threads 256 or 512; v in
+// {0, 4, 8, 12, 16}.
+int probe_overlap(float* out, unsigned long long* stats, int blocks, int threads, int iters,
+                  int v, void* stream) {
+  if (blocks < 1 || iters < 1 || (threads != 256 && threads != 512)) return -1;
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(blocks), dim3(threads), 0, (hipStream_t)stream, out, stats,
+                       iters);
+  };
+  switch (v) {
+    case 0: go(overlap_probe<0>); break;
+    case 4: go(overlap_probe<4>); break;
+    case 8: go(overlap_probe<8>); break;
+    case 12: go(overlap_probe<12>); break;
+    case 16: go(overlap_probe<16>); break;
+    default: return -1;
+  }
   return (int)hipGetLastError();
 }
 
