@@ -47,6 +47,9 @@ int check_common(int B, int Hq, int Hkv, int N, int d, int causal, float scale) 
   if (!isfinite(scale)) return ATTN_EINVAL;
   // every flat row index b*Hq*N + h*N + i must fit in 32 bits
   if ((long long)B * Hq * N >= (1LL << 31)) return ATTN_EUNSUPPORTED;
+  // the forwards address one head's K and V tiles through buffer descriptors with 32-bit
+  // byte offsets: one head's bf16 K (N * d * 2 bytes) must stay under 2 GiB
+  if ((long long)N * d * 2 >= (1LL << 31)) return ATTN_EUNSUPPORTED;
   return ATTN_OK;
 }
 

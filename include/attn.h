@@ -27,6 +27,10 @@
  *  - Arguments are validated before anything is launched; on error nothing is
  *    written.  Return codes are attn_status values; no C++ exception crosses
  *    the ABI.
+ *  - Size limits (attention calls): B*Hq*N < 2^31 rows, and one head's bf16 K
+ *    under 2 GiB (N*d*2 < 2^31, i.e. N < 2^23 at d = 128); larger requests return
+ *    ATTN_EUNSUPPORTED (the kernels address rows and a head's K/V tiles with
+ *    32-bit offsets).
  */
 #ifndef ATTN_H
 #define ATTN_H
@@ -41,7 +45,8 @@ typedef enum attn_status {
     ATTN_OK = 0,
     ATTN_EINVAL = -1,        /* null pointer, non-positive size, Hq % Hkv != 0, causal not 0/1,
                                 non-finite scale, bad option value */
-    ATTN_EUNSUPPORTED = -2,  /* valid request the library does not implement (e.g. d not 64/128) */
+    ATTN_EUNSUPPORTED = -2,  /* valid request the library does not implement (e.g. d not 64/128,
+                                sizes past the limits below) */
     ATTN_EHIP = -3           /* a HIP runtime call or kernel launch failed; see attn_last_hip_error */
 } attn_status;
 

@@ -55,6 +55,8 @@ FAKE = 4096  # a 16-byte aligned non-null address; never dereferenced on these p
     (dict(scale=float("inf")), -1),
     (dict(d=96), -2),
     (dict(d=256), -2),
+    (dict(N=1 << 23, d=128, Hq=1), -2),        # one head's K reaches 2 GiB
+    (dict(B=1 << 16, N=1 << 15, Hq=1), -2),    # 2^31 rows
 ])
 def test_fwd_validation(fa, args, code):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, Hq=2, Hkv=1, N=16, d=64, causal=0,
