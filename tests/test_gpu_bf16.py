@@ -240,6 +240,35 @@ def test_sliding_window_large_sampled_rows():
         _check(o[0, h, rows], lse[0, h, rows], ro, rl, f"head {h}")
 
 
+def test_long_sequence_sampled_rows():
+    """One head of N = 2^18 keys (non-causal, 64 MiB of K and of V), far past the workloads'
+    lengths: sampled rows, both ends and tile edges included, against the oracle's rows."""
+    B, Hq, Hkv, N, d = 1, 1, 1, 1 << 18, 128
+    qb, kb, vb = random_case(61, B, Hq, Hkv, N, d)
+    o, lse = _run(qb, kb, vb, False, d ** -0.5)
+    q64, k64, v64 = (synth.bf16_bits_to_f64(x) for x in (qb, kb, vb))
+    rng = np.random.default_rng(61)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 255, 256, N - 257, N - 65, N - 64, N - 1],
+                                     rng.integers(0, N, 10)]))
+    ro, rl = oracle.attention_rows(q64, k64, v64, False, d ** -0.5, 0, 0, rows)
+    _check(o[0, 0, rows], lse[0, 0, rows], ro, rl, "N = 2^18")
+
+
+def test_long_sequence_window_sampled_rows():
+    """Causal GQA over N = 2^19 keys with a 2048-key window (the band bookkeeping and row
+    offsets at half a million rows): sampled rows of both query heads."""
+    B, Hq, Hkv, N, d, W = 1, 2, 1, 1 << 19, 128, 2048
+    qb, kb, vb = random_case(62, B, Hq, Hkv, N, d)
+    o, lse = _run(qb, kb, vb, True, d ** -0.5, window=W)
+    q64, k64, v64 = (synth.bf16_bits_to_f64(x) for x in (qb, kb, vb))
+    rng = np.random.default_rng(62)
+    rows = np.unique(np.concatenate([[0, 1, W - 1, W, W + 1, N - 257, N - 1],
+                                     rng.integers(0, N, 9)]))
+    for h in range(Hq):
+        ro, rl = oracle.attention_rows(q64, k64, v64, True, d ** -0.5, 0, h, rows, window=W)
+        _check(o[0, h, rows], lse[0, h, rows], ro, rl, f"N = 2^19, W {W}, head {h}")
+
+
 MOD_CASES = [
     # B, Hq, Hkv, N, d, causal, softcap, alibi, window
     (1, 2, 2, 256, 128, False, 5.0, False, 0),
