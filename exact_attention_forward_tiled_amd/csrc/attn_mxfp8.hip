@@ -420,6 +420,10 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict_
   const int ka0 = kpos8(kr0) * k8KStride + 16 * h, ka1 = kpos8(kr1) * k8KStride + 16 * h;
   const int va = n32 * k8VStride + 16 * h;
   const uint32_t ONES = 0x38383838u;           // E4M3 1.0 in every byte
+  // the all-ones A operand of the row-sum product, built once: opaque to the compiler, so
+  // it stays in its registers instead of being rebuilt before every product
+  i32x8 ones8 = fp8_operand(u32x4{ONES, ONES, ONES, ONES}, u32x4{ONES, ONES, ONES, ONES});
+  asm volatile("" : "+v"(ones8));
 
   // MFMAs of one pipeline step: QK of this step's tile into sn (K from bb), then PV and
   // row sum of the previous tile (P codes pp, P scale byte ep, V^T from bb).  The PV
@@ -454,9 +458,8 @@ void fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict_
                                                                   acc[cb], 0, 0, 0, vs, 0,
                                                                   (int)ep);
       }
-      const u32x4 ones = {ONES, ONES, ONES, ONES};
-      lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp8_operand(ones, ones), bp, lacc,
-                                                             0, 0, 0, 127, 0, (int)ep);
+      lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones8, bp, lacc, 0, 0, 0, 127, 0,
+                                                             (int)ep);
     }
   };
 
