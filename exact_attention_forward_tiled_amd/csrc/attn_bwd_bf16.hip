@@ -41,7 +41,6 @@ constexpr int kBThreads = kBWaves * 64;
 constexpr int kBBlock = kBWaves * 32;    // keys (dK/dV) or queries (dQ) per workgroup
 constexpr int kBTile = 64;               // queries (dK/dV) or keys (dQ) staged per loop step
 constexpr int kSub = 32;                 // rows per MFMA block: a step is two such halves
-constexpr int kColStride = kBTile * 2 + 16;  // bytes per staged transposed column (padded)
 
 __device__ __forceinline__ int perm_row(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
@@ -59,67 +58,6 @@ __device__ __forceinline__ u32x4 pack_chunk(const f32x16& x, int c) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) r[i] = pack_bf16x2(x[8 * c + 2 * i], x[8 * c + 2 * i + 1]);
   return r;
-}
-
-// Staged tile: 64 rows x D bf16 of two tensors, row-major (rows padded by 16 bytes: the
-// 16 rows read together start 4 banks apart) and transposed.
-template <int D>
-struct alignas(16) BTile {
-  static constexpr int kRow = D * 2 + 16;   // bytes per staged row
-  float s0[kBTile];                   // per-row scalars (LSE, D) of the dK/dV tile
-  float s1[kBTile];
-  uint8_t a[kBTile * kRow];           // tensor A, row r at r * kRow
-  uint8_t b[kBTile * kRow];           // tensor B
-  uint8_t at[D * kColStride];         // A transposed: column d at d * kColStride, 64 rows
-  uint8_t bt[D * kColStride];         // B transposed
-};
-
-// One thread's share of a staged tile pair: D / 32 units of 16 bytes of each tensor.
-// Unit u is row u % 64, bytes 16 * (u / 64) .. + 15, so the lanes of a wave take 64
-// consecutive rows: their 2-byte writes into the transposed copy fall on 32 distinct
-// dwords of one column instead of piling onto two banks.
-template <int D>
-struct StageRegs {
-  static constexpr int kUnits = kBTile * D * 2 / 16 / kBThreads;
-  u32x4 a[kUnits], b[kUnits];
-};
-
-// Fetch rows r0 .. r0 + 63 of two [N, D] bf16 tensors into registers (rows past N read
-// as row N - 1: in bounds; their contributions are masked by the caller).
-template <int D>
-__device__ __forceinline__ void stage_load(StageRegs<D>& sr, const uint16_t* A,
-                                           const uint16_t* B, int r0, int N) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int u = 0; u < StageRegs<D>::kUnits; ++u) {
-    const int unit = tid + u * kBThreads;
-    const int row = unit % kBTile, c16 = unit / kBTile;
-    const int gr = min(r0 + row, N - 1);
-    sr.a[u] = *(const u32x4*)(A + (size_t)gr * D + 8 * c16);
-    sr.b[u] = *(const u32x4*)(B + (size_t)gr * D + 8 * c16);
-  }
-}
-
-__device__ __forceinline__ void put_transposed(uint8_t* t, const u32x4& v, int row, int c16) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    *(uint16_t*)(t + (8 * c16 + i) * kColStride + 2 * row) = (uint16_t)(v[i >> 1] >> (16 * (i & 1)));
-}
-
-// Write the fetched rows into LDS: both tensors row-major, and transposed where asked.
-template <int D>
-__device__ __forceinline__ void stage_store(BTile<D>& t, const StageRegs<D>& sr,
-                                            bool transposed_a, bool transposed_b) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int u = 0; u < StageRegs<D>::kUnits; ++u) {
-    const int unit = tid + u * kBThreads;
-    const int row = unit % kBTile, c16 = unit / kBTile;
-    *(u32x4*)(t.a + row * BTile<D>::kRow + 16 * c16) = sr.a[u];
-    *(u32x4*)(t.b + row * BTile<D>::kRow + 16 * c16) = sr.b[u];
-    if (transposed_a) put_transposed(t.at, sr.a[u], row, c16);
-    if (transposed_b) put_transposed(t.bt, sr.b[u], row, c16);
-  }
 }
 
 __device__ __forceinline__ u32x4 lds_u32x4(const uint8_t* p) { return *(const u32x4*)p; }
@@ -598,8 +536,9 @@ struct alignas(16) KVTile {
 // dQ for 128 queries of one (batch, query head): each wave owns 32 queries; the loop
 // runs over 64-key tiles (causal: up to the workgroup's last query; BAND: the tiles within
 // the queries' window and documents).  The key tiles are double-buffered: the next tile is
-// fetched into registers at the top of a step and written to the other buffer at its end,
-// one barrier per step.  K^T comes from the stored K rows through transposing reads.
+// loaded straight into the other buffer (direct-to-LDS, no registers) at the top of a step
+// and waited for at the step's one barrier.  K^T comes from the stored K rows through
+// transposing reads.
 // (The body; the kernels below set the waves per SIMD.)
 // CAP: the soft-capping path is compiled in (MODS with ALiBi only leaves it out).
 template <int D, bool CAUSAL, bool BAND, bool MODS, bool CAP_ON = MODS>
@@ -610,7 +549,6 @@ __device__ __forceinline__ void dq_body(
     int Hq, int Hkv, int N, int nqb, float c, float scale, Band band, Mods mods) {
   using Tile = KVTile<D>;
   constexpr int kChunk = Tile::kChunk;
-  constexpr int kUnits = kBTile * D * 2 / 16 / kBThreads;    // 16-byte units per thread
   __shared__ Tile tiles[2];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -680,37 +618,37 @@ __device__ __forceinline__ void dq_body(
                     (8 * h + ((lane & 15) >> 2)) * 16 + 8 * (lane & 1);
   // staging: unit u of a thread is row unit % 64, chunk unit / 64 (rows past N read as row
   // N - 1: in bounds; their keys are masked)
-  u32x4 sk[kUnits], sv[kUnits];
-  auto fetch = [&](int kt) {
-    const int k0 = kt * kBTile;
-#pragma unroll
-    for (int u = 0; u < kUnits; ++u) {
-      const int unit = tid + u * kBThreads;
-      const size_t gr = khead + min(k0 + unit % kBTile, N - 1);
-      sk[u] = *(const u32x4*)(K + gr * D + 8 * (unit / kBTile));
-      sv[u] = *(const u32x4*)(V + gr * D + 8 * (unit / kBTile));
-    }
-  };
-  auto store = [&](Tile& t) {
-#pragma unroll
-    for (int u = 0; u < kUnits; ++u) {
-      const int unit = tid + u * kBThreads;
-      const int off = (unit / kBTile) * kChunk + (unit % kBTile) * 16;
-      *(u32x4*)(t.k + off) = sk[u];
-      *(u32x4*)(t.v + off) = sv[u];
-    }
-  };
+
   // ALiBi slope of this query head, log2 units (0: no bias)
   const float slope2 = (MODS && mods.alibi != nullptr) ? mods.alibi[hq] * kLog2e : 0.f;
-  if (kt1 > kt0) {
-    fetch(kt0);
-    store(tiles[0]);
-  }
-  __syncthreads();
+  // the next tile straight from global memory into LDS: one wave-wide 16-byte load per
+  // 64-row column chunk (lane = row, consecutive LDS slots); waited for at the barrier
+  auto fetch_lds = [&](int kt, Tile& t) {
+    const size_t gr = khead + min(kt * kBTile + lane, N - 1);
+#pragma unroll
+    for (int i = 0; i < 2 * (D / 8) / kBWaves; ++i) {
+      const int cid = wave + i * kBWaves;
+      const int c = cid % (D / 8);
+      const bool isv = cid >= D / 8;
+      const uint16_t* src = (isv ? V : K) + gr * D + 8 * c;
+      const uint32_t lds = __builtin_amdgcn_readfirstlane(
+          (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)((isv ? t.v : t.k) + c * kChunk));
+      // written out rather than the builtin, with which the compiler makes the next LDS read
+      // of any address wait for these loads.  m0 is a register the compiler reserves: no
+      // other code in these kernels uses it, so its clobber needs no save or restore.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
+                   : "memory", "m0");
+#pragma clang diagnostic pop
+    }
+  };
+  if (kt1 > kt0) fetch_lds(kt0, tiles[0]);
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   for (int kt = kt0; kt < kt1; ++kt) {
     const Tile& tl = tiles[(kt - kt0) & 1];
     const int k0 = kt * kBTile;
-    if (kt + 1 < kt1) fetch(kt + 1);
+    if (kt + 1 < kt1) fetch_lds(kt + 1, tiles[(kt + 1 - kt0) & 1]);
     // this wave's queries see none of the tile's keys: nothing to do in this step
     const bool idle = BAND ? (qw0 >= N || k0 > w_hi || k0 + kBTile - 1 < w_lo)
                            : (CAUSAL && k0 > qw0 + 31);
@@ -800,8 +738,7 @@ __device__ __forceinline__ void dq_body(
         for (int sub = 0; sub < kBTile / kSub; ++sub) half(sub);
       }
     }
-    if (kt + 1 < kt1) store(tiles[(kt + 1 - kt0) & 1]);
-    __syncthreads();
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
   if (qi < N) {
     float* row = dQ + (qhead + qi) * D;
