@@ -6,11 +6,14 @@
 // tiling plus recomputation; "Hardware-Aware FP4 FlashAttention-4", section
 // "2. Causal Backward Cuantizado": the forward saves the LSE and the backward
 // rebuilds the probabilities from it).  With s = scale q.k and P = exp(s - LSE):
-//   D_i  = dO_i . O_i                         (delta_kernel)
+//   D_i  = dO_i . O_i                         (dq_kernel, for its own query rows, into the
+//                                              caller's workspace)
 //   dS   = P * (dO V^T - D)
+//   dQ   = scale dS K                          (dq_kernel, one workgroup per query block;
+//                                              launched first)
 //   dV   = P^T dO,  dK = scale dS^T Q          (dkdv_kernel, one workgroup per key block,
-//                                              two waves of different roles per 32 keys)
-//   dQ   = scale dS K                          (dq_kernel, one workgroup per query block)
+//                                              two waves of different roles per 32 keys;
+//                                              reads D from the workspace)
 // Each kernel recomputes S and dP for its own orientation, so every output is
 // written once by one workgroup: no atomics, deterministic results.  The forward's
 // masks (causal, sliding window, documents) and score modifications (soft-capping,
@@ -107,33 +110,6 @@ struct Band {
     }
   }
 };
-
-// D_i = dO_i . O_i, HD / 8 threads per row (8 elements each).
-template <int HD>
-__global__ void delta_kernel(const float* __restrict__ O, const uint16_t* __restrict__ dO,
-                             float* __restrict__ D, long long rows) {
-  constexpr int kParts = HD / 8;
-  const long long row = (long long)blockIdx.x * (256 / kParts) + (threadIdx.x / kParts);
-  const int part = threadIdx.x % kParts;
-  float acc = 0.f;
-  if (row < rows) {
-    const f32x4* o = (const f32x4*)(O + row * HD + 8 * part);
-    const u32x4 g = *(const u32x4*)(dO + row * HD + 8 * part);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const f32x4 ov = o[i];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t w = g[2 * i + (e >> 1)];
-        const float gv = __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
-        acc = __builtin_fmaf(ov[e], gv, acc);
-      }
-    }
-  }
-#pragma unroll
-  for (int off = kParts / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, kParts);
-  if (row < rows && part == 0) D[row] = acc;
-}
 
 // The forward's score modifications, on the scaled score s (log2 units below): soft-capping
 // t = C tanh(s / C), then the ALiBi bias t -= a_h |i - j|.  P is rebuilt from the modified
@@ -545,8 +521,9 @@ template <int D, bool CAUSAL, bool BAND, bool MODS, bool CAP_ON = MODS>
 __device__ __forceinline__ void dq_body(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ Delta, float* __restrict__ dQ,
-    int Hq, int Hkv, int N, int nqb, float c, float scale, Band band, Mods mods) {
+    const float* __restrict__ LSE, const float* __restrict__ O, float* __restrict__ Delta,
+    float* __restrict__ dQ, int Hq, int Hkv, int N, int nqb, float c, float scale, Band band,
+    Mods mods) {
   using Tile = KVTile<D>;
   constexpr int kChunk = Tile::kChunk;
   __shared__ Tile tiles[2];
@@ -577,10 +554,28 @@ __device__ __forceinline__ void dq_body(
       qop[cc] = *(const u32x4*)(qrow + 16 * cc + 8 * h);
       gop[cc] = *(const u32x4*)(grow + 16 * cc + 8 * h);
     }
+    // D = dO . O for this lane's query: the lane holds dO at d = 16 cc + 8 h .. + 7; the
+    // other half-wave holds the rest of the row
+    const float* orow = O + (qhead + qr) * D;
+    float part = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc) {
+      const f32x4 o0 = *(const f32x4*)(orow + 16 * cc + 8 * h);
+      const f32x4 o1 = *(const f32x4*)(orow + 16 * cc + 8 * h + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w = gop[cc][e >> 1];
+        const float gv = __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+        part = __builtin_fmaf(e < 4 ? o0[e] : o1[e - 4], gv, part);
+      }
+    }
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part),
+                                               false, false);
+    dlt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     if (qi < N) {
       const float l = LSE[qhead + qi];
       lse2 = (l == -__builtin_inff()) ? __builtin_inff() : l * kLog2e;
-      dlt = Delta[qhead + qi];
+      if (h == 0) Delta[qhead + qi] = dlt;   // for the dK / dV kernel, launched after this one
     }
     // wait for the operands here: left pending into the loop, they would make every step
     // wait for its own prefetch of the next tile as well
@@ -759,10 +754,11 @@ template <int D, bool CAUSAL, bool BAND, bool MODS, bool CAP_ON = MODS>
 __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ Delta, float* __restrict__ dQ,
-    int Hq, int Hkv, int N, int nqb, float c, float scale, Band band, Mods mods) {
-  dq_body<D, CAUSAL, BAND, MODS, CAP_ON>(Q, K, V, dO, LSE, Delta, dQ, Hq, Hkv, N, nqb, c, scale,
-                                         band, mods);
+    const float* __restrict__ LSE, const float* __restrict__ O, float* __restrict__ Delta,
+    float* __restrict__ dQ, int Hq, int Hkv, int N, int nqb, float c, float scale, Band band,
+    Mods mods) {
+  dq_body<D, CAUSAL, BAND, MODS, CAP_ON>(Q, K, V, dO, LSE, O, Delta, dQ, Hq, Hkv, N, nqb, c,
+                                         scale, band, mods);
 }
 
 // The same at one wave per SIMD (up to 512 registers): the soft-capping form at d = 128,
@@ -771,37 +767,26 @@ template <int D, bool CAUSAL, bool BAND, bool MODS>
 __global__ __launch_bounds__(kBThreads) void dq_kernel_1w(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ Delta, float* __restrict__ dQ,
-    int Hq, int Hkv, int N, int nqb, float c, float scale, Band band, Mods mods) {
-  dq_body<D, CAUSAL, BAND, MODS>(Q, K, V, dO, LSE, Delta, dQ, Hq, Hkv, N, nqb, c, scale, band,
-                                 mods);
+    const float* __restrict__ LSE, const float* __restrict__ O, float* __restrict__ Delta,
+    float* __restrict__ dQ, int Hq, int Hkv, int N, int nqb, float c, float scale, Band band,
+    Mods mods) {
+  dq_body<D, CAUSAL, BAND, MODS>(Q, K, V, dO, LSE, O, Delta, dQ, Hq, Hkv, N, nqb, c, scale,
+                                 band, mods);
 }
 
 template <int D, bool CAUSAL, bool BAND, bool MODS>
 hipError_t launch_bwd_t(const BwdArgs& a) {
-  const long long rows = (long long)a.B * a.Hq * a.N;
-  constexpr int kRowsPerBlock = 256 / (D / 8);
-  hipLaunchKernelGGL(delta_kernel<D>, dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)),
-                     dim3(256), 0, (hipStream_t)a.stream, a.o, (const uint16_t*)a.dout, a.delta,
-                     rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int nb = (a.N + kBBlock - 1) / kBBlock;
   const Band band{a.N, a.window, a.n_docs, a.doc_offsets};
   const Mods mods{a.alibi, a.softcap > 0.f ? 2.f * a.c / a.softcap : 0.f,
                   a.softcap * kLog2e};
-  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, BAND, MODS>), dim3((unsigned)(a.B * a.Hkv * nb)),
-                     dim3(kKVThreads), 0, (hipStream_t)a.stream, (const uint16_t*)a.q,
-                     (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse,
-                     a.delta, a.dk, a.dv, a.Hq, a.Hkv, a.N, nb, a.c, a.scale, band, mods);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // dQ first: it also computes D = dO . O for its rows into the workspace
   const dim3 grid((unsigned)(a.B * a.Hq * nb));
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, dim3(kBThreads), 0, (hipStream_t)a.stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dout, a.lse, a.delta, a.dq, a.Hq, a.Hkv, a.N, nb, a.c,
-                       a.scale, band, mods);
+                       (const uint16_t*)a.dout, a.lse, a.o, a.delta, a.dq, a.Hq, a.Hkv, a.N, nb,
+                       a.c, a.scale, band, mods);
   };
   if constexpr (MODS && D == 128) {
     if (a.softcap > 0.f) go(dq_kernel_1w<D, CAUSAL, BAND, MODS>);
@@ -809,6 +794,12 @@ hipError_t launch_bwd_t(const BwdArgs& a) {
   } else {
     go(dq_kernel<D, CAUSAL, BAND, MODS>);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, BAND, MODS>), dim3((unsigned)(a.B * a.Hkv * nb)),
+                     dim3(kKVThreads), 0, (hipStream_t)a.stream, (const uint16_t*)a.q,
+                     (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse,
+                     a.delta, a.dk, a.dv, a.Hq, a.Hkv, a.N, nb, a.c, a.scale, band, mods);
   return hipGetLastError();
 }
 
