@@ -474,6 +474,9 @@ __global__ __launch_bounds__(kKVThreads) void dkdv_kernel(
       f32x16 dp0, dp1;
       if (!idle) rows_product_pair(tl.g, vop, dp0, dp1);
       __syncthreads();
+      // the dS wave's dS and dK are this phase's longest chain (the P wave only has its dV
+      // products): its instructions go first when both waves of the SIMD are ready
+      __builtin_amdgcn_s_setprio(1);
       if (!idle) {
         // dS = P (dP - D) for both halves, then dK^T += Q^T dS
         u32x4 db[2][2];
@@ -494,6 +497,7 @@ __global__ __launch_bounds__(kKVThreads) void dkdv_kernel(
         }
         cols_product_pair(dk, tl.q, db[0], db[1]);
       }
+      __builtin_amdgcn_s_setprio(0);
       if (st + 1 < nsteps) store(tiles[(st + 1) & 1]);
       __syncthreads();
     }
@@ -711,7 +715,10 @@ __device__ __forceinline__ void dq_body(
         if (full) elements(std::false_type{}, std::false_type{});
         else elements(std::false_type{}, std::true_type{});
       }
-      // dQ^T += K^T dS^T (d x queries), over the two 16-key chunks; K^T by transposing reads
+      // dQ^T += K^T dS^T (d x queries), over the two 16-key chunks; K^T by transposing reads.
+      // Raised priority: the other workgroup's wave on this SIMD then does its element work
+      // beside these products instead of taking turns with them
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
         const u32x4 db = pack_chunk(ds, k2);
@@ -721,6 +728,7 @@ __device__ __forceinline__ void dq_body(
               lds_tr_operand(tl.k + 4 * dbk * kChunk + (kSub * sub + 16 * k2) * 16 + t_off), db,
               dq[dbk]);
       }
+      __builtin_amdgcn_s_setprio(0);
     };
     if (!idle) {
       // the band and modified forms' extra work would not fit two halves at once in the
