@@ -229,8 +229,9 @@ int attn_quantize_mxfp8_cols_t(const float* x, uint8_t* codes, uint8_t* scales,
  *   dq fp32 [B, Hq, N, d], dk, dv fp32 [B, Hkv, N, d] (outputs, every element written);
  *   delta: caller-owned device workspace of B*Hq*N floats (overwritten; holds D afterwards).
  *   d in {64, 128} (else ATTN_EUNSUPPORTED); any N >= 1; causal in {0, 1}; scale finite.
- *   Three kernels are queued on `stream` (null: the null stream); no atomics, so the
- *   results are deterministic.
+ *   Two kernels are queued on `stream` (null: the null stream): dQ, which also writes D
+ *   into the workspace, then dK / dV, which reads it; no atomics, so the results are
+ *   deterministic.
  */
 int attn_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse,
              const void* dout, float* dq, float* dk, float* dv, float* delta,
