@@ -513,8 +513,9 @@ struct alignas(16) KVTile {
   uint8_t v[D / 8 * kChunk];
 };
 
-// dQ for 128 queries of one (batch, query head): each wave owns 32 queries; the loop
-// runs over 64-key tiles (causal: up to the workgroup's last query; BAND: the tiles within
+// dQ for 128 queries of one (batch, query head), and D = dO . O for those queries (written
+// to the workspace for the dK / dV kernel): each wave owns 32 queries; the loop runs over
+// 64-key tiles (causal: up to the workgroup's last query; BAND: the tiles within
 // the queries' window and documents).  The key tiles are double-buffered: the next tile is
 // loaded straight into the other buffer (direct-to-LDS, no registers) at the top of a step
 // and waited for at the step's one barrier.  K^T comes from the stored K rows through
