@@ -227,23 +227,39 @@ def test_bwd_score_modifications(case):
            ref, "GPU forward O/LSE")
 
 
-def test_bwd_delta_workspace():
-    """The caller's workspace ends holding D_i = dO_i . O_i (the first kernel's output), which
-    the oracle pins as sum_j P_ij dP_ij."""
+DELTA_CASES = [
+    # causal, window, docs, d, softcap: every form of the dQ kernel that writes D
+    (True, 0, None, 128, 0.0),
+    (False, 40, None, 128, 0.0),
+    (True, 0, [0, 1, 120, 300], 128, 0.0),
+    (False, 0, None, 64, 0.0),
+    (False, 0, None, 128, 30.0),    # soft-capping at d = 128: the one-wave dQ kernel
+]
+
+
+@pytest.mark.parametrize("case", DELTA_CASES, ids=lambda c: "{}_w{}_{}_d{}_cap{}".format(
+    "c" if c[0] else "n", c[1], "docs" if c[2] else "", c[3], c[4]))
+def test_bwd_delta_workspace(case):
+    """The caller's workspace, filled with NaN beforehand, ends holding D_i = dO_i . O_i for
+    every row (written by the first kernel, whatever the mask), which the oracle pins as
+    sum_j P_ij dP_ij."""
     import torch
     import exact_attention_forward_tiled_amd as fa
-    bits, (q, k, v, g) = _case(53, 1, 4, 2, 300)
-    scale = 1.0 / math.sqrt(128)
-    o, lse = oracle.attention(q, k, v, True, scale)
+    causal, window, docs, d, softcap = case
+    bits, (q, k, v, g) = _case(53 + d, 1, 4, 2, 300, d)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = oracle.attention(q, k, v, causal, scale, window=window, docs=docs, softcap=softcap)
     qd, kd, vd, gd = (to_dev_bf16(x) for x in bits)
+    dd = None if docs is None else torch.tensor(docs, dtype=torch.int32, device="cuda")
     delta = torch.full((1, 4, 300), float("nan"), dtype=torch.float32, device="cuda")
-    log("bwd delta workspace")
-    fa.bwd(qd, kd, vd, to_dev_f32(o), to_dev_f32(lse), gd, causal=True, scale=scale, delta=delta)
+    log(f"bwd delta workspace {case}")
+    fa.bwd(qd, kd, vd, to_dev_f32(o), to_dev_f32(lse), gd, causal=causal, scale=scale,
+           delta=delta, window=window, docs=dd, softcap=softcap)
     torch.cuda.synchronize()
     got = delta.cpu().numpy()
-    # O is fed in fp32 and dO is exact in bf16: D is an fp32 dot product of 128 terms
+    # O is fed in fp32 and dO is exact in bf16: D is an fp32 dot product of d terms
     want = bw.delta(o.astype(np.float32).astype(np.float64), g)
-    bound = 128 * 2.0 ** -24 * np.sum(np.abs(o * g), axis=-1) + 1e-7
+    bound = d * 2.0 ** -24 * np.sum(np.abs(o * g), axis=-1) + 1e-7
     assert np.all(np.abs(got - want) <= bound)
 
 
