@@ -466,6 +466,9 @@ void fwd_mxfp4_kernel(const uint8_t* __restrict__ Q4, const uint8_t* __restrict_
                                               tau, h, klo, khi);
     any_prev = any;
     alpha_prev = alpha;
+    // the weights are done before the barrier: left alone, the compiler moves them into the
+    // next step, beside that step's own weights and in front of the products that use them
+    asm volatile("" ::"v"(pc), "v"(ec));
     store_stage(stg, j + 1);
     load_stage(stg, j + 2);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
