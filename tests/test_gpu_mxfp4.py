@@ -215,6 +215,23 @@ def test_directp_workload_sampled_rows():
     log(f"  mean row cosine vs unquantised exact {cos:.4f}")
 
 
+
+def test_directp_long_sequence_sampled_rows():
+    """One head of N = 2^18 keys (non-causal), far past the workloads' lengths: sampled rows,
+    both ends and block edges included, against the Direct-P emulation."""
+    N = 1 << 18
+    scale = 1.0 / math.sqrt(128)
+    q, k, v = _case(64, 1, 1, 1, N)
+    log("mxfp4 N = 2^18")
+    o, lse = _run(q, k, v, False, scale)
+    rng = np.random.default_rng(64)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 255, 256, N - 257, N - 33, N - 32, N - 1],
+                                     rng.integers(0, N, 10)]))
+    t = mx.quantize_inputs(q[:, :, rows], k, v)
+    ro, rl, _ = mx.directp_rows(t["q"][0, 0], t["k"][0, 0], t["v"][0, 0], rows, False, scale)
+    assert np.max(np.abs(lse[0, 0, rows] - rl)) < 0.05
+    gate(o[0, 0, rows], ro, MXFP4_O_RELRMS, MXFP4_O_ROW, "N = 2^18 rows vs emulation O")
+
 def test_directp_skip_ratio_stats():
     """The MXFP4 kernel's counters (steps in closed form, rescales counted where they are
     applied) against the skip-ratio model with the integer reference rule, on the

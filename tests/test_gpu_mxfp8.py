@@ -222,6 +222,26 @@ def test_fp8_workload_sampled_rows(idx):
     log(f"  mean row cosine vs unquantised exact {cos:.5f}")
 
 
+
+def test_fp8_long_sequence_sampled_rows():
+    """One head of N = 2^18 keys (non-causal), far past the workloads' lengths: sampled rows,
+    both ends and scale-block edges included, against the emulation."""
+    N = 1 << 18
+    scale = 1.0 / math.sqrt(128)
+    q, k, v = _case(63, 1, 1, 1, N)
+    log("mxfp8 N = 2^18")
+    o, lse = _run(q, k, v, False, scale)
+    rng = np.random.default_rng(63)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 255, 256, N - 257, N - 33, N - 32, N - 1],
+                                     rng.integers(0, N, 10)]))
+    t = m8.quantize_inputs(q[:, :, rows], k, v)
+    tol = mxfp8_lse_tol(t["q"], t["k"], scale)
+    ro, rl, _ = m8.fp8p_rows(t["q"][0, 0], t["k"][0, 0], t["v"][0, 0], rows, False, scale)
+    e = float(np.max(np.abs(lse[0, 0, rows] - rl)))
+    log(f"  max|dLSE|={e:.3e} (gate {tol:.3e})")
+    assert e <= tol
+    gate(o[0, 0, rows], ro, MXFP8_O_RELRMS, MXFP8_O_ROW, "N = 2^18 rows vs emulation O")
+
 MASKED = [
     # B, Hq, Hkv, N, causal, window, docs
     (1, 2, 2, 512, True, 100, None),
