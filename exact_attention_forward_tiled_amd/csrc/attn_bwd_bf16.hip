@@ -41,9 +41,12 @@ namespace {
 
 constexpr int kBWaves = 4;
 constexpr int kBThreads = kBWaves * 64;
-constexpr int kBBlock = kBWaves * 32;    // keys (dK/dV) or queries (dQ) per workgroup
+constexpr int kBBlock = kBWaves * 32;    // keys per dK / dV workgroup
 constexpr int kBTile = 64;               // queries (dK/dV) or keys (dQ) staged per loop step
 constexpr int kSub = 32;                 // rows per MFMA block: a step is two such halves
+constexpr int kQWaves = 8;               // dQ workgroup: 8 waves of 32 queries each
+constexpr int kQThreads = kQWaves * 64;
+constexpr int kQBlock = kQWaves * 32;    // queries per dQ workgroup
 
 __device__ __forceinline__ int perm_row(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
@@ -513,7 +516,7 @@ struct alignas(16) KVTile {
   uint8_t v[D / 8 * kChunk];
 };
 
-// dQ for 128 queries of one (batch, query head), and D = dO . O for those queries (written
+// dQ for 256 queries of one (batch, query head), and D = dO . O for those queries (written
 // to the workspace for the dK / dV kernel): each wave owns 32 queries; the loop runs over
 // 64-key tiles (causal: up to the workgroup's last query; BAND: the tiles within
 // the queries' window and documents).  The key tiles are double-buffered: the next tile is
@@ -541,7 +544,7 @@ __device__ __forceinline__ void dq_body(
   const WorkItem wi = decode_workgroup(blockIdx.x, gridDim.x, Hkv, group, nqb, CAUSAL);
   const int qb = CAUSAL ? nqb - 1 - wi.qb_rank : wi.qb_rank;
   const int hkv = wi.hkv, b = wi.b, hq = hkv * group + wi.g;
-  const int Q0 = qb * kBBlock;
+  const int Q0 = qb * kQBlock;
   const int qw0 = Q0 + wave * 32;
   const int qi = qw0 + n32;                 // this lane's query (accumulator column)
 
@@ -594,12 +597,12 @@ __device__ __forceinline__ void dq_body(
 
   // key tiles [kt0, kt1) reach the workgroup's queries; BAND: this lane's query sees keys
   // [q_lo, q_hi], this wave's queries see [w_lo, w_hi] together and [f_lo, f_hi] each
-  int kt0 = 0, kt1 = ((CAUSAL ? min(N, Q0 + kBBlock) : N) + kBTile - 1) / kBTile;
+  int kt0 = 0, kt1 = ((CAUSAL ? min(N, Q0 + kQBlock) : N) + kBTile - 1) / kBTile;
   int q_lo = 0, q_hi = 0, w_lo = 0, w_hi = 0, f_lo = 0, f_hi = -1;
   if (BAND) {
     int lo, hi, lo2, hi2;
     band.keys<CAUSAL>(Q0, lo, hi);
-    band.keys<CAUSAL>(min(Q0 + kBBlock - 1, N - 1), lo2, hi2);
+    band.keys<CAUSAL>(min(Q0 + kQBlock - 1, N - 1), lo2, hi2);
     kt0 = lo / kBTile;
     kt1 = hi2 / kBTile + 1;
     band.keys<CAUSAL>(min(qi, N - 1), q_lo, q_hi);
@@ -626,8 +629,8 @@ __device__ __forceinline__ void dq_body(
   auto fetch_lds = [&](int kt, Tile& t) {
     const size_t gr = khead + min(kt * kBTile + lane, N - 1);
 #pragma unroll
-    for (int i = 0; i < 2 * (D / 8) / kBWaves; ++i) {
-      const int cid = wave + i * kBWaves;
+    for (int i = 0; i < 2 * (D / 8) / kQWaves; ++i) {
+      const int cid = wave + i * kQWaves;
       const int c = cid % (D / 8);
       const bool isv = cid >= D / 8;
       const uint16_t* src = (isv ? V : K) + gr * D + 8 * c;
@@ -660,11 +663,25 @@ __device__ __forceinline__ void dq_body(
       // S^T = K_pi Q^T and dP^T = V_pi dO^T (keys x queries; rows permuted); the two
       // chains alternate, so neither product waits on its own previous one
       f32x16 s = zero16(), dp = zero16();
+      {
+        // each LDS operand read kRing products ahead (one read and one product per
+        // scheduling slot), as in the dK / dV kernel
+        constexpr int NK = 2 * (D / 16);
+        auto rd = [&](int k) {
+          return lds_u32x4(((k & 1) ? tl.v : tl.k) + 2 * (k >> 1) * kChunk + kSub * sub * 16 +
+                           a_off);
+        };
+        u32x4 ring[kRing];
 #pragma unroll
-      for (int cc = 0; cc < D / 16; ++cc) {
-        const int off = 2 * cc * kChunk + kSub * sub * 16 + a_off;
-        s = mfma_bf16(lds_u32x4(tl.k + off), qop[cc], s);
-        dp = mfma_bf16(lds_u32x4(tl.v + off), gop[cc], dp);
+        for (int i = 0; i < kRing; ++i) ring[i] = rd(i);
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+          const u32x4 op = ring[k % kRing];
+          if (k + kRing < NK) ring[k % kRing] = rd(k + kRing);
+          if (k & 1) dp = mfma_bf16(op, gop[k >> 1], dp);
+          else s = mfma_bf16(op, qop[k >> 1], s);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       // dS^T.  CAP: soft-capping; MASKED: some (key, query) pair of the half is hidden
       // (uniform choices)
@@ -716,18 +733,27 @@ __device__ __forceinline__ void dq_body(
         if (full) elements(std::false_type{}, std::false_type{});
         else elements(std::false_type{}, std::true_type{});
       }
-      // dQ^T += K^T dS^T (d x queries), over the two 16-key chunks; K^T by transposing reads.
-      // Raised priority: the other workgroup's wave on this SIMD then does its element work
-      // beside these products instead of taking turns with them
+      // dQ^T += K^T dS^T (d x queries), over the two 16-key chunks; K^T by transposing reads,
+      // through an operand ring.  Raised priority: the other wave on this SIMD then does its
+      // element work beside these products instead of taking turns with them
       __builtin_amdgcn_s_setprio(1);
+      {
+        constexpr int NK = 2 * (D / 32);
+        const u32x4 dbs[2] = {pack_chunk(ds, 0), pack_chunk(ds, 1)};
+        auto rd = [&](int k) {
+          const int k2 = k / (D / 32), dbk = k % (D / 32);
+          return lds_tr_operand(tl.k + 4 * dbk * kChunk + (kSub * sub + 16 * k2) * 16 + t_off);
+        };
+        u32x4 ring[kRing];
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const u32x4 db = pack_chunk(ds, k2);
+        for (int i = 0; i < kRing; ++i) ring[i] = rd(i);
 #pragma unroll
-        for (int dbk = 0; dbk < D / 32; ++dbk)
-          dq[dbk] = mfma_bf16(
-              lds_tr_operand(tl.k + 4 * dbk * kChunk + (kSub * sub + 16 * k2) * 16 + t_off), db,
-              dq[dbk]);
+        for (int k = 0; k < NK; ++k) {
+          const u32x4 op = ring[k % kRing];
+          if (k + kRing < NK) ring[k % kRing] = rd(k + kRing);
+          dq[k % (D / 32)] = mfma_bf16(op, dbs[k / (D / 32)], dq[k % (D / 32)]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       __builtin_amdgcn_s_setprio(0);
     };
@@ -757,10 +783,10 @@ __device__ __forceinline__ void dq_body(
   }
 }
 
-// Two waves per SIMD (at most 256 registers each; two workgroups' tiles fit the CU's LDS),
-// so one workgroup's products overlap the other's exponentials and staging.
+// One workgroup of 8 waves per CU, two waves per SIMD (at most 256 registers each): every
+// staged K / V tile serves 256 queries.  CAP_ON: the soft-capping path is compiled in.
 template <int D, bool CAUSAL, bool BAND, bool MODS, bool CAP_ON = MODS>
-__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(
+__global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ O, float* __restrict__ Delta,
@@ -770,36 +796,25 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
                                          scale, band, mods);
 }
 
-// The same at one wave per SIMD (up to 512 registers): the soft-capping form at d = 128,
-// whose per-element work does not fit the 256 registers of two waves per SIMD.
-template <int D, bool CAUSAL, bool BAND, bool MODS>
-__global__ __launch_bounds__(kBThreads) void dq_kernel_1w(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ O, float* __restrict__ Delta,
-    float* __restrict__ dQ, int Hq, int Hkv, int N, int nqb, float c, float scale, Band band,
-    Mods mods) {
-  dq_body<D, CAUSAL, BAND, MODS>(Q, K, V, dO, LSE, O, Delta, dQ, Hq, Hkv, N, nqb, c, scale,
-                                 band, mods);
-}
-
 template <int D, bool CAUSAL, bool BAND, bool MODS>
 hipError_t launch_bwd_t(const BwdArgs& a) {
-  const int nb = (a.N + kBBlock - 1) / kBBlock;
+  const int nb = (a.N + kBBlock - 1) / kBBlock;     // dK / dV: key blocks
+  const int nqb = (a.N + kQBlock - 1) / kQBlock;    // dQ: query blocks
   const Band band{a.N, a.window, a.n_docs, a.doc_offsets};
   const Mods mods{a.alibi, a.softcap > 0.f ? 2.f * a.c / a.softcap : 0.f,
                   a.softcap * kLog2e};
   // dQ first: it also computes D = dO . O for its rows into the workspace
-  const dim3 grid((unsigned)(a.B * a.Hq * nb));
+  const dim3 grid((unsigned)(a.B * a.Hq * nqb));
   auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, grid, dim3(kBThreads), 0, (hipStream_t)a.stream,
+    hipLaunchKernelGGL(kernel, grid, dim3(kQThreads), 0, (hipStream_t)a.stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dout, a.lse, a.o, a.delta, a.dq, a.Hq, a.Hkv, a.N, nb,
+                       (const uint16_t*)a.dout, a.lse, a.o, a.delta, a.dq, a.Hq, a.Hkv, a.N, nqb,
                        a.c, a.scale, band, mods);
   };
   if constexpr (MODS && D == 128) {
-    if (a.softcap > 0.f) go(dq_kernel_1w<D, CAUSAL, BAND, MODS>);
-    else go(dq_kernel<D, CAUSAL, BAND, MODS, false>);   // ALiBi only: two waves per SIMD
+    // ALiBi alone: the soft-capping path compiled out (fewer registers and instructions)
+    if (a.softcap > 0.f) go(dq_kernel<D, CAUSAL, BAND, MODS, true>);
+    else go(dq_kernel<D, CAUSAL, BAND, MODS, false>);
   } else {
     go(dq_kernel<D, CAUSAL, BAND, MODS>);
   }
